@@ -1,0 +1,152 @@
+/*
+ * oal.h -- C ABI of liboal.so: causal OAL attention on AMD Instinct MI355X (gfx950).
+ *
+ * The method is Outlier-Aware Attention Linearization, from "Not All Dimensions
+ * Are Equal: Outlier-Aware Attention Linearization with Grouped Quadratic
+ * Kernels" (Sun, Wu, Wang, Hu; arXiv 2610.13674), cited below as [OAL].
+ *
+ *   kernel      kappa(q, k) = eps + s_bar^T L L^T s_bar,  s_bar = [1, s_1 .. s_G],
+ *               s_g = sum_{r in group g} q_r k_r / sqrt(d_h)       ([OAL] §4.3, Eq. 7)
+ *   output      y_i = sum_{j<=i} kappa(q_i, k_j) v_j / sum_{j<=i} kappa(q_i, k_j)
+ *   evaluation  prefix states H0 = sum [v;1], H1_r = sum k_r [v;1],
+ *               H2_rt = sum k_r k_t [v;1] and the readout of [OAL] Eq. 5-6,
+ *               which equals the direct sum exactly ([OAL] App. D, Eq. 25).
+ *
+ * Conventions shared by every entry point
+ *   - All tensor pointers are DEVICE pointers owned by the caller, except the
+ *     opaque oal_state, which the library owns from oal_state_alloc to
+ *     oal_state_free.  Tensors are dense, row-major and contiguous.
+ *   - Every call is enqueued on `stream` and returns without synchronising.
+ *     Argument errors are detected on the host before anything is launched and
+ *     return OAL_ERR_INVALID_ARG / OAL_ERR_UNSUPPORTED; a failed launch returns
+ *     OAL_ERR_HIP.  Faults inside kernels surface at the caller's next
+ *     synchronisation.  No C++ exception crosses this boundary.
+ *   - oal_prefill and oal_decode_step never allocate device memory.
+ *   - A state must not be used from two streams at once.
+ *   - Supported shapes: d_h = d_v = 64; n_q_heads % n_kv_heads == 0, query head h
+ *     reading KV head h / (n_q_heads / n_kv_heads) (grouped-query sharing of the
+ *     KV states, [OAL] App. D); 1 <= G_h <= g_max <= 6 groups per query head.
+ *   - After a failing call, oal_last_error() returns a message for this thread.
+ */
+#ifndef OAL_H
+#define OAL_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  OAL_OK = 0,
+  OAL_ERR_INVALID_ARG = 1,   /* null pointer, bad size, inconsistent shapes           */
+  OAL_ERR_UNSUPPORTED = 2,   /* valid request this build does not implement (d_h!=64) */
+  OAL_ERR_OUT_OF_MEMORY = 3, /* oal_state_alloc could not allocate                     */
+  OAL_ERR_HIP = 4            /* a HIP runtime call or kernel launch failed             */
+} oal_status;
+
+typedef enum { OAL_F32 = 0, OAL_BF16 = 1 } oal_dtype;
+
+typedef struct oal_state oal_state; /* opaque; device memory owned by the library */
+
+/* Layout of the coefficient buffer written by oal_expand_coeffs: one record of
+ * OAL_COEF_WORDS 32-bit words per query head, record h at word h*OAL_COEF_WORDS.
+ * Word offsets inside a record (float unless noted):                              */
+#define OAL_COEF_A      0     /* a = eps + M_00                                       */
+#define OAL_COEF_EPS    1     /* eps                                                  */
+#define OAL_COEF_NG     2     /* int32: G_h                                           */
+#define OAL_COEF_BP     16    /* [64]  b'_r = b_r / sqrt(d_h) = 2 M_{0,g(r)} / sqrt(d_h) */
+#define OAL_COEF_GMAP   80    /* [64]  int32 g(r) in 1..G_h                           */
+#define OAL_COEF_M      144   /* [7][7] M = L L^T (rows/cols >= G_h+1 are zero)        */
+#define OAL_COEF_L      208   /* [7][7] L with the upper triangle zeroed              */
+#define OAL_COEF_ELL    272   /* [7][64] ell_p[r] = L_{g(r),p} / sqrt(d_h)             */
+#define OAL_COEF_CM     720   /* [64][64] C_rt / d_h = M_{g(r),g(t)} / d_h             */
+#define OAL_COEF_CP     4816  /* [2080] c'_rt = m_rt C_rt / d_h over pairs r <= t in   */
+                              /* row-major order; m = 1 if r == t else 2               */
+#define OAL_COEF_MG     6896  /* [7][64] M_{gamma,g(t)} / d_h, gamma = 0..6            */
+#define OAL_COEF_WORDS  7424
+
+/* Bytes of the coefficient buffer for n_q_heads heads (d_h must be 64, g_max <= 6). */
+size_t oal_coeffs_bytes(int n_q_heads, int d_h, int g_max);
+
+/* Coefficient expansion, [OAL] §4.3 ("set M = L L^T; a = eps + M_00,
+ * b_r = 2 M_{0,g(r)}, C_rt = M_{g(r),g(t)}") and Algorithm 1, causal-evaluation
+ * step 5.  The expanded coefficients put the grouped kernel in the dimension-wise
+ * form of [OAL] Eq. 3, which the readout of Eq. 6 evaluates.
+ *   n_groups  device int32 [n_q_heads], G_h in 1..g_max
+ *   group_map device int32 [n_q_heads][d_h], values 1..G_h (any partition, groups
+ *             need not be contiguous); out-of-range labels are clamped to 1..G_h
+ *   L         device float [n_q_heads][g_max+1][g_max+1]; only the lower triangle
+ *             of the leading (G_h+1)x(G_h+1) block is read
+ *   eps       > 0
+ *   coeffs    device output, oal_coeffs_bytes() bytes, layout above            */
+oal_status oal_expand_coeffs(int n_q_heads, int d_h, int g_max, const int32_t* n_groups,
+                             const int32_t* group_map, const float* L, float eps,
+                             void* coeffs, hipStream_t stream);
+
+/* Allocate a zeroed prefix state (H0 = H1 = H2 = 0, [OAL] Algorithm 1 step 5) for
+ * batch x n_kv_heads sequences.  The state is fp32 and its device layout is private
+ * (use oal_state_export to read it).  Size: batch*n_kv_heads*65*2176*4 bytes. */
+oal_status oal_state_alloc(int batch, int n_kv_heads, int d_h, int d_v, oal_state** out);
+/* Zero a state again (enqueued on stream). */
+oal_status oal_state_reset(oal_state* state, hipStream_t stream);
+/* Release a state (synchronises the device first).  NULL is accepted. */
+oal_status oal_state_free(oal_state* state);
+/* Copy src into dst (same shape), enqueued on stream. */
+oal_status oal_state_copy(oal_state* dst, const oal_state* src, hipStream_t stream);
+/* Bytes of device memory the state holds. */
+size_t oal_state_bytes(const oal_state* state);
+/* Number of tokens absorbed into the state so far (host-side counter kept by the
+ * library: prefill adds seq_len, a decode step adds 1, reset sets 0). */
+int64_t oal_state_tokens(const oal_state* state);
+/* Export the state in canonical packed order ([OAL] Eq. 5; packed-symmetric rows,
+ * App. D): dst is device float [batch][n_kv_heads][2145][65]; row 0 = H0,
+ * rows 1..64 = H1_r, then one row per pair r <= t of H2 in row-major pair order;
+ * column 64 is the all-ones (denominator) channel. */
+oal_status oal_state_export(const oal_state* state, float* dst, hipStream_t stream);
+
+/* Device workspace oal_prefill needs for these sizes (per-chunk prefix states).
+ * chunk = 0 selects the default (128).  Returns 0 for unsupported arguments. */
+size_t oal_prefill_workspace_bytes(int batch, int n_q_heads, int n_kv_heads, int seq_len,
+                                   int d_h, int d_v, int chunk, oal_dtype in_dtype);
+
+/* Causal prefill over seq_len tokens: [OAL] Algorithm 1 steps 6-12 evaluated in
+ * chunks (the paper's backend works on 128-token blocks, [OAL] App. E).
+ *   q   [batch][n_q_heads][seq_len][d_h];  k, v [batch][n_kv_heads][seq_len][d_h/d_v]
+ *       in in_dtype (fp32 or bf16).  q may be NULL when y is NULL.
+ *   coeffs  written by oal_expand_coeffs for n_q_heads heads
+ *   chunk   0 (= 128), 64, 128 or 256
+ *   state   NULL: the sequence starts empty.  Otherwise the prefix it holds is
+ *           read first and, on return, it holds the state after the seq_len
+ *           tokens have been appended.
+ *   y       [batch][n_q_heads][seq_len][d_v] in out_dtype, or NULL to only
+ *           advance the state (then state must not be NULL).
+ *   workspace  >= oal_prefill_workspace_bytes(...) bytes of device memory, 256-byte
+ *           aligned; may be NULL when y is NULL.
+ * seq_len == 0 is a valid no-op. */
+oal_status oal_prefill(int batch, int n_q_heads, int n_kv_heads, int seq_len, int d_h, int d_v,
+                       oal_dtype in_dtype, const void* q, const void* k, const void* v,
+                       const void* coeffs, int chunk, oal_state* state, void* y,
+                       oal_dtype out_dtype, void* workspace, size_t workspace_bytes,
+                       hipStream_t stream);
+
+/* One decode step: [OAL] Algorithm 1 loop body (steps 7-10) for one new token per
+ * sequence: u = [v; 1]; H0 += u; H1_r += k_r u; H2_rt += k_r k_t u; then the
+ * readout of Eq. 6 for every query head of the KV group (inclusive of the new
+ * token).  q [batch][n_q_heads][d_h], k [batch][n_kv_heads][d_h],
+ * v [batch][n_kv_heads][d_v] in in_dtype; y [batch][n_q_heads][d_v] in out_dtype;
+ * state in/out. */
+oal_status oal_decode_step(int batch, int n_q_heads, int n_kv_heads, int d_h, int d_v,
+                           oal_dtype in_dtype, const void* q, const void* k, const void* v,
+                           const void* coeffs, oal_state* state, void* y, oal_dtype out_dtype,
+                           hipStream_t stream);
+
+const char* oal_status_string(oal_status status);
+const char* oal_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* OAL_H */

@@ -1,0 +1,233 @@
+// Host side of the liboal C ABI: argument validation, dispatch to the kernels,
+// ownership of prefix states and error reporting.  See include/oal.h.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <new>
+
+#include "oal_common.h"
+
+namespace oal {
+
+static thread_local char g_last_error[512] = "";
+
+oal_status set_error(oal_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+oal_status check_launch(const char* what) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess)
+    return set_error(OAL_ERR_HIP, "%s: launch failed: %s", what, hipGetErrorString(e));
+  return OAL_OK;
+}
+
+// kernels' launchers (one per source file)
+oal_status launch_expand(int n_q_heads, int g_max, const int32_t* n_groups,
+                         const int32_t* group_map, const float* L, float eps, void* coeffs,
+                         hipStream_t stream);
+oal_status launch_fill_zero(float* p, size_t n_floats, hipStream_t stream);
+oal_status launch_export(const oal_state* st, float* dst, hipStream_t stream);
+oal_status launch_decode(int batch, int n_q_heads, int n_kv_heads, oal_dtype in_dtype,
+                         const void* q, const void* k, const void* v, const void* coeffs,
+                         float* state, void* y, oal_dtype out_dtype, hipStream_t stream);
+size_t prefill_vec_workspace(int batch, int n_kv_heads, int seq_len, int chunk);
+oal_status launch_prefill_vec(int batch, int n_q_heads, int n_kv_heads, int seq_len,
+                              oal_dtype in_dtype, const void* q, const void* k, const void* v,
+                              const void* coeffs, int chunk, float* state, void* y,
+                              oal_dtype out_dtype, void* ws, hipStream_t stream);
+
+static bool valid_dtype(oal_dtype d) { return d == OAL_F32 || d == OAL_BF16; }
+
+static oal_status check_heads(int batch, int n_q_heads, int n_kv_heads, int d_h, int d_v) {
+  if (batch < 1 || n_q_heads < 1 || n_kv_heads < 1)
+    return set_error(OAL_ERR_INVALID_ARG, "batch (%d), n_q_heads (%d) and n_kv_heads (%d) must be >= 1",
+                     batch, n_q_heads, n_kv_heads);
+  if (n_q_heads % n_kv_heads != 0)
+    return set_error(OAL_ERR_INVALID_ARG, "n_q_heads (%d) must be a multiple of n_kv_heads (%d)",
+                     n_q_heads, n_kv_heads);
+  if (d_h != DH || d_v != DV)
+    return set_error(OAL_ERR_UNSUPPORTED, "only d_h = d_v = 64 is supported (got %d, %d)", d_h, d_v);
+  if ((long long)batch * n_kv_heads > 65535 || (long long)batch * n_q_heads > 65535 * 64LL)
+    return set_error(OAL_ERR_UNSUPPORTED, "batch * heads too large for one launch");
+  return OAL_OK;
+}
+
+static int resolve_chunk(int chunk) { return chunk == 0 ? 128 : chunk; }
+
+}  // namespace oal
+
+using namespace oal;
+
+extern "C" {
+
+const char* oal_status_string(oal_status s) {
+  switch (s) {
+    case OAL_OK: return "OAL_OK";
+    case OAL_ERR_INVALID_ARG: return "OAL_ERR_INVALID_ARG";
+    case OAL_ERR_UNSUPPORTED: return "OAL_ERR_UNSUPPORTED";
+    case OAL_ERR_OUT_OF_MEMORY: return "OAL_ERR_OUT_OF_MEMORY";
+    case OAL_ERR_HIP: return "OAL_ERR_HIP";
+  }
+  return "OAL_ERR_UNKNOWN";
+}
+
+const char* oal_last_error(void) { return g_last_error; }
+
+size_t oal_coeffs_bytes(int n_q_heads, int d_h, int g_max) {
+  if (n_q_heads < 1 || d_h != DH || g_max < 1 || g_max > GMAX) return 0;
+  return (size_t)n_q_heads * OAL_COEF_WORDS * sizeof(float);
+}
+
+oal_status oal_expand_coeffs(int n_q_heads, int d_h, int g_max, const int32_t* n_groups,
+                             const int32_t* group_map, const float* L, float eps, void* coeffs,
+                             hipStream_t stream) {
+  if (n_q_heads < 1) return set_error(OAL_ERR_INVALID_ARG, "n_q_heads must be >= 1");
+  if (d_h != DH) return set_error(OAL_ERR_UNSUPPORTED, "only d_h = 64 is supported (got %d)", d_h);
+  if (g_max < 1 || g_max > GMAX)
+    return set_error(OAL_ERR_UNSUPPORTED, "g_max must be in 1..%d (got %d)", GMAX, g_max);
+  if (!n_groups || !group_map || !L || !coeffs)
+    return set_error(OAL_ERR_INVALID_ARG, "null pointer argument");
+  if (!(eps > 0.0f)) return set_error(OAL_ERR_INVALID_ARG, "eps must be > 0 (got %g)", (double)eps);
+  return launch_expand(n_q_heads, g_max, n_groups, group_map, L, eps, coeffs, stream);
+}
+
+oal_status oal_state_alloc(int batch, int n_kv_heads, int d_h, int d_v, oal_state** out) {
+  if (!out) return set_error(OAL_ERR_INVALID_ARG, "out is null");
+  *out = nullptr;
+  oal_status st = check_heads(batch, n_kv_heads, n_kv_heads, d_h, d_v);
+  if (st != OAL_OK) return st;
+  oal_state* s = new (std::nothrow) oal_state();
+  if (!s) return set_error(OAL_ERR_OUT_OF_MEMORY, "host allocation failed");
+  s->batch = batch;
+  s->n_kv_heads = n_kv_heads;
+  s->tokens = 0;
+  s->bytes = (size_t)batch * n_kv_heads * STATE_FLOATS * sizeof(float);
+  if (hipGetDevice(&s->device) != hipSuccess) {
+    delete s;
+    return set_error(OAL_ERR_HIP, "hipGetDevice failed");
+  }
+  if (hipMalloc(reinterpret_cast<void**>(&s->data), s->bytes) != hipSuccess) {
+    (void)hipGetLastError();
+    delete s;
+    return set_error(OAL_ERR_OUT_OF_MEMORY, "hipMalloc of %zu bytes failed", (size_t)s->bytes);
+  }
+  st = launch_fill_zero(s->data, s->bytes / sizeof(float), nullptr);
+  if (st == OAL_OK && hipDeviceSynchronize() != hipSuccess)
+    st = set_error(OAL_ERR_HIP, "zeroing the state failed");
+  if (st != OAL_OK) {
+    (void)hipFree(s->data);
+    delete s;
+    return st;
+  }
+  *out = s;
+  return OAL_OK;
+}
+
+oal_status oal_state_reset(oal_state* s, hipStream_t stream) {
+  if (!s) return set_error(OAL_ERR_INVALID_ARG, "state is null");
+  s->tokens = 0;
+  return launch_fill_zero(s->data, s->bytes / sizeof(float), stream);
+}
+
+oal_status oal_state_free(oal_state* s) {
+  if (!s) return OAL_OK;
+  oal_status st = OAL_OK;
+  if (hipDeviceSynchronize() != hipSuccess) st = set_error(OAL_ERR_HIP, "hipDeviceSynchronize failed");
+  if (hipFree(s->data) != hipSuccess) st = set_error(OAL_ERR_HIP, "hipFree failed");
+  delete s;
+  return st;
+}
+
+oal_status oal_state_copy(oal_state* dst, const oal_state* src, hipStream_t stream) {
+  if (!dst || !src) return set_error(OAL_ERR_INVALID_ARG, "state is null");
+  if (dst->batch != src->batch || dst->n_kv_heads != src->n_kv_heads)
+    return set_error(OAL_ERR_INVALID_ARG, "state shapes differ");
+  if (hipMemcpyAsync(dst->data, src->data, src->bytes, hipMemcpyDeviceToDevice, stream) != hipSuccess)
+    return set_error(OAL_ERR_HIP, "hipMemcpyAsync failed");
+  dst->tokens = src->tokens;
+  return OAL_OK;
+}
+
+size_t oal_state_bytes(const oal_state* s) { return s ? s->bytes : 0; }
+
+int64_t oal_state_tokens(const oal_state* s) { return s ? s->tokens : -1; }
+
+oal_status oal_state_export(const oal_state* s, float* dst, hipStream_t stream) {
+  if (!s || !dst) return set_error(OAL_ERR_INVALID_ARG, "null pointer argument");
+  return launch_export(s, dst, stream);
+}
+
+size_t oal_prefill_workspace_bytes(int batch, int n_q_heads, int n_kv_heads, int seq_len, int d_h,
+                                   int d_v, int chunk, oal_dtype in_dtype) {
+  if (check_heads(batch, n_q_heads, n_kv_heads, d_h, d_v) != OAL_OK) return 0;
+  if (seq_len < 0 || !valid_dtype(in_dtype)) return 0;
+  chunk = resolve_chunk(chunk);
+  if (chunk != 64 && chunk != 128 && chunk != 256) return 0;
+  if (seq_len == 0) return 0;
+  return prefill_vec_workspace(batch, n_kv_heads, seq_len, chunk);
+}
+
+oal_status oal_prefill(int batch, int n_q_heads, int n_kv_heads, int seq_len, int d_h, int d_v,
+                       oal_dtype in_dtype, const void* q, const void* k, const void* v,
+                       const void* coeffs, int chunk, oal_state* state, void* y,
+                       oal_dtype out_dtype, void* workspace, size_t workspace_bytes,
+                       hipStream_t stream) {
+  oal_status st = check_heads(batch, n_q_heads, n_kv_heads, d_h, d_v);
+  if (st != OAL_OK) return st;
+  if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype))
+    return set_error(OAL_ERR_INVALID_ARG, "unknown dtype");
+  if (seq_len < 0) return set_error(OAL_ERR_INVALID_ARG, "seq_len must be >= 0 (got %d)", seq_len);
+  chunk = resolve_chunk(chunk);
+  if (chunk != 64 && chunk != 128 && chunk != 256)
+    return set_error(OAL_ERR_INVALID_ARG, "chunk must be 0, 64, 128 or 256 (got %d)", chunk);
+  if (state && (state->batch != batch || state->n_kv_heads != n_kv_heads))
+    return set_error(OAL_ERR_INVALID_ARG, "state shape (%d, %d) does not match (%d, %d)",
+                     state->batch, state->n_kv_heads, batch, n_kv_heads);
+  if (!y && !state)
+    return set_error(OAL_ERR_INVALID_ARG, "y and state are both null: nothing to compute");
+  if (seq_len == 0) return OAL_OK;
+  if (!k || !v) return set_error(OAL_ERR_INVALID_ARG, "k and v must not be null");
+  if (y && (!q || !coeffs)) return set_error(OAL_ERR_INVALID_ARG, "q and coeffs must not be null");
+  if ((long long)seq_len * 64 * (long long)batch * n_q_heads > (1LL << 40))
+    return set_error(OAL_ERR_UNSUPPORTED, "problem too large");
+  if (y) {
+    size_t need = oal_prefill_workspace_bytes(batch, n_q_heads, n_kv_heads, seq_len, d_h, d_v, chunk,
+                                              in_dtype);
+    if (!workspace || workspace_bytes < need)
+      return set_error(OAL_ERR_INVALID_ARG, "workspace too small: need %zu bytes, got %zu", need,
+                       workspace ? workspace_bytes : (size_t)0);
+    if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+      return set_error(OAL_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  }
+  st = launch_prefill_vec(batch, n_q_heads, n_kv_heads, seq_len, in_dtype, q, k, v, coeffs, chunk,
+                          state ? state->data : nullptr, y, out_dtype, workspace, stream);
+  if (st == OAL_OK && state) state->tokens += seq_len;
+  return st;
+}
+
+oal_status oal_decode_step(int batch, int n_q_heads, int n_kv_heads, int d_h, int d_v,
+                           oal_dtype in_dtype, const void* q, const void* k, const void* v,
+                           const void* coeffs, oal_state* state, void* y, oal_dtype out_dtype,
+                           hipStream_t stream) {
+  oal_status st = check_heads(batch, n_q_heads, n_kv_heads, d_h, d_v);
+  if (st != OAL_OK) return st;
+  if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype))
+    return set_error(OAL_ERR_INVALID_ARG, "unknown dtype");
+  if (!q || !k || !v || !coeffs || !state || !y)
+    return set_error(OAL_ERR_INVALID_ARG, "null pointer argument");
+  if (state->batch != batch || state->n_kv_heads != n_kv_heads)
+    return set_error(OAL_ERR_INVALID_ARG, "state shape (%d, %d) does not match (%d, %d)",
+                     state->batch, state->n_kv_heads, batch, n_kv_heads);
+  st = launch_decode(batch, n_q_heads, n_kv_heads, in_dtype, q, k, v, coeffs, state->data, y,
+                     out_dtype, stream);
+  if (st == OAL_OK) state->tokens += 1;
+  return st;
+}
+
+}  // extern "C"

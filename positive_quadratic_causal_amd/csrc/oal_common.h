@@ -1,0 +1,98 @@
+// Internal definitions shared by the liboal HIP sources (not part of the ABI).
+//
+// Feature layout of the prefix state.  With u = [v; 1] (W = d_v + 1 = 65 columns)
+// the state of [OAL] Eq. 5 is  H = sum_j phi_k(k_j) u_j^T  where the key-side
+// feature vector phi_k has, in canonical packed order ([OAL] App. D, packed-
+// symmetric states):
+//   f = 0                 1                      (H0)
+//   f = 1 .. 64           k_r                    (H1_r)
+//   f = 65 + p            k_r k_t, p-th pair r <= t in row-major order (H2_rt)
+// and the readout of Eq. 6 is  u~ = phi_q(q)^T H  with
+//   phi_q = [a, b'_r q_r, c'_rt q_r q_t]   (b' = b / sqrt d_h, c' = m_rt C_rt / d_h,
+//   m_rt = 1 on the diagonal and 2 off it).
+// The persistent state stores H column-major: [unit][w = 0..64][f = 0..DS-1]
+// (fp32, DS = 2176 >= 2145, padding rows are zero), unit = b * n_kv_heads + kv.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <hip/hip_bf16.h>
+#include <stdint.h>
+
+#include "../../include/oal.h"
+
+namespace oal {
+
+constexpr int DH = 64;                  // query/key head dimension
+constexpr int DV = 64;                  // value head dimension
+constexpr int W = DV + 1;               // value channels + the all-ones channel
+constexpr int NPAIR = DH * (DH + 1) / 2;  // 2080 packed pairs r <= t
+constexpr int DCAN = 1 + DH + NPAIR;    // 2145 canonical feature rows
+constexpr int DS = 2176;                // padded row count of a state column
+constexpr int GMAX = 6;                 // largest supported group count
+constexpr int LDIM = GMAX + 1;          // leading dimension of L and M in coeffs
+constexpr size_t STATE_FLOATS = (size_t)W * DS;  // per (batch, kv head) unit
+
+// Packed pair table: entry p holds (r << 8) | t for the p-th pair r <= t.
+struct PairTable {
+  uint16_t rt[NPAIR];
+  constexpr PairTable() : rt() {
+    int p = 0;
+    for (int r = 0; r < DH; ++r)
+      for (int t = r; t < DH; ++t) rt[p++] = (uint16_t)((r << 8) | t);
+  }
+};
+
+// Index of pair (r, t), r <= t, in the packed order.
+__host__ __device__ constexpr inline int pair_index(int r, int t) {
+  return r * DH - r * (r - 1) / 2 + (t - r);
+}
+
+// ---- element access ------------------------------------------------------
+
+__device__ __forceinline__ float bf16_bits_to_float(uint16_t b) {
+  return __uint_as_float(((uint32_t)b) << 16);
+}
+
+// Round-to-nearest-even fp32 -> bf16 bits (inputs here are finite).
+__device__ __forceinline__ uint16_t float_to_bf16_bits(float x) {
+  uint32_t u = __float_as_uint(x);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+  static __device__ __forceinline__ float load(const float* p, size_t i) { return p[i]; }
+  static __device__ __forceinline__ void store(float* p, size_t i, float x) { p[i] = x; }
+};
+template <> struct Elem<uint16_t> {  // bf16 stored as raw bits
+  static __device__ __forceinline__ float load(const uint16_t* p, size_t i) {
+    return bf16_bits_to_float(p[i]);
+  }
+  static __device__ __forceinline__ void store(uint16_t* p, size_t i, float x) {
+    p[i] = float_to_bf16_bits(x);
+  }
+};
+
+// ---- coefficient record accessors ---------------------------------------
+
+__device__ __forceinline__ const float* coef_rec(const void* coeffs, int h) {
+  return reinterpret_cast<const float*>(coeffs) + (size_t)h * OAL_COEF_WORDS;
+}
+
+// ---- host-side launch helpers (defined in oal_api.cpp) ----------------------
+
+oal_status set_error(oal_status st, const char* fmt, ...);
+oal_status check_launch(const char* what);
+
+}  // namespace oal
+
+// Opaque state handle (definition shared by the host shim and kernels' launchers).
+struct oal_state {
+  int batch;
+  int n_kv_heads;
+  int device;
+  float* data;        // [batch * n_kv_heads][W][DS] fp32
+  size_t bytes;
+  int64_t tokens;     // tokens absorbed so far (host-side bookkeeping)
+};

@@ -1,0 +1,94 @@
+// Coefficient expansion: (L, g, eps) -> the dimension-wise coefficients of the
+// grouped positive kernel, [OAL] §4.3 ("Positive group-aware kernel"):
+//   M = L L^T,  a = eps + M_00,  b_r = 2 M_{0,g(r)},  C_rt = M_{g(r),g(t)}
+// together with the derived tables the kernels read (scaled by 1/sqrt d_h and
+// 1/d_h as in the readout of [OAL] Eq. 6, and the packed multiplicities of
+// App. D).  One workgroup per query head; the record layout is in oal.h.
+#include "oal_common.h"
+
+namespace oal {
+
+__global__ void __launch_bounds__(256)
+k_expand(int g_max, const int32_t* __restrict__ n_groups, const int32_t* __restrict__ group_map,
+         const float* __restrict__ Lin, float eps, float* __restrict__ coeffs) {
+  const int h = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int ld = g_max + 1;
+  __shared__ float sL[LDIM][LDIM];
+  __shared__ float sM[LDIM][LDIM];
+  __shared__ int sg[DH];
+  __shared__ int sG;
+  float* rec = coeffs + (size_t)h * OAL_COEF_WORDS;
+
+  if (tid == 0) {
+    int G = n_groups[h];
+    sG = G < 1 ? 1 : (G > g_max ? g_max : G);
+  }
+  __syncthreads();
+  const int G = sG;
+  if (tid < LDIM * LDIM) {
+    int u = tid / LDIM, v = tid % LDIM;
+    float x = 0.f;
+    if (u <= G && v <= G && v <= u) x = Lin[(size_t)h * ld * ld + u * ld + v];
+    sL[u][v] = x;
+  }
+  if (tid < DH) {
+    int gr = group_map[(size_t)h * DH + tid];
+    sg[tid] = gr < 1 ? 1 : (gr > G ? G : gr);
+  }
+  __syncthreads();
+  if (tid < LDIM * LDIM) {
+    int u = tid / LDIM, v = tid % LDIM;
+    double m = 0.0;
+    for (int p = 0; p < LDIM; ++p) m += (double)sL[u][p] * (double)sL[v][p];
+    sM[u][v] = (float)m;
+  }
+  __syncthreads();
+
+  // zero the whole record first so padding words are defined
+  for (int i = tid; i < OAL_COEF_WORDS; i += blockDim.x) rec[i] = 0.f;
+  __syncthreads();
+
+  const float inv_sqrt_d = 0.125f;   // 1 / sqrt(64)
+  const float inv_d = 1.0f / 64.0f;
+  if (tid == 0) {
+    rec[OAL_COEF_A] = eps + sM[0][0];
+    rec[OAL_COEF_EPS] = eps;
+    reinterpret_cast<int32_t*>(rec)[OAL_COEF_NG] = G;
+  }
+  if (tid < DH) {
+    const int gr = sg[tid];
+    rec[OAL_COEF_BP + tid] = 2.0f * sM[0][gr] * inv_sqrt_d;
+    reinterpret_cast<int32_t*>(rec)[OAL_COEF_GMAP + tid] = gr;
+    for (int p = 0; p < LDIM; ++p)
+      rec[OAL_COEF_ELL + p * DH + tid] = sL[gr][p] * inv_sqrt_d;
+    for (int gam = 0; gam < LDIM; ++gam)
+      rec[OAL_COEF_MG + gam * DH + tid] = (gam <= G ? sM[gam][gr] : 0.f) * inv_d;
+  }
+  if (tid < LDIM * LDIM) {
+    int u = tid / LDIM, v = tid % LDIM;
+    rec[OAL_COEF_M + tid] = sM[u][v];
+    rec[OAL_COEF_L + tid] = sL[u][v];
+  }
+  for (int i = tid; i < DH * DH; i += blockDim.x) {
+    int r = i / DH, t = i % DH;
+    rec[OAL_COEF_CM + i] = sM[sg[r]][sg[t]] * inv_d;
+  }
+  for (int r = 0; r < DH; ++r) {
+    // pairs (r, t), t >= r, occupy indices pair_index(r, r) .. + (63 - r)
+    for (int t = r + tid; t < DH; t += blockDim.x) {
+      float m = (r == t) ? 1.0f : 2.0f;
+      rec[OAL_COEF_CP + pair_index(r, t)] = m * sM[sg[r]][sg[t]] * inv_d;
+    }
+  }
+}
+
+oal_status launch_expand(int n_q_heads, int g_max, const int32_t* n_groups,
+                         const int32_t* group_map, const float* L, float eps, void* coeffs,
+                         hipStream_t stream) {
+  hipLaunchKernelGGL(k_expand, dim3(n_q_heads), dim3(256), 0, stream, g_max, n_groups,
+                     group_map, L, eps, reinterpret_cast<float*>(coeffs));
+  return check_launch("k_expand");
+}
+
+}  // namespace oal

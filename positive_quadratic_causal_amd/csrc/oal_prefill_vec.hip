@@ -1,0 +1,288 @@
+// Chunked causal prefill on the vector ALUs in fp32 (the fp32-input path).
+//
+// [OAL] Algorithm 1 evaluated chunk by chunk (the paper's backend uses 128-token
+// blocks, App. E).  For chunk c with tokens T_c:
+//   build   dH_c = sum_{j in T_c} phi_k(k_j) u_j^T              ([OAL] Eq. 5)
+//   scan    H_{<c} = H_init + sum_{c' < c} dH_{c'}               (exclusive prefix)
+//   readout u~_i = phi_q(q_i)^T H_{<c} + sum_{j in T_c, j <= i} kappa(q_i, k_j) u_j
+//           y_i = u~_{i,1:64} / u~_{i,65}                         ([OAL] Eq. 6, 7)
+// The intra-chunk kernel values use kappa = eps + sum_p t_p^2 with
+// t_p = L_0p + sum_r ell_p[r] q_r k_r, the expansion of ||L^T s_bar||^2 of Eq. 7.
+// Everything is fp32 with fp32 accumulation; this path favours simplicity over
+// speed (the bf16 inputs go through the matrix-core path).
+#include "oal_common.h"
+
+namespace oal {
+
+namespace {
+__constant__ PairTable c_vec_pairs = PairTable();
+constexpr int FB = 64;                 // feature rows per build block
+constexpr int NFB = DS / FB;           // 34 build blocks per unit
+constexpr int TB = 64;                 // tokens staged per step
+constexpr int WPT = (W + 3) / 4;       // 17 columns per thread in the build
+}  // namespace
+
+// dH over tokens [t0, t1) of one unit for feature rows [fb*64, fb*64+64).
+// mode 0: store into out (a per-chunk slot), mode 1: add into out (the state).
+template <typename T>
+__global__ void __launch_bounds__(256)
+k_build_vec(int n_kv_heads, int seq_len, int chunk, int n_chunks, const T* __restrict__ k,
+            const T* __restrict__ v, float* __restrict__ out, int mode) {
+  const int fb = blockIdx.x;
+  const int c = blockIdx.y;
+  const int unit = blockIdx.z;
+  const int tid = threadIdx.x;
+  const int f = fb * FB + (tid & 63);
+  const int wq = tid >> 6;
+  __shared__ float s_k[TB][DH + 1];
+  __shared__ float s_u[TB][W];
+
+  int r = 0, t = 0, kind;
+  if (f == 0) kind = 0;
+  else if (f <= DH) { kind = 1; r = f - 1; }
+  else if (f < DCAN) { kind = 2; uint16_t rt = c_vec_pairs.rt[f - 1 - DH]; r = rt >> 8; t = rt & 0xff; }
+  else kind = 3;
+
+  float acc[WPT];
+#pragma unroll
+  for (int j = 0; j < WPT; ++j) acc[j] = 0.f;
+
+  const int t0 = c * chunk;
+  const int t1 = min(seq_len, t0 + chunk);
+  const size_t base = (size_t)unit * seq_len;
+  for (int j0 = t0; j0 < t1; j0 += TB) {
+    const int nj = min(TB, t1 - j0);
+    __syncthreads();
+    for (int i = tid; i < TB * DH; i += blockDim.x) {
+      int jj = i / DH, d = i % DH;
+      float kv_ = 0.f, vv_ = 0.f;
+      if (jj < nj) {
+        kv_ = Elem<T>::load(k, (base + j0 + jj) * DH + d);
+        vv_ = Elem<T>::load(v, (base + j0 + jj) * DV + d);
+      }
+      s_k[jj][d] = kv_;
+      s_u[jj][d] = vv_;
+    }
+    for (int jj = tid; jj < TB; jj += blockDim.x) s_u[jj][DV] = jj < nj ? 1.f : 0.f;
+    __syncthreads();
+    for (int jj = 0; jj < nj; ++jj) {
+      float phi = kind == 0 ? 1.f : kind == 1 ? s_k[jj][r] : kind == 2 ? s_k[jj][r] * s_k[jj][t] : 0.f;
+#pragma unroll
+      for (int j = 0; j < WPT; ++j) {
+        int w = wq + 4 * j;
+        if (w < W) acc[j] = fmaf(phi, s_u[jj][w], acc[j]);
+      }
+    }
+  }
+  float* o = out + (mode == 0 ? ((size_t)unit * n_chunks + c) * STATE_FLOATS
+                              : (size_t)unit * STATE_FLOATS);
+#pragma unroll
+  for (int j = 0; j < WPT; ++j) {
+    int w = wq + 4 * j;
+    if (w < W) {
+      float* p = o + (size_t)w * DS + f;
+      if (mode == 0) *p = acc[j];
+      else *p += acc[j];
+    }
+  }
+}
+
+// In-place exclusive prefix over chunk slots; optional initial/final state.
+__global__ void __launch_bounds__(256)
+k_scan_vec(int n_chunks, float* __restrict__ ws, float* __restrict__ state) {
+  const int unit = blockIdx.y;
+  const size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= STATE_FLOATS) return;
+  float run = state ? state[(size_t)unit * STATE_FLOATS + e] : 0.f;
+  float* p = ws + (size_t)unit * n_chunks * STATE_FLOATS + e;
+  for (int c = 0; c < n_chunks; ++c) {
+    float x = p[(size_t)c * STATE_FLOATS];
+    p[(size_t)c * STATE_FLOATS] = run;
+    run += x;
+  }
+  if (state) state[(size_t)unit * STATE_FLOATS + e] = run;
+}
+
+// One block per (chunk, query head, batch); thread i owns token i of the chunk.
+template <typename T, typename O>
+__global__ void __launch_bounds__(256)
+k_readout_vec(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunks,
+              const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+              const void* __restrict__ coeffs, const float* __restrict__ ws, O* __restrict__ y) {
+  const int c = blockIdx.x;
+  const int hq = blockIdx.y;
+  const int b = blockIdx.z;
+  const int rep = n_q_heads / n_kv_heads;
+  const int kv = hq / rep;
+  const int unit = b * n_kv_heads + kv;
+  const int tid = threadIdx.x;
+  const int t0 = c * chunk;
+  const int clen = min(chunk, seq_len - t0);
+
+  extern __shared__ float smem[];
+  float* s_q = smem;                          // [chunk][DH + 1]
+  float* s_H = s_q + chunk * (DH + 1);        // [32][W]
+  float* s_cf = s_H + 32 * W;                 // [32]
+  float* s_k = s_cf + 32;                     // [TB][DH + 1]
+  float* s_u = s_k + TB * (DH + 1);           // [TB][W]
+  float* s_ell = s_u + TB * W;                // [LDIM][DH]
+  float* s_L0 = s_ell + LDIM * DH;            // [LDIM]
+
+  const float* rec = coef_rec(coeffs, hq);
+  const float a = rec[OAL_COEF_A];
+  const float eps = rec[OAL_COEF_EPS];
+  const int G = reinterpret_cast<const int32_t*>(rec)[OAL_COEF_NG];
+
+  for (int i = tid; i < chunk * DH; i += blockDim.x) {
+    int ii = i / DH, d = i % DH;
+    s_q[ii * (DH + 1) + d] =
+        ii < clen ? Elem<T>::load(q, (((size_t)b * n_q_heads + hq) * seq_len + t0 + ii) * DH + d) : 0.f;
+  }
+  for (int i = tid; i < LDIM * DH; i += blockDim.x) s_ell[i] = rec[OAL_COEF_ELL + i];
+  if (tid < LDIM) s_L0[tid] = rec[OAL_COEF_L + tid];   // row 0 of L: L_{0,p}
+  __syncthreads();
+
+  float acc[W];
+#pragma unroll
+  for (int w = 0; w < W; ++w) acc[w] = 0.f;
+  const bool active = tid < clen;
+  const float* qi = s_q + tid * (DH + 1);
+
+  // inter-chunk part: phi_q(q_i)^T H_{<c}
+  const float* Hc = ws + ((size_t)unit * n_chunks + c) * STATE_FLOATS;
+  for (int f0 = 0; f0 < DCAN; f0 += 32) {
+    __syncthreads();
+    for (int i = tid; i < 32 * W; i += blockDim.x) {
+      int w = i / 32, ff = i % 32;
+      s_H[ff * W + w] = (f0 + ff < DS) ? Hc[(size_t)w * DS + f0 + ff] : 0.f;
+    }
+    if (tid < 32) {
+      int f = f0 + tid;
+      float cf = 0.f;
+      if (f == 0) cf = a;
+      else if (f <= DH) cf = rec[OAL_COEF_BP + f - 1];
+      else if (f < DCAN) cf = rec[OAL_COEF_CP + f - 1 - DH];
+      s_cf[tid] = cf;
+    }
+    __syncthreads();
+    if (active) {
+      const int nf = min(32, DCAN - f0);
+      for (int ff = 0; ff < nf; ++ff) {
+        int f = f0 + ff;
+        float phi;
+        if (f == 0) phi = s_cf[ff];
+        else if (f <= DH) phi = s_cf[ff] * qi[f - 1];
+        else {
+          uint16_t rt = c_vec_pairs.rt[f - 1 - DH];
+          phi = s_cf[ff] * qi[rt >> 8] * qi[rt & 0xff];
+        }
+        const float* hrow = s_H + ff * W;
+#pragma unroll
+        for (int w = 0; w < W; ++w) acc[w] = fmaf(phi, hrow[w], acc[w]);
+      }
+    }
+  }
+
+  // intra-chunk part: direct kernel sum over j <= i inside the chunk
+  const size_t kbase = ((size_t)unit * seq_len + t0);
+  for (int j0 = 0; j0 < clen; j0 += TB) {
+    const int nj = min(TB, clen - j0);
+    __syncthreads();
+    for (int i = tid; i < TB * DH; i += blockDim.x) {
+      int jj = i / DH, d = i % DH;
+      float kv_ = 0.f, vv_ = 0.f;
+      if (jj < nj) {
+        kv_ = Elem<T>::load(k, (kbase + j0 + jj) * DH + d);
+        vv_ = Elem<T>::load(v, (kbase + j0 + jj) * DV + d);
+      }
+      s_k[jj * (DH + 1) + d] = kv_;
+      s_u[jj * W + d] = vv_;
+    }
+    for (int jj = tid; jj < TB; jj += blockDim.x) s_u[jj * W + DV] = 1.f;
+    __syncthreads();
+    if (active) {
+      const int jmax = min(nj, tid - j0 + 1);
+      for (int jj = 0; jj < jmax; ++jj) {
+        const float* kj = s_k + jj * (DH + 1);
+        float tp[LDIM];
+#pragma unroll
+        for (int p = 0; p < LDIM; ++p) tp[p] = s_L0[p];
+        for (int r = 0; r < DH; ++r) {
+          float x = qi[r] * kj[r];
+#pragma unroll
+          for (int p = 0; p < LDIM; ++p) tp[p] = fmaf(s_ell[p * DH + r], x, tp[p]);
+        }
+        float kap = eps;
+#pragma unroll
+        for (int p = 0; p < LDIM; ++p)
+          if (p <= G) kap = fmaf(tp[p], tp[p], kap);
+        const float* uj = s_u + jj * W;
+#pragma unroll
+        for (int w = 0; w < W; ++w) acc[w] = fmaf(kap, uj[w], acc[w]);
+      }
+    }
+  }
+
+  if (active) {
+    const float inv = 1.0f / acc[DV];
+    O* yo = y + (((size_t)b * n_q_heads + hq) * seq_len + t0 + tid) * DV;
+#pragma unroll
+    for (int w = 0; w < DV; ++w) Elem<O>::store(yo, w, acc[w] * inv);
+  }
+}
+
+template <typename T, typename O>
+static oal_status prefill_vec_typed(int batch, int n_q_heads, int n_kv_heads, int seq_len,
+                                    const void* q, const void* k, const void* v,
+                                    const void* coeffs, int chunk, float* state, void* y,
+                                    float* ws, hipStream_t stream) {
+  const int units = batch * n_kv_heads;
+  const T* kk = reinterpret_cast<const T*>(k);
+  const T* vv = reinterpret_cast<const T*>(v);
+  if (y == nullptr) {
+    // only advance the state: accumulate all tokens straight into it
+    hipLaunchKernelGGL(k_build_vec<T>, dim3(NFB, 1, units), dim3(256), 0, stream, n_kv_heads,
+                       seq_len, seq_len, 1, kk, vv, state, 1);
+    return check_launch("k_build_vec(state)");
+  }
+  const int n_chunks = (seq_len + chunk - 1) / chunk;
+  hipLaunchKernelGGL(k_build_vec<T>, dim3(NFB, n_chunks, units), dim3(256), 0, stream,
+                     n_kv_heads, seq_len, chunk, n_chunks, kk, vv, ws, 0);
+  oal_status st = check_launch("k_build_vec");
+  if (st != OAL_OK) return st;
+  hipLaunchKernelGGL(k_scan_vec, dim3((unsigned)((STATE_FLOATS + 255) / 256), units), dim3(256), 0,
+                     stream, n_chunks, ws, state);
+  st = check_launch("k_scan_vec");
+  if (st != OAL_OK) return st;
+  size_t smem = sizeof(float) * ((size_t)chunk * (DH + 1) + 32 * W + 32 + TB * (DH + 1) + TB * W +
+                                 LDIM * DH + LDIM);
+  if (hipFuncSetAttribute(reinterpret_cast<const void*>(&k_readout_vec<T, O>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem) != hipSuccess)
+    return set_error(OAL_ERR_HIP, "k_readout_vec: cannot reserve %zu bytes of LDS", smem);
+  hipLaunchKernelGGL((k_readout_vec<T, O>), dim3(n_chunks, n_q_heads, batch), dim3(chunk), smem,
+                     stream, n_q_heads, n_kv_heads, seq_len, chunk, n_chunks,
+                     reinterpret_cast<const T*>(q), kk, vv, coeffs, ws, reinterpret_cast<O*>(y));
+  return check_launch("k_readout_vec");
+}
+
+size_t prefill_vec_workspace(int batch, int n_kv_heads, int seq_len, int chunk) {
+  const size_t n_chunks = (size_t)((seq_len + chunk - 1) / chunk);
+  return (size_t)batch * n_kv_heads * n_chunks * STATE_FLOATS * sizeof(float);
+}
+
+oal_status launch_prefill_vec(int batch, int n_q_heads, int n_kv_heads, int seq_len,
+                              oal_dtype in_dtype, const void* q, const void* k, const void* v,
+                              const void* coeffs, int chunk, float* state, void* y,
+                              oal_dtype out_dtype, void* ws, hipStream_t stream) {
+  float* w = reinterpret_cast<float*>(ws);
+  if (in_dtype == OAL_F32) {
+    if (out_dtype == OAL_F32)
+      return prefill_vec_typed<float, float>(batch, n_q_heads, n_kv_heads, seq_len, q, k, v, coeffs, chunk, state, y, w, stream);
+    return prefill_vec_typed<float, uint16_t>(batch, n_q_heads, n_kv_heads, seq_len, q, k, v, coeffs, chunk, state, y, w, stream);
+  }
+  if (out_dtype == OAL_F32)
+    return prefill_vec_typed<uint16_t, float>(batch, n_q_heads, n_kv_heads, seq_len, q, k, v, coeffs, chunk, state, y, w, stream);
+  return prefill_vec_typed<uint16_t, uint16_t>(batch, n_q_heads, n_kv_heads, seq_len, q, k, v, coeffs, chunk, state, y, w, stream);
+}
+
+}  // namespace oal

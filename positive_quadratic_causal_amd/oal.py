@@ -1,0 +1,263 @@
+"""ctypes binding of liboal.so (the C ABI declared in include/oal.h).
+
+Argument marshalling only: every step of the computation runs in the library's
+HIP kernels.  Tensors are torch CUDA (HIP) tensors, which supply device memory;
+calls are enqueued on torch's current stream of the tensors' device.  Importing
+this module raises if liboal.so has not been built; there is no fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liboal.so")
+
+OAL_OK, OAL_ERR_INVALID_ARG, OAL_ERR_UNSUPPORTED, OAL_ERR_OUT_OF_MEMORY, OAL_ERR_HIP = range(5)
+OAL_F32, OAL_BF16 = 0, 1
+
+# coefficient record layout (words), mirrors include/oal.h
+COEF_A, COEF_EPS, COEF_NG = 0, 1, 2
+COEF_BP, COEF_GMAP, COEF_M, COEF_L = 16, 80, 144, 208
+COEF_ELL, COEF_CM, COEF_CP, COEF_MG = 272, 720, 4816, 6896
+COEF_WORDS = 7424
+
+D_H = 64
+D_V = 64
+D_CANON = 2145
+
+
+class OALError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{_status_name(status)}: {message}")
+        self.status = status
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it with positive_quadratic_causal_amd.build.build() "
+            "(hipcc --offload-arch=gfx950); there is no non-HIP fallback")
+    lib = ctypes.CDLL(LIB_PATH)
+    c_int, c_size, c_void, c_float = ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_float
+    sigs = {
+        "oal_coeffs_bytes": (c_size, [c_int, c_int, c_int]),
+        "oal_expand_coeffs": (c_int, [c_int, c_int, c_int, c_void, c_void, c_void, c_float,
+                                      c_void, c_void]),
+        "oal_state_alloc": (c_int, [c_int, c_int, c_int, c_int, ctypes.POINTER(c_void)]),
+        "oal_state_reset": (c_int, [c_void, c_void]),
+        "oal_state_free": (c_int, [c_void]),
+        "oal_state_copy": (c_int, [c_void, c_void, c_void]),
+        "oal_state_bytes": (c_size, [c_void]),
+        "oal_state_tokens": (ctypes.c_int64, [c_void]),
+        "oal_state_export": (c_int, [c_void, c_void, c_void]),
+        "oal_prefill_workspace_bytes": (c_size, [c_int, c_int, c_int, c_int, c_int, c_int,
+                                                 c_int, c_int]),
+        "oal_prefill": (c_int, [c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_void, c_void,
+                                c_void, c_void, c_int, c_void, c_void, c_int, c_void, c_size,
+                                c_void]),
+        "oal_decode_step": (c_int, [c_int, c_int, c_int, c_int, c_int, c_int, c_void, c_void,
+                                    c_void, c_void, c_void, c_void, c_int, c_void]),
+        "oal_status_string": (ctypes.c_char_p, [c_int]),
+        "oal_last_error": (ctypes.c_char_p, []),
+    }
+    for name, (res, args) in sigs.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+_lib = _load()
+
+EXPORTED = ("oal_coeffs_bytes", "oal_expand_coeffs", "oal_state_alloc", "oal_state_reset",
+            "oal_state_free", "oal_state_copy", "oal_state_bytes", "oal_state_tokens",
+            "oal_state_export", "oal_prefill_workspace_bytes", "oal_prefill",
+            "oal_decode_step", "oal_status_string", "oal_last_error")
+
+
+def _status_name(status: int) -> str:
+    return _lib.oal_status_string(status).decode()
+
+
+def _check(status: int) -> None:
+    if status != OAL_OK:
+        raise OALError(status, _lib.oal_last_error().decode())
+
+
+def _stream(t: torch.Tensor | None = None):
+    dev = t.device if t is not None and t.is_cuda else None
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _ptr(t: torch.Tensor | None):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensor must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return OAL_F32
+    if t.dtype == torch.bfloat16:
+        return OAL_BF16
+    raise ValueError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+
+
+# ---------------------------------------------------------------------------
+
+
+def oal_coeffs_bytes(n_q_heads: int, d_h: int = D_H, g_max: int = 6) -> int:
+    return int(_lib.oal_coeffs_bytes(n_q_heads, d_h, g_max))
+
+
+def oal_expand_coeffs(n_groups: torch.Tensor, group_map: torch.Tensor, L: torch.Tensor,
+                      eps: float, coeffs: torch.Tensor | None = None) -> torch.Tensor:
+    """n_groups int32 [Hq], group_map int32 [Hq, 64], L float32 [Hq, g+1, g+1].
+    Returns (or fills) the coefficient buffer as a float32 tensor [Hq, COEF_WORDS]."""
+    Hq = n_groups.shape[0]
+    g_max = L.shape[-1] - 1
+    if coeffs is None:
+        coeffs = torch.empty((Hq, COEF_WORDS), dtype=torch.float32, device=L.device)
+    if coeffs.numel() * 4 < oal_coeffs_bytes(Hq, D_H, g_max):
+        raise ValueError("coeffs buffer too small")
+    assert n_groups.dtype == torch.int32 and group_map.dtype == torch.int32
+    assert L.dtype == torch.float32
+    _check(_lib.oal_expand_coeffs(Hq, group_map.shape[-1], g_max, _ptr(n_groups), _ptr(group_map),
+                                  _ptr(L), float(eps), _ptr(coeffs), _stream(L)))
+    return coeffs
+
+
+class OalState:
+    """Owns an oal_state* (library-owned device memory)."""
+
+    def __init__(self, batch: int, n_kv_heads: int, d_h: int = D_H, d_v: int = D_V):
+        h = ctypes.c_void_p()
+        _check(_lib.oal_state_alloc(batch, n_kv_heads, d_h, d_v, ctypes.byref(h)))
+        self.handle = h
+        self.batch = batch
+        self.n_kv_heads = n_kv_heads
+
+    @property
+    def nbytes(self) -> int:
+        return int(_lib.oal_state_bytes(self.handle))
+
+    @property
+    def tokens(self) -> int:
+        return int(_lib.oal_state_tokens(self.handle))
+
+    def free(self) -> None:
+        if self.handle:
+            _check(_lib.oal_state_free(self.handle))
+            self.handle = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            if self.handle:
+                _lib.oal_state_free(self.handle)
+        except Exception:
+            pass
+
+
+def oal_state_alloc(batch: int, n_kv_heads: int, d_h: int = D_H, d_v: int = D_V) -> OalState:
+    return OalState(batch, n_kv_heads, d_h, d_v)
+
+
+def oal_state_reset(state: OalState) -> None:
+    _check(_lib.oal_state_reset(state.handle, _stream()))
+
+
+def oal_state_free(state: OalState) -> None:
+    state.free()
+
+
+def oal_state_copy(dst: OalState, src: OalState) -> None:
+    _check(_lib.oal_state_copy(dst.handle, src.handle, _stream()))
+
+
+def oal_state_export(state: OalState, out: torch.Tensor | None = None,
+                     device: str | torch.device = "cuda") -> torch.Tensor:
+    """Canonical packed state, float32 [B, Hkv, 2145, 65]."""
+    if out is None:
+        out = torch.empty((state.batch, state.n_kv_heads, D_CANON, D_V + 1), dtype=torch.float32,
+                          device=device)
+    _check(_lib.oal_state_export(state.handle, _ptr(out), _stream(out)))
+    return out
+
+
+def oal_prefill_workspace_bytes(batch: int, n_q_heads: int, n_kv_heads: int, seq_len: int,
+                                chunk: int = 0, in_dtype: int = OAL_BF16) -> int:
+    return int(_lib.oal_prefill_workspace_bytes(batch, n_q_heads, n_kv_heads, seq_len, D_H, D_V,
+                                                chunk, in_dtype))
+
+
+def alloc_workspace(nbytes: int, device="cuda") -> torch.Tensor | None:
+    """A device buffer of at least nbytes (torch's allocator aligns to 512 B)."""
+    if nbytes == 0:
+        return None
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def oal_prefill(q: torch.Tensor | None, k: torch.Tensor, v: torch.Tensor, coeffs: torch.Tensor | None,
+                chunk: int = 0, state: OalState | None = None, y: torch.Tensor | None = None,
+                workspace: torch.Tensor | None = None, want_output: bool = True) -> torch.Tensor | None:
+    """q [B, Hq, N, 64] (or None with want_output=False), k/v [B, Hkv, N, 64].
+    Returns y [B, Hq, N, 64] in q's dtype unless y is given or want_output is False."""
+    B, Hkv, N, dh = k.shape
+    dv = v.shape[-1]
+    if q is not None:
+        Hq = q.shape[1]
+    elif coeffs is not None:
+        Hq = coeffs.shape[0]
+    else:
+        Hq = Hkv
+    in_dt = _dtype_code(k)
+    if want_output and y is None:
+        y = torch.empty((B, Hq, N, dv), dtype=q.dtype, device=q.device)
+    out_dt = _dtype_code(y) if y is not None else OAL_F32
+    ws_bytes = 0
+    if y is not None:
+        ws_bytes = oal_prefill_workspace_bytes(B, Hq, Hkv, N, chunk, in_dt)
+        if workspace is None:
+            workspace = alloc_workspace(ws_bytes, k.device)
+    _check(_lib.oal_prefill(B, Hq, Hkv, N, dh, dv, in_dt, _ptr(q), _ptr(k), _ptr(v), _ptr(coeffs),
+                            chunk, state.handle if state is not None else None, _ptr(y), out_dt,
+                            _ptr(workspace) if workspace is not None else None,
+                            workspace.numel() if workspace is not None else 0, _stream(k)))
+    return y
+
+
+def oal_decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, coeffs: torch.Tensor,
+                    state: OalState, y: torch.Tensor | None = None) -> torch.Tensor:
+    """q [B, Hq, 64], k/v [B, Hkv, 64]; returns y [B, Hq, 64]."""
+    B, Hq, dh = q.shape
+    Hkv = k.shape[1]
+    dv = v.shape[-1]
+    if y is None:
+        y = torch.empty((B, Hq, dv), dtype=q.dtype, device=q.device)
+    _check(_lib.oal_decode_step(B, Hq, Hkv, dh, dv, _dtype_code(q), _ptr(q), _ptr(k), _ptr(v),
+                                _ptr(coeffs), state.handle, _ptr(y), _dtype_code(y), _stream(q)))
+    return y
+
+
+def oal_status_string(status: int) -> str:
+    return _status_name(status)
+
+
+def oal_last_error() -> str:
+    return _lib.oal_last_error().decode()
+
+
+def oal_state_bytes(state: OalState) -> int:
+    return state.nbytes
+
+
+def oal_state_tokens(state: OalState) -> int:
+    return state.tokens

@@ -1,0 +1,105 @@
+"""CPU checks of the C ABI: the library loads, exports every function that
+include/oal.h declares, and rejects invalid arguments on the host before any
+HIP call (no compute runs here: this host has no GPU)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+LIB = os.path.join(ROOT, "positive_quadratic_causal_amd", "liboal.so")
+HEADER = os.path.join(ROOT, "include", "oal.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="liboal.so not built")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"\b(oal_[a-z_]+)\s*\(", text)
+    return sorted(set(names))
+
+
+def test_header_declares_the_boundary():
+    names = _declared_functions()
+    for required in ("oal_expand_coeffs", "oal_prefill", "oal_decode_step", "oal_state_alloc"):
+        assert required in names
+
+
+def test_every_declared_symbol_is_exported():
+    lib = ctypes.CDLL(LIB)
+    missing = [n for n in _declared_functions() if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def test_binding_names_match_the_abi():
+    from positive_quadratic_causal_amd import oal
+    for n in _declared_functions():
+        assert hasattr(oal, n), n
+        assert n in oal.EXPORTED
+
+
+def _lib():
+    from positive_quadratic_causal_amd import oal
+    return oal._lib, oal
+
+
+def test_sizes():
+    lib, oal = _lib()
+    assert lib.oal_coeffs_bytes(14, 64, 6) == 14 * oal.COEF_WORDS * 4
+    assert lib.oal_coeffs_bytes(14, 32, 6) == 0
+    assert lib.oal_coeffs_bytes(14, 64, 7) == 0
+    assert lib.oal_prefill_workspace_bytes(1, 14, 2, 0, 64, 64, 128, oal.OAL_BF16) == 0
+    assert lib.oal_prefill_workspace_bytes(1, 14, 3, 100, 64, 64, 128, oal.OAL_BF16) == 0
+    assert lib.oal_prefill_workspace_bytes(1, 14, 2, 100, 64, 64, 100, oal.OAL_BF16) == 0
+    assert lib.oal_prefill_workspace_bytes(1, 14, 2, 100, 64, 64, 0, oal.OAL_BF16) > 0
+    assert lib.oal_state_bytes(None) == 0
+    assert lib.oal_state_tokens(None) == -1
+
+
+P = ctypes.c_void_p(0x1000)   # never dereferenced: validation fails first
+
+
+@pytest.mark.parametrize("args,expect", [
+    # batch, Hq, Hkv, N, d_h, d_v, in_dt, q, k, v, coeffs, chunk, state, y, out_dt, ws, wsb
+    ((0, 14, 2, 16, 64, 64, 1, P, P, P, P, 0, None, P, 1, P, 1 << 30), 1),
+    ((1, 14, 3, 16, 64, 64, 1, P, P, P, P, 0, None, P, 1, P, 1 << 30), 1),
+    ((1, 14, 2, 16, 32, 64, 1, P, P, P, P, 0, None, P, 1, P, 1 << 30), 2),
+    ((1, 14, 2, 16, 64, 64, 7, P, P, P, P, 0, None, P, 1, P, 1 << 30), 1),
+    ((1, 14, 2, 16, 64, 64, 1, P, P, P, P, 100, None, P, 1, P, 1 << 30), 1),
+    ((1, 14, 2, -1, 64, 64, 1, P, P, P, P, 0, None, P, 1, P, 1 << 30), 1),
+    ((1, 14, 2, 16, 64, 64, 1, P, P, P, P, 0, None, None, 1, P, 1 << 30), 1),  # nothing to do
+    ((1, 14, 2, 16, 64, 64, 1, None, P, P, P, 0, None, P, 1, P, 1 << 30), 1),  # q null
+    ((1, 14, 2, 16, 64, 64, 1, P, P, P, P, 0, None, P, 1, P, 10), 1),          # ws too small
+    ((1, 14, 2, 16, 64, 64, 1, P, P, P, P, 0, None, P, 1, None, 1 << 30), 1),  # ws null
+    ((1, 14, 2, 16, 64, 64, 1, P, P, P, P, 0, None, P, 1, ctypes.c_void_p(0x1010), 1 << 30), 1),
+])
+def test_prefill_rejects_invalid_arguments(args, expect):
+    lib, oal = _lib()
+    st = lib.oal_prefill(*args, None)
+    assert st == expect, lib.oal_last_error()
+    assert lib.oal_last_error()
+
+
+def test_prefill_empty_sequence_is_a_noop():
+    lib, oal = _lib()
+    assert lib.oal_prefill(1, 14, 2, 0, 64, 64, 1, P, P, P, P, 0, None, P, 1, None, 0, None) == 0
+
+
+def test_decode_and_expand_reject_invalid_arguments():
+    lib, oal = _lib()
+    assert lib.oal_decode_step(1, 14, 2, 64, 64, 1, P, P, P, P, None, P, 1, None) == 1
+    assert lib.oal_decode_step(1, 14, 4, 64, 64, 1, P, P, P, P, P, P, 1, None) == 1
+    assert lib.oal_decode_step(1, 14, 2, 48, 64, 1, P, P, P, P, P, P, 1, None) == 2
+    assert lib.oal_expand_coeffs(4, 64, 6, P, P, P, 0.0, P, None) == 1      # eps must be > 0
+    assert lib.oal_expand_coeffs(4, 64, 7, P, P, P, 1e-6, P, None) == 2     # g_max <= 6
+    assert lib.oal_expand_coeffs(4, 64, 6, None, P, P, 1e-6, P, None) == 1
+    assert lib.oal_state_alloc(1, 2, 64, 64, None) == 1
+    out = ctypes.c_void_p()
+    assert lib.oal_state_alloc(0, 2, 64, 64, ctypes.byref(out)) == 1
+    assert lib.oal_state_alloc(1, 2, 64, 32, ctypes.byref(out)) == 2
+    assert lib.oal_state_free(None) == 0
+    for s in range(5):
+        assert lib.oal_status_string(s).startswith(b"OAL_")

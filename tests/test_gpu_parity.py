@@ -1,0 +1,247 @@
+"""GPU parity of every C-ABI call against the float64 oracle.
+
+Inputs come from the seeded generator; the oracle consumes exactly the values
+the GPU consumed (bf16 values upcast to float64).  Metric: rel-L2 over the
+evaluated outputs, float64; bars 1e-4 (fp32 inputs) and 2e-2 (bf16 inputs with
+an fp32 state).  Every output is also checked to be finite."""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import oal_oracle as O
+from positive_quadratic_causal_amd import synth
+
+from gpu_util import Case, announce, rel_l2, tol_for
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def oal():
+    from positive_quadratic_causal_amd import oal as mod
+    return mod
+
+
+def _prefill(oal, case, chunk=128, state=None, y=True):
+    return oal.oal_prefill(case.q if y else None, case.k, case.v, case.coeffs(), chunk=chunk,
+                           state=state, want_output=y)
+
+
+def _check_heads(case, y_gpu, heads, tol):
+    y = y_gpu.float().cpu().numpy()
+    assert np.all(np.isfinite(y))
+    worst = 0.0
+    for b, h in heads:
+        ref = case.oracle_head(b, h)
+        err = rel_l2(y[b, h], ref)
+        worst = max(worst, err)
+        assert err <= tol, (b, h, err)
+    return worst
+
+
+# ---------------------------------------------------------------------------
+
+def test_expand_coeffs(oal):
+    announce("expand_coeffs: 12 heads, G = 1..6, random maps")
+    rng = np.random.default_rng(5)
+    Hq, g_max = 12, 6
+    n_groups = np.array([1 + (h % 6) for h in range(Hq)], dtype=np.int32)
+    gmap = np.ones((Hq, 64), dtype=np.int32)
+    L = np.zeros((Hq, 7, 7), dtype=np.float32)
+    for h in range(Hq):
+        G = n_groups[h]
+        gmap[h] = rng.permutation(np.concatenate([np.arange(1, G + 1),
+                                                  rng.integers(1, G + 1, 64 - G)]))
+        Lh = rng.normal(0, 0.5, size=(7, 7)).astype(np.float32)   # junk outside the block too
+        L[h] = Lh
+    dev = "cuda"
+    coeffs = oal.oal_expand_coeffs(torch.from_numpy(n_groups).to(dev), torch.from_numpy(gmap).to(dev),
+                                   torch.from_numpy(L).to(dev), 1e-3)
+    cf = coeffs.cpu().numpy()
+    pairs = O.packed_pairs(64)
+    r_ = np.array([p[0] for p in pairs]); t_ = np.array([p[1] for p in pairs])
+    for h in range(Hq):
+        G = int(n_groups[h])
+        Lh = L[h].astype(np.float64)[: G + 1, : G + 1]
+        a, b, C = O.expand_coeffs(Lh, gmap[h], G, 1e-3)
+        rec = cf[h]
+        np.testing.assert_allclose(rec[oal.COEF_A], a, rtol=1e-6)
+        assert rec[oal.COEF_NG:oal.COEF_NG + 1].view(np.int32)[0] == G
+        np.testing.assert_allclose(rec[oal.COEF_BP:oal.COEF_BP + 64], b / 8.0, rtol=1e-6, atol=1e-7)
+        np.testing.assert_allclose(rec[oal.COEF_CM:oal.COEF_CM + 4096].reshape(64, 64), C / 64.0,
+                                   rtol=1e-6, atol=1e-8)
+        mult = np.where(r_ == t_, 1.0, 2.0)
+        np.testing.assert_allclose(rec[oal.COEF_CP:oal.COEF_CP + 2080], mult * C[r_, t_] / 64.0,
+                                   rtol=1e-6, atol=1e-8)
+        Lt = np.tril(Lh)
+        M = Lt @ Lt.T
+        np.testing.assert_allclose(rec[oal.COEF_M:oal.COEF_M + 49].reshape(7, 7)[: G + 1, : G + 1], M,
+                                   rtol=1e-6, atol=1e-7)
+        ell = rec[oal.COEF_ELL:oal.COEF_ELL + 7 * 64].reshape(7, 64)
+        np.testing.assert_allclose(ell[: G + 1].T, Lt[gmap[h]] / 8.0, rtol=1e-6, atol=1e-8)
+        assert np.all(ell[G + 1:] == 0)
+        mg = rec[oal.COEF_MG:oal.COEF_MG + 7 * 64].reshape(7, 64)
+        np.testing.assert_allclose(mg[: G + 1], M[:, gmap[h]] / 64.0, rtol=1e-6, atol=1e-8)
+
+
+@pytest.mark.parametrize("chunk", [64, 128, 256])
+def test_prefill_tiny_fp32(oal, chunk):
+    w = synth.WORKLOADS[0]
+    announce(f"prefill tiny fp32 N=256 chunk={chunk}")
+    case = Case(w)
+    y = _prefill(oal, case, chunk)
+    torch.cuda.synchronize()
+    _check_heads(case, y, [(0, 0)], tol_for(w))
+
+
+def test_prefill_qwen_2048_all_heads(oal):
+    w = synth.WORKLOADS[1]
+    announce("prefill Qwen-shaped 14/2 N=2048 bf16 chunk=128, all heads")
+    case = Case(w)
+    y = _prefill(oal, case, 128)
+    torch.cuda.synchronize()
+    _check_heads(case, y, [(0, h) for h in range(w.n_q_heads)], tol_for(w))
+
+
+RAGGED = [(1, 64), (2, 64), (63, 64), (64, 64), (65, 64), (127, 128), (129, 128),
+          (200, 64), (300, 128), (257, 256), (511, 256)]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("n,chunk", RAGGED)
+def test_prefill_ragged(oal, n, chunk, dtype):
+    w = synth.small_workload(100 + n, "ragged", 2, 6, 2, n, dtype, grouping="llama")
+    announce(f"prefill ragged B=2 6/2 N={n} chunk={chunk} {dtype}")
+    case = Case(w)
+    y = _prefill(oal, case, chunk)
+    torch.cuda.synchronize()
+    _check_heads(case, y, [(b, h) for b in range(2) for h in range(6)], tol_for(w))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_prefill_continues_from_state(oal, dtype):
+    """prefill(N1) then prefill(N2) from the state == the last N2 outputs of
+    prefill(N1 + N2) (Algorithm 1 is one loop over all tokens)."""
+    n1, n2 = 190, 147
+    w = synth.small_workload(300, "continue", 1, 4, 2, n1 + n2, dtype)
+    announce(f"prefill continuation {n1}+{n2} {dtype}")
+    case = Case(w)
+    coeffs = case.coeffs()
+    st = oal.oal_state_alloc(1, 2)
+    y1 = oal.oal_prefill(case.q[:, :, :n1].contiguous(), case.k[:, :, :n1].contiguous(),
+                         case.v[:, :, :n1].contiguous(), coeffs, chunk=64, state=st)
+    y2 = oal.oal_prefill(case.q[:, :, n1:].contiguous(), case.k[:, :, n1:].contiguous(),
+                         case.v[:, :, n1:].contiguous(), coeffs, chunk=128, state=st)
+    torch.cuda.synchronize()
+    assert st.tokens == n1 + n2
+    y = torch.cat([y1, y2], dim=2).float().cpu().numpy()
+    for h in range(4):
+        ref = case.oracle_head(0, h)
+        assert rel_l2(y[0, h], ref) <= tol_for(w)
+        assert rel_l2(y[0, h, n1:], ref[n1:]) <= tol_for(w)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_state_export_matches_oracle_state(oal, dtype):
+    n = 150
+    w = synth.small_workload(301, "export", 2, 4, 2, n, dtype)
+    announce(f"state export B=2 Hkv=2 N={n} {dtype}")
+    case = Case(w)
+    st = oal.oal_state_alloc(2, 2)
+    oal.oal_prefill(None, case.k, case.v, None, chunk=128, state=st, want_output=False)
+    exp = oal.oal_state_export(st).cpu().numpy()
+    tol = 1e-5 if dtype == "f32" else 1e-3
+    for b in range(2):
+        for kv in range(2):
+            _, k, v = case.head_qkv(b, kv * 2, n)
+            ref = O.canonical_state(k, v)
+            assert rel_l2(exp[b, kv], ref) <= tol
+    # and the readout path writes the same state as the state-only path
+    st2 = oal.oal_state_alloc(2, 2)
+    _prefill(oal, case, 64, state=st2)
+    exp2 = oal.oal_state_export(st2).cpu().numpy()
+    assert rel_l2(exp2, exp) <= 1e-6
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_decode_after_prefill(oal, dtype):
+    n0, steps = 130, 9
+    w = synth.small_workload(302, "decode", 2, 8, 2, n0, dtype, decode_steps=steps)
+    announce(f"decode B=2 8/2 after N={n0}, {steps} steps {dtype}")
+    case = Case(w)
+    coeffs = case.coeffs()
+    st = oal.oal_state_alloc(2, 2)
+    oal.oal_prefill(case.q[:, :, :n0].contiguous(), case.k[:, :, :n0].contiguous(),
+                    case.v[:, :, :n0].contiguous(), coeffs, chunk=128, state=st)
+    outs = []
+    for s in range(steps):
+        t = n0 + s
+        outs.append(oal.oal_decode_step(case.q[:, :, t].contiguous(), case.k[:, :, t].contiguous(),
+                                        case.v[:, :, t].contiguous(), coeffs, st))
+    torch.cuda.synchronize()
+    assert st.tokens == n0 + steps
+    y = torch.stack(outs, dim=2).float().cpu().numpy()      # [B, Hq, steps, 64]
+    assert np.all(np.isfinite(y))
+    for b in range(2):
+        for h in range(8):
+            ref = case.oracle_rows(b, h, np.arange(n0, n0 + steps))
+            assert rel_l2(y[b, h], ref) <= tol_for(w), (b, h)
+
+
+def test_decode_from_empty_state(oal):
+    """The first decode step on a zero state returns v (one key: y_1 = v_1)."""
+    w = synth.small_workload(303, "decode0", 3, 4, 1, 0, "f32", decode_steps=1)
+    announce("decode from an empty state")
+    case = Case(w)
+    st = oal.oal_state_alloc(3, 1)
+    y = oal.oal_decode_step(case.q[:, :, 0].contiguous(), case.k[:, :, 0].contiguous(),
+                            case.v[:, :, 0].contiguous(), case.coeffs(), st)
+    torch.cuda.synchronize()
+    v = np.repeat(case.v[:, :, 0].cpu().numpy(), 4, axis=1)
+    # fp32 readout: numerator and denominator are separate 2145-term dot products
+    assert rel_l2(y.cpu().numpy(), v) <= tol_for(w)
+
+
+def test_prefill_chunk_invariance_and_determinism(oal):
+    w = synth.small_workload(304, "chunks", 1, 4, 2, 700, "bf16")
+    announce("chunk invariance N=700 bf16, chunks 64/128/256, repeated run")
+    case = Case(w)
+    ys = {c: _prefill(oal, case, c).float().cpu().numpy() for c in (64, 128, 256)}
+    again = _prefill(oal, case, 128).float().cpu().numpy()
+    assert np.array_equal(again, ys[128])
+    for c in (64, 256):
+        assert rel_l2(ys[c], ys[128]) <= 1e-2
+    ref = [case.oracle_head(0, h) for h in range(4)]
+    for c in ys:
+        for h in range(4):
+            assert rel_l2(ys[c][0, h], ref[h]) <= tol_for(w)
+
+
+def test_prefill_llama_4096_sampled_heads(oal):
+    w = synth.WORKLOADS[2]
+    announce("prefill Llama-shaped 32/8 B=4 N=4096 bf16 chunk=128, sampled heads")
+    case = Case(w)
+    y = _prefill(oal, case, 128)
+    torch.cuda.synchronize()
+    yc = y.float().cpu().numpy()
+    assert np.all(np.isfinite(yc))
+    rng = np.random.default_rng(2)
+    heads = [(int(rng.integers(4)), int(rng.integers(32))) for _ in range(5)] + [(3, 31), (0, 0)]
+    _check_heads(case, y, heads, tol_for(w))
+
+
+@pytest.mark.parametrize("chunk", [64, 128, 256])
+def test_prefill_long_32768_sampled_rows(oal, chunk):
+    w = synth.WORKLOADS[3]
+    announce(f"prefill Qwen-shaped 14/2 N=32768 bf16 chunk={chunk}, sampled rows")
+    case = Case(w)
+    y = _prefill(oal, case, chunk)
+    torch.cuda.synchronize()
+    yc = y.float().cpu().numpy()
+    assert np.all(np.isfinite(yc))
+    rng = np.random.default_rng(3)
+    rows = np.unique(np.concatenate([rng.integers(0, 32768, 40), [0, 1, 127, 128, 32767]]))
+    for h in (0, 6, 7, 13):
+        ref = case.oracle_rows(0, h, rows)
+        assert rel_l2(yc[0, h, rows], ref) <= tol_for(w), h
