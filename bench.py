@@ -1,0 +1,355 @@
+#!/usr/bin/env python3
+"""Benchmark of OAL causal attention on one MI355X.
+
+Headline (``value``): prefill tokens/s on the Qwen2.5-0.5B-shaped long-context
+workload (batch 1, 14 query / 2 KV heads, d_h = d_v = 64, N = 32768, G = 4 per
+head, bf16 inputs, fp32 state).  One step = coefficient expansion + state reset +
+one chunked prefill of all N tokens (outputs y and the final state).
+
+Also reported: batched decode (Llama-3.2-1B-shaped 32/8, batch 64, state
+prefilled from 8192 tokens, 256 single-token steps; ``decode``), a chunk-size
+sweep, the linear-time check against N = 2048, the roofline of the dominant
+kernel of each path (algorithmic flops or bytes per launch over the launch's
+average duration, from HIP events recorded on the launch stream inside the timed
+region), and the float64 CPU oracle timed on a bounded sample of the prefill
+workload (``cpu_baseline``).
+
+Inputs are synthetic (seeded generator in positive_quadratic_causal_amd.synth)
+and resident in HBM before the timed region starts.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "OAL causal attn tokens/s (prefill, decode) at 1 GPU; % MFMA/HBM roofline"
+
+D_CANON = 2145          # feature rows of one packed state: 1 + 64 + 64*65/2
+W = 65                  # value channels + the all-ones channel
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_F32_VECTOR_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0
+
+# kernel name -> (bound, peak, unit)
+KERNEL_BOUND = {
+    "k_readout_mfma": ("mfma", PEAK_BF16_TFLOPS, "TFLOP/s"),
+    "k_state_mfma": ("mfma", PEAK_BF16_TFLOPS, "TFLOP/s"),
+    "k_readout_vec": ("alu", PEAK_F32_VECTOR_TFLOPS, "TFLOP/s"),
+    "k_build_vec": ("alu", PEAK_F32_VECTOR_TFLOPS, "TFLOP/s"),
+    "k_scan_vec": ("hbm", PEAK_HBM_GBS, "GB/s"),
+    "k_decode": ("hbm", PEAK_HBM_GBS, "GB/s"),
+}
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def prefill_flops_per_token(n_q: int, n_kv: int, chunk: int) -> dict:
+    """Algorithmic (useful, unpadded) flops per token: state build 2*D*W per KV
+    head, inter-chunk readout 2*D*W per query head, intra-chunk causal triangle
+    (C+1)*(d_h + W) per query head (average (C+1)/2 keys, 2 flops per MAC)."""
+    build = 2 * D_CANON * W * n_kv
+    readout = 2 * D_CANON * W * n_q
+    intra = n_q * (chunk + 1) * (64 + W)
+    return {"build": build, "readout": readout, "intra": intra,
+            "total": build + readout + intra}
+
+
+def gen_inputs(w, st, device, kinds=("q", "k", "v"), t0=0, t1=None):
+    import torch
+
+    from positive_quadratic_causal_amd import synth
+    dt = torch.float32 if w.dtype == "f32" else torch.bfloat16
+    kind_id = {"q": synth.KIND_Q, "k": synth.KIND_K, "v": synth.KIND_V}
+    out = {}
+    for name in kinds:
+        arr = synth.full_tensor(w, st, kind_id[name], t0, t1)
+        out[name] = torch.from_numpy(arr).to(device=device, dtype=dt)
+        del arr
+    return out
+
+
+def kernel_times(oal, names):
+    res = {}
+    for n in names:
+        ms, cnt = oal.oal_profile_query(n)
+        if cnt:
+            res[n] = {"total_ms": ms, "launches": cnt, "avg_ms": ms / cnt}
+    return res
+
+
+ALL_KERNELS = ["k_expand", "k_fill_zero", "k_build_vec", "k_scan_vec", "k_readout_vec",
+               "k_state_mfma", "k_readout_mfma", "k_decode", "k_export"]
+
+
+def bench_prefill(oal, w, chunk, steps, warmup, device):
+    import torch
+
+    from positive_quadratic_causal_amd import synth
+    st = synth.structure(w)
+    x = gen_inputs(w, st, device, t1=w.seq_len)
+    ng = torch.from_numpy(st.n_groups).to(device)
+    gm = torch.from_numpy(st.group_map).to(device)
+    L = torch.from_numpy(st.L).to(device)
+    coeffs = oal.oal_expand_coeffs(ng, gm, L, w.eps)
+    state = oal.oal_state_alloc(w.batch, w.n_kv_heads)
+    y = torch.empty((w.batch, w.n_q_heads, w.seq_len, 64), dtype=x["q"].dtype, device=device)
+    ws = oal.alloc_workspace(oal.oal_prefill_workspace_bytes(w.batch, w.n_q_heads, w.n_kv_heads,
+                                                             w.seq_len, chunk, oal.OAL_BF16), device)
+
+    def step():
+        oal.oal_expand_coeffs(ng, gm, L, w.eps, coeffs)
+        oal.oal_state_reset(state)
+        oal.oal_prefill(x["q"], x["k"], x["v"], coeffs, chunk=chunk, state=state, y=y,
+                        workspace=ws)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    oal.oal_profile_reset()
+    oal.oal_profile_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    oal.oal_profile_enable(False)
+    kt = kernel_times(oal, ALL_KERNELS)
+    ms = (t1 - t0) * 1e3 / steps
+    del ws, y, x
+    state.free()
+    torch.cuda.empty_cache()
+    return ms, kt
+
+
+def roofline_prefill(kt, w, chunk):
+    """Roofline of the prefill's dominant kernel (largest total time)."""
+    prefill_kernels = {k: v for k, v in kt.items() if k not in ("k_expand", "k_fill_zero")}
+    name = max(prefill_kernels, key=lambda k: prefill_kernels[k]["total_ms"])
+    fl = prefill_flops_per_token(w.n_q_heads, w.n_kv_heads, chunk)
+    tokens = w.batch * w.seq_len
+    bound, peak, unit = KERNEL_BOUND.get(name, ("mfma", PEAK_BF16_TFLOPS, "TFLOP/s"))
+    avg_s = prefill_kernels[name]["avg_ms"] * 1e-3
+    if name.startswith("k_readout"):
+        work = tokens * (fl["readout"] + fl["intra"])
+    elif name in ("k_state_mfma", "k_build_vec"):
+        work = tokens * fl["build"]
+    else:   # scan: state slots read + written, fp32
+        n_chunks = -(-w.seq_len // chunk)
+        work = w.batch * w.n_kv_heads * n_chunks * D_CANON * W * 4 * 2
+    if unit == "TFLOP/s":
+        achieved = work / avg_s / 1e12
+    else:
+        achieved = work / avg_s / 1e9
+    return {"kernel": name, "bound": bound, "achieved": round(achieved, 3), "peak": peak,
+            "unit": unit, "frac": round(achieved / peak, 5), "traffic": None,
+            "work_per_launch": work, "avg_launch_ms": round(prefill_kernels[name]["avg_ms"], 5)}
+
+
+def bench_decode(oal, w, reps, n_steps, device):
+    import torch
+
+    from positive_quadratic_causal_amd import synth
+    st = synth.structure(w)
+    n0 = w.seq_len
+    log(f"decode: generating k/v for {w.batch}x{w.n_kv_heads} units x {n0 + n_steps} tokens")
+    kv = gen_inputs(w, st, device, kinds=("k", "v"), t1=n0 + n_steps)
+    qd = gen_inputs(w, st, device, kinds=("q",), t0=n0, t1=n0 + n_steps)["q"]
+    ng = torch.from_numpy(st.n_groups).to(device)
+    gm = torch.from_numpy(st.group_map).to(device)
+    L = torch.from_numpy(st.L).to(device)
+    coeffs = oal.oal_expand_coeffs(ng, gm, L, w.eps)
+    base = oal.oal_state_alloc(w.batch, w.n_kv_heads)
+    oal.oal_prefill(None, kv["k"][:, :, :n0].contiguous(), kv["v"][:, :, :n0].contiguous(), None,
+                    chunk=128, state=base, want_output=False)
+    state = oal.oal_state_alloc(w.batch, w.n_kv_heads)
+    steps_q = [qd[:, :, s].contiguous() for s in range(n_steps)]
+    steps_k = [kv["k"][:, :, n0 + s].contiguous() for s in range(n_steps)]
+    steps_v = [kv["v"][:, :, n0 + s].contiguous() for s in range(n_steps)]
+    del kv
+    y = torch.empty((w.batch, w.n_q_heads, 64), dtype=torch.bfloat16, device=device)
+
+    def rep_once():
+        for s in range(n_steps):
+            oal.oal_decode_step(steps_q[s], steps_k[s], steps_v[s], coeffs, state, y)
+
+    oal.oal_state_copy(state, base)
+    rep_once()      # warmup
+    torch.cuda.synchronize()
+    total = 0.0
+    oal.oal_profile_reset()
+    for _ in range(reps):
+        oal.oal_state_copy(state, base)
+        torch.cuda.synchronize()
+        oal.oal_profile_enable(True)
+        t0 = time.perf_counter()
+        rep_once()
+        torch.cuda.synchronize()
+        total += time.perf_counter() - t0
+        oal.oal_profile_enable(False)
+    kt = kernel_times(oal, ["k_decode"])
+    ms_step = total * 1e3 / (reps * n_steps)
+    units = w.batch * w.n_kv_heads
+    bytes_launch = (units * 2 * D_CANON * W * 4            # state read + write
+                    + 2 * (w.batch * w.n_q_heads * 64)     # q in (bf16)
+                    + 2 * 2 * (units * 64)                 # k, v in (bf16)
+                    + 2 * (w.batch * w.n_q_heads * 64))    # y out (bf16)
+    avg_s = kt["k_decode"]["avg_ms"] * 1e-3
+    achieved = bytes_launch / avg_s / 1e9
+    base.free()
+    state.free()
+    torch.cuda.empty_cache()
+    return {
+        "workload": w.name,
+        "value": round(w.batch / (ms_step * 1e-3), 1),
+        "unit": "tokens/s",
+        "ms_per_step": round(ms_step, 5),
+        "steps_timed": reps * n_steps,
+        "prefilled_tokens": n0,
+        "roofline": {"kernel": "k_decode", "bound": "hbm", "achieved": round(achieved, 2),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                     "traffic": None, "work_per_launch": bytes_launch,
+                     "avg_launch_ms": round(kt["k_decode"]["avg_ms"], 5)},
+    }
+
+
+def cpu_baseline(w, seconds):
+    """The float64 oracle on stratified row blocks of query head 0, scaled to the
+    whole workload (every query head, every row)."""
+    import numpy as np
+
+    from oracle import oal_oracle as O
+    from positive_quadratic_causal_amd import synth
+    try:
+        import threadpoolctl
+        info = threadpoolctl.threadpool_info()
+        threads = max([i.get("num_threads", 1) for i in info] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    st = synth.structure(w)
+    q = synth.head_tensor(w, st, synth.KIND_Q, 0, 0, w.seq_len).astype(np.float64)
+    k = synth.head_tensor(w, st, synth.KIND_K, 0, 0, w.seq_len).astype(np.float64)
+    v = synth.head_tensor(w, st, synth.KIND_V, 0, 0, w.seq_len).astype(np.float64)
+    blk = 256
+    n_blocks = -(-w.seq_len // blk)
+    # 16 strata of the sequence, visited in bit-reversed order so that any prefix
+    # of the visit order is spread over the whole sequence
+    n_strata = 16
+    width = max(1, n_blocks // n_strata)
+    order = [width // 2 + width * int(f"{i:04b}"[::-1], 2) for i in range(n_strata)]
+    order = [bi for bi in order if bi < n_blocks]
+    done, t_spent = 0, 0.0
+    for bi in order:
+        i0, i1 = bi * blk, min(w.seq_len, bi * blk + blk)
+        t0 = time.perf_counter()
+        O.causal_attention_rows(q[i0:i1], np.arange(i0, i1), k, v, st.L[0].astype(np.float64),
+                                st.group_map[0], int(st.n_groups[0]), w.eps)
+        t_spent += time.perf_counter() - t0
+        done += 1
+        if t_spent >= seconds:
+            break
+    # the sampled blocks are spread evenly over the sequence, so their mean cost
+    # is the mean cost of a block of the whole head
+    t_head = t_spent / done * n_blocks
+    t_all = t_head * w.n_q_heads * w.batch
+    return {"value": round(w.batch * w.seq_len / t_all, 3), "unit": "tokens/s", "cores": threads,
+            "kind": "oracle",
+            "sample": (f"{done} of {n_blocks} row blocks ({blk} rows each, evenly spread) of query "
+                       f"head 0 of the {w.name} workload, direct float64 sum, {t_spent:.1f} s; "
+                       f"scaled to all {w.n_q_heads} query heads x {w.seq_len} rows")}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--chunk", type=int, default=128)
+    ap.add_argument("--decode-steps", type=int, default=256)
+    ap.add_argument("--decode-reps", type=int, default=3)
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: every box here has a single MI355X and the "
+              "OAL path has no multi-GPU leg (each (batch, KV head) unit is independent; "
+              "see DESIGN.md for how it would shard).", file=sys.stderr)
+        return 2
+
+    import torch
+
+    from positive_quadratic_causal_amd import oal, synth
+    device = "cuda:0"
+    torch.cuda.set_device(0)
+
+    w3 = synth.WORKLOADS[3]
+    log(f"prefill: {w3.name}, chunk {args.chunk}, {args.warmup} warmup + {args.steps} steps")
+    ms, kt = bench_prefill(oal, w3, args.chunk, args.steps, args.warmup, device)
+    tokens = w3.batch * w3.seq_len
+    result = {
+        "metric": METRIC,
+        "value": round(tokens / (ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; outlier-structured q/k, N(0,1) v)",
+        "config": {"workload": w3.name, "batch": w3.batch, "n_q_heads": w3.n_q_heads,
+                   "n_kv_heads": w3.n_kv_heads, "seq_len": w3.seq_len, "d_h": 64, "d_v": 64,
+                   "groups_per_head": 4, "chunk": args.chunk, "state": "fp32",
+                   "parallelism": "single GPU"},
+        "roofline": roofline_prefill(kt, w3, args.chunk),
+        "kernels_ms": {k: round(v["avg_ms"], 5) for k, v in kt.items()},
+    }
+    fl = prefill_flops_per_token(w3.n_q_heads, w3.n_kv_heads, args.chunk)
+    result["prefill_end_to_end"] = {
+        "algorithmic_flops": fl["total"] * tokens,
+        "tflops": round(fl["total"] * tokens / (ms * 1e-3) / 1e12, 3),
+        "frac_bf16_peak": round(fl["total"] * tokens / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 5),
+    }
+    if not args.no_sweep:
+        sweep = {}
+        for c in (64, 128, 256):
+            if c == args.chunk:
+                sweep[str(c)] = round(ms, 5)
+                continue
+            log(f"prefill chunk sweep: chunk {c}")
+            msc, _ = bench_prefill(oal, w3, c, max(3, args.steps // 4), 2, device)
+            sweep[str(c)] = round(msc, 5)
+        result["chunk_sweep_ms"] = sweep
+        w1 = synth.WORKLOADS[1]
+        log("linear-time check: N = 2048")
+        ms1, _ = bench_prefill(oal, w1, args.chunk, args.steps, args.warmup, device)
+        result["linear_time_check"] = {"ms_n2048": round(ms1, 5), "ms_n32768": round(ms, 5),
+                                       "ratio": round(ms / ms1, 3), "ideal_ratio": 16.0}
+    if not args.no_decode:
+        log("decode: setting up")
+        result["decode"] = bench_decode(oal, synth.WORKLOADS[4], args.decode_reps,
+                                        args.decode_steps, device)
+    if not args.no_cpu_baseline:
+        log("cpu baseline: float64 oracle on a bounded sample")
+        result["cpu_baseline"] = cpu_baseline(w3, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -143,6 +143,16 @@ oal_status oal_decode_step(int batch, int n_q_heads, int n_kv_heads, int d_h, in
                            const void* coeffs, oal_state* state, void* y, oal_dtype out_dtype,
                            hipStream_t stream);
 
+/* Per-kernel timing (a tracing aid, off by default).  While enabled, the library
+ * records a pair of HIP events on the launch stream around every kernel it
+ * launches.  oal_profile_query waits for the pending events of the named kernel
+ * ("k_decode", "k_readout_vec", ...; NULL = all kernels) and returns their total
+ * duration and launch count since the last reset.  Host-global, not thread-safe
+ * against concurrent launches from several threads. */
+oal_status oal_profile_enable(int enable);
+oal_status oal_profile_reset(void);
+oal_status oal_profile_query(const char* kernel, double* total_ms, int64_t* launches);
+
 const char* oal_status_string(oal_status status);
 const char* oal_last_error(void);
 

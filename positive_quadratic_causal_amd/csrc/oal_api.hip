@@ -4,7 +4,11 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <map>
+#include <mutex>
 #include <new>
+#include <string>
+#include <vector>
 
 #include "oal_common.h"
 
@@ -25,6 +29,69 @@ oal_status check_launch(const char* what) {
   if (e != hipSuccess)
     return set_error(OAL_ERR_HIP, "%s: launch failed: %s", what, hipGetErrorString(e));
   return OAL_OK;
+}
+
+// ---- per-kernel event timing -------------------------------------------------
+
+namespace {
+struct ProfEntry {
+  std::string kernel;
+  hipEvent_t start, stop;
+};
+struct ProfTotals {
+  double ms = 0.0;
+  int64_t launches = 0;
+};
+std::mutex g_prof_mu;
+bool g_prof_on = false;
+std::vector<ProfEntry> g_prof_pending;
+std::vector<hipEvent_t> g_prof_pool;
+std::map<std::string, ProfTotals> g_prof_totals;
+
+hipEvent_t prof_event() {
+  if (!g_prof_pool.empty()) {
+    hipEvent_t e = g_prof_pool.back();
+    g_prof_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+// Resolve every pending entry (waits for its stop event).
+oal_status prof_drain() {
+  oal_status st = OAL_OK;
+  for (auto& p : g_prof_pending) {
+    float ms = 0.f;
+    if (hipEventSynchronize(p.stop) != hipSuccess ||
+        hipEventElapsedTime(&ms, p.start, p.stop) != hipSuccess)
+      st = set_error(OAL_ERR_HIP, "profiling events for %s failed", p.kernel.c_str());
+    ProfTotals& t = g_prof_totals[p.kernel];
+    t.ms += ms;
+    t.launches += 1;
+    g_prof_pool.push_back(p.start);
+    g_prof_pool.push_back(p.stop);
+  }
+  g_prof_pending.clear();
+  return st;
+}
+}  // namespace
+
+int prof_begin(const char* kernel, hipStream_t stream) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  if (!g_prof_on) return -1;
+  hipEvent_t a = prof_event(), b = prof_event();
+  if (!a || !b) return -1;
+  if (hipEventRecord(a, stream) != hipSuccess) return -1;
+  g_prof_pending.push_back(ProfEntry{kernel, a, b});
+  return (int)g_prof_pending.size() - 1;
+}
+
+void prof_end(int slot, hipStream_t stream) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  if (slot < 0 || slot >= (int)g_prof_pending.size()) return;
+  (void)hipEventRecord(g_prof_pending[slot].stop, stream);
 }
 
 // kernels' launchers (one per source file)
@@ -78,6 +145,36 @@ const char* oal_status_string(oal_status s) {
 }
 
 const char* oal_last_error(void) { return g_last_error; }
+
+oal_status oal_profile_enable(int enable) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  g_prof_on = enable != 0;
+  return OAL_OK;
+}
+
+oal_status oal_profile_reset(void) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  oal_status st = prof_drain();
+  g_prof_totals.clear();
+  return st;
+}
+
+oal_status oal_profile_query(const char* kernel, double* total_ms, int64_t* launches) {
+  if (!total_ms || !launches) return set_error(OAL_ERR_INVALID_ARG, "null output pointer");
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  oal_status st = prof_drain();
+  double ms = 0.0;
+  int64_t n = 0;
+  for (auto& kv : g_prof_totals) {
+    if (kernel == nullptr || kv.first == kernel) {
+      ms += kv.second.ms;
+      n += kv.second.launches;
+    }
+  }
+  *total_ms = ms;
+  *launches = n;
+  return st;
+}
 
 size_t oal_coeffs_bytes(int n_q_heads, int d_h, int g_max) {
   if (n_q_heads < 1 || d_h != DH || g_max < 1 || g_max > GMAX) return 0;

@@ -80,10 +80,23 @@ __device__ __forceinline__ const float* coef_rec(const void* coeffs, int h) {
   return reinterpret_cast<const float*>(coeffs) + (size_t)h * OAL_COEF_WORDS;
 }
 
-// ---- host-side launch helpers (defined in oal_api.cpp) ----------------------
+// ---- host-side launch helpers (defined in oal_api.hip) ----------------------
 
 oal_status set_error(oal_status st, const char* fmt, ...);
 oal_status check_launch(const char* what);
+
+// Optional per-kernel timing with HIP events recorded on the launch stream
+// (enabled through oal_profile_enable).  prof_begin returns -1 when disabled.
+int prof_begin(const char* kernel, hipStream_t stream);
+void prof_end(int slot, hipStream_t stream);
+struct ProfScope {
+  int slot;
+  hipStream_t stream;
+  ProfScope(const char* kernel, hipStream_t s) : slot(prof_begin(kernel, s)), stream(s) {}
+  ~ProfScope() {
+    if (slot >= 0) prof_end(slot, stream);
+  }
+};
 
 }  // namespace oal
 

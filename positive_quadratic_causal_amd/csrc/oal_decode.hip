@@ -159,6 +159,7 @@ static oal_status decode_typed(int batch, int n_q_heads, int n_kv_heads, const v
     const T* kk = reinterpret_cast<const T*>(k);
     const T* vv = reinterpret_cast<const T*>(v);
     O* yy = reinterpret_cast<O*>(y);
+    ProfScope ps("k_decode", stream);
     if (nh <= 1)
       hipLaunchKernelGGL((k_decode<T, O, 1>), dim3(units), dim3(256), 0, stream, n_q_heads,
                          n_kv_heads, head0, nh, update, qq, kk, vv, coeffs, state, yy);

@@ -86,6 +86,7 @@ k_expand(int g_max, const int32_t* __restrict__ n_groups, const int32_t* __restr
 oal_status launch_expand(int n_q_heads, int g_max, const int32_t* n_groups,
                          const int32_t* group_map, const float* L, float eps, void* coeffs,
                          hipStream_t stream) {
+  ProfScope ps("k_expand", stream);
   hipLaunchKernelGGL(k_expand, dim3(n_q_heads), dim3(256), 0, stream, g_max, n_groups,
                      group_map, L, eps, reinterpret_cast<float*>(coeffs));
   return check_launch("k_expand");

@@ -241,24 +241,33 @@ static oal_status prefill_vec_typed(int batch, int n_q_heads, int n_kv_heads, in
   const T* vv = reinterpret_cast<const T*>(v);
   if (y == nullptr) {
     // only advance the state: accumulate all tokens straight into it
+    ProfScope ps("k_build_vec", stream);
     hipLaunchKernelGGL(k_build_vec<T>, dim3(NFB, 1, units), dim3(256), 0, stream, n_kv_heads,
                        seq_len, seq_len, 1, kk, vv, state, 1);
     return check_launch("k_build_vec(state)");
   }
   const int n_chunks = (seq_len + chunk - 1) / chunk;
-  hipLaunchKernelGGL(k_build_vec<T>, dim3(NFB, n_chunks, units), dim3(256), 0, stream,
-                     n_kv_heads, seq_len, chunk, n_chunks, kk, vv, ws, 0);
-  oal_status st = check_launch("k_build_vec");
+  oal_status st;
+  {
+    ProfScope ps("k_build_vec", stream);
+    hipLaunchKernelGGL(k_build_vec<T>, dim3(NFB, n_chunks, units), dim3(256), 0, stream,
+                       n_kv_heads, seq_len, chunk, n_chunks, kk, vv, ws, 0);
+    st = check_launch("k_build_vec");
+  }
   if (st != OAL_OK) return st;
-  hipLaunchKernelGGL(k_scan_vec, dim3((unsigned)((STATE_FLOATS + 255) / 256), units), dim3(256), 0,
-                     stream, n_chunks, ws, state);
-  st = check_launch("k_scan_vec");
+  {
+    ProfScope ps("k_scan_vec", stream);
+    hipLaunchKernelGGL(k_scan_vec, dim3((unsigned)((STATE_FLOATS + 255) / 256), units), dim3(256),
+                       0, stream, n_chunks, ws, state);
+    st = check_launch("k_scan_vec");
+  }
   if (st != OAL_OK) return st;
   size_t smem = sizeof(float) * ((size_t)chunk * (DH + 1) + 32 * W + 32 + TB * (DH + 1) + TB * W +
                                  LDIM * DH + LDIM);
   if (hipFuncSetAttribute(reinterpret_cast<const void*>(&k_readout_vec<T, O>),
                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem) != hipSuccess)
     return set_error(OAL_ERR_HIP, "k_readout_vec: cannot reserve %zu bytes of LDS", smem);
+  ProfScope ps("k_readout_vec", stream);
   hipLaunchKernelGGL((k_readout_vec<T, O>), dim3(n_chunks, n_q_heads, batch), dim3(chunk), smem,
                      stream, n_q_heads, n_kv_heads, seq_len, chunk, n_chunks,
                      reinterpret_cast<const T*>(q), kk, vv, coeffs, ws, reinterpret_cast<O*>(y));

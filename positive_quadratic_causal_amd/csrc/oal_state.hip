@@ -36,6 +36,7 @@ oal_status launch_fill_zero(float* p, size_t n_floats, hipStream_t stream) {
   size_t blocks = (n4 + 255) / 256;
   if (blocks > 65536) blocks = 65536;
   if (blocks == 0) return OAL_OK;
+  ProfScope ps("k_fill_zero", stream);
   hipLaunchKernelGGL(k_fill_zero, dim3((unsigned)blocks), dim3(256), 0, stream,
                      reinterpret_cast<float4*>(p), n4);
   return check_launch("k_fill_zero");
@@ -44,6 +45,7 @@ oal_status launch_fill_zero(float* p, size_t n_floats, hipStream_t stream) {
 oal_status launch_export(const oal_state* st, float* dst, hipStream_t stream) {
   int units = st->batch * st->n_kv_heads;
   dim3 grid((DCAN + 31) / 32, units);
+  ProfScope ps("k_export", stream);
   hipLaunchKernelGGL(k_export, grid, dim3(256), 0, stream, st->data, dst);
   return check_launch("k_export");
 }

@@ -61,6 +61,10 @@ def _load() -> ctypes.CDLL:
                                 c_void]),
         "oal_decode_step": (c_int, [c_int, c_int, c_int, c_int, c_int, c_int, c_void, c_void,
                                     c_void, c_void, c_void, c_void, c_int, c_void]),
+        "oal_profile_enable": (c_int, [c_int]),
+        "oal_profile_reset": (c_int, []),
+        "oal_profile_query": (c_int, [ctypes.c_char_p, ctypes.POINTER(ctypes.c_double),
+                                      ctypes.POINTER(ctypes.c_int64)]),
         "oal_status_string": (ctypes.c_char_p, [c_int]),
         "oal_last_error": (ctypes.c_char_p, []),
     }
@@ -76,7 +80,8 @@ _lib = _load()
 EXPORTED = ("oal_coeffs_bytes", "oal_expand_coeffs", "oal_state_alloc", "oal_state_reset",
             "oal_state_free", "oal_state_copy", "oal_state_bytes", "oal_state_tokens",
             "oal_state_export", "oal_prefill_workspace_bytes", "oal_prefill",
-            "oal_decode_step", "oal_status_string", "oal_last_error")
+            "oal_decode_step", "oal_profile_enable", "oal_profile_reset", "oal_profile_query",
+            "oal_status_string", "oal_last_error")
 
 
 def _status_name(status: int) -> str:
@@ -261,3 +266,20 @@ def oal_state_bytes(state: OalState) -> int:
 
 def oal_state_tokens(state: OalState) -> int:
     return state.tokens
+
+
+def oal_profile_enable(enable: bool = True) -> None:
+    _check(_lib.oal_profile_enable(1 if enable else 0))
+
+
+def oal_profile_reset() -> None:
+    _check(_lib.oal_profile_reset())
+
+
+def oal_profile_query(kernel: str | None = None) -> tuple[float, int]:
+    """(total milliseconds, launches) of the named kernel since the last reset."""
+    ms = ctypes.c_double()
+    n = ctypes.c_int64()
+    _check(_lib.oal_profile_query(kernel.encode() if kernel else None, ctypes.byref(ms),
+                                  ctypes.byref(n)))
+    return ms.value, n.value
