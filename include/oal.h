@@ -66,6 +66,8 @@ typedef struct oal_state oal_state; /* opaque; device memory owned by the librar
 #define OAL_COEF_CP     4816  /* [2080] c'_rt = m_rt C_rt / d_h over pairs r <= t in   */
                               /* row-major order; m = 1 if r == t else 2               */
 #define OAL_COEF_MG     6896  /* [7][64] M_{gamma,g(t)} / d_h, gamma = 0..6            */
+#define OAL_COEF_GPACK  7344  /* [8]   uint32: g(r) packed 4 bits per r, r = 8 i .. 8 i + 7
+                                 in word i, low nibble first                          */
 #define OAL_COEF_WORDS  7424
 
 /* Bytes of the coefficient buffer for n_q_heads heads (d_h must be 64, g_max <= 6). */

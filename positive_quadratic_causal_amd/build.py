@@ -24,6 +24,7 @@ SOURCES = [
     "oal_state.hip",
     "oal_decode.hip",
     "oal_prefill_vec.hip",
+    "oal_prefill_mfma.hip",
 ]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
@@ -31,6 +32,7 @@ CFLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function", "-Wno-unknown-pragmas",
+    "-Rpass-analysis=kernel-resource-usage",
 ]
 
 

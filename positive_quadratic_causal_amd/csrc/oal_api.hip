@@ -104,6 +104,11 @@ oal_status launch_decode(int batch, int n_q_heads, int n_kv_heads, oal_dtype in_
                          const void* q, const void* k, const void* v, const void* coeffs,
                          float* state, void* y, oal_dtype out_dtype, hipStream_t stream);
 size_t prefill_vec_workspace(int batch, int n_kv_heads, int seq_len, int chunk);
+size_t prefill_mfma_workspace(int batch, int n_kv_heads, int seq_len, int chunk);
+oal_status launch_prefill_mfma(int batch, int n_q_heads, int n_kv_heads, int seq_len,
+                               const void* q, const void* k, const void* v, const void* coeffs,
+                               int chunk, float* state, void* y, oal_dtype out_dtype, void* ws,
+                               hipStream_t stream);
 oal_status launch_prefill_vec(int batch, int n_q_heads, int n_kv_heads, int seq_len,
                               oal_dtype in_dtype, const void* q, const void* k, const void* v,
                               const void* coeffs, int chunk, float* state, void* y,
@@ -267,6 +272,7 @@ size_t oal_prefill_workspace_bytes(int batch, int n_q_heads, int n_kv_heads, int
   chunk = resolve_chunk(chunk);
   if (chunk != 64 && chunk != 128 && chunk != 256) return 0;
   if (seq_len == 0) return 0;
+  if (in_dtype == OAL_BF16) return prefill_mfma_workspace(batch, n_kv_heads, seq_len, chunk);
   return prefill_vec_workspace(batch, n_kv_heads, seq_len, chunk);
 }
 
@@ -302,8 +308,12 @@ oal_status oal_prefill(int batch, int n_q_heads, int n_kv_heads, int seq_len, in
     if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
       return set_error(OAL_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
   }
-  st = launch_prefill_vec(batch, n_q_heads, n_kv_heads, seq_len, in_dtype, q, k, v, coeffs, chunk,
-                          state ? state->data : nullptr, y, out_dtype, workspace, stream);
+  if (in_dtype == OAL_BF16)
+    st = launch_prefill_mfma(batch, n_q_heads, n_kv_heads, seq_len, q, k, v, coeffs, chunk,
+                             state ? state->data : nullptr, y, out_dtype, workspace, stream);
+  else
+    st = launch_prefill_vec(batch, n_q_heads, n_kv_heads, seq_len, in_dtype, q, k, v, coeffs, chunk,
+                            state ? state->data : nullptr, y, out_dtype, workspace, stream);
   if (st == OAL_OK && state) state->tokens += seq_len;
   return st;
 }

@@ -65,6 +65,11 @@ k_expand(int g_max, const int32_t* __restrict__ n_groups, const int32_t* __restr
     for (int gam = 0; gam < LDIM; ++gam)
       rec[OAL_COEF_MG + gam * DH + tid] = (gam <= G ? sM[gam][gr] : 0.f) * inv_d;
   }
+  if (tid < DH / 8) {
+    uint32_t word = 0;
+    for (int i = 0; i < 8; ++i) word |= (uint32_t)sg[8 * tid + i] << (4 * i);
+    reinterpret_cast<uint32_t*>(rec)[OAL_COEF_GPACK + tid] = word;
+  }
   if (tid < LDIM * LDIM) {
     int u = tid / LDIM, v = tid % LDIM;
     rec[OAL_COEF_M + tid] = sM[u][v];

@@ -274,6 +274,17 @@ static oal_status prefill_vec_typed(int batch, int n_q_heads, int n_kv_heads, in
   return check_launch("k_readout_vec");
 }
 
+oal_status launch_build_vec_chunks(int batch, int n_kv_heads, int seq_len, int chunk,
+                                   const void* k, const void* v, float* dh, hipStream_t stream) {
+  const int units = batch * n_kv_heads;
+  const int n_chunks = (seq_len + chunk - 1) / chunk;
+  ProfScope ps("k_build_vec", stream);
+  hipLaunchKernelGGL(k_build_vec<uint16_t>, dim3(NFB, n_chunks, units), dim3(256), 0, stream,
+                     n_kv_heads, seq_len, chunk, n_chunks, reinterpret_cast<const uint16_t*>(k),
+                     reinterpret_cast<const uint16_t*>(v), dh, 0);
+  return check_launch("k_build_vec");
+}
+
 size_t prefill_vec_workspace(int batch, int n_kv_heads, int seq_len, int chunk) {
   const size_t n_chunks = (size_t)((seq_len + chunk - 1) / chunk);
   return (size_t)batch * n_kv_heads * n_chunks * STATE_FLOATS * sizeof(float);

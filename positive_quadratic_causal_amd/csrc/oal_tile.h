@@ -1,0 +1,98 @@
+// Tiled per-chunk prefix-state layout read by the matrix-core readout, and the
+// MFMA helpers shared by the matrix-core kernels (gfx950, wave64).
+//
+// The readout of [OAL] Eq. 6 is a contraction over feature rows f of the state:
+//   u~^T[w][i] = sum_f H[f][w] phi_q(q_i)[f]
+// evaluated on v_mfma_f32_32x32x16_bf16 with the state as the A operand (rows w)
+// and the query features as the B operand (columns = tokens).  The K dimension
+// (features) is cut into K-steps of 16 rows:
+//   K-steps 0..3         linear rows H1_r, r = 16 ks + j                (j = 0..15)
+//   K-steps 4..163       quadratic rows H2_rt for the item (r, c) with
+//                        t = 16 c + j, c = 0..3, r = 0..16 c + 15; items are
+//                        ordered by c, then r (K-step = 4 + 8 c (c + 1) + r).
+// In the diagonal 16-block (r / 16 == c) all ordered pairs are kept (so H2_rt and
+// H2_tr both appear, each read with multiplicity 1); off the diagonal only t > r
+// is stored and read with multiplicity 2 ([OAL] App. D: packed-symmetric states,
+// multiplicity one on the diagonal and two off it).  Every K-step has a single r,
+// so the query feature c_rt q_r q_t / d_h of a K-step is (m q_r) * qhat_{g(r)}[t]
+// with qhat_gamma[t] = q_t M_{gamma, g(t)} / d_h precomputed per 16-wide t-block.
+// Layout of one K-step: [w = 0..63][j = 0..15] bf16 (2 KB).
+//
+// The all-ones channel (denominator) is kept separately in fp32 "side" data:
+// H0 value channels, z1_r = sum k_r, z0 = token count, Z_rt = sum k_r k_t (full
+// 64 x 64); the denominator is a z0 + sum_r b'_r q_r z1_r + q^T (C/d_h o Z) q.
+#pragma once
+
+#include "oal_common.h"
+
+namespace oal {
+namespace tile {
+
+constexpr int NKS_LIN = 4;
+constexpr int NKS = 164;
+constexpr int KS_BYTES = 64 * 16 * 2;                  // one K-step, bf16
+constexpr size_t TILE_BYTES = (size_t)NKS * KS_BYTES;  // 335872
+constexpr int SIDE_H0 = 0;       // [64] sum v (value channels of H0)
+constexpr int SIDE_Z1 = 64;      // [64] sum k_r
+constexpr int SIDE_Z0 = 128;     // token count (then padding to 192)
+constexpr int SIDE_Z = 192;      // [64][64] sum k_r k_t
+constexpr int SIDE_FLOATS = SIDE_Z + DH * DH;           // 4288
+constexpr size_t BYTES = TILE_BYTES + (size_t)SIDE_FLOATS * 4;   // 353024 = 1379 * 256
+
+__host__ __device__ constexpr int quad_base(int c) { return NKS_LIN + 8 * c * (c + 1); }
+
+__host__ __device__ inline int ks_block(int ks) {   // c of a quadratic K-step
+  return ks >= quad_base(3) ? 3 : ks >= quad_base(2) ? 2 : ks >= quad_base(1) ? 1 : 0;
+}
+
+// Canonical state row (see oal_common.h) of element j of K-step ks.
+__host__ __device__ inline int canon_row(int ks, int j) {
+  if (ks < NKS_LIN) return 1 + 16 * ks + j;
+  const int c = ks_block(ks);
+  const int r = ks - quad_base(c);
+  const int t = 16 * c + j;
+  const int a = r < t ? r : t, b = r < t ? t : r;
+  return 1 + DH + pair_index(a, b);
+}
+
+// True when element j of K-step ks is the stored copy of a canonical row (the
+// diagonal blocks also hold the mirrored pairs t < r).
+__host__ __device__ inline bool canon_primary(int ks, int j) {
+  if (ks < NKS_LIN) return true;
+  const int c = ks_block(ks);
+  return ks - quad_base(c) <= 16 * c + j;
+}
+
+}  // namespace tile
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+
+// D = A B + C on a 32x32x16 tile.  Lane layout (wave64):
+//   A[i][k]: lane = i + 32 (k / 8), element k % 8
+//   B[k][j]: lane = j + 32 (k / 8), element k % 8
+//   D[i][j]: lane = j + 32 ((i / 4) % 2), register (i % 4) + 4 (i / 8)
+__device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Row of D held in register i by lane-half h.
+__device__ __forceinline__ int acc_row(int i, int h) { return 8 * (i >> 2) + 4 * h + (i & 3); }
+
+__device__ __forceinline__ f32x16 splat16(float x) {
+  f32x16 r;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) r[i] = x;
+  return r;
+}
+
+__device__ __forceinline__ bf16x8 pack8(const float* x) {
+  bf16x8 r;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r[i] = (__bf16)x[i];
+  return r;
+}
+
+__device__ __forceinline__ float bf(const __bf16 x) { return (float)x; }
+
+}  // namespace oal

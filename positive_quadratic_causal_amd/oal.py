@@ -22,7 +22,7 @@ OAL_F32, OAL_BF16 = 0, 1
 # coefficient record layout (words), mirrors include/oal.h
 COEF_A, COEF_EPS, COEF_NG = 0, 1, 2
 COEF_BP, COEF_GMAP, COEF_M, COEF_L = 16, 80, 144, 208
-COEF_ELL, COEF_CM, COEF_CP, COEF_MG = 272, 720, 4816, 6896
+COEF_ELL, COEF_CM, COEF_CP, COEF_MG, COEF_GPACK = 272, 720, 4816, 6896, 7344
 COEF_WORDS = 7424
 
 D_H = 64
