@@ -105,7 +105,8 @@ def bench_prefill(oal, w, chunk, steps, warmup, device):
     state = oal.oal_state_alloc(w.batch, w.n_kv_heads)
     y = torch.empty((w.batch, w.n_q_heads, w.seq_len, 64), dtype=x["q"].dtype, device=device)
     ws = oal.alloc_workspace(oal.oal_prefill_workspace_bytes(w.batch, w.n_q_heads, w.n_kv_heads,
-                                                             w.seq_len, chunk, oal.OAL_BF16), device)
+                                                             w.seq_len, chunk, oal.OAL_BF16, True),
+                             device)
 
     def step():
         oal.oal_expand_coeffs(ng, gm, L, w.eps, coeffs)

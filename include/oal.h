@@ -109,10 +109,14 @@ int64_t oal_state_tokens(const oal_state* state);
  * column 64 is the all-ones (denominator) channel. */
 oal_status oal_state_export(const oal_state* state, float* dst, hipStream_t stream);
 
-/* Device workspace oal_prefill needs for these sizes (per-chunk prefix states).
- * chunk = 0 selects the default (128).  Returns 0 for unsupported arguments. */
+/* Device workspace oal_prefill needs for these sizes: the per-chunk prefix states
+ * read by the readout (with_output != 0) and the scratch of the state builder.
+ * With with_output == 0 the size covers a call with y == NULL (state only).
+ * chunk = 0 selects the default (128).  Returns 0 when no workspace is needed or
+ * the arguments are unsupported. */
 size_t oal_prefill_workspace_bytes(int batch, int n_q_heads, int n_kv_heads, int seq_len,
-                                   int d_h, int d_v, int chunk, oal_dtype in_dtype);
+                                   int d_h, int d_v, int chunk, oal_dtype in_dtype,
+                                   int with_output);
 
 /* Causal prefill over seq_len tokens: [OAL] Algorithm 1 steps 6-12 evaluated in
  * chunks (the paper's backend works on 128-token blocks, [OAL] App. E).
@@ -125,8 +129,8 @@ size_t oal_prefill_workspace_bytes(int batch, int n_q_heads, int n_kv_heads, int
  *           tokens have been appended.
  *   y       [batch][n_q_heads][seq_len][d_v] in out_dtype, or NULL to only
  *           advance the state (then state must not be NULL).
- *   workspace  >= oal_prefill_workspace_bytes(...) bytes of device memory, 256-byte
- *           aligned; may be NULL when y is NULL.
+ *   workspace  >= oal_prefill_workspace_bytes(..., with_output = y != NULL) bytes of
+ *           device memory, 256-byte aligned; may be NULL when that size is 0.
  * seq_len == 0 is a valid no-op. */
 oal_status oal_prefill(int batch, int n_q_heads, int n_kv_heads, int seq_len, int d_h, int d_v,
                        oal_dtype in_dtype, const void* q, const void* k, const void* v,

@@ -25,6 +25,7 @@ SOURCES = [
     "oal_decode.hip",
     "oal_prefill_vec.hip",
     "oal_prefill_mfma.hip",
+    "oal_state_mfma.hip",
 ]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")

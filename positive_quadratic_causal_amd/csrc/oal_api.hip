@@ -104,7 +104,7 @@ oal_status launch_decode(int batch, int n_q_heads, int n_kv_heads, oal_dtype in_
                          const void* q, const void* k, const void* v, const void* coeffs,
                          float* state, void* y, oal_dtype out_dtype, hipStream_t stream);
 size_t prefill_vec_workspace(int batch, int n_kv_heads, int seq_len, int chunk);
-size_t prefill_mfma_workspace(int batch, int n_kv_heads, int seq_len, int chunk);
+size_t state_mfma_workspace(int batch, int n_kv_heads, int seq_len, int chunk, bool with_tiles);
 oal_status launch_prefill_mfma(int batch, int n_q_heads, int n_kv_heads, int seq_len,
                                const void* q, const void* k, const void* v, const void* coeffs,
                                int chunk, float* state, void* y, oal_dtype out_dtype, void* ws,
@@ -266,14 +266,14 @@ oal_status oal_state_export(const oal_state* s, float* dst, hipStream_t stream) 
 }
 
 size_t oal_prefill_workspace_bytes(int batch, int n_q_heads, int n_kv_heads, int seq_len, int d_h,
-                                   int d_v, int chunk, oal_dtype in_dtype) {
+                                   int d_v, int chunk, oal_dtype in_dtype, int with_output) {
   if (check_heads(batch, n_q_heads, n_kv_heads, d_h, d_v) != OAL_OK) return 0;
   if (seq_len < 0 || !valid_dtype(in_dtype)) return 0;
   chunk = resolve_chunk(chunk);
   if (chunk != 64 && chunk != 128 && chunk != 256) return 0;
   if (seq_len == 0) return 0;
-  if (in_dtype == OAL_BF16) return prefill_mfma_workspace(batch, n_kv_heads, seq_len, chunk);
-  return prefill_vec_workspace(batch, n_kv_heads, seq_len, chunk);
+  if (in_dtype == OAL_BF16) return state_mfma_workspace(batch, n_kv_heads, seq_len, chunk, with_output != 0);
+  return with_output ? prefill_vec_workspace(batch, n_kv_heads, seq_len, chunk) : 0;
 }
 
 oal_status oal_prefill(int batch, int n_q_heads, int n_kv_heads, int seq_len, int d_h, int d_v,
@@ -299,10 +299,10 @@ oal_status oal_prefill(int batch, int n_q_heads, int n_kv_heads, int seq_len, in
   if (y && (!q || !coeffs)) return set_error(OAL_ERR_INVALID_ARG, "q and coeffs must not be null");
   if ((long long)seq_len * 64 * (long long)batch * n_q_heads > (1LL << 40))
     return set_error(OAL_ERR_UNSUPPORTED, "problem too large");
-  if (y) {
-    size_t need = oal_prefill_workspace_bytes(batch, n_q_heads, n_kv_heads, seq_len, d_h, d_v, chunk,
-                                              in_dtype);
-    if (!workspace || workspace_bytes < need)
+  {
+    const size_t need = oal_prefill_workspace_bytes(batch, n_q_heads, n_kv_heads, seq_len, d_h, d_v,
+                                                    chunk, in_dtype, y != nullptr);
+    if (need > 0 && (!workspace || workspace_bytes < need))
       return set_error(OAL_ERR_INVALID_ARG, "workspace too small: need %zu bytes, got %zu", need,
                        workspace ? workspace_bytes : (size_t)0);
     if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)

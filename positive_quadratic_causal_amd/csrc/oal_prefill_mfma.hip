@@ -15,52 +15,6 @@
 namespace oal {
 
 // ---------------------------------------------------------------------------
-// Prefix scan of per-chunk fp32 deltas (canonical layout) into the tiled bf16
-// prefix states; also folds in the initial state and writes the final state.
-// One thread per element of the tiled layout, sequential over chunks.
-// ---------------------------------------------------------------------------
-__global__ void __launch_bounds__(256)
-k_scan_tile(int n_chunks, const float* __restrict__ dh, uint8_t* __restrict__ ts,
-            float* __restrict__ state) {
-  const int unit = blockIdx.y;
-  const int e = blockIdx.x * blockDim.x + threadIdx.x;
-  constexpr int NT = tile::NKS * 1024;
-  if (e >= NT + tile::SIDE_FLOATS) return;
-  int f = 0, w = 0;
-  bool primary = true, pad = false, is_tile = e < NT;
-  if (is_tile) {
-    const int ks = e >> 10, j = e & 15;
-    w = (e >> 4) & 63;
-    f = tile::canon_row(ks, j);
-    primary = tile::canon_primary(ks, j);
-  } else {
-    const int s = e - NT;
-    if (s < tile::SIDE_Z1) { f = 0; w = s; }
-    else if (s < tile::SIDE_Z0) { f = 1 + (s - tile::SIDE_Z1); w = DV; }
-    else if (s == tile::SIDE_Z0) { f = 0; w = DV; }
-    else if (s < tile::SIDE_Z) { pad = true; }
-    else {
-      const int rt = s - tile::SIDE_Z, r = rt >> 6, t = rt & 63;
-      f = 1 + DH + pair_index(r < t ? r : t, r < t ? t : r);
-      w = DV;
-      primary = r <= t;
-    }
-  }
-  const size_t off = (size_t)w * DS + f;
-  float run = (state && !pad) ? state[(size_t)unit * STATE_FLOATS + off] : 0.f;
-  for (int c = 0; c < n_chunks; ++c) {
-    uint8_t* slot = ts + ((size_t)unit * n_chunks + c) * tile::BYTES;
-    if (is_tile) {
-      reinterpret_cast<uint16_t*>(slot)[e] = float_to_bf16_bits(run);
-    } else {
-      reinterpret_cast<float*>(slot + tile::TILE_BYTES)[e - NT] = run;
-    }
-    if (!pad) run += dh[((size_t)unit * n_chunks + c) * STATE_FLOATS + off];
-  }
-  if (state && primary && !pad) state[(size_t)unit * STATE_FLOATS + off] = run;
-}
-
-// ---------------------------------------------------------------------------
 // Readout.  Workgroup = 4 waves = (256 / C) query heads of one KV group x C
 // tokens of one chunk; wave = one head x 64 tokens.  In the u~^T orientation
 // (rows = value channel w, columns = tokens) each wave owns a 64 x 64 tile of
@@ -466,18 +420,10 @@ k_readout_mfma(int n_q_heads, int n_kv_heads, int seq_len, int n_chunks, int n_h
 
 // ---------------------------------------------------------------------------
 
-size_t prefill_mfma_workspace(int batch, int n_kv_heads, int seq_len, int chunk) {
-  const size_t n_chunks = (size_t)((seq_len + chunk - 1) / chunk);
-  const size_t units = (size_t)batch * n_kv_heads;
-  return units * n_chunks * (STATE_FLOATS * sizeof(float) + tile::BYTES);
-}
-
-oal_status launch_prefill_vec(int batch, int n_q_heads, int n_kv_heads, int seq_len,
-                              oal_dtype in_dtype, const void* q, const void* k, const void* v,
-                              const void* coeffs, int chunk, float* state, void* y,
-                              oal_dtype out_dtype, void* ws, hipStream_t stream);
-oal_status launch_build_vec_chunks(int batch, int n_kv_heads, int seq_len, int chunk,
-                                   const void* k, const void* v, float* dh, hipStream_t stream);
+size_t state_mfma_workspace(int batch, int n_kv_heads, int seq_len, int chunk, bool with_tiles);
+oal_status launch_state_mfma(int batch, int n_kv_heads, int seq_len, int chunk, const void* k,
+                             const void* v, float* state, uint8_t* ts, void* ws,
+                             hipStream_t stream);
 
 template <int CH, typename O>
 static oal_status readout_launch(int batch, int n_q_heads, int n_kv_heads, int seq_len,
@@ -519,22 +465,16 @@ oal_status launch_prefill_mfma(int batch, int n_q_heads, int n_kv_heads, int seq
                                const void* q, const void* k, const void* v, const void* coeffs,
                                int chunk, float* state, void* y, oal_dtype out_dtype, void* ws,
                                hipStream_t stream) {
-  if (y == nullptr)   // state only: nothing to read out
-    return launch_prefill_vec(batch, n_q_heads, n_kv_heads, seq_len, OAL_BF16, q, k, v, coeffs,
-                              chunk, state, y, out_dtype, ws, stream);
   const int units = batch * n_kv_heads;
   const int n_chunks = (seq_len + chunk - 1) / chunk;
-  float* dh = reinterpret_cast<float*>(ws);
-  uint8_t* ts = reinterpret_cast<uint8_t*>(ws) + (size_t)units * n_chunks * STATE_FLOATS * sizeof(float);
-  oal_status st = launch_build_vec_chunks(batch, n_kv_heads, seq_len, chunk, k, v, dh, stream);
+  // workspace: the per-chunk prefix tiles (with output), then the builder's scratch
+  if (y == nullptr)   // state only: no per-chunk prefixes are needed
+    return launch_state_mfma(batch, n_kv_heads, seq_len, chunk, k, v, state, nullptr, ws, stream);
+  uint8_t* ts = reinterpret_cast<uint8_t*>(ws);
+  uint8_t* scratch = ts + (size_t)units * n_chunks * tile::BYTES;
+  oal_status st = launch_state_mfma(batch, n_kv_heads, seq_len, chunk, k, v, state, ts, scratch,
+                                    stream);
   if (st != OAL_OK) return st;
-  {
-    ProfScope ps("k_scan_tile", stream);
-    dim3 grid((tile::NKS * 1024 + tile::SIDE_FLOATS + 255) / 256, units);
-    hipLaunchKernelGGL(k_scan_tile, grid, dim3(256), 0, stream, n_chunks, dh, ts, state);
-    st = check_launch("k_scan_tile");
-    if (st != OAL_OK) return st;
-  }
   if (out_dtype == OAL_F32)
     return readout_dispatch<float>(chunk, batch, n_q_heads, n_kv_heads, seq_len, n_chunks, q, k, v,
                                    coeffs, ts, y, stream);

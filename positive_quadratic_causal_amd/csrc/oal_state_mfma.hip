@@ -1,0 +1,444 @@
+// Prefix states of the chunked prefill on the gfx950 matrix cores.
+//
+// [OAL] Eq. 5: H = sum_j phi_k(k_j) u_j^T with u_j = [v_j; 1] and
+// phi_k = [1, k_r, k_r k_t].  The readout of chunk c needs the exclusive prefix
+// H_{<c}; this kernel keeps the running prefix of a slice of feature rows in MFMA
+// accumulators (fp32) while it walks the chunks of a sequence segment, writes the
+// bf16 prefix tile of each chunk (layout in oal_tile.h) before adding the chunk,
+// and adds each 16-token step as  D[(r,t)][w] += sum_tok (k_r k_t)[tok] v[tok][w]
+// (A = key products, built on the vector ALUs; B = V, exact bf16).
+//
+// Work decomposition per (batch, KV head) unit and segment: 25 waves.
+//   waves 0..7  : quadratic rows (r, t), r in 4w .. 4w+3,        t in 0..31
+//   waves 8..23 : quadratic rows (r, t), r in 4(w-8) .. 4(w-8)+3, t in 32..63
+//   wave 24     : linear rows H1_r (A = K^T), the all-ones channel Z_rt = sum k_r k_t
+//                 (A = K^T, B = K), and H0 = sum v, z1 = sum k, z0 = count.
+// Each wave holds 4 x 2 accumulator tiles (128 rows x 64 channels).  Rows (r, t)
+// with t below r's 16-block are computed but never stored (the tiled layout keeps
+// their mirror images).  Waves 0..23 run identical code; wave 24 lives in a
+// workgroup of its own so that the two kinds of accumulators never share a loop.
+//
+// The running prefix is seeded from, and summed into, per-(unit, segment) buffers
+// in the raw accumulator layout; the small segment-scan kernel converts between
+// that layout and the canonical state (initial state in, final state out).
+// A batch-1 long sequence has too few units to fill 256 CUs, so the sequence is
+// cut into S segments:  pass 1 (sum mode) adds up every segment,  the scan forms
+// each segment's starting prefix (plus the caller's initial state) and the final
+// state,  pass 2 (prefix mode) replays each segment writing the per-chunk tiles.
+#include "oal_tile.h"
+
+namespace oal {
+
+namespace st {
+constexpr int NWAVES = 25;              // compute waves per (unit, segment)
+constexpr int WAVES_PER_WG = 4;
+constexpr int NWG = (NWAVES + WAVES_PER_WG - 1) / WAVES_PER_WG;   // 7 workgroups
+constexpr int SLOT_REGS = 132;          // registers per wave in the seg buffers
+constexpr int SLOT_FLOATS = SLOT_REGS * 64;
+constexpr int UNIT_SEG_FLOATS = NWAVES * SLOT_FLOATS;   // one (unit, segment)
+constexpr int TB = 64;                  // tokens staged per block
+constexpr int TS = TB + 8;              // bf16 row stride of the transposed tiles
+constexpr int REG_H0 = 128, REG_Z1 = 129, REG_Z0 = 130;
+}  // namespace st
+
+// Canonical location (row f, channel w) of accumulator register `reg` of `lane`
+// in wave `omega`.  valid: the element is a real state entry (quadratic rows
+// below r's 16-block are not); primary: it is the stored copy of the pair.
+__host__ __device__ inline void state_elem(int omega, int reg, int lane, int& f, int& w,
+                                           bool& valid, bool& primary) {
+  const int h = lane >> 5, col = lane & 31;
+  f = 0;
+  w = 0;
+  valid = true;
+  primary = true;
+  if (reg >= 128) {   // side values of wave 24
+    valid = omega == 24 && (reg != st::REG_Z0 || lane == 0) && reg <= st::REG_Z0;
+    if (reg == st::REG_H0) { f = 0; w = lane; }
+    else if (reg == st::REG_Z1) { f = 1 + lane; w = DV; }
+    else { f = 0; w = DV; }
+    return;
+  }
+  const int m = reg >> 5, nt = (reg >> 4) & 1, i = reg & 15;
+  const int row = 8 * (i >> 2) + 4 * h + (i & 3);
+  if (omega < 24) {
+    const int tb = omega < 8 ? 0 : 1;
+    const int r = (omega < 8 ? 4 * omega : 4 * (omega - 8)) + m;
+    const int t = 32 * tb + row;
+    w = 32 * nt + col;
+    valid = t >= 16 * (r >> 4);
+    primary = r <= t;
+    f = 1 + DH + pair_index(r < t ? r : t, r < t ? t : r);
+    return;
+  }
+  if (m < 2) {               // linear rows
+    f = 1 + 32 * m + row;
+    w = 32 * nt + col;
+    return;
+  }
+  const int r = 32 * (m - 2) + row, t = 32 * nt + col;   // Z_rt
+  f = 1 + DH + pair_index(r < t ? r : t, r < t ? t : r);
+  w = DV;
+  primary = r <= t;
+}
+
+namespace {
+
+// Stage one block of TB tokens: global (token-major) -> registers -> LDS
+// (dimension-major).  Used by both workgroup kinds.
+struct Stager {
+  const uint16_t* k;
+  const uint16_t* v;
+  size_t row0;
+  int tok_end;
+  uint4 pk[2], pv[2];
+  __device__ void fetch(int t0, int tid) {
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int piece = tid + 256 * e;            // 512 pieces = 64 tokens x 8
+      const int tok = piece >> 3, part = piece & 7;
+      const int gt = t0 + tok;
+      if (gt < tok_end) {
+        pk[e] = reinterpret_cast<const uint4*>(k + (row0 + gt) * DH)[part];
+        pv[e] = reinterpret_cast<const uint4*>(v + (row0 + gt) * DV)[part];
+      } else {
+        pk[e] = make_uint4(0, 0, 0, 0);
+        pv[e] = make_uint4(0, 0, 0, 0);
+      }
+    }
+  }
+  __device__ void deposit(__bf16 (*skt)[st::TS], __bf16 (*svt)[st::TS], int tid) {
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int piece = tid + 256 * e;
+      const int tok = piece >> 3, part = piece & 7;
+      const uint16_t* a = reinterpret_cast<const uint16_t*>(&pk[e]);
+      const uint16_t* b = reinterpret_cast<const uint16_t*>(&pv[e]);
+      uint16_t* dk = reinterpret_cast<uint16_t*>(&skt[0][0]);
+      uint16_t* dv = reinterpret_cast<uint16_t*>(&svt[0][0]);
+#pragma unroll
+      for (int x = 0; x < 8; ++x) {
+        dk[(part * 8 + x) * st::TS + tok] = a[x];
+        dv[(part * 8 + x) * st::TS + tok] = b[x];
+      }
+    }
+  }
+};
+
+__device__ __forceinline__ uint2 pack4_bf16(float a, float b, float c, float d) {
+  uint2 r;
+  r.x = (uint32_t)float_to_bf16_bits(a) | ((uint32_t)float_to_bf16_bits(b) << 16);
+  r.y = (uint32_t)float_to_bf16_bits(c) | ((uint32_t)float_to_bf16_bits(d) << 16);
+  return r;
+}
+
+}  // namespace
+
+template <int MODE>   // 0: segment sums, 1: per-chunk prefix tiles
+__global__ void __launch_bounds__(256, 2)
+k_state_mfma(int seq_len, int chunk, int n_chunks, int n_seg, int cps,
+             const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+             float* __restrict__ segbuf,          // MODE 0: out sums; MODE 1: in prefixes
+             uint8_t* __restrict__ ts) {          // MODE 1: per-chunk prefix tiles
+  __shared__ __attribute__((aligned(16))) __bf16 s_kt[2][DH][st::TS];
+  __shared__ __attribute__((aligned(16))) __bf16 s_vt[2][DV][st::TS];
+
+  const int g = blockIdx.x % st::NWG;
+  const int seg = (blockIdx.x / st::NWG) % n_seg;
+  const int unit = blockIdx.x / (st::NWG * n_seg);
+  const int tid = threadIdx.x;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, col = lane & 31, half = lane >> 5;
+  const int c0 = seg * cps;
+  const int c1 = min(n_chunks, c0 + cps);
+  const int tok_begin = c0 * chunk;
+  const int tok_end = min(seq_len, c1 * chunk);
+  const int n_blocks = (tok_end - tok_begin + st::TB - 1) / st::TB;
+  Stager sg{k, v, (size_t)unit * seq_len, tok_end, {}, {}};
+  float* segslot = segbuf + ((size_t)unit * n_seg + seg) * st::UNIT_SEG_FLOATS;
+
+  if (g < st::NWG - 1) {
+    // ===================== quadratic rows (waves 0..23) =====================
+    const int omega = g * st::WAVES_PER_WG + wv;
+    const int tb = omega < 8 ? 0 : 1;
+    const int r0 = omega < 8 ? 4 * omega : 4 * (omega - 8);
+    float* slot = segslot + (size_t)omega * st::SLOT_FLOATS;
+    f32x16 acc[4][2];
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          acc[m][nt][i] = MODE == 1 ? slot[(size_t)((m * 2 + nt) * 16 + i) * 64 + lane] : 0.f;
+    if (n_blocks > 0) sg.fetch(tok_begin, tid);
+    for (int bi = 0; bi < n_blocks; ++bi) {
+      const int t0 = tok_begin + bi * st::TB;
+      const int buf = bi & 1;
+      sg.deposit(s_kt[buf], s_vt[buf], tid);
+      if (MODE == 1 && (t0 % chunk) == 0) {
+        // the running prefix is chunk (t0 / chunk)'s exclusive prefix: store it
+        uint16_t* tl = reinterpret_cast<uint16_t*>(ts + ((size_t)unit * n_chunks + t0 / chunk) * tile::BYTES);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const int r = r0 + m;
+#pragma unroll
+          for (int nt = 0; nt < 2; ++nt) {
+            const int w = 32 * nt + col;
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq) {
+              const int t = 32 * tb + 8 * gq + 4 * half;   // rows t .. t+3
+              const int cblk = t >> 4;
+              if (cblk < (r >> 4)) continue;               // not in the tiled layout
+              const int ks = tile::quad_base(cblk) + r;
+              *reinterpret_cast<uint2*>(tl + (size_t)ks * 1024 + w * 16 + (t & 15)) =
+                  pack4_bf16(acc[m][nt][4 * gq], acc[m][nt][4 * gq + 1], acc[m][nt][4 * gq + 2],
+                             acc[m][nt][4 * gq + 3]);
+            }
+            asm volatile("" ::: "memory");   // keep the conversions next to their stores
+          }
+        }
+      }
+      __syncthreads();
+      if (bi + 1 < n_blocks) sg.fetch(t0 + st::TB, tid);
+#pragma unroll
+      for (int kk = 0; kk < st::TB / 16; ++kk) {
+        const int tk = 16 * kk + 8 * half;     // this lane's 8 tokens inside the block
+        bf16x8 bv[2];
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+          bv[nt] = *reinterpret_cast<const bf16x8*>(&s_vt[buf][32 * nt + col][tk]);
+        float kt8[8];
+        {
+          const bf16x8 x = *reinterpret_cast<const bf16x8*>(&s_kt[buf][32 * tb + col][tk]);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) kt8[j] = bf(x[j]);
+        }
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const bf16x8 x = *reinterpret_cast<const bf16x8*>(&s_kt[buf][r0 + m][tk]);   // k_r, broadcast
+          float p[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) p[j] = bf(x[j]) * kt8[j];
+          const bf16x8 af = pack8(p);
+#pragma unroll
+          for (int nt = 0; nt < 2; ++nt) acc[m][nt] = mfma32(af, bv[nt], acc[m][nt]);
+        }
+      }
+      __syncthreads();
+    }
+    if (MODE == 0) {
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) slot[(size_t)((m * 2 + nt) * 16 + i) * 64 + lane] = acc[m][nt][i];
+    }
+    return;
+  }
+
+  // ===================== linear rows and the all-ones channel (wave 24) ======
+  const bool worker = wv == 0;
+  float* slot = segslot + (size_t)24 * st::SLOT_FLOATS;
+  f32x16 acc[4][2];   // [0..1]: H1 rows 32m.., [2..3]: Z rows 32(m-2).., columns 32 nt..
+  float side_h0 = 0.f, side_z1 = 0.f, side_z0 = 0.f;
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        acc[m][nt][i] = (MODE == 1 && worker) ? slot[(size_t)((m * 2 + nt) * 16 + i) * 64 + lane] : 0.f;
+  if (MODE == 1 && worker) {
+    side_h0 = slot[(size_t)st::REG_H0 * 64 + lane];
+    side_z1 = slot[(size_t)st::REG_Z1 * 64 + lane];
+    side_z0 = slot[(size_t)st::REG_Z0 * 64];
+  }
+  if (n_blocks > 0) sg.fetch(tok_begin, tid);
+  for (int bi = 0; bi < n_blocks; ++bi) {
+    const int t0 = tok_begin + bi * st::TB;
+    const int buf = bi & 1;
+    sg.deposit(s_kt[buf], s_vt[buf], tid);
+    if (MODE == 1 && worker && (t0 % chunk) == 0) {
+      uint8_t* slotp = ts + ((size_t)unit * n_chunks + t0 / chunk) * tile::BYTES;
+      uint16_t* tl = reinterpret_cast<uint16_t*>(slotp);
+      float* side = reinterpret_cast<float*>(slotp + tile::TILE_BYTES);
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+          const int w = 32 * nt + col;
+#pragma unroll
+          for (int gq = 0; gq < 4; ++gq) {
+            const int r = 32 * m + 8 * gq + 4 * half;
+            *reinterpret_cast<uint2*>(tl + (size_t)(r >> 4) * 1024 + w * 16 + (r & 15)) =
+                pack4_bf16(acc[m][nt][4 * gq], acc[m][nt][4 * gq + 1], acc[m][nt][4 * gq + 2],
+                           acc[m][nt][4 * gq + 3]);
+          }
+          asm volatile("" ::: "memory");
+        }
+#pragma unroll
+      for (int m = 2; m < 4; ++m)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+          // rows r = 32 (m - 2) + 8 (i / 4) + 4 half + i % 4, column t = 32 nt + col
+          float* zb = side + tile::SIDE_Z + (32 * (m - 2) + 4 * half) * DH + 32 * nt + col;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) zb[(8 * (i >> 2) + (i & 3)) * DH] = acc[m][nt][i];
+          asm volatile("" ::: "memory");
+        }
+      side[tile::SIDE_H0 + lane] = side_h0;
+      side[tile::SIDE_Z1 + lane] = side_z1;
+      if (lane == 0) side[tile::SIDE_Z0] = side_z0;
+    }
+    __syncthreads();
+    if (bi + 1 < n_blocks) sg.fetch(t0 + st::TB, tid);
+    if (worker) {
+      // H0 = sum v, z1 = sum k, z0 = count over this block
+      float sh = 0.f, sz = 0.f;
+#pragma unroll 8
+      for (int x = 0; x < st::TB; ++x) {
+        sh += bf(s_vt[buf][lane][x]);
+        sz += bf(s_kt[buf][lane][x]);
+      }
+      side_h0 += sh;
+      side_z1 += sz;
+      side_z0 += (float)min(st::TB, tok_end - t0);
+#pragma unroll
+      for (int kk = 0; kk < st::TB / 16; ++kk) {
+        const int tk = 16 * kk + 8 * half;
+        bf16x8 ak[2], bv[2];
+#pragma unroll
+        for (int x = 0; x < 2; ++x) {
+          ak[x] = *reinterpret_cast<const bf16x8*>(&s_kt[buf][32 * x + col][tk]);
+          bv[x] = *reinterpret_cast<const bf16x8*>(&s_vt[buf][32 * x + col][tk]);
+        }
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+          for (int nt = 0; nt < 2; ++nt) {
+            acc[m][nt] = mfma32(ak[m], bv[nt], acc[m][nt]);         // H1 += K^T V
+            acc[2 + m][nt] = mfma32(ak[m], ak[nt], acc[2 + m][nt]); // Z  += K^T K
+          }
+      }
+    }
+    __syncthreads();
+  }
+  if (MODE == 0 && worker) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) slot[(size_t)((m * 2 + nt) * 16 + i) * 64 + lane] = acc[m][nt][i];
+    slot[(size_t)st::REG_H0 * 64 + lane] = side_h0;
+    slot[(size_t)st::REG_Z1 * 64 + lane] = side_z1;
+    slot[(size_t)st::REG_Z0 * 64 + lane] = lane == 0 ? side_z0 : 0.f;
+  }
+}
+
+// Exclusive prefix over segments (plus the initial state), in the accumulator
+// layout; optionally writes init + the total as the final state.
+__global__ void __launch_bounds__(256)
+k_state_segscan(int n_seg, float* __restrict__ segsum, float* __restrict__ segpre,
+                const float* __restrict__ state, int write_final) {
+  const int unit = blockIdx.y;
+  const int e = blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= st::UNIT_SEG_FLOATS) return;
+  const int omega = e / st::SLOT_FLOATS, reg = (e / 64) % st::SLOT_REGS, lane = e & 63;
+  int f = 0, w = 0;
+  bool valid, primary;
+  state_elem(omega, reg, lane, f, w, valid, primary);
+  float run = (state && valid) ? state[(size_t)unit * STATE_FLOATS + (size_t)w * DS + f] : 0.f;
+  for (int s = 0; s < n_seg; ++s) {
+    const size_t off = ((size_t)unit * n_seg + s) * st::UNIT_SEG_FLOATS + e;
+    if (segpre) segpre[off] = run;
+    if (segsum) run += segsum[off];
+  }
+  // the final value goes through segment 0's slot (no longer read): mirrored
+  // elements of other threads may still read the initial state here
+  if (write_final) segsum[(size_t)unit * n_seg * st::UNIT_SEG_FLOATS + e] = run;
+}
+
+// Final state (canonical layout) from the totals left in segment 0's slot.
+__global__ void __launch_bounds__(256)
+k_state_final(int n_seg, const float* __restrict__ segsum, float* __restrict__ state) {
+  const int unit = blockIdx.y;
+  const int e = blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= st::UNIT_SEG_FLOATS) return;
+  const int omega = e / st::SLOT_FLOATS, reg = (e / 64) % st::SLOT_REGS, lane = e & 63;
+  int f = 0, w = 0;
+  bool valid, primary;
+  state_elem(omega, reg, lane, f, w, valid, primary);
+  if (valid && primary)
+    state[(size_t)unit * STATE_FLOATS + (size_t)w * DS + f] =
+        segsum[(size_t)unit * n_seg * st::UNIT_SEG_FLOATS + e];
+}
+
+// ---------------------------------------------------------------------------
+
+static int choose_segments(int units, int n_chunks) {
+  // aim for >= ~2 workgroups per CU on 256 CUs
+  int s = (512 + units * st::NWG - 1) / (units * st::NWG);
+  if (s < 1) s = 1;
+  if (s > n_chunks) s = n_chunks;
+  return s;
+}
+
+size_t state_mfma_workspace(int batch, int n_kv_heads, int seq_len, int chunk, bool with_tiles) {
+  const int units = batch * n_kv_heads;
+  const int n_chunks = (seq_len + chunk - 1) / chunk;
+  const int n_seg = choose_segments(units, n_chunks);
+  const int cps = (n_chunks + n_seg - 1) / n_seg;
+  const int n_seg_eff = (n_chunks + cps - 1) / cps;
+  size_t bytes = (with_tiles ? 2 : 1) * (size_t)units * n_seg_eff * st::UNIT_SEG_FLOATS * sizeof(float);
+  if (with_tiles) bytes += (size_t)units * n_chunks * tile::BYTES;
+  return bytes;
+}
+
+// Builds the per-chunk prefix tiles (when ts != null) and the final state (when
+// state != null; its content on entry is the initial state).  ws: the scratch part
+// of state_mfma_workspace (segment sums, then segment prefixes).
+oal_status launch_state_mfma(int batch, int n_kv_heads, int seq_len, int chunk, const void* k,
+                             const void* v, float* state, uint8_t* ts, void* ws,
+                             hipStream_t stream) {
+  const int units = batch * n_kv_heads;
+  const int n_chunks = (seq_len + chunk - 1) / chunk;
+  const int n_seg = choose_segments(units, n_chunks);
+  const int cps = (n_chunks + n_seg - 1) / n_seg;
+  const int n_seg_eff = (n_chunks + cps - 1) / cps;
+  const uint16_t* kk = reinterpret_cast<const uint16_t*>(k);
+  const uint16_t* vv = reinterpret_cast<const uint16_t*>(v);
+  const dim3 grid(units * n_seg_eff * st::NWG);
+  float* segsum = reinterpret_cast<float*>(ws);
+  float* segpre = segsum + (size_t)units * n_seg_eff * st::UNIT_SEG_FLOATS;
+  {
+    ProfScope ps("k_state_seg", stream);
+    hipLaunchKernelGGL(k_state_mfma<0>, grid, dim3(256), 0, stream, seq_len, chunk, n_chunks,
+                       n_seg_eff, cps, kk, vv, segsum, (uint8_t*)nullptr);
+    oal_status s = check_launch("k_state_seg");
+    if (s != OAL_OK) return s;
+  }
+  {
+    ProfScope ps("k_state_segscan", stream);
+    hipLaunchKernelGGL(k_state_segscan, dim3((st::UNIT_SEG_FLOATS + 255) / 256, units), dim3(256),
+                       0, stream, n_seg_eff, segsum, ts ? segpre : (float*)nullptr,
+                       (const float*)state, state != nullptr ? 1 : 0);
+    oal_status s = check_launch("k_state_segscan");
+    if (s != OAL_OK) return s;
+  }
+  if (state != nullptr) {
+    ProfScope ps("k_state_final", stream);
+    hipLaunchKernelGGL(k_state_final, dim3((st::UNIT_SEG_FLOATS + 255) / 256, units), dim3(256), 0,
+                       stream, n_seg_eff, (const float*)segsum, state);
+    oal_status s = check_launch("k_state_final");
+    if (s != OAL_OK) return s;
+  }
+  if (ts == nullptr) return OAL_OK;
+  ProfScope ps("k_state_mfma", stream);
+  hipLaunchKernelGGL(k_state_mfma<1>, grid, dim3(256), 0, stream, seq_len, chunk, n_chunks,
+                     n_seg_eff, cps, kk, vv, segpre, ts);
+  return check_launch("k_state_mfma");
+}
+
+}  // namespace oal

@@ -55,7 +55,7 @@ def _load() -> ctypes.CDLL:
         "oal_state_tokens": (ctypes.c_int64, [c_void]),
         "oal_state_export": (c_int, [c_void, c_void, c_void]),
         "oal_prefill_workspace_bytes": (c_size, [c_int, c_int, c_int, c_int, c_int, c_int,
-                                                 c_int, c_int]),
+                                                 c_int, c_int, c_int]),
         "oal_prefill": (c_int, [c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_void, c_void,
                                 c_void, c_void, c_int, c_void, c_void, c_int, c_void, c_size,
                                 c_void]),
@@ -198,9 +198,10 @@ def oal_state_export(state: OalState, out: torch.Tensor | None = None,
 
 
 def oal_prefill_workspace_bytes(batch: int, n_q_heads: int, n_kv_heads: int, seq_len: int,
-                                chunk: int = 0, in_dtype: int = OAL_BF16) -> int:
+                                chunk: int = 0, in_dtype: int = OAL_BF16,
+                                with_output: bool = True) -> int:
     return int(_lib.oal_prefill_workspace_bytes(batch, n_q_heads, n_kv_heads, seq_len, D_H, D_V,
-                                                chunk, in_dtype))
+                                                chunk, in_dtype, 1 if with_output else 0))
 
 
 def alloc_workspace(nbytes: int, device="cuda") -> torch.Tensor | None:
@@ -227,11 +228,9 @@ def oal_prefill(q: torch.Tensor | None, k: torch.Tensor, v: torch.Tensor, coeffs
     if want_output and y is None:
         y = torch.empty((B, Hq, N, dv), dtype=q.dtype, device=q.device)
     out_dt = _dtype_code(y) if y is not None else OAL_F32
-    ws_bytes = 0
-    if y is not None:
-        ws_bytes = oal_prefill_workspace_bytes(B, Hq, Hkv, N, chunk, in_dt)
-        if workspace is None:
-            workspace = alloc_workspace(ws_bytes, k.device)
+    ws_bytes = oal_prefill_workspace_bytes(B, Hq, Hkv, N, chunk, in_dt, y is not None)
+    if workspace is None:
+        workspace = alloc_workspace(ws_bytes, k.device)
     _check(_lib.oal_prefill(B, Hq, Hkv, N, dh, dv, in_dt, _ptr(q), _ptr(k), _ptr(v), _ptr(coeffs),
                             chunk, state.handle if state is not None else None, _ptr(y), out_dt,
                             _ptr(workspace) if workspace is not None else None,

@@ -51,10 +51,17 @@ def test_sizes():
     assert lib.oal_coeffs_bytes(14, 64, 6) == 14 * oal.COEF_WORDS * 4
     assert lib.oal_coeffs_bytes(14, 32, 6) == 0
     assert lib.oal_coeffs_bytes(14, 64, 7) == 0
-    assert lib.oal_prefill_workspace_bytes(1, 14, 2, 0, 64, 64, 128, oal.OAL_BF16) == 0
-    assert lib.oal_prefill_workspace_bytes(1, 14, 3, 100, 64, 64, 128, oal.OAL_BF16) == 0
-    assert lib.oal_prefill_workspace_bytes(1, 14, 2, 100, 64, 64, 100, oal.OAL_BF16) == 0
-    assert lib.oal_prefill_workspace_bytes(1, 14, 2, 100, 64, 64, 0, oal.OAL_BF16) > 0
+    assert lib.oal_prefill_workspace_bytes(1, 14, 2, 0, 64, 64, 128, oal.OAL_BF16, 1) == 0
+    assert lib.oal_prefill_workspace_bytes(1, 14, 3, 100, 64, 64, 128, oal.OAL_BF16, 1) == 0
+    assert lib.oal_prefill_workspace_bytes(1, 14, 2, 100, 64, 64, 100, oal.OAL_BF16, 1) == 0
+    assert lib.oal_prefill_workspace_bytes(1, 14, 2, 100, 64, 64, 0, oal.OAL_BF16, 1) > 0
+    assert lib.oal_prefill_workspace_bytes(1, 14, 2, 100, 64, 64, 0, oal.OAL_F32, 1) > 0
+    assert lib.oal_prefill_workspace_bytes(1, 14, 2, 100, 64, 64, 0, oal.OAL_F32, 0) == 0
+    # state only: scratch for the segment sums, far less than the per-chunk tiles
+    so = lib.oal_prefill_workspace_bytes(64, 32, 8, 8192, 64, 64, 128, oal.OAL_BF16, 0)
+    wo = lib.oal_prefill_workspace_bytes(64, 32, 8, 8192, 64, 64, 128, oal.OAL_BF16, 1)
+    assert 0 < so < wo / 10
+    assert lib.oal_prefill_workspace_bytes(1, 14, 2, 32768, 64, 64, 128, oal.OAL_BF16, 0) > 0
     assert lib.oal_state_bytes(None) == 0
     assert lib.oal_state_tokens(None) == -1
 

@@ -151,7 +151,10 @@ def test_state_export_matches_oracle_state(oal, dtype):
     st = oal.oal_state_alloc(2, 2)
     oal.oal_prefill(None, case.k, case.v, None, chunk=128, state=st, want_output=False)
     exp = oal.oal_state_export(st).cpu().numpy()
-    tol = 1e-5 if dtype == "f32" else 1e-3
+    # bf16 inputs: the matrix-core build rounds each key feature k_r k_t to bf16
+    # (unit roundoff 2^-9, about 1.1e-3 RMS relative per product), so the fp32
+    # state carries ~1e-3 relative error; the bar is 2^-8.
+    tol = 1e-5 if dtype == "f32" else 2.0 ** -8
     for b in range(2):
         for kv in range(2):
             _, k, v = case.head_qkv(b, kv * 2, n)
@@ -161,7 +164,7 @@ def test_state_export_matches_oracle_state(oal, dtype):
     st2 = oal.oal_state_alloc(2, 2)
     _prefill(oal, case, 64, state=st2)
     exp2 = oal.oal_state_export(st2).cpu().numpy()
-    assert rel_l2(exp2, exp) <= 1e-6
+    assert rel_l2(exp2, exp) <= (1e-6 if dtype == "f32" else 1e-5)
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
