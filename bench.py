@@ -283,6 +283,8 @@ def main() -> int:
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--only", choices=["prefill", "decode"], default=None,
+                    help="time one leg only (used to profile each workload on its own)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -298,6 +300,10 @@ def main() -> int:
     torch.cuda.set_device(0)
 
     w3 = synth.WORKLOADS[3]
+    if args.only == "decode":
+        res = bench_decode(oal, synth.WORKLOADS[4], args.decode_reps, args.decode_steps, device)
+        print(json.dumps({"metric": METRIC, "decode": res}), flush=True)
+        return 0
     log(f"prefill: {w3.name}, chunk {args.chunk}, {args.warmup} warmup + {args.steps} steps")
     ms, kt = bench_prefill(oal, w3, args.chunk, args.steps, args.warmup, device)
     tokens = w3.batch * w3.seq_len
@@ -327,7 +333,7 @@ def main() -> int:
         "tflops": round(fl["total"] * tokens / (ms * 1e-3) / 1e12, 3),
         "frac_bf16_peak": round(fl["total"] * tokens / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 5),
     }
-    if not args.no_sweep:
+    if not args.no_sweep and args.only is None:
         sweep = {}
         for c in (64, 128, 256):
             if c == args.chunk:
@@ -342,7 +348,7 @@ def main() -> int:
         ms1, _ = bench_prefill(oal, w1, args.chunk, args.steps, args.warmup, device)
         result["linear_time_check"] = {"ms_n2048": round(ms1, 5), "ms_n32768": round(ms, 5),
                                        "ratio": round(ms / ms1, 3), "ideal_ratio": 16.0}
-    if not args.no_decode:
+    if not args.no_decode and args.only is None:
         log("decode: setting up")
         result["decode"] = bench_decode(oal, synth.WORKLOADS[4], args.decode_reps,
                                         args.decode_steps, device)
