@@ -34,7 +34,7 @@ struct ReadoutCfg {
   static constexpr int V_BYTES = 64 * VS * 2;
   static constexpr int U_BYTES = (2 * SLAB_BYTES > K_BYTES + V_BYTES) ? 2 * SLAB_BYTES
                                                                       : K_BYTES + V_BYTES;
-  static constexpr int MG_BYTES = HPW * LDIM * DH * 4;  // M_{gamma,g(t)}/d_h per head slot
+  static constexpr int MG_BYTES = HPW * 2 * LDIM * DH * 4;  // m M_{gamma,g(t)}/d_h, m = 1, 2
   static constexpr int LDS_BYTES = Q_BYTES + U_BYTES + MG_BYTES;
 };
 
@@ -107,7 +107,9 @@ k_readout_mfma(int n_q_heads, int n_kv_heads, int seq_len, int n_chunks, int n_h
   for (int i = tid; i < Cfg::HPW * LDIM * DH; i += 256) {
     const int hs = i / (LDIM * DH), e = i % (LDIM * DH);
     const int hh = hg * Cfg::HPW + hs;
-    s_mg[i] = hh < rep ? coef_rec(coeffs, kv * rep + hh)[OAL_COEF_MG + e] : 0.f;
+    const float x = hh < rep ? coef_rec(coeffs, kv * rep + hh)[OAL_COEF_MG + e] : 0.f;
+    s_mg[(hs * 2 + 0) * LDIM * DH + e] = x;          // multiplicity 1 (diagonal block)
+    s_mg[(hs * 2 + 1) * LDIM * DH + e] = 2.0f * x;   // multiplicity 2
   }
   __syncthreads();
 
@@ -269,53 +271,30 @@ k_readout_mfma(int n_q_heads, int n_kv_heads, int seq_len, int n_chunks, int n_h
   __syncthreads();
 
   const int32_t* gmap = reinterpret_cast<const int32_t*>(rec) + OAL_COEF_GMAP;   // g(r), uniform
-  const float* mgw = s_mg + hslot * LDIM * DH;
+  const float* mgw = s_mg + hslot * 2 * LDIM * DH;
   const __bf16* qrow0 = qw + (size_t)(tok0 + col) * Cfg::QS;        // token of N-tile 0
   const __bf16* qrow1 = qw + (size_t)(tok0 + 32 + col) * Cfg::QS;   // token of N-tile 1
-  float qt[2][8];               // q_t of this lane's 8 t's of the current t-block (c)
-  int cur_c = -1;
+  float qt0[8], qt1[8];   // q_t of this lane's 8 t's of the current t-block (c)
+  float qh0[8], qh1[8];   // qhat[t] = m q_t M_{g(r), g(t)} / d_h for the current (g(r), m)
+  int cur_c = -1, cur_key = -1;
 
   for (int s = 0; s < Cfg::NSLAB; ++s) {
     const int buf = s & 1;
     if (s + 1 < Cfg::NSLAB) load_slab(s + 1);
     if (head_ok) {
       const uint8_t* sb = s_u + buf * Cfg::SLAB_BYTES;
-      // K-step scalars of the slab (uniform) and the lane's m * q_r, fetched together
-      float mq[2][Cfg::SK];
-      int gam[Cfg::SK];
-      uint32_t todo = 0;
+      // Two half-slabs of 4 K-steps.  A new t-block starts at K-step 4 + 8 c (c + 1),
+      // i.e. always at a half-slab boundary, and the 4 r's of a half-slab are the
+      // consecutive, 4-aligned values r0 .. r0 + 3.
 #pragma unroll
-      for (int kk = 0; kk < Cfg::SK; ++kk) {
-        const int ks = s * Cfg::SK + kk;
-        gam[kk] = 0;
-        mq[0][kk] = mq[1][kk] = 0.f;
-        if (ks < tile::NKS_LIN) {
-          todo |= 1u << kk;
-        } else if (ks < tile::NKS) {
-          const int c = tile::ks_block(ks);
-          const int r = ks - tile::quad_base(c);
-          const float m = (r >= 16 * c) ? 1.0f : 2.0f;
-          gam[kk] = __builtin_amdgcn_readfirstlane(gmap[r]);
-          mq[0][kk] = m * bf(qrow0[r]);
-          mq[1][kk] = m * bf(qrow1[r]);
-          todo |= 1u << kk;
-        }
-      }
-      // The K-steps of a slab may be taken in any order: take them group by
-      // group so that one qhat vector is live at a time.  A slab spans at most
-      // two t-blocks (a new block starts at K-step 4 + 8 c (c + 1), i.e. at
-      // kk = 4), so blocks are handled as the two halves of the slab.
+      for (int hh = 0; hh < 2; ++hh) {
+        const int ks0 = s * Cfg::SK + 4 * hh;
+        if (ks0 >= tile::NKS) break;
+        if (ks0 < tile::NKS_LIN) {
+          // linear rows (slab 0, first half): phi = b'_r q_r, r = 16 ks + 8 half + j
 #pragma unroll
-      for (int part = 0; part < 2; ++part) {
-        const uint32_t pmask = part == 0 ? 0x0Fu : 0xF0u;
-        uint32_t left = todo & pmask;
-        if (!left) continue;
-        const int ks_first = s * Cfg::SK + 4 * part;
-        if (ks_first < tile::NKS_LIN) {
-          // linear rows (first half of slab 0): phi = b'_r q_r, r = 16 ks + 8 half + j
-#pragma unroll
-          for (int kk = 0; kk < 4; ++kk) {
-            const int ks = kk;
+          for (int i = 0; i < 4; ++i) {
+            const int ks = ks0 + i;
             float b8[8];
 #pragma unroll
             for (int j = 0; j < 8; ++j) b8[j] = rec[OAL_COEF_BP + 16 * ks + 8 * half + j];
@@ -330,60 +309,63 @@ k_readout_mfma(int n_q_heads, int n_kv_heads, int seq_len, int n_chunks, int n_h
             const bf16x8 b0 = pack8(x0), b1 = pack8(x1);
 #pragma unroll
             for (int mt = 0; mt < 2; ++mt) {
-              const bf16x8 af = *reinterpret_cast<const bf16x8*>(sb + slab_off(kk, 32 * mt + col, half));
+              const bf16x8 af = *reinterpret_cast<const bf16x8*>(sb + slab_off(4 * hh + i, 32 * mt + col, half));
               acc[mt][0] = mfma32(af, b0, acc[mt][0]);
               acc[mt][1] = mfma32(af, b1, acc[mt][1]);
             }
           }
           continue;
         }
-        const int c = tile::ks_block(ks_first);
+        const int c = tile::ks_block(ks0);
+        const int r0 = ks0 - tile::quad_base(c);
         if (c != cur_c) {
           cur_c = c;
+          cur_key = -1;
           const bf16x8 q0 = *reinterpret_cast<const bf16x8*>(qrow0 + 16 * c + 8 * half);
           const bf16x8 q1 = *reinterpret_cast<const bf16x8*>(qrow1 + 16 * c + 8 * half);
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
-            qt[0][j] = bf(q0[j]);
-            qt[1][j] = bf(q1[j]);
+            qt0[j] = bf(q0[j]);
+            qt1[j] = bf(q1[j]);
           }
         }
-        while (left) {
-          const int first = __builtin_ctz(left);
-          int gsel = 0;
+        // q_r for r0 .. r0 + 3 of both tokens (one 8-byte read each)
+        const uint2 qa = *reinterpret_cast<const uint2*>(qrow0 + r0);
+        const uint2 qb = *reinterpret_cast<const uint2*>(qrow1 + r0);
+        const float qr0[4] = {__uint_as_float(qa.x << 16), __uint_as_float(qa.x & 0xffff0000u),
+                              __uint_as_float(qa.y << 16), __uint_as_float(qa.y & 0xffff0000u)};
+        const float qr1[4] = {__uint_as_float(qb.x << 16), __uint_as_float(qb.x & 0xffff0000u),
+                              __uint_as_float(qb.y << 16), __uint_as_float(qb.y & 0xffff0000u)};
 #pragma unroll
-          for (int kk = 0; kk < Cfg::SK; ++kk)
-            if (kk == first) gsel = gam[kk];
-          // qhat_gamma[t] = q_t M_{gamma, g(t)} / d_h,  t = 16 c + 8 half + j
-          float qh0[8], qh1[8];
-          {
-            const float4* mrow = reinterpret_cast<const float4*>(mgw + gsel * DH + 16 * c + 8 * half);
+        for (int i = 0; i < 4; ++i) {
+          const int r = r0 + i;
+          const int gam = __builtin_amdgcn_readfirstlane(gmap[r]);
+          const int key = 2 * gam + (r >= 16 * c ? 0 : 1);     // (group, multiplicity)
+          if (key != cur_key) {
+            cur_key = key;
+            const float4* mrow = reinterpret_cast<const float4*>(
+                mgw + ((key & 1) * LDIM + gam) * DH + 16 * c + 8 * half);
             const float4 ma = mrow[0], mb = mrow[1];
             const float m8[8] = {ma.x, ma.y, ma.z, ma.w, mb.x, mb.y, mb.z, mb.w};
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-              qh0[j] = qt[0][j] * m8[j];
-              qh1[j] = qt[1][j] * m8[j];
+              qh0[j] = qt0[j] * m8[j];
+              qh1[j] = qt1[j] * m8[j];
             }
           }
+          // quadratic rows of item (r, c): phi = q_r * qhat[t]
+          float x0[8], x1[8];
 #pragma unroll
-          for (int kk = 0; kk < Cfg::SK; ++kk) {
-            if (!((left >> kk) & 1u) || gam[kk] != gsel) continue;
-            left &= ~(1u << kk);
-            // quadratic rows of item (r, c): phi = (m q_r) * qhat_{g(r)}[t]
-            float x0[8], x1[8];
+          for (int j = 0; j < 8; ++j) {
+            x0[j] = qr0[i] * qh0[j];
+            x1[j] = qr1[i] * qh1[j];
+          }
+          const bf16x8 b0 = pack8(x0), b1 = pack8(x1);
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-              x0[j] = mq[0][kk] * qh0[j];
-              x1[j] = mq[1][kk] * qh1[j];
-            }
-            const bf16x8 b0 = pack8(x0), b1 = pack8(x1);
-#pragma unroll
-            for (int mt = 0; mt < 2; ++mt) {
-              const bf16x8 af = *reinterpret_cast<const bf16x8*>(sb + slab_off(kk, 32 * mt + col, half));
-              acc[mt][0] = mfma32(af, b0, acc[mt][0]);
-              acc[mt][1] = mfma32(af, b1, acc[mt][1]);
-            }
+          for (int mt = 0; mt < 2; ++mt) {
+            const bf16x8 af = *reinterpret_cast<const bf16x8*>(sb + slab_off(4 * hh + i, 32 * mt + col, half));
+            acc[mt][0] = mfma32(af, b0, acc[mt][0]);
+            acc[mt][1] = mfma32(af, b1, acc[mt][1]);
           }
         }
       }
