@@ -6,10 +6,12 @@
 //   u~_i = phi_q(q_i)^T H_{<c}  +  sum_{j in chunk, j <= i} kappa(q_i, k_j) u_j
 //   y_i  = u~_{i,1:64} / u~_{i,65}
 // The inter-chunk term reads the exclusive prefix state H_{<c} of the chunk (a
-// bf16 copy in the tiled layout of oal_tile.h, plus fp32 side data for the
-// denominator); the intra-chunk term evaluates kappa = eps + sum_p t_p^2,
+// scaled fp16 copy in the tiled layout of oal_tile.h, plus fp32 side data for
+// the denominator); the intra-chunk term evaluates kappa = eps + sum_p t_p^2,
 // t_p = L_0p + sum_r ell_p[r] q_r k_r (the expansion of ||L^T s_bar||^2, Eq. 7)
 // on the matrix cores and applies it to [V; 1].
+#include <type_traits>
+
 #include "oal_tile.h"
 
 namespace oal {
@@ -18,45 +20,153 @@ namespace oal {
 // Readout.  Workgroup = 4 waves = (256 / C) query heads of one KV group x C
 // tokens of one chunk; wave = one head x 64 tokens.  In the u~^T orientation
 // (rows = value channel w, columns = tokens) each wave owns a 64 x 64 tile of
-// accumulators (2 x 2 MFMA tiles).
+// fp32 accumulators (2 x 2 MFMA tiles).
+//
+// Scaling.  The inter-chunk contraction runs in fp16 (A = state tile, stored as
+// H 2^-e_S; B = query features built with packed fp16 multiplies).  Per head the
+// query features are scaled by F_f = 2^(12 - 2 e_q - e_M - x) so that every
+// fp16 operand and intermediate stays below 2^14 (|q| < 2^e_q, |M/d_h| < 2^e_M,
+// x keeps the linear features in range as well).  Every other term added into
+// the same accumulators or the denominator (the intra-chunk kappa, a H0, the
+// inter-chunk denominator) is multiplied by the same F = 2^E, E = F_f's
+// exponent - e_S: the factor cancels in y = u~_{1:64} / u~_65 and all scalings
+// are exact powers of two.
+//
+// LDS.  Every region is a __shared__ object of its own, so that the compiler
+// can tell the state half-slab buffers (filled by direct-to-LDS loads that stay
+// in flight across iterations) from the q tile and the tables it reads
+// meanwhile.  Rows of 64 bf16 are 128 bytes with the 16-byte chunks XOR-swizzled
+// by (row & 7) instead of padded.  Before the inter-chunk loop the buffers hold
+// the chunk's k rows and v^T rows.
 // ---------------------------------------------------------------------------
 template <int CH>
 struct ReadoutCfg {
   static constexpr int WPH = CH / 64;               // waves per head
   static constexpr int HPW = 4 / WPH;               // heads per workgroup
-  static constexpr int QS = 72;                     // bf16 row stride of q / k tiles
-  static constexpr int VS = CH + 8;                 // bf16 row stride of v^T
-  static constexpr int SK = 8;                      // K-steps per state slab
-  static constexpr int NSLAB = (tile::NKS + SK - 1) / SK;
-  static constexpr int SLAB_BYTES = SK * tile::KS_BYTES;
-  static constexpr int Q_BYTES = HPW * CH * QS * 2;
-  static constexpr int K_BYTES = CH * QS * 2;
-  static constexpr int V_BYTES = 64 * VS * 2;
-  static constexpr int U_BYTES = (2 * SLAB_BYTES > K_BYTES + V_BYTES) ? 2 * SLAB_BYTES
-                                                                      : K_BYTES + V_BYTES;
-  static constexpr int MG_BYTES = HPW * 2 * LDIM * DH * 4;  // m M_{gamma,g(t)}/d_h, m = 1, 2
-  static constexpr int LDS_BYTES = Q_BYTES + U_BYTES + MG_BYTES;
+  static constexpr int HS_BYTES = 4 * tile::KS_BYTES;   // one half-slab = 4 K-steps = 8 KB
+  static constexpr int NHS = tile::NKS / 4;         // 41 half-slabs per tile
+  static constexpr int Q_BYTES = HPW * CH * 128;    // = 32 KB
+  static constexpr int XB = CH == 256 ? HS_BYTES : 16;   // extra staging arrays (C = 256)
 };
 
-// Swizzled LDS offset of the 16-byte half-row (w, h) of a K-step inside a slab
-// (avoids bank conflicts between rows w and w + 4).
+// Per-head table (floats), written from the coefficient record with the head's
+// scales folded in.
+namespace htab {
+constexpr int ELL = 0;                  // [LDIM][DH] ell_p[r] 2^(E/2)
+constexpr int L0 = LDIM * DH;           // [8]  L_{0,p} 2^(E/2)
+constexpr int ELLC = L0 + 8;            // [LDIM][16] ell_p at the compact dims, 2^(E/2)
+constexpr int CIDX = ELLC + LDIM * 16;  // [16] int: the dims with g(r) >= 2 (compact path)
+constexpr int BPF = CIDX + 16;          // [DH] b'_r F_f
+constexpr int FLOATS = BPF + DH;
+}  // namespace htab
+
+// A row of 64 bf16 in a swizzled 128-byte LDS row.
+struct SwRow {
+  const uint8_t* p;
+  int key;   // row & 7
+  __device__ __forceinline__ SwRow(const uint8_t* base, int row) : p(base + row * 128), key(row & 7) {}
+  // 16-byte chunk c (elements 8 c .. 8 c + 7)
+  __device__ __forceinline__ const uint8_t* chunk(int c) const { return p + ((c ^ key) << 4); }
+  // element d
+  __device__ __forceinline__ const __bf16* elem(int d) const {
+    return reinterpret_cast<const __bf16*>(p + (((d >> 3) ^ key) << 4) + ((d & 7) << 1));
+  }
+};
+
+// Swizzled LDS offset of the 16-byte half-row (w, h) of a K-step inside a
+// half-slab (avoids bank conflicts between rows w and w + 4).
 __device__ __forceinline__ int slab_off(int kk, int w, int h) {
   return kk * tile::KS_BYTES + w * 32 + 16 * (h ^ ((w >> 2) & 1));
 }
 
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
+  return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(x)));
+}
+
+__device__ __forceinline__ uint32_t wave_umax(uint32_t x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x = max(x, (uint32_t)__shfl_xor((int)x, o, 64));
+  return x;
+}
+
+// e with x < 2^e for x > 0; 0 for x == 0.
+__device__ __forceinline__ int exp_above(float x) {
+  int e = 0;
+  if (x > 0.f) frexpf(x, &e);
+  return e;
+}
+
+// Wait until at most N vector-memory operations of this wave are outstanding
+// (the direct-to-LDS loads count there); other counters are left alone.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 16, "vmcnt immediate");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+}
+
+// Workgroup barrier without the memory fence of __syncthreads (which would wait
+// for the prefetches still in flight); the clobber keeps LDS accesses in place.
+__device__ __forceinline__ void barrier_nofence() { asm volatile("s_barrier" ::: "memory"); }
+
+template <bool B>
+using bool_t = std::integral_constant<bool, B>;
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Raw buffer resource over [base, base + bytes) (reads beyond it return zero).
+__device__ __forceinline__ i32x4 buffer_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  i32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  r[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));   // stride 0
+  r[2] = __builtin_amdgcn_readfirstlane((int)bytes);
+  r[3] = 0x00020000;                                                  // 32-bit data format
+  return r;
+}
+
+// LDS byte address of a __shared__ pointer.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// 16 bytes per lane from rsrc + soff + voff into LDS at lds + 16 * lane.
+__device__ __forceinline__ void load_lds16(const i32x4& rsrc, uint32_t lds, uint32_t voff, int soff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :
+               : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(rsrc), "s"(soff)
+               : "memory");
+}
+
+__device__ __forceinline__ uint8_t* pick4(int i, uint8_t* a, uint8_t* b, uint8_t* c, uint8_t* d) {
+  return i == 0 ? a : i == 1 ? b : i == 2 ? c : d;
+}
+
 template <int CH, typename O>
-__global__ void __launch_bounds__(256, 2)
+__global__ void __launch_bounds__(256, CH == 256 ? 1 : 2)   // C = 256: LDS allows one
 k_readout_mfma(int n_q_heads, int n_kv_heads, int seq_len, int n_chunks, int n_hg, int n_uc,
                const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                const uint16_t* __restrict__ v, const float* __restrict__ coeffs,
                const uint8_t* __restrict__ ws_tile, O* __restrict__ y) {
   using Cfg = ReadoutCfg<CH>;
-  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  __bf16* s_q = reinterpret_cast<__bf16*>(smem);
-  uint8_t* s_u = smem + Cfg::Q_BYTES;
-  __bf16* s_k = reinterpret_cast<__bf16*>(s_u);
-  __bf16* s_vt = reinterpret_cast<__bf16*>(s_u + Cfg::K_BYTES);
-  float* s_mg = reinterpret_cast<float*>(smem + Cfg::Q_BYTES + Cfg::U_BYTES);
+  __shared__ __attribute__((aligned(16))) uint8_t s_q[Cfg::Q_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t s_b0[Cfg::HS_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t s_b1[Cfg::HS_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t s_b2[Cfg::HS_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t s_b3[Cfg::HS_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t s_x0[Cfg::XB];
+  __shared__ __attribute__((aligned(16))) uint8_t s_x1[Cfg::XB];
+  __shared__ __attribute__((aligned(16))) uint8_t s_x2[Cfg::XB];
+  __shared__ __attribute__((aligned(16))) uint8_t s_x3[Cfg::XB];
+  __shared__ __attribute__((aligned(16))) _Float16 s_mg[Cfg::HPW * LDIM * DH];
+  __shared__ __attribute__((aligned(16))) float s_ht[Cfg::HPW * htab::FLOATS];
+  __shared__ float s_red[16];
+  // k rows (64 per array) and v^T rows (64 keys per array) of the chunk
+  auto k_arr = [&](int i) -> uint8_t* { return pick4(i, s_b0, s_b1, s_b2, s_b3); };
+  auto v_arr = [&](int i) -> uint8_t* {
+    return CH == 256 ? pick4(i, s_x0, s_x1, s_x2, s_x3) : pick4(i, s_b2, s_b3, s_b2, s_b3);
+  };
 
   // ---- which (unit, chunk, head group): the head groups of one (unit, chunk)
   //      share an XCD (blockIdx % 8) so they hit the same L2 for the state.
@@ -78,18 +188,30 @@ k_readout_mfma(int n_q_heads, int n_kv_heads, int seq_len, int n_chunks, int n_h
   const int hl = hg * Cfg::HPW + hslot;
   const bool head_ok = hl < rep;
   const int hq = kv * rep + (head_ok ? hl : 0);
+  const float* rec = coef_rec(coeffs, hq);
+  const uint8_t* tsrc = ws_tile + ((size_t)unit * n_chunks + chunk) * tile::BYTES;
+  const float* ts_side = reinterpret_cast<const float*>(tsrc + tile::TILE_BYTES);
 
-  // ---- stage q (all heads of the group), k and v^T of the chunk
-  for (int i = tid; i < Cfg::HPW * CH * 8; i += 256) {
-    const int hs = i / (CH * 8), rem = i % (CH * 8), tok = rem >> 3, part = rem & 7;
+  // ---- stage q (all heads of the group), keeping each thread's max |q| per head
+  uint32_t qmax[Cfg::HPW];
+#pragma unroll
+  for (int hs = 0; hs < Cfg::HPW; ++hs) qmax[hs] = 0;
+#pragma unroll
+  for (int it = 0; it < Cfg::HPW * CH * 8 / 256; ++it) {
+    const int hs = it * 256 / (CH * 8);          // compile-time after unrolling
+    const int rem = tid + 256 * it - hs * CH * 8, tok = rem >> 3, part = rem & 7;
     const int hh = hg * Cfg::HPW + hs;
     uint4 val = make_uint4(0, 0, 0, 0);
     if (hh < rep && tok < clen) {
       const size_t row = ((size_t)b * n_q_heads + kv * rep + hh) * seq_len + t0 + tok;
       val = reinterpret_cast<const uint4*>(q + row * DH)[part];
     }
-    *reinterpret_cast<uint4*>(s_q + ((size_t)hs * CH + tok) * Cfg::QS + part * 8) = val;
+    const int qrow = hs * CH + tok;
+    *reinterpret_cast<uint4*>(s_q + qrow * 128 + ((part ^ (qrow & 7)) << 4)) = val;
+    qmax[hs] = max(qmax[hs], absmax8_bits(val));
   }
+  // ---- k, and v^T with the keys of each 16-block permuted: position 8h + 4a + e
+  //      holds key 8a + 4h + e (the key order of the kappa accumulator rows)
   const size_t kvrow0 = (size_t)unit * seq_len + t0;
   for (int i = tid; i < CH * 8; i += 256) {
     const int tok = i >> 3, part = i & 7;
@@ -98,43 +220,248 @@ k_readout_mfma(int n_q_heads, int n_kv_heads, int seq_len, int n_chunks, int n_h
       kk = reinterpret_cast<const uint4*>(k + (kvrow0 + tok) * DH)[part];
       vv = reinterpret_cast<const uint4*>(v + (kvrow0 + tok) * DV)[part];
     }
-    *reinterpret_cast<uint4*>(s_k + (size_t)tok * Cfg::QS + part * 8) = kk;
+    *reinterpret_cast<uint4*>(k_arr(tok >> 6) + (tok & 63) * 128 + ((part ^ (tok & 7)) << 4)) = kk;
+    const int pos = (tok & ~15) | (((tok >> 2) & 1) << 3) | (((tok >> 3) & 1) << 2) | (tok & 3);
+    uint8_t* va = v_arr(pos >> 6);
+    const int pk = pos & 63;
     const uint16_t* pv = reinterpret_cast<const uint16_t*>(&vv);
-    uint16_t* vt = reinterpret_cast<uint16_t*>(s_vt);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) vt[(size_t)(part * 8 + e) * Cfg::VS + tok] = pv[e];
+    for (int e = 0; e < 8; ++e) {
+      const int w = part * 8 + e;
+      *reinterpret_cast<uint16_t*>(va + w * 128 + (((pk >> 3) ^ (w & 7)) << 4) + ((pk & 7) << 1)) = pv[e];
+    }
   }
-  for (int i = tid; i < Cfg::HPW * LDIM * DH; i += 256) {
-    const int hs = i / (LDIM * DH), e = i % (LDIM * DH);
-    const int hh = hg * Cfg::HPW + hs;
-    const float x = hh < rep ? coef_rec(coeffs, kv * rep + hh)[OAL_COEF_MG + e] : 0.f;
-    s_mg[(hs * 2 + 0) * LDIM * DH + e] = x;          // multiplicity 1 (diagonal block)
-    s_mg[(hs * 2 + 1) * LDIM * DH + e] = 2.0f * x;   // multiplicity 2
+
+  // ---- this head's coefficient magnitudes (wave-uniform) and group map (lane r)
+  float mn = 0.f, bn = 0.f;
+  int gl = 1;
+  if (head_ok) {
+    mn = lane < LDIM * LDIM ? fabsf(rec[OAL_COEF_M + lane]) * (1.0f / DH) : 0.f;
+    bn = fabsf(rec[OAL_COEF_BP + lane]);
+    gl = reinterpret_cast<const int32_t*>(rec)[OAL_COEF_GMAP + lane];
+  }
+  const int e_m = exp_above(wave_max(mn));
+  const int e_b = exp_above(wave_max(bn));
+  if (head_ok && sub == 0) {   // fp16 table M_{gamma,g(t)} / d_h 2^-e_M of the head
+    _Float16* mg = s_mg + hslot * LDIM * DH;
+    const float sc = ldexpf(1.0f, -e_m);
+    for (int e = lane; e < LDIM * DH; e += 64) mg[e] = (_Float16)(rec[OAL_COEF_MG + e] * sc);
+  }
+#pragma unroll
+  for (int hs = 0; hs < Cfg::HPW; ++hs) {
+    const uint32_t m = wave_umax(qmax[hs]);
+    if (lane == 0) s_red[wave * 4 + hs] = __uint_as_float(m << 16);
   }
   __syncthreads();
 
-  const float* rec = coef_rec(coeffs, hq);
-  const int G = reinterpret_cast<const int32_t*>(rec)[OAL_COEF_NG];
-  const float* ts_side = reinterpret_cast<const float*>(
-      ws_tile + ((size_t)unit * n_chunks + chunk) * tile::BYTES + tile::TILE_BYTES);
-  const int tok0 = sub * 64;                 // first token of this wave in the chunk
-  const __bf16* qw = s_q + (size_t)hslot * CH * Cfg::QS;
+  // ---- the head's scales (identical in the waves of one head)
+  const float qm = fmaxf(fmaxf(s_red[0 * 4 + hslot], s_red[1 * 4 + hslot]),
+                         fmaxf(s_red[2 * 4 + hslot], s_red[3 * 4 + hslot]));
+  const int e_q = exp_above(qm);
+  const int e_s = (int)ts_side[tile::SIDE_SEXP];
+  int xs = max(0, e_b - e_q - e_m - 3);
+  int E = -e_s + 12 - 2 * e_q - e_m - xs;
+  if (E & 1) {   // even, so that sqrt(F) is a power of two as well
+    ++xs;
+    --E;
+  }
+  const float F = ldexpf(1.0f, E);
+  const float sroot = ldexpf(1.0f, E / 2);
+  const float Ff = ldexpf(1.0f, 12 - 2 * e_q - e_m - xs);
+  const float qt_scale = ldexpf(1.0f, 6 - e_q - xs);
+  const float qr_scale = ldexpf(1.0f, 6 - e_q);
 
+  // ---- per-head table; both waves of a head write the same values, and each
+  //      wave only reads back what it wrote itself (LDS ops of a wave are ordered)
+  const int G = reinterpret_cast<const int32_t*>(rec)[OAL_COEF_NG];
+  float* ht = s_ht + hslot * htab::FLOATS;
+  const uint64_t cmask = __ballot(gl >= 2);   // dims of the groups 2..G
+  const int n_out = __popcll(cmask);
+  const bool compact = n_out <= 16;            // t_p, p >= 2, from one 16-deep K-step
+  if (head_ok) {
+    for (int e = lane; e < LDIM * DH; e += 64) ht[htab::ELL + e] = rec[OAL_COEF_ELL + e] * sroot;
+    if (lane < LDIM) ht[htab::L0 + lane] = rec[OAL_COEF_L + lane] * sroot;   // L_{0,p}
+    ht[htab::BPF + lane] = rec[OAL_COEF_BP + lane] * Ff;
+    if (compact) {
+      int* cidx = reinterpret_cast<int*>(ht + htab::CIDX);
+      if (gl >= 2) {
+        const int rank = __builtin_amdgcn_mbcnt_hi((uint32_t)(cmask >> 32),
+                                                   __builtin_amdgcn_mbcnt_lo((uint32_t)cmask, 0));
+        cidx[rank] = lane;
+        for (int p = 0; p < LDIM; ++p)
+          ht[htab::ELLC + p * 16 + rank] = rec[OAL_COEF_ELL + p * DH + lane] * sroot;
+      }
+      if (lane >= n_out && lane < 16) {
+        cidx[lane] = 0;
+        for (int p = 0; p < LDIM; ++p) ht[htab::ELLC + p * 16 + lane] = 0.f;
+      }
+    }
+  }
+
+  const int tok0 = sub * 64;                 // first token of this wave in the chunk
+  const uint8_t* qw = s_q + hslot * CH * 128;
+  const SwRow qrow0(qw, tok0 + col), qrow1(qw, tok0 + 32 + col);   // tokens of N-tiles 0, 1
   // q fragment (B operand, columns = tokens, K = head dims): exact bf16 inputs
   auto qfrag = [&](int nt, int ks) {
-    return *reinterpret_cast<const bf16x8*>(qw + (size_t)(tok0 + 32 * nt + col) * Cfg::QS +
-                                            16 * ks + 8 * half);
+    return *reinterpret_cast<const bf16x8*>((nt ? qrow1 : qrow0).chunk(2 * ks + half));
   };
 
-  float den[2] = {0.f, 0.f};   // this lane's partial denominators of tokens (col, nt)
+  float den[2] = {0.f, 0.f};   // this lane's partial denominators of tokens (col, nt), times F
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = splat16(0.f);
 
-  // ================= inter-chunk denominator ===============================
-  // den = a z0 + sum_r b'_r q_r z1_r + q^T (C / d_h o Z) q: the all-ones channel
-  // of the readout; the quadratic part as T = (C/d_h o Z) q^T on the matrix cores,
-  // one 32-row block of T at a time.
+  // ================= intra-chunk part ======================================
+  // kappa^T[key][tok] F = eps F + sum_p (sqrt(F) (L_0p + sum_r ell_p[r] k_r q_r))^2 on
+  // the matrix cores (A = k o ell_p, B = q^T, the accumulator seeded with L_0p),
+  // causal mask, then u~^T += [V; 1]^T kappa^T (values on the matrix cores, the
+  // ones channel as column sums into the denominator).  ell_p is supported on the
+  // dims with g(r) >= p, so for p >= 2 only the outlier dims (g >= 2) contribute:
+  // when there are at most 16 of them they are gathered into one K-step.
+  if (head_ok) {
+    const float epsF = rec[OAL_COEF_EPS] * F;
+    const bool use_c = compact && G >= 2;
+    const int p_full = use_c ? 1 : G;          // p = 0 .. p_full on the 64-deep path
+    const int* cidx = reinterpret_cast<const int*>(ht + htab::CIDX) + 8 * half;
+    bf16x8 qc[2];                              // compact q (B operand) of the wave's tokens
+    if (use_c) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int d = cidx[j];
+        qc[0][j] = *qrow0.elem(d);
+        qc[1][j] = *qrow1.elem(d);
+      }
+    }
+    // One 32-key tile.  DO0: token tile 0 is not entirely masked; MASKn: token
+    // tile n is the diagonal one (key row acc_row(i, h) visible iff <= col).
+    auto key_tile = [&](int kt, auto do0_t, auto mask0_t, auto mask1_t) {
+      constexpr bool DO0 = decltype(do0_t)::value;
+      constexpr bool MASK[2] = {decltype(mask0_t)::value, decltype(mask1_t)::value};
+      f32x16 kap[2] = {splat16(epsF), splat16(epsF)};
+      const SwRow krow(k_arr(kt >> 1), (32 * kt + col) & 63);
+      float kf[4][8];
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const bf16x8 x = *reinterpret_cast<const bf16x8*>(krow.chunk(2 * ks + half));
+#pragma unroll
+        for (int j = 0; j < 8; ++j) kf[ks][j] = bf(x[j]);
+      }
+      for (int p = 0; p <= p_full; ++p) {
+        const float* ell = ht + htab::ELL + p * DH + 8 * half;
+        bf16x8 ak[4];
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          const float4 e0 = *reinterpret_cast<const float4*>(ell + 16 * ks);
+          const float4 e1 = *reinterpret_cast<const float4*>(ell + 16 * ks + 4);
+          const float x[8] = {kf[ks][0] * e0.x, kf[ks][1] * e0.y, kf[ks][2] * e0.z, kf[ks][3] * e0.w,
+                              kf[ks][4] * e1.x, kf[ks][5] * e1.y, kf[ks][6] * e1.z, kf[ks][7] * e1.w};
+          ak[ks] = pack8(x);
+        }
+        const float l0 = ht[htab::L0 + p];
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+          if (nt == 0 && !DO0) continue;
+          f32x16 sacc = splat16(l0);
+#pragma unroll
+          for (int ks = 0; ks < 4; ++ks) sacc = mfma32(ak[ks], qfrag(nt, ks), sacc);
+#pragma unroll
+          for (int i = 0; i < 16; ++i) kap[nt][i] = fmaf(sacc[i], sacc[i], kap[nt][i]);
+        }
+      }
+      if (use_c) {
+        float kc[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) kc[j] = bf(*krow.elem(cidx[j]));
+        for (int p = 2; p <= G; ++p) {
+          const float* ec = ht + htab::ELLC + p * 16 + 8 * half;
+          const float4 e0 = *reinterpret_cast<const float4*>(ec);
+          const float4 e1 = *reinterpret_cast<const float4*>(ec + 4);
+          const float x[8] = {kc[0] * e0.x, kc[1] * e0.y, kc[2] * e0.z, kc[3] * e0.w,
+                              kc[4] * e1.x, kc[5] * e1.y, kc[6] * e1.z, kc[7] * e1.w};
+          const bf16x8 akc = pack8(x);
+          const float l0 = ht[htab::L0 + p];
+#pragma unroll
+          for (int nt = 0; nt < 2; ++nt) {
+            if (nt == 0 && !DO0) continue;
+            const f32x16 sacc = mfma32(akc, qc[nt], splat16(l0));
+#pragma unroll
+            for (int i = 0; i < 16; ++i) kap[nt][i] = fmaf(sacc[i], sacc[i], kap[nt][i]);
+          }
+        }
+      }
+      // causal mask, denominators, and P [V; 1]
+      const uint8_t* va = v_arr(kt >> 1);
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        if (nt == 0 && !DO0) continue;
+        if (MASK[nt]) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            if (acc_row(i, half) > col) kap[nt][i] = 0.f;
+        }
+        float ds = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) ds += kap[nt][i];
+        den[nt] += ds;
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+          float x[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) x[j] = kap[nt][8 * s2 + j];
+          const bf16x8 pb = pack8(x);
+          const int kc8 = (4 * (kt & 1) + 2 * s2 + half);   // 16-byte chunk of the v^T row
+#pragma unroll
+          for (int mt = 0; mt < 2; ++mt) {
+            const SwRow vr(va, 32 * mt + col);
+            const bf16x8 av = *reinterpret_cast<const bf16x8*>(vr.chunk(kc8));
+            acc[mt][nt] = mfma32(av, pb, acc[mt][nt]);
+          }
+        }
+      }
+    };
+    for (int kt = 0; kt < 2 * sub; ++kt) key_tile(kt, bool_t<true>{}, bool_t<false>{}, bool_t<false>{});
+    key_tile(2 * sub, bool_t<true>{}, bool_t<true>{}, bool_t<false>{});
+    key_tile(2 * sub + 1, bool_t<false>{}, bool_t<false>{}, bool_t<true>{});
+  }
+
+  // ================= inter-chunk part ======================================
+  __syncthreads();   // the half-slab buffers held k / v^T
+  // Half-slab hs of the tile goes to buffer hs % 4 by direct-to-LDS buffer loads:
+  // each wave moves two 1 KB pieces, lane l writing bytes 16 l .. 16 l + 15 of a
+  // piece, fetched from the tile position that the swizzle of slab_off puts there.
+  // The loads are issued from inline assembly: the compiler then neither waits
+  // for them before LDS reads it cannot prove disjoint from the buffers, nor
+  // before rewriting their operand registers.  Their completion is awaited by
+  // hand (wait_vmcnt) before the barrier that hands a buffer to the waves;
+  // other memory operations of the wave complete in issue order with them, so
+  // the compiler's own counts stay safe (only stricter).
+  uint32_t dma_off[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int piece = wave * 2 + i;                 // 1 KB piece of the half-slab
+    const int kk = piece >> 1, pos = (piece & 1) * 64 + lane;
+    const int w = pos >> 1, hh = (pos & 1) ^ ((w >> 2) & 1);
+    dma_off[i] = kk * tile::KS_BYTES + w * 32 + hh * 16;
+  }
+  const i32x4 tile_rsrc = buffer_rsrc(tsrc, (uint32_t)tile::TILE_BYTES);
+  auto issue = [&](int hs, uint8_t* buf) {
+    const int soff = min(hs, Cfg::NHS - 1) * Cfg::HS_BYTES;
+    const uint32_t dst = lds_addr(buf) + wave * 2048;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) load_lds16(tile_rsrc, dst + i * 1024, dma_off[i], soff);
+  };
+  issue(0, s_b0);
+  issue(1, s_b1);
+  issue(2, s_b2);
+
+  // ---- inter-chunk denominator: a z0 + sum_r b'_r q_r z1_r + q^T (C / d_h o Z) q,
+  //      the quadratic part as T = (C/d_h o Z) q^T on the matrix cores
   if (head_ok) {
     const float* cm = rec + OAL_COEF_CM;
     const float* Zs = ts_side + tile::SIDE_Z;
+    float dd[2] = {0.f, 0.f};
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
       f32x16 T[2] = {splat16(0.f), splat16(0.f)};
@@ -153,11 +480,11 @@ k_readout_mfma(int n_q_heads, int n_kv_heads, int seq_len, int n_chunks, int n_h
       }
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
-        const __bf16* qrow = qw + (size_t)(tok0 + 32 * nt + col) * Cfg::QS;
+        const SwRow& qr = nt ? qrow1 : qrow0;
         float d = 0.f;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) d = fmaf(bf(qrow[32 * mt + acc_row(i, half)]), T[nt][i], d);
-        den[nt] += d;
+        for (int i = 0; i < 16; ++i) d = fmaf(bf(*qr.elem(32 * mt + acc_row(i, half))), T[nt][i], d);
+        dd[nt] += d;
       }
     }
     const float a = rec[OAL_COEF_A];
@@ -165,220 +492,136 @@ k_readout_mfma(int n_q_heads, int n_kv_heads, int seq_len, int n_chunks, int n_h
     const float* z1 = ts_side + tile::SIDE_Z1;
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
-      const __bf16* qrow = qw + (size_t)(tok0 + 32 * nt + col) * Cfg::QS;
+      const SwRow& qr = nt ? qrow1 : qrow0;
       float d = half == 0 ? a * ts_side[tile::SIDE_Z0] : 0.f;
 #pragma unroll 8
-      for (int r = 32 * half; r < 32 * half + 32; ++r) d = fmaf(bp[r] * bf(qrow[r]), z1[r], d);
-      den[nt] += d;
+      for (int r = 32 * half; r < 32 * half + 32; ++r) d = fmaf(bp[r] * bf(*qr.elem(r)), z1[r], d);
+      den[nt] += (dd[nt] + d) * F;
     }
   }
 
-  f32x16 acc[2][2];
+  // ---- main K loop over the 41 half-slabs: 1 linear, then 4 (c + 1) per t-block c;
+  //      quadratic half-slab hs = 1 + 2 c (c + 1) + h sits in buffer (1 + h) % 4
+  const uint8_t* mgh = reinterpret_cast<const uint8_t*>(s_mg + hslot * LDIM * DH) + 16 * half;
+  f16x8 qt[2], qh[2];
+  int cur = -1;
+  // one quadratic half-slab: K-steps (r0 + i, c), i = 0..3
+  auto quad = [&](int c, int h, const uint8_t* sb) {
+    const int r0 = 4 * h;
+    // m q_r of r0 .. r0 + 3 (m = 2 off the diagonal 16-block), scaled, as fp16
+    const float qs = r0 < 16 * c ? 2.0f * qr_scale : qr_scale;
+    _Float16 qr[2][4];
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt)
+    for (int nt = 0; nt < 2; ++nt) {
+      const uint2 u = *reinterpret_cast<const uint2*>((nt ? qrow1 : qrow0).elem(r0));
+      const f16x2 lo = __builtin_convertvector(
+          (f32x2){__uint_as_float(u.x << 16) * qs, __uint_as_float(u.x & 0xffff0000u) * qs}, f16x2);
+      const f16x2 hi = __builtin_convertvector(
+          (f32x2){__uint_as_float(u.y << 16) * qs, __uint_as_float(u.y & 0xffff0000u) * qs}, f16x2);
+      qr[nt][0] = lo[0];
+      qr[nt][1] = lo[1];
+      qr[nt][2] = hi[0];
+      qr[nt][3] = hi[1];
+    }
+    const uint8_t* mgc = mgh + 32 * c;
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = splat16(0.f);
-
-  // ================= intra-chunk part ======================================
-  // kappa^T[key][tok] = eps + sum_p (L_0p + sum_r ell_p[r] k_r q_r)^2 on the matrix
-  // cores (A = k o ell_p, B = q^T, the accumulator seeded with L_0p), causal mask,
-  // then u~^T += [V; 1]^T kappa^T (values on the matrix cores, the ones channel as
-  // column sums into the denominator).  One 32-key tile at a time.
-  if (head_ok) {
-    const float eps = rec[OAL_COEF_EPS];
-    const int n_kt = 2 * (sub + 1);          // key tiles covering keys <= last token
-    for (int kt = 0; kt < n_kt; ++kt) {
-      f32x16 kap[2] = {splat16(eps), splat16(eps)};
-      const __bf16* krow = s_k + (size_t)(32 * kt + col) * Cfg::QS;
-      for (int p = 0; p <= G; ++p) {
-        const float l0p = rec[OAL_COEF_L + p];          // L_{0,p}
-        const float* ell = rec + OAL_COEF_ELL + p * DH;
-        bf16x8 ak[4];
+    for (int i = 0; i < 4; ++i) {
+      // qhat = q_t M_{g(r), g(t)} / d_h (scaled), recomputed when g(r) changes
+      const int g = __builtin_amdgcn_readlane(gl, r0 + i);
+      if (g != cur) {
+        cur = g;
+        const f16x8 m8 = *reinterpret_cast<const f16x8*>(mgc + g * (DH * 2));
+        qh[0] = qt[0] * m8;
+        qh[1] = qt[1] * m8;
+      }
+      const f16x8 f0 = qh[0] * qr[0][i];
+      const f16x8 f1 = qh[1] * qr[1][i];
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          const bf16x8 kf = *reinterpret_cast<const bf16x8*>(krow + 16 * ks + 8 * half);
-          float x[8];
+      for (int mt = 0; mt < 2; ++mt) {
+        const f16x8 af = *reinterpret_cast<const f16x8*>(sb + slab_off(i, 32 * mt + col, half));
+        acc[mt][0] = mfma32h(af, f0, acc[mt][0]);
+        acc[mt][1] = mfma32h(af, f1, acc[mt][1]);
+      }
+    }
+  };
+  auto main_loop = [&](auto compute_t) {
+    constexpr bool COMPUTE = decltype(compute_t)::value;
+    // linear half-slab (buffer 0): phi = b'_r F_f q_r, r = 16 ks + 8 half + j
+    wait_vmcnt<4>();
+    barrier_nofence();
+    issue(3, s_b3);
+    if (COMPUTE) {
 #pragma unroll
-          for (int j = 0; j < 8; ++j) x[j] = bf(kf[j]) * ell[16 * ks + 8 * half + j];
-          ak[ks] = pack8(x);
-        }
+      for (int ks = 0; ks < 4; ++ks) {
+        const float4 b0 = *reinterpret_cast<const float4*>(ht + htab::BPF + 16 * ks + 8 * half);
+        const float4 b1 = *reinterpret_cast<const float4*>(ht + htab::BPF + 16 * ks + 8 * half + 4);
+        const float bq[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+        f16x8 fb[2];
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) {
-          f32x16 sacc = splat16(l0p);
+          const bf16x8 qv = *reinterpret_cast<const bf16x8*>((nt ? qrow1 : qrow0).chunk(2 * ks + half));
 #pragma unroll
-          for (int ks = 0; ks < 4; ++ks) sacc = mfma32(ak[ks], qfrag(nt, ks), sacc);
-#pragma unroll
-          for (int i = 0; i < 16; ++i) kap[nt][i] = fmaf(sacc[i], sacc[i], kap[nt][i]);
-        }
-      }
-      // causal mask, denominators, and P [V; 1]
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        const int tok = tok0 + 32 * nt + col;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = 32 * kt + acc_row(i, half);
-          const float x = key <= tok ? kap[nt][i] : 0.f;
-          kap[nt][i] = x;
-          den[nt] += x;
-        }
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-          float x[8];
-#pragma unroll
-          for (int j = 0; j < 8; ++j) x[j] = kap[nt][8 * s2 + j];
-          const bf16x8 pb = pack8(x);
-          const int key0 = 32 * kt + 16 * s2 + 4 * half;
-#pragma unroll
-          for (int mt = 0; mt < 2; ++mt) {
-            const __bf16* vr = s_vt + (size_t)(32 * mt + col) * Cfg::VS;
-            const uint2 lo = *reinterpret_cast<const uint2*>(vr + key0);
-            const uint2 hi = *reinterpret_cast<const uint2*>(vr + key0 + 8);
-            uint4 pk = make_uint4(lo.x, lo.y, hi.x, hi.y);
-            const bf16x8 av = *reinterpret_cast<const bf16x8*>(&pk);
-            acc[mt][nt] = mfma32(av, pb, acc[mt][nt]);
+          for (int j = 0; j < 8; j += 2) {
+            const f16x2 hv = __builtin_convertvector((f32x2){bq[j] * bf(qv[j]), bq[j + 1] * bf(qv[j + 1])}, f16x2);
+            fb[nt][j] = hv[0];
+            fb[nt][j + 1] = hv[1];
           }
         }
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+          const f16x8 af = *reinterpret_cast<const f16x8*>(s_b0 + slab_off(ks, 32 * mt + col, half));
+          acc[mt][0] = mfma32h(af, fb[0], acc[mt][0]);
+          acc[mt][1] = mfma32h(af, fb[1], acc[mt][1]);
+        }
       }
     }
-  }
-
-  // ================= inter-chunk numerator: main K loop ======================
-  __syncthreads();   // the slab buffers reuse the k / v^T staging area
-  const uint8_t* tsrc = ws_tile + ((size_t)unit * n_chunks + chunk) * tile::BYTES;
-  constexpr int NST = Cfg::SLAB_BYTES / (256 * 16);   // 16-byte pieces per thread per slab
-  uint4 stage[NST];
-  auto load_slab = [&](int s) {
+    int hs = 1;
+    for (int c = 0; c < 4; ++c) {
+      if (COMPUTE) {
+        // q_t of this lane's 8 t's of block c, times qt_scale, as fp16
 #pragma unroll
-    for (int i = 0; i < NST; ++i) {
-      const int piece = tid + 256 * i;                // 16-byte piece within the slab
-      const int ks = s * Cfg::SK + (piece >> 7);
-      stage[i] = ks < tile::NKS ? reinterpret_cast<const uint4*>(tsrc)[(size_t)s * Cfg::SK * 128 + piece]
-                                : make_uint4(0, 0, 0, 0);
+        for (int nt = 0; nt < 2; ++nt) {
+          const bf16x8 qv = *reinterpret_cast<const bf16x8*>((nt ? qrow1 : qrow0).chunk(2 * c + half));
+#pragma unroll
+          for (int j = 0; j < 8; j += 2) {
+            const f16x2 hv = __builtin_convertvector((f32x2){bf(qv[j]) * qt_scale, bf(qv[j + 1]) * qt_scale}, f16x2);
+            qt[nt][j] = hv[0];
+            qt[nt][j + 1] = hv[1];
+          }
+        }
+        cur = -1;
+      }
+      for (int h = 0; h < 4 * (c + 1); h += 4, hs += 4) {
+        wait_vmcnt<4>();
+        barrier_nofence();
+        issue(hs + 3, s_b0);
+        if (COMPUTE) quad(c, h, s_b1);
+        wait_vmcnt<4>();
+        barrier_nofence();
+        issue(hs + 4, s_b1);
+        if (COMPUTE) quad(c, h + 1, s_b2);
+        wait_vmcnt<4>();
+        barrier_nofence();
+        issue(hs + 5, s_b2);
+        if (COMPUTE) quad(c, h + 2, s_b3);
+        wait_vmcnt<4>();
+        barrier_nofence();
+        issue(hs + 6, s_b3);
+        if (COMPUTE) quad(c, h + 3, s_b0);
+      }
     }
+    wait_vmcnt<0>();   // the last (repeated) prefetches
   };
-  auto store_slab = [&](int buf) {
-    uint8_t* base = s_u + buf * Cfg::SLAB_BYTES;
-#pragma unroll
-    for (int i = 0; i < NST; ++i) {
-      const int piece = tid + 256 * i;
-      const int kk = piece >> 7, w = (piece >> 1) & 63, h = piece & 1;
-      *reinterpret_cast<uint4*>(base + slab_off(kk, w, h)) = stage[i];
-    }
-  };
-  load_slab(0);
-  store_slab(0);
-  __syncthreads();
+  if (head_ok)
+    main_loop(bool_t<true>{});
+  else
+    main_loop(bool_t<false>{});
 
-  const int32_t* gmap = reinterpret_cast<const int32_t*>(rec) + OAL_COEF_GMAP;   // g(r), uniform
-  const float* mgw = s_mg + hslot * 2 * LDIM * DH;
-  const __bf16* qrow0 = qw + (size_t)(tok0 + col) * Cfg::QS;        // token of N-tile 0
-  const __bf16* qrow1 = qw + (size_t)(tok0 + 32 + col) * Cfg::QS;   // token of N-tile 1
-  float qt0[8], qt1[8];   // q_t of this lane's 8 t's of the current t-block (c)
-  float qh0[8], qh1[8];   // qhat[t] = m q_t M_{g(r), g(t)} / d_h for the current (g(r), m)
-  int cur_c = -1, cur_key = -1;
-
-  for (int s = 0; s < Cfg::NSLAB; ++s) {
-    const int buf = s & 1;
-    if (s + 1 < Cfg::NSLAB) load_slab(s + 1);
-    if (head_ok) {
-      const uint8_t* sb = s_u + buf * Cfg::SLAB_BYTES;
-      // Two half-slabs of 4 K-steps.  A new t-block starts at K-step 4 + 8 c (c + 1),
-      // i.e. always at a half-slab boundary, and the 4 r's of a half-slab are the
-      // consecutive, 4-aligned values r0 .. r0 + 3.
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const int ks0 = s * Cfg::SK + 4 * hh;
-        if (ks0 >= tile::NKS) break;
-        if (ks0 < tile::NKS_LIN) {
-          // linear rows (slab 0, first half): phi = b'_r q_r, r = 16 ks + 8 half + j
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int ks = ks0 + i;
-            float b8[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) b8[j] = rec[OAL_COEF_BP + 16 * ks + 8 * half + j];
-            const bf16x8 q0 = *reinterpret_cast<const bf16x8*>(qrow0 + 16 * ks + 8 * half);
-            const bf16x8 q1 = *reinterpret_cast<const bf16x8*>(qrow1 + 16 * ks + 8 * half);
-            float x0[8], x1[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-              x0[j] = b8[j] * bf(q0[j]);
-              x1[j] = b8[j] * bf(q1[j]);
-            }
-            const bf16x8 b0 = pack8(x0), b1 = pack8(x1);
-#pragma unroll
-            for (int mt = 0; mt < 2; ++mt) {
-              const bf16x8 af = *reinterpret_cast<const bf16x8*>(sb + slab_off(4 * hh + i, 32 * mt + col, half));
-              acc[mt][0] = mfma32(af, b0, acc[mt][0]);
-              acc[mt][1] = mfma32(af, b1, acc[mt][1]);
-            }
-          }
-          continue;
-        }
-        const int c = tile::ks_block(ks0);
-        const int r0 = ks0 - tile::quad_base(c);
-        if (c != cur_c) {
-          cur_c = c;
-          cur_key = -1;
-          const bf16x8 q0 = *reinterpret_cast<const bf16x8*>(qrow0 + 16 * c + 8 * half);
-          const bf16x8 q1 = *reinterpret_cast<const bf16x8*>(qrow1 + 16 * c + 8 * half);
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            qt0[j] = bf(q0[j]);
-            qt1[j] = bf(q1[j]);
-          }
-        }
-        // q_r for r0 .. r0 + 3 of both tokens (one 8-byte read each)
-        const uint2 qa = *reinterpret_cast<const uint2*>(qrow0 + r0);
-        const uint2 qb = *reinterpret_cast<const uint2*>(qrow1 + r0);
-        const float qr0[4] = {__uint_as_float(qa.x << 16), __uint_as_float(qa.x & 0xffff0000u),
-                              __uint_as_float(qa.y << 16), __uint_as_float(qa.y & 0xffff0000u)};
-        const float qr1[4] = {__uint_as_float(qb.x << 16), __uint_as_float(qb.x & 0xffff0000u),
-                              __uint_as_float(qb.y << 16), __uint_as_float(qb.y & 0xffff0000u)};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = r0 + i;
-          const int gam = __builtin_amdgcn_readfirstlane(gmap[r]);
-          const int key = 2 * gam + (r >= 16 * c ? 0 : 1);     // (group, multiplicity)
-          if (key != cur_key) {
-            cur_key = key;
-            const float4* mrow = reinterpret_cast<const float4*>(
-                mgw + ((key & 1) * LDIM + gam) * DH + 16 * c + 8 * half);
-            const float4 ma = mrow[0], mb = mrow[1];
-            const float m8[8] = {ma.x, ma.y, ma.z, ma.w, mb.x, mb.y, mb.z, mb.w};
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-              qh0[j] = qt0[j] * m8[j];
-              qh1[j] = qt1[j] * m8[j];
-            }
-          }
-          // quadratic rows of item (r, c): phi = q_r * qhat[t]
-          float x0[8], x1[8];
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            x0[j] = qr0[i] * qh0[j];
-            x1[j] = qr1[i] * qh1[j];
-          }
-          const bf16x8 b0 = pack8(x0), b1 = pack8(x1);
-#pragma unroll
-          for (int mt = 0; mt < 2; ++mt) {
-            const bf16x8 af = *reinterpret_cast<const bf16x8*>(sb + slab_off(4 * hh + i, 32 * mt + col, half));
-            acc[mt][0] = mfma32(af, b0, acc[mt][0]);
-            acc[mt][1] = mfma32(af, b1, acc[mt][1]);
-          }
-        }
-      }
-    }
-    if (s + 1 < Cfg::NSLAB) store_slab(buf ^ 1);
-    __syncthreads();
-  }
-
-  // ================= epilogue: + a H0, normalise, store ======================
+  // ================= epilogue: + a F H0, normalise, store ======================
   if (!head_ok) return;
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt) den[nt] += __shfl_xor(den[nt], 32, 64);
-  const float a = rec[OAL_COEF_A];
+  const float aF = rec[OAL_COEF_A] * F;
   const float* h0 = ts_side + tile::SIDE_H0;
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt) {
@@ -393,7 +636,7 @@ k_readout_mfma(int n_q_heads, int n_kv_heads, int seq_len, int n_chunks, int n_h
         const int w0 = 32 * mt + 8 * g4 + 4 * half;
         float o[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) o[e] = (acc[mt][nt][4 * g4 + e] + a * h0[w0 + e]) * inv;
+        for (int e = 0; e < 4; ++e) o[e] = (acc[mt][nt][4 * g4 + e] + aF * h0[w0 + e]) * inv;
 #pragma unroll
         for (int e = 0; e < 4; ++e) Elem<O>::store(yr, w0 + e, o[e]);
       }
@@ -419,11 +662,8 @@ static oal_status readout_launch(int batch, int n_q_heads, int n_kv_heads, int s
   const int n_uc = units * n_chunks;
   const long long blocks = 8LL * n_hg * ((n_uc + 7) / 8);
   auto kern = &k_readout_mfma<CH, O>;
-  if (hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, Cfg::LDS_BYTES) != hipSuccess)
-    return set_error(OAL_ERR_HIP, "k_readout_mfma: cannot reserve %d bytes of LDS", Cfg::LDS_BYTES);
   ProfScope ps("k_readout_mfma", stream);
-  hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(256), Cfg::LDS_BYTES, stream, n_q_heads,
+  hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(256), 0, stream, n_q_heads,
                      n_kv_heads, seq_len, n_chunks, n_hg, n_uc,
                      reinterpret_cast<const uint16_t*>(q), reinterpret_cast<const uint16_t*>(k),
                      reinterpret_cast<const uint16_t*>(v), reinterpret_cast<const float*>(coeffs), ts,

@@ -4,7 +4,7 @@
 // phi_k = [1, k_r, k_r k_t].  The readout of chunk c needs the exclusive prefix
 // H_{<c}; this kernel keeps the running prefix of a slice of feature rows in MFMA
 // accumulators (fp32) while it walks the chunks of a sequence segment, writes the
-// bf16 prefix tile of each chunk (layout in oal_tile.h) before adding the chunk,
+// fp16 prefix tile of each chunk (layout in oal_tile.h) before adding the chunk,
 // and adds each 16-token step as  D[(r,t)][w] += sum_tok (k_r k_t)[tok] v[tok][w]
 // (A = key products, built on the vector ALUs; B = V, exact bf16).
 //
@@ -25,6 +25,13 @@
 // cut into S segments:  pass 1 (sum mode) adds up every segment,  the scan forms
 // each segment's starting prefix (plus the caller's initial state) and the final
 // state,  pass 2 (prefix mode) replays each segment writing the per-chunk tiles.
+//
+// fp16 tiles need a scale: every entry of every prefix of a unit is bounded by
+//   B = max |H_init| + sum_j beta_j,   beta_j = max(|k_j|, |k_j|^2) |v_j|
+// (|.| the largest magnitude of a vector), since each entry of H1 and H2 is a sum
+// of k_r v_w or k_r k_t v_w over the tokens.  Pass 1 adds up beta per segment,
+// the scan takes max |H_init|, and pass 2 stores H * 2^-e_S with 2^(e_S + 15) > B,
+// so that no entry exceeds 2^15 (the fp16 limit is 65504).
 #include "oal_tile.h"
 
 namespace oal {
@@ -124,11 +131,34 @@ struct Stager {
   }
 };
 
-__device__ __forceinline__ uint2 pack4_bf16(float a, float b, float c, float d) {
+// Four fp32 accumulators times the tile scale s, as fp16 (round to nearest even).
+__device__ __forceinline__ uint2 pack4_f16(float a, float b, float c, float d, float s) {
+  const f16x2 lo = __builtin_convertvector((f32x2){a * s, b * s}, f16x2);
+  const f16x2 hi = __builtin_convertvector((f32x2){c * s, d * s}, f16x2);
   uint2 r;
-  r.x = (uint32_t)float_to_bf16_bits(a) | ((uint32_t)float_to_bf16_bits(b) << 16);
-  r.y = (uint32_t)float_to_bf16_bits(c) | ((uint32_t)float_to_bf16_bits(d) << 16);
+  r.x = __builtin_bit_cast(uint32_t, lo);
+  r.y = __builtin_bit_cast(uint32_t, hi);
   return r;
+}
+
+// Tile exponent e_S of a unit from the bound pieces (identical in every wave that
+// evaluates it: lane 0's sum order is fixed).  bound: [units] max |H_init| (as
+// float bits), then [units][n_seg] per-segment sums of beta.
+__device__ __forceinline__ int tile_scale_exp(const float* bound, int units, int n_seg, int unit,
+                                              int lane) {
+  float sum = 0.f;
+  for (int i = lane; i < n_seg; i += 64) sum += bound[units + (size_t)unit * n_seg + i];
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) sum += __shfl_xor(sum, o, 64);
+  sum = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(sum)));
+  const float B = bound[unit] + sum;
+  int e = 0;
+  if (B > 0.f) {
+    int ex;
+    frexpf(B, &ex);   // B < 2^ex
+    e = ex - 15;
+  }
+  return min(max(e, -40), 100);
 }
 
 }  // namespace
@@ -138,9 +168,12 @@ __global__ void __launch_bounds__(256, 2)
 k_state_mfma(int seq_len, int chunk, int n_chunks, int n_seg, int cps,
              const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
              float* __restrict__ segbuf,          // MODE 0: out sums; MODE 1: in prefixes
-             uint8_t* __restrict__ ts) {          // MODE 1: per-chunk prefix tiles
+             uint8_t* __restrict__ ts,            // MODE 1: per-chunk prefix tiles
+             float* __restrict__ bound,           // tile-scale bound (null: no tiles follow)
+             int units) {
   __shared__ __attribute__((aligned(16))) __bf16 s_kt[2][DH][st::TS];
   __shared__ __attribute__((aligned(16))) __bf16 s_vt[2][DV][st::TS];
+  __shared__ float s_bred[st::WAVES_PER_WG];
 
   const int g = blockIdx.x % st::NWG;
   const int seg = (blockIdx.x / st::NWG) % n_seg;
@@ -155,6 +188,9 @@ k_state_mfma(int seq_len, int chunk, int n_chunks, int n_seg, int cps,
   const int n_blocks = (tok_end - tok_begin + st::TB - 1) / st::TB;
   Stager sg{k, v, (size_t)unit * seq_len, tok_end, {}, {}};
   float* segslot = segbuf + ((size_t)unit * n_seg + seg) * st::UNIT_SEG_FLOATS;
+  // MODE 1: the tile scale 2^-e_S of this unit
+  const int e_s = MODE == 1 ? tile_scale_exp(bound, units, n_seg, unit, lane) : 0;
+  const float tscale = ldexpf(1.0f, -e_s);
 
   if (g < st::NWG - 1) {
     // ===================== quadratic rows (waves 0..23) =====================
@@ -191,8 +227,8 @@ k_state_mfma(int seq_len, int chunk, int n_chunks, int n_seg, int cps,
               if (cblk < (r >> 4)) continue;               // not in the tiled layout
               const int ks = tile::quad_base(cblk) + r;
               *reinterpret_cast<uint2*>(tl + (size_t)ks * 1024 + w * 16 + (t & 15)) =
-                  pack4_bf16(acc[m][nt][4 * gq], acc[m][nt][4 * gq + 1], acc[m][nt][4 * gq + 2],
-                             acc[m][nt][4 * gq + 3]);
+                  pack4_f16(acc[m][nt][4 * gq], acc[m][nt][4 * gq + 1], acc[m][nt][4 * gq + 2],
+                            acc[m][nt][4 * gq + 3], tscale);
             }
             asm volatile("" ::: "memory");   // keep the conversions next to their stores
           }
@@ -254,10 +290,26 @@ k_state_mfma(int seq_len, int chunk, int n_chunks, int n_seg, int cps,
     side_z1 = slot[(size_t)st::REG_Z1 * 64 + lane];
     side_z0 = slot[(size_t)st::REG_Z0 * 64];
   }
+  float beta_sum = 0.f;   // MODE 0 with tiles: sum of beta over this thread's tokens
   if (n_blocks > 0) sg.fetch(tok_begin, tid);
   for (int bi = 0; bi < n_blocks; ++bi) {
     const int t0 = tok_begin + bi * st::TB;
     const int buf = bi & 1;
+    if (MODE == 0 && bound != nullptr) {
+      // beta_j = max(|k_j|, |k_j|^2) |v_j|: each thread holds 8 dims of 2 tokens,
+      // the 8 threads of a token are consecutive lanes
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        float km = __uint_as_float(absmax8_bits(sg.pk[e]) << 16);
+        float vm = __uint_as_float(absmax8_bits(sg.pv[e]) << 16);
+#pragma unroll
+        for (int o = 1; o < 8; o <<= 1) {
+          km = fmaxf(km, __shfl_xor(km, o, 64));
+          vm = fmaxf(vm, __shfl_xor(vm, o, 64));
+        }
+        if ((tid & 7) == 0) beta_sum += fmaxf(km, km * km) * vm;
+      }
+    }
     sg.deposit(s_kt[buf], s_vt[buf], tid);
     if (MODE == 1 && worker && (t0 % chunk) == 0) {
       uint8_t* slotp = ts + ((size_t)unit * n_chunks + t0 / chunk) * tile::BYTES;
@@ -272,8 +324,8 @@ k_state_mfma(int seq_len, int chunk, int n_chunks, int n_seg, int cps,
           for (int gq = 0; gq < 4; ++gq) {
             const int r = 32 * m + 8 * gq + 4 * half;
             *reinterpret_cast<uint2*>(tl + (size_t)(r >> 4) * 1024 + w * 16 + (r & 15)) =
-                pack4_bf16(acc[m][nt][4 * gq], acc[m][nt][4 * gq + 1], acc[m][nt][4 * gq + 2],
-                           acc[m][nt][4 * gq + 3]);
+                pack4_f16(acc[m][nt][4 * gq], acc[m][nt][4 * gq + 1], acc[m][nt][4 * gq + 2],
+                          acc[m][nt][4 * gq + 3], tscale);
           }
           asm volatile("" ::: "memory");
         }
@@ -289,7 +341,10 @@ k_state_mfma(int seq_len, int chunk, int n_chunks, int n_seg, int cps,
         }
       side[tile::SIDE_H0 + lane] = side_h0;
       side[tile::SIDE_Z1 + lane] = side_z1;
-      if (lane == 0) side[tile::SIDE_Z0] = side_z0;
+      if (lane == 0) {
+        side[tile::SIDE_Z0] = side_z0;
+        side[tile::SIDE_SEXP] = (float)e_s;
+      }
     }
     __syncthreads();
     if (bi + 1 < n_blocks) sg.fetch(t0 + st::TB, tid);
@@ -324,6 +379,16 @@ k_state_mfma(int seq_len, int chunk, int n_chunks, int n_seg, int cps,
     }
     __syncthreads();
   }
+  if (MODE == 0 && bound != nullptr) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) beta_sum += __shfl_xor(beta_sum, o, 64);
+    if (lane == 0) s_bred[wv] = beta_sum;
+    __syncthreads();
+    if (tid == 0) {
+      bound[units + (size_t)unit * n_seg + seg] = (s_bred[0] + s_bred[1]) + (s_bred[2] + s_bred[3]);
+      if (seg == 0) bound[unit] = 0.f;   // max |H_init|, raised by the scan
+    }
+  }
   if (MODE == 0 && worker) {
 #pragma unroll
     for (int m = 0; m < 4; ++m)
@@ -341,15 +406,24 @@ k_state_mfma(int seq_len, int chunk, int n_chunks, int n_seg, int cps,
 // layout; optionally writes init + the total as the final state.
 __global__ void __launch_bounds__(256)
 k_state_segscan(int n_seg, float* __restrict__ segsum, float* __restrict__ segpre,
-                const float* __restrict__ state, int write_final) {
+                const float* __restrict__ state, int write_final, float* __restrict__ bound) {
   const int unit = blockIdx.y;
   const int e = blockIdx.x * blockDim.x + threadIdx.x;
-  if (e >= st::UNIT_SEG_FLOATS) return;
   const int omega = e / st::SLOT_FLOATS, reg = (e / 64) % st::SLOT_REGS, lane = e & 63;
   int f = 0, w = 0;
-  bool valid, primary;
-  state_elem(omega, reg, lane, f, w, valid, primary);
+  bool valid = false, primary;
+  if (e < st::UNIT_SEG_FLOATS) state_elem(omega, reg, lane, f, w, valid, primary);
   float run = (state && valid) ? state[(size_t)unit * STATE_FLOATS + (size_t)w * DS + f] : 0.f;
+  if (state && bound) {
+    // max |H_init| of the unit: wave maximum, one atomic per wave (non-negative
+    // floats order like their bit patterns)
+    float m = fabsf(run);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+    if ((threadIdx.x & 63) == 0 && m > 0.f)
+      atomicMax(reinterpret_cast<unsigned int*>(bound) + unit, __float_as_uint(m));
+  }
+  if (e >= st::UNIT_SEG_FLOATS) return;
   for (int s = 0; s < n_seg; ++s) {
     const size_t off = ((size_t)unit * n_seg + s) * st::UNIT_SEG_FLOATS + e;
     if (segpre) segpre[off] = run;
@@ -392,13 +466,16 @@ size_t state_mfma_workspace(int batch, int n_kv_heads, int seq_len, int chunk, b
   const int cps = (n_chunks + n_seg - 1) / n_seg;
   const int n_seg_eff = (n_chunks + cps - 1) / cps;
   size_t bytes = (with_tiles ? 2 : 1) * (size_t)units * n_seg_eff * st::UNIT_SEG_FLOATS * sizeof(float);
-  if (with_tiles) bytes += (size_t)units * n_chunks * tile::BYTES;
+  if (with_tiles) {
+    bytes += (size_t)units * n_chunks * tile::BYTES;
+    bytes += ((size_t)units * (n_seg_eff + 1) * sizeof(float) + 255) / 256 * 256;   // scale bound
+  }
   return bytes;
 }
 
 // Builds the per-chunk prefix tiles (when ts != null) and the final state (when
 // state != null; its content on entry is the initial state).  ws: the scratch part
-// of state_mfma_workspace (segment sums, then segment prefixes).
+// of state_mfma_workspace (segment sums, then segment prefixes and the scale bound).
 oal_status launch_state_mfma(int batch, int n_kv_heads, int seq_len, int chunk, const void* k,
                              const void* v, float* state, uint8_t* ts, void* ws,
                              hipStream_t stream) {
@@ -412,10 +489,11 @@ oal_status launch_state_mfma(int batch, int n_kv_heads, int seq_len, int chunk, 
   const dim3 grid(units * n_seg_eff * st::NWG);
   float* segsum = reinterpret_cast<float*>(ws);
   float* segpre = segsum + (size_t)units * n_seg_eff * st::UNIT_SEG_FLOATS;
+  float* bound = ts ? segpre + (size_t)units * n_seg_eff * st::UNIT_SEG_FLOATS : nullptr;
   {
     ProfScope ps("k_state_seg", stream);
     hipLaunchKernelGGL(k_state_mfma<0>, grid, dim3(256), 0, stream, seq_len, chunk, n_chunks,
-                       n_seg_eff, cps, kk, vv, segsum, (uint8_t*)nullptr);
+                       n_seg_eff, cps, kk, vv, segsum, (uint8_t*)nullptr, bound, units);
     oal_status s = check_launch("k_state_seg");
     if (s != OAL_OK) return s;
   }
@@ -423,7 +501,7 @@ oal_status launch_state_mfma(int batch, int n_kv_heads, int seq_len, int chunk, 
     ProfScope ps("k_state_segscan", stream);
     hipLaunchKernelGGL(k_state_segscan, dim3((st::UNIT_SEG_FLOATS + 255) / 256, units), dim3(256),
                        0, stream, n_seg_eff, segsum, ts ? segpre : (float*)nullptr,
-                       (const float*)state, state != nullptr ? 1 : 0);
+                       (const float*)state, state != nullptr ? 1 : 0, bound);
     oal_status s = check_launch("k_state_segscan");
     if (s != OAL_OK) return s;
   }
@@ -437,7 +515,7 @@ oal_status launch_state_mfma(int batch, int n_kv_heads, int seq_len, int chunk, 
   if (ts == nullptr) return OAL_OK;
   ProfScope ps("k_state_mfma", stream);
   hipLaunchKernelGGL(k_state_mfma<1>, grid, dim3(256), 0, stream, seq_len, chunk, n_chunks,
-                     n_seg_eff, cps, kk, vv, segpre, ts);
+                     n_seg_eff, cps, kk, vv, segpre, ts, bound, units);
   return check_launch("k_state_mfma");
 }
 

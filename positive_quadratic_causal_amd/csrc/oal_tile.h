@@ -3,7 +3,7 @@
 //
 // The readout of [OAL] Eq. 6 is a contraction over feature rows f of the state:
 //   u~^T[w][i] = sum_f H[f][w] phi_q(q_i)[f]
-// evaluated on v_mfma_f32_32x32x16_bf16 with the state as the A operand (rows w)
+// evaluated on v_mfma_f32_32x32x16_f16 with the state as the A operand (rows w)
 // and the query features as the B operand (columns = tokens).  The K dimension
 // (features) is cut into K-steps of 16 rows:
 //   K-steps 0..3         linear rows H1_r, r = 16 ks + j                (j = 0..15)
@@ -16,11 +16,16 @@
 // multiplicity one on the diagonal and two off it).  Every K-step has a single r,
 // so the query feature c_rt q_r q_t / d_h of a K-step is (m q_r) * qhat_{g(r)}[t]
 // with qhat_gamma[t] = q_t M_{gamma, g(t)} / d_h precomputed per 16-wide t-block.
-// Layout of one K-step: [w = 0..63][j = 0..15] bf16 (2 KB).
+// Layout of one K-step: [w = 0..63][j = 0..15] fp16 (2 KB).  The fp16 values are
+// H * 2^-e_S with one exponent e_S per (unit, call), chosen from a bound on |H|
+// (see oal_state_mfma.hip) so that every entry stays below 2^15; the readout
+// scales its query features and everything else it adds into the same
+// accumulators by powers of two, so the common factor cancels in y = u~/u~_65.
 //
 // The all-ones channel (denominator) is kept separately in fp32 "side" data:
 // H0 value channels, z1_r = sum k_r, z0 = token count, Z_rt = sum k_r k_t (full
 // 64 x 64); the denominator is a z0 + sum_r b'_r q_r z1_r + q^T (C/d_h o Z) q.
+// These side values are not scaled; side[SIDE_SEXP] holds e_S as a float.
 #pragma once
 
 #include "oal_common.h"
@@ -30,11 +35,12 @@ namespace tile {
 
 constexpr int NKS_LIN = 4;
 constexpr int NKS = 164;
-constexpr int KS_BYTES = 64 * 16 * 2;                  // one K-step, bf16
+constexpr int KS_BYTES = 64 * 16 * 2;                  // one K-step, fp16
 constexpr size_t TILE_BYTES = (size_t)NKS * KS_BYTES;  // 335872
 constexpr int SIDE_H0 = 0;       // [64] sum v (value channels of H0)
 constexpr int SIDE_Z1 = 64;      // [64] sum k_r
-constexpr int SIDE_Z0 = 128;     // token count (then padding to 192)
+constexpr int SIDE_Z0 = 128;     // token count
+constexpr int SIDE_SEXP = 129;   // e_S: the fp16 entries are H * 2^-e_S (then padding to 192)
 constexpr int SIDE_Z = 192;      // [64][64] sum k_r k_t
 constexpr int SIDE_FLOATS = SIDE_Z + DH * DH;           // 4288
 constexpr size_t BYTES = TILE_BYTES + (size_t)SIDE_FLOATS * 4;   // 353024 = 1379 * 256
@@ -67,6 +73,9 @@ __host__ __device__ inline bool canon_primary(int ks, int j) {
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 // D = A B + C on a 32x32x16 tile.  Lane layout (wave64):
 //   A[i][k]: lane = i + 32 (k / 8), element k % 8
@@ -74,6 +83,11 @@ typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
 //   D[i][j]: lane = j + 32 ((i / 4) % 2), register (i % 4) + 4 (i / 8)
 __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// The same tile shape with fp16 operands.
+__device__ __forceinline__ f32x16 mfma32h(const f16x8& a, const f16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 
 // Row of D held in register i by lane-half h.
@@ -94,5 +108,15 @@ __device__ __forceinline__ bf16x8 pack8(const float* x) {
 }
 
 __device__ __forceinline__ float bf(const __bf16 x) { return (float)x; }
+
+// Largest magnitude among 8 bf16 values, as bf16 magnitude bits (for
+// non-negative bf16 numbers the integer order is the numeric order).
+__device__ __forceinline__ uint32_t absmax8_bits(const uint4& x) {
+  const uint32_t a = x.x & 0x7fff7fffu, b = x.y & 0x7fff7fffu;
+  const uint32_t c = x.z & 0x7fff7fffu, d = x.w & 0x7fff7fffu;
+  const uint32_t m0 = max(max(a & 0xffffu, a >> 16), max(b & 0xffffu, b >> 16));
+  const uint32_t m1 = max(max(c & 0xffffu, c >> 16), max(d & 0xffffu, d >> 16));
+  return max(m0, m1);
+}
 
 }  // namespace oal

@@ -248,3 +248,56 @@ def test_prefill_long_32768_sampled_rows(oal, chunk):
     for h in (0, 6, 7, 13):
         ref = case.oracle_rows(0, h, rows)
         assert rel_l2(yc[0, h, rows], ref) <= tol_for(w), h
+
+
+# Powers of two: exact in bf16, so the oracle sees the same values scaled.
+SCALES = [(2.0 ** 8, 2.0 ** 4, 2.0 ** 10), (2.0 ** -10, 2.0 ** -6, 2.0 ** -12),
+          (1.0, 2.0 ** 6, 2.0 ** -8)]
+
+
+@pytest.mark.parametrize("sq,sk,sv", SCALES)
+def test_prefill_magnitude_range(oal, sq, sk, sv):
+    """bf16 inputs far from unit scale, continued from a state: the fp16 stages of
+    the matrix-core readout (state tiles, query features) are rescaled by powers
+    of two chosen from the data, which must not change the result."""
+    n1, n2 = 200, 150
+    w = synth.small_workload(305, "scale", 1, 4, 2, n1 + n2, "bf16")
+    announce(f"prefill magnitude range q*{sq} k*{sk} v*{sv}, {n1}+{n2} from a state")
+    case = Case(w)
+    case.q *= sq
+    case.k *= sk
+    case.v *= sv
+    coeffs = case.coeffs()
+    st = oal.oal_state_alloc(1, 2)
+    y1 = oal.oal_prefill(case.q[:, :, :n1].contiguous(), case.k[:, :, :n1].contiguous(),
+                         case.v[:, :, :n1].contiguous(), coeffs, chunk=64, state=st)
+    y2 = oal.oal_prefill(case.q[:, :, n1:].contiguous(), case.k[:, :, n1:].contiguous(),
+                         case.v[:, :, n1:].contiguous(), coeffs, chunk=128, state=st)
+    torch.cuda.synchronize()
+    y = torch.cat([y1, y2], dim=2).float().cpu().numpy()
+    assert np.all(np.isfinite(y))
+    for h in range(4):
+        q, k, v = case.head_qkv(0, h)
+        ref = O.causal_attention(q * sq, k * sk, v * sv, case.st.L[h].astype(np.float64),
+                                 case.st.group_map[h], int(case.st.n_groups[h]), w.eps)
+        assert rel_l2(y[0, h], ref) <= tol_for(w), h
+
+
+def test_prefill_many_outlier_dims(oal):
+    """Group maps with far more than 16 dims outside group 1: the intra-chunk
+    terms t_p, p >= 2, then run on the full 64-deep path."""
+    w = synth.small_workload(306, "wide", 1, 4, 2, 300, "bf16")
+    announce("prefill N=300 bf16, G=6 with ~53 dims in groups 2..6")
+    case = Case(w)
+    rng = np.random.default_rng(11)
+    for h in range(4):
+        case.st.n_groups[h] = 6
+        case.st.group_map[h] = rng.integers(1, 7, 64)
+        case.st.L[h] = synth.random_L(rng, 6)
+    case.n_groups = torch.from_numpy(case.st.n_groups.astype(np.int32)).to("cuda")
+    case.group_map = torch.from_numpy(case.st.group_map.astype(np.int32)).to("cuda")
+    case.L = torch.from_numpy(case.st.L.astype(np.float32)).to("cuda")
+    for chunk in (64, 128):
+        y = _prefill(oal, case, chunk)
+        torch.cuda.synchronize()
+        _check_heads(case, y, [(0, h) for h in range(4)], tol_for(w))
