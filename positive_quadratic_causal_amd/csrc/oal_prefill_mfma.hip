@@ -36,8 +36,8 @@ namespace oal {
 // can tell the state half-slab buffers (filled by direct-to-LDS loads that stay
 // in flight across iterations) from the q tile and the tables it reads
 // meanwhile.  Rows of 64 bf16 are 128 bytes with the 16-byte chunks XOR-swizzled
-// by (row & 7) instead of padded.  Before the inter-chunk loop the buffers hold
-// the chunk's k rows and v^T rows.
+// by row_key(row) instead of padded.  Before the inter-chunk loop the buffers
+// hold the chunk's k rows and v^T rows.
 // ---------------------------------------------------------------------------
 template <int CH>
 struct ReadoutCfg {
@@ -57,14 +57,22 @@ constexpr int L0 = LDIM * DH;           // [8]  L_{0,p} 2^(E/2)
 constexpr int ELLC = L0 + 8;            // [LDIM][16] ell_p at the compact dims, 2^(E/2)
 constexpr int CIDX = ELLC + LDIM * 16;  // [16] int: the dims with g(r) >= 2 (compact path)
 constexpr int BPF = CIDX + 16;          // [DH] b'_r F_f
-constexpr int FLOATS = BPF + DH;
+constexpr int BZ = BPF + DH;            // [DH] b'_r z1_r 2^-e_M (z1 of the chunk's prefix)
+constexpr int FLOATS = BZ + DH;
 }  // namespace htab
+
+// Swizzle key of a 128-byte LDS row: 16-byte chunk c of row r sits at slot
+// c ^ row_key(r).  Consecutive rows read by consecutive lanes then fall on
+// distinct banks whether the LDS serves 8, 16 or 32 lanes of a 16-byte read per
+// cycle (any 8 aligned consecutive rows, the 8 rows of one parity among 16, and
+// the 8 rows of one residue mod 4 among 32 have distinct keys).
+__device__ __forceinline__ int row_key(int r) { return (r ^ (r >> 3)) & 7; }
 
 // A row of 64 bf16 in a swizzled 128-byte LDS row.
 struct SwRow {
   const uint8_t* p;
-  int key;   // row & 7
-  __device__ __forceinline__ SwRow(const uint8_t* base, int row) : p(base + row * 128), key(row & 7) {}
+  int key;
+  __device__ __forceinline__ SwRow(const uint8_t* base, int row) : p(base + row * 128), key(row_key(row)) {}
   // 16-byte chunk c (elements 8 c .. 8 c + 7)
   __device__ __forceinline__ const uint8_t* chunk(int c) const { return p + ((c ^ key) << 4); }
   // element d
@@ -74,9 +82,11 @@ struct SwRow {
 };
 
 // Swizzled LDS offset of the 16-byte half-row (w, h) of a K-step inside a
-// half-slab (avoids bank conflicts between rows w and w + 4).
+// half-slab: the half is flipped by bit 2 ^ bit 3 ^ bit 4 of w, so that lanes
+// reading rows w = 0..31 hit distinct banks for 8, 16 or 32 lanes per cycle.
+__device__ __forceinline__ int slab_flip(int w) { return ((w >> 2) ^ (w >> 3) ^ (w >> 4)) & 1; }
 __device__ __forceinline__ int slab_off(int kk, int w, int h) {
-  return kk * tile::KS_BYTES + w * 32 + 16 * (h ^ ((w >> 2) & 1));
+  return kk * tile::KS_BYTES + w * 32 + 16 * (h ^ slab_flip(w));
 }
 
 __device__ __forceinline__ float wave_max(float x) {
@@ -206,8 +216,7 @@ k_readout_mfma(int n_q_heads, int n_kv_heads, int seq_len, int n_chunks, int n_h
       const size_t row = ((size_t)b * n_q_heads + kv * rep + hh) * seq_len + t0 + tok;
       val = reinterpret_cast<const uint4*>(q + row * DH)[part];
     }
-    const int qrow = hs * CH + tok;
-    *reinterpret_cast<uint4*>(s_q + qrow * 128 + ((part ^ (qrow & 7)) << 4)) = val;
+    *reinterpret_cast<uint4*>(s_q + (hs * CH + tok) * 128 + ((part ^ row_key(tok)) << 4)) = val;
     qmax[hs] = max(qmax[hs], absmax8_bits(val));
   }
   // ---- k, and v^T with the keys of each 16-block permuted: position 8h + 4a + e
@@ -220,7 +229,7 @@ k_readout_mfma(int n_q_heads, int n_kv_heads, int seq_len, int n_chunks, int n_h
       kk = reinterpret_cast<const uint4*>(k + (kvrow0 + tok) * DH)[part];
       vv = reinterpret_cast<const uint4*>(v + (kvrow0 + tok) * DV)[part];
     }
-    *reinterpret_cast<uint4*>(k_arr(tok >> 6) + (tok & 63) * 128 + ((part ^ (tok & 7)) << 4)) = kk;
+    *reinterpret_cast<uint4*>(k_arr(tok >> 6) + (tok & 63) * 128 + ((part ^ row_key(tok & 63)) << 4)) = kk;
     const int pos = (tok & ~15) | (((tok >> 2) & 1) << 3) | (((tok >> 3) & 1) << 2) | (tok & 3);
     uint8_t* va = v_arr(pos >> 6);
     const int pk = pos & 63;
@@ -228,7 +237,7 @@ k_readout_mfma(int n_q_heads, int n_kv_heads, int seq_len, int n_chunks, int n_h
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int w = part * 8 + e;
-      *reinterpret_cast<uint16_t*>(va + w * 128 + (((pk >> 3) ^ (w & 7)) << 4) + ((pk & 7) << 1)) = pv[e];
+      *reinterpret_cast<uint16_t*>(va + w * 128 + (((pk >> 3) ^ row_key(w)) << 4) + ((pk & 7) << 1)) = pv[e];
     }
   }
 
@@ -282,6 +291,7 @@ k_readout_mfma(int n_q_heads, int n_kv_heads, int seq_len, int n_chunks, int n_h
     for (int e = lane; e < LDIM * DH; e += 64) ht[htab::ELL + e] = rec[OAL_COEF_ELL + e] * sroot;
     if (lane < LDIM) ht[htab::L0 + lane] = rec[OAL_COEF_L + lane] * sroot;   // L_{0,p}
     ht[htab::BPF + lane] = rec[OAL_COEF_BP + lane] * Ff;
+    ht[htab::BZ + lane] = rec[OAL_COEF_BP + lane] * ts_side[tile::SIDE_Z1 + lane] * ldexpf(1.0f, -e_m);
     if (compact) {
       int* cidx = reinterpret_cast<int*>(ht + htab::CIDX);
       if (gl >= 2) {
@@ -442,7 +452,7 @@ k_readout_mfma(int n_q_heads, int n_kv_heads, int seq_len, int n_chunks, int n_h
   for (int i = 0; i < 2; ++i) {
     const int piece = wave * 2 + i;                 // 1 KB piece of the half-slab
     const int kk = piece >> 1, pos = (piece & 1) * 64 + lane;
-    const int w = pos >> 1, hh = (pos & 1) ^ ((w >> 2) & 1);
+    const int w = pos >> 1, hh = (pos & 1) ^ slab_flip(w);
     dma_off[i] = kk * tile::KS_BYTES + w * 32 + hh * 16;
   }
   const i32x4 tile_rsrc = buffer_rsrc(tsrc, (uint32_t)tile::TILE_BYTES);
@@ -456,24 +466,33 @@ k_readout_mfma(int n_q_heads, int n_kv_heads, int seq_len, int n_chunks, int n_h
   issue(1, s_b1);
   issue(2, s_b2);
 
-  // ---- inter-chunk denominator: a z0 + sum_r b'_r q_r z1_r + q^T (C / d_h o Z) q,
-  //      the quadratic part as T = (C/d_h o Z) q^T on the matrix cores
+  // ---- inter-chunk denominator: a z0 + sum_r q_r (b'_r z1_r + ((C / d_h o Z) q)_r),
+  //      T = b' o z1 + (C/d_h o Z) q^T on the matrix cores (the first term as the
+  //      accumulator seed); C/d_h from the head's M_{g(n),g(t)}/d_h 2^-e_M table
   if (head_ok) {
-    const float* cm = rec + OAL_COEF_CM;
     const float* Zs = ts_side + tile::SIDE_Z;
     float dd[2] = {0.f, 0.f};
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
-      f32x16 T[2] = {splat16(0.f), splat16(0.f)};
       const int n = 32 * mt + col;
+      const int gn = __shfl(gl, n, 64);   // g(n)
+      const _Float16* mrow = s_mg + (hslot * LDIM + gn) * DH + 8 * half;
+      f32x16 T[2];
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const float4 bz = *reinterpret_cast<const float4*>(ht + htab::BZ + 32 * mt + 8 * g4 + 4 * half);
+        T[0][4 * g4 + 0] = T[1][4 * g4 + 0] = bz.x;
+        T[0][4 * g4 + 1] = T[1][4 * g4 + 1] = bz.y;
+        T[0][4 * g4 + 2] = T[1][4 * g4 + 2] = bz.z;
+        T[0][4 * g4 + 3] = T[1][4 * g4 + 3] = bz.w;
+      }
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        float x[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int t = 16 * ks + 8 * half + j;
-          x[j] = cm[n * DH + t] * Zs[n * DH + t];
-        }
+        const float4 z0 = *reinterpret_cast<const float4*>(Zs + n * DH + 16 * ks + 8 * half);
+        const float4 z1 = *reinterpret_cast<const float4*>(Zs + n * DH + 16 * ks + 8 * half + 4);
+        const f16x8 m8 = *reinterpret_cast<const f16x8*>(mrow + 16 * ks);
+        const float x[8] = {z0.x * (float)m8[0], z0.y * (float)m8[1], z0.z * (float)m8[2], z0.w * (float)m8[3],
+                            z1.x * (float)m8[4], z1.y * (float)m8[5], z1.z * (float)m8[6], z1.w * (float)m8[7]};
         const bf16x8 az = pack8(x);
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) T[nt] = mfma32(az, qfrag(nt, ks), T[nt]);
@@ -483,21 +502,20 @@ k_readout_mfma(int n_q_heads, int n_kv_heads, int seq_len, int n_chunks, int n_h
         const SwRow& qr = nt ? qrow1 : qrow0;
         float d = 0.f;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) d = fmaf(bf(*qr.elem(32 * mt + acc_row(i, half))), T[nt][i], d);
+        for (int g4 = 0; g4 < 4; ++g4) {   // rows 32 mt + 8 g4 + 4 half + e, e = 0..3
+          const uint2 u = *reinterpret_cast<const uint2*>(qr.elem(32 * mt + 8 * g4 + 4 * half));
+          d = fmaf(__uint_as_float(u.x << 16), T[nt][4 * g4 + 0], d);
+          d = fmaf(__uint_as_float(u.x & 0xffff0000u), T[nt][4 * g4 + 1], d);
+          d = fmaf(__uint_as_float(u.y << 16), T[nt][4 * g4 + 2], d);
+          d = fmaf(__uint_as_float(u.y & 0xffff0000u), T[nt][4 * g4 + 3], d);
+        }
         dd[nt] += d;
       }
     }
-    const float a = rec[OAL_COEF_A];
-    const float* bp = rec + OAL_COEF_BP;
-    const float* z1 = ts_side + tile::SIDE_Z1;
+    const float az0 = half == 0 ? rec[OAL_COEF_A] * ts_side[tile::SIDE_Z0] : 0.f;
+    const float sc = ldexpf(F, e_m);
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      const SwRow& qr = nt ? qrow1 : qrow0;
-      float d = half == 0 ? a * ts_side[tile::SIDE_Z0] : 0.f;
-#pragma unroll 8
-      for (int r = 32 * half; r < 32 * half + 32; ++r) d = fmaf(bp[r] * bf(*qr.elem(r)), z1[r], d);
-      den[nt] += (dd[nt] + d) * F;
-    }
+    for (int nt = 0; nt < 2; ++nt) den[nt] += dd[nt] * sc + az0 * F;
   }
 
   // ---- main K loop over the 41 half-slabs: 1 linear, then 4 (c + 1) per t-block c;
@@ -508,6 +526,14 @@ k_readout_mfma(int n_q_heads, int n_kv_heads, int seq_len, int n_chunks, int n_h
   // one quadratic half-slab: K-steps (r0 + i, c), i = 0..3
   auto quad = [&](int c, int h, const uint8_t* sb) {
     const int r0 = 4 * h;
+    // the state fragments of all four K-steps first, so that their LDS latency
+    // overlaps the feature arithmetic below
+    f16x8 af[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+        af[i][mt] = *reinterpret_cast<const f16x8*>(sb + slab_off(i, 32 * mt + col, half));
     // m q_r of r0 .. r0 + 3 (m = 2 off the diagonal 16-block), scaled, as fp16
     const float qs = r0 < 16 * c ? 2.0f * qr_scale : qr_scale;
     _Float16 qr[2][4];
@@ -538,9 +564,8 @@ k_readout_mfma(int n_q_heads, int n_kv_heads, int seq_len, int n_chunks, int n_h
       const f16x8 f1 = qh[1] * qr[1][i];
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt) {
-        const f16x8 af = *reinterpret_cast<const f16x8*>(sb + slab_off(i, 32 * mt + col, half));
-        acc[mt][0] = mfma32h(af, f0, acc[mt][0]);
-        acc[mt][1] = mfma32h(af, f1, acc[mt][1]);
+        acc[mt][0] = mfma32h(af[i][mt], f0, acc[mt][0]);
+        acc[mt][1] = mfma32h(af[i][mt], f1, acc[mt][1]);
       }
     }
   };
