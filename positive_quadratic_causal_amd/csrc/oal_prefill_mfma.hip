@@ -61,13 +61,6 @@ constexpr int BZ = BPF + DH;            // [DH] b'_r z1_r 2^-e_M (z1 of the chun
 constexpr int FLOATS = BZ + DH;
 }  // namespace htab
 
-// Swizzle key of a 128-byte LDS row: 16-byte chunk c of row r sits at slot
-// c ^ row_key(r).  Consecutive rows read by consecutive lanes then fall on
-// distinct banks whether the LDS serves 8, 16 or 32 lanes of a 16-byte read per
-// cycle (any 8 aligned consecutive rows, the 8 rows of one parity among 16, and
-// the 8 rows of one residue mod 4 among 32 have distinct keys).
-__device__ __forceinline__ int row_key(int r) { return (r ^ (r >> 3)) & 7; }
-
 // A row of 64 bf16 in a swizzled 128-byte LDS row.
 struct SwRow {
   const uint8_t* p;

@@ -6,7 +6,8 @@
 // accumulators (fp32) while it walks the chunks of a sequence segment, writes the
 // fp16 prefix tile of each chunk (layout in oal_tile.h) before adding the chunk,
 // and adds each 16-token step as  D[(r,t)][w] += sum_tok (k_r k_t)[tok] v[tok][w]
-// (A = key products, built on the vector ALUs; B = V, exact bf16).
+// (A = key products in fp16, two per packed multiply; B = V in fp16; both scaled
+// by powers of two taken from the segment's largest |k| and |v|).
 //
 // Work decomposition per (batch, KV head) unit and segment: 25 waves.
 //   waves 0..7  : quadratic rows (r, t), r in 4w .. 4w+3,        t in 0..31
@@ -44,7 +45,6 @@ constexpr int SLOT_REGS = 132;          // registers per wave in the seg buffers
 constexpr int SLOT_FLOATS = SLOT_REGS * 64;
 constexpr int UNIT_SEG_FLOATS = NWAVES * SLOT_FLOATS;   // one (unit, segment)
 constexpr int TB = 64;                  // tokens staged per block
-constexpr int TS = TB + 8;              // bf16 row stride of the transposed tiles
 constexpr int REG_H0 = 128, REG_Z1 = 129, REG_Z0 = 130;
 }  // namespace st
 
@@ -90,8 +90,19 @@ __host__ __device__ inline void state_elem(int omega, int reg, int lane, int& f,
 
 namespace {
 
+// Byte offset of element `tok` (0..63) of transposed row d in a staged block:
+// each row holds the block's 64 tokens (128 bytes), its 16-byte chunks swizzled
+// by row_key(d) so that the lanes of every read and write hit distinct banks.
+__device__ __forceinline__ int st_off(int d, int tok) {
+  return d * 128 + (((tok >> 3) ^ row_key(d)) << 4) + ((tok & 7) << 1);
+}
+
 // Stage one block of TB tokens: global (token-major) -> registers -> LDS
-// (dimension-major).  Used by both workgroup kinds.
+// (dimension-major).  Thread t holds dims 8 (t & 7) .. + 7 of the tokens
+// 2 (t >> 3) and 2 (t >> 3) + 1, so that each LDS write stores both tokens of a
+// dim as one 32-bit word; the 8 threads of a token are consecutive lanes.  The
+// quadratic workgroups stage fp16 values times a power of two; the side
+// workgroup stages the raw bf16 bits.
 struct Stager {
   const uint16_t* k;
   const uint16_t* v;
@@ -99,11 +110,10 @@ struct Stager {
   int tok_end;
   uint4 pk[2], pv[2];
   __device__ void fetch(int t0, int tid) {
+    const int i = tid >> 3, part = tid & 7;
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
-      const int piece = tid + 256 * e;            // 512 pieces = 64 tokens x 8
-      const int tok = piece >> 3, part = piece & 7;
-      const int gt = t0 + tok;
+      const int gt = t0 + 2 * i + e;
       if (gt < tok_end) {
         pk[e] = reinterpret_cast<const uint4*>(k + (row0 + gt) * DH)[part];
         pv[e] = reinterpret_cast<const uint4*>(v + (row0 + gt) * DV)[part];
@@ -113,20 +123,30 @@ struct Stager {
       }
     }
   }
-  __device__ void deposit(__bf16 (*skt)[st::TS], __bf16 (*svt)[st::TS], int tid) {
+  // word of dim 2 j + hi of both tokens
+  static __device__ __forceinline__ uint32_t bf16_pair(uint32_t w0, uint32_t w1, int hi) {
+    return hi ? (w0 >> 16) | (w1 & 0xffff0000u) : (w0 & 0xffffu) | (w1 << 16);
+  }
+  static __device__ __forceinline__ uint32_t f16_pair(uint32_t w0, uint32_t w1, int hi, float s) {
+    const float a = __uint_as_float(hi ? (w0 & 0xffff0000u) : (w0 << 16));
+    const float b = __uint_as_float(hi ? (w1 & 0xffff0000u) : (w1 << 16));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a * s, b * s}, f16x2));
+  }
+  template <bool F16>
+  __device__ void deposit(uint8_t* skt, uint8_t* svt, int tid, float ks, float vs) {
+    const int i = tid >> 3, part = tid & 7;
+    const uint32_t* a0 = reinterpret_cast<const uint32_t*>(&pk[0]);
+    const uint32_t* a1 = reinterpret_cast<const uint32_t*>(&pk[1]);
+    const uint32_t* b0 = reinterpret_cast<const uint32_t*>(&pv[0]);
+    const uint32_t* b1 = reinterpret_cast<const uint32_t*>(&pv[1]);
 #pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const int piece = tid + 256 * e;
-      const int tok = piece >> 3, part = piece & 7;
-      const uint16_t* a = reinterpret_cast<const uint16_t*>(&pk[e]);
-      const uint16_t* b = reinterpret_cast<const uint16_t*>(&pv[e]);
-      uint16_t* dk = reinterpret_cast<uint16_t*>(&skt[0][0]);
-      uint16_t* dv = reinterpret_cast<uint16_t*>(&svt[0][0]);
-#pragma unroll
-      for (int x = 0; x < 8; ++x) {
-        dk[(part * 8 + x) * st::TS + tok] = a[x];
-        dv[(part * 8 + x) * st::TS + tok] = b[x];
-      }
+    for (int x = 0; x < 8; ++x) {
+      const int d = part * 8 + x;
+      const int off = st_off(d, 2 * i);
+      const uint32_t wk = F16 ? f16_pair(a0[x >> 1], a1[x >> 1], x & 1, ks) : bf16_pair(a0[x >> 1], a1[x >> 1], x & 1);
+      const uint32_t wv = F16 ? f16_pair(b0[x >> 1], b1[x >> 1], x & 1, vs) : bf16_pair(b0[x >> 1], b1[x >> 1], x & 1);
+      *reinterpret_cast<uint32_t*>(skt + off) = wk;
+      *reinterpret_cast<uint32_t*>(svt + off) = wv;
     }
   }
 };
@@ -161,7 +181,62 @@ __device__ __forceinline__ int tile_scale_exp(const float* bound, int units, int
   return min(max(e, -40), 100);
 }
 
+// e with x < 2^e for x > 0; 0 otherwise.
+__device__ __forceinline__ int st_exp_above(float x) {
+  int e = 0;
+  if (x > 0.f) frexpf(x, &e);
+  return e;
+}
+
 }  // namespace
+
+// Largest |k| and |v| of each (unit, segment), as KVP partial maxima over
+// interleaved token ranges: the fp16 staging scales of the quadratic workgroups.
+// One workgroup per (segment, part, unit).
+constexpr int KVP = 8;
+__global__ void __launch_bounds__(256)
+k_state_kvmax(int seq_len, int chunk, int n_chunks, int cps, const uint16_t* __restrict__ k,
+              const uint16_t* __restrict__ v, float* __restrict__ kvmax) {
+  __shared__ uint32_t s_m[2][4];
+  const int seg = blockIdx.x / KVP, part = blockIdx.x % KVP, unit = blockIdx.y;
+  const int n_seg = gridDim.x / KVP;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int s_begin = seg * cps * chunk;
+  const int s_end = min(seq_len, min(n_chunks, (seg + 1) * cps) * chunk);
+  const int per = (s_end - s_begin + KVP - 1) / KVP;
+  const int t_begin = s_begin + part * per;
+  const int t_end = min(s_end, t_begin + per);
+  const size_t row0 = (size_t)unit * seq_len;
+  uint32_t mk = 0, mv = 0;
+  for (int p = tid; p < (t_end - t_begin) * 8; p += 256) {
+    const size_t row = row0 + t_begin + (p >> 3);
+    mk = max(mk, absmax8_bits(reinterpret_cast<const uint4*>(k + row * DH)[p & 7]));
+    mv = max(mv, absmax8_bits(reinterpret_cast<const uint4*>(v + row * DV)[p & 7]));
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    mk = max(mk, (uint32_t)__shfl_xor((int)mk, o, 64));
+    mv = max(mv, (uint32_t)__shfl_xor((int)mv, o, 64));
+  }
+  if (lane == 0) {
+    s_m[0][wv] = mk;
+    s_m[1][wv] = mv;
+  }
+  __syncthreads();
+  if (tid < 2) {
+    const uint32_t m = max(max(s_m[tid][0], s_m[tid][1]), max(s_m[tid][2], s_m[tid][3]));
+    kvmax[(((size_t)unit * n_seg + seg) * KVP + part) * 2 + tid] = __uint_as_float(m << 16);
+  }
+}
+
+// Largest |k| (which = 0) or |v| (which = 1) of a (unit, segment).
+__device__ __forceinline__ float seg_max(const float* kvmax, int unit, int n_seg, int seg, int which) {
+  const float* p = kvmax + ((size_t)unit * n_seg + seg) * KVP * 2 + which;
+  float m = 0.f;
+#pragma unroll
+  for (int i = 0; i < KVP; ++i) m = fmaxf(m, p[2 * i]);
+  return m;
+}
 
 template <int MODE>   // 0: segment sums, 1: per-chunk prefix tiles
 __global__ void __launch_bounds__(256, 2)
@@ -170,9 +245,10 @@ k_state_mfma(int seq_len, int chunk, int n_chunks, int n_seg, int cps,
              float* __restrict__ segbuf,          // MODE 0: out sums; MODE 1: in prefixes
              uint8_t* __restrict__ ts,            // MODE 1: per-chunk prefix tiles
              float* __restrict__ bound,           // tile-scale bound (null: no tiles follow)
+             const float* __restrict__ kvmax,     // per (unit, segment): max |k|, max |v|
              int units) {
-  __shared__ __attribute__((aligned(16))) __bf16 s_kt[2][DH][st::TS];
-  __shared__ __attribute__((aligned(16))) __bf16 s_vt[2][DV][st::TS];
+  __shared__ __attribute__((aligned(16))) uint8_t s_kt[2][DH * 128];
+  __shared__ __attribute__((aligned(16))) uint8_t s_vt[2][DV * 128];
   __shared__ float s_bred[st::WAVES_PER_WG];
 
   const int g = blockIdx.x % st::NWG;
@@ -194,23 +270,35 @@ k_state_mfma(int seq_len, int chunk, int n_chunks, int n_seg, int cps,
 
   if (g < st::NWG - 1) {
     // ===================== quadratic rows (waves 0..23) =====================
+    // Staged k and v are k 2^-e_k and v 2^-e_v in fp16 (|k| 2^-e_k < 128), so the
+    // accumulators hold the sums times 2^-(2 e_k + e_v).
+    const int e_k = st_exp_above(seg_max(kvmax, unit, n_seg, seg, 0)) - 7;
+    const int e_v = st_exp_above(seg_max(kvmax, unit, n_seg, seg, 1)) - 7;
+    const float ks = ldexpf(1.0f, -e_k), vs = ldexpf(1.0f, -e_v);
+    const float unscale = ldexpf(1.0f, 2 * e_k + e_v);
     const int omega = g * st::WAVES_PER_WG + wv;
     const int tb = omega < 8 ? 0 : 1;
     const int r0 = omega < 8 ? 4 * omega : 4 * (omega - 8);
     float* slot = segslot + (size_t)omega * st::SLOT_FLOATS;
     f32x16 acc[4][2];
+    const float rescale = ldexpf(1.0f, -(2 * e_k + e_v));
 #pragma unroll
     for (int m = 0; m < 4; ++m)
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
         for (int i = 0; i < 16; ++i)
-          acc[m][nt][i] = MODE == 1 ? slot[(size_t)((m * 2 + nt) * 16 + i) * 64 + lane] : 0.f;
-    if (n_blocks > 0) sg.fetch(tok_begin, tid);
+          acc[m][nt][i] = MODE == 1 ? slot[(size_t)((m * 2 + nt) * 16 + i) * 64 + lane] * rescale : 0.f;
+    const float wscale = unscale * tscale;   // accumulator -> tile entry
+    if (n_blocks > 0) {
+      sg.fetch(tok_begin, tid);
+      sg.deposit<true>(s_kt[0], s_vt[0], tid, ks, vs);
+    }
+    __syncthreads();
     for (int bi = 0; bi < n_blocks; ++bi) {
       const int t0 = tok_begin + bi * st::TB;
       const int buf = bi & 1;
-      sg.deposit(s_kt[buf], s_vt[buf], tid);
+      if (bi + 1 < n_blocks) sg.fetch(t0 + st::TB, tid);
       if (MODE == 1 && (t0 % chunk) == 0) {
         // the running prefix is chunk (t0 / chunk)'s exclusive prefix: store it
         uint16_t* tl = reinterpret_cast<uint16_t*>(ts + ((size_t)unit * n_chunks + t0 / chunk) * tile::BYTES);
@@ -225,41 +313,34 @@ k_state_mfma(int seq_len, int chunk, int n_chunks, int n_seg, int cps,
               const int t = 32 * tb + 8 * gq + 4 * half;   // rows t .. t+3
               const int cblk = t >> 4;
               if (cblk < (r >> 4)) continue;               // not in the tiled layout
-              const int ks = tile::quad_base(cblk) + r;
-              *reinterpret_cast<uint2*>(tl + (size_t)ks * 1024 + w * 16 + (t & 15)) =
+              const int ks_ = tile::quad_base(cblk) + r;
+              *reinterpret_cast<uint2*>(tl + (size_t)ks_ * 1024 + w * 16 + (t & 15)) =
                   pack4_f16(acc[m][nt][4 * gq], acc[m][nt][4 * gq + 1], acc[m][nt][4 * gq + 2],
-                            acc[m][nt][4 * gq + 3], tscale);
+                            acc[m][nt][4 * gq + 3], wscale);
             }
             asm volatile("" ::: "memory");   // keep the conversions next to their stores
           }
         }
       }
-      __syncthreads();
-      if (bi + 1 < n_blocks) sg.fetch(t0 + st::TB, tid);
+      const uint8_t* kt_ = s_kt[buf];
+      const uint8_t* vt_ = s_vt[buf];
 #pragma unroll
       for (int kk = 0; kk < st::TB / 16; ++kk) {
         const int tk = 16 * kk + 8 * half;     // this lane's 8 tokens inside the block
-        bf16x8 bv[2];
+        f16x8 bv[2];
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt)
-          bv[nt] = *reinterpret_cast<const bf16x8*>(&s_vt[buf][32 * nt + col][tk]);
-        float kt8[8];
-        {
-          const bf16x8 x = *reinterpret_cast<const bf16x8*>(&s_kt[buf][32 * tb + col][tk]);
-#pragma unroll
-          for (int j = 0; j < 8; ++j) kt8[j] = bf(x[j]);
-        }
+          bv[nt] = *reinterpret_cast<const f16x8*>(vt_ + st_off(32 * nt + col, tk));
+        const f16x8 kt8 = *reinterpret_cast<const f16x8*>(kt_ + st_off(32 * tb + col, tk));
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
-          const bf16x8 x = *reinterpret_cast<const bf16x8*>(&s_kt[buf][r0 + m][tk]);   // k_r, broadcast
-          float p[8];
+          const f16x8 kr = *reinterpret_cast<const f16x8*>(kt_ + st_off(r0 + m, tk));   // k_r, broadcast
+          const f16x8 af = kr * kt8;                                                     // k_r k_t
 #pragma unroll
-          for (int j = 0; j < 8; ++j) p[j] = bf(x[j]) * kt8[j];
-          const bf16x8 af = pack8(p);
-#pragma unroll
-          for (int nt = 0; nt < 2; ++nt) acc[m][nt] = mfma32(af, bv[nt], acc[m][nt]);
+          for (int nt = 0; nt < 2; ++nt) acc[m][nt] = mfma32h(af, bv[nt], acc[m][nt]);
         }
       }
+      if (bi + 1 < n_blocks) sg.deposit<true>(s_kt[buf ^ 1], s_vt[buf ^ 1], tid, ks, vs);
       __syncthreads();
     }
     if (MODE == 0) {
@@ -268,7 +349,8 @@ k_state_mfma(int seq_len, int chunk, int n_chunks, int n_seg, int cps,
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) slot[(size_t)((m * 2 + nt) * 16 + i) * 64 + lane] = acc[m][nt][i];
+          for (int i = 0; i < 16; ++i)
+            slot[(size_t)((m * 2 + nt) * 16 + i) * 64 + lane] = acc[m][nt][i] * unscale;
     }
     return;
   }
@@ -291,26 +373,30 @@ k_state_mfma(int seq_len, int chunk, int n_chunks, int n_seg, int cps,
     side_z0 = slot[(size_t)st::REG_Z0 * 64];
   }
   float beta_sum = 0.f;   // MODE 0 with tiles: sum of beta over this thread's tokens
-  if (n_blocks > 0) sg.fetch(tok_begin, tid);
+  // beta_j = max(|k_j|, |k_j|^2) |v_j| of the two staged tokens
+  auto add_beta = [&]() {
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      float km = __uint_as_float(absmax8_bits(sg.pk[e]) << 16);
+      float vm = __uint_as_float(absmax8_bits(sg.pv[e]) << 16);
+#pragma unroll
+      for (int o = 1; o < 8; o <<= 1) {
+        km = fmaxf(km, __shfl_xor(km, o, 64));
+        vm = fmaxf(vm, __shfl_xor(vm, o, 64));
+      }
+      if ((tid & 7) == 0) beta_sum += fmaxf(km, km * km) * vm;
+    }
+  };
+  if (n_blocks > 0) {
+    sg.fetch(tok_begin, tid);
+    if (MODE == 0 && bound != nullptr) add_beta();
+    sg.deposit<false>(s_kt[0], s_vt[0], tid, 1.f, 1.f);
+  }
+  __syncthreads();
   for (int bi = 0; bi < n_blocks; ++bi) {
     const int t0 = tok_begin + bi * st::TB;
     const int buf = bi & 1;
-    if (MODE == 0 && bound != nullptr) {
-      // beta_j = max(|k_j|, |k_j|^2) |v_j|: each thread holds 8 dims of 2 tokens,
-      // the 8 threads of a token are consecutive lanes
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        float km = __uint_as_float(absmax8_bits(sg.pk[e]) << 16);
-        float vm = __uint_as_float(absmax8_bits(sg.pv[e]) << 16);
-#pragma unroll
-        for (int o = 1; o < 8; o <<= 1) {
-          km = fmaxf(km, __shfl_xor(km, o, 64));
-          vm = fmaxf(vm, __shfl_xor(vm, o, 64));
-        }
-        if ((tid & 7) == 0) beta_sum += fmaxf(km, km * km) * vm;
-      }
-    }
-    sg.deposit(s_kt[buf], s_vt[buf], tid);
+    if (bi + 1 < n_blocks) sg.fetch(t0 + st::TB, tid);
     if (MODE == 1 && worker && (t0 % chunk) == 0) {
       uint8_t* slotp = ts + ((size_t)unit * n_chunks + t0 / chunk) * tile::BYTES;
       uint16_t* tl = reinterpret_cast<uint16_t*>(slotp);
@@ -346,15 +432,20 @@ k_state_mfma(int seq_len, int chunk, int n_chunks, int n_seg, int cps,
         side[tile::SIDE_SEXP] = (float)e_s;
       }
     }
-    __syncthreads();
-    if (bi + 1 < n_blocks) sg.fetch(t0 + st::TB, tid);
     if (worker) {
-      // H0 = sum v, z1 = sum k, z0 = count over this block
+      const uint8_t* kt_ = s_kt[buf];
+      const uint8_t* vt_ = s_vt[buf];
+      // H0 = sum v, z1 = sum k, z0 = count over this block (row `lane`)
       float sh = 0.f, sz = 0.f;
-#pragma unroll 8
-      for (int x = 0; x < st::TB; ++x) {
-        sh += bf(s_vt[buf][lane][x]);
-        sz += bf(s_kt[buf][lane][x]);
+#pragma unroll
+      for (int c = 0; c < st::TB / 8; ++c) {
+        const bf16x8 xv = *reinterpret_cast<const bf16x8*>(vt_ + st_off(lane, 8 * c));
+        const bf16x8 xk = *reinterpret_cast<const bf16x8*>(kt_ + st_off(lane, 8 * c));
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          sh += bf(xv[j]);
+          sz += bf(xk[j]);
+        }
       }
       side_h0 += sh;
       side_z1 += sz;
@@ -365,8 +456,8 @@ k_state_mfma(int seq_len, int chunk, int n_chunks, int n_seg, int cps,
         bf16x8 ak[2], bv[2];
 #pragma unroll
         for (int x = 0; x < 2; ++x) {
-          ak[x] = *reinterpret_cast<const bf16x8*>(&s_kt[buf][32 * x + col][tk]);
-          bv[x] = *reinterpret_cast<const bf16x8*>(&s_vt[buf][32 * x + col][tk]);
+          ak[x] = *reinterpret_cast<const bf16x8*>(kt_ + st_off(32 * x + col, tk));
+          bv[x] = *reinterpret_cast<const bf16x8*>(vt_ + st_off(32 * x + col, tk));
         }
 #pragma unroll
         for (int m = 0; m < 2; ++m)
@@ -376,6 +467,10 @@ k_state_mfma(int seq_len, int chunk, int n_chunks, int n_seg, int cps,
             acc[2 + m][nt] = mfma32(ak[m], ak[nt], acc[2 + m][nt]); // Z  += K^T K
           }
       }
+    }
+    if (bi + 1 < n_blocks) {
+      if (MODE == 0 && bound != nullptr) add_beta();
+      sg.deposit<false>(s_kt[buf ^ 1], s_vt[buf ^ 1], tid, 1.f, 1.f);
     }
     __syncthreads();
   }
@@ -403,35 +498,51 @@ k_state_mfma(int seq_len, int chunk, int n_chunks, int n_seg, int cps,
 }
 
 // Exclusive prefix over segments (plus the initial state), in the accumulator
-// layout; optionally writes init + the total as the final state.
+// layout; optionally writes init + the total as the final state.  Four
+// consecutive elements (same wave slot and register, lanes 4 j .. 4 j + 3) per
+// thread.
 __global__ void __launch_bounds__(256)
 k_state_segscan(int n_seg, float* __restrict__ segsum, float* __restrict__ segpre,
                 const float* __restrict__ state, int write_final, float* __restrict__ bound) {
   const int unit = blockIdx.y;
-  const int e = blockIdx.x * blockDim.x + threadIdx.x;
-  const int omega = e / st::SLOT_FLOATS, reg = (e / 64) % st::SLOT_REGS, lane = e & 63;
-  int f = 0, w = 0;
-  bool valid = false, primary;
-  if (e < st::UNIT_SEG_FLOATS) state_elem(omega, reg, lane, f, w, valid, primary);
-  float run = (state && valid) ? state[(size_t)unit * STATE_FLOATS + (size_t)w * DS + f] : 0.f;
+  const int e0 = 4 * (blockIdx.x * blockDim.x + threadIdx.x);
+  const bool in = e0 < st::UNIT_SEG_FLOATS;
+  float run[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int e = e0 + j;
+    const int omega = e / st::SLOT_FLOATS, reg = (e / 64) % st::SLOT_REGS, lane = e & 63;
+    int f = 0, w = 0;
+    bool valid = false, primary;
+    if (in) state_elem(omega, reg, lane, f, w, valid, primary);
+    run[j] = (state && valid) ? state[(size_t)unit * STATE_FLOATS + (size_t)w * DS + f] : 0.f;
+  }
   if (state && bound) {
     // max |H_init| of the unit: wave maximum, one atomic per wave (non-negative
     // floats order like their bit patterns)
-    float m = fabsf(run);
+    float m = fmaxf(fmaxf(fabsf(run[0]), fabsf(run[1])), fmaxf(fabsf(run[2]), fabsf(run[3])));
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
     if ((threadIdx.x & 63) == 0 && m > 0.f)
       atomicMax(reinterpret_cast<unsigned int*>(bound) + unit, __float_as_uint(m));
   }
-  if (e >= st::UNIT_SEG_FLOATS) return;
+  if (!in) return;
+  float4 r = make_float4(run[0], run[1], run[2], run[3]);
+  const size_t base = (size_t)unit * n_seg * st::UNIT_SEG_FLOATS + e0;
   for (int s = 0; s < n_seg; ++s) {
-    const size_t off = ((size_t)unit * n_seg + s) * st::UNIT_SEG_FLOATS + e;
-    if (segpre) segpre[off] = run;
-    if (segsum) run += segsum[off];
+    const size_t off = base + (size_t)s * st::UNIT_SEG_FLOATS;
+    if (segpre) *reinterpret_cast<float4*>(segpre + off) = r;
+    if (segsum) {
+      const float4 a = *reinterpret_cast<const float4*>(segsum + off);
+      r.x += a.x;
+      r.y += a.y;
+      r.z += a.z;
+      r.w += a.w;
+    }
   }
   // the final value goes through segment 0's slot (no longer read): mirrored
   // elements of other threads may still read the initial state here
-  if (write_final) segsum[(size_t)unit * n_seg * st::UNIT_SEG_FLOATS + e] = run;
+  if (write_final) *reinterpret_cast<float4*>(segsum + base) = r;
 }
 
 // Final state (canonical layout) from the totals left in segment 0's slot.
@@ -452,11 +563,16 @@ k_state_final(int n_seg, const float* __restrict__ segsum, float* __restrict__ s
 // ---------------------------------------------------------------------------
 
 static int choose_segments(int units, int n_chunks) {
-  // aim for >= ~2 workgroups per CU on 256 CUs
-  int s = (512 + units * st::NWG - 1) / (units * st::NWG);
+  // as many segments as fit in one round of 2 workgroups per CU on 256 CUs: a
+  // few workgroups more than the slots would add a second round of equal length
+  int s = 512 / (units * st::NWG);
   if (s < 1) s = 1;
   if (s > n_chunks) s = n_chunks;
   return s;
+}
+
+static size_t kvmax_bytes(int units, int n_seg) {
+  return ((size_t)units * n_seg * KVP * 2 * sizeof(float) + 255) / 256 * 256;
 }
 
 size_t state_mfma_workspace(int batch, int n_kv_heads, int seq_len, int chunk, bool with_tiles) {
@@ -466,6 +582,7 @@ size_t state_mfma_workspace(int batch, int n_kv_heads, int seq_len, int chunk, b
   const int cps = (n_chunks + n_seg - 1) / n_seg;
   const int n_seg_eff = (n_chunks + cps - 1) / cps;
   size_t bytes = (with_tiles ? 2 : 1) * (size_t)units * n_seg_eff * st::UNIT_SEG_FLOATS * sizeof(float);
+  bytes += kvmax_bytes(units, n_seg_eff);
   if (with_tiles) {
     bytes += (size_t)units * n_chunks * tile::BYTES;
     bytes += ((size_t)units * (n_seg_eff + 1) * sizeof(float) + 255) / 256 * 256;   // scale bound
@@ -475,7 +592,8 @@ size_t state_mfma_workspace(int batch, int n_kv_heads, int seq_len, int chunk, b
 
 // Builds the per-chunk prefix tiles (when ts != null) and the final state (when
 // state != null; its content on entry is the initial state).  ws: the scratch part
-// of state_mfma_workspace (segment sums, then segment prefixes and the scale bound).
+// of state_mfma_workspace (segment sums, the segments' max |k| and |v|, then the
+// segment prefixes and the tile-scale bound).
 oal_status launch_state_mfma(int batch, int n_kv_heads, int seq_len, int chunk, const void* k,
                              const void* v, float* state, uint8_t* ts, void* ws,
                              hipStream_t stream) {
@@ -488,18 +606,27 @@ oal_status launch_state_mfma(int batch, int n_kv_heads, int seq_len, int chunk, 
   const uint16_t* vv = reinterpret_cast<const uint16_t*>(v);
   const dim3 grid(units * n_seg_eff * st::NWG);
   float* segsum = reinterpret_cast<float*>(ws);
-  float* segpre = segsum + (size_t)units * n_seg_eff * st::UNIT_SEG_FLOATS;
+  float* kvmax = segsum + (size_t)units * n_seg_eff * st::UNIT_SEG_FLOATS;
+  float* segpre = kvmax + kvmax_bytes(units, n_seg_eff) / sizeof(float);
   float* bound = ts ? segpre + (size_t)units * n_seg_eff * st::UNIT_SEG_FLOATS : nullptr;
+  {
+    ProfScope ps("k_state_kvmax", stream);
+    hipLaunchKernelGGL(k_state_kvmax, dim3(n_seg_eff * KVP, units), dim3(256), 0, stream, seq_len, chunk,
+                       n_chunks, cps, kk, vv, kvmax);
+    oal_status s = check_launch("k_state_kvmax");
+    if (s != OAL_OK) return s;
+  }
   {
     ProfScope ps("k_state_seg", stream);
     hipLaunchKernelGGL(k_state_mfma<0>, grid, dim3(256), 0, stream, seq_len, chunk, n_chunks,
-                       n_seg_eff, cps, kk, vv, segsum, (uint8_t*)nullptr, bound, units);
+                       n_seg_eff, cps, kk, vv, segsum, (uint8_t*)nullptr, bound, (const float*)kvmax,
+                       units);
     oal_status s = check_launch("k_state_seg");
     if (s != OAL_OK) return s;
   }
   {
     ProfScope ps("k_state_segscan", stream);
-    hipLaunchKernelGGL(k_state_segscan, dim3((st::UNIT_SEG_FLOATS + 255) / 256, units), dim3(256),
+    hipLaunchKernelGGL(k_state_segscan, dim3((st::UNIT_SEG_FLOATS / 4 + 255) / 256, units), dim3(256),
                        0, stream, n_seg_eff, segsum, ts ? segpre : (float*)nullptr,
                        (const float*)state, state != nullptr ? 1 : 0, bound);
     oal_status s = check_launch("k_state_segscan");
@@ -515,7 +642,7 @@ oal_status launch_state_mfma(int batch, int n_kv_heads, int seq_len, int chunk, 
   if (ts == nullptr) return OAL_OK;
   ProfScope ps("k_state_mfma", stream);
   hipLaunchKernelGGL(k_state_mfma<1>, grid, dim3(256), 0, stream, seq_len, chunk, n_chunks,
-                     n_seg_eff, cps, kk, vv, segpre, ts, bound, units);
+                     n_seg_eff, cps, kk, vv, segpre, ts, bound, (const float*)kvmax, units);
   return check_launch("k_state_mfma");
 }
 

@@ -109,6 +109,13 @@ __device__ __forceinline__ bf16x8 pack8(const float* x) {
 
 __device__ __forceinline__ float bf(const __bf16 x) { return (float)x; }
 
+// Swizzle key of a 128-byte LDS row: 16-byte chunk c of row r sits at slot
+// c ^ row_key(r).  Consecutive rows read by consecutive lanes then fall on
+// distinct banks whether the LDS serves 8, 16 or 32 lanes of a 16-byte read per
+// cycle (any 8 aligned consecutive rows, the 8 rows of one parity among 16, and
+// the 8 rows of one residue mod 4 among 32 have distinct keys).
+__device__ __forceinline__ int row_key(int r) { return (r ^ (r >> 3)) & 7; }
+
 // Largest magnitude among 8 bf16 values, as bf16 magnitude bits (for
 // non-negative bf16 numbers the integer order is the numeric order).
 __device__ __forceinline__ uint32_t absmax8_bits(const uint4& x) {
