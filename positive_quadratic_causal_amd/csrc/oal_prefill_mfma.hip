@@ -195,59 +195,94 @@ k_readout_mfma(int n_q_heads, int n_kv_heads, int seq_len, int n_chunks, int n_h
   const uint8_t* tsrc = ws_tile + ((size_t)unit * n_chunks + chunk) * tile::BYTES;
   const float* ts_side = reinterpret_cast<const float*>(tsrc + tile::TILE_BYTES);
 
-  // ---- stage q (all heads of the group), keeping each thread's max |q| per head
+  // ---- prologue loads, all issued before any of them is used (bounds by
+  //      clamping the address and zeroing the value afterwards): q of all heads
+  //      of the group, k and v of the chunk, and this wave's coefficients
+  constexpr int QIT = Cfg::HPW * CH * 8 / 256;   // 16-byte q pieces per thread
+  constexpr int KIT = CH / 64;                   // token pairs per thread
+  uint4 qv[QIT];
+#pragma unroll
+  for (int it = 0; it < QIT; ++it) {
+    const int hs = it * 256 / (CH * 8);          // compile-time after unrolling
+    const int rem = tid + 256 * it - hs * CH * 8, tok = rem >> 3, part = rem & 7;
+    const int hh = min(hg * Cfg::HPW + hs, rep - 1);
+    const size_t row = ((size_t)b * n_q_heads + kv * rep + hh) * seq_len + t0 + min(tok, clen - 1);
+    qv[it] = reinterpret_cast<const uint4*>(q + row * DH)[part];
+  }
+  // k and v: thread t holds dims 8 (t & 7) .. + 7 of the tokens 64 it + 2 (t >> 3) + e
+  const size_t kvrow0 = (size_t)unit * seq_len + t0;
+  const int kpart = tid & 7, kpair = tid >> 3;
+  uint4 kq[KIT][2], vq[KIT][2];
+#pragma unroll
+  for (int it = 0; it < KIT; ++it)
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const size_t row = kvrow0 + min(64 * it + 2 * kpair + e, clen - 1);
+      kq[it][e] = reinterpret_cast<const uint4*>(k + row * DH)[kpart];
+      vq[it][e] = reinterpret_cast<const uint4*>(v + row * DV)[kpart];
+    }
+  const float mval = rec[OAL_COEF_M + min(lane, LDIM * LDIM - 1)];
+  const float bval = rec[OAL_COEF_BP + lane];
+  const int gl = reinterpret_cast<const int32_t*>(rec)[OAL_COEF_GMAP + lane];   // g(r), lane r
+  float mgv[LDIM], ellv[LDIM];
+#pragma unroll
+  for (int p = 0; p < LDIM; ++p) {
+    mgv[p] = rec[OAL_COEF_MG + p * DH + lane];
+    ellv[p] = rec[OAL_COEF_ELL + p * DH + lane];
+  }
+  const float l0v = rec[OAL_COEF_L + min(lane, LDIM - 1)];   // L_{0,lane}
+  const float z1v = ts_side[tile::SIDE_Z1 + lane];
+  const float esv = ts_side[tile::SIDE_SEXP];
+
+  // ---- q tile, with each thread's max |q| per head
   uint32_t qmax[Cfg::HPW];
 #pragma unroll
   for (int hs = 0; hs < Cfg::HPW; ++hs) qmax[hs] = 0;
 #pragma unroll
-  for (int it = 0; it < Cfg::HPW * CH * 8 / 256; ++it) {
-    const int hs = it * 256 / (CH * 8);          // compile-time after unrolling
+  for (int it = 0; it < QIT; ++it) {
+    const int hs = it * 256 / (CH * 8);
     const int rem = tid + 256 * it - hs * CH * 8, tok = rem >> 3, part = rem & 7;
-    const int hh = hg * Cfg::HPW + hs;
-    uint4 val = make_uint4(0, 0, 0, 0);
-    if (hh < rep && tok < clen) {
-      const size_t row = ((size_t)b * n_q_heads + kv * rep + hh) * seq_len + t0 + tok;
-      val = reinterpret_cast<const uint4*>(q + row * DH)[part];
-    }
+    const bool ok = hg * Cfg::HPW + hs < rep && tok < clen;
+    const uint4 val = ok ? qv[it] : make_uint4(0, 0, 0, 0);
     *reinterpret_cast<uint4*>(s_q + (hs * CH + tok) * 128 + ((part ^ row_key(tok)) << 4)) = val;
     qmax[hs] = max(qmax[hs], absmax8_bits(val));
   }
-  // ---- k, and v^T with the keys of each 16-block permuted: position 8h + 4a + e
-  //      holds key 8a + 4h + e (the key order of the kappa accumulator rows)
-  const size_t kvrow0 = (size_t)unit * seq_len + t0;
-  for (int i = tid; i < CH * 8; i += 256) {
-    const int tok = i >> 3, part = i & 7;
-    uint4 kk = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
-    if (tok < clen) {
-      kk = reinterpret_cast<const uint4*>(k + (kvrow0 + tok) * DH)[part];
-      vv = reinterpret_cast<const uint4*>(v + (kvrow0 + tok) * DV)[part];
-    }
-    *reinterpret_cast<uint4*>(k_arr(tok >> 6) + (tok & 63) * 128 + ((part ^ row_key(tok & 63)) << 4)) = kk;
+  // ---- k rows, and v^T rows with the keys of each 16-block permuted: position
+  //      8h + 4a + e holds key 8a + 4h + e (the key order of the kappa accumulator
+  //      rows); the two tokens of a thread are adjacent there (one 32-bit write)
+#pragma unroll
+  for (int it = 0; it < KIT; ++it) {
+    const int tok = 64 * it + 2 * kpair;       // even; tok + 1 is the pair's second token
+    const bool ok0 = tok < clen, ok1 = tok + 1 < clen;
+    const uint4 k0 = ok0 ? kq[it][0] : make_uint4(0, 0, 0, 0);
+    const uint4 k1 = ok1 ? kq[it][1] : make_uint4(0, 0, 0, 0);
+    const uint4 v0 = ok0 ? vq[it][0] : make_uint4(0, 0, 0, 0);
+    const uint4 v1 = ok1 ? vq[it][1] : make_uint4(0, 0, 0, 0);
+    uint8_t* ka = k_arr(tok >> 6);
+    *reinterpret_cast<uint4*>(ka + (tok & 63) * 128 + ((kpart ^ row_key(tok & 63)) << 4)) = k0;
+    *reinterpret_cast<uint4*>(ka + ((tok + 1) & 63) * 128 + ((kpart ^ row_key((tok + 1) & 63)) << 4)) = k1;
     const int pos = (tok & ~15) | (((tok >> 2) & 1) << 3) | (((tok >> 3) & 1) << 2) | (tok & 3);
     uint8_t* va = v_arr(pos >> 6);
     const int pk = pos & 63;
-    const uint16_t* pv = reinterpret_cast<const uint16_t*>(&vv);
+    const uint32_t* a0 = reinterpret_cast<const uint32_t*>(&v0);
+    const uint32_t* a1 = reinterpret_cast<const uint32_t*>(&v1);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int w = part * 8 + e;
-      *reinterpret_cast<uint16_t*>(va + w * 128 + (((pk >> 3) ^ row_key(w)) << 4) + ((pk & 7) << 1)) = pv[e];
+    for (int x = 0; x < 8; ++x) {
+      const int w = kpart * 8 + x;
+      const uint32_t word = (x & 1) ? (a0[x >> 1] >> 16) | (a1[x >> 1] & 0xffff0000u)
+                                    : (a0[x >> 1] & 0xffffu) | (a1[x >> 1] << 16);
+      *reinterpret_cast<uint32_t*>(va + w * 128 + (((pk >> 3) ^ row_key(w)) << 4) + ((pk & 7) << 1)) = word;
     }
   }
 
-  // ---- this head's coefficient magnitudes (wave-uniform) and group map (lane r)
-  float mn = 0.f, bn = 0.f;
-  int gl = 1;
-  if (head_ok) {
-    mn = lane < LDIM * LDIM ? fabsf(rec[OAL_COEF_M + lane]) * (1.0f / DH) : 0.f;
-    bn = fabsf(rec[OAL_COEF_BP + lane]);
-    gl = reinterpret_cast<const int32_t*>(rec)[OAL_COEF_GMAP + lane];
-  }
-  const int e_m = exp_above(wave_max(mn));
-  const int e_b = exp_above(wave_max(bn));
+  // ---- this head's coefficient magnitudes (wave-uniform)
+  const int e_m = exp_above(wave_max(lane < LDIM * LDIM ? fabsf(mval) * (1.0f / DH) : 0.f));
+  const int e_b = exp_above(wave_max(fabsf(bval)));
   if (head_ok && sub == 0) {   // fp16 table M_{gamma,g(t)} / d_h 2^-e_M of the head
     _Float16* mg = s_mg + hslot * LDIM * DH;
     const float sc = ldexpf(1.0f, -e_m);
-    for (int e = lane; e < LDIM * DH; e += 64) mg[e] = (_Float16)(rec[OAL_COEF_MG + e] * sc);
+#pragma unroll
+    for (int p = 0; p < LDIM; ++p) mg[p * DH + lane] = (_Float16)(mgv[p] * sc);
   }
 #pragma unroll
   for (int hs = 0; hs < Cfg::HPW; ++hs) {
@@ -260,7 +295,7 @@ k_readout_mfma(int n_q_heads, int n_kv_heads, int seq_len, int n_chunks, int n_h
   const float qm = fmaxf(fmaxf(s_red[0 * 4 + hslot], s_red[1 * 4 + hslot]),
                          fmaxf(s_red[2 * 4 + hslot], s_red[3 * 4 + hslot]));
   const int e_q = exp_above(qm);
-  const int e_s = (int)ts_side[tile::SIDE_SEXP];
+  const int e_s = (int)esv;
   int xs = max(0, e_b - e_q - e_m - 3);
   int E = -e_s + 12 - 2 * e_q - e_m - xs;
   if (E & 1) {   // even, so that sqrt(F) is a power of two as well
@@ -281,21 +316,23 @@ k_readout_mfma(int n_q_heads, int n_kv_heads, int seq_len, int n_chunks, int n_h
   const int n_out = __popcll(cmask);
   const bool compact = n_out <= 16;            // t_p, p >= 2, from one 16-deep K-step
   if (head_ok) {
-    for (int e = lane; e < LDIM * DH; e += 64) ht[htab::ELL + e] = rec[OAL_COEF_ELL + e] * sroot;
-    if (lane < LDIM) ht[htab::L0 + lane] = rec[OAL_COEF_L + lane] * sroot;   // L_{0,p}
-    ht[htab::BPF + lane] = rec[OAL_COEF_BP + lane] * Ff;
-    ht[htab::BZ + lane] = rec[OAL_COEF_BP + lane] * ts_side[tile::SIDE_Z1 + lane] * ldexpf(1.0f, -e_m);
+#pragma unroll
+    for (int p = 0; p < LDIM; ++p) ht[htab::ELL + p * DH + lane] = ellv[p] * sroot;
+    if (lane < LDIM) ht[htab::L0 + lane] = l0v * sroot;
+    ht[htab::BPF + lane] = bval * Ff;
+    ht[htab::BZ + lane] = bval * z1v * ldexpf(1.0f, -e_m);
     if (compact) {
       int* cidx = reinterpret_cast<int*>(ht + htab::CIDX);
       if (gl >= 2) {
         const int rank = __builtin_amdgcn_mbcnt_hi((uint32_t)(cmask >> 32),
                                                    __builtin_amdgcn_mbcnt_lo((uint32_t)cmask, 0));
         cidx[rank] = lane;
-        for (int p = 0; p < LDIM; ++p)
-          ht[htab::ELLC + p * 16 + rank] = rec[OAL_COEF_ELL + p * DH + lane] * sroot;
+#pragma unroll
+        for (int p = 0; p < LDIM; ++p) ht[htab::ELLC + p * 16 + rank] = ellv[p] * sroot;
       }
       if (lane >= n_out && lane < 16) {
         cidx[lane] = 0;
+#pragma unroll
         for (int p = 0; p < LDIM; ++p) ht[htab::ELLC + p * 16 + lane] = 0.f;
       }
     }
