@@ -54,9 +54,10 @@ struct ReadoutCfg {
 namespace htab {
 constexpr int ELL = 0;                  // [LDIM][DH] ell_p[r] 2^(E/2)
 constexpr int L0 = LDIM * DH;           // [8]  L_{0,p} 2^(E/2)
-constexpr int ELLC = L0 + 8;            // [LDIM][16] ell_p at the compact dims, 2^(E/2)
+constexpr int ELLC = L0 + 8;            // [LDIM][16] (ell_p - c_p) at the compact dims, 2^(E/2)
 constexpr int CIDX = ELLC + LDIM * 16;  // [16] int: the dims with g(r) >= 2 (compact path)
-constexpr int BPF = CIDX + 16;          // [DH] b'_r F_f
+constexpr int CP = CIDX + 16;           // [8] c_p = L_{1,p} / sqrt(d_h) (ell_p on group 1), 2^(E/2)
+constexpr int BPF = CP + 8;             // [DH] b'_r F_f
 constexpr int BZ = BPF + DH;            // [DH] b'_r z1_r 2^-e_M (z1 of the chunk's prefix)
 constexpr int FLOATS = BZ + DH;
 }  // namespace htab
@@ -230,7 +231,8 @@ k_readout_mfma(int n_q_heads, int n_kv_heads, int seq_len, int n_chunks, int n_h
     mgv[p] = rec[OAL_COEF_MG + p * DH + lane];
     ellv[p] = rec[OAL_COEF_ELL + p * DH + lane];
   }
-  const float l0v = rec[OAL_COEF_L + min(lane, LDIM - 1)];   // L_{0,lane}
+  const float l0v = rec[OAL_COEF_L + min(lane, LDIM - 1)];           // L_{0,lane}
+  const float l1v = rec[OAL_COEF_L + LDIM + min(lane, LDIM - 1)];    // L_{1,lane}
   const float z1v = ts_side[tile::SIDE_Z1 + lane];
   const float esv = ts_side[tile::SIDE_SEXP];
 
@@ -319,16 +321,21 @@ k_readout_mfma(int n_q_heads, int n_kv_heads, int seq_len, int n_chunks, int n_h
 #pragma unroll
     for (int p = 0; p < LDIM; ++p) ht[htab::ELL + p * DH + lane] = ellv[p] * sroot;
     if (lane < LDIM) ht[htab::L0 + lane] = l0v * sroot;
+    if (lane < LDIM) ht[htab::CP + lane] = l1v * (0.125f * sroot);
     ht[htab::BPF + lane] = bval * Ff;
     ht[htab::BZ + lane] = bval * z1v * ldexpf(1.0f, -e_m);
     if (compact) {
       int* cidx = reinterpret_cast<int*>(ht + htab::CIDX);
+      float c1[LDIM];   // L_{1,p} / sqrt(d_h), read across lanes before the branch below
+#pragma unroll
+      for (int p = 0; p < LDIM; ++p) c1[p] = __shfl(l1v, p, 64) * 0.125f;
       if (gl >= 2) {
         const int rank = __builtin_amdgcn_mbcnt_hi((uint32_t)(cmask >> 32),
                                                    __builtin_amdgcn_mbcnt_lo((uint32_t)cmask, 0));
         cidx[rank] = lane;
 #pragma unroll
-        for (int p = 0; p < LDIM; ++p) ht[htab::ELLC + p * 16 + rank] = ellv[p] * sroot;
+        for (int p = 0; p < LDIM; ++p)
+          ht[htab::ELLC + p * 16 + rank] = (ellv[p] - c1[p]) * sroot;
       }
       if (lane >= n_out && lane < 16) {
         cidx[lane] = 0;
@@ -354,19 +361,20 @@ k_readout_mfma(int n_q_heads, int n_kv_heads, int seq_len, int n_chunks, int n_h
     for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = splat16(0.f);
 
   // ================= intra-chunk part ======================================
-  // kappa^T[key][tok] F = eps F + sum_p (sqrt(F) (L_0p + sum_r ell_p[r] k_r q_r))^2 on
-  // the matrix cores (A = k o ell_p, B = q^T, the accumulator seeded with L_0p),
-  // causal mask, then u~^T += [V; 1]^T kappa^T (values on the matrix cores, the
-  // ones channel as column sums into the denominator).  ell_p is supported on the
-  // dims with g(r) >= p, so for p >= 2 only the outlier dims (g >= 2) contribute:
-  // when there are at most 16 of them they are gathered into one K-step.
+  // kappa^T[key][tok] F = eps F + sum_p t_p^2,  t_p = sqrt(F) (L_0p + sum_r ell_p[r] q_r k_r),
+  // then the causal mask and u~^T += [V; 1]^T kappa^T (values on the matrix cores,
+  // the ones channel as column sums into the denominator).  ell_p[r] = L_{g(r),p} /
+  // sqrt(d_h) equals c_p = L_{1,p} / sqrt(d_h) on group 1, so with S = q . k
+  //   t_p = sqrt(F) (L_0p + c_p S + sum_{g(r) >= 2} (ell_p[r] - c_p) q_r k_r);
+  // when at most 16 dims lie outside group 1 (compact), S is one 64-deep product of
+  // the raw inputs and each t_p one 16-deep product over the gathered outlier dims,
+  // seeded with L_0p + c_p S.  Otherwise each t_p is a 64-deep product with
+  // A = k o ell_p.
   if (head_ok) {
     const float epsF = rec[OAL_COEF_EPS] * F;
-    const bool use_c = compact && G >= 2;
-    const int p_full = use_c ? 1 : G;          // p = 0 .. p_full on the 64-deep path
     const int* cidx = reinterpret_cast<const int*>(ht + htab::CIDX) + 8 * half;
     bf16x8 qc[2];                              // compact q (B operand) of the wave's tokens
-    if (use_c) {
+    if (compact) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int d = cidx[j];
@@ -381,51 +389,68 @@ k_readout_mfma(int n_q_heads, int n_kv_heads, int seq_len, int n_chunks, int n_h
       constexpr bool MASK[2] = {decltype(mask0_t)::value, decltype(mask1_t)::value};
       f32x16 kap[2] = {splat16(epsF), splat16(epsF)};
       const SwRow krow(k_arr(kt >> 1), (32 * kt + col) & 63);
-      float kf[4][8];
+      bf16x8 kr[4];
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const bf16x8 x = *reinterpret_cast<const bf16x8*>(krow.chunk(2 * ks + half));
-#pragma unroll
-        for (int j = 0; j < 8; ++j) kf[ks][j] = bf(x[j]);
-      }
-      for (int p = 0; p <= p_full; ++p) {
-        const float* ell = ht + htab::ELL + p * DH + 8 * half;
-        bf16x8 ak[4];
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          const float4 e0 = *reinterpret_cast<const float4*>(ell + 16 * ks);
-          const float4 e1 = *reinterpret_cast<const float4*>(ell + 16 * ks + 4);
-          const float x[8] = {kf[ks][0] * e0.x, kf[ks][1] * e0.y, kf[ks][2] * e0.z, kf[ks][3] * e0.w,
-                              kf[ks][4] * e1.x, kf[ks][5] * e1.y, kf[ks][6] * e1.z, kf[ks][7] * e1.w};
-          ak[ks] = pack8(x);
-        }
-        const float l0 = ht[htab::L0 + p];
+      for (int ks = 0; ks < 4; ++ks) kr[ks] = *reinterpret_cast<const bf16x8*>(krow.chunk(2 * ks + half));
+      if (compact) {
+        f32x16 S[2];
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) {
           if (nt == 0 && !DO0) continue;
-          f32x16 sacc = splat16(l0);
+          S[nt] = splat16(0.f);
 #pragma unroll
-          for (int ks = 0; ks < 4; ++ks) sacc = mfma32(ak[ks], qfrag(nt, ks), sacc);
-#pragma unroll
-          for (int i = 0; i < 16; ++i) kap[nt][i] = fmaf(sacc[i], sacc[i], kap[nt][i]);
+          for (int ks = 0; ks < 4; ++ks) S[nt] = mfma32(kr[ks], qfrag(nt, ks), S[nt]);
         }
-      }
-      if (use_c) {
         float kc[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) kc[j] = bf(*krow.elem(cidx[j]));
-        for (int p = 2; p <= G; ++p) {
+        for (int p = 0; p <= G; ++p) {
           const float* ec = ht + htab::ELLC + p * 16 + 8 * half;
           const float4 e0 = *reinterpret_cast<const float4*>(ec);
           const float4 e1 = *reinterpret_cast<const float4*>(ec + 4);
           const float x[8] = {kc[0] * e0.x, kc[1] * e0.y, kc[2] * e0.z, kc[3] * e0.w,
                               kc[4] * e1.x, kc[5] * e1.y, kc[6] * e1.z, kc[7] * e1.w};
           const bf16x8 akc = pack8(x);
+          const float l0 = ht[htab::L0 + p], cp = ht[htab::CP + p];
+#pragma unroll
+          for (int nt = 0; nt < 2; ++nt) {
+            if (nt == 0 && !DO0) continue;
+            f32x16 seed;
+            if (p <= 1) {
+#pragma unroll
+              for (int i = 0; i < 16; ++i) seed[i] = fmaf(cp, S[nt][i], l0);
+            } else {
+              seed = splat16(l0);   // c_p = 0 for p >= 2 (L is lower triangular)
+            }
+            const f32x16 t = mfma32(akc, qc[nt], seed);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) kap[nt][i] = fmaf(t[i], t[i], kap[nt][i]);
+          }
+        }
+      } else {
+        float kf[4][8];
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+          for (int j = 0; j < 8; ++j) kf[ks][j] = bf(kr[ks][j]);
+        for (int p = 0; p <= G; ++p) {
+          const float* ell = ht + htab::ELL + p * DH + 8 * half;
+          bf16x8 ak[4];
+#pragma unroll
+          for (int ks = 0; ks < 4; ++ks) {
+            const float4 e0 = *reinterpret_cast<const float4*>(ell + 16 * ks);
+            const float4 e1 = *reinterpret_cast<const float4*>(ell + 16 * ks + 4);
+            const float x[8] = {kf[ks][0] * e0.x, kf[ks][1] * e0.y, kf[ks][2] * e0.z, kf[ks][3] * e0.w,
+                                kf[ks][4] * e1.x, kf[ks][5] * e1.y, kf[ks][6] * e1.z, kf[ks][7] * e1.w};
+            ak[ks] = pack8(x);
+          }
           const float l0 = ht[htab::L0 + p];
 #pragma unroll
           for (int nt = 0; nt < 2; ++nt) {
             if (nt == 0 && !DO0) continue;
-            const f32x16 sacc = mfma32(akc, qc[nt], splat16(l0));
+            f32x16 sacc = splat16(l0);
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) sacc = mfma32(ak[ks], qfrag(nt, ks), sacc);
 #pragma unroll
             for (int i = 0; i < 16; ++i) kap[nt][i] = fmaf(sacc[i], sacc[i], kap[nt][i]);
           }
