@@ -75,16 +75,13 @@ k_expand(int g_max, const int32_t* __restrict__ n_groups, const int32_t* __restr
     rec[OAL_COEF_M + tid] = sM[u][v];
     rec[OAL_COEF_L + tid] = sL[u][v];
   }
+  // C_rt / d_h over the full square, and with the multiplicity of the packed
+  // pair (r <= t) at pair_index(r, t)
   for (int i = tid; i < DH * DH; i += blockDim.x) {
-    int r = i / DH, t = i % DH;
-    rec[OAL_COEF_CM + i] = sM[sg[r]][sg[t]] * inv_d;
-  }
-  for (int r = 0; r < DH; ++r) {
-    // pairs (r, t), t >= r, occupy indices pair_index(r, r) .. + (63 - r)
-    for (int t = r + tid; t < DH; t += blockDim.x) {
-      float m = (r == t) ? 1.0f : 2.0f;
-      rec[OAL_COEF_CP + pair_index(r, t)] = m * sM[sg[r]][sg[t]] * inv_d;
-    }
+    const int r = i / DH, t = i % DH;
+    const float c = sM[sg[r]][sg[t]] * inv_d;
+    rec[OAL_COEF_CM + i] = c;
+    if (t >= r) rec[OAL_COEF_CP + pair_index(r, t)] = (r == t ? 1.0f : 2.0f) * c;
   }
 }
 
