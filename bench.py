@@ -10,9 +10,10 @@ Also reported: batched decode (Llama-3.2-1B-shaped 32/8, batch 64, state
 prefilled from 8192 tokens, 256 single-token steps; ``decode``), a chunk-size
 sweep, the linear-time check against N = 2048, the roofline of the dominant
 kernel of each path (algorithmic flops or bytes per launch over the launch's
-average duration, from HIP events recorded on the launch stream inside the timed
-region), and the float64 CPU oracle timed on a bounded sample of the prefill
-workload (``cpu_baseline``).
+average duration, from HIP events recorded on the launch stream around every
+launch of a second timed pass over the same steps: the events would widen the
+gaps between launches of the pass that gives ``value``), and the float64 CPU
+oracle timed on a bounded sample of the prefill workload (``cpu_baseline``).
 
 Inputs are synthetic (seeded generator in positive_quadratic_causal_amd.synth)
 and resident in HBM before the timed region starts.
@@ -118,17 +119,21 @@ def bench_prefill(oal, w, chunk, steps, warmup, device):
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    oal.oal_profile_reset()
-    oal.oal_profile_enable(True)
-    torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(steps):
         step()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    ms = (t1 - t0) * 1e3 / steps
+    # per-kernel durations: the same steps again with HIP events around every
+    # launch (kept out of the timed steps above, whose gaps the events would widen)
+    oal.oal_profile_reset()
+    oal.oal_profile_enable(True)
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
     oal.oal_profile_enable(False)
     kt = kernel_times(oal, ALL_KERNELS)
-    ms = (t1 - t0) * 1e3 / steps
     del ws, y, x
     state.free()
     torch.cuda.empty_cache()
@@ -190,16 +195,21 @@ def bench_decode(oal, w, reps, n_steps, device):
     rep_once()      # warmup
     torch.cuda.synchronize()
     total = 0.0
-    oal.oal_profile_reset()
     for _ in range(reps):
         oal.oal_state_copy(state, base)
         torch.cuda.synchronize()
-        oal.oal_profile_enable(True)
         t0 = time.perf_counter()
         rep_once()
         torch.cuda.synchronize()
         total += time.perf_counter() - t0
-        oal.oal_profile_enable(False)
+    # per-kernel durations from HIP events, in a separate pass over the same steps
+    oal.oal_profile_reset()
+    oal.oal_state_copy(state, base)
+    torch.cuda.synchronize()
+    oal.oal_profile_enable(True)
+    rep_once()
+    torch.cuda.synchronize()
+    oal.oal_profile_enable(False)
     kt = kernel_times(oal, ["k_decode"])
     ms_step = total * 1e3 / (reps * n_steps)
     units = w.batch * w.n_kv_heads
