@@ -64,6 +64,10 @@ template <typename T> struct Elem;
 template <> struct Elem<float> {
   static __device__ __forceinline__ float load(const float* p, size_t i) { return p[i]; }
   static __device__ __forceinline__ void store(float* p, size_t i, float x) { p[i] = x; }
+  // four consecutive elements, i a multiple of 4
+  static __device__ __forceinline__ void store4(float* p, size_t i, const float* x) {
+    *reinterpret_cast<float4*>(p + i) = make_float4(x[0], x[1], x[2], x[3]);
+  }
 };
 template <> struct Elem<uint16_t> {  // bf16 stored as raw bits
   static __device__ __forceinline__ float load(const uint16_t* p, size_t i) {
@@ -71,6 +75,12 @@ template <> struct Elem<uint16_t> {  // bf16 stored as raw bits
   }
   static __device__ __forceinline__ void store(uint16_t* p, size_t i, float x) {
     p[i] = float_to_bf16_bits(x);
+  }
+  static __device__ __forceinline__ void store4(uint16_t* p, size_t i, const float* x) {
+    uint2 w;
+    w.x = (uint32_t)float_to_bf16_bits(x[0]) | ((uint32_t)float_to_bf16_bits(x[1]) << 16);
+    w.y = (uint32_t)float_to_bf16_bits(x[2]) | ((uint32_t)float_to_bf16_bits(x[3]) << 16);
+    *reinterpret_cast<uint2*>(p + i) = w;
   }
 };
 

@@ -714,11 +714,10 @@ k_readout_mfma(int n_q_heads, int n_kv_heads, int seq_len, int n_chunks, int n_h
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         const int w0 = 32 * mt + 8 * g4 + 4 * half;
-        float o[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) o[e] = (acc[mt][nt][4 * g4 + e] + aF * h0[w0 + e]) * inv;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) Elem<O>::store(yr, w0 + e, o[e]);
+        const float4 hv = *reinterpret_cast<const float4*>(h0 + w0);
+        const float o[4] = {(acc[mt][nt][4 * g4 + 0] + aF * hv.x) * inv, (acc[mt][nt][4 * g4 + 1] + aF * hv.y) * inv,
+                            (acc[mt][nt][4 * g4 + 2] + aF * hv.z) * inv, (acc[mt][nt][4 * g4 + 3] + aF * hv.w) * inv};
+        Elem<O>::store4(yr, w0, o);
       }
   }
 }
