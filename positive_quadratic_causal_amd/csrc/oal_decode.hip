@@ -68,20 +68,35 @@ k_decode(int n_q_heads, int n_kv_heads, int head0, int nh, int update,
     }
     phik[f] = pk;
   }
+  // query features of every head: the coefficient of feature f (a, b'_r or the
+  // packed c'_rt) comes from the head's record; all of a thread's coefficient
+  // loads are issued before the first is used
+  constexpr int FIT = (DS + 255) / 256;   // features per thread
 #pragma unroll
   for (int hh = 0; hh < HG; ++hh) {
     if (hh >= nh) break;
     const float* rec = coef_rec(coeffs, kv * rep + head0 + hh);
+    float cf[FIT];
+#pragma unroll
+    for (int i = 0; i < FIT; ++i) {
+      const int f = tid + 256 * i;
+      // record offset of feature f's coefficient: A, BP + r, CP + pair (f < DCAN)
+      const int off = f == 0 ? OAL_COEF_A : f <= DH ? OAL_COEF_BP + f - 1 : OAL_COEF_CP + min(f, DCAN - 1) - 1 - DH;
+      cf[i] = rec[off];
+    }
     float* phiq = reinterpret_cast<float*>(s_phiq4[hh]);
-    for (int f = tid; f < DS; f += blockDim.x) {
+#pragma unroll
+    for (int i = 0; i < FIT; ++i) {
+      const int f = tid + 256 * i;
+      if (f >= DS) break;
       float pq;
       if (f == 0) {
-        pq = rec[OAL_COEF_A];
+        pq = cf[i];
       } else if (f <= DH) {
-        pq = rec[OAL_COEF_BP + f - 1] * s_q[hh][f - 1];
+        pq = cf[i] * s_q[hh][f - 1];
       } else if (f < DCAN) {
-        uint16_t rt = c_dec_pairs.rt[f - 1 - DH];
-        pq = rec[OAL_COEF_CP + f - 1 - DH] * s_q[hh][rt >> 8] * s_q[hh][rt & 0xff];
+        const uint16_t rt = c_dec_pairs.rt[f - 1 - DH];
+        pq = cf[i] * s_q[hh][rt >> 8] * s_q[hh][rt & 0xff];
       } else {
         pq = 0.f;
       }
@@ -93,15 +108,25 @@ k_decode(int n_q_heads, int n_kv_heads, int head0, int nh, int update,
   constexpr int N4 = DS / 4;               // 544 float4 per column
   constexpr int IT = (N4 + 63) / 64;       // 9 iterations, the last one half full
   float4* st4 = reinterpret_cast<float4*>(state + (size_t)unit * STATE_FLOATS);
+  // columns col, col + 4, ..: the next column's loads are issued before the
+  // current one is processed (two columns in flight per wave)
+  float4 hn[IT];
+  auto load_col = [&](int c) {
+    const float4* src = st4 + (size_t)c * N4;
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      const int i4 = lane + 64 * it;
+      if (i4 < N4) hn[it] = src[i4];
+    }
+  };
+  if (wave < W) load_col(wave);
   for (int col = wave; col < W; col += 4) {
     float4* hc = st4 + (size_t)col * N4;
     const float uc = s_u[col];
     float4 hv[IT];
 #pragma unroll
-    for (int it = 0; it < IT; ++it) {
-      int i4 = lane + 64 * it;
-      if (i4 < N4) hv[it] = hc[i4];
-    }
+    for (int it = 0; it < IT; ++it) hv[it] = hn[it];
+    if (col + 4 < W) load_col(col + 4);
     float acc[HG];
 #pragma unroll
     for (int hh = 0; hh < HG; ++hh) acc[hh] = 0.f;
