@@ -140,6 +140,64 @@ def bench_prefill(oal, w, chunk, steps, warmup, device):
     return ms, kt
 
 
+# HBM traffic per launch of a kernel, from rocprofv3 FETCH_SIZE / WRITE_SIZE
+# counters scaled against a plain copy of known size (profiles/*_traffic.txt).
+# The figure is used only while the kernel's sources are unchanged since the
+# counters were taken (sha256 over the listed sources).
+TRAFFIC_FILES = {
+    "k_readout_mfma": ("profiles/k_readout_mfma_qwen14x2_n32768_c128_traffic.txt",
+                       ["positive_quadratic_causal_amd/csrc/oal_prefill_mfma.hip",
+                        "positive_quadratic_causal_amd/csrc/oal_tile.h",
+                        "positive_quadratic_causal_amd/csrc/oal_common.h"]),
+    "k_decode": ("profiles/k_decode_llama32x8_b64_traffic.txt",
+                 ["positive_quadratic_causal_amd/csrc/oal_decode.hip",
+                  "positive_quadratic_causal_amd/csrc/oal_common.h"]),
+}
+
+
+def sources_sha256(paths):
+    import hashlib
+    h = hashlib.sha256()
+    for rel in paths:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel):
+    """Bytes per launch from the kernel's traffic summary, or None when there is
+    none or the kernel's sources changed since it was taken."""
+    if kernel not in TRAFFIC_FILES:
+        return None
+    path, srcs = TRAFFIC_FILES[kernel]
+    try:
+        fields = {}
+        with open(os.path.join(ROOT, path)) as f:
+            for line in f:
+                if ":" in line and not line.startswith(" "):
+                    key, _, val = line.partition(":")
+                    fields[key.strip()] = val.strip()
+        if fields.get("source_sha256") != sources_sha256(srcs):
+            return None
+        return int(fields["traffic_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def copy_probe(mib):
+    """A plain device copy of known size (mib MiB read + mib MiB written, 5
+    times): the reference that scales the FETCH_SIZE / WRITE_SIZE counters of a
+    profiled run of this command."""
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"copy probe: {mib} MiB x 5")
+
+
 def roofline_prefill(kt, w, chunk):
     """Roofline of the prefill's dominant kernel (largest total time)."""
     prefill_kernels = {k: v for k, v in kt.items() if k not in ("k_expand", "k_fill_zero")}
@@ -160,7 +218,7 @@ def roofline_prefill(kt, w, chunk):
     else:
         achieved = work / avg_s / 1e9
     return {"kernel": name, "bound": bound, "achieved": round(achieved, 3), "peak": peak,
-            "unit": unit, "frac": round(achieved / peak, 5), "traffic": None,
+            "unit": unit, "frac": round(achieved / peak, 5), "traffic": measured_traffic(name),
             "work_per_launch": work, "avg_launch_ms": round(prefill_kernels[name]["avg_ms"], 5)}
 
 
@@ -231,7 +289,7 @@ def bench_decode(oal, w, reps, n_steps, device):
         "prefilled_tokens": n0,
         "roofline": {"kernel": "k_decode", "bound": "hbm", "achieved": round(achieved, 2),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
-                     "traffic": None, "work_per_launch": bytes_launch,
+                     "traffic": measured_traffic("k_decode"), "work_per_launch": bytes_launch,
                      "avg_launch_ms": round(kt["k_decode"]["avg_ms"], 5)},
     }
 
@@ -296,6 +354,8 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--only", choices=["prefill", "decode"], default=None,
                     help="time one leg only (used to profile each workload on its own)")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="after the legs, copy MIB MiB 5 times (reference for HBM counters)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -313,6 +373,8 @@ def main() -> int:
     w3 = synth.WORKLOADS[3]
     if args.only == "decode":
         res = bench_decode(oal, synth.WORKLOADS[4], args.decode_reps, args.decode_steps, device)
+        if args.copy_probe:
+            copy_probe(args.copy_probe)
         print(json.dumps({"metric": METRIC, "decode": res}), flush=True)
         return 0
     log(f"prefill: {w3.name}, chunk {args.chunk}, {args.warmup} warmup + {args.steps} steps")
@@ -363,6 +425,8 @@ def main() -> int:
         log("decode: setting up")
         result["decode"] = bench_decode(oal, synth.WORKLOADS[4], args.decode_reps,
                                         args.decode_steps, device)
+    if args.copy_probe:
+        copy_probe(args.copy_probe)
     if not args.no_cpu_baseline:
         log("cpu baseline: float64 oracle on a bounded sample")
         result["cpu_baseline"] = cpu_baseline(w3, args.cpu_seconds)
