@@ -102,46 +102,8 @@ __device__ __forceinline__ int exp_above(float x) {
   return e;
 }
 
-// Wait until at most N vector-memory operations of this wave are outstanding
-// (the direct-to-LDS loads count there); other counters are left alone.
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 16, "vmcnt immediate");
-  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
-}
-
-// Workgroup barrier without the memory fence of __syncthreads (which would wait
-// for the prefetches still in flight); the clobber keeps LDS accesses in place.
-__device__ __forceinline__ void barrier_nofence() { asm volatile("s_barrier" ::: "memory"); }
-
 template <bool B>
 using bool_t = std::integral_constant<bool, B>;
-
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-
-// Raw buffer resource over [base, base + bytes) (reads beyond it return zero).
-__device__ __forceinline__ i32x4 buffer_rsrc(const void* base, uint32_t bytes) {
-  const uint64_t a = reinterpret_cast<uint64_t>(base);
-  i32x4 r;
-  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
-  r[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));   // stride 0
-  r[2] = __builtin_amdgcn_readfirstlane((int)bytes);
-  r[3] = 0x00020000;                                                  // 32-bit data format
-  return r;
-}
-
-// LDS byte address of a __shared__ pointer.
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
-}
-
-// 16 bytes per lane from rsrc + soff + voff into LDS at lds + 16 * lane.
-__device__ __forceinline__ void load_lds16(const i32x4& rsrc, uint32_t lds, uint32_t voff, int soff) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-               :
-               : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(rsrc), "s"(soff)
-               : "memory");
-}
 
 __device__ __forceinline__ uint8_t* pick4(int i, uint8_t* a, uint8_t* b, uint8_t* c, uint8_t* d) {
   return i == 0 ? a : i == 1 ? b : i == 2 ? c : d;

@@ -45,6 +45,7 @@ constexpr int SLOT_REGS = 132;          // registers per wave in the seg buffers
 constexpr int SLOT_FLOATS = SLOT_REGS * 64;
 constexpr int UNIT_SEG_FLOATS = NWAVES * SLOT_FLOATS;   // one (unit, segment)
 constexpr int TB = 64;                  // tokens staged per block
+constexpr int STG_BYTES = (DH + DV) * TB * 2;   // one staged block: k^T, v^T in fp16
 constexpr int REG_H0 = 128, REG_Z1 = 129, REG_Z0 = 130;
 }  // namespace st
 
@@ -188,6 +189,19 @@ __device__ __forceinline__ int st_exp_above(float x) {
   return e;
 }
 
+// Wait until at most x (>= 0, any value) vector-memory operations of this wave
+// are outstanding, and for its LDS reads: the largest immediate not above x.
+__device__ __forceinline__ void wait_vm_upto(int x) {
+  if (x >= 63) wait_vmcnt<63, true>();
+  else if (x >= 50) wait_vmcnt<50, true>();
+  else if (x >= 36) wait_vmcnt<36, true>();
+  else if (x >= 32) wait_vmcnt<32, true>();
+  else if (x >= 20) wait_vmcnt<20, true>();
+  else if (x >= 16) wait_vmcnt<16, true>();
+  else if (x >= 4) wait_vmcnt<4, true>();
+  else wait_vmcnt<0, true>();
+}
+
 }  // namespace
 
 // Largest |k| and |v| of each (unit, segment), as KVP partial maxima over
@@ -238,22 +252,79 @@ __device__ __forceinline__ float seg_max(const float* kvmax, int unit, int n_seg
   return m;
 }
 
+// One 64-token block of one unit, staged once for both builder passes: k^T then
+// v^T (64 rows of 128 bytes each), fp16 times the segment's scales 2^-e_k and
+// 2^-e_v, in the st_off layout, so that the passes fill LDS with straight
+// direct-to-LDS copies.  Also adds up beta over the block for the tile-scale
+// bound: bound[units + unit * n_blk + blk] (block 0 clears bound[unit], the
+// max |H_init| that the segment scan raises).  One workgroup per (block, unit).
+__global__ void __launch_bounds__(256)
+k_state_stage(int seq_len, int chunk, int n_seg, int cps, const uint16_t* __restrict__ k,
+              const uint16_t* __restrict__ v, const float* __restrict__ kvmax,
+              uint8_t* __restrict__ stg, float* __restrict__ bound, int units) {
+  __shared__ __attribute__((aligned(16))) uint8_t s_img[st::STG_BYTES];
+  __shared__ float s_bred[4];
+  const int blk = blockIdx.x, unit = blockIdx.y, n_blk = gridDim.x;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int t0 = blk * st::TB;
+  const int seg = t0 / (cps * chunk);
+  const int e_k = st_exp_above(seg_max(kvmax, unit, n_seg, seg, 0)) - 7;
+  const int e_v = st_exp_above(seg_max(kvmax, unit, n_seg, seg, 1)) - 7;
+  Stager sg{k, v, (size_t)unit * seq_len, seq_len, {}, {}};
+  sg.fetch(t0, tid);
+  if (bound != nullptr) {
+    // beta_j = max(|k_j|, |k_j|^2) |v_j| of the thread's two tokens (8 lanes each)
+    float beta = 0.f;
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      float km = __uint_as_float(absmax8_bits(sg.pk[e]) << 16);
+      float vm = __uint_as_float(absmax8_bits(sg.pv[e]) << 16);
+#pragma unroll
+      for (int o = 1; o < 8; o <<= 1) {
+        km = fmaxf(km, __shfl_xor(km, o, 64));
+        vm = fmaxf(vm, __shfl_xor(vm, o, 64));
+      }
+      if ((tid & 7) == 0) beta += fmaxf(km, km * km) * vm;
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) beta += __shfl_xor(beta, o, 64);
+    if (lane == 0) s_bred[wv] = beta;
+  }
+  sg.deposit<true>(s_img, s_img + DH * 128, tid, ldexpf(1.0f, -e_k), ldexpf(1.0f, -e_v));
+  __syncthreads();
+  uint4* dst = reinterpret_cast<uint4*>(stg + ((size_t)unit * n_blk + blk) * st::STG_BYTES);
+#pragma unroll
+  for (int i = 0; i < st::STG_BYTES / 16 / 256; ++i)
+    dst[i * 256 + tid] = reinterpret_cast<const uint4*>(s_img)[i * 256 + tid];
+  if (bound != nullptr && tid == 0) {
+    bound[units + (size_t)unit * n_blk + blk] = (s_bred[0] + s_bred[1]) + (s_bred[2] + s_bred[3]);
+    if (blk == 0) bound[unit] = 0.f;
+  }
+}
+
 template <int MODE>   // 0: segment sums, 1: per-chunk prefix tiles
 __global__ void __launch_bounds__(256, 2)
-k_state_mfma(int seq_len, int chunk, int n_chunks, int n_seg, int cps,
-             const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+k_state_mfma(int seq_len, int chunk, int n_chunks, int n_seg, int cps, int n_blk,
+             const uint8_t* __restrict__ stg,     // staged blocks (k_state_stage)
              float* __restrict__ segbuf,          // MODE 0: out sums; MODE 1: in prefixes
              uint8_t* __restrict__ ts,            // MODE 1: per-chunk prefix tiles
-             float* __restrict__ bound,           // tile-scale bound (null: no tiles follow)
+             const float* __restrict__ bound,     // MODE 1: tile-scale bound
              const float* __restrict__ kvmax,     // per (unit, segment): max |k|, max |v|
              int units) {
-  __shared__ __attribute__((aligned(16))) uint8_t s_kt[2][DH * 128];
-  __shared__ __attribute__((aligned(16))) uint8_t s_vt[2][DV * 128];
-  __shared__ float s_bred[st::WAVES_PER_WG];
+  // three staged blocks in flight: block i is read while i + 1 and i + 2 load
+  __shared__ __attribute__((aligned(16))) uint8_t s_b0[st::STG_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t s_b1[st::STG_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t s_b2[st::STG_BYTES];
 
-  const int g = blockIdx.x % st::NWG;
-  const int seg = (blockIdx.x / st::NWG) % n_seg;
-  const int unit = blockIdx.x / (st::NWG * n_seg);
+  // Workgroups are dealt to the 8 XCDs round robin (XCD = blockIdx mod 8); the 7
+  // workgroups of a (unit, segment) sit on one XCD, so that its L2 serves their
+  // shared reads of the staged blocks.  The grid is padded to whole rounds.
+  const int xcd = blockIdx.x & 7, j = blockIdx.x >> 3;
+  const int g = j % st::NWG;
+  const int us = (j / st::NWG) * 8 + xcd;   // unit * n_seg + seg
+  if (us >= units * n_seg) return;
+  const int seg = us % n_seg;
+  const int unit = us / n_seg;
   const int tid = threadIdx.x;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, col = lane & 31, half = lane >> 5;
@@ -262,26 +333,37 @@ k_state_mfma(int seq_len, int chunk, int n_chunks, int n_seg, int cps,
   const int tok_begin = c0 * chunk;
   const int tok_end = min(seq_len, c1 * chunk);
   const int n_blocks = (tok_end - tok_begin + st::TB - 1) / st::TB;
-  Stager sg{k, v, (size_t)unit * seq_len, tok_end, {}, {}};
+  const uint8_t* sblk = stg + ((size_t)unit * n_blk + tok_begin / st::TB) * st::STG_BYTES;
   float* segslot = segbuf + ((size_t)unit * n_seg + seg) * st::UNIT_SEG_FLOATS;
+  // staged values are k 2^-e_k and v 2^-e_v
+  const int e_k = st_exp_above(seg_max(kvmax, unit, n_seg, seg, 0)) - 7;
+  const int e_v = st_exp_above(seg_max(kvmax, unit, n_seg, seg, 1)) - 7;
   // MODE 1: the tile scale 2^-e_S of this unit
-  const int e_s = MODE == 1 ? tile_scale_exp(bound, units, n_seg, unit, lane) : 0;
+  const int e_s = MODE == 1 ? tile_scale_exp(bound, units, n_blk, unit, lane) : 0;
   const float tscale = ldexpf(1.0f, -e_s);
+
+  // Copies block bi of the segment into buf: PIECES 1 KB pieces per wave.
+  auto issue = [&](int bi, uint8_t* buf, auto pieces) {
+    constexpr int P = decltype(pieces)::value;
+    const i32x4 rs = buffer_rsrc(sblk + (size_t)bi * st::STG_BYTES, (uint32_t)st::STG_BYTES);
+    const uint32_t dst = lds_addr(buf) + wv * P * 1024;
+#pragma unroll
+    for (int j = 0; j < P; ++j) load_lds16(rs, dst + j * 1024, lane * 16, (wv * P + j) * 1024);
+  };
 
   if (g < st::NWG - 1) {
     // ===================== quadratic rows (waves 0..23) =====================
-    // Staged k and v are k 2^-e_k and v 2^-e_v in fp16 (|k| 2^-e_k < 128), so the
-    // accumulators hold the sums times 2^-(2 e_k + e_v).
-    const int e_k = st_exp_above(seg_max(kvmax, unit, n_seg, seg, 0)) - 7;
-    const int e_v = st_exp_above(seg_max(kvmax, unit, n_seg, seg, 1)) - 7;
-    const float ks = ldexpf(1.0f, -e_k), vs = ldexpf(1.0f, -e_v);
+    // The accumulators hold the sums times 2^-(2 e_k + e_v).
+    using P4 = std::integral_constant<int, 4>;
     const float unscale = ldexpf(1.0f, 2 * e_k + e_v);
+    const float rescale = ldexpf(1.0f, -(2 * e_k + e_v));
     const int omega = g * st::WAVES_PER_WG + wv;
     const int tb = omega < 8 ? 0 : 1;
     const int r0 = omega < 8 ? 4 * omega : 4 * (omega - 8);
     float* slot = segslot + (size_t)omega * st::SLOT_FLOATS;
+    if (n_blocks > 0) issue(0, s_b0, P4{});
+    if (n_blocks > 1) issue(1, s_b1, P4{});
     f32x16 acc[4][2];
-    const float rescale = ldexpf(1.0f, -(2 * e_k + e_v));
 #pragma unroll
     for (int m = 0; m < 4; ++m)
 #pragma unroll
@@ -290,15 +372,25 @@ k_state_mfma(int seq_len, int chunk, int n_chunks, int n_seg, int cps,
         for (int i = 0; i < 16; ++i)
           acc[m][nt][i] = MODE == 1 ? slot[(size_t)((m * 2 + nt) * 16 + i) * 64 + lane] * rescale : 0.f;
     const float wscale = unscale * tscale;   // accumulator -> tile entry
-    if (n_blocks > 0) {
-      sg.fetch(tok_begin, tid);
-      sg.deposit<true>(s_kt[0], s_vt[0], tid, ks, vs);
-    }
-    __syncthreads();
-    for (int bi = 0; bi < n_blocks; ++bi) {
+
+    // Tile stores issued per chunk start (wave-uniform): 2 per (m, row group)
+    // inside the tiled layout.
+    int nst = 0;
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) nst += (2 * tb + (gq >> 1)) < ((r0 + m) >> 4) ? 0 : 2;
+    auto stores_at = [&](int b) { return (MODE == 1 && b >= 0 && (b * st::TB) % chunk == 0) ? nst : 0; };
+
+    auto body = [&](int bi, const uint8_t* cur, uint8_t* nxt) {
+      if (bi >= n_blocks) return;
+      // Block bi has landed, for every wave.  Memory operations complete in issue
+      // order, and the ones issued after block bi's copy may stay in flight: the
+      // tile stores of the two previous blocks and the copy of block bi + 1.
+      wait_vm_upto(stores_at(bi - 2) + (bi + 1 < n_blocks ? 4 : 0) + stores_at(bi - 1));
+      barrier_nofence();
+      if (bi + 2 < n_blocks) issue(bi + 2, nxt, P4{});
       const int t0 = tok_begin + bi * st::TB;
-      const int buf = bi & 1;
-      if (bi + 1 < n_blocks) sg.fetch(t0 + st::TB, tid);
       if (MODE == 1 && (t0 % chunk) == 0) {
         // the running prefix is chunk (t0 / chunk)'s exclusive prefix: store it
         uint16_t* tl = reinterpret_cast<uint16_t*>(ts + ((size_t)unit * n_chunks + t0 / chunk) * tile::BYTES);
@@ -311,7 +403,7 @@ k_state_mfma(int seq_len, int chunk, int n_chunks, int n_seg, int cps,
 #pragma unroll
             for (int gq = 0; gq < 4; ++gq) {
               const int t = 32 * tb + 8 * gq + 4 * half;   // rows t .. t+3
-              const int cblk = t >> 4;
+              const int cblk = 2 * tb + (gq >> 1);           // t >> 4, wave-uniform
               if (cblk < (r >> 4)) continue;               // not in the tiled layout
               const int ks_ = tile::quad_base(cblk) + r;
               *reinterpret_cast<uint2*>(tl + (size_t)ks_ * 1024 + w * 16 + (t & 15)) =
@@ -322,8 +414,8 @@ k_state_mfma(int seq_len, int chunk, int n_chunks, int n_seg, int cps,
           }
         }
       }
-      const uint8_t* kt_ = s_kt[buf];
-      const uint8_t* vt_ = s_vt[buf];
+      const uint8_t* kt_ = cur;
+      const uint8_t* vt_ = cur + DH * 128;
 #pragma unroll
       for (int kk = 0; kk < st::TB / 16; ++kk) {
         const int tk = 16 * kk + 8 * half;     // this lane's 8 tokens inside the block
@@ -340,8 +432,11 @@ k_state_mfma(int seq_len, int chunk, int n_chunks, int n_seg, int cps,
           for (int nt = 0; nt < 2; ++nt) acc[m][nt] = mfma32h(af, bv[nt], acc[m][nt]);
         }
       }
-      if (bi + 1 < n_blocks) sg.deposit<true>(s_kt[buf ^ 1], s_vt[buf ^ 1], tid, ks, vs);
-      __syncthreads();
+    };
+    for (int bi = 0; bi < n_blocks; bi += 3) {
+      body(bi, s_b0, s_b2);
+      body(bi + 1, s_b1, s_b0);
+      body(bi + 2, s_b2, s_b1);
     }
     if (MODE == 0) {
 #pragma unroll
@@ -356,8 +451,16 @@ k_state_mfma(int seq_len, int chunk, int n_chunks, int n_seg, int cps,
   }
 
   // ===================== linear rows and the all-ones channel (wave 24) ======
-  const bool worker = wv == 0;
+  // One wave does everything (the other three of the workgroup have no work), so
+  // it needs no barrier: its own loads are awaited with wait_vmcnt.  Sums held
+  // scaled: H1 by 2^-(e_k + e_v), Z by 2^-2 e_k, H0 by 2^-e_v, z1 by 2^-e_k.
+  if (wv != 0) return;
+  using P16 = std::integral_constant<int, 16>;
+  if (n_blocks > 0) issue(0, s_b0, P16{});
+  if (n_blocks > 1) issue(1, s_b1, P16{});
   float* slot = segslot + (size_t)24 * st::SLOT_FLOATS;
+  const float sc_h1 = ldexpf(1.0f, e_k + e_v), sc_z = ldexpf(1.0f, 2 * e_k);
+  const float sc_h0 = ldexpf(1.0f, e_v), sc_z1 = ldexpf(1.0f, e_k);
   f32x16 acc[4][2];   // [0..1]: H1 rows 32m.., [2..3]: Z rows 32(m-2).., columns 32 nt..
   float side_h0 = 0.f, side_z1 = 0.f, side_z0 = 0.f;
 #pragma unroll
@@ -366,38 +469,27 @@ k_state_mfma(int seq_len, int chunk, int n_chunks, int n_seg, int cps,
     for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
       for (int i = 0; i < 16; ++i)
-        acc[m][nt][i] = (MODE == 1 && worker) ? slot[(size_t)((m * 2 + nt) * 16 + i) * 64 + lane] : 0.f;
-  if (MODE == 1 && worker) {
-    side_h0 = slot[(size_t)st::REG_H0 * 64 + lane];
-    side_z1 = slot[(size_t)st::REG_Z1 * 64 + lane];
+        acc[m][nt][i] = MODE == 1 ? slot[(size_t)((m * 2 + nt) * 16 + i) * 64 + lane] *
+                                        (m < 2 ? ldexpf(1.0f, -(e_k + e_v)) : ldexpf(1.0f, -2 * e_k))
+                                  : 0.f;
+  if (MODE == 1) {
+    side_h0 = slot[(size_t)st::REG_H0 * 64 + lane] * ldexpf(1.0f, -e_v);
+    side_z1 = slot[(size_t)st::REG_Z1 * 64 + lane] * ldexpf(1.0f, -e_k);
     side_z0 = slot[(size_t)st::REG_Z0 * 64];
   }
-  float beta_sum = 0.f;   // MODE 0 with tiles: sum of beta over this thread's tokens
-  // beta_j = max(|k_j|, |k_j|^2) |v_j| of the two staged tokens
-  auto add_beta = [&]() {
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      float km = __uint_as_float(absmax8_bits(sg.pk[e]) << 16);
-      float vm = __uint_as_float(absmax8_bits(sg.pv[e]) << 16);
-#pragma unroll
-      for (int o = 1; o < 8; o <<= 1) {
-        km = fmaxf(km, __shfl_xor(km, o, 64));
-        vm = fmaxf(vm, __shfl_xor(vm, o, 64));
-      }
-      if ((tid & 7) == 0) beta_sum += fmaxf(km, km * km) * vm;
-    }
-  };
-  if (n_blocks > 0) {
-    sg.fetch(tok_begin, tid);
-    if (MODE == 0 && bound != nullptr) add_beta();
-    sg.deposit<false>(s_kt[0], s_vt[0], tid, 1.f, 1.f);
-  }
-  __syncthreads();
-  for (int bi = 0; bi < n_blocks; ++bi) {
+  const float h1scale = sc_h1 * tscale;
+  // side stores per chunk start: 16 for H1, 16 for Z, 2 for H0 and z1, 1 or 2 by
+  // lane 0 (adjacent words): a lower bound, so that the wait below is never short
+  constexpr int SIDE_STORES = 34;
+  auto stores_at = [&](int b) { return (MODE == 1 && b >= 0 && (b * st::TB) % chunk == 0) ? SIDE_STORES : 0; };
+  auto body = [&](int bi, const uint8_t* cur, uint8_t* nxt) {
+    if (bi >= n_blocks) return;
+    // block bi has landed (later stores and the copy of block bi + 1 may be in flight)
+    wait_vm_upto(stores_at(bi - 2) + (bi + 1 < n_blocks ? 16 : 0) + stores_at(bi - 1));
+    asm volatile("" ::: "memory");
+    if (bi + 2 < n_blocks) issue(bi + 2, nxt, P16{});
     const int t0 = tok_begin + bi * st::TB;
-    const int buf = bi & 1;
-    if (bi + 1 < n_blocks) sg.fetch(t0 + st::TB, tid);
-    if (MODE == 1 && worker && (t0 % chunk) == 0) {
+    if (MODE == 1 && (t0 % chunk) == 0) {
       uint8_t* slotp = ts + ((size_t)unit * n_chunks + t0 / chunk) * tile::BYTES;
       uint16_t* tl = reinterpret_cast<uint16_t*>(slotp);
       float* side = reinterpret_cast<float*>(slotp + tile::TILE_BYTES);
@@ -411,7 +503,7 @@ k_state_mfma(int seq_len, int chunk, int n_chunks, int n_seg, int cps,
             const int r = 32 * m + 8 * gq + 4 * half;
             *reinterpret_cast<uint2*>(tl + (size_t)(r >> 4) * 1024 + w * 16 + (r & 15)) =
                 pack4_f16(acc[m][nt][4 * gq], acc[m][nt][4 * gq + 1], acc[m][nt][4 * gq + 2],
-                          acc[m][nt][4 * gq + 3], tscale);
+                          acc[m][nt][4 * gq + 3], h1scale);
           }
           asm volatile("" ::: "memory");
         }
@@ -419,80 +511,74 @@ k_state_mfma(int seq_len, int chunk, int n_chunks, int n_seg, int cps,
       for (int m = 2; m < 4; ++m)
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) {
-          // rows r = 32 (m - 2) + 8 (i / 4) + 4 half + i % 4, column t = 32 nt + col
-          float* zb = side + tile::SIDE_Z + (32 * (m - 2) + 4 * half) * DH + 32 * nt + col;
+          // Z is symmetric: block (rows r, columns t) goes to (t, r), so that each
+          // lane's four consecutive rows r form one float4 of row t = 32 nt + col
+          float* zb = side + tile::SIDE_Z + (32 * nt + col) * DH + 32 * (m - 2) + 4 * half;
 #pragma unroll
-          for (int i = 0; i < 16; ++i) zb[(8 * (i >> 2) + (i & 3)) * DH] = acc[m][nt][i];
+          for (int gq = 0; gq < 4; ++gq)
+            *reinterpret_cast<float4*>(zb + 8 * gq) =
+                make_float4(acc[m][nt][4 * gq] * sc_z, acc[m][nt][4 * gq + 1] * sc_z,
+                            acc[m][nt][4 * gq + 2] * sc_z, acc[m][nt][4 * gq + 3] * sc_z);
           asm volatile("" ::: "memory");
         }
-      side[tile::SIDE_H0 + lane] = side_h0;
-      side[tile::SIDE_Z1 + lane] = side_z1;
+      side[tile::SIDE_H0 + lane] = side_h0 * sc_h0;
+      side[tile::SIDE_Z1 + lane] = side_z1 * sc_z1;
       if (lane == 0) {
         side[tile::SIDE_Z0] = side_z0;
         side[tile::SIDE_SEXP] = (float)e_s;
       }
     }
-    if (worker) {
-      const uint8_t* kt_ = s_kt[buf];
-      const uint8_t* vt_ = s_vt[buf];
-      // H0 = sum v, z1 = sum k, z0 = count over this block (row `lane`)
-      float sh = 0.f, sz = 0.f;
+    const uint8_t* kt_ = cur;
+    const uint8_t* vt_ = cur + DH * 128;
+    // H0 = sum v, z1 = sum k, z0 = count over this block (row `lane`)
+    const f16x2 one2 = {(_Float16)1.0f, (_Float16)1.0f};
+    float sh = 0.f, sz = 0.f;
 #pragma unroll
-      for (int c = 0; c < st::TB / 8; ++c) {
-        const bf16x8 xv = *reinterpret_cast<const bf16x8*>(vt_ + st_off(lane, 8 * c));
-        const bf16x8 xk = *reinterpret_cast<const bf16x8*>(kt_ + st_off(lane, 8 * c));
+    for (int c = 0; c < st::TB / 8; ++c) {
+      const f16x8 xv = *reinterpret_cast<const f16x8*>(vt_ + st_off(lane, 8 * c));
+      const f16x8 xk = *reinterpret_cast<const f16x8*>(kt_ + st_off(lane, 8 * c));
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          sh += bf(xv[j]);
-          sz += bf(xk[j]);
-        }
-      }
-      side_h0 += sh;
-      side_z1 += sz;
-      side_z0 += (float)min(st::TB, tok_end - t0);
-#pragma unroll
-      for (int kk = 0; kk < st::TB / 16; ++kk) {
-        const int tk = 16 * kk + 8 * half;
-        bf16x8 ak[2], bv[2];
-#pragma unroll
-        for (int x = 0; x < 2; ++x) {
-          ak[x] = *reinterpret_cast<const bf16x8*>(kt_ + st_off(32 * x + col, tk));
-          bv[x] = *reinterpret_cast<const bf16x8*>(vt_ + st_off(32 * x + col, tk));
-        }
-#pragma unroll
-        for (int m = 0; m < 2; ++m)
-#pragma unroll
-          for (int nt = 0; nt < 2; ++nt) {
-            acc[m][nt] = mfma32(ak[m], bv[nt], acc[m][nt]);         // H1 += K^T V
-            acc[2 + m][nt] = mfma32(ak[m], ak[nt], acc[2 + m][nt]); // Z  += K^T K
-          }
+      for (int j = 0; j < 4; ++j) {
+        sh = __builtin_amdgcn_fdot2((f16x2){xv[2 * j], xv[2 * j + 1]}, one2, sh, false);
+        sz = __builtin_amdgcn_fdot2((f16x2){xk[2 * j], xk[2 * j + 1]}, one2, sz, false);
       }
     }
-    if (bi + 1 < n_blocks) {
-      if (MODE == 0 && bound != nullptr) add_beta();
-      sg.deposit<false>(s_kt[buf ^ 1], s_vt[buf ^ 1], tid, 1.f, 1.f);
-    }
-    __syncthreads();
-  }
-  if (MODE == 0 && bound != nullptr) {
+    side_h0 += sh;
+    side_z1 += sz;
+    side_z0 += (float)min(st::TB, tok_end - t0);
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) beta_sum += __shfl_xor(beta_sum, o, 64);
-    if (lane == 0) s_bred[wv] = beta_sum;
-    __syncthreads();
-    if (tid == 0) {
-      bound[units + (size_t)unit * n_seg + seg] = (s_bred[0] + s_bred[1]) + (s_bred[2] + s_bred[3]);
-      if (seg == 0) bound[unit] = 0.f;   // max |H_init|, raised by the scan
+    for (int kk = 0; kk < st::TB / 16; ++kk) {
+      const int tk = 16 * kk + 8 * half;
+      f16x8 ak[2], bv[2];
+#pragma unroll
+      for (int x = 0; x < 2; ++x) {
+        ak[x] = *reinterpret_cast<const f16x8*>(kt_ + st_off(32 * x + col, tk));
+        bv[x] = *reinterpret_cast<const f16x8*>(vt_ + st_off(32 * x + col, tk));
+      }
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+          acc[m][nt] = mfma32h(ak[m], bv[nt], acc[m][nt]);         // H1 += K^T V
+          acc[2 + m][nt] = mfma32h(ak[m], ak[nt], acc[2 + m][nt]); // Z  += K^T K
+        }
     }
+  };
+  for (int bi = 0; bi < n_blocks; bi += 3) {
+    body(bi, s_b0, s_b2);
+    body(bi + 1, s_b1, s_b0);
+    body(bi + 2, s_b2, s_b1);
   }
-  if (MODE == 0 && worker) {
+  if (MODE == 0) {
 #pragma unroll
     for (int m = 0; m < 4; ++m)
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) slot[(size_t)((m * 2 + nt) * 16 + i) * 64 + lane] = acc[m][nt][i];
-    slot[(size_t)st::REG_H0 * 64 + lane] = side_h0;
-    slot[(size_t)st::REG_Z1 * 64 + lane] = side_z1;
+        for (int i = 0; i < 16; ++i)
+          slot[(size_t)((m * 2 + nt) * 16 + i) * 64 + lane] = acc[m][nt][i] * (m < 2 ? sc_h1 : sc_z);
+    slot[(size_t)st::REG_H0 * 64 + lane] = side_h0 * sc_h0;
+    slot[(size_t)st::REG_Z1 * 64 + lane] = side_z1 * sc_z1;
     slot[(size_t)st::REG_Z0 * 64 + lane] = lane == 0 ? side_z0 : 0.f;
   }
 }
@@ -529,16 +615,24 @@ k_state_segscan(int n_seg, float* __restrict__ segsum, float* __restrict__ segpr
   if (!in) return;
   float4 r = make_float4(run[0], run[1], run[2], run[3]);
   const size_t base = (size_t)unit * n_seg * st::UNIT_SEG_FLOATS + e0;
-  for (int s = 0; s < n_seg; ++s) {
-    const size_t off = base + (size_t)s * st::UNIT_SEG_FLOATS;
-    if (segpre) *reinterpret_cast<float4*>(segpre + off) = r;
-    if (segsum) {
-      const float4 a = *reinterpret_cast<const float4*>(segsum + off);
-      r.x += a.x;
-      r.y += a.y;
-      r.z += a.z;
-      r.w += a.w;
-    }
+  // the loads of SB segments are issued together: one at a time, each thread
+  // would wait out the full memory latency n_seg times
+  constexpr int SB = 8;
+  for (int s0 = 0; s0 < n_seg; s0 += SB) {
+    float4 a[SB];
+#pragma unroll
+    for (int j = 0; j < SB; ++j)
+      if (s0 + j < n_seg)
+        a[j] = *reinterpret_cast<const float4*>(segsum + base + (size_t)(s0 + j) * st::UNIT_SEG_FLOATS);
+#pragma unroll
+    for (int j = 0; j < SB; ++j)
+      if (s0 + j < n_seg) {
+        if (segpre) *reinterpret_cast<float4*>(segpre + base + (size_t)(s0 + j) * st::UNIT_SEG_FLOATS) = r;
+        r.x += a[j].x;
+        r.y += a[j].y;
+        r.z += a[j].z;
+        r.w += a[j].w;
+      }
   }
   // the final value goes through segment 0's slot (no longer read): mirrored
   // elements of other threads may still read the initial state here
@@ -575,25 +669,30 @@ static size_t kvmax_bytes(int units, int n_seg) {
   return ((size_t)units * n_seg * KVP * 2 * sizeof(float) + 255) / 256 * 256;
 }
 
+static size_t stage_bytes(int units, int seq_len) {
+  return (size_t)units * ((seq_len + st::TB - 1) / st::TB) * st::STG_BYTES;
+}
+
 size_t state_mfma_workspace(int batch, int n_kv_heads, int seq_len, int chunk, bool with_tiles) {
   const int units = batch * n_kv_heads;
   const int n_chunks = (seq_len + chunk - 1) / chunk;
   const int n_seg = choose_segments(units, n_chunks);
   const int cps = (n_chunks + n_seg - 1) / n_seg;
   const int n_seg_eff = (n_chunks + cps - 1) / cps;
+  const int n_blk = (seq_len + st::TB - 1) / st::TB;
   size_t bytes = (with_tiles ? 2 : 1) * (size_t)units * n_seg_eff * st::UNIT_SEG_FLOATS * sizeof(float);
-  bytes += kvmax_bytes(units, n_seg_eff);
+  bytes += kvmax_bytes(units, n_seg_eff) + stage_bytes(units, seq_len);
   if (with_tiles) {
     bytes += (size_t)units * n_chunks * tile::BYTES;
-    bytes += ((size_t)units * (n_seg_eff + 1) * sizeof(float) + 255) / 256 * 256;   // scale bound
+    bytes += ((size_t)units * (n_blk + 1) * sizeof(float) + 255) / 256 * 256;   // scale bound
   }
   return bytes;
 }
 
 // Builds the per-chunk prefix tiles (when ts != null) and the final state (when
 // state != null; its content on entry is the initial state).  ws: the scratch part
-// of state_mfma_workspace (segment sums, the segments' max |k| and |v|, then the
-// segment prefixes and the tile-scale bound).
+// of state_mfma_workspace (segment sums, the segments' max |k| and |v|, the staged
+// blocks, then the segment prefixes and the tile-scale bound).
 oal_status launch_state_mfma(int batch, int n_kv_heads, int seq_len, int chunk, const void* k,
                              const void* v, float* state, uint8_t* ts, void* ws,
                              hipStream_t stream) {
@@ -602,12 +701,14 @@ oal_status launch_state_mfma(int batch, int n_kv_heads, int seq_len, int chunk, 
   const int n_seg = choose_segments(units, n_chunks);
   const int cps = (n_chunks + n_seg - 1) / n_seg;
   const int n_seg_eff = (n_chunks + cps - 1) / cps;
+  const int n_blk = (seq_len + st::TB - 1) / st::TB;
   const uint16_t* kk = reinterpret_cast<const uint16_t*>(k);
   const uint16_t* vv = reinterpret_cast<const uint16_t*>(v);
-  const dim3 grid(units * n_seg_eff * st::NWG);
+  const dim3 grid((units * n_seg_eff + 7) / 8 * 8 * st::NWG);
   float* segsum = reinterpret_cast<float*>(ws);
   float* kvmax = segsum + (size_t)units * n_seg_eff * st::UNIT_SEG_FLOATS;
-  float* segpre = kvmax + kvmax_bytes(units, n_seg_eff) / sizeof(float);
+  uint8_t* stg = reinterpret_cast<uint8_t*>(kvmax) + kvmax_bytes(units, n_seg_eff);
+  float* segpre = reinterpret_cast<float*>(stg + stage_bytes(units, seq_len));
   float* bound = ts ? segpre + (size_t)units * n_seg_eff * st::UNIT_SEG_FLOATS : nullptr;
   {
     ProfScope ps("k_state_kvmax", stream);
@@ -617,10 +718,17 @@ oal_status launch_state_mfma(int batch, int n_kv_heads, int seq_len, int chunk, 
     if (s != OAL_OK) return s;
   }
   {
+    ProfScope ps("k_state_stage", stream);
+    hipLaunchKernelGGL(k_state_stage, dim3(n_blk, units), dim3(256), 0, stream, seq_len, chunk, n_seg_eff,
+                       cps, kk, vv, (const float*)kvmax, stg, bound, units);
+    oal_status s = check_launch("k_state_stage");
+    if (s != OAL_OK) return s;
+  }
+  {
     ProfScope ps("k_state_seg", stream);
     hipLaunchKernelGGL(k_state_mfma<0>, grid, dim3(256), 0, stream, seq_len, chunk, n_chunks,
-                       n_seg_eff, cps, kk, vv, segsum, (uint8_t*)nullptr, bound, (const float*)kvmax,
-                       units);
+                       n_seg_eff, cps, n_blk, (const uint8_t*)stg, segsum, (uint8_t*)nullptr,
+                       (const float*)nullptr, (const float*)kvmax, units);
     oal_status s = check_launch("k_state_seg");
     if (s != OAL_OK) return s;
   }
@@ -642,7 +750,8 @@ oal_status launch_state_mfma(int batch, int n_kv_heads, int seq_len, int chunk, 
   if (ts == nullptr) return OAL_OK;
   ProfScope ps("k_state_mfma", stream);
   hipLaunchKernelGGL(k_state_mfma<1>, grid, dim3(256), 0, stream, seq_len, chunk, n_chunks,
-                     n_seg_eff, cps, kk, vv, segpre, ts, bound, (const float*)kvmax, units);
+                     n_seg_eff, cps, n_blk, (const uint8_t*)stg, segpre, ts, (const float*)bound,
+                     (const float*)kvmax, units);
   return check_launch("k_state_mfma");
 }
 

@@ -116,6 +116,54 @@ __device__ __forceinline__ float bf(const __bf16 x) { return (float)x; }
 // the 8 rows of one residue mod 4 among 32 have distinct keys).
 __device__ __forceinline__ int row_key(int r) { return (r ^ (r >> 3)) & 7; }
 
+// ---- direct-to-LDS loads ---------------------------------------------------
+// The loads are issued from inline assembly so that the compiler neither waits
+// for them before LDS reads it cannot prove disjoint from their destination,
+// nor before rewriting their operand registers; their completion is awaited
+// explicitly with wait_vmcnt before the barrier that hands a buffer to the
+// waves.  Other memory operations of a wave complete in issue order with them,
+// so the compiler's own counts stay safe (only stricter).
+
+// Wait until at most N vector-memory operations of this wave are outstanding
+// (the direct-to-LDS loads count there); LDS: also until this wave's LDS reads
+// have returned, so that no buffer is refilled while one of them is in flight.
+// The immediate holds vmcnt in bits 3:0 and 15:14, lgkmcnt in 11:8, expcnt in 6:4.
+template <int N, bool LDS = false>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt immediate");
+  __builtin_amdgcn_s_waitcnt((LDS ? 0x0070 : 0x0F70) | (N & 15) | ((N >> 4) << 14));
+}
+
+// Workgroup barrier without the memory fence of __syncthreads (which would wait
+// for the prefetches still in flight); the clobber keeps LDS accesses in place.
+__device__ __forceinline__ void barrier_nofence() { asm volatile("s_barrier" ::: "memory"); }
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Raw buffer resource over [base, base + bytes) (reads beyond it return zero).
+__device__ __forceinline__ i32x4 buffer_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  i32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  r[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));   // stride 0
+  r[2] = __builtin_amdgcn_readfirstlane((int)bytes);
+  r[3] = 0x00020000;                                                  // 32-bit data format
+  return r;
+}
+
+// LDS byte address of a __shared__ pointer.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// 16 bytes per lane from rsrc + soff + voff into LDS at lds + 16 * lane.
+__device__ __forceinline__ void load_lds16(const i32x4& rsrc, uint32_t lds, uint32_t voff, int soff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :
+               : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(rsrc), "s"(soff)
+               : "memory");
+}
+
 // Largest magnitude among 8 bf16 values, as bf16 magnitude bits (for
 // non-negative bf16 numbers the integer order is the numeric order).
 __device__ __forceinline__ uint32_t absmax8_bits(const uint4& x) {
