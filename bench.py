@@ -89,7 +89,7 @@ def kernel_times(oal, names):
 
 
 ALL_KERNELS = ["k_expand", "k_fill_zero", "k_build_vec", "k_scan_vec", "k_readout_vec",
-               "k_scan_tile", "k_state_mfma", "k_state_seg", "k_state_segscan", "k_state_kvmax", "k_state_stage", "k_state_final",
+               "k_scan_tile", "k_state_mfma", "k_state_seg", "k_state_segscan", "k_state_kvmax", "k_state_stage",
                "k_readout_mfma",
                "k_decode", "k_export"]
 

@@ -19,9 +19,13 @@
 // their mirror images).  Waves 0..23 run identical code; wave 24 lives in a
 // workgroup of its own so that the two kinds of accumulators never share a loop.
 //
-// The running prefix is seeded from, and summed into, per-(unit, segment) buffers
-// in the raw accumulator layout; the small segment-scan kernel converts between
-// that layout and the canonical state (initial state in, final state out).
+// The running prefix is summed into, and seeded from, per-(unit, segment) buffers
+// in the raw accumulator layout (sums in fp32; the starting prefixes of the
+// quadratic rows as fp16 in the tiles' scale, the precision they are stored in
+// anyway, those of wave 24 in fp32: the all-ones channel and H0 are not covered
+// by the tiles' bound); the segment-scan kernel
+// converts between that layout and the canonical state (initial state in, final
+// state out).
 // A batch-1 long sequence has too few units to fill 256 CUs, so the sequence is
 // cut into S segments:  pass 1 (sum mode) adds up every segment,  the scan forms
 // each segment's starting prefix (plus the caller's initial state) and the final
@@ -30,9 +34,9 @@
 // fp16 tiles need a scale: every entry of every prefix of a unit is bounded by
 //   B = max |H_init| + sum_j beta_j,   beta_j = max(|k_j|, |k_j|^2) |v_j|
 // (|.| the largest magnitude of a vector), since each entry of H1 and H2 is a sum
-// of k_r v_w or k_r k_t v_w over the tokens.  Pass 1 adds up beta per segment,
-// the scan takes max |H_init|, and pass 2 stores H * 2^-e_S with 2^(e_S + 15) > B,
-// so that no entry exceeds 2^15 (the fp16 limit is 65504).
+// of k_r v_w or k_r k_t v_w over the tokens.  The staging pass adds up beta per
+// block, the first pass takes max |H_init|, and pass 2 stores H * 2^-e_S with
+// 2^(e_S + 15) > B, so that no entry exceeds 2^15 (the fp16 limit is 65504).
 #include "oal_tile.h"
 
 namespace oal {
@@ -44,6 +48,7 @@ constexpr int NWG = (NWAVES + WAVES_PER_WG - 1) / WAVES_PER_WG;   // 7 workgroup
 constexpr int SLOT_REGS = 132;          // registers per wave in the seg buffers
 constexpr int SLOT_FLOATS = SLOT_REGS * 64;
 constexpr int UNIT_SEG_FLOATS = NWAVES * SLOT_FLOATS;   // one (unit, segment)
+constexpr int QUAD_SEG_FLOATS = 24 * SLOT_FLOATS;       // its quadratic waves
 constexpr int TB = 64;                  // tokens staged per block
 constexpr int STG_BYTES = (DH + DV) * TB * 2;   // one staged block: k^T, v^T in fp16
 constexpr int REG_H0 = 128, REG_Z1 = 129, REG_Z0 = 130;
@@ -163,16 +168,21 @@ __device__ __forceinline__ uint2 pack4_f16(float a, float b, float c, float d, f
 }
 
 // Tile exponent e_S of a unit from the bound pieces (identical in every wave that
-// evaluates it: lane 0's sum order is fixed).  bound: [units] max |H_init| (as
-// float bits), then [units][n_seg] per-segment sums of beta.
-__device__ __forceinline__ int tile_scale_exp(const float* bound, int units, int n_seg, int unit,
-                                              int lane) {
-  float sum = 0.f;
-  for (int i = lane; i < n_seg; i += 64) sum += bound[units + (size_t)unit * n_seg + i];
+// evaluates it: the summation order is fixed).  bound: [units][n_blk] per-block
+// sums of beta, then [units][nip] partial maxima of |H_init|.
+__device__ __forceinline__ int tile_scale_exp(const float* bound, int units, int n_blk, int nip,
+                                              int unit, int lane) {
+  float sum = 0.f, mx = 0.f;
+  for (int i = lane; i < n_blk; i += 64) sum += bound[(size_t)unit * n_blk + i];
+  for (int i = lane; i < nip; i += 64) mx = fmaxf(mx, bound[(size_t)units * n_blk + (size_t)unit * nip + i]);
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) sum += __shfl_xor(sum, o, 64);
+  for (int o = 32; o >= 1; o >>= 1) {
+    sum += __shfl_xor(sum, o, 64);
+    mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+  }
   sum = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(sum)));
-  const float B = bound[unit] + sum;
+  mx = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(mx)));
+  const float B = mx + sum;
   int e = 0;
   if (B > 0.f) {
     int ex;
@@ -206,13 +216,18 @@ __device__ __forceinline__ void wait_vm_upto(int x) {
 
 // Largest |k| and |v| of each (unit, segment), as KVP partial maxima over
 // interleaved token ranges: the fp16 staging scales of the quadratic workgroups.
-// One workgroup per (segment, part, unit).
+// One workgroup per (segment, part, unit).  The nip = gridDim.x workgroups of a
+// unit also copy its initial state (when there is one) to init, in nip pieces,
+// so that the segment scan can overwrite the state with the final one, and
+// record the largest |H_init| of each piece in bmax (when not null).
 constexpr int KVP = 8;
 __global__ void __launch_bounds__(256)
 k_state_kvmax(int seq_len, int chunk, int n_chunks, int cps, const uint16_t* __restrict__ k,
-              const uint16_t* __restrict__ v, float* __restrict__ kvmax) {
-  __shared__ uint32_t s_m[2][4];
+              const uint16_t* __restrict__ v, float* __restrict__ kvmax,
+              const float* __restrict__ state, float* __restrict__ init, float* __restrict__ bmax) {
+  __shared__ uint32_t s_m[3][4];
   const int seg = blockIdx.x / KVP, part = blockIdx.x % KVP, unit = blockIdx.y;
+  const int nip = gridDim.x;
   const int n_seg = gridDim.x / KVP;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int s_begin = seg * cps * chunk;
@@ -221,7 +236,20 @@ k_state_kvmax(int seq_len, int chunk, int n_chunks, int cps, const uint16_t* __r
   const int t_begin = s_begin + part * per;
   const int t_end = min(s_end, t_begin + per);
   const size_t row0 = (size_t)unit * seq_len;
-  uint32_t mk = 0, mv = 0;
+  uint32_t mk = 0, mv = 0, mi = 0;   // mi: largest |H_init| as bits (non-negative floats order alike)
+  if (state != nullptr) {
+    constexpr int PER4 = (int)((STATE_FLOATS / 4 + 255) / 256);   // float4 per thread, at most
+    const size_t per = (STATE_FLOATS / 4 + nip - 1) / nip;
+    const size_t i0 = blockIdx.x * per, i1 = min(STATE_FLOATS / 4, i0 + per);
+    const float4* src = reinterpret_cast<const float4*>(state + (size_t)unit * STATE_FLOATS);
+    float4* dst = reinterpret_cast<float4*>(init + (size_t)unit * STATE_FLOATS);
+    (void)PER4;
+    for (size_t i = i0 + tid; i < i1; i += 256) {
+      const float4 x = src[i];
+      dst[i] = x;
+      mi = max(mi, __float_as_uint(fmaxf(fmaxf(fabsf(x.x), fabsf(x.y)), fmaxf(fabsf(x.z), fabsf(x.w)))));
+    }
+  }
   for (int p = tid; p < (t_end - t_begin) * 8; p += 256) {
     const size_t row = row0 + t_begin + (p >> 3);
     mk = max(mk, absmax8_bits(reinterpret_cast<const uint4*>(k + row * DH)[p & 7]));
@@ -231,15 +259,18 @@ k_state_kvmax(int seq_len, int chunk, int n_chunks, int cps, const uint16_t* __r
   for (int o = 32; o >= 1; o >>= 1) {
     mk = max(mk, (uint32_t)__shfl_xor((int)mk, o, 64));
     mv = max(mv, (uint32_t)__shfl_xor((int)mv, o, 64));
+    mi = max(mi, (uint32_t)__shfl_xor((int)mi, o, 64));
   }
   if (lane == 0) {
     s_m[0][wv] = mk;
     s_m[1][wv] = mv;
+    s_m[2][wv] = mi;
   }
   __syncthreads();
-  if (tid < 2) {
+  if (tid < 3) {
     const uint32_t m = max(max(s_m[tid][0], s_m[tid][1]), max(s_m[tid][2], s_m[tid][3]));
-    kvmax[(((size_t)unit * n_seg + seg) * KVP + part) * 2 + tid] = __uint_as_float(m << 16);
+    if (tid < 2) kvmax[(((size_t)unit * n_seg + seg) * KVP + part) * 2 + tid] = __uint_as_float(m << 16);
+    else if (bmax != nullptr) bmax[(size_t)unit * nip + blockIdx.x] = __uint_as_float(m);
   }
 }
 
@@ -256,12 +287,11 @@ __device__ __forceinline__ float seg_max(const float* kvmax, int unit, int n_seg
 // v^T (64 rows of 128 bytes each), fp16 times the segment's scales 2^-e_k and
 // 2^-e_v, in the st_off layout, so that the passes fill LDS with straight
 // direct-to-LDS copies.  Also adds up beta over the block for the tile-scale
-// bound: bound[units + unit * n_blk + blk] (block 0 clears bound[unit], the
-// max |H_init| that the segment scan raises).  One workgroup per (block, unit).
+// bound: bound[unit * n_blk + blk].  One workgroup per (block, unit).
 __global__ void __launch_bounds__(256)
 k_state_stage(int seq_len, int chunk, int n_seg, int cps, const uint16_t* __restrict__ k,
               const uint16_t* __restrict__ v, const float* __restrict__ kvmax,
-              uint8_t* __restrict__ stg, float* __restrict__ bound, int units) {
+              uint8_t* __restrict__ stg, float* __restrict__ bound) {
   __shared__ __attribute__((aligned(16))) uint8_t s_img[st::STG_BYTES];
   __shared__ float s_bred[4];
   const int blk = blockIdx.x, unit = blockIdx.y, n_blk = gridDim.x;
@@ -296,21 +326,21 @@ k_state_stage(int seq_len, int chunk, int n_seg, int cps, const uint16_t* __rest
 #pragma unroll
   for (int i = 0; i < st::STG_BYTES / 16 / 256; ++i)
     dst[i * 256 + tid] = reinterpret_cast<const uint4*>(s_img)[i * 256 + tid];
-  if (bound != nullptr && tid == 0) {
-    bound[units + (size_t)unit * n_blk + blk] = (s_bred[0] + s_bred[1]) + (s_bred[2] + s_bred[3]);
-    if (blk == 0) bound[unit] = 0.f;
-  }
+  if (bound != nullptr && tid == 0)
+    bound[(size_t)unit * n_blk + blk] = (s_bred[0] + s_bred[1]) + (s_bred[2] + s_bred[3]);
 }
 
 template <int MODE>   // 0: segment sums, 1: per-chunk prefix tiles
 __global__ void __launch_bounds__(256, 2)
 k_state_mfma(int seq_len, int chunk, int n_chunks, int n_seg, int cps, int n_blk,
              const uint8_t* __restrict__ stg,     // staged blocks (k_state_stage)
-             float* __restrict__ segbuf,          // MODE 0: out sums; MODE 1: in prefixes
+             float* __restrict__ segsum,          // MODE 0: out sums
+             const uint16_t* __restrict__ segpre, // MODE 1: starting prefixes of waves 0..23, fp16 times 2^-e_S
+             const float* __restrict__ sidepre,   // MODE 1: starting prefixes of wave 24
              uint8_t* __restrict__ ts,            // MODE 1: per-chunk prefix tiles
              const float* __restrict__ bound,     // MODE 1: tile-scale bound
              const float* __restrict__ kvmax,     // per (unit, segment): max |k|, max |v|
-             int units) {
+             int units, int nip) {
   // three staged blocks in flight: block i is read while i + 1 and i + 2 load
   __shared__ __attribute__((aligned(16))) uint8_t s_b0[st::STG_BYTES];
   __shared__ __attribute__((aligned(16))) uint8_t s_b1[st::STG_BYTES];
@@ -334,12 +364,13 @@ k_state_mfma(int seq_len, int chunk, int n_chunks, int n_seg, int cps, int n_blk
   const int tok_end = min(seq_len, c1 * chunk);
   const int n_blocks = (tok_end - tok_begin + st::TB - 1) / st::TB;
   const uint8_t* sblk = stg + ((size_t)unit * n_blk + tok_begin / st::TB) * st::STG_BYTES;
-  float* segslot = segbuf + ((size_t)unit * n_seg + seg) * st::UNIT_SEG_FLOATS;
+  float* segslot = segsum + ((size_t)unit * n_seg + seg) * st::UNIT_SEG_FLOATS;
+  const uint16_t* preslot = segpre + ((size_t)unit * n_seg + seg) * st::QUAD_SEG_FLOATS;
   // staged values are k 2^-e_k and v 2^-e_v
   const int e_k = st_exp_above(seg_max(kvmax, unit, n_seg, seg, 0)) - 7;
   const int e_v = st_exp_above(seg_max(kvmax, unit, n_seg, seg, 1)) - 7;
   // MODE 1: the tile scale 2^-e_S of this unit
-  const int e_s = MODE == 1 ? tile_scale_exp(bound, units, n_blk, unit, lane) : 0;
+  const int e_s = MODE == 1 ? tile_scale_exp(bound, units, n_blk, nip, unit, lane) : 0;
   const float tscale = ldexpf(1.0f, -e_s);
 
   // Copies block bi of the segment into buf: PIECES 1 KB pieces per wave.
@@ -356,11 +387,12 @@ k_state_mfma(int seq_len, int chunk, int n_chunks, int n_seg, int cps, int n_blk
     // The accumulators hold the sums times 2^-(2 e_k + e_v).
     using P4 = std::integral_constant<int, 4>;
     const float unscale = ldexpf(1.0f, 2 * e_k + e_v);
-    const float rescale = ldexpf(1.0f, -(2 * e_k + e_v));
+    const float rescale = ldexpf(1.0f, e_s - (2 * e_k + e_v));   // seed -> accumulator
     const int omega = g * st::WAVES_PER_WG + wv;
     const int tb = omega < 8 ? 0 : 1;
     const int r0 = omega < 8 ? 4 * omega : 4 * (omega - 8);
     float* slot = segslot + (size_t)omega * st::SLOT_FLOATS;
+    const uint16_t* pslot = preslot + (size_t)omega * st::SLOT_FLOATS;
     if (n_blocks > 0) issue(0, s_b0, P4{});
     if (n_blocks > 1) issue(1, s_b1, P4{});
     f32x16 acc[4][2];
@@ -370,7 +402,8 @@ k_state_mfma(int seq_len, int chunk, int n_chunks, int n_seg, int cps, int n_blk
       for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
         for (int i = 0; i < 16; ++i)
-          acc[m][nt][i] = MODE == 1 ? slot[(size_t)((m * 2 + nt) * 16 + i) * 64 + lane] * rescale : 0.f;
+          acc[m][nt][i] = MODE == 1 ? (float)__builtin_bit_cast(_Float16, pslot[(size_t)((m * 2 + nt) * 16 + i) * 64 + lane]) * rescale
+                                    : 0.f;
     const float wscale = unscale * tscale;   // accumulator -> tile entry
 
     // Tile stores issued per chunk start (wave-uniform): 2 per (m, row group)
@@ -459,6 +492,7 @@ k_state_mfma(int seq_len, int chunk, int n_chunks, int n_seg, int cps, int n_blk
   if (n_blocks > 0) issue(0, s_b0, P16{});
   if (n_blocks > 1) issue(1, s_b1, P16{});
   float* slot = segslot + (size_t)24 * st::SLOT_FLOATS;
+  const float* pslot = sidepre + ((size_t)unit * n_seg + seg) * st::SLOT_FLOATS;
   const float sc_h1 = ldexpf(1.0f, e_k + e_v), sc_z = ldexpf(1.0f, 2 * e_k);
   const float sc_h0 = ldexpf(1.0f, e_v), sc_z1 = ldexpf(1.0f, e_k);
   f32x16 acc[4][2];   // [0..1]: H1 rows 32m.., [2..3]: Z rows 32(m-2).., columns 32 nt..
@@ -469,13 +503,13 @@ k_state_mfma(int seq_len, int chunk, int n_chunks, int n_seg, int cps, int n_blk
     for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
       for (int i = 0; i < 16; ++i)
-        acc[m][nt][i] = MODE == 1 ? slot[(size_t)((m * 2 + nt) * 16 + i) * 64 + lane] *
+        acc[m][nt][i] = MODE == 1 ? pslot[(size_t)((m * 2 + nt) * 16 + i) * 64 + lane] *
                                         (m < 2 ? ldexpf(1.0f, -(e_k + e_v)) : ldexpf(1.0f, -2 * e_k))
                                   : 0.f;
   if (MODE == 1) {
-    side_h0 = slot[(size_t)st::REG_H0 * 64 + lane] * ldexpf(1.0f, -e_v);
-    side_z1 = slot[(size_t)st::REG_Z1 * 64 + lane] * ldexpf(1.0f, -e_k);
-    side_z0 = slot[(size_t)st::REG_Z0 * 64];
+    side_h0 = pslot[(size_t)st::REG_H0 * 64 + lane] * ldexpf(1.0f, -e_v);
+    side_z1 = pslot[(size_t)st::REG_Z1 * 64 + lane] * ldexpf(1.0f, -e_k);
+    side_z0 = pslot[(size_t)st::REG_Z0 * 64];
   }
   const float h1scale = sc_h1 * tscale;
   // side stores per chunk start: 16 for H1, 16 for Z, 2 for H0 and z1, 1 or 2 by
@@ -584,35 +618,36 @@ k_state_mfma(int seq_len, int chunk, int n_chunks, int n_seg, int cps, int n_blk
 }
 
 // Exclusive prefix over segments (plus the initial state), in the accumulator
-// layout; optionally writes init + the total as the final state.  Four
-// consecutive elements (same wave slot and register, lanes 4 j .. 4 j + 3) per
-// thread.
+// layout, four consecutive elements (same wave slot and register, lanes
+// 4 j .. 4 j + 3) per thread.  segpre (when not null): the starting prefixes of
+// waves 0..23 as fp16 times 2^-e_S, of wave 24 in fp32 (sidepre).  state (when
+// not null): receives init + the total in the canonical layout; init is the
+// initial state's copy (null: zero), so no thread reads what another writes.
 __global__ void __launch_bounds__(256)
-k_state_segscan(int n_seg, float* __restrict__ segsum, float* __restrict__ segpre,
-                const float* __restrict__ state, int write_final, float* __restrict__ bound) {
-  const int unit = blockIdx.y;
+k_state_segscan(int n_seg, const float* __restrict__ segsum, uint16_t* __restrict__ segpre,
+                float* __restrict__ sidepre, const float* __restrict__ init, float* __restrict__ state,
+                const float* __restrict__ bound, int n_blk, int nip) {
+  const int unit = blockIdx.y, units = gridDim.y;
   const int e0 = 4 * (blockIdx.x * blockDim.x + threadIdx.x);
   const bool in = e0 < st::UNIT_SEG_FLOATS;
+  const int omega = e0 / st::SLOT_FLOATS;
+  // every wave evaluates the tile scale (the same value everywhere)
+  const float tscale = segpre ? ldexpf(1.0f, -tile_scale_exp(bound, units, n_blk, nip, unit, threadIdx.x & 63)) : 1.f;
+  if (!in) return;
   float run[4];
+  int fw[4];
+  bool keep[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int e = e0 + j;
-    const int omega = e / st::SLOT_FLOATS, reg = (e / 64) % st::SLOT_REGS, lane = e & 63;
+    const int reg = (e / 64) % st::SLOT_REGS, lane = e & 63;
     int f = 0, w = 0;
-    bool valid = false, primary;
-    if (in) state_elem(omega, reg, lane, f, w, valid, primary);
-    run[j] = (state && valid) ? state[(size_t)unit * STATE_FLOATS + (size_t)w * DS + f] : 0.f;
+    bool valid = false, primary = false;
+    state_elem(omega, reg, lane, f, w, valid, primary);
+    fw[j] = w * DS + f;
+    keep[j] = valid && primary;
+    run[j] = (init && valid) ? init[(size_t)unit * STATE_FLOATS + fw[j]] : 0.f;
   }
-  if (state && bound) {
-    // max |H_init| of the unit: wave maximum, one atomic per wave (non-negative
-    // floats order like their bit patterns)
-    float m = fmaxf(fmaxf(fabsf(run[0]), fabsf(run[1])), fmaxf(fabsf(run[2]), fabsf(run[3])));
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
-    if ((threadIdx.x & 63) == 0 && m > 0.f)
-      atomicMax(reinterpret_cast<unsigned int*>(bound) + unit, __float_as_uint(m));
-  }
-  if (!in) return;
   float4 r = make_float4(run[0], run[1], run[2], run[3]);
   const size_t base = (size_t)unit * n_seg * st::UNIT_SEG_FLOATS + e0;
   // the loads of SB segments are issued together: one at a time, each thread
@@ -627,31 +662,29 @@ k_state_segscan(int n_seg, float* __restrict__ segsum, float* __restrict__ segpr
 #pragma unroll
     for (int j = 0; j < SB; ++j)
       if (s0 + j < n_seg) {
-        if (segpre) *reinterpret_cast<float4*>(segpre + base + (size_t)(s0 + j) * st::UNIT_SEG_FLOATS) = r;
+        if (segpre) {
+          const size_t us = (size_t)unit * n_seg + s0 + j;
+          if (omega < 24) {
+            const f16x2 lo = __builtin_convertvector((f32x2){r.x * tscale, r.y * tscale}, f16x2);
+            const f16x2 hi = __builtin_convertvector((f32x2){r.z * tscale, r.w * tscale}, f16x2);
+            *reinterpret_cast<uint2*>(segpre + us * st::QUAD_SEG_FLOATS + e0) =
+                make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
+          } else {
+            *reinterpret_cast<float4*>(sidepre + us * st::SLOT_FLOATS + (e0 - 24 * st::SLOT_FLOATS)) = r;
+          }
+        }
         r.x += a[j].x;
         r.y += a[j].y;
         r.z += a[j].z;
         r.w += a[j].w;
       }
   }
-  // the final value goes through segment 0's slot (no longer read): mirrored
-  // elements of other threads may still read the initial state here
-  if (write_final) *reinterpret_cast<float4*>(segsum + base) = r;
-}
-
-// Final state (canonical layout) from the totals left in segment 0's slot.
-__global__ void __launch_bounds__(256)
-k_state_final(int n_seg, const float* __restrict__ segsum, float* __restrict__ state) {
-  const int unit = blockIdx.y;
-  const int e = blockIdx.x * blockDim.x + threadIdx.x;
-  if (e >= st::UNIT_SEG_FLOATS) return;
-  const int omega = e / st::SLOT_FLOATS, reg = (e / 64) % st::SLOT_REGS, lane = e & 63;
-  int f = 0, w = 0;
-  bool valid, primary;
-  state_elem(omega, reg, lane, f, w, valid, primary);
-  if (valid && primary)
-    state[(size_t)unit * STATE_FLOATS + (size_t)w * DS + f] =
-        segsum[(size_t)unit * n_seg * st::UNIT_SEG_FLOATS + e];
+  if (state) {
+    const float fin[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (keep[j]) state[(size_t)unit * STATE_FLOATS + fw[j]] = fin[j];
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -665,12 +698,47 @@ static int choose_segments(int units, int n_chunks) {
   return s;
 }
 
-static size_t kvmax_bytes(int units, int n_seg) {
-  return ((size_t)units * n_seg * KVP * 2 * sizeof(float) + 255) / 256 * 256;
-}
-
 static size_t stage_bytes(int units, int seq_len) {
   return (size_t)units * ((seq_len + st::TB - 1) / st::TB) * st::STG_BYTES;
+}
+
+static size_t round256(size_t b) { return (b + 255) / 256 * 256; }
+
+// Scratch of the builder, in this order: segment sums, the segments' max |k| and
+// |v|, the staged blocks, the initial state's copy, then (with tiles) the
+// quadratic and side starting prefixes and the tile-scale bound.
+struct StateWs {
+  float* segsum;
+  float* kvmax;
+  uint8_t* stg;
+  float* init;
+  uint16_t* segpre;
+  float* sidepre;
+  float* bound;
+  size_t bytes;
+};
+
+static StateWs state_ws(void* ws, int units, int seq_len, int n_seg, bool with_tiles) {
+  const int n_blk = (seq_len + st::TB - 1) / st::TB;
+  const int nip = n_seg * KVP;
+  StateWs w{};
+  size_t off = 0;
+  auto take = [&](size_t b) {
+    uint8_t* p = ws ? reinterpret_cast<uint8_t*>(ws) + off : nullptr;
+    off += round256(b);
+    return p;
+  };
+  w.segsum = reinterpret_cast<float*>(take((size_t)units * n_seg * st::UNIT_SEG_FLOATS * sizeof(float)));
+  w.kvmax = reinterpret_cast<float*>(take((size_t)units * n_seg * KVP * 2 * sizeof(float)));
+  w.stg = take(stage_bytes(units, seq_len));
+  w.init = reinterpret_cast<float*>(take((size_t)units * STATE_FLOATS * sizeof(float)));
+  if (with_tiles) {
+    w.segpre = reinterpret_cast<uint16_t*>(take((size_t)units * n_seg * st::QUAD_SEG_FLOATS * sizeof(uint16_t)));
+    w.sidepre = reinterpret_cast<float*>(take((size_t)units * n_seg * st::SLOT_FLOATS * sizeof(float)));
+    w.bound = reinterpret_cast<float*>(take((size_t)units * (n_blk + nip) * sizeof(float)));
+  }
+  w.bytes = off;
+  return w;
 }
 
 size_t state_mfma_workspace(int batch, int n_kv_heads, int seq_len, int chunk, bool with_tiles) {
@@ -679,20 +747,14 @@ size_t state_mfma_workspace(int batch, int n_kv_heads, int seq_len, int chunk, b
   const int n_seg = choose_segments(units, n_chunks);
   const int cps = (n_chunks + n_seg - 1) / n_seg;
   const int n_seg_eff = (n_chunks + cps - 1) / cps;
-  const int n_blk = (seq_len + st::TB - 1) / st::TB;
-  size_t bytes = (with_tiles ? 2 : 1) * (size_t)units * n_seg_eff * st::UNIT_SEG_FLOATS * sizeof(float);
-  bytes += kvmax_bytes(units, n_seg_eff) + stage_bytes(units, seq_len);
-  if (with_tiles) {
-    bytes += (size_t)units * n_chunks * tile::BYTES;
-    bytes += ((size_t)units * (n_blk + 1) * sizeof(float) + 255) / 256 * 256;   // scale bound
-  }
+  size_t bytes = state_ws(nullptr, units, seq_len, n_seg_eff, with_tiles).bytes;
+  if (with_tiles) bytes += (size_t)units * n_chunks * tile::BYTES;
   return bytes;
 }
 
 // Builds the per-chunk prefix tiles (when ts != null) and the final state (when
 // state != null; its content on entry is the initial state).  ws: the scratch part
-// of state_mfma_workspace (segment sums, the segments' max |k| and |v|, the staged
-// blocks, then the segment prefixes and the tile-scale bound).
+// of state_mfma_workspace (see state_ws).
 oal_status launch_state_mfma(int batch, int n_kv_heads, int seq_len, int chunk, const void* k,
                              const void* v, float* state, uint8_t* ts, void* ws,
                              hipStream_t stream) {
@@ -702,56 +764,50 @@ oal_status launch_state_mfma(int batch, int n_kv_heads, int seq_len, int chunk, 
   const int cps = (n_chunks + n_seg - 1) / n_seg;
   const int n_seg_eff = (n_chunks + cps - 1) / cps;
   const int n_blk = (seq_len + st::TB - 1) / st::TB;
+  const int nip = n_seg_eff * KVP;
   const uint16_t* kk = reinterpret_cast<const uint16_t*>(k);
   const uint16_t* vv = reinterpret_cast<const uint16_t*>(v);
   const dim3 grid((units * n_seg_eff + 7) / 8 * 8 * st::NWG);
-  float* segsum = reinterpret_cast<float*>(ws);
-  float* kvmax = segsum + (size_t)units * n_seg_eff * st::UNIT_SEG_FLOATS;
-  uint8_t* stg = reinterpret_cast<uint8_t*>(kvmax) + kvmax_bytes(units, n_seg_eff);
-  float* segpre = reinterpret_cast<float*>(stg + stage_bytes(units, seq_len));
-  float* bound = ts ? segpre + (size_t)units * n_seg_eff * st::UNIT_SEG_FLOATS : nullptr;
+  const StateWs w = state_ws(ws, units, seq_len, n_seg_eff, ts != nullptr);
   {
     ProfScope ps("k_state_kvmax", stream);
-    hipLaunchKernelGGL(k_state_kvmax, dim3(n_seg_eff * KVP, units), dim3(256), 0, stream, seq_len, chunk,
-                       n_chunks, cps, kk, vv, kvmax);
+    hipLaunchKernelGGL(k_state_kvmax, dim3(nip, units), dim3(256), 0, stream, seq_len, chunk,
+                       n_chunks, cps, kk, vv, w.kvmax, (const float*)state, w.init,
+                       ts ? w.bound + (size_t)units * n_blk : (float*)nullptr);
     oal_status s = check_launch("k_state_kvmax");
     if (s != OAL_OK) return s;
   }
   {
     ProfScope ps("k_state_stage", stream);
     hipLaunchKernelGGL(k_state_stage, dim3(n_blk, units), dim3(256), 0, stream, seq_len, chunk, n_seg_eff,
-                       cps, kk, vv, (const float*)kvmax, stg, bound, units);
+                       cps, kk, vv, (const float*)w.kvmax, w.stg, w.bound);
     oal_status s = check_launch("k_state_stage");
     if (s != OAL_OK) return s;
   }
   {
     ProfScope ps("k_state_seg", stream);
     hipLaunchKernelGGL(k_state_mfma<0>, grid, dim3(256), 0, stream, seq_len, chunk, n_chunks,
-                       n_seg_eff, cps, n_blk, (const uint8_t*)stg, segsum, (uint8_t*)nullptr,
-                       (const float*)nullptr, (const float*)kvmax, units);
+                       n_seg_eff, cps, n_blk, (const uint8_t*)w.stg, w.segsum, (const uint16_t*)nullptr,
+                       (const float*)nullptr, (uint8_t*)nullptr, (const float*)nullptr,
+                       (const float*)w.kvmax, units, nip);
     oal_status s = check_launch("k_state_seg");
     if (s != OAL_OK) return s;
   }
   {
     ProfScope ps("k_state_segscan", stream);
     hipLaunchKernelGGL(k_state_segscan, dim3((st::UNIT_SEG_FLOATS / 4 + 255) / 256, units), dim3(256),
-                       0, stream, n_seg_eff, segsum, ts ? segpre : (float*)nullptr,
-                       (const float*)state, state != nullptr ? 1 : 0, bound);
+                       0, stream, n_seg_eff, (const float*)w.segsum, w.segpre, w.sidepre,
+                       state ? (const float*)w.init : (const float*)nullptr, state,
+                       (const float*)w.bound, n_blk, nip);
     oal_status s = check_launch("k_state_segscan");
-    if (s != OAL_OK) return s;
-  }
-  if (state != nullptr) {
-    ProfScope ps("k_state_final", stream);
-    hipLaunchKernelGGL(k_state_final, dim3((st::UNIT_SEG_FLOATS + 255) / 256, units), dim3(256), 0,
-                       stream, n_seg_eff, (const float*)segsum, state);
-    oal_status s = check_launch("k_state_final");
     if (s != OAL_OK) return s;
   }
   if (ts == nullptr) return OAL_OK;
   ProfScope ps("k_state_mfma", stream);
   hipLaunchKernelGGL(k_state_mfma<1>, grid, dim3(256), 0, stream, seq_len, chunk, n_chunks,
-                     n_seg_eff, cps, n_blk, (const uint8_t*)stg, segpre, ts, (const float*)bound,
-                     (const float*)kvmax, units);
+                     n_seg_eff, cps, n_blk, (const uint8_t*)w.stg, w.segsum, (const uint16_t*)w.segpre,
+                     (const float*)w.sidepre, ts, (const float*)w.bound, (const float*)w.kvmax, units,
+                     nip);
   return check_launch("k_state_mfma");
 }
 
