@@ -340,6 +340,42 @@ def cpu_baseline(w, seconds):
                        f"scaled to all {w.n_q_heads} query heads x {w.seq_len} rows")}
 
 
+def measured_peaks(device):
+    """Achievable rates on this GPU beside the datasheet peaks: a large bf16 GEMM
+    through torch.matmul (hipBLASLt) and a device-to-device copy."""
+    import torch
+    n = 8192
+    a = torch.randn(n, n, device=device, dtype=torch.bfloat16)
+    b = torch.randn(n, n, device=device, dtype=torch.bfloat16)
+    for _ in range(3):
+        torch.matmul(a, b)
+    reps = 20
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        torch.matmul(a, b)
+    e1.record()
+    torch.cuda.synchronize()
+    gemm_s = e0.elapsed_time(e1) * 1e-3 / reps
+    del a, b
+    nbytes = 1 << 30
+    src = torch.empty(nbytes, dtype=torch.uint8, device=device).fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    copy_s = e0.elapsed_time(e1) * 1e-3 / reps
+    return {"gemm_bf16_8192_tflops": round(2 * n ** 3 / gemm_s / 1e12, 1),
+            "copy_1gib_gbps": round(2 * nbytes / copy_s / 1e9, 1),
+            "note": "copy counts bytes read + written; datasheet: 2500 TFLOP/s bf16, 8000 GB/s"}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -421,6 +457,18 @@ def main() -> int:
         ms1, _ = bench_prefill(oal, w1, args.chunk, args.steps, args.warmup, device)
         result["linear_time_check"] = {"ms_n2048": round(ms1, 5), "ms_n32768": round(ms, 5),
                                        "ratio": round(ms / ms1, 3), "ideal_ratio": 16.0}
+        w2 = synth.WORKLOADS[2]
+        log(f"prefill: {w2.name}, chunk {args.chunk}")
+        ms2, kt2 = bench_prefill(oal, w2, args.chunk, args.steps, args.warmup, device)
+        fl2 = prefill_flops_per_token(w2.n_q_heads, w2.n_kv_heads, args.chunk)["total"] * w2.batch * w2.seq_len
+        result["prefill_llama_b4_n4096"] = {
+            "workload": w2.name, "chunk": args.chunk, "ms_per_step": round(ms2, 5),
+            "tokens_per_s": round(w2.batch * w2.seq_len / (ms2 * 1e-3), 1),
+            "tflops": round(fl2 / (ms2 * 1e-3) / 1e12, 3),
+            "frac_bf16_peak": round(fl2 / (ms2 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 5),
+            "kernels_ms": {k: round(v["avg_ms"], 5) for k, v in kt2.items()}}
+        log("measured peaks: bf16 GEMM (hipBLASLt) and a device copy")
+        result["measured_peaks"] = measured_peaks(device)
     if not args.no_decode and args.only is None:
         log("decode: setting up")
         result["decode"] = bench_decode(oal, synth.WORKLOADS[4], args.decode_reps,
