@@ -44,7 +44,7 @@ struct ReadoutCfg {
   static constexpr int WPH = CH / 64;               // waves per head
   static constexpr int HPW = 4 / WPH;               // heads per workgroup
   static constexpr int HS_BYTES = 4 * tile::KS_BYTES;   // one half-slab = 4 K-steps = 8 KB
-  static constexpr int NHS = tile::NKS / 4;         // 41 half-slabs per tile
+  static constexpr int NHS = tile::NKS / 4;         // 37 half-slabs per tile
   static constexpr int Q_BYTES = HPW * CH * 128;    // = 32 KB
   static constexpr int XB = CH == 256 ? HS_BYTES : 16;   // extra staging arrays (C = 256)
 };
@@ -322,6 +322,34 @@ k_readout_mfma(int n_q_heads, int n_kv_heads, int seq_len, int n_chunks, int n_h
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = splat16(0.f);
 
+  // Half-slab hs of the tile goes to buffer hs % 4 by direct-to-LDS buffer loads,
+  // three half-slabs ahead of the one being read (the buffers hold k and v^T
+  // until the intra-chunk part is done).  Each wave moves two 1 KB pieces of a
+  // half-slab, lane l writing bytes 16 l .. 16 l + 15 of a piece,
+  // fetched from the tile position that the swizzle of slab_off puts there.
+  // The loads are issued from inline assembly: the compiler then neither waits
+  // for them before LDS reads it cannot prove disjoint from the buffers, nor
+  // before rewriting their operand registers.  Their completion is awaited by
+  // hand (wait_vmcnt) before the barrier that hands a buffer to the waves;
+  // other memory operations of the wave complete in issue order with them, so
+  // the compiler's own counts stay safe (only stricter).
+  uint32_t dma_off[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int piece = wave * 2 + i;                 // 1 KB piece of the half-slab
+    const int kk = piece >> 1, pos = (piece & 1) * 64 + lane;
+    const int w = pos >> 1, hh = (pos & 1) ^ slab_flip(w);
+    dma_off[i] = kk * tile::KS_BYTES + w * 32 + hh * 16;
+  }
+  const i32x4 tile_rsrc = buffer_rsrc(tsrc, (uint32_t)tile::TILE_BYTES);
+  auto buf = [&](int hs) -> uint8_t* { return pick4(hs & 3, s_b0, s_b1, s_b2, s_b3); };
+  auto issue = [&](int hs, uint8_t* buf) {
+    const int soff = min(hs, Cfg::NHS - 1) * Cfg::HS_BYTES;
+    const uint32_t dst = lds_addr(buf) + wave * 2048;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) load_lds16(tile_rsrc, dst + i * 1024, dma_off[i], soff);
+  };
+
   // ================= intra-chunk part ======================================
   // kappa^T[key][tok] F = eps F + sum_p t_p^2,  t_p = sqrt(F) (L_0p + sum_r ell_p[r] q_r k_r),
   // then the causal mask and u~^T += [V; 1]^T kappa^T (values on the matrix cores,
@@ -455,33 +483,9 @@ k_readout_mfma(int n_q_heads, int n_kv_heads, int seq_len, int n_chunks, int n_h
 
   // ================= inter-chunk part ======================================
   __syncthreads();   // the half-slab buffers held k / v^T
-  // Half-slab hs of the tile goes to buffer hs % 4 by direct-to-LDS buffer loads:
-  // each wave moves two 1 KB pieces, lane l writing bytes 16 l .. 16 l + 15 of a
-  // piece, fetched from the tile position that the swizzle of slab_off puts there.
-  // The loads are issued from inline assembly: the compiler then neither waits
-  // for them before LDS reads it cannot prove disjoint from the buffers, nor
-  // before rewriting their operand registers.  Their completion is awaited by
-  // hand (wait_vmcnt) before the barrier that hands a buffer to the waves;
-  // other memory operations of the wave complete in issue order with them, so
-  // the compiler's own counts stay safe (only stricter).
-  uint32_t dma_off[2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int piece = wave * 2 + i;                 // 1 KB piece of the half-slab
-    const int kk = piece >> 1, pos = (piece & 1) * 64 + lane;
-    const int w = pos >> 1, hh = (pos & 1) ^ slab_flip(w);
-    dma_off[i] = kk * tile::KS_BYTES + w * 32 + hh * 16;
-  }
-  const i32x4 tile_rsrc = buffer_rsrc(tsrc, (uint32_t)tile::TILE_BYTES);
-  auto issue = [&](int hs, uint8_t* buf) {
-    const int soff = min(hs, Cfg::NHS - 1) * Cfg::HS_BYTES;
-    const uint32_t dst = lds_addr(buf) + wave * 2048;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) load_lds16(tile_rsrc, dst + i * 1024, dma_off[i], soff);
-  };
-  issue(0, s_b0);
-  issue(1, s_b1);
-  issue(2, s_b2);
+  issue(0, buf(0));
+  issue(1, buf(1));
+  issue(2, buf(2));
 
   // ---- inter-chunk denominator: a z0 + sum_r q_r (b'_r z1_r + ((C / d_h o Z) q)_r),
   //      T = b' o z1 + (C/d_h o Z) q^T on the matrix cores (the first term as the
@@ -535,12 +539,14 @@ k_readout_mfma(int n_q_heads, int n_kv_heads, int seq_len, int n_chunks, int n_h
     for (int nt = 0; nt < 2; ++nt) den[nt] += dd[nt] * sc + az0 * F;
   }
 
-  // ---- main K loop over the 41 half-slabs: 1 linear, then 4 (c + 1) per t-block c;
-  //      quadratic half-slab hs = 1 + 2 c (c + 1) + h sits in buffer (1 + h) % 4
-  const uint8_t* mgh = reinterpret_cast<const uint8_t*>(s_mg + hslot * LDIM * DH) + 16 * half;
+  // ---- main K loop over the 37 half-slabs: 1 linear, then 4 c + 3 per t-block c
+  //      (the last of them the merged rows of the diagonal block); half-slab hs
+  //      sits in buffer hs % 4
+  const uint8_t* mgh0 = reinterpret_cast<const uint8_t*>(s_mg + hslot * LDIM * DH);
+  const uint8_t* mgh = mgh0 + 16 * half;
   f16x8 qt[2], qh[2];
   int cur = -1;
-  // one quadratic half-slab: K-steps (r0 + i, c), i = 0..3
+  // one half-slab of rows r0 .. r0 + 3 of t-block c: K-steps (r0 + i, c)
   auto quad = [&](int c, int h, const uint8_t* sb) {
     const int r0 = 4 * h;
     // the state fragments of all four K-steps first, so that their LDS latency
@@ -551,8 +557,9 @@ k_readout_mfma(int n_q_heads, int n_kv_heads, int seq_len, int n_chunks, int n_h
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
         af[i][mt] = *reinterpret_cast<const f16x8*>(sb + slab_off(i, 32 * mt + col, half));
-    // m q_r of r0 .. r0 + 3 (m = 2 off the diagonal 16-block), scaled, as fp16
-    const float qs = r0 < 16 * c ? 2.0f * qr_scale : qr_scale;
+    // m q_r of r0 .. r0 + 3, scaled, as fp16: m = 2 off the diagonal 16-block and
+    // for its upper t-half (whose mirrored pairs are not stored), 1 otherwise
+    const float qs = (r0 < 16 * c || half == 1) ? 2.0f * qr_scale : qr_scale;
     _Float16 qr[2][4];
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
@@ -586,12 +593,50 @@ k_readout_mfma(int n_q_heads, int n_kv_heads, int seq_len, int n_chunks, int n_h
       }
     }
   };
+  // the merged half-slab of t-block c: K-step i holds rows 16 c + 8 + 2 i + half
+  // against t = 16 c + 8 .. 16 c + 15 in both lane halves (multiplicity 1)
+  auto quad_merged = [&](int c, const uint8_t* sb) {
+    f16x8 af[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+        af[i][mt] = *reinterpret_cast<const f16x8*>(sb + slab_off(i, 32 * mt + col, half));
+    f16x8 qu[2];          // q_t, t = 16 c + 8 .. + 7, times qt_scale
+    _Float16 qr[2][4];    // q_r, r = 16 c + 8 + 2 i + half, times qr_scale
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      const bf16x8 qv = *reinterpret_cast<const bf16x8*>((nt ? qrow1 : qrow0).chunk(2 * c + 1));
+#pragma unroll
+      for (int j = 0; j < 8; j += 2) {
+        const f16x2 hv = __builtin_convertvector((f32x2){bf(qv[j]) * qt_scale, bf(qv[j + 1]) * qt_scale}, f16x2);
+        qu[nt][j] = hv[0];
+        qu[nt][j + 1] = hv[1];
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) qr[nt][i] = (_Float16)(bf(half ? qv[2 * i + 1] : qv[2 * i]) * qr_scale);
+    }
+    const uint8_t* mgc = mgh0 + 32 * c + 16;   // M rows at t = 16 c + 8 .. + 7
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int g0 = __builtin_amdgcn_readlane(gl, 16 * c + 8 + 2 * i);
+      const int g1 = __builtin_amdgcn_readlane(gl, 16 * c + 9 + 2 * i);
+      const f16x8 m8 = *reinterpret_cast<const f16x8*>(mgc + (half ? g1 : g0) * (DH * 2));
+      const f16x8 f0 = (qu[0] * m8) * qr[0][i];
+      const f16x8 f1 = (qu[1] * m8) * qr[1][i];
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+        acc[mt][0] = mfma32h(af[i][mt], f0, acc[mt][0]);
+        acc[mt][1] = mfma32h(af[i][mt], f1, acc[mt][1]);
+      }
+    }
+  };
   auto main_loop = [&](auto compute_t) {
     constexpr bool COMPUTE = decltype(compute_t)::value;
     // linear half-slab (buffer 0): phi = b'_r F_f q_r, r = 16 ks + 8 half + j
     wait_vmcnt<4>();
     barrier_nofence();
-    issue(3, s_b3);
+    issue(3, buf(3));
     if (COMPUTE) {
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
@@ -611,7 +656,7 @@ k_readout_mfma(int n_q_heads, int n_kv_heads, int seq_len, int n_chunks, int n_h
         }
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) {
-          const f16x8 af = *reinterpret_cast<const f16x8*>(s_b0 + slab_off(ks, 32 * mt + col, half));
+          const f16x8 af = *reinterpret_cast<const f16x8*>(buf(0) + slab_off(ks, 32 * mt + col, half));
           acc[mt][0] = mfma32h(af, fb[0], acc[mt][0]);
           acc[mt][1] = mfma32h(af, fb[1], acc[mt][1]);
         }
@@ -633,24 +678,17 @@ k_readout_mfma(int n_q_heads, int n_kv_heads, int seq_len, int n_chunks, int n_h
         }
         cur = -1;
       }
-      for (int h = 0; h < 4 * (c + 1); h += 4, hs += 4) {
+      for (int h = 0; h < 4 * c + 2; ++h, ++hs) {
         wait_vmcnt<4>();
         barrier_nofence();
-        issue(hs + 3, s_b0);
-        if (COMPUTE) quad(c, h, s_b1);
-        wait_vmcnt<4>();
-        barrier_nofence();
-        issue(hs + 4, s_b1);
-        if (COMPUTE) quad(c, h + 1, s_b2);
-        wait_vmcnt<4>();
-        barrier_nofence();
-        issue(hs + 5, s_b2);
-        if (COMPUTE) quad(c, h + 2, s_b3);
-        wait_vmcnt<4>();
-        barrier_nofence();
-        issue(hs + 6, s_b3);
-        if (COMPUTE) quad(c, h + 3, s_b0);
+        issue(hs + 3, buf(hs + 3));
+        if (COMPUTE) quad(c, h, buf(hs));
       }
+      wait_vmcnt<4>();
+      barrier_nofence();
+      issue(hs + 3, buf(hs + 3));
+      if (COMPUTE) quad_merged(c, buf(hs));
+      ++hs;
     }
     wait_vmcnt<0>();   // the last (repeated) prefetches
   };

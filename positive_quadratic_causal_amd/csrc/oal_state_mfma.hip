@@ -406,13 +406,19 @@ k_state_mfma(int seq_len, int chunk, int n_chunks, int n_seg, int cps, int n_blk
                                     : 0.f;
     const float wscale = unscale * tscale;   // accumulator -> tile entry
 
-    // Tile stores issued per chunk start (wave-uniform): 2 per (m, row group)
-    // inside the tiled layout.
+    // Whether rows t = 32 tb + 8 gq .. + 7 of item r are in the tiled layout
+    // (wave-uniform): not below r's 16-block, and not the lower half of the
+    // diagonal block for the merged rows of its upper half.
+    auto stored = [&](int r, int gq) {
+      const int cblk = 2 * tb + (gq >> 1);   // t >> 4
+      return cblk > (r >> 4) || (cblk == (r >> 4) && (!tile::quad_merged(r, cblk) || (gq & 1)));
+    };
+    // Tile stores issued per chunk start (wave-uniform): 2 per stored (m, row group).
     int nst = 0;
 #pragma unroll
     for (int m = 0; m < 4; ++m)
 #pragma unroll
-      for (int gq = 0; gq < 4; ++gq) nst += (2 * tb + (gq >> 1)) < ((r0 + m) >> 4) ? 0 : 2;
+      for (int gq = 0; gq < 4; ++gq) nst += stored(r0 + m, gq) ? 2 : 0;
     auto stores_at = [&](int b) { return (MODE == 1 && b >= 0 && (b * st::TB) % chunk == 0) ? nst : 0; };
 
     auto body = [&](int bi, const uint8_t* cur, uint8_t* nxt) {
@@ -437,9 +443,10 @@ k_state_mfma(int seq_len, int chunk, int n_chunks, int n_seg, int cps, int n_blk
             for (int gq = 0; gq < 4; ++gq) {
               const int t = 32 * tb + 8 * gq + 4 * half;   // rows t .. t+3
               const int cblk = 2 * tb + (gq >> 1);           // t >> 4, wave-uniform
-              if (cblk < (r >> 4)) continue;               // not in the tiled layout
-              const int ks_ = tile::quad_base(cblk) + r;
-              *reinterpret_cast<uint2*>(tl + (size_t)ks_ * 1024 + w * 16 + (t & 15)) =
+              if (!stored(r, gq)) continue;
+              const int ks_ = tile::quad_ks(r, cblk);
+              const int el = tile::quad_merged(r, cblk) ? 8 * (r & 1) + (t & 7) : (t & 15);
+              *reinterpret_cast<uint2*>(tl + (size_t)ks_ * 1024 + w * 16 + el) =
                   pack4_f16(acc[m][nt][4 * gq], acc[m][nt][4 * gq + 1], acc[m][nt][4 * gq + 2],
                             acc[m][nt][4 * gq + 3], wscale);
             }

@@ -6,16 +6,20 @@
 // evaluated on v_mfma_f32_32x32x16_f16 with the state as the A operand (rows w)
 // and the query features as the B operand (columns = tokens).  The K dimension
 // (features) is cut into K-steps of 16 rows:
-//   K-steps 0..3         linear rows H1_r, r = 16 ks + j                (j = 0..15)
-//   K-steps 4..163       quadratic rows H2_rt for the item (r, c) with
-//                        t = 16 c + j, c = 0..3, r = 0..16 c + 15; items are
-//                        ordered by c, then r (K-step = 4 + 8 c (c + 1) + r).
-// In the diagonal 16-block (r / 16 == c) all ordered pairs are kept (so H2_rt and
-// H2_tr both appear, each read with multiplicity 1); off the diagonal only t > r
-// is stored and read with multiplicity 2 ([OAL] App. D: packed-symmetric states,
-// multiplicity one on the diagonal and two off it).  Every K-step has a single r,
-// so the query feature c_rt q_r q_t / d_h of a K-step is (m q_r) * qhat_{g(r)}[t]
-// with qhat_gamma[t] = q_t M_{gamma, g(t)} / d_h precomputed per 16-wide t-block.
+//   K-steps 0..3      linear rows H1_r, r = 16 ks + j                  (j = 0..15)
+//   then, per t-block c = 0..3 (t = 16 c + j), 16 c + 12 K-steps from quad_base(c):
+//     r = 0 .. 16 c + 7     one K-step per r (quad_base(c) + r), element j = H2_rt
+//     r = 16 c + 8 + 2 s + e (s = 0..3, e = 0, 1): K-step quad_base(c) + 16 c + 8 + s,
+//                           element 8 e + jj = H2_rt at t = 16 c + 8 + jj
+// Symmetric pairs follow [OAL] App. D (packed states: multiplicity one on the
+// diagonal, two off it).  Off the diagonal 16-block (r < 16 c) only t > r is
+// stored, read with multiplicity 2.  In the diagonal block, rows r = 16 c + i
+// with i < 8 keep all 16 t's: for t < 16 c + 8 both orders of a pair are present
+// (multiplicity 1 each), for t >= 16 c + 8 only this one (multiplicity 2); rows
+// with i >= 8 keep only t >= 16 c + 8, where again both orders are present, and
+// two such rows share a K-step.  Every half K-step (8 elements) has a single r,
+// so the query feature c_rt q_r q_t / d_h of it is (m q_r) * qhat_{g(r)}[t] with
+// qhat_gamma[t] = q_t M_{gamma, g(t)} / d_h per 8-wide t-range.
 // Layout of one K-step: [w = 0..63][j = 0..15] fp16 (2 KB).  The fp16 values are
 // H * 2^-e_S with one exponent e_S per (unit, call), chosen from a bound on |H|
 // (see oal_state_mfma.hip) so that every entry stays below 2^15; the readout
@@ -34,40 +38,27 @@ namespace oal {
 namespace tile {
 
 constexpr int NKS_LIN = 4;
-constexpr int NKS = 164;
+constexpr int NKS = 148;
 constexpr int KS_BYTES = 64 * 16 * 2;                  // one K-step, fp16
-constexpr size_t TILE_BYTES = (size_t)NKS * KS_BYTES;  // 335872
+constexpr size_t TILE_BYTES = (size_t)NKS * KS_BYTES;  // 303104
 constexpr int SIDE_H0 = 0;       // [64] sum v (value channels of H0)
 constexpr int SIDE_Z1 = 64;      // [64] sum k_r
 constexpr int SIDE_Z0 = 128;     // token count
 constexpr int SIDE_SEXP = 129;   // e_S: the fp16 entries are H * 2^-e_S (then padding to 192)
 constexpr int SIDE_Z = 192;      // [64][64] sum k_r k_t
 constexpr int SIDE_FLOATS = SIDE_Z + DH * DH;           // 4288
-constexpr size_t BYTES = TILE_BYTES + (size_t)SIDE_FLOATS * 4;   // 353024 = 1379 * 256
+constexpr size_t BYTES = TILE_BYTES + (size_t)SIDE_FLOATS * 4;   // 320256 = 1251 * 256
 
-__host__ __device__ constexpr int quad_base(int c) { return NKS_LIN + 8 * c * (c + 1); }
+// First K-step of t-block c (c = 4: the end of the tile).
+__host__ __device__ constexpr int quad_base(int c) { return NKS_LIN + 8 * c * c + 4 * c; }
+static_assert(quad_base(4) == NKS, "K-step count");
 
-__host__ __device__ inline int ks_block(int ks) {   // c of a quadratic K-step
-  return ks >= quad_base(3) ? 3 : ks >= quad_base(2) ? 2 : ks >= quad_base(1) ? 1 : 0;
+// K-step that holds row r of t-block c (r < 16 c + 16); element of t in it: t % 16,
+// or for the merged rows (r - 16 c >= 8, t % 16 >= 8 only) 8 (r % 2) + t % 8.
+__host__ __device__ constexpr int quad_ks(int r, int c) {
+  return quad_base(c) + (r - 16 * c < 8 ? r : 16 * c + 8 + ((r - 16 * c - 8) >> 1));
 }
-
-// Canonical state row (see oal_common.h) of element j of K-step ks.
-__host__ __device__ inline int canon_row(int ks, int j) {
-  if (ks < NKS_LIN) return 1 + 16 * ks + j;
-  const int c = ks_block(ks);
-  const int r = ks - quad_base(c);
-  const int t = 16 * c + j;
-  const int a = r < t ? r : t, b = r < t ? t : r;
-  return 1 + DH + pair_index(a, b);
-}
-
-// True when element j of K-step ks is the stored copy of a canonical row (the
-// diagonal blocks also hold the mirrored pairs t < r).
-__host__ __device__ inline bool canon_primary(int ks, int j) {
-  if (ks < NKS_LIN) return true;
-  const int c = ks_block(ks);
-  return ks - quad_base(c) <= 16 * c + j;
-}
+__host__ __device__ constexpr bool quad_merged(int r, int c) { return r - 16 * c >= 8; }
 
 }  // namespace tile
 
