@@ -128,6 +128,7 @@ k_readout_mfma(int n_q_heads, int n_kv_heads, int seq_len, int n_chunks, int n_h
   __shared__ __attribute__((aligned(16))) _Float16 s_mg[Cfg::HPW * LDIM * DH];
   __shared__ __attribute__((aligned(16))) float s_ht[Cfg::HPW * htab::FLOATS];
   __shared__ float s_red[16];
+  __shared__ __attribute__((aligned(16))) float s_h0[DV];   // H0 of the chunk's prefix
   // k rows (64 per array) and v^T rows (64 keys per array) of the chunk
   auto k_arr = [&](int i) -> uint8_t* { return pick4(i, s_b0, s_b1, s_b2, s_b3); };
   auto v_arr = [&](int i) -> uint8_t* {
@@ -196,6 +197,7 @@ k_readout_mfma(int n_q_heads, int n_kv_heads, int seq_len, int n_chunks, int n_h
   const float l0v = rec[OAL_COEF_L + min(lane, LDIM - 1)];           // L_{0,lane}
   const float l1v = rec[OAL_COEF_L + LDIM + min(lane, LDIM - 1)];    // L_{1,lane}
   const float z1v = ts_side[tile::SIDE_Z1 + lane];
+  const float h0v = ts_side[tile::SIDE_H0 + lane];   // read in the epilogue, from LDS
   const float esv = ts_side[tile::SIDE_SEXP];
 
   // ---- q tile, with each thread's max |q| per head
@@ -253,6 +255,7 @@ k_readout_mfma(int n_q_heads, int n_kv_heads, int seq_len, int n_chunks, int n_h
     const uint32_t m = wave_umax(qmax[hs]);
     if (lane == 0) s_red[wave * 4 + hs] = __uint_as_float(m << 16);
   }
+  if (wave == 0) s_h0[lane] = h0v;
   __syncthreads();
 
   // ---- the head's scales (identical in the waves of one head)
@@ -702,7 +705,6 @@ k_readout_mfma(int n_q_heads, int n_kv_heads, int seq_len, int n_chunks, int n_h
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt) den[nt] += __shfl_xor(den[nt], 32, 64);
   const float aF = rec[OAL_COEF_A] * F;
-  const float* h0 = ts_side + tile::SIDE_H0;
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt) {
     const int tok = tok0 + 32 * nt + col;
@@ -714,7 +716,7 @@ k_readout_mfma(int n_q_heads, int n_kv_heads, int seq_len, int n_chunks, int n_h
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         const int w0 = 32 * mt + 8 * g4 + 4 * half;
-        const float4 hv = *reinterpret_cast<const float4*>(h0 + w0);
+        const float4 hv = *reinterpret_cast<const float4*>(s_h0 + w0);
         const float o[4] = {(acc[mt][nt][4 * g4 + 0] + aF * hv.x) * inv, (acc[mt][nt][4 * g4 + 1] + aF * hv.y) * inv,
                             (acc[mt][nt][4 * g4 + 2] + aF * hv.z) * inv, (acc[mt][nt][4 * g4 + 3] + aF * hv.w) * inv};
         Elem<O>::store4(yr, w0, o);
