@@ -221,6 +221,26 @@ def test_prefill_chunk_invariance_and_determinism(oal):
             assert rel_l2(ys[c][0, h], ref[h]) <= tol_for(w)
 
 
+# The bf16 path rounds the intra-chunk weights kappa to bf16 for the P V product
+# (relative 2^-9 each) and the inter-chunk features and state tiles to fp16
+# (2^-11); the expected rel-L2 of an fp32 output is therefore about 2e-3.  A
+# bound three times that, well inside the 2e-2 bar, catches a structural slip
+# (a wrong multiplicity or a lost block of pairs) that the bar alone could let
+# through.
+MARGIN_F32_OUT = 6e-3
+
+
+@pytest.mark.parametrize("chunk", [64, 128, 256])
+def test_prefill_precision_margin(oal, chunk):
+    w = synth.WORKLOADS[1]
+    announce(f"precision margin Qwen-shaped 14/2 N=2048 bf16 in, fp32 out, chunk={chunk}")
+    case = Case(w)
+    y = torch.empty(case.q.shape, dtype=torch.float32, device="cuda")
+    oal.oal_prefill(case.q, case.k, case.v, case.coeffs(), chunk=chunk, y=y)
+    torch.cuda.synchronize()
+    _check_heads(case, y, [(0, h) for h in (0, 3, 6, 7, 10, 13)], MARGIN_F32_OUT)
+
+
 def test_prefill_llama_4096_sampled_heads(oal):
     w = synth.WORKLOADS[2]
     announce("prefill Llama-shaped 32/8 B=4 N=4096 bf16 chunk=128, sampled heads")
