@@ -9,21 +9,24 @@
 // (A = key products in fp16, two per packed multiply; B = V in fp16; both scaled
 // by powers of two taken from the segment's largest |k| and |v|).
 //
-// Work decomposition per (batch, KV head) unit and segment: 25 waves.
-//   waves 0..7  : quadratic rows (r, t), r in 4w .. 4w+3,        t in 0..31
-//   waves 8..23 : quadratic rows (r, t), r in 4(w-8) .. 4(w-8)+3, t in 32..63
-//   wave 24     : linear rows H1_r (A = K^T), the all-ones channel Z_rt = sum k_r k_t
-//                 (A = K^T, B = K), and H0 = sum v, z1 = sum k, z0 = count.
-// Each wave holds 4 x 2 accumulator tiles (128 rows x 64 channels).  Rows (r, t)
-// with t below r's 16-block are computed but never stored (the tiled layout keeps
-// their mirror images).  Waves 0..23 run identical code; wave 24 lives in a
-// workgroup of its own so that the two kinds of accumulators never share a loop.
+// Work decomposition per (batch, KV head) unit and segment: 7 workgroups of 4 waves.
+//   waves 0..23 (workgroups 0..5): the quadratic rows, as the 144 quadratic
+//                 K-steps of the tile layout (oal_tile.h) taken two at a time as
+//                 72 accumulator tiles of 32 rows, three per wave; row i of tile j
+//                 is element i % 16 of K-step 2 j + i / 16, so every accumulator
+//                 row is a stored tile row (the diagonal-block mirrors included)
+//                 and lane i forms the key products k_r k_t of its own pair.
+//   workgroup 6:  wave 0 the linear rows H1_r (A = K^T) and H0 = sum v, z1 = sum k,
+//                 z0 = count; wave 1 the all-ones channel Z_rt = sum k_r k_t
+//                 (A = K^T, B = K); waves 2, 3 only help copy the blocks.
+// Each computing wave holds 3 (quadratic) or 2 (side) accumulator tiles of 32
+// rows x 2 channel halves.
 //
 // The running prefix is summed into, and seeded from, per-(unit, segment) buffers
 // in the raw accumulator layout (sums in fp32; the starting prefixes of the
 // quadratic rows as fp16 in the tiles' scale, the precision they are stored in
-// anyway, those of wave 24 in fp32: the all-ones channel and H0 are not covered
-// by the tiles' bound); the segment-scan kernel
+// anyway, those of the side workgroup in fp32: the all-ones channel and H0 are
+// not covered by the tiles' bound); the segment-scan kernel
 // converts between that layout and the canonical state (initial state in, final
 // state out).
 // A batch-1 long sequence has too few units to fill 256 CUs, so the sequence is
@@ -42,21 +45,28 @@
 namespace oal {
 
 namespace st {
-constexpr int NWAVES = 25;              // compute waves per (unit, segment)
 constexpr int WAVES_PER_WG = 4;
-constexpr int NWG = (NWAVES + WAVES_PER_WG - 1) / WAVES_PER_WG;   // 7 workgroups
-constexpr int SLOT_REGS = 132;          // registers per wave in the seg buffers
-constexpr int SLOT_FLOATS = SLOT_REGS * 64;
-constexpr int UNIT_SEG_FLOATS = NWAVES * SLOT_FLOATS;   // one (unit, segment)
-constexpr int QUAD_SEG_FLOATS = 24 * SLOT_FLOATS;       // its quadratic waves
+constexpr int NWG = 7;                  // workgroups per (unit, segment): 6 quadratic, 1 side
+constexpr int QTILES = 3;               // accumulator tiles per quadratic wave
+static_assert(24 * QTILES * 2 == tile::NKS - tile::NKS_LIN, "two K-steps per tile");
+// Slots of the per-(unit, segment) buffers, in the raw accumulator layout
+// [register][lane]: quadratic wave omega at omega * QSLOT_FLOATS, then the side
+// slot (H1 registers 0..63 from wave 0, Z 64..127 from wave 1, then H0, z1, z0).
+constexpr int QSLOT_REGS = QTILES * 2 * 16;   // 96
+constexpr int QSLOT_FLOATS = QSLOT_REGS * 64;
+constexpr int SIDE_REGS = 132;
+constexpr int SIDE_FLOATS = SIDE_REGS * 64;
+constexpr int QUAD_SEG_FLOATS = 24 * QSLOT_FLOATS;             // the quadratic waves
+constexpr int UNIT_SEG_FLOATS = QUAD_SEG_FLOATS + SIDE_FLOATS;  // one (unit, segment)
 constexpr int TB = 64;                  // tokens staged per block
 constexpr int STG_BYTES = (DH + DV) * TB * 2;   // one staged block: k^T, v^T in fp16
 constexpr int REG_H0 = 128, REG_Z1 = 129, REG_Z0 = 130;
 }  // namespace st
 
 // Canonical location (row f, channel w) of accumulator register `reg` of `lane`
-// in wave `omega`.  valid: the element is a real state entry (quadratic rows
-// below r's 16-block are not); primary: it is the stored copy of the pair.
+// in quadratic wave `omega` (24: the side slot).  valid: the element is a real
+// state entry; primary: it is the stored copy of its pair (the tile rows also
+// hold mirrors).
 __host__ __device__ inline void state_elem(int omega, int reg, int lane, int& f, int& w,
                                            bool& valid, bool& primary) {
   const int h = lane >> 5, col = lane & 31;
@@ -64,8 +74,18 @@ __host__ __device__ inline void state_elem(int omega, int reg, int lane, int& f,
   w = 0;
   valid = true;
   primary = true;
-  if (reg >= 128) {   // side values of wave 24
-    valid = omega == 24 && (reg != st::REG_Z0 || lane == 0) && reg <= st::REG_Z0;
+  if (omega < 24) {
+    const int m = reg >> 5, nt = (reg >> 4) & 1, i = reg & 15;
+    const int row = 8 * (i >> 2) + 4 * h + (i & 3);
+    int r, t;
+    tile::quad_rt(tile::NKS_LIN + 2 * (st::QTILES * omega + m) + (row >> 4), row & 15, r, t);
+    w = 32 * nt + col;
+    primary = r <= t;
+    f = 1 + DH + pair_index(r < t ? r : t, r < t ? t : r);
+    return;
+  }
+  if (reg >= 128) {   // H0, z1, z0
+    valid = (reg != st::REG_Z0 || lane == 0) && reg <= st::REG_Z0;
     if (reg == st::REG_H0) { f = 0; w = lane; }
     else if (reg == st::REG_Z1) { f = 1 + lane; w = DV; }
     else { f = 0; w = DV; }
@@ -73,16 +93,6 @@ __host__ __device__ inline void state_elem(int omega, int reg, int lane, int& f,
   }
   const int m = reg >> 5, nt = (reg >> 4) & 1, i = reg & 15;
   const int row = 8 * (i >> 2) + 4 * h + (i & 3);
-  if (omega < 24) {
-    const int tb = omega < 8 ? 0 : 1;
-    const int r = (omega < 8 ? 4 * omega : 4 * (omega - 8)) + m;
-    const int t = 32 * tb + row;
-    w = 32 * nt + col;
-    valid = t >= 16 * (r >> 4);
-    primary = r <= t;
-    f = 1 + DH + pair_index(r < t ? r : t, r < t ? t : r);
-    return;
-  }
   if (m < 2) {               // linear rows
     f = 1 + 32 * m + row;
     w = 32 * nt + col;
@@ -382,22 +392,28 @@ k_state_mfma(int seq_len, int chunk, int n_chunks, int n_seg, int cps, int n_blk
     for (int j = 0; j < P; ++j) load_lds16(rs, dst + j * 1024, lane * 16, (wv * P + j) * 1024);
   };
 
+  using P4 = std::integral_constant<int, 4>;
+  if (n_blocks > 0) issue(0, s_b0, P4{});
+  if (n_blocks > 1) issue(1, s_b1, P4{});
+
   if (g < st::NWG - 1) {
     // ===================== quadratic rows (waves 0..23) =====================
     // The accumulators hold the sums times 2^-(2 e_k + e_v).
-    using P4 = std::integral_constant<int, 4>;
     const float unscale = ldexpf(1.0f, 2 * e_k + e_v);
     const float rescale = ldexpf(1.0f, e_s - (2 * e_k + e_v));   // seed -> accumulator
     const int omega = g * st::WAVES_PER_WG + wv;
-    const int tb = omega < 8 ? 0 : 1;
-    const int r0 = omega < 8 ? 4 * omega : 4 * (omega - 8);
-    float* slot = segslot + (size_t)omega * st::SLOT_FLOATS;
-    const uint16_t* pslot = preslot + (size_t)omega * st::SLOT_FLOATS;
-    if (n_blocks > 0) issue(0, s_b0, P4{});
-    if (n_blocks > 1) issue(1, s_b1, P4{});
-    f32x16 acc[4][2];
+    float* slot = segslot + (size_t)omega * st::QSLOT_FLOATS;
+    const uint16_t* pslot = preslot + (size_t)omega * st::QSLOT_FLOATS;
+    // K-step of tile m's first row; this lane's pair (r, t) = A row `col` of tile m
+    int ks0[st::QTILES], ra[st::QTILES], ta[st::QTILES];
 #pragma unroll
-    for (int m = 0; m < 4; ++m)
+    for (int m = 0; m < st::QTILES; ++m) {
+      ks0[m] = tile::NKS_LIN + 2 * (st::QTILES * omega + m);
+      tile::quad_rt(ks0[m] + (col >> 4), col & 15, ra[m], ta[m]);
+    }
+    f32x16 acc[st::QTILES][2];
+#pragma unroll
+    for (int m = 0; m < st::QTILES; ++m)
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
@@ -405,21 +421,9 @@ k_state_mfma(int seq_len, int chunk, int n_chunks, int n_seg, int cps, int n_blk
           acc[m][nt][i] = MODE == 1 ? (float)__builtin_bit_cast(_Float16, pslot[(size_t)((m * 2 + nt) * 16 + i) * 64 + lane]) * rescale
                                     : 0.f;
     const float wscale = unscale * tscale;   // accumulator -> tile entry
-
-    // Whether rows t = 32 tb + 8 gq .. + 7 of item r are in the tiled layout
-    // (wave-uniform): not below r's 16-block, and not the lower half of the
-    // diagonal block for the merged rows of its upper half.
-    auto stored = [&](int r, int gq) {
-      const int cblk = 2 * tb + (gq >> 1);   // t >> 4
-      return cblk > (r >> 4) || (cblk == (r >> 4) && (!tile::quad_merged(r, cblk) || (gq & 1)));
-    };
-    // Tile stores issued per chunk start (wave-uniform): 2 per stored (m, row group).
-    int nst = 0;
-#pragma unroll
-    for (int m = 0; m < 4; ++m)
-#pragma unroll
-      for (int gq = 0; gq < 4; ++gq) nst += stored(r0 + m, gq) ? 2 : 0;
-    auto stores_at = [&](int b) { return (MODE == 1 && b >= 0 && (b * st::TB) % chunk == 0) ? nst : 0; };
+    // tile stores per chunk start: every row of every tile, 4 rows per store
+    constexpr int NST = st::QTILES * 2 * 4;
+    auto stores_at = [&](int b) { return (MODE == 1 && b >= 0 && (b * st::TB) % chunk == 0) ? NST : 0; };
 
     auto body = [&](int bi, const uint8_t* cur, uint8_t* nxt) {
       if (bi >= n_blocks) return;
@@ -431,21 +435,18 @@ k_state_mfma(int seq_len, int chunk, int n_chunks, int n_seg, int cps, int n_blk
       if (bi + 2 < n_blocks) issue(bi + 2, nxt, P4{});
       const int t0 = tok_begin + bi * st::TB;
       if (MODE == 1 && (t0 % chunk) == 0) {
-        // the running prefix is chunk (t0 / chunk)'s exclusive prefix: store it
+        // the running prefix is chunk (t0 / chunk)'s exclusive prefix: store it;
+        // rows 8 gq + 4 half .. + 3 of tile m are elements of one K-step
         uint16_t* tl = reinterpret_cast<uint16_t*>(ts + ((size_t)unit * n_chunks + t0 / chunk) * tile::BYTES);
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          const int r = r0 + m;
+        for (int m = 0; m < st::QTILES; ++m) {
 #pragma unroll
           for (int nt = 0; nt < 2; ++nt) {
             const int w = 32 * nt + col;
 #pragma unroll
             for (int gq = 0; gq < 4; ++gq) {
-              const int t = 32 * tb + 8 * gq + 4 * half;   // rows t .. t+3
-              const int cblk = 2 * tb + (gq >> 1);           // t >> 4, wave-uniform
-              if (!stored(r, gq)) continue;
-              const int ks_ = tile::quad_ks(r, cblk);
-              const int el = tile::quad_merged(r, cblk) ? 8 * (r & 1) + (t & 7) : (t & 15);
+              const int ks_ = ks0[m] + (gq >> 1);
+              const int el = 8 * (gq & 1) + 4 * half;
               *reinterpret_cast<uint2*>(tl + (size_t)ks_ * 1024 + w * 16 + el) =
                   pack4_f16(acc[m][nt][4 * gq], acc[m][nt][4 * gq + 1], acc[m][nt][4 * gq + 2],
                             acc[m][nt][4 * gq + 3], wscale);
@@ -463,11 +464,11 @@ k_state_mfma(int seq_len, int chunk, int n_chunks, int n_seg, int cps, int n_blk
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt)
           bv[nt] = *reinterpret_cast<const f16x8*>(vt_ + st_off(32 * nt + col, tk));
-        const f16x8 kt8 = *reinterpret_cast<const f16x8*>(kt_ + st_off(32 * tb + col, tk));
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          const f16x8 kr = *reinterpret_cast<const f16x8*>(kt_ + st_off(r0 + m, tk));   // k_r, broadcast
-          const f16x8 af = kr * kt8;                                                     // k_r k_t
+        for (int m = 0; m < st::QTILES; ++m) {
+          const f16x8 kr = *reinterpret_cast<const f16x8*>(kt_ + st_off(ra[m], tk));
+          const f16x8 kt = *reinterpret_cast<const f16x8*>(kt_ + st_off(ta[m], tk));
+          const f16x8 af = kr * kt;                                                   // k_r k_t
 #pragma unroll
           for (int nt = 0; nt < 2; ++nt) acc[m][nt] = mfma32h(af, bv[nt], acc[m][nt]);
         }
@@ -480,7 +481,7 @@ k_state_mfma(int seq_len, int chunk, int n_chunks, int n_seg, int cps, int n_blk
     }
     if (MODE == 0) {
 #pragma unroll
-      for (int m = 0; m < 4; ++m)
+      for (int m = 0; m < st::QTILES; ++m)
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
@@ -490,119 +491,126 @@ k_state_mfma(int seq_len, int chunk, int n_chunks, int n_seg, int cps, int n_blk
     return;
   }
 
-  // ===================== linear rows and the all-ones channel (wave 24) ======
-  // One wave does everything (the other three of the workgroup have no work), so
-  // it needs no barrier: its own loads are awaited with wait_vmcnt.  Sums held
-  // scaled: H1 by 2^-(e_k + e_v), Z by 2^-2 e_k, H0 by 2^-e_v, z1 by 2^-e_k.
-  if (wv != 0) return;
-  using P16 = std::integral_constant<int, 16>;
-  if (n_blocks > 0) issue(0, s_b0, P16{});
-  if (n_blocks > 1) issue(1, s_b1, P16{});
-  float* slot = segslot + (size_t)24 * st::SLOT_FLOATS;
-  const float* pslot = sidepre + ((size_t)unit * n_seg + seg) * st::SLOT_FLOATS;
-  const float sc_h1 = ldexpf(1.0f, e_k + e_v), sc_z = ldexpf(1.0f, 2 * e_k);
+  // ===================== linear rows and the all-ones channel ================
+  // All four waves copy the blocks; wave 0 adds up H1 = K^T V and H0, z1, z0,
+  // wave 1 Z = K^T K.  Sums held scaled: H1 by 2^-(e_k + e_v), Z by 2^-2 e_k,
+  // H0 by 2^-e_v, z1 by 2^-e_k.
+  const bool lin = wv == 0, ones = wv == 1;
+  float* slot = segslot + st::QUAD_SEG_FLOATS;
+  const float* pslot = sidepre + ((size_t)unit * n_seg + seg) * st::SIDE_FLOATS;
+  const int mo = ones ? 2 : 0;   // first register tile of this wave in the side slot
+  const float sc_acc = ldexpf(1.0f, ones ? 2 * e_k : e_k + e_v);
   const float sc_h0 = ldexpf(1.0f, e_v), sc_z1 = ldexpf(1.0f, e_k);
-  f32x16 acc[4][2];   // [0..1]: H1 rows 32m.., [2..3]: Z rows 32(m-2).., columns 32 nt..
+  const float inv_acc = ldexpf(1.0f, ones ? -2 * e_k : -(e_k + e_v));
+  f32x16 acc[2][2];   // H1 (wave 0) or Z (wave 1): rows 32 m.., columns 32 nt..
   float side_h0 = 0.f, side_z1 = 0.f, side_z0 = 0.f;
 #pragma unroll
-  for (int m = 0; m < 4; ++m)
+  for (int m = 0; m < 2; ++m)
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt)
+    for (int nt = 0; nt < 2; ++nt) acc[m][nt] = splat16(0.f);
+  if (MODE == 1 && (lin || ones)) {   // one branch: all loads in flight together
 #pragma unroll
-      for (int i = 0; i < 16; ++i)
-        acc[m][nt][i] = MODE == 1 ? pslot[(size_t)((m * 2 + nt) * 16 + i) * 64 + lane] *
-                                        (m < 2 ? ldexpf(1.0f, -(e_k + e_v)) : ldexpf(1.0f, -2 * e_k))
-                                  : 0.f;
-  if (MODE == 1) {
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          acc[m][nt][i] = pslot[(size_t)(((mo + m) * 2 + nt) * 16 + i) * 64 + lane] * inv_acc;
+  }
+  if (MODE == 1 && lin) {
     side_h0 = pslot[(size_t)st::REG_H0 * 64 + lane] * ldexpf(1.0f, -e_v);
     side_z1 = pslot[(size_t)st::REG_Z1 * 64 + lane] * ldexpf(1.0f, -e_k);
     side_z0 = pslot[(size_t)st::REG_Z0 * 64];
   }
-  const float h1scale = sc_h1 * tscale;
-  // side stores per chunk start: 16 for H1, 16 for Z, 2 for H0 and z1, 1 or 2 by
-  // lane 0 (adjacent words): a lower bound, so that the wait below is never short
-  constexpr int SIDE_STORES = 34;
-  auto stores_at = [&](int b) { return (MODE == 1 && b >= 0 && (b * st::TB) % chunk == 0) ? SIDE_STORES : 0; };
+  const float h1scale = sc_acc * tscale;
+  // side stores per chunk start: wave 0 16 for H1, 2 for H0 and z1, 1 or 2 by lane 0
+  // (adjacent words; the lower count, so that the wait below is never short);
+  // wave 1 16 for Z
+  const int side_stores = lin ? 19 : ones ? 16 : 0;
+  auto stores_at = [&](int b) { return (MODE == 1 && b >= 0 && (b * st::TB) % chunk == 0) ? side_stores : 0; };
   auto body = [&](int bi, const uint8_t* cur, uint8_t* nxt) {
     if (bi >= n_blocks) return;
-    // block bi has landed (later stores and the copy of block bi + 1 may be in flight)
-    wait_vm_upto(stores_at(bi - 2) + (bi + 1 < n_blocks ? 16 : 0) + stores_at(bi - 1));
-    asm volatile("" ::: "memory");
-    if (bi + 2 < n_blocks) issue(bi + 2, nxt, P16{});
+    wait_vm_upto(stores_at(bi - 2) + (bi + 1 < n_blocks ? 4 : 0) + stores_at(bi - 1));
+    barrier_nofence();
+    if (bi + 2 < n_blocks) issue(bi + 2, nxt, P4{});
     const int t0 = tok_begin + bi * st::TB;
     if (MODE == 1 && (t0 % chunk) == 0) {
       uint8_t* slotp = ts + ((size_t)unit * n_chunks + t0 / chunk) * tile::BYTES;
       uint16_t* tl = reinterpret_cast<uint16_t*>(slotp);
       float* side = reinterpret_cast<float*>(slotp + tile::TILE_BYTES);
+      if (lin) {
 #pragma unroll
-      for (int m = 0; m < 2; ++m)
+        for (int m = 0; m < 2; ++m)
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-          const int w = 32 * nt + col;
+          for (int nt = 0; nt < 2; ++nt) {
+            const int w = 32 * nt + col;
 #pragma unroll
-          for (int gq = 0; gq < 4; ++gq) {
-            const int r = 32 * m + 8 * gq + 4 * half;
-            *reinterpret_cast<uint2*>(tl + (size_t)(r >> 4) * 1024 + w * 16 + (r & 15)) =
-                pack4_f16(acc[m][nt][4 * gq], acc[m][nt][4 * gq + 1], acc[m][nt][4 * gq + 2],
-                          acc[m][nt][4 * gq + 3], h1scale);
+            for (int gq = 0; gq < 4; ++gq) {
+              const int r = 32 * m + 8 * gq + 4 * half;
+              *reinterpret_cast<uint2*>(tl + (size_t)(r >> 4) * 1024 + w * 16 + (r & 15)) =
+                  pack4_f16(acc[m][nt][4 * gq], acc[m][nt][4 * gq + 1], acc[m][nt][4 * gq + 2],
+                            acc[m][nt][4 * gq + 3], h1scale);
+            }
+            asm volatile("" ::: "memory");
           }
-          asm volatile("" ::: "memory");
+        side[tile::SIDE_H0 + lane] = side_h0 * sc_h0;
+        side[tile::SIDE_Z1 + lane] = side_z1 * sc_z1;
+        if (lane == 0) {
+          side[tile::SIDE_Z0] = side_z0;
+          side[tile::SIDE_SEXP] = (float)e_s;
         }
+      } else if (ones) {
 #pragma unroll
-      for (int m = 2; m < 4; ++m)
+        for (int m = 0; m < 2; ++m)
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-          // Z is symmetric: block (rows r, columns t) goes to (t, r), so that each
-          // lane's four consecutive rows r form one float4 of row t = 32 nt + col
-          float* zb = side + tile::SIDE_Z + (32 * nt + col) * DH + 32 * (m - 2) + 4 * half;
+          for (int nt = 0; nt < 2; ++nt) {
+            // Z is symmetric: block (rows r, columns t) goes to (t, r), so that each
+            // lane's four consecutive rows r form one float4 of row t = 32 nt + col
+            float* zb = side + tile::SIDE_Z + (32 * nt + col) * DH + 32 * m + 4 * half;
 #pragma unroll
-          for (int gq = 0; gq < 4; ++gq)
-            *reinterpret_cast<float4*>(zb + 8 * gq) =
-                make_float4(acc[m][nt][4 * gq] * sc_z, acc[m][nt][4 * gq + 1] * sc_z,
-                            acc[m][nt][4 * gq + 2] * sc_z, acc[m][nt][4 * gq + 3] * sc_z);
-          asm volatile("" ::: "memory");
-        }
-      side[tile::SIDE_H0 + lane] = side_h0 * sc_h0;
-      side[tile::SIDE_Z1 + lane] = side_z1 * sc_z1;
-      if (lane == 0) {
-        side[tile::SIDE_Z0] = side_z0;
-        side[tile::SIDE_SEXP] = (float)e_s;
+            for (int gq = 0; gq < 4; ++gq)
+              *reinterpret_cast<float4*>(zb + 8 * gq) =
+                  make_float4(acc[m][nt][4 * gq] * sc_acc, acc[m][nt][4 * gq + 1] * sc_acc,
+                              acc[m][nt][4 * gq + 2] * sc_acc, acc[m][nt][4 * gq + 3] * sc_acc);
+            asm volatile("" ::: "memory");
+          }
       }
     }
     const uint8_t* kt_ = cur;
     const uint8_t* vt_ = cur + DH * 128;
-    // H0 = sum v, z1 = sum k, z0 = count over this block (row `lane`)
-    const f16x2 one2 = {(_Float16)1.0f, (_Float16)1.0f};
-    float sh = 0.f, sz = 0.f;
+    if (lin) {
+      // H0 = sum v, z1 = sum k, z0 = count over this block (row `lane`)
+      const f16x2 one2 = {(_Float16)1.0f, (_Float16)1.0f};
+      float sh = 0.f, sz = 0.f;
 #pragma unroll
-    for (int c = 0; c < st::TB / 8; ++c) {
-      const f16x8 xv = *reinterpret_cast<const f16x8*>(vt_ + st_off(lane, 8 * c));
-      const f16x8 xk = *reinterpret_cast<const f16x8*>(kt_ + st_off(lane, 8 * c));
+      for (int c = 0; c < st::TB / 8; ++c) {
+        const f16x8 xv = *reinterpret_cast<const f16x8*>(vt_ + st_off(lane, 8 * c));
+        const f16x8 xk = *reinterpret_cast<const f16x8*>(kt_ + st_off(lane, 8 * c));
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        sh = __builtin_amdgcn_fdot2((f16x2){xv[2 * j], xv[2 * j + 1]}, one2, sh, false);
-        sz = __builtin_amdgcn_fdot2((f16x2){xk[2 * j], xk[2 * j + 1]}, one2, sz, false);
-      }
-    }
-    side_h0 += sh;
-    side_z1 += sz;
-    side_z0 += (float)min(st::TB, tok_end - t0);
-#pragma unroll
-    for (int kk = 0; kk < st::TB / 16; ++kk) {
-      const int tk = 16 * kk + 8 * half;
-      f16x8 ak[2], bv[2];
-#pragma unroll
-      for (int x = 0; x < 2; ++x) {
-        ak[x] = *reinterpret_cast<const f16x8*>(kt_ + st_off(32 * x + col, tk));
-        bv[x] = *reinterpret_cast<const f16x8*>(vt_ + st_off(32 * x + col, tk));
-      }
-#pragma unroll
-      for (int m = 0; m < 2; ++m)
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-          acc[m][nt] = mfma32h(ak[m], bv[nt], acc[m][nt]);         // H1 += K^T V
-          acc[2 + m][nt] = mfma32h(ak[m], ak[nt], acc[2 + m][nt]); // Z  += K^T K
+        for (int j = 0; j < 4; ++j) {
+          sh = __builtin_amdgcn_fdot2((f16x2){xv[2 * j], xv[2 * j + 1]}, one2, sh, false);
+          sz = __builtin_amdgcn_fdot2((f16x2){xk[2 * j], xk[2 * j + 1]}, one2, sz, false);
         }
+      }
+      side_h0 += sh;
+      side_z1 += sz;
+      side_z0 += (float)min(st::TB, tok_end - t0);
+    }
+    if (lin || ones) {
+#pragma unroll
+      for (int kk = 0; kk < st::TB / 16; ++kk) {
+        const int tk = 16 * kk + 8 * half;
+        f16x8 ak[2], bn[2];   // A = K^T rows; B = V^T (wave 0) or K^T (wave 1) rows
+#pragma unroll
+        for (int x = 0; x < 2; ++x) {
+          ak[x] = *reinterpret_cast<const f16x8*>(kt_ + st_off(32 * x + col, tk));
+          bn[x] = *reinterpret_cast<const f16x8*>((ones ? kt_ : vt_) + st_off(32 * x + col, tk));
+        }
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+          for (int nt = 0; nt < 2; ++nt) acc[m][nt] = mfma32h(ak[m], bn[nt], acc[m][nt]);
+      }
     }
   };
   for (int bi = 0; bi < n_blocks; bi += 3) {
@@ -610,17 +618,19 @@ k_state_mfma(int seq_len, int chunk, int n_chunks, int n_seg, int cps, int n_blk
     body(bi + 1, s_b1, s_b0);
     body(bi + 2, s_b2, s_b1);
   }
-  if (MODE == 0) {
+  if (MODE == 0 && (lin || ones)) {
 #pragma unroll
-    for (int m = 0; m < 4; ++m)
+    for (int m = 0; m < 2; ++m)
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
         for (int i = 0; i < 16; ++i)
-          slot[(size_t)((m * 2 + nt) * 16 + i) * 64 + lane] = acc[m][nt][i] * (m < 2 ? sc_h1 : sc_z);
-    slot[(size_t)st::REG_H0 * 64 + lane] = side_h0 * sc_h0;
-    slot[(size_t)st::REG_Z1 * 64 + lane] = side_z1 * sc_z1;
-    slot[(size_t)st::REG_Z0 * 64 + lane] = lane == 0 ? side_z0 : 0.f;
+          slot[(size_t)(((mo + m) * 2 + nt) * 16 + i) * 64 + lane] = acc[m][nt][i] * sc_acc;
+    if (lin) {
+      slot[(size_t)st::REG_H0 * 64 + lane] = side_h0 * sc_h0;
+      slot[(size_t)st::REG_Z1 * 64 + lane] = side_z1 * sc_z1;
+      slot[(size_t)st::REG_Z0 * 64 + lane] = lane == 0 ? side_z0 : 0.f;
+    }
   }
 }
 
@@ -637,7 +647,8 @@ k_state_segscan(int n_seg, const float* __restrict__ segsum, uint16_t* __restric
   const int unit = blockIdx.y, units = gridDim.y;
   const int e0 = 4 * (blockIdx.x * blockDim.x + threadIdx.x);
   const bool in = e0 < st::UNIT_SEG_FLOATS;
-  const int omega = e0 / st::SLOT_FLOATS;
+  const bool quad = e0 < st::QUAD_SEG_FLOATS;
+  const int omega = quad ? e0 / st::QSLOT_FLOATS : 24;
   // every wave evaluates the tile scale (the same value everywhere)
   const float tscale = segpre ? ldexpf(1.0f, -tile_scale_exp(bound, units, n_blk, nip, unit, threadIdx.x & 63)) : 1.f;
   if (!in) return;
@@ -647,7 +658,7 @@ k_state_segscan(int n_seg, const float* __restrict__ segsum, uint16_t* __restric
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int e = e0 + j;
-    const int reg = (e / 64) % st::SLOT_REGS, lane = e & 63;
+    const int reg = quad ? (e / 64) % st::QSLOT_REGS : (e - st::QUAD_SEG_FLOATS) / 64, lane = e & 63;
     int f = 0, w = 0;
     bool valid = false, primary = false;
     state_elem(omega, reg, lane, f, w, valid, primary);
@@ -671,13 +682,13 @@ k_state_segscan(int n_seg, const float* __restrict__ segsum, uint16_t* __restric
       if (s0 + j < n_seg) {
         if (segpre) {
           const size_t us = (size_t)unit * n_seg + s0 + j;
-          if (omega < 24) {
+          if (quad) {
             const f16x2 lo = __builtin_convertvector((f32x2){r.x * tscale, r.y * tscale}, f16x2);
             const f16x2 hi = __builtin_convertvector((f32x2){r.z * tscale, r.w * tscale}, f16x2);
             *reinterpret_cast<uint2*>(segpre + us * st::QUAD_SEG_FLOATS + e0) =
                 make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
           } else {
-            *reinterpret_cast<float4*>(sidepre + us * st::SLOT_FLOATS + (e0 - 24 * st::SLOT_FLOATS)) = r;
+            *reinterpret_cast<float4*>(sidepre + us * st::SIDE_FLOATS + (e0 - st::QUAD_SEG_FLOATS)) = r;
           }
         }
         r.x += a[j].x;
@@ -741,7 +752,7 @@ static StateWs state_ws(void* ws, int units, int seq_len, int n_seg, bool with_t
   w.init = reinterpret_cast<float*>(take((size_t)units * STATE_FLOATS * sizeof(float)));
   if (with_tiles) {
     w.segpre = reinterpret_cast<uint16_t*>(take((size_t)units * n_seg * st::QUAD_SEG_FLOATS * sizeof(uint16_t)));
-    w.sidepre = reinterpret_cast<float*>(take((size_t)units * n_seg * st::SLOT_FLOATS * sizeof(float)));
+    w.sidepre = reinterpret_cast<float*>(take((size_t)units * n_seg * st::SIDE_FLOATS * sizeof(float)));
     w.bound = reinterpret_cast<float*>(take((size_t)units * (n_blk + nip) * sizeof(float)));
   }
   w.bytes = off;

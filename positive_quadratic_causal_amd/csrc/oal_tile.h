@@ -60,6 +60,19 @@ __host__ __device__ constexpr int quad_ks(int r, int c) {
 }
 __host__ __device__ constexpr bool quad_merged(int r, int c) { return r - 16 * c >= 8; }
 
+// Inverse: the pair (r, t) that element pos of quadratic K-step ks holds.
+__host__ __device__ inline void quad_rt(int ks, int pos, int& r, int& t) {
+  const int c = ks >= quad_base(3) ? 3 : ks >= quad_base(2) ? 2 : ks >= quad_base(1) ? 1 : 0;
+  const int i = ks - quad_base(c);
+  if (i < 16 * c + 8) {
+    r = i;
+    t = 16 * c + pos;
+  } else {
+    r = 16 * c + 8 + 2 * (i - 16 * c - 8) + (pos >> 3);
+    t = 16 * c + 8 + (pos & 7);
+  }
+}
+
 }  // namespace tile
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;

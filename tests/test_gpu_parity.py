@@ -321,3 +321,40 @@ def test_prefill_many_outlier_dims(oal):
         y = _prefill(oal, case, chunk)
         torch.cuda.synchronize()
         _check_heads(case, y, [(0, h) for h in range(4)], tol_for(w))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_learned_global_single_group(oal, dtype):
+    """G = 1 (one group holding every dim, a 2 x 2 L): the learned-global kernel
+    kappa = eps + (L00 + L10 s)^2 + (L11 s)^2 of the pages' ablations, through the
+    same calls: prefill (with a ragged tail) and decode steps after it."""
+    w = synth.small_workload(307, "global", 1, 4, 2, 333, dtype)
+    announce(f"learned-global G=1 prefill N=333 + 3 decode steps {dtype}")
+    case = Case(w)
+    rng = np.random.default_rng(12)
+    for h in range(4):
+        case.st.n_groups[h] = 1
+        case.st.group_map[h] = 1
+        case.st.L[h] = synth.random_L(rng, 1)
+    case.n_groups = torch.from_numpy(case.st.n_groups.astype(np.int32)).to("cuda")
+    case.group_map = torch.from_numpy(case.st.group_map.astype(np.int32)).to("cuda")
+    case.L = torch.from_numpy(case.st.L.astype(np.float32)).to("cuda")
+    for chunk in (64, 128):
+        y = _prefill(oal, case, chunk)
+        torch.cuda.synchronize()
+        _check_heads(case, y, [(0, h) for h in range(4)], tol_for(w))
+    n0 = 330
+    coeffs = case.coeffs()
+    st = oal.oal_state_alloc(1, 2)
+    oal.oal_prefill(None, case.k[:, :, :n0].contiguous(), case.v[:, :, :n0].contiguous(), None,
+                    chunk=128, state=st, want_output=False)
+    outs = []
+    for t in range(n0, 333):
+        outs.append(oal.oal_decode_step(case.q[:, :, t].contiguous(), case.k[:, :, t].contiguous(),
+                                        case.v[:, :, t].contiguous(), coeffs, st))
+    torch.cuda.synchronize()
+    yd = torch.stack(outs, dim=2).float().cpu().numpy()
+    assert np.all(np.isfinite(yd))
+    for h in range(4):
+        ref = case.oracle_head(0, h)[n0:]
+        assert rel_l2(yd[0, h], ref) <= tol_for(w), h
