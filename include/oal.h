@@ -149,6 +149,18 @@ oal_status oal_decode_step(int batch, int n_q_heads, int n_kv_heads, int d_h, in
                            const void* coeffs, oal_state* state, void* y, oal_dtype out_dtype,
                            hipStream_t stream);
 
+/* Exact causal softmax attention, the reference OAL approximates ([OAL] §3:
+ * y_i = sum_{j<=i} exp(s_ij) v_j / sum_{j<=i} exp(s_ij), s_ij = q_i . k_j / sqrt(d_h),
+ * query head h reading KV head h / (n_q_heads / n_kv_heads)); used for the
+ * frozen-attention fidelity metrics of [OAL] App. C (Eqs. 21-22).
+ *   q [batch][n_q_heads][seq_len][d_h], k, v [batch][n_kv_heads][seq_len][d_h/d_v]
+ *   in bf16 (in_dtype must be OAL_BF16: other types return OAL_ERR_UNSUPPORTED);
+ *   y [batch][n_q_heads][seq_len][d_v] in out_dtype.  d_h = d_v = 64.
+ * seq_len == 0 is a valid no-op.  Allocates nothing. */
+oal_status oal_softmax_attention(int batch, int n_q_heads, int n_kv_heads, int seq_len, int d_h,
+                                 int d_v, oal_dtype in_dtype, const void* q, const void* k,
+                                 const void* v, void* y, oal_dtype out_dtype, hipStream_t stream);
+
 /* Per-kernel timing (a tracing aid, off by default).  While enabled, the library
  * records a pair of HIP events on the launch stream around every kernel it
  * launches.  oal_profile_query waits for the pending events of the named kernel

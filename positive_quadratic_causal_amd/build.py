@@ -26,6 +26,7 @@ SOURCES = [
     "oal_prefill_vec.hip",
     "oal_prefill_mfma.hip",
     "oal_state_mfma.hip",
+    "oal_softmax.hip",
 ]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")

@@ -105,6 +105,9 @@ oal_status launch_decode(int batch, int n_q_heads, int n_kv_heads, oal_dtype in_
                          float* state, void* y, oal_dtype out_dtype, hipStream_t stream);
 size_t prefill_vec_workspace(int batch, int n_kv_heads, int seq_len, int chunk);
 size_t state_mfma_workspace(int batch, int n_kv_heads, int seq_len, int chunk, bool with_tiles);
+oal_status launch_softmax(int batch, int n_q_heads, int n_kv_heads, int seq_len, const void* q,
+                          const void* k, const void* v, void* y, oal_dtype out_dtype,
+                          hipStream_t stream);
 oal_status launch_prefill_mfma(int batch, int n_q_heads, int n_kv_heads, int seq_len,
                                const void* q, const void* k, const void* v, const void* coeffs,
                                int chunk, float* state, void* y, oal_dtype out_dtype, void* ws,
@@ -316,6 +319,21 @@ oal_status oal_prefill(int batch, int n_q_heads, int n_kv_heads, int seq_len, in
                             state ? state->data : nullptr, y, out_dtype, workspace, stream);
   if (st == OAL_OK && state) state->tokens += seq_len;
   return st;
+}
+
+oal_status oal_softmax_attention(int batch, int n_q_heads, int n_kv_heads, int seq_len, int d_h,
+                                 int d_v, oal_dtype in_dtype, const void* q, const void* k,
+                                 const void* v, void* y, oal_dtype out_dtype, hipStream_t stream) {
+  oal_status st = check_heads(batch, n_q_heads, n_kv_heads, d_h, d_v);
+  if (st != OAL_OK) return st;
+  if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype))
+    return set_error(OAL_ERR_INVALID_ARG, "unknown dtype");
+  if (in_dtype != OAL_BF16)
+    return set_error(OAL_ERR_UNSUPPORTED, "oal_softmax_attention takes bf16 inputs only");
+  if (seq_len < 0) return set_error(OAL_ERR_INVALID_ARG, "seq_len must be >= 0 (got %d)", seq_len);
+  if (seq_len == 0) return OAL_OK;
+  if (!q || !k || !v || !y) return set_error(OAL_ERR_INVALID_ARG, "null pointer argument");
+  return launch_softmax(batch, n_q_heads, n_kv_heads, seq_len, q, k, v, y, out_dtype, stream);
 }
 
 oal_status oal_decode_step(int batch, int n_q_heads, int n_kv_heads, int d_h, int d_v,

@@ -62,18 +62,6 @@ constexpr int BZ = BPF + DH;            // [DH] b'_r z1_r 2^-e_M (z1 of the chun
 constexpr int FLOATS = BZ + DH;
 }  // namespace htab
 
-// A row of 64 bf16 in a swizzled 128-byte LDS row.
-struct SwRow {
-  const uint8_t* p;
-  int key;
-  __device__ __forceinline__ SwRow(const uint8_t* base, int row) : p(base + row * 128), key(row_key(row)) {}
-  // 16-byte chunk c (elements 8 c .. 8 c + 7)
-  __device__ __forceinline__ const uint8_t* chunk(int c) const { return p + ((c ^ key) << 4); }
-  // element d
-  __device__ __forceinline__ const __bf16* elem(int d) const {
-    return reinterpret_cast<const __bf16*>(p + (((d >> 3) ^ key) << 4) + ((d & 7) << 1));
-  }
-};
 
 // Swizzled LDS offset of the 16-byte half-row (w, h) of a K-step inside a
 // half-slab: the half is flipped by bit 2 ^ bit 3 ^ bit 4 of w, so that lanes

@@ -120,6 +120,19 @@ __device__ __forceinline__ float bf(const __bf16 x) { return (float)x; }
 // the 8 rows of one residue mod 4 among 32 have distinct keys).
 __device__ __forceinline__ int row_key(int r) { return (r ^ (r >> 3)) & 7; }
 
+// A row of 64 bf16 in a swizzled 128-byte LDS row.
+struct SwRow {
+  const uint8_t* p;
+  int key;
+  __device__ __forceinline__ SwRow(const uint8_t* base, int row) : p(base + row * 128), key(row_key(row)) {}
+  // 16-byte chunk c (elements 8 c .. 8 c + 7)
+  __device__ __forceinline__ const uint8_t* chunk(int c) const { return p + ((c ^ key) << 4); }
+  // element d
+  __device__ __forceinline__ const __bf16* elem(int d) const {
+    return reinterpret_cast<const __bf16*>(p + (((d >> 3) ^ key) << 4) + ((d & 7) << 1));
+  }
+};
+
 // ---- direct-to-LDS loads ---------------------------------------------------
 // The loads are issued from inline assembly so that the compiler neither waits
 // for them before LDS reads it cannot prove disjoint from their destination,

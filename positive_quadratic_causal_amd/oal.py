@@ -61,6 +61,8 @@ def _load() -> ctypes.CDLL:
                                 c_void]),
         "oal_decode_step": (c_int, [c_int, c_int, c_int, c_int, c_int, c_int, c_void, c_void,
                                     c_void, c_void, c_void, c_void, c_int, c_void]),
+        "oal_softmax_attention": (c_int, [c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_void,
+                                          c_void, c_void, c_void, c_int, c_void]),
         "oal_profile_enable": (c_int, [c_int]),
         "oal_profile_reset": (c_int, []),
         "oal_profile_query": (c_int, [ctypes.c_char_p, ctypes.POINTER(ctypes.c_double),
@@ -80,7 +82,8 @@ _lib = _load()
 EXPORTED = ("oal_coeffs_bytes", "oal_expand_coeffs", "oal_state_alloc", "oal_state_reset",
             "oal_state_free", "oal_state_copy", "oal_state_bytes", "oal_state_tokens",
             "oal_state_export", "oal_prefill_workspace_bytes", "oal_prefill",
-            "oal_decode_step", "oal_profile_enable", "oal_profile_reset", "oal_profile_query",
+            "oal_decode_step", "oal_softmax_attention", "oal_profile_enable", "oal_profile_reset",
+            "oal_profile_query",
             "oal_status_string", "oal_last_error")
 
 
@@ -248,6 +251,20 @@ def oal_decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, coeffs: t
         y = torch.empty((B, Hq, dv), dtype=q.dtype, device=q.device)
     _check(_lib.oal_decode_step(B, Hq, Hkv, dh, dv, _dtype_code(q), _ptr(q), _ptr(k), _ptr(v),
                                 _ptr(coeffs), state.handle, _ptr(y), _dtype_code(y), _stream(q)))
+    return y
+
+
+def oal_softmax_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                          y: torch.Tensor | None = None) -> torch.Tensor:
+    """Exact causal softmax attention (the reference OAL approximates): q [B, Hq, N, 64],
+    k/v [B, Hkv, N, 64] in bf16; returns y [B, Hq, N, 64] in q's dtype unless y is given."""
+    B, Hq, N, dh = q.shape
+    Hkv = k.shape[1]
+    dv = v.shape[-1]
+    if y is None:
+        y = torch.empty((B, Hq, N, dv), dtype=q.dtype, device=q.device)
+    _check(_lib.oal_softmax_attention(B, Hq, Hkv, N, dh, dv, _dtype_code(q), _ptr(q), _ptr(k), _ptr(v),
+                                      _ptr(y), _dtype_code(y), _stream(q)))
     return y
 
 

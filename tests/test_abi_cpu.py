@@ -112,3 +112,14 @@ def test_decode_and_expand_reject_invalid_arguments():
     assert lib.oal_state_free(None) == 0
     for s in range(5):
         assert lib.oal_status_string(s).startswith(b"OAL_")
+
+
+def test_softmax_rejects_invalid_arguments():
+    lib, oal = _lib()
+    # batch, Hq, Hkv, N, d_h, d_v, in_dt, q, k, v, y, out_dt, stream
+    assert lib.oal_softmax_attention(1, 14, 2, 16, 64, 64, 0, P, P, P, P, 1, None) == 2   # fp32 in
+    assert lib.oal_softmax_attention(1, 14, 3, 16, 64, 64, 1, P, P, P, P, 1, None) == 1   # Hq % Hkv
+    assert lib.oal_softmax_attention(1, 14, 2, 16, 32, 64, 1, P, P, P, P, 1, None) == 2   # d_h
+    assert lib.oal_softmax_attention(1, 14, 2, 16, 64, 64, 1, None, P, P, P, 1, None) == 1
+    assert lib.oal_softmax_attention(1, 14, 2, -1, 64, 64, 1, P, P, P, P, 1, None) == 1
+    assert lib.oal_softmax_attention(1, 14, 2, 0, 64, 64, 1, P, P, P, P, 1, None) == 0     # no-op

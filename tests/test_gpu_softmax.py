@@ -1,0 +1,65 @@
+"""GPU parity of oal_softmax_attention (exact causal softmax attention, the
+reference OAL approximates: [OAL] §3) against the float64 softmax oracle, on the
+same bf16 input values.  Bars: rel-L2 2e-2 per head (bf16 inputs), and 6e-3 with
+fp32 output (the weights P enter the P V product in bf16, relative 2^-9 each)."""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import softmax_oracle as S
+from positive_quadratic_causal_amd import synth
+
+from gpu_util import Case, announce, rel_l2
+
+pytestmark = pytest.mark.gpu
+
+BAR = 2e-2
+MARGIN_F32_OUT = 6e-3
+
+
+@pytest.fixture(scope="module")
+def oal():
+    from positive_quadratic_causal_amd import oal as mod
+    return mod
+
+
+def _check(case, y, heads, tol):
+    yc = y.float().cpu().numpy()
+    assert np.all(np.isfinite(yc))
+    for b, h in heads:
+        q, k, v = case.head_qkv(b, h)
+        err = rel_l2(yc[b, h], S.softmax_attention(q, k, v))
+        assert err <= tol, (b, h, err)
+
+
+@pytest.mark.parametrize("n", [1, 2, 31, 64, 100, 128, 129, 300, 511])
+def test_softmax_ragged(oal, n):
+    w = synth.small_workload(500 + n, "softmax", 2, 6, 2, n, "bf16", grouping="llama")
+    announce(f"softmax B=2 6/2 N={n} bf16")
+    case = Case(w)
+    y = oal.oal_softmax_attention(case.q, case.k, case.v)
+    torch.cuda.synchronize()
+    _check(case, y, [(b, h) for b in range(2) for h in range(6)], BAR)
+
+
+def test_softmax_fp32_output_margin(oal):
+    w = synth.small_workload(520, "softmax", 1, 7, 1, 700, "bf16")
+    announce("softmax 7/1 N=700 bf16 in, fp32 out")
+    case = Case(w)
+    y = torch.empty(case.q.shape, dtype=torch.float32, device="cuda")
+    oal.oal_softmax_attention(case.q, case.k, case.v, y)
+    again = torch.empty_like(y)
+    oal.oal_softmax_attention(case.q, case.k, case.v, again)
+    torch.cuda.synchronize()
+    assert torch.equal(y, again)
+    _check(case, y, [(0, h) for h in range(7)], MARGIN_F32_OUT)
+
+
+def test_softmax_qwen_2048_sampled_heads(oal):
+    w = synth.WORKLOADS[1]
+    announce("softmax Qwen-shaped 14/2 N=2048 bf16, sampled heads")
+    case = Case(w)
+    y = oal.oal_softmax_attention(case.q, case.k, case.v)
+    torch.cuda.synchronize()
+    _check(case, y, [(0, 0), (0, 6), (0, 7), (0, 13)], BAR)
