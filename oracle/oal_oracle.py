@@ -48,6 +48,8 @@ __all__ = [
     "causal_attention",
     "causal_attention_rows",
     "causal_attention_gqa",
+    "causal_attention_dim_rows",
+    "causal_attention_dim",
     "recurrence",
     "canonical_state",
     "packed_pairs",
@@ -193,6 +195,39 @@ def causal_attention(q, k, v, L, group_map, n_groups, eps, row_block=256):
         y[i0:i1] = causal_attention_rows(q[i0:i1], np.arange(i0, i1), k, v, L,
                                          group_map, n_groups, eps)
     return y
+
+
+def causal_attention_dim_rows(q_rows, positions, k, v, a, b, C, return_parts=False):
+    """Causal attention with the dimension-specific kernel of [OAL] §4.1 (Eq. 3),
+    arbitrary a, b_r, C_rt: for query row q_i at 0-based position p_i,
+    y_i = sum_{j <= p_i} kappa_dim(q_i, k_j) v_j / sum_{j <= p_i} kappa_dim(q_i, k_j)
+    (the normalisation of [OAL] §2 over the causal prefix of Eq. 5).  One row at a
+    time, each through :func:`kappa_dim`; C need not be symmetric.
+
+    q_rows: [R, d_h]; positions: [R]; k: [N, d_h]; v: [N, d_v].  Returns y [R, d_v]
+    (and, with return_parts, the numerator [R, d_v] and denominator [R])."""
+    q_rows = np.asarray(q_rows, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    positions = np.asarray(positions, dtype=np.int64)
+    R = q_rows.shape[0]
+    num = np.zeros((R, v.shape[1]))
+    den = np.zeros(R)
+    for i in range(R):
+        n_keys = int(positions[i]) + 1
+        kap = kappa_dim(q_rows[i][None, :], k[:n_keys], a, b, C)      # [n_keys]
+        num[i] = kap @ v[:n_keys]
+        den[i] = kap.sum()
+    y = num / den[:, None] if R else np.zeros((0, v.shape[1]))
+    if return_parts:
+        return y, num, den
+    return y
+
+
+def causal_attention_dim(q, k, v, a, b, C):
+    """:func:`causal_attention_dim_rows` for every row of one head's sequence."""
+    q = np.asarray(q, dtype=np.float64)
+    return causal_attention_dim_rows(q, np.arange(q.shape[0]), k, v, a, b, C)
 
 
 def causal_attention_gqa(q, k, v, L, group_map, n_groups, eps, heads=None):

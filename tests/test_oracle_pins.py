@@ -343,3 +343,62 @@ def test_p14_canonical_state_readout():
                                           return_parts=True)
     np.testing.assert_allclose(ut[:64], num[0], rtol=1e-11, atol=1e-9)
     np.testing.assert_allclose(ut[64], den[0], rtol=1e-12)
+
+
+# --- P15: the dimension-specific kernel ([OAL] §4.1, Eq. 3) with arbitrary a, b,
+#          C: direct sum == Algorithm 1 recurrence; the grouped kernel is the
+#          special case of [OAL] §4.3; closed forms -----------------------------
+
+def _rand_dim(rng, d, skew=1.0):
+    """a, b, C with [[a, b^T/2], [b/2, sym(C)]] positive definite (so kappa_dim > 0)
+    and no group structure, plus an antisymmetric part of C, which Eq. 3 ignores."""
+    R = rng.normal(size=(d + 1, d + 1)) * rng.uniform(0.2, 1.5, size=(d + 1, 1))
+    Mp = R @ R.T / (d + 1) + 0.05 * np.eye(d + 1)
+    A = rng.normal(size=(d, d))
+    return float(Mp[0, 0]), 2.0 * Mp[0, 1:], Mp[1:, 1:] + skew * (A - A.T)
+
+
+@pytest.mark.parametrize("d,N", [(4, 15), (8, 12), (64, 5)])
+def test_p15_dim_direct_equals_recurrence(d, N):
+    rng = np.random.default_rng(1500 + d + N)
+    q = rng.normal(size=(N, d)) * rng.uniform(0.5, 3, size=(1, d))
+    k = rng.normal(size=(N, d)) * rng.uniform(0.5, 3, size=(1, d))
+    v = rng.normal(size=(N, 5))
+    a, b, C = _rand_dim(rng, d)
+    y_direct = O.causal_attention_dim(q, k, v, a, b, C)
+    y_rec = O.recurrence(q, k, v, a, b, C, packed=False)   # full C, unsymmetrised
+    np.testing.assert_allclose(y_direct, y_rec, rtol=1e-10, atol=1e-12)
+
+
+@pytest.mark.parametrize("G", [1, 3, 6])
+def test_p15_dim_reduces_to_grouped(G):
+    rng = np.random.default_rng(1510 + G)
+    N, d = 40, 64
+    q = rng.normal(size=(N, d)) * 2
+    k = rng.normal(size=(N, d)) * 2
+    v = rng.normal(size=(N, 64))
+    L = _rand_L(rng, G)
+    g = _rand_groups(rng, d, G)
+    a, b, C = O.expand_coeffs(L, g, G, 1e-3)
+    np.testing.assert_allclose(O.causal_attention_dim(q, k, v, a, b, C),
+                               O.causal_attention(q, k, v, L, g, G, 1e-3), rtol=1e-10, atol=1e-12)
+
+
+def test_p15_dim_closed_forms():
+    rng = np.random.default_rng(1520)
+    N, d = 30, 64
+    q = rng.normal(size=(N, d))
+    k = rng.normal(size=(N, d))
+    v = rng.normal(size=(N, 64))
+    # b = 0, C = 0: equal weights, the causal prefix mean
+    y = O.causal_attention_dim(q, k, v, 0.7, np.zeros(d), np.zeros((d, d)))
+    np.testing.assert_allclose(y, np.cumsum(v, axis=0) / np.arange(1, N + 1)[:, None], rtol=1e-12)
+    # a = 0, b = 0, C = d I: kappa = sum_r (q_r k_r)^2, written out for one row
+    y = O.causal_attention_dim(q, k, v, 0.0, np.zeros(d), d * np.eye(d))
+    w = ((q[17][None, :] * k[:18]) ** 2).sum(axis=1)
+    np.testing.assert_allclose(y[17], w @ v[:18] / w.sum(), rtol=1e-12)
+    # the antisymmetric part of C leaves every output unchanged
+    a, b, C = _rand_dim(rng, d, skew=0.0)
+    A = rng.normal(size=(d, d)) * 3
+    np.testing.assert_allclose(O.causal_attention_dim(q, k, v, a, b, C + A - A.T),
+                               O.causal_attention_dim(q, k, v, a, b, C), rtol=1e-11, atol=1e-13)
