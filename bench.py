@@ -91,7 +91,7 @@ def kernel_times(oal, names):
 ALL_KERNELS = ["k_expand", "k_fill_zero", "k_build_vec", "k_scan_vec", "k_readout_vec",
                "k_scan_tile", "k_state_mfma", "k_state_seg", "k_state_segscan", "k_state_kvmax", "k_state_stage",
                "k_readout_mfma",
-               "k_decode", "k_export"]
+               "k_decode", "k_export", "k_softmax"]
 
 
 def bench_prefill(oal, w, chunk, steps, warmup, device):
@@ -138,6 +138,152 @@ def bench_prefill(oal, w, chunk, steps, warmup, device):
     state.free()
     torch.cuda.empty_cache()
     return ms, kt
+
+
+def softmax_flops(w) -> int:
+    """Algorithmic flops of exact causal attention: per query head, Q K^T and P V
+    over the N (N + 1) / 2 causal (i, j) pairs, 2 d flops each."""
+    return 2 * 2 * 64 * (w.seq_len * (w.seq_len + 1) // 2) * w.batch * w.n_q_heads
+
+
+def bench_softmax(oal, w, steps, warmup, device):
+    """Exact causal softmax attention ([OAL] §3) on the same inputs: the reference
+    the method approximates, timed through the library's own MFMA kernel."""
+    import torch
+
+    from positive_quadratic_causal_amd import synth
+    st = synth.structure(w)
+    x = gen_inputs(w, st, device, t1=w.seq_len)
+    y = torch.empty((w.batch, w.n_q_heads, w.seq_len, 64), dtype=x["q"].dtype, device=device)
+
+    def step():
+        oal.oal_softmax_attention(x["q"], x["k"], x["v"], y)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    oal.oal_profile_reset()
+    oal.oal_profile_enable(True)
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    oal.oal_profile_enable(False)
+    kt = kernel_times(oal, ["k_softmax"])
+    fl = softmax_flops(w)
+    kern_ms = kt["k_softmax"]["avg_ms"]
+    del x, y
+    torch.cuda.empty_cache()
+    return {"workload": w.name, "ms_per_step": round(ms, 5),
+            "tokens_per_s": round(w.batch * w.seq_len / (ms * 1e-3), 1),
+            "algorithmic_flops": fl,
+            "roofline": {"bound": "mfma", "achieved": round(fl / (kern_ms * 1e-3) / 1e12, 3),
+                         "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(fl / (kern_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 5)},
+            "kernel_avg_ms": round(kern_ms, 5)}
+
+
+def dim_readout_flops_per_launch(w, chunk) -> int:
+    """Algorithmic flops of the general readout (dimension-specific kernel, [OAL]
+    Eq. 3 and Eq. 6) over one prefill: per query, the state readout phi_q(q)^T H
+    (2145 features x 65 columns, 2 flops each) plus, per causal pair inside its
+    chunk, kappa_dim in its packed form (64 products, 64 + 2080 multiply-adds of
+    b' and the symmetric c') and the 65-wide accumulation."""
+    n, c = w.seq_len, chunk
+    pairs = 0
+    for t0 in range(0, n, c):
+        m = min(c, n - t0)
+        pairs += m * (m + 1) // 2
+    per_q = 2145 * 65 * 2
+    per_pair = 64 + 2 * (64 + 2080) + 2 * 65
+    return (n * per_q + pairs * per_pair) * w.batch * w.n_q_heads
+
+
+def bench_prefill_dim(oal, w, chunk, steps, warmup, device):
+    """The general (dimension-specific kernel) prefill: oal_dim_coeffs records and
+    oal_prefill_dim, on the vector ALUs in fp32."""
+    import torch
+
+    from positive_quadratic_causal_amd import synth
+    st = synth.structure(w)
+    x = gen_inputs(w, st, device, t1=w.seq_len)
+    a, b, C = (torch.from_numpy(t).to(device) for t in synth.dim_coefficients(w))
+    coeffs = oal.oal_dim_coeffs(a, b, C)
+    state = oal.oal_state_alloc(w.batch, w.n_kv_heads)
+    y = torch.empty((w.batch, w.n_q_heads, w.seq_len, 64), dtype=x["q"].dtype, device=device)
+    ws = oal.alloc_workspace(oal.oal_prefill_dim_workspace_bytes(
+        w.batch, w.n_q_heads, w.n_kv_heads, w.seq_len, chunk, True), device)
+
+    def step():
+        oal.oal_dim_coeffs(a, b, C, coeffs)
+        oal.oal_state_reset(state)
+        oal.oal_prefill_dim(x["q"], x["k"], x["v"], coeffs, chunk=chunk, state=state, y=y,
+                            workspace=ws)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    oal.oal_profile_reset()
+    oal.oal_profile_enable(True)
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    oal.oal_profile_enable(False)
+    kt = kernel_times(oal, ALL_KERNELS + ["k_dim_coeffs"])
+    fl = dim_readout_flops_per_launch(w, chunk)
+    r_ms = kt["k_readout_vec"]["avg_ms"]
+    del x, y, ws
+    state.free()
+    torch.cuda.empty_cache()
+    return {"workload": w.name, "chunk": chunk, "ms_per_step": round(ms, 5),
+            "tokens_per_s": round(w.batch * w.seq_len / (ms * 1e-3), 1),
+            "roofline_k_readout_vec": {
+                "bound": "alu", "achieved": round(fl / (r_ms * 1e-3) / 1e12, 3),
+                "peak": PEAK_F32_VECTOR_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(fl / (r_ms * 1e-3) / 1e12 / PEAK_F32_VECTOR_TFLOPS, 5),
+                "algorithmic_flops": fl},
+            "kernels_ms": {k: round(v["avg_ms"], 5) for k, v in kt.items()}}
+
+
+def fidelity_report(oal, w, chunk, device):
+    """[OAL] App. C, Eqs. 21-22: MSE and RelMSE of the OAL output against exact
+    softmax attention on the same synthetic inputs, one sequence = all heads of a
+    batch row.  Both outputs come from the library (fp32 outputs, bf16 inputs); the
+    metric itself is plain float64 numpy.  The inputs' L is the seeded synthetic one,
+    not a calibrated one, so the figure is context for this input recipe only."""
+    import numpy as np
+    import torch
+
+    from positive_quadratic_causal_amd import synth
+    st = synth.structure(w)
+    x = gen_inputs(w, st, device, t1=w.seq_len)
+    coeffs = oal.oal_expand_coeffs(torch.from_numpy(st.n_groups).to(device),
+                                   torch.from_numpy(st.group_map).to(device),
+                                   torch.from_numpy(st.L).to(device), w.eps)
+    shape = (w.batch, w.n_q_heads, w.seq_len, 64)
+    y_oal = torch.empty(shape, dtype=torch.float32, device=device)
+    y_sm = torch.empty(shape, dtype=torch.float32, device=device)
+    state = oal.oal_state_alloc(w.batch, w.n_kv_heads)
+    oal.oal_prefill(x["q"], x["k"], x["v"], coeffs, chunk=chunk, state=state, y=y_oal)
+    oal.oal_softmax_attention(x["q"], x["k"], x["v"], y_sm)
+    torch.cuda.synchronize()
+    a = y_oal.cpu().numpy().astype(np.float64)
+    e = y_sm.cpu().numpy().astype(np.float64)
+    state.free()
+    err = ((a - e) ** 2).reshape(w.batch, -1).sum(axis=1)
+    mse = float(np.mean(err / e[0].size))
+    rel = float(np.mean(err / (e ** 2).reshape(w.batch, -1).sum(axis=1)))
+    return {"workload": w.name, "chunk": chunk, "mse": mse, "rel_mse": rel,
+            "L": "seeded synthetic (not calibrated)"}
 
 
 # HBM traffic per launch of a kernel, from rocprofv3 FETCH_SIZE / WRITE_SIZE
@@ -340,6 +486,37 @@ def cpu_baseline(w, seconds):
                        f"scaled to all {w.n_q_heads} query heads x {w.seq_len} rows")}
 
 
+def cpu_baseline_variants(w):
+    """The float64 oracles of the two variant legs on a small sample of the
+    Qwen-shaped N = 2048 workload (a few seconds each), scaled to tokens/s of the
+    whole workload: softmax attention of one head (all rows), and the
+    dimension-specific direct sum for 64 rows spread over the sequence."""
+    import numpy as np
+
+    from oracle import oal_oracle as O
+    from oracle import softmax_oracle as S
+    from positive_quadratic_causal_amd import synth
+    st = synth.structure(w)
+    q = synth.head_tensor(w, st, synth.KIND_Q, 0, 0, w.seq_len).astype(np.float64)
+    k = synth.head_tensor(w, st, synth.KIND_K, 0, 0, w.seq_len).astype(np.float64)
+    v = synth.head_tensor(w, st, synth.KIND_V, 0, 0, w.seq_len).astype(np.float64)
+    t0 = time.perf_counter()
+    S.softmax_attention(q, k, v)
+    t_sm = (time.perf_counter() - t0) * w.n_q_heads * w.batch
+    a, b, C = synth.dim_coefficients(w)
+    rows = np.linspace(0, w.seq_len - 1, 64).astype(np.int64)
+    t0 = time.perf_counter()
+    O.causal_attention_dim_rows(q[rows], rows, k, v, float(a[0]), b[0].astype(np.float64),
+                                C[0].astype(np.float64))
+    # a row's cost grows with its position; the evenly spread rows average it
+    t_dim = (time.perf_counter() - t0) / len(rows) * w.seq_len * w.n_q_heads * w.batch
+    return {"softmax": {"value": round(w.batch * w.seq_len / t_sm, 3), "unit": "tokens/s",
+                        "sample": f"query head 0 of {w.name}, all rows; scaled to {w.n_q_heads} heads"},
+            "prefill_dim": {"value": round(w.batch * w.seq_len / t_dim, 3), "unit": "tokens/s",
+                            "sample": f"64 evenly spread rows of query head 0 of {w.name}; "
+                                      f"scaled to all rows and {w.n_q_heads} heads"}}
+
+
 def measured_peaks(device):
     """Achievable rates on this GPU beside the datasheet peaks: a large bf16 GEMM
     through torch.matmul (hipBLASLt) and a device-to-device copy."""
@@ -388,7 +565,8 @@ def main() -> int:
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
-    ap.add_argument("--only", choices=["prefill", "decode"], default=None,
+    ap.add_argument("--no-softmax", action="store_true")
+    ap.add_argument("--only", choices=["prefill", "decode", "softmax", "prefill_dim"], default=None,
                     help="time one leg only (used to profile each workload on its own)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="after the legs, copy MIB MiB 5 times (reference for HBM counters)")
@@ -412,6 +590,14 @@ def main() -> int:
         if args.copy_probe:
             copy_probe(args.copy_probe)
         print(json.dumps({"metric": METRIC, "decode": res}), flush=True)
+        return 0
+    if args.only == "softmax":
+        res = bench_softmax(oal, w3, args.steps, args.warmup, device)
+        print(json.dumps({"metric": METRIC, "softmax": res}), flush=True)
+        return 0
+    if args.only == "prefill_dim":
+        res = bench_prefill_dim(oal, synth.WORKLOADS[1], args.chunk, args.steps, args.warmup, device)
+        print(json.dumps({"metric": METRIC, "prefill_dim": res}), flush=True)
         return 0
     log(f"prefill: {w3.name}, chunk {args.chunk}, {args.warmup} warmup + {args.steps} steps")
     ms, kt = bench_prefill(oal, w3, args.chunk, args.steps, args.warmup, device)
@@ -473,11 +659,24 @@ def main() -> int:
         log("decode: setting up")
         result["decode"] = bench_decode(oal, synth.WORKLOADS[4], args.decode_reps,
                                         args.decode_steps, device)
+    if not args.no_softmax and args.only is None:
+        log(f"softmax reference: {w3.name}")
+        sm = bench_softmax(oal, w3, max(3, args.steps // 4), 2, device)
+        sm["oal_speedup"] = round(sm["ms_per_step"] / ms, 3)
+        result["softmax_reference"] = sm
+        log("general prefill (dimension-specific kernel): Qwen-shaped N = 2048")
+        result["prefill_dim"] = bench_prefill_dim(oal, synth.WORKLOADS[1], args.chunk,
+                                                  max(3, args.steps // 4), 2, device)
+        log("fidelity: OAL vs softmax, MSE / RelMSE")
+        result["fidelity"] = [fidelity_report(oal, synth.WORKLOADS[i], args.chunk, device)
+                              for i in (1, 2)]
     if args.copy_probe:
         copy_probe(args.copy_probe)
     if not args.no_cpu_baseline:
         log("cpu baseline: float64 oracle on a bounded sample")
         result["cpu_baseline"] = cpu_baseline(w3, args.cpu_seconds)
+        if not args.no_softmax:
+            result["cpu_baseline"]["variants"] = cpu_baseline_variants(synth.WORKLOADS[1])
     print(json.dumps(result), flush=True)
     return 0
 

@@ -88,6 +88,24 @@ oal_status oal_expand_coeffs(int n_q_heads, int d_h, int g_max, const int32_t* n
                              const int32_t* group_map, const float* L, float eps,
                              void* coeffs, hipStream_t stream);
 
+/* Dimension-specific coefficients: the general kernel of [OAL] §4.1, Eq. 3,
+ *   kappa_dim(q, k) = a + sum_r b_r x_r + sum_{r,t} C_rt x_r x_t,  x_r = q_r k_r / sqrt(d_h),
+ * with arbitrary a, b_r and C_rt per query head (no group structure; the grouped
+ * kernel of oal_expand_coeffs is the special case a = eps + M_00,
+ * b_r = 2 M_{0,g(r)}, C_rt = M_{g(r),g(t)}).
+ *   a   device float [n_q_heads]
+ *   b   device float [n_q_heads][d_h]
+ *   C   device float [n_q_heads][d_h][d_h], row-major; only (C + C^T) / 2 enters
+ *       kappa_dim, and the record stores that symmetric part
+ *   coeffs  device output, oal_coeffs_bytes(n_q_heads, d_h, 1) bytes; the record
+ *       has NG = 0, EPS = 0, A = a, BP, CM and CP filled and the group fields zero.
+ * Such a record is read by oal_prefill_dim and oal_decode_step.  oal_prefill's
+ * readouts evaluate grouped records only and return NaN outputs for it.
+ * kappa_dim must stay positive on the inputs for the outputs to be meaningful
+ * (e.g. [[a, b^T/2], [b/2, C]] positive definite); nothing checks this. */
+oal_status oal_dim_coeffs(int n_q_heads, int d_h, const float* a, const float* b, const float* C,
+                          void* coeffs, hipStream_t stream);
+
 /* Allocate a zeroed prefix state (H0 = H1 = H2 = 0, [OAL] Algorithm 1 step 5) for
  * batch x n_kv_heads sequences.  The state is fp32 and its device layout is private
  * (use oal_state_export to read it).  Size: batch*n_kv_heads*65*2176*4 bytes. */
@@ -122,7 +140,8 @@ size_t oal_prefill_workspace_bytes(int batch, int n_q_heads, int n_kv_heads, int
  * chunks (the paper's backend works on 128-token blocks, [OAL] App. E).
  *   q   [batch][n_q_heads][seq_len][d_h];  k, v [batch][n_kv_heads][seq_len][d_h/d_v]
  *       in in_dtype (fp32 or bf16).  q may be NULL when y is NULL.
- *   coeffs  written by oal_expand_coeffs for n_q_heads heads
+ *   coeffs  written by oal_expand_coeffs for n_q_heads heads (a record of
+ *           oal_dim_coeffs gives NaN outputs here: use oal_prefill_dim)
  *   chunk   0 (= 128), 64, 128 or 256
  *   state   NULL: the sequence starts empty.  Otherwise the prefix it holds is
  *           read first and, on return, it holds the state after the seq_len
@@ -138,12 +157,31 @@ oal_status oal_prefill(int batch, int n_q_heads, int n_kv_heads, int seq_len, in
                        oal_dtype out_dtype, void* workspace, size_t workspace_bytes,
                        hipStream_t stream);
 
+/* Device workspace oal_prefill_dim needs (same conventions as
+ * oal_prefill_workspace_bytes; the size does not depend on the input dtype). */
+size_t oal_prefill_dim_workspace_bytes(int batch, int n_q_heads, int n_kv_heads, int seq_len,
+                                       int d_h, int d_v, int chunk, int with_output);
+
+/* Causal prefill for any coefficient record, including the dimension-specific ones
+ * of oal_dim_coeffs: the same chunked evaluation of [OAL] Algorithm 1 (Eq. 5-6)
+ * with the same arguments, state semantics and errors as oal_prefill, but every
+ * kernel value inside a chunk is a + sum_r b'_r p_r + sum_{r<=t} c'_rt p_r p_t
+ * (p_r = q_r k_r) from the record's expanded coefficients.  It runs on the vector
+ * ALUs in fp32 for fp32 and bf16 inputs alike (slower than oal_prefill's matrix
+ * core path for grouped records); workspace >= oal_prefill_dim_workspace_bytes(). */
+oal_status oal_prefill_dim(int batch, int n_q_heads, int n_kv_heads, int seq_len, int d_h,
+                           int d_v, oal_dtype in_dtype, const void* q, const void* k,
+                           const void* v, const void* coeffs, int chunk, oal_state* state,
+                           void* y, oal_dtype out_dtype, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream);
+
 /* One decode step: [OAL] Algorithm 1 loop body (steps 7-10) for one new token per
  * sequence: u = [v; 1]; H0 += u; H1_r += k_r u; H2_rt += k_r k_t u; then the
  * readout of Eq. 6 for every query head of the KV group (inclusive of the new
  * token).  q [batch][n_q_heads][d_h], k [batch][n_kv_heads][d_h],
  * v [batch][n_kv_heads][d_v] in in_dtype; y [batch][n_q_heads][d_v] in out_dtype;
- * state in/out. */
+ * state in/out.  coeffs may come from oal_expand_coeffs or oal_dim_coeffs (the
+ * readout uses only the expanded a, b', c'). */
 oal_status oal_decode_step(int batch, int n_q_heads, int n_kv_heads, int d_h, int d_v,
                            oal_dtype in_dtype, const void* q, const void* k, const void* v,
                            const void* coeffs, oal_state* state, void* y, oal_dtype out_dtype,

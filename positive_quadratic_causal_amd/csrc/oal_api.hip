@@ -95,6 +95,8 @@ void prof_end(int slot, hipStream_t stream) {
 }
 
 // kernels' launchers (one per source file)
+oal_status launch_dim_coeffs(int n_q_heads, const float* a, const float* b, const float* C,
+                             void* coeffs, hipStream_t stream);
 oal_status launch_expand(int n_q_heads, int g_max, const int32_t* n_groups,
                          const int32_t* group_map, const float* L, float eps, void* coeffs,
                          hipStream_t stream);
@@ -115,7 +117,7 @@ oal_status launch_prefill_mfma(int batch, int n_q_heads, int n_kv_heads, int seq
 oal_status launch_prefill_vec(int batch, int n_q_heads, int n_kv_heads, int seq_len,
                               oal_dtype in_dtype, const void* q, const void* k, const void* v,
                               const void* coeffs, int chunk, float* state, void* y,
-                              oal_dtype out_dtype, void* ws, hipStream_t stream);
+                              oal_dtype out_dtype, void* ws, bool dim, hipStream_t stream);
 
 static bool valid_dtype(oal_dtype d) { return d == OAL_F32 || d == OAL_BF16; }
 
@@ -202,6 +204,14 @@ oal_status oal_expand_coeffs(int n_q_heads, int d_h, int g_max, const int32_t* n
   return launch_expand(n_q_heads, g_max, n_groups, group_map, L, eps, coeffs, stream);
 }
 
+oal_status oal_dim_coeffs(int n_q_heads, int d_h, const float* a, const float* b, const float* C,
+                          void* coeffs, hipStream_t stream) {
+  if (n_q_heads < 1) return set_error(OAL_ERR_INVALID_ARG, "n_q_heads must be >= 1");
+  if (d_h != DH) return set_error(OAL_ERR_UNSUPPORTED, "only d_h = 64 is supported (got %d)", d_h);
+  if (!a || !b || !C || !coeffs) return set_error(OAL_ERR_INVALID_ARG, "null pointer argument");
+  return launch_dim_coeffs(n_q_heads, a, b, C, coeffs, stream);
+}
+
 oal_status oal_state_alloc(int batch, int n_kv_heads, int d_h, int d_v, oal_state** out) {
   if (!out) return set_error(OAL_ERR_INVALID_ARG, "out is null");
   *out = nullptr;
@@ -279,17 +289,18 @@ size_t oal_prefill_workspace_bytes(int batch, int n_q_heads, int n_kv_heads, int
   return with_output ? prefill_vec_workspace(batch, n_kv_heads, seq_len, chunk) : 0;
 }
 
-oal_status oal_prefill(int batch, int n_q_heads, int n_kv_heads, int seq_len, int d_h, int d_v,
-                       oal_dtype in_dtype, const void* q, const void* k, const void* v,
-                       const void* coeffs, int chunk, oal_state* state, void* y,
-                       oal_dtype out_dtype, void* workspace, size_t workspace_bytes,
-                       hipStream_t stream) {
+// Argument checks shared by oal_prefill and oal_prefill_dim; need = the
+// workspace size the chosen path requires.
+static oal_status prefill_checks(int batch, int n_q_heads, int n_kv_heads, int seq_len, int d_h,
+                                 int d_v, oal_dtype in_dtype, const void* q, const void* k,
+                                 const void* v, const void* coeffs, int chunk,
+                                 const oal_state* state, const void* y, oal_dtype out_dtype,
+                                 const void* workspace, size_t workspace_bytes, size_t need) {
   oal_status st = check_heads(batch, n_q_heads, n_kv_heads, d_h, d_v);
   if (st != OAL_OK) return st;
   if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype))
     return set_error(OAL_ERR_INVALID_ARG, "unknown dtype");
   if (seq_len < 0) return set_error(OAL_ERR_INVALID_ARG, "seq_len must be >= 0 (got %d)", seq_len);
-  chunk = resolve_chunk(chunk);
   if (chunk != 64 && chunk != 128 && chunk != 256)
     return set_error(OAL_ERR_INVALID_ARG, "chunk must be 0, 64, 128 or 256 (got %d)", chunk);
   if (state && (state->batch != batch || state->n_kv_heads != n_kv_heads))
@@ -302,21 +313,56 @@ oal_status oal_prefill(int batch, int n_q_heads, int n_kv_heads, int seq_len, in
   if (y && (!q || !coeffs)) return set_error(OAL_ERR_INVALID_ARG, "q and coeffs must not be null");
   if ((long long)seq_len * 64 * (long long)batch * n_q_heads > (1LL << 40))
     return set_error(OAL_ERR_UNSUPPORTED, "problem too large");
-  {
-    const size_t need = oal_prefill_workspace_bytes(batch, n_q_heads, n_kv_heads, seq_len, d_h, d_v,
-                                                    chunk, in_dtype, y != nullptr);
-    if (need > 0 && (!workspace || workspace_bytes < need))
-      return set_error(OAL_ERR_INVALID_ARG, "workspace too small: need %zu bytes, got %zu", need,
-                       workspace ? workspace_bytes : (size_t)0);
-    if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
-      return set_error(OAL_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
-  }
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return set_error(OAL_ERR_INVALID_ARG, "workspace too small: need %zu bytes, got %zu", need,
+                     workspace ? workspace_bytes : (size_t)0);
+  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+    return set_error(OAL_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  return OAL_OK;
+}
+
+oal_status oal_prefill(int batch, int n_q_heads, int n_kv_heads, int seq_len, int d_h, int d_v,
+                       oal_dtype in_dtype, const void* q, const void* k, const void* v,
+                       const void* coeffs, int chunk, oal_state* state, void* y,
+                       oal_dtype out_dtype, void* workspace, size_t workspace_bytes,
+                       hipStream_t stream) {
+  chunk = resolve_chunk(chunk);
+  const size_t need = oal_prefill_workspace_bytes(batch, n_q_heads, n_kv_heads, seq_len, d_h, d_v,
+                                                  chunk, in_dtype, y != nullptr);
+  oal_status st = prefill_checks(batch, n_q_heads, n_kv_heads, seq_len, d_h, d_v, in_dtype, q, k, v,
+                                 coeffs, chunk, state, y, out_dtype, workspace, workspace_bytes, need);
+  if (st != OAL_OK || seq_len == 0) return st;
   if (in_dtype == OAL_BF16)
     st = launch_prefill_mfma(batch, n_q_heads, n_kv_heads, seq_len, q, k, v, coeffs, chunk,
                              state ? state->data : nullptr, y, out_dtype, workspace, stream);
   else
     st = launch_prefill_vec(batch, n_q_heads, n_kv_heads, seq_len, in_dtype, q, k, v, coeffs, chunk,
-                            state ? state->data : nullptr, y, out_dtype, workspace, stream);
+                            state ? state->data : nullptr, y, out_dtype, workspace, false, stream);
+  if (st == OAL_OK && state) state->tokens += seq_len;
+  return st;
+}
+
+size_t oal_prefill_dim_workspace_bytes(int batch, int n_q_heads, int n_kv_heads, int seq_len,
+                                       int d_h, int d_v, int chunk, int with_output) {
+  if (check_heads(batch, n_q_heads, n_kv_heads, d_h, d_v) != OAL_OK) return 0;
+  chunk = resolve_chunk(chunk);
+  if (seq_len <= 0 || (chunk != 64 && chunk != 128 && chunk != 256)) return 0;
+  return with_output ? prefill_vec_workspace(batch, n_kv_heads, seq_len, chunk) : 0;
+}
+
+oal_status oal_prefill_dim(int batch, int n_q_heads, int n_kv_heads, int seq_len, int d_h,
+                           int d_v, oal_dtype in_dtype, const void* q, const void* k,
+                           const void* v, const void* coeffs, int chunk, oal_state* state,
+                           void* y, oal_dtype out_dtype, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream) {
+  chunk = resolve_chunk(chunk);
+  const size_t need = oal_prefill_dim_workspace_bytes(batch, n_q_heads, n_kv_heads, seq_len, d_h,
+                                                      d_v, chunk, y != nullptr);
+  oal_status st = prefill_checks(batch, n_q_heads, n_kv_heads, seq_len, d_h, d_v, in_dtype, q, k, v,
+                                 coeffs, chunk, state, y, out_dtype, workspace, workspace_bytes, need);
+  if (st != OAL_OK || seq_len == 0) return st;
+  st = launch_prefill_vec(batch, n_q_heads, n_kv_heads, seq_len, in_dtype, q, k, v, coeffs, chunk,
+                          state ? state->data : nullptr, y, out_dtype, workspace, true, stream);
   if (st == OAL_OK && state) state->tokens += seq_len;
   return st;
 }

@@ -85,6 +85,41 @@ k_expand(int g_max, const int32_t* __restrict__ n_groups, const int32_t* __restr
   }
 }
 
+// Dimension-specific coefficients, the general kernel of [OAL] §4.1 (Eq. 3):
+//   kappa_dim(q, k) = a + sum_r b_r x_r + sum_{r,t} C_rt x_r x_t,  x_r = q_r k_r / sqrt(d_h)
+// with arbitrary a, b_r, C_rt (no group structure).  x^T C x depends only on the
+// symmetric part of C, so the record holds S = (C + C^T) / 2: the full square in
+// CM and the packed pairs, weighted 1 on the diagonal and 2 off it, in CP.  The
+// group fields stay zero and NG = 0 marks the record as dimension-specific.
+__global__ void __launch_bounds__(256)
+k_dim_coeffs(const float* __restrict__ a, const float* __restrict__ b,
+             const float* __restrict__ C, float* __restrict__ coeffs) {
+  const int h = blockIdx.x;
+  const int tid = threadIdx.x;
+  float* rec = coeffs + (size_t)h * OAL_COEF_WORDS;
+  const float* Ch = C + (size_t)h * DH * DH;
+  for (int i = tid; i < OAL_COEF_WORDS; i += blockDim.x) rec[i] = 0.f;
+  __syncthreads();
+  const float inv_sqrt_d = 0.125f;   // 1 / sqrt(64)
+  const float inv_d = 1.0f / 64.0f;
+  if (tid == 0) rec[OAL_COEF_A] = a[h];   // NG and EPS stay 0
+  if (tid < DH) rec[OAL_COEF_BP + tid] = b[(size_t)h * DH + tid] * inv_sqrt_d;
+  for (int i = tid; i < DH * DH; i += blockDim.x) {
+    const int r = i / DH, t = i % DH;
+    const float sym = 0.5f * (Ch[r * DH + t] + Ch[t * DH + r]);
+    rec[OAL_COEF_CM + i] = sym * inv_d;
+    if (t >= r) rec[OAL_COEF_CP + pair_index(r, t)] = (r == t ? 1.0f : 2.0f) * sym * inv_d;
+  }
+}
+
+oal_status launch_dim_coeffs(int n_q_heads, const float* a, const float* b, const float* C,
+                             void* coeffs, hipStream_t stream) {
+  ProfScope ps("k_dim_coeffs", stream);
+  hipLaunchKernelGGL(k_dim_coeffs, dim3(n_q_heads), dim3(256), 0, stream, a, b, C,
+                     reinterpret_cast<float*>(coeffs));
+  return check_launch("k_dim_coeffs");
+}
+
 oal_status launch_expand(int n_q_heads, int g_max, const int32_t* n_groups,
                          const int32_t* group_map, const float* L, float eps, void* coeffs,
                          hipStream_t stream) {

@@ -697,7 +697,9 @@ k_readout_mfma(int n_q_heads, int n_kv_heads, int seq_len, int n_chunks, int n_h
   for (int nt = 0; nt < 2; ++nt) {
     const int tok = tok0 + 32 * nt + col;
     if (tok >= clen) continue;
-    const float inv = 1.0f / den[nt];
+    // NG = 0 marks a dimension-specific record, which this grouped readout
+    // cannot evaluate: its outputs are made NaN rather than silently wrong
+    const float inv = G >= 1 ? 1.0f / den[nt] : __builtin_nanf("");
     O* yr = y + (((size_t)b * n_q_heads + hq) * seq_len + t0 + tok) * DV;
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)

@@ -6,8 +6,12 @@
 //   scan    H_{<c} = H_init + sum_{c' < c} dH_{c'}               (exclusive prefix)
 //   readout u~_i = phi_q(q_i)^T H_{<c} + sum_{j in T_c, j <= i} kappa(q_i, k_j) u_j
 //           y_i = u~_{i,1:64} / u~_{i,65}                         ([OAL] Eq. 6, 7)
-// The intra-chunk kernel values use kappa = eps + sum_p t_p^2 with
-// t_p = L_0p + sum_r ell_p[r] q_r k_r, the expansion of ||L^T s_bar||^2 of Eq. 7.
+// The intra-chunk kernel values of a grouped record use kappa = eps + sum_p t_p^2
+// with t_p = L_0p + sum_r ell_p[r] q_r k_r, the expansion of ||L^T s_bar||^2 of
+// Eq. 7.  A dimension-specific record (the general kernel of [OAL] Eq. 3) takes
+// kappa = a + sum_r p_r (b'_r + sum_t S_rt p_t) with p_r = q_r k_r and S the
+// symmetric C / d_h square of the record (equal to the packed-pair sum the state
+// readout uses).
 // Everything is fp32 with fp32 accumulation; this path favours simplicity over
 // speed (the bf16 inputs go through the matrix-core path).
 #include "oal_common.h"
@@ -20,6 +24,22 @@ constexpr int FB = 64;                 // feature rows per build block
 constexpr int NFB = DS / FB;           // 34 build blocks per unit
 constexpr int TB = 64;                 // tokens staged per step
 constexpr int WPT = (W + 3) / 4;       // 17 columns per thread in the build
+constexpr int WP = 68;                 // readout rows of H and u padded to 16 bytes
+
+// acc[0..WP) += s * row[0..WP) for a 16-byte aligned LDS row: the whole row is
+// read into registers first (17 wide reads in flight), then the multiply-adds
+__device__ __forceinline__ void axpy_row(float (&acc)[WP], float s, const float* row) {
+  float4 r4[WP / 4];
+#pragma unroll
+  for (int i = 0; i < WP / 4; ++i) r4[i] = reinterpret_cast<const float4*>(row)[i];
+#pragma unroll
+  for (int i = 0; i < WP / 4; ++i) {
+    acc[4 * i + 0] = fmaf(s, r4[i].x, acc[4 * i + 0]);
+    acc[4 * i + 1] = fmaf(s, r4[i].y, acc[4 * i + 1]);
+    acc[4 * i + 2] = fmaf(s, r4[i].z, acc[4 * i + 2]);
+    acc[4 * i + 3] = fmaf(s, r4[i].w, acc[4 * i + 3]);
+  }
+}
 }  // namespace
 
 // dH over tokens [t0, t1) of one unit for feature rows [fb*64, fb*64+64).
@@ -104,7 +124,10 @@ k_scan_vec(int n_chunks, float* __restrict__ ws, float* __restrict__ state) {
 }
 
 // One block per (chunk, query head, batch); thread i owns token i of the chunk.
-template <typename T, typename O>
+// DIM: the record is dimension-specific (intra-chunk kappa from b', c');
+// otherwise it is grouped, and a record with NG = 0 (dimension-specific) makes
+// every output NaN instead of a silently wrong value.
+template <typename T, typename O, bool DIM>
 __global__ void __launch_bounds__(256)
 k_readout_vec(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunks,
               const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
@@ -120,13 +143,15 @@ k_readout_vec(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunk
   const int clen = min(chunk, seq_len - t0);
 
   extern __shared__ float smem[];
+  // every array starts at a multiple of 4 floats (chunk and TB are multiples of 64)
   float* s_q = smem;                          // [chunk][DH + 1]
-  float* s_H = s_q + chunk * (DH + 1);        // [32][W]
-  float* s_cf = s_H + 32 * W;                 // [32]
+  float* s_H = s_q + chunk * (DH + 1);        // [32][WP]
+  float* s_cf = s_H + 32 * WP;                // [32]
   float* s_k = s_cf + 32;                     // [TB][DH + 1]
-  float* s_u = s_k + TB * (DH + 1);           // [TB][W]
-  float* s_ell = s_u + TB * W;                // [LDIM][DH]
-  float* s_L0 = s_ell + LDIM * DH;            // [LDIM]
+  float* s_u = s_k + TB * (DH + 1);           // [TB][WP]
+  float* s_ell = s_u + TB * WP;               // grouped: [LDIM][DH]; DIM: b' [DH]
+  float* s_L0 = s_ell + LDIM * DH;            // grouped: [LDIM]
+  float* s_cm = s_ell + DH;                   // DIM: S = C / d_h [DH][DH]
 
   const float* rec = coef_rec(coeffs, hq);
   const float a = rec[OAL_COEF_A];
@@ -138,13 +163,21 @@ k_readout_vec(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunk
     s_q[ii * (DH + 1) + d] =
         ii < clen ? Elem<T>::load(q, (((size_t)b * n_q_heads + hq) * seq_len + t0 + ii) * DH + d) : 0.f;
   }
-  for (int i = tid; i < LDIM * DH; i += blockDim.x) s_ell[i] = rec[OAL_COEF_ELL + i];
-  if (tid < LDIM) s_L0[tid] = rec[OAL_COEF_L + tid];   // row 0 of L: L_{0,p}
+  if constexpr (DIM) {
+    for (int i = tid; i < DH; i += blockDim.x) s_ell[i] = rec[OAL_COEF_BP + i];
+    for (int i = tid; i < DH * DH; i += blockDim.x) s_cm[i] = rec[OAL_COEF_CM + i];
+  } else {
+    for (int i = tid; i < LDIM * DH; i += blockDim.x) s_ell[i] = rec[OAL_COEF_ELL + i];
+    if (tid < LDIM) s_L0[tid] = rec[OAL_COEF_L + tid];   // row 0 of L: L_{0,p}
+  }
+  // the pad columns W..WP-1 of the H and u rows are never written again
+  for (int i = tid; i < 32 * (WP - W); i += blockDim.x) s_H[(i / (WP - W)) * WP + W + i % (WP - W)] = 0.f;
+  for (int i = tid; i < TB * (WP - W); i += blockDim.x) s_u[(i / (WP - W)) * WP + W + i % (WP - W)] = 0.f;
   __syncthreads();
 
-  float acc[W];
+  float acc[WP];
 #pragma unroll
-  for (int w = 0; w < W; ++w) acc[w] = 0.f;
+  for (int w = 0; w < WP; ++w) acc[w] = 0.f;
   const bool active = tid < clen;
   const float* qi = s_q + tid * (DH + 1);
 
@@ -154,7 +187,7 @@ k_readout_vec(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunk
     __syncthreads();
     for (int i = tid; i < 32 * W; i += blockDim.x) {
       int w = i / 32, ff = i % 32;
-      s_H[ff * W + w] = (f0 + ff < DS) ? Hc[(size_t)w * DS + f0 + ff] : 0.f;
+      s_H[ff * WP + w] = Hc[(size_t)w * DS + f0 + ff];   // f0 + 31 < DS always
     }
     if (tid < 32) {
       int f = f0 + tid;
@@ -176,9 +209,7 @@ k_readout_vec(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunk
           uint16_t rt = c_vec_pairs.rt[f - 1 - DH];
           phi = s_cf[ff] * qi[rt >> 8] * qi[rt & 0xff];
         }
-        const float* hrow = s_H + ff * W;
-#pragma unroll
-        for (int w = 0; w < W; ++w) acc[w] = fmaf(phi, hrow[w], acc[w]);
+        axpy_row(acc, phi, s_H + ff * WP);
       }
     }
   }
@@ -196,42 +227,65 @@ k_readout_vec(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunk
         vv_ = Elem<T>::load(v, (kbase + j0 + jj) * DV + d);
       }
       s_k[jj * (DH + 1) + d] = kv_;
-      s_u[jj * W + d] = vv_;
+      s_u[jj * WP + d] = vv_;
     }
-    for (int jj = tid; jj < TB; jj += blockDim.x) s_u[jj * W + DV] = 1.f;
+    for (int jj = tid; jj < TB; jj += blockDim.x) s_u[jj * WP + DV] = 1.f;
     __syncthreads();
     if (active) {
       const int jmax = min(nj, tid - j0 + 1);
       for (int jj = 0; jj < jmax; ++jj) {
         const float* kj = s_k + jj * (DH + 1);
-        float tp[LDIM];
+        float kap;
+        if constexpr (DIM) {
+          float pr[DH];
 #pragma unroll
-        for (int p = 0; p < LDIM; ++p) tp[p] = s_L0[p];
-        for (int r = 0; r < DH; ++r) {
-          float x = qi[r] * kj[r];
+          for (int t = 0; t < DH; ++t) pr[t] = qi[t] * kj[t];
+          kap = a;
+          // rows of S stream from LDS (one broadcast row per r); a rolled r loop
+          // keeps the 4096 coefficients out of registers
+#pragma unroll 1
+          for (int r = 0; r < DH; ++r) {
+            float4 s4[DH / 4];
 #pragma unroll
-          for (int p = 0; p < LDIM; ++p) tp[p] = fmaf(s_ell[p * DH + r], x, tp[p]);
+            for (int i = 0; i < DH / 4; ++i) s4[i] = reinterpret_cast<const float4*>(s_cm + r * DH)[i];
+            float sa = s_ell[r], sb = 0.f;   // two chains halve the dependent adds
+#pragma unroll
+            for (int i = 0; i < DH / 4; ++i) {
+              sa = fmaf(s4[i].x, pr[4 * i + 0], sa);
+              sb = fmaf(s4[i].y, pr[4 * i + 1], sb);
+              sa = fmaf(s4[i].z, pr[4 * i + 2], sa);
+              sb = fmaf(s4[i].w, pr[4 * i + 3], sb);
+            }
+            kap = fmaf(sa + sb, qi[r] * kj[r], kap);
+          }
+        } else {
+          float tp[LDIM];
+#pragma unroll
+          for (int p = 0; p < LDIM; ++p) tp[p] = s_L0[p];
+          for (int r = 0; r < DH; ++r) {
+            float x = qi[r] * kj[r];
+#pragma unroll
+            for (int p = 0; p < LDIM; ++p) tp[p] = fmaf(s_ell[p * DH + r], x, tp[p]);
+          }
+          kap = eps;
+#pragma unroll
+          for (int p = 0; p < LDIM; ++p)
+            if (p <= G) kap = fmaf(tp[p], tp[p], kap);
         }
-        float kap = eps;
-#pragma unroll
-        for (int p = 0; p < LDIM; ++p)
-          if (p <= G) kap = fmaf(tp[p], tp[p], kap);
-        const float* uj = s_u + jj * W;
-#pragma unroll
-        for (int w = 0; w < W; ++w) acc[w] = fmaf(kap, uj[w], acc[w]);
+        axpy_row(acc, kap, s_u + jj * WP);
       }
     }
   }
 
   if (active) {
-    const float inv = 1.0f / acc[DV];
+    const float inv = (DIM || G >= 1) ? 1.0f / acc[DV] : __builtin_nanf("");
     O* yo = y + (((size_t)b * n_q_heads + hq) * seq_len + t0 + tid) * DV;
 #pragma unroll
     for (int w = 0; w < DV; ++w) Elem<O>::store(yo, w, acc[w] * inv);
   }
 }
 
-template <typename T, typename O>
+template <typename T, typename O, bool DIM>
 static oal_status prefill_vec_typed(int batch, int n_q_heads, int n_kv_heads, int seq_len,
                                     const void* q, const void* k, const void* v,
                                     const void* coeffs, int chunk, float* state, void* y,
@@ -262,13 +316,13 @@ static oal_status prefill_vec_typed(int batch, int n_q_heads, int n_kv_heads, in
     st = check_launch("k_scan_vec");
   }
   if (st != OAL_OK) return st;
-  size_t smem = sizeof(float) * ((size_t)chunk * (DH + 1) + 32 * W + 32 + TB * (DH + 1) + TB * W +
-                                 LDIM * DH + LDIM);
-  if (hipFuncSetAttribute(reinterpret_cast<const void*>(&k_readout_vec<T, O>),
+  size_t smem = sizeof(float) * ((size_t)chunk * (DH + 1) + 32 * WP + 32 + TB * (DH + 1) + TB * WP +
+                                 (DIM ? DH + DH * DH : LDIM * DH + LDIM));
+  if (hipFuncSetAttribute(reinterpret_cast<const void*>(&k_readout_vec<T, O, DIM>),
                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem) != hipSuccess)
     return set_error(OAL_ERR_HIP, "k_readout_vec: cannot reserve %zu bytes of LDS", smem);
   ProfScope ps("k_readout_vec", stream);
-  hipLaunchKernelGGL((k_readout_vec<T, O>), dim3(n_chunks, n_q_heads, batch), dim3(chunk), smem,
+  hipLaunchKernelGGL((k_readout_vec<T, O, DIM>), dim3(n_chunks, n_q_heads, batch), dim3(chunk), smem,
                      stream, n_q_heads, n_kv_heads, seq_len, chunk, n_chunks,
                      reinterpret_cast<const T*>(q), kk, vv, coeffs, ws, reinterpret_cast<O*>(y));
   return check_launch("k_readout_vec");
@@ -293,16 +347,18 @@ size_t prefill_vec_workspace(int batch, int n_kv_heads, int seq_len, int chunk) 
 oal_status launch_prefill_vec(int batch, int n_q_heads, int n_kv_heads, int seq_len,
                               oal_dtype in_dtype, const void* q, const void* k, const void* v,
                               const void* coeffs, int chunk, float* state, void* y,
-                              oal_dtype out_dtype, void* ws, hipStream_t stream) {
+                              oal_dtype out_dtype, void* ws, bool dim, hipStream_t stream) {
   float* w = reinterpret_cast<float*>(ws);
-  if (in_dtype == OAL_F32) {
-    if (out_dtype == OAL_F32)
-      return prefill_vec_typed<float, float>(batch, n_q_heads, n_kv_heads, seq_len, q, k, v, coeffs, chunk, state, y, w, stream);
-    return prefill_vec_typed<float, uint16_t>(batch, n_q_heads, n_kv_heads, seq_len, q, k, v, coeffs, chunk, state, y, w, stream);
+#define OAL_VEC_CALL(T, O, D) \
+  prefill_vec_typed<T, O, D>(batch, n_q_heads, n_kv_heads, seq_len, q, k, v, coeffs, chunk, state, y, w, stream)
+  const bool f32_in = in_dtype == OAL_F32, f32_out = out_dtype == OAL_F32;
+  if (dim) {
+    if (f32_in) return f32_out ? OAL_VEC_CALL(float, float, true) : OAL_VEC_CALL(float, uint16_t, true);
+    return f32_out ? OAL_VEC_CALL(uint16_t, float, true) : OAL_VEC_CALL(uint16_t, uint16_t, true);
   }
-  if (out_dtype == OAL_F32)
-    return prefill_vec_typed<uint16_t, float>(batch, n_q_heads, n_kv_heads, seq_len, q, k, v, coeffs, chunk, state, y, w, stream);
-  return prefill_vec_typed<uint16_t, uint16_t>(batch, n_q_heads, n_kv_heads, seq_len, q, k, v, coeffs, chunk, state, y, w, stream);
+  if (f32_in) return f32_out ? OAL_VEC_CALL(float, float, false) : OAL_VEC_CALL(float, uint16_t, false);
+  return f32_out ? OAL_VEC_CALL(uint16_t, float, false) : OAL_VEC_CALL(uint16_t, uint16_t, false);
+#undef OAL_VEC_CALL
 }
 
 }  // namespace oal

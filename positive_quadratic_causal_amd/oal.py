@@ -47,6 +47,7 @@ def _load() -> ctypes.CDLL:
         "oal_coeffs_bytes": (c_size, [c_int, c_int, c_int]),
         "oal_expand_coeffs": (c_int, [c_int, c_int, c_int, c_void, c_void, c_void, c_float,
                                       c_void, c_void]),
+        "oal_dim_coeffs": (c_int, [c_int, c_int, c_void, c_void, c_void, c_void, c_void]),
         "oal_state_alloc": (c_int, [c_int, c_int, c_int, c_int, ctypes.POINTER(c_void)]),
         "oal_state_reset": (c_int, [c_void, c_void]),
         "oal_state_free": (c_int, [c_void]),
@@ -59,6 +60,11 @@ def _load() -> ctypes.CDLL:
         "oal_prefill": (c_int, [c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_void, c_void,
                                 c_void, c_void, c_int, c_void, c_void, c_int, c_void, c_size,
                                 c_void]),
+        "oal_prefill_dim_workspace_bytes": (c_size, [c_int, c_int, c_int, c_int, c_int, c_int,
+                                                     c_int, c_int]),
+        "oal_prefill_dim": (c_int, [c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_void,
+                                    c_void, c_void, c_void, c_int, c_void, c_void, c_int, c_void,
+                                    c_size, c_void]),
         "oal_decode_step": (c_int, [c_int, c_int, c_int, c_int, c_int, c_int, c_void, c_void,
                                     c_void, c_void, c_void, c_void, c_int, c_void]),
         "oal_softmax_attention": (c_int, [c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_void,
@@ -79,9 +85,10 @@ def _load() -> ctypes.CDLL:
 
 _lib = _load()
 
-EXPORTED = ("oal_coeffs_bytes", "oal_expand_coeffs", "oal_state_alloc", "oal_state_reset",
-            "oal_state_free", "oal_state_copy", "oal_state_bytes", "oal_state_tokens",
-            "oal_state_export", "oal_prefill_workspace_bytes", "oal_prefill",
+EXPORTED = ("oal_coeffs_bytes", "oal_expand_coeffs", "oal_dim_coeffs", "oal_state_alloc",
+            "oal_state_reset", "oal_state_free", "oal_state_copy", "oal_state_bytes",
+            "oal_state_tokens", "oal_state_export", "oal_prefill_workspace_bytes", "oal_prefill",
+            "oal_prefill_dim_workspace_bytes", "oal_prefill_dim",
             "oal_decode_step", "oal_softmax_attention", "oal_profile_enable", "oal_profile_reset",
             "oal_profile_query",
             "oal_status_string", "oal_last_error")
@@ -140,6 +147,23 @@ def oal_expand_coeffs(n_groups: torch.Tensor, group_map: torch.Tensor, L: torch.
     assert L.dtype == torch.float32
     _check(_lib.oal_expand_coeffs(Hq, group_map.shape[-1], g_max, _ptr(n_groups), _ptr(group_map),
                                   _ptr(L), float(eps), _ptr(coeffs), _stream(L)))
+    return coeffs
+
+
+def oal_dim_coeffs(a: torch.Tensor, b: torch.Tensor, C: torch.Tensor,
+                   coeffs: torch.Tensor | None = None) -> torch.Tensor:
+    """Dimension-specific coefficients: a float32 [Hq], b float32 [Hq, 64],
+    C float32 [Hq, 64, 64].  Returns (or fills) a coefficient buffer [Hq, COEF_WORDS]
+    for oal_prefill_dim and oal_decode_step."""
+    Hq = a.shape[0]
+    assert a.dtype == b.dtype == C.dtype == torch.float32
+    assert tuple(b.shape) == (Hq, D_H) and tuple(C.shape) == (Hq, D_H, D_H)
+    assert a.is_contiguous() and b.is_contiguous() and C.is_contiguous()
+    if coeffs is None:
+        coeffs = torch.empty((Hq, COEF_WORDS), dtype=torch.float32, device=a.device)
+    if coeffs.numel() * 4 < oal_coeffs_bytes(Hq, D_H, 1):
+        raise ValueError("coeffs buffer too small")
+    _check(_lib.oal_dim_coeffs(Hq, D_H, _ptr(a), _ptr(b), _ptr(C), _ptr(coeffs), _stream(a)))
     return coeffs
 
 
@@ -238,6 +262,34 @@ def oal_prefill(q: torch.Tensor | None, k: torch.Tensor, v: torch.Tensor, coeffs
                             chunk, state.handle if state is not None else None, _ptr(y), out_dt,
                             _ptr(workspace) if workspace is not None else None,
                             workspace.numel() if workspace is not None else 0, _stream(k)))
+    return y
+
+
+def oal_prefill_dim_workspace_bytes(batch: int, n_q_heads: int, n_kv_heads: int, seq_len: int,
+                                    chunk: int = 0, with_output: bool = True) -> int:
+    return int(_lib.oal_prefill_dim_workspace_bytes(batch, n_q_heads, n_kv_heads, seq_len, D_H,
+                                                    D_V, chunk, 1 if with_output else 0))
+
+
+def oal_prefill_dim(q: torch.Tensor | None, k: torch.Tensor, v: torch.Tensor,
+                    coeffs: torch.Tensor | None, chunk: int = 0, state: OalState | None = None,
+                    y: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                    want_output: bool = True) -> torch.Tensor | None:
+    """Prefill for any coefficient record (dimension-specific ones included); same
+    shapes and semantics as oal_prefill."""
+    B, Hkv, N, dh = k.shape
+    dv = v.shape[-1]
+    Hq = q.shape[1] if q is not None else (coeffs.shape[0] if coeffs is not None else Hkv)
+    if want_output and y is None:
+        y = torch.empty((B, Hq, N, dv), dtype=q.dtype, device=q.device)
+    out_dt = _dtype_code(y) if y is not None else OAL_F32
+    if workspace is None:
+        workspace = alloc_workspace(oal_prefill_dim_workspace_bytes(B, Hq, Hkv, N, chunk, y is not None),
+                                    k.device)
+    _check(_lib.oal_prefill_dim(B, Hq, Hkv, N, dh, dv, _dtype_code(k), _ptr(q), _ptr(k), _ptr(v),
+                                _ptr(coeffs), chunk, state.handle if state is not None else None,
+                                _ptr(y), out_dt, _ptr(workspace) if workspace is not None else None,
+                                workspace.numel() if workspace is not None else 0, _stream(k)))
     return y
 
 

@@ -24,7 +24,11 @@ Recipe (also stated in the design doc):
   bf16 workloads;
 * L per query head: (G+1)x(G+1) lower triangular, N(0, 0.3^2) entries, diagonal
   replaced by |.| + 0.5, zero above the diagonal; eps = 1e-6;
-* groups are labelled 1..G, group 1 being the bulk of non-outlier dimensions.
+* groups are labelled 1..G, group 1 being the bulk of non-outlier dimensions;
+* dimension-specific coefficients (stream kind 4, one per query head): with
+  F ~ N(0, 1)^{65x65} and P = F F^T / 65 + 0.05 I, a = P_00, b_r = 2 P_0r and
+  C = P_{1:,1:} + 0.3 (A - A^T), A ~ N(0, 1)^{64x64}: a positive definite form in
+  [1, x] plus an antisymmetric part, all float32.
 """
 
 from __future__ import annotations
@@ -38,7 +42,7 @@ D_H = 64
 D_V = 64
 G_MAX = 6
 
-KIND_STRUCT, KIND_Q, KIND_K, KIND_V = 0, 1, 2, 3
+KIND_STRUCT, KIND_Q, KIND_K, KIND_V, KIND_DIM = 0, 1, 2, 3, 4
 
 
 @dataclass(frozen=True)
@@ -110,6 +114,25 @@ def random_L(rng: np.random.Generator, n_groups: int) -> np.ndarray:
     out = np.zeros((G_MAX + 1, G_MAX + 1), dtype=np.float32)
     out[:n, :n] = Lh
     return out
+
+
+def dim_coefficients(w: Workload):
+    """(a [Hq], b [Hq, 64], C [Hq, 64, 64]) float32 for the dimension-specific kernel:
+    the form [[a, b^T / 2], [b / 2, sym(C)]] is positive definite, so the kernel is
+    positive for every q, k, and C carries an antisymmetric part as well."""
+    d = w.d_h
+    a = np.empty(w.n_q_heads, dtype=np.float32)
+    b = np.empty((w.n_q_heads, d), dtype=np.float32)
+    C = np.empty((w.n_q_heads, d, d), dtype=np.float32)
+    for h in range(w.n_q_heads):
+        rng = _rng(w.wid, KIND_DIM, 0, h)
+        F = rng.standard_normal((d + 1, d + 1))
+        P = F @ F.T / (d + 1) + 0.05 * np.eye(d + 1)
+        A = rng.standard_normal((d, d))
+        a[h] = P[0, 0]
+        b[h] = 2.0 * P[0, 1:]
+        C[h] = P[1:, 1:] + 0.3 * (A - A.T)
+    return a, b, C
 
 
 def structure(w: Workload) -> Structure:

@@ -85,9 +85,10 @@ P = ctypes.c_void_p(0x1000)   # never dereferenced: validation fails first
     ((1, 14, 2, 16, 64, 64, 1, P, P, P, P, 0, None, P, 1, None, 1 << 30), 1),  # ws null
     ((1, 14, 2, 16, 64, 64, 1, P, P, P, P, 0, None, P, 1, ctypes.c_void_p(0x1010), 1 << 30), 1),
 ])
-def test_prefill_rejects_invalid_arguments(args, expect):
+@pytest.mark.parametrize("entry", ["oal_prefill", "oal_prefill_dim"])
+def test_prefill_rejects_invalid_arguments(args, expect, entry):
     lib, oal = _lib()
-    st = lib.oal_prefill(*args, None)
+    st = getattr(lib, entry)(*args, None)
     assert st == expect, lib.oal_last_error()
     assert lib.oal_last_error()
 
@@ -95,6 +96,21 @@ def test_prefill_rejects_invalid_arguments(args, expect):
 def test_prefill_empty_sequence_is_a_noop():
     lib, oal = _lib()
     assert lib.oal_prefill(1, 14, 2, 0, 64, 64, 1, P, P, P, P, 0, None, P, 1, None, 0, None) == 0
+    assert lib.oal_prefill_dim(1, 14, 2, 0, 64, 64, 1, P, P, P, P, 0, None, P, 1, None, 0, None) == 0
+
+
+def test_dim_entries_sizes_and_checks():
+    lib, oal = _lib()
+    # the general path's workspace: one prefix state per (unit, chunk), any input dtype
+    per_state = 65 * 2176 * 4
+    assert lib.oal_prefill_dim_workspace_bytes(1, 14, 2, 300, 64, 64, 128, 1) == 2 * 3 * per_state
+    assert lib.oal_prefill_dim_workspace_bytes(1, 14, 2, 300, 64, 64, 0, 0) == 0
+    assert lib.oal_prefill_dim_workspace_bytes(1, 14, 2, 300, 64, 64, 96, 1) == 0
+    assert lib.oal_prefill_dim_workspace_bytes(1, 14, 3, 300, 64, 64, 128, 1) == 0
+    assert lib.oal_dim_coeffs(0, 64, P, P, P, P, None) == 1
+    assert lib.oal_dim_coeffs(2, 32, P, P, P, P, None) == 2
+    assert lib.oal_dim_coeffs(2, 64, P, None, P, P, None) == 1
+    assert lib.oal_dim_coeffs(2, 64, P, P, P, None, None) == 1
 
 
 def test_decode_and_expand_reject_invalid_arguments():

@@ -63,3 +63,31 @@ def test_softmax_qwen_2048_sampled_heads(oal):
     y = oal.oal_softmax_attention(case.q, case.k, case.v)
     torch.cuda.synchronize()
     _check(case, y, [(0, 0), (0, 6), (0, 7), (0, 13)], BAR)
+
+
+def test_fidelity_of_library_outputs_matches_oracle(oal):
+    """MSE / RelMSE ([OAL] App. C, Eqs. 21-22) of OAL against softmax, from the
+    library's two fp32 outputs, agree with the same metrics taken between the two
+    float64 oracles on the same inputs (both outputs are within 1e-3 rel-L2 of
+    their oracles, so the metrics agree to well under 5%)."""
+    w = synth.small_workload(530, "fidelity", 2, 6, 2, 600, "bf16", grouping="llama")
+    announce("fidelity B=2 6/2 N=600: library outputs vs the oracles")
+    case = Case(w)
+    shape = tuple(case.q.shape)
+    y_oal = torch.empty(shape, dtype=torch.float32, device="cuda")
+    y_sm = torch.empty(shape, dtype=torch.float32, device="cuda")
+    state = oal.oal_state_alloc(2, 2)
+    oal.oal_prefill(case.q, case.k, case.v, case.coeffs(), chunk=128, state=state, y=y_oal)
+    oal.oal_softmax_attention(case.q, case.k, case.v, y_sm)
+    torch.cuda.synchronize()
+    state.free()
+    a = y_oal.cpu().numpy()
+    e = y_sm.cpu().numpy()
+    o_oal = np.stack([np.stack([case.oracle_head(b, h) for h in range(6)]) for b in range(2)])
+    o_sm = np.stack([np.stack([S.softmax_attention(*case.head_qkv(b, h)) for h in range(6)])
+                     for b in range(2)])
+    mse_lib, rel_lib = S.fidelity(list(a), list(e))
+    mse_ref, rel_ref = S.fidelity(list(o_oal), list(o_sm))
+    assert rel_ref > 1e-3          # the two attentions really differ on these inputs
+    assert abs(mse_lib - mse_ref) <= 0.05 * mse_ref, (mse_lib, mse_ref)
+    assert abs(rel_lib - rel_ref) <= 0.05 * rel_ref, (rel_lib, rel_ref)
