@@ -50,6 +50,8 @@ __all__ = [
     "causal_attention_gqa",
     "causal_attention_dim_rows",
     "causal_attention_dim",
+    "causal_attention_dim_grad",
+    "grouped_coeff_grad",
     "recurrence",
     "canonical_state",
     "packed_pairs",
@@ -228,6 +230,82 @@ def causal_attention_dim(q, k, v, a, b, C):
     """:func:`causal_attention_dim_rows` for every row of one head's sequence."""
     q = np.asarray(q, dtype=np.float64)
     return causal_attention_dim_rows(q, np.arange(q.shape[0]), k, v, a, b, C)
+
+
+def causal_attention_dim_grad(q, k, v, a, b, C, dy):
+    """Gradients of the causal attention of :func:`causal_attention_dim` (the
+    dimension-specific kernel of [OAL] Eq. 3) for the loss sum_i dy_i . y_i, by
+    differentiating the direct sum term by term (the chain rule written out).
+
+    Per row i, with den_i = sum_{j<=i} kappa_ij and u_j = [v_j; 1]:
+    g_i = [dy_i / den_i ; -(dy_i . y_i) / den_i] is the gradient with respect to
+    the unnormalised [numerator; denominator] of row i, and alpha_ij = g_i . u_j
+    the gradient with respect to kappa_ij.  With x_ij = q_i o k_j / sqrt(d_h) and
+    w_ij = b + 2 sym(C) x_ij (the gradient of kappa_ij with respect to x_ij):
+      dv_j = sum_{i>=j} kappa_ij g_i[:d_v]
+      dq_i = sum_{j<=i} alpha_ij k_j o w_ij / sqrt(d_h)
+      dk_j = sum_{i>=j} alpha_ij q_i o w_ij / sqrt(d_h)
+      da = sum alpha_ij,  db = sum alpha_ij x_ij,  dC = sum alpha_ij x_ij x_ij^T.
+    Returns (dq, dk, dv, da, db, dC); dC is symmetric (only sym(C) enters kappa)."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    dy = np.asarray(dy, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    C = np.asarray(C, dtype=np.float64)
+    N, d_h = q.shape
+    d_v = v.shape[1]
+    sq = math.sqrt(d_h)
+    Cs = 0.5 * (C + C.T)
+    u = np.concatenate([v, np.ones((N, 1))], axis=1)
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    da = 0.0
+    db = np.zeros(d_h)
+    dC = np.zeros((d_h, d_h))
+    for i in range(N):
+        x = q[i][None, :] * k[: i + 1] / sq                       # [i+1, d_h]
+        kap = a + x @ b + np.einsum("jr,rt,jt->j", x, C, x)
+        ut = kap @ u[: i + 1]
+        den = ut[d_v]
+        y = ut[:d_v] / den
+        g = np.append(dy[i] / den, -(dy[i] @ y) / den)
+        alpha = u[: i + 1] @ g                                     # [i+1]
+        w = b[None, :] + 2.0 * x @ Cs                              # [i+1, d_h]
+        dq[i] = (alpha[:, None] * k[: i + 1] * w).sum(axis=0) / sq
+        dk[: i + 1] += alpha[:, None] * q[i][None, :] * w / sq
+        dv[: i + 1] += kap[:, None] * g[None, :d_v]
+        da += alpha.sum()
+        db += alpha @ x
+        dC += (alpha[:, None] * x).T @ x
+    return dq, dk, dv, da, db, dC
+
+
+def grouped_coeff_grad(L, group_map, n_groups, da, db, dC):
+    """Gradient with respect to L of a loss whose gradient with respect to the
+    dimension-wise coefficients (a, b, C) of [OAL] Eq. 3 is (da, db, dC), through
+    the grouped map of [OAL] §4.3 (a = eps + M_00, b_r = 2 M_{0,g(r)},
+    C_rt = M_{g(r),g(t)}, M = L L^T).  In the group sums s_bar the kernel is
+    eps + sum_uv M_uv s_bar_u s_bar_v, so the gradient with respect to the entry
+    M_uv is sum alpha s_bar_u s_bar_v: dM_00 = da, dM_{0,gam} = dM_{gam,0} =
+    sum_{r in gam} db_r, dM_{gam,del} = sum_{r in gam, t in del} dC_rt; then
+    dL = (dM + dM^T) L, of which the lower triangle is returned (the entries of L
+    above its diagonal are not parameters).  Shape as L."""
+    L = np.asarray(L, dtype=np.float64)
+    n = n_groups + 1
+    g = np.asarray(group_map, dtype=np.int64)
+    dM = np.zeros((n, n))
+    dM[0, 0] = da
+    for gam in range(1, n):
+        cols = g == gam
+        dM[0, gam] = dM[gam, 0] = np.sum(np.asarray(db)[cols])
+        for dlt in range(1, n):
+            dM[gam, dlt] = np.sum(np.asarray(dC)[np.ix_(cols, g == dlt)])
+    Lf = lower_factor(L)[:n, :n]
+    out = np.zeros_like(L)
+    out[:n, :n] = np.tril((dM + dM.T) @ Lf)
+    return out
 
 
 def causal_attention_gqa(q, k, v, L, group_map, n_groups, eps, heads=None):

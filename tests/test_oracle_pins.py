@@ -402,3 +402,57 @@ def test_p15_dim_closed_forms():
     A = rng.normal(size=(d, d)) * 3
     np.testing.assert_allclose(O.causal_attention_dim(q, k, v, a, b, C + A - A.T),
                                O.causal_attention_dim(q, k, v, a, b, C), rtol=1e-11, atol=1e-13)
+
+
+# --- P16: the backward oracle against central finite differences of the
+#          (pinned) forward oracles: every gradient, both parameterisations ------
+
+def _fd(f, x, h=1e-6):
+    """Central differences of the scalar function f at every entry of x."""
+    x = np.array(x, dtype=np.float64)
+    out = np.zeros_like(x)
+    it = np.nditer(x, flags=["multi_index"])
+    for _ in it:
+        idx = it.multi_index
+        xp = x.copy(); xp[idx] += h
+        xm = x.copy(); xm[idx] -= h
+        out[idx] = (f(xp) - f(xm)) / (2 * h)
+    return out
+
+
+def test_p16_dim_grad_matches_finite_differences():
+    rng = np.random.default_rng(1600)
+    N, d, dv = 9, 4, 3
+    q = rng.normal(size=(N, d)) * 1.5
+    k = rng.normal(size=(N, d)) * 1.5
+    v = rng.normal(size=(N, dv))
+    dy = rng.normal(size=(N, dv))
+    a, b, C = _rand_dim(rng, d, skew=0.7)
+    dq, dk, dvv, da, db, dC = O.causal_attention_dim_grad(q, k, v, a, b, C, dy)
+    loss = lambda q_, k_, v_, a_, b_, C_: float(np.sum(dy * O.causal_attention_dim(q_, k_, v_, a_, b_, C_)))
+    np.testing.assert_allclose(dq, _fd(lambda x: loss(x, k, v, a, b, C), q), rtol=1e-6, atol=1e-8)
+    np.testing.assert_allclose(dk, _fd(lambda x: loss(q, x, v, a, b, C), k), rtol=1e-6, atol=1e-8)
+    np.testing.assert_allclose(dvv, _fd(lambda x: loss(q, k, x, a, b, C), v), rtol=1e-6, atol=1e-8)
+    np.testing.assert_allclose(da, _fd(lambda x: loss(q, k, v, float(x), b, C), np.array(a)), rtol=1e-6, atol=1e-8)
+    np.testing.assert_allclose(db, _fd(lambda x: loss(q, k, v, a, x, C), b), rtol=1e-6, atol=1e-8)
+    np.testing.assert_allclose(dC, _fd(lambda x: loss(q, k, v, a, b, x), C), rtol=1e-6, atol=1e-8)
+    assert np.allclose(dC, dC.T)
+
+
+@pytest.mark.parametrize("G", [1, 3])
+def test_p16_grouped_L_grad_matches_finite_differences(G):
+    rng = np.random.default_rng(1610 + G)
+    N, d = 8, 8
+    q = rng.normal(size=(N, d)) * 1.5
+    k = rng.normal(size=(N, d)) * 1.5
+    v = rng.normal(size=(N, 5))
+    dy = rng.normal(size=(N, 5))
+    L = _rand_L(rng, G)
+    g = _rand_groups(rng, d, G)
+    eps = 1e-3
+    a, b, C = O.expand_coeffs(L, g, G, eps)
+    _, _, _, da, db, dC = O.causal_attention_dim_grad(q, k, v, a, b, C, dy)
+    dL = O.grouped_coeff_grad(L, g, G, da, db, dC)
+    fd = _fd(lambda x: float(np.sum(dy * O.causal_attention(q, k, v, x, g, G, eps))), L)
+    fd = np.tril(fd)          # entries above the diagonal do not enter (the oracle ignores them)
+    np.testing.assert_allclose(dL, fd, rtol=1e-6, atol=1e-8)
