@@ -187,6 +187,52 @@ oal_status oal_decode_step(int batch, int n_q_heads, int n_kv_heads, int d_h, in
                            const void* coeffs, oal_state* state, void* y, oal_dtype out_dtype,
                            hipStream_t stream);
 
+/* Device workspace oal_prefill_backward needs: the per-chunk prefix and suffix
+ * states (2 x batch x n_kv_heads x ceil(seq_len/chunk) x 565,760 B), the rows
+ * g_i and alpha_ij of every chunk, and the per-chunk coefficient sums.  chunk 0
+ * selects 128; returns 0 for unsupported arguments or seq_len == 0. */
+size_t oal_prefill_backward_workspace_bytes(int batch, int n_q_heads, int n_kv_heads, int seq_len,
+                                            int d_h, int d_v, int chunk);
+
+/* Backward of a prefill that starts from an empty state (oal_prefill with a
+ * fresh state, or oal_prefill_dim): for the loss sum_i dy_i . y_i, the gradients
+ * with respect to q, k, v and the kernel's dimension-wise coefficients.  It
+ * differentiates the causal sum of [OAL] Eq. 5-7 (exact, like the forward):
+ * with g_i = [dy_i / den_i ; -(dy_i . y_i) / den_i] and alpha_ij = g_i . [v_j; 1],
+ *   dv_j = sum_{i>=j} kappa_ij dy_i / den_i,   dq_i = sum_{j<=i} alpha_ij d kappa_ij / d q_i,
+ *   dk_j = sum_{i>=j} alpha_ij d kappa_ij / d k_j,  and for [OAL] Eq. 3's a, b_r, C_rt:
+ *   da = sum alpha_ij, db_r = sum alpha_ij x_r, dC_rt = sum alpha_ij x_r x_t
+ * (x = q_i o k_j / sqrt(d_h)); sums over i include every query head that shares
+ * the KV head.  Linear in seq_len: the parts outside a row's chunk go through
+ * prefix and suffix states, the chunk itself pair by pair; fp32 on the vector
+ * ALUs.
+ *   q, k, v, coeffs as for oal_prefill (fp32 or bf16 inputs; any record kind)
+ *   dy      device float [batch][n_q_heads][seq_len][d_v]
+ *   chunk   0 (= 128), 64 or 128
+ *   dq      device float out [batch][n_q_heads][seq_len][d_h]
+ *   dk, dv  device float out [batch][n_kv_heads][seq_len][d_h / d_v]
+ *   da, db, dC  device float out [n_q_heads], [n_q_heads][d_h], [n_q_heads][d_h][d_h]
+ *           (dC symmetric, summed over the batch), or all three NULL to skip them
+ *   workspace  >= oal_prefill_backward_workspace_bytes() bytes, 256-byte aligned
+ * seq_len == 0 writes zero coefficient gradients (when requested) and nothing
+ * else.  Allocates nothing. */
+oal_status oal_prefill_backward(int batch, int n_q_heads, int n_kv_heads, int seq_len, int d_h,
+                                int d_v, oal_dtype in_dtype, const void* q, const void* k,
+                                const void* v, const void* coeffs, const float* dy, int chunk,
+                                float* dq, float* dk, float* dv, float* da, float* db, float* dC,
+                                void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Gradient with respect to L of the grouped kernel ([OAL] §4.3, M = L L^T,
+ * a = eps + M_00, b_r = 2 M_{0,g(r)}, C_rt = M_{g(r),g(t)}) from the gradients
+ * (da, db, dC) with respect to the dimension-wise coefficients: dM_00 = da,
+ * dM_{0,g} = dM_{g,0} = sum_{r in g} db_r, dM_{g,h} = sum_{r in g, t in h} dC_rt,
+ * dL = (dM + dM^T) L.  Same n_groups / group_map / L conventions (and clamping)
+ * as oal_expand_coeffs; dL [n_q_heads][g_max+1][g_max+1] holds the lower
+ * triangle of the leading (G_h+1) block and zero elsewhere. */
+oal_status oal_coeffs_backward(int n_q_heads, int d_h, int g_max, const int32_t* n_groups,
+                               const int32_t* group_map, const float* L, const float* da,
+                               const float* db, const float* dC, float* dL, hipStream_t stream);
+
 /* Exact causal softmax attention, the reference OAL approximates ([OAL] §3:
  * y_i = sum_{j<=i} exp(s_ij) v_j / sum_{j<=i} exp(s_ij), s_ij = q_i . k_j / sqrt(d_h),
  * query head h reading KV head h / (n_q_heads / n_kv_heads)); used for the

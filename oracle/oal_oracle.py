@@ -232,7 +232,7 @@ def causal_attention_dim(q, k, v, a, b, C):
     return causal_attention_dim_rows(q, np.arange(q.shape[0]), k, v, a, b, C)
 
 
-def causal_attention_dim_grad(q, k, v, a, b, C, dy):
+def causal_attention_dim_grad(q, k, v, a, b, C, dy, rows=None):
     """Gradients of the causal attention of :func:`causal_attention_dim` (the
     dimension-specific kernel of [OAL] Eq. 3) for the loss sum_i dy_i . y_i, by
     differentiating the direct sum term by term (the chain rule written out).
@@ -246,7 +246,11 @@ def causal_attention_dim_grad(q, k, v, a, b, C, dy):
       dq_i = sum_{j<=i} alpha_ij k_j o w_ij / sqrt(d_h)
       dk_j = sum_{i>=j} alpha_ij q_i o w_ij / sqrt(d_h)
       da = sum alpha_ij,  db = sum alpha_ij x_ij,  dC = sum alpha_ij x_ij x_ij^T.
-    Returns (dq, dk, dv, da, db, dC); dC is symmetric (only sym(C) enters kappa)."""
+    Returns (dq, dk, dv, da, db, dC); dC is symmetric (only sym(C) enters kappa).
+
+    ``rows`` restricts the loss to those query rows (dy of the other rows taken
+    as zero): then dq is exact on those rows, and dk_j, dv_j are exact for every
+    key j whose rows i >= j are all included."""
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
@@ -264,9 +268,9 @@ def causal_attention_dim_grad(q, k, v, a, b, C, dy):
     da = 0.0
     db = np.zeros(d_h)
     dC = np.zeros((d_h, d_h))
-    for i in range(N):
+    for i in (range(N) if rows is None else sorted(set(int(r) for r in rows))):
         x = q[i][None, :] * k[: i + 1] / sq                       # [i+1, d_h]
-        kap = a + x @ b + np.einsum("jr,rt,jt->j", x, C, x)
+        kap = a + x @ b + ((x @ C) * x).sum(axis=1)              # x_j^T C x_j per key
         ut = kap @ u[: i + 1]
         den = ut[d_v]
         y = ut[:d_v] / den

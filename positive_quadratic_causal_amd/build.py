@@ -27,6 +27,7 @@ SOURCES = [
     "oal_prefill_mfma.hip",
     "oal_state_mfma.hip",
     "oal_softmax.hip",
+    "oal_backward.hip",
 ]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")

@@ -95,6 +95,14 @@ void prof_end(int slot, hipStream_t stream) {
 }
 
 // kernels' launchers (one per source file)
+size_t backward_workspace(int batch, int n_q_heads, int n_kv_heads, int seq_len, int chunk);
+oal_status launch_backward(int batch, int n_q_heads, int n_kv_heads, int seq_len, int chunk,
+                           oal_dtype in_dtype, const void* q, const void* k, const void* v,
+                           const void* coeffs, const float* dy, float* dq, float* dk, float* dv,
+                           float* da, float* db, float* dC, void* ws, hipStream_t stream);
+oal_status launch_coeffs_backward(int n_q_heads, int g_max, const int32_t* n_groups,
+                                  const int32_t* group_map, const float* L, const float* da,
+                                  const float* db, const float* dC, float* dL, hipStream_t stream);
 oal_status launch_dim_coeffs(int n_q_heads, const float* a, const float* b, const float* C,
                              void* coeffs, hipStream_t stream);
 oal_status launch_expand(int n_q_heads, int g_max, const int32_t* n_groups,
@@ -365,6 +373,62 @@ oal_status oal_prefill_dim(int batch, int n_q_heads, int n_kv_heads, int seq_len
                           state ? state->data : nullptr, y, out_dtype, workspace, true, stream);
   if (st == OAL_OK && state) state->tokens += seq_len;
   return st;
+}
+
+size_t oal_prefill_backward_workspace_bytes(int batch, int n_q_heads, int n_kv_heads, int seq_len,
+                                            int d_h, int d_v, int chunk) {
+  if (check_heads(batch, n_q_heads, n_kv_heads, d_h, d_v) != OAL_OK) return 0;
+  chunk = resolve_chunk(chunk);
+  if (seq_len <= 0 || (chunk != 64 && chunk != 128)) return 0;
+  return backward_workspace(batch, n_q_heads, n_kv_heads, seq_len, chunk);
+}
+
+oal_status oal_prefill_backward(int batch, int n_q_heads, int n_kv_heads, int seq_len, int d_h,
+                                int d_v, oal_dtype in_dtype, const void* q, const void* k,
+                                const void* v, const void* coeffs, const float* dy, int chunk,
+                                float* dq, float* dk, float* dv, float* da, float* db, float* dC,
+                                void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  oal_status st = check_heads(batch, n_q_heads, n_kv_heads, d_h, d_v);
+  if (st != OAL_OK) return st;
+  if (!valid_dtype(in_dtype)) return set_error(OAL_ERR_INVALID_ARG, "unknown dtype");
+  if (seq_len < 0) return set_error(OAL_ERR_INVALID_ARG, "seq_len must be >= 0 (got %d)", seq_len);
+  chunk = resolve_chunk(chunk);
+  if (chunk != 64 && chunk != 128)
+    return set_error(OAL_ERR_INVALID_ARG, "backward chunk must be 0, 64 or 128 (got %d)", chunk);
+  const int n_coef = (da != nullptr) + (db != nullptr) + (dC != nullptr);
+  if (n_coef != 0 && n_coef != 3)
+    return set_error(OAL_ERR_INVALID_ARG, "da, db and dC must be all given or all null");
+  if (seq_len == 0) {
+    if (n_coef == 0) return OAL_OK;
+    st = launch_fill_zero(da, (size_t)n_q_heads, stream);
+    if (st == OAL_OK) st = launch_fill_zero(db, (size_t)n_q_heads * DH, stream);
+    if (st == OAL_OK) st = launch_fill_zero(dC, (size_t)n_q_heads * DH * DH, stream);
+    return st;
+  }
+  if (!q || !k || !v || !coeffs || !dy || !dq || !dk || !dv)
+    return set_error(OAL_ERR_INVALID_ARG, "null pointer argument");
+  if ((long long)seq_len * 64 * (long long)batch * n_q_heads > (1LL << 40))
+    return set_error(OAL_ERR_UNSUPPORTED, "problem too large");
+  const size_t need = backward_workspace(batch, n_q_heads, n_kv_heads, seq_len, chunk);
+  if (!workspace || workspace_bytes < need)
+    return set_error(OAL_ERR_INVALID_ARG, "workspace too small: need %zu bytes, got %zu", need,
+                     workspace ? workspace_bytes : (size_t)0);
+  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+    return set_error(OAL_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  return launch_backward(batch, n_q_heads, n_kv_heads, seq_len, chunk, in_dtype, q, k, v, coeffs, dy,
+                         dq, dk, dv, da, db, dC, workspace, stream);
+}
+
+oal_status oal_coeffs_backward(int n_q_heads, int d_h, int g_max, const int32_t* n_groups,
+                               const int32_t* group_map, const float* L, const float* da,
+                               const float* db, const float* dC, float* dL, hipStream_t stream) {
+  if (n_q_heads < 1) return set_error(OAL_ERR_INVALID_ARG, "n_q_heads must be >= 1");
+  if (d_h != DH) return set_error(OAL_ERR_UNSUPPORTED, "only d_h = 64 is supported (got %d)", d_h);
+  if (g_max < 1 || g_max > GMAX)
+    return set_error(OAL_ERR_UNSUPPORTED, "g_max must be in 1..%d (got %d)", GMAX, g_max);
+  if (!n_groups || !group_map || !L || !da || !db || !dC || !dL)
+    return set_error(OAL_ERR_INVALID_ARG, "null pointer argument");
+  return launch_coeffs_backward(n_q_heads, g_max, n_groups, group_map, L, da, db, dC, dL, stream);
 }
 
 oal_status oal_softmax_attention(int batch, int n_q_heads, int n_kv_heads, int seq_len, int d_h,

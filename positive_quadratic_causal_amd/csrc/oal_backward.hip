@@ -1,0 +1,818 @@
+// Backward pass of the causal prefill on the vector ALUs in fp32.
+//
+// The forward of a sequence that starts from an empty state ([OAL] Algorithm 1,
+// Eq. 5-6) is, per query head, u~_i = sum_{j<=i} kappa_ij u_j with u_j = [v_j; 1],
+// kappa_ij = phi_q(q_i) . phi_k(k_j) = sum_f c_f psi_f(q_i) psi_f(k_j), the
+// monomials psi = (1, x_r, x_r x_t (r <= t)) and the record's expanded
+// coefficients c = (a, b'_r, c'_rt), and y_i = u~_i[:64] / u~_i[64].  For a loss
+// with gradient dy_i on y_i:
+//   g_i = [dy_i / den_i ; -(dy_i . y_i) / den_i]   (gradient on u~_i)
+//   alpha_ij = g_i . u_j                            (gradient on kappa_ij)
+//   dq_i = sum_{j<=i} alpha_ij grad_q kappa_ij,  grad_q kappa = k o (b' + 2 S p)
+//   dk_j = sum_h sum_{i>=j} alpha_ij grad_k kappa_ij,  grad_k kappa = q o (b' + 2 S p)
+//   dv_j = sum_h sum_{i>=j} kappa_ij g_i[:64]
+//   dc_f = sum_{i, j<=i} alpha_ij psi_f(q_i) psi_f(k_j)
+// with p = q o k and S the symmetric C / d_h square of the record; the sums over
+// h run over the query heads that share the KV head.  Linear time, chunk by
+// chunk like the forward: the part of a row's sums that lies in earlier chunks
+// goes through the prefix states H_{<c} (dq_i from H_{<c} g_i), the part in later
+// chunks through suffix states R_{>c} = sum_h sum_{i in later chunks}
+// phi_q(q_i) g_i^T (dv_j and dk_j from R_{>c}^T psi(k_j) and R_{>c} u_j), and the
+// chunk itself is summed pair by pair.
+//
+// Kernels, in launch order:
+//   prefix build + scan (oal_prefill_vec.hip)  H_{<c}
+//   k_bwd_query     one thread per query: recompute u~_i, g_i; dq_i; alpha rows
+//   k_bwd_rbuild    per chunk: sum_h c_f psi_f(q_i) g_i^T (suffix deltas) and the
+//                   state part of dc: sum_i psi_f(q_i) (H_{<c} g_i)_f
+//   k_bwd_rscan     exclusive suffix sums over chunks: R_{>c}
+//   k_bwd_key       one thread per key: dv_j, dk_j
+//   k_bwd_dc_intra  pair part of dc: sum_{i, j<=i in the chunk} alpha_ij psi_f(q_i) psi_f(k_j)
+//   k_bwd_dcoef     sum over chunks and batch; (da, db, dC) of [OAL] Eq. 3
+#include "oal_common.h"
+
+namespace oal {
+
+namespace {
+__constant__ PairTable c_bwd_pairs = PairTable();
+constexpr int WP = 68;                 // rows of H, R, u and g padded to 16 bytes
+constexpr int TB = 64;                 // tokens per staged tile
+constexpr int FB = 64;                 // feature rows per build block
+constexpr int NFB = DS / FB;           // 34
+constexpr int WPT = (W + 3) / 4;       // 17 columns per thread in the build
+
+// feature f of the canonical order: kind 0 constant, 1 linear x_r, 2 pair x_r x_t,
+// 3 padding
+__device__ __forceinline__ int feat_decode(int f, int& r, int& t) {
+  r = 0;
+  t = 0;
+  if (f == 0) return 0;
+  if (f <= DH) {
+    r = f - 1;
+    return 1;
+  }
+  if (f < DCAN) {
+    const uint16_t rt = c_bwd_pairs.rt[f - 1 - DH];
+    r = rt >> 8;
+    t = rt & 0xff;
+    return 2;
+  }
+  return 3;
+}
+
+__device__ __forceinline__ float coef_of(const float* rec, int f) {
+  if (f == 0) return rec[OAL_COEF_A];
+  if (f <= DH) return rec[OAL_COEF_BP + f - 1];
+  if (f < DCAN) return rec[OAL_COEF_CP + f - 1 - DH];
+  return 0.f;
+}
+
+// acc += s * row (16-byte aligned LDS row of WP floats)
+__device__ __forceinline__ void axpy_row(float (&acc)[WP], float s, const float* row) {
+  float4 r4[WP / 4];
+#pragma unroll
+  for (int i = 0; i < WP / 4; ++i) r4[i] = reinterpret_cast<const float4*>(row)[i];
+#pragma unroll
+  for (int i = 0; i < WP / 4; ++i) {
+    acc[4 * i + 0] = fmaf(s, r4[i].x, acc[4 * i + 0]);
+    acc[4 * i + 1] = fmaf(s, r4[i].y, acc[4 * i + 1]);
+    acc[4 * i + 2] = fmaf(s, r4[i].z, acc[4 * i + 2]);
+    acc[4 * i + 3] = fmaf(s, r4[i].w, acc[4 * i + 3]);
+  }
+}
+
+// row . x over WP entries (the pads of x are zero)
+__device__ __forceinline__ float dot_row(const float* row, const float (&x)[WP]) {
+  float4 r4[WP / 4];
+#pragma unroll
+  for (int i = 0; i < WP / 4; ++i) r4[i] = reinterpret_cast<const float4*>(row)[i];
+  float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+  for (int i = 0; i < WP / 4; ++i) {
+    s0 = fmaf(r4[i].x, x[4 * i + 0], s0);
+    s1 = fmaf(r4[i].y, x[4 * i + 1], s1);
+    s0 = fmaf(r4[i].z, x[4 * i + 2], s0);
+    s1 = fmaf(r4[i].w, x[4 * i + 3], s1);
+  }
+  return s0 + s1;
+}
+
+// (S p)_r for the 64-float row r of S in LDS (16-byte aligned) and p in registers
+__device__ __forceinline__ float srow_dot(const float* srow, const float (&p)[DH]) {
+  float4 s4[DH / 4];
+#pragma unroll
+  for (int i = 0; i < DH / 4; ++i) s4[i] = reinterpret_cast<const float4*>(srow)[i];
+  float sa = 0.f, sb = 0.f;
+#pragma unroll
+  for (int i = 0; i < DH / 4; ++i) {
+    sa = fmaf(s4[i].x, p[4 * i + 0], sa);
+    sb = fmaf(s4[i].y, p[4 * i + 1], sb);
+    sa = fmaf(s4[i].z, p[4 * i + 2], sa);
+    sb = fmaf(s4[i].w, p[4 * i + 3], sb);
+  }
+  return sa + sb;
+}
+
+// kappa of one pair from a query row and a key row in LDS: a + sum_r p_r (b'_r + (S p)_r)
+// (p_r of the rolled r loop is re-read from LDS: a register array indexed by it
+// would live in scratch)
+__device__ __forceinline__ float kappa_pair(float a, const float* qi, const float* kj,
+                                            const float* s_b, const float* s_S) {
+  float p[DH];
+#pragma unroll
+  for (int t = 0; t < DH; ++t) p[t] = qi[t] * kj[t];
+  float kap = a;
+#pragma unroll 1
+  for (int r = 0; r < DH; ++r) kap = fmaf(s_b[r] + srow_dot(s_S + r * DH, p), qi[r] * kj[r], kap);
+  return kap;
+}
+
+size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
+}  // namespace
+
+// Workspace regions of the backward (each 256-byte aligned).
+struct BwdWs {
+  float* hc;      // [units][n_chunks][STATE_FLOATS]  H_{<c}
+  float* rc;      // [units][n_chunks][STATE_FLOATS]  suffix deltas, then R_{>c}
+  float* gbuf;    // [batch][Hq][n_chunks * chunk][WP] g rows (zero beyond seq_len)
+  float* alpha;   // [batch][Hq][n_chunks][chunk][chunk] alpha_ij (zero for j > i)
+  float* dcp;     // [batch][Hq][n_chunks][DS] per-chunk parts of dc
+  size_t bytes;
+};
+
+static BwdWs bwd_ws(void* base, int batch, int n_q_heads, int n_kv_heads, int seq_len, int chunk) {
+  const size_t units = (size_t)batch * n_kv_heads;
+  const size_t nc = (size_t)((seq_len + chunk - 1) / chunk);
+  const size_t bh = (size_t)batch * n_q_heads;
+  size_t off = 0;
+  auto take = [&](size_t floats) {
+    const size_t at = off;
+    off += al256(floats * sizeof(float));
+    return at;
+  };
+  const size_t o_h = take(units * nc * STATE_FLOATS);
+  const size_t o_r = take(units * nc * STATE_FLOATS);
+  const size_t o_g = take(bh * nc * chunk * WP);
+  const size_t o_a = take(bh * nc * chunk * chunk);
+  const size_t o_d = take(bh * nc * DS);
+  BwdWs w;
+  uint8_t* p = reinterpret_cast<uint8_t*>(base);
+  w.hc = reinterpret_cast<float*>(p + o_h);
+  w.rc = reinterpret_cast<float*>(p + o_r);
+  w.gbuf = reinterpret_cast<float*>(p + o_g);
+  w.alpha = reinterpret_cast<float*>(p + o_a);
+  w.dcp = reinterpret_cast<float*>(p + o_d);
+  w.bytes = off;
+  return w;
+}
+
+size_t backward_workspace(int batch, int n_q_heads, int n_kv_heads, int seq_len, int chunk) {
+  return bwd_ws(nullptr, batch, n_q_heads, n_kv_heads, seq_len, chunk).bytes;
+}
+
+// ---------------------------------------------------------------------------
+// Query side.  One block per (chunk, query head, batch), thread i = query t0 + i.
+template <typename T>
+__global__ void __launch_bounds__(128)
+k_bwd_query(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunks,
+            const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+            const void* __restrict__ coeffs, const float* __restrict__ dy,
+            const float* __restrict__ hc, float* __restrict__ gbuf, float* __restrict__ alpha,
+            float* __restrict__ dq) {
+  const int c = blockIdx.x;
+  const int hq = blockIdx.y;
+  const int b = blockIdx.z;
+  const int rep = n_q_heads / n_kv_heads;
+  const int unit = b * n_kv_heads + hq / rep;
+  const int tid = threadIdx.x;
+  const int t0 = c * chunk;
+  const int clen = min(chunk, seq_len - t0);
+  const bool active = tid < clen;
+
+  extern __shared__ float smem[];
+  float* s_q = smem;                          // [chunk][DH + 1]
+  float* s_dq = s_q + chunk * (DH + 1);       // [chunk][DH + 1]
+  float* s_H = s_dq + chunk * (DH + 1);       // [32][WP]
+  float* s_cf = s_H + 32 * WP;                // [32]
+  float* s_k = s_cf + 32;                     // [TB][DH + 1]
+  float* s_u = s_k + TB * (DH + 1);           // [TB][WP]
+  float* s_b = s_u + TB * WP;                 // [DH]  b'
+  float* s_S = s_b + DH;                      // [DH][DH]  C / d_h (symmetric)
+
+  const float* rec = coef_rec(coeffs, hq);
+  const float a = rec[OAL_COEF_A];
+  const size_t qrow0 = ((size_t)b * n_q_heads + hq) * seq_len + t0;
+  for (int i = tid; i < chunk * DH; i += blockDim.x) {
+    const int ii = i / DH, d = i % DH;
+    s_q[ii * (DH + 1) + d] = ii < clen ? Elem<T>::load(q, (qrow0 + ii) * DH + d) : 0.f;
+    s_dq[ii * (DH + 1) + d] = 0.f;
+  }
+  for (int i = tid; i < DH; i += blockDim.x) s_b[i] = rec[OAL_COEF_BP + i];
+  for (int i = tid; i < DH * DH; i += blockDim.x) s_S[i] = rec[OAL_COEF_CM + i];
+  for (int i = tid; i < 32 * (WP - W); i += blockDim.x) s_H[(i / (WP - W)) * WP + W + i % (WP - W)] = 0.f;
+  for (int i = tid; i < TB * (WP - W); i += blockDim.x) s_u[(i / (WP - W)) * WP + W + i % (WP - W)] = 0.f;
+  __syncthreads();
+  const float* qi = s_q + tid * (DH + 1);
+  float* dqi = s_dq + tid * (DH + 1);
+  const float* Hc = hc + ((size_t)unit * n_chunks + c) * STATE_FLOATS;
+  const size_t kbase = (size_t)unit * seq_len + t0;
+
+  auto stage_block = [&](int f0) {
+    for (int i = tid; i < 32 * W; i += blockDim.x) {
+      const int w = i / 32, ff = i % 32;
+      s_H[ff * WP + w] = Hc[(size_t)w * DS + f0 + ff];   // f0 + 31 < DS always
+    }
+    if (tid < 32) s_cf[tid] = coef_of(rec, f0 + tid);
+  };
+  auto stage_keys = [&](int j0, int nj) {
+    for (int i = tid; i < TB * DH; i += blockDim.x) {
+      const int jj = i / DH, d = i % DH;
+      float kv_ = 0.f, vv_ = 0.f;
+      if (jj < nj) {
+        kv_ = Elem<T>::load(k, (kbase + j0 + jj) * DH + d);
+        vv_ = Elem<T>::load(v, (kbase + j0 + jj) * DV + d);
+      }
+      s_k[jj * (DH + 1) + d] = kv_;
+      s_u[jj * WP + d] = vv_;
+    }
+    for (int jj = tid; jj < TB; jj += blockDim.x) s_u[jj * WP + DV] = jj < nj ? 1.f : 0.f;
+  };
+
+  // ---- 1. recompute u~_i: state part, then the pairs of the chunk
+  float acc[WP];
+#pragma unroll
+  for (int w = 0; w < WP; ++w) acc[w] = 0.f;
+  for (int f0 = 0; f0 < DCAN; f0 += 32) {
+    __syncthreads();
+    stage_block(f0);
+    __syncthreads();
+    if (active) {
+      const int nf = min(32, DCAN - f0);
+      for (int ff = 0; ff < nf; ++ff) {
+        int r, t;
+        const int kind = feat_decode(f0 + ff, r, t);
+        const float psi = kind == 0 ? 1.f : kind == 1 ? qi[r] : qi[r] * qi[t];
+        axpy_row(acc, s_cf[ff] * psi, s_H + ff * WP);
+      }
+    }
+  }
+  for (int j0 = 0; j0 < clen; j0 += TB) {
+    const int nj = min(TB, clen - j0);
+    __syncthreads();
+    stage_keys(j0, nj);
+    __syncthreads();
+    if (active) {
+      const int jmax = min(nj, tid - j0 + 1);
+      for (int jj = 0; jj < jmax; ++jj)
+        axpy_row(acc, kappa_pair(a, qi, s_k + jj * (DH + 1), s_b, s_S), s_u + jj * WP);
+    }
+  }
+
+  // ---- 2. g_i (zero for rows beyond the sequence)
+  float g[WP];
+#pragma unroll
+  for (int w = 0; w < WP; ++w) g[w] = 0.f;
+  if (active) {
+    const float inv = 1.0f / acc[DV];
+    const float* dyi = dy + (qrow0 + tid) * DV;
+    float ydot = 0.f;
+#pragma unroll
+    for (int w = 0; w < DV; ++w) {
+      const float d = dyi[w];
+      g[w] = d * inv;
+      ydot = fmaf(d, acc[w] * inv, ydot);
+    }
+    g[DV] = -ydot * inv;
+  }
+  {
+    float* gr = gbuf + (((size_t)b * n_q_heads + hq) * ((size_t)n_chunks * chunk) + t0 + tid) * WP;
+#pragma unroll
+    for (int i = 0; i < WP / 4; ++i)
+      reinterpret_cast<float4*>(gr)[i] = make_float4(g[4 * i], g[4 * i + 1], g[4 * i + 2], g[4 * i + 3]);
+  }
+
+  // ---- 3. the chunk's pairs: alpha_ij and dq_i += alpha_ij k_j o (b' + 2 S p)
+  float* arow = alpha + ((((size_t)b * n_q_heads + hq) * n_chunks + c) * chunk + tid) * chunk;
+  for (int j0 = 0; j0 < chunk; j0 += TB) {
+    const int nj = max(0, min(TB, clen - j0));
+    __syncthreads();
+    stage_keys(j0, nj);
+    __syncthreads();
+    const int jmax = active ? max(0, min(nj, tid - j0 + 1)) : 0;
+    for (int jj = 0; jj < jmax; ++jj) {
+      const float* kj = s_k + jj * (DH + 1);
+      const float al = dot_row(s_u + jj * WP, g);
+      arow[j0 + jj] = al;
+      float p[DH];
+#pragma unroll
+      for (int t = 0; t < DH; ++t) p[t] = qi[t] * kj[t];
+#pragma unroll 1
+      for (int r = 0; r < DH; ++r)
+        dqi[r] = fmaf(al * kj[r], s_b[r] + 2.f * srow_dot(s_S + r * DH, p), dqi[r]);
+    }
+    for (int jj = jmax; jj < TB; ++jj) arow[j0 + jj] = 0.f;
+  }
+
+  // ---- 4. state part: d_f = H_{<c}[f] . g_i, then the monomials' derivatives
+  for (int f0 = 0; f0 < DCAN; f0 += 32) {
+    __syncthreads();
+    stage_block(f0);
+    __syncthreads();
+    if (active) {
+      const int nf = min(32, DCAN - f0);
+      for (int ff = 0; ff < nf; ++ff) {
+        int r, t;
+        const int kind = feat_decode(f0 + ff, r, t);
+        if (kind == 0) continue;
+        const float cd = s_cf[ff] * dot_row(s_H + ff * WP, g);
+        if (kind == 1) {
+          dqi[r] += cd;
+        } else {
+          dqi[r] = fmaf(cd, qi[t], dqi[r]);
+          dqi[t] = fmaf(cd, qi[r], dqi[t]);
+        }
+      }
+    }
+  }
+  if (active) {
+    float* o = dq + (qrow0 + tid) * DH;
+#pragma unroll
+    for (int d = 0; d < DH; ++d) o[d] = dqi[d];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Suffix deltas and the state part of dc.  Block (feature block, chunk, unit);
+// thread: feature f = 64 fb + (tid & 63), columns w = (tid >> 6) + 4 j.
+template <typename T>
+__global__ void __launch_bounds__(256)
+k_bwd_rbuild(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunks,
+             const T* __restrict__ q, const void* __restrict__ coeffs,
+             const float* __restrict__ gbuf, const float* __restrict__ hc,
+             float* __restrict__ rc, float* __restrict__ dcp) {
+  const int fb = blockIdx.x;
+  const int c = blockIdx.y;
+  const int unit = blockIdx.z;
+  const int b = unit / n_kv_heads, kv = unit % n_kv_heads;
+  const int rep = n_q_heads / n_kv_heads;
+  const int tid = threadIdx.x;
+  const int f = fb * FB + (tid & 63);
+  const int wq = tid >> 6;
+  __shared__ float s_q[TB][DH + 1];
+  __shared__ float s_g[TB][WP];
+  __shared__ float s_red[4][FB];
+  int r, t;
+  const int kind = feat_decode(f, r, t);
+  const size_t slot = ((size_t)unit * n_chunks + c) * STATE_FLOATS;
+  float hval[WPT], rd[WPT];
+#pragma unroll
+  for (int j = 0; j < WPT; ++j) {
+    const int w = wq + 4 * j;
+    hval[j] = w < W ? hc[slot + (size_t)w * DS + f] : 0.f;
+    rd[j] = 0.f;
+  }
+  const int t0 = c * chunk;
+  const int t1 = min(seq_len, t0 + chunk);
+  const size_t npad = (size_t)n_chunks * chunk;
+  for (int hh = 0; hh < rep; ++hh) {
+    const int hq = kv * rep + hh;
+    const float cf = coef_of(coef_rec(coeffs, hq), f);
+    float acc[WPT];
+#pragma unroll
+    for (int j = 0; j < WPT; ++j) acc[j] = 0.f;
+    const size_t qrow0 = ((size_t)b * n_q_heads + hq) * seq_len;
+    const size_t grow0 = ((size_t)b * n_q_heads + hq) * npad;
+    for (int i0 = t0; i0 < t1; i0 += TB) {
+      const int ni = min(TB, t1 - i0);
+      __syncthreads();
+      for (int i = tid; i < TB * DH; i += blockDim.x) {
+        const int ii = i / DH, d = i % DH;
+        s_q[ii][d] = ii < ni ? Elem<T>::load(q, (qrow0 + i0 + ii) * DH + d) : 0.f;
+      }
+      for (int i = tid; i < TB * WP; i += blockDim.x) {
+        const int ii = i / WP, w = i % WP;
+        s_g[ii][w] = ii < ni ? gbuf[(grow0 + i0 + ii) * WP + w] : 0.f;
+      }
+      __syncthreads();
+      for (int ii = 0; ii < ni; ++ii) {
+        const float psi = kind == 0 ? 1.f : kind == 1 ? s_q[ii][r] : kind == 2 ? s_q[ii][r] * s_q[ii][t] : 0.f;
+#pragma unroll
+        for (int j = 0; j < WPT; ++j) {
+          const int w = wq + 4 * j;
+          if (w < W) acc[j] = fmaf(psi, s_g[ii][w], acc[j]);
+        }
+      }
+    }
+    float part = 0.f;
+#pragma unroll
+    for (int j = 0; j < WPT; ++j) {
+      rd[j] = fmaf(cf, acc[j], rd[j]);
+      part = fmaf(hval[j], acc[j], part);
+    }
+    if (dcp != nullptr) {
+      s_red[wq][tid & 63] = part;
+      __syncthreads();
+      if (wq == 0)
+        dcp[(((size_t)b * n_q_heads + hq) * n_chunks + c) * DS + f] =
+            kind == 3 ? 0.f : s_red[0][tid] + s_red[1][tid] + s_red[2][tid] + s_red[3][tid];
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < WPT; ++j) {
+    const int w = wq + 4 * j;
+    if (w < W) rc[slot + (size_t)w * DS + f] = rd[j];
+  }
+}
+
+// Exclusive suffix sums over the chunks of every unit, in place.
+__global__ void __launch_bounds__(256)
+k_bwd_rscan(int n_chunks, float* __restrict__ rc) {
+  const int unit = blockIdx.y;
+  const size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= STATE_FLOATS) return;
+  float* p = rc + (size_t)unit * n_chunks * STATE_FLOATS + e;
+  float run = 0.f;
+  for (int c = n_chunks - 1; c >= 0; --c) {
+    const float x = p[(size_t)c * STATE_FLOATS];
+    p[(size_t)c * STATE_FLOATS] = run;
+    run += x;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Key side.  One block per (chunk, unit), thread j = key t0 + j.
+template <typename T>
+__global__ void __launch_bounds__(128)
+k_bwd_key(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunks,
+          const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+          const void* __restrict__ coeffs, const float* __restrict__ gbuf,
+          const float* __restrict__ rc, float* __restrict__ dk, float* __restrict__ dv) {
+  const int c = blockIdx.x;
+  const int unit = blockIdx.y;
+  const int b = unit / n_kv_heads, kv = unit % n_kv_heads;
+  const int rep = n_q_heads / n_kv_heads;
+  const int tid = threadIdx.x;
+  const int t0 = c * chunk;
+  const int clen = min(chunk, seq_len - t0);
+  const bool active = tid < clen;
+
+  extern __shared__ float smem[];
+  float* s_k = smem;                          // [chunk][DH + 1]
+  float* s_dk = s_k + chunk * (DH + 1);       // [chunk][DH + 1]
+  float* s_R = s_dk + chunk * (DH + 1);       // [32][WP]
+  float* s_q = s_R + 32 * WP;                 // [TB][DH + 1]
+  float* s_g = s_q + TB * (DH + 1);           // [TB][WP]
+  float* s_b = s_g + TB * WP;                 // [DH]
+  float* s_S = s_b + DH;                      // [DH][DH]
+
+  const size_t krow0 = (size_t)unit * seq_len + t0;
+  for (int i = tid; i < chunk * DH; i += blockDim.x) {
+    const int jj = i / DH, d = i % DH;
+    s_k[jj * (DH + 1) + d] = jj < clen ? Elem<T>::load(k, (krow0 + jj) * DH + d) : 0.f;
+    s_dk[jj * (DH + 1) + d] = 0.f;
+  }
+  for (int i = tid; i < 32 * (WP - W); i += blockDim.x) s_R[(i / (WP - W)) * WP + W + i % (WP - W)] = 0.f;
+  float uj[WP];
+#pragma unroll
+  for (int w = 0; w < WP; ++w) uj[w] = 0.f;
+  if (active) {
+#pragma unroll
+    for (int w = 0; w < DV; ++w) uj[w] = Elem<T>::load(v, (krow0 + tid) * DV + w);
+    uj[DV] = 1.f;
+  }
+  __syncthreads();
+  const float* kj = s_k + tid * (DH + 1);
+  float* dkj = s_dk + tid * (DH + 1);
+  float du[WP];
+#pragma unroll
+  for (int w = 0; w < WP; ++w) du[w] = 0.f;
+
+  // ---- later chunks, through R_{>c}: du_j = R^T psi(k_j), d psi(k_j) = R u_j
+  const float* Rs = rc + ((size_t)unit * n_chunks + c) * STATE_FLOATS;
+  for (int f0 = 0; f0 < DCAN; f0 += 32) {
+    __syncthreads();
+    for (int i = tid; i < 32 * W; i += blockDim.x) {
+      const int w = i / 32, ff = i % 32;
+      s_R[ff * WP + w] = Rs[(size_t)w * DS + f0 + ff];
+    }
+    __syncthreads();
+    if (active) {
+      const int nf = min(32, DCAN - f0);
+      for (int ff = 0; ff < nf; ++ff) {
+        int r, t;
+        const int kind = feat_decode(f0 + ff, r, t);
+        const float* row = s_R + ff * WP;
+        const float psi = kind == 0 ? 1.f : kind == 1 ? kj[r] : kj[r] * kj[t];
+        axpy_row(du, psi, row);
+        if (kind == 0) continue;
+        const float e = dot_row(row, uj);
+        if (kind == 1) {
+          dkj[r] += e;
+        } else {
+          dkj[r] = fmaf(e, kj[t], dkj[r]);
+          dkj[t] = fmaf(e, kj[r], dkj[t]);
+        }
+      }
+    }
+  }
+
+  // ---- the chunk's pairs (i >= j), every query head of the group
+  const size_t npad = (size_t)n_chunks * chunk;
+  for (int hh = 0; hh < rep; ++hh) {
+    const int hq = kv * rep + hh;
+    const float* rec = coef_rec(coeffs, hq);
+    const float a = rec[OAL_COEF_A];
+    const size_t qrow0 = ((size_t)b * n_q_heads + hq) * seq_len;
+    const size_t grow0 = ((size_t)b * n_q_heads + hq) * npad;
+    __syncthreads();
+    for (int i = tid; i < DH; i += blockDim.x) s_b[i] = rec[OAL_COEF_BP + i];
+    for (int i = tid; i < DH * DH; i += blockDim.x) s_S[i] = rec[OAL_COEF_CM + i];
+    for (int i0 = 0; i0 < clen; i0 += TB) {
+      const int ni = min(TB, clen - i0);
+      __syncthreads();
+      for (int i = tid; i < TB * DH; i += blockDim.x) {
+        const int ii = i / DH, d = i % DH;
+        s_q[ii * (DH + 1) + d] = ii < ni ? Elem<T>::load(q, (qrow0 + t0 + i0 + ii) * DH + d) : 0.f;
+      }
+      for (int i = tid; i < TB * WP; i += blockDim.x) {
+        const int ii = i / WP, w = i % WP;
+        s_g[ii * WP + w] = ii < ni ? gbuf[(grow0 + t0 + i0 + ii) * WP + w] : 0.f;
+      }
+      __syncthreads();
+      if (active) {
+        for (int ii = max(0, tid - i0); ii < ni; ++ii) {
+          const float* qi = s_q + ii * (DH + 1);
+          const float* gi = s_g + ii * WP;
+          const float al = dot_row(gi, uj);
+          float p[DH];
+#pragma unroll
+          for (int t = 0; t < DH; ++t) p[t] = qi[t] * kj[t];
+          float kap = a;
+#pragma unroll 1
+          for (int r = 0; r < DH; ++r) {
+            const float sp = srow_dot(s_S + r * DH, p);
+            kap = fmaf(s_b[r] + sp, qi[r] * kj[r], kap);   // p_r from LDS: r is not unrolled
+            dkj[r] = fmaf(al * qi[r], s_b[r] + 2.f * sp, dkj[r]);
+          }
+          axpy_row(du, kap, gi);
+        }
+      }
+    }
+  }
+  if (active) {
+    float* ov = dv + (krow0 + tid) * DV;
+    float* ok = dk + (krow0 + tid) * DH;
+#pragma unroll
+    for (int w = 0; w < DV; ++w) ov[w] = du[w];
+#pragma unroll
+    for (int d = 0; d < DH; ++d) ok[d] = dkj[d];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Pair part of dc: block (feature block of 256, chunk, batch x query head);
+// thread f holds psi_f(k_j) for the chunk's keys in registers.
+template <typename T, int CH>
+__global__ void __launch_bounds__(256)
+k_bwd_dc_intra(int n_q_heads, int n_kv_heads, int seq_len, int n_chunks,
+               const T* __restrict__ q, const T* __restrict__ k, const float* __restrict__ alpha,
+               float* __restrict__ dcp) {
+  const int f = blockIdx.x * 256 + threadIdx.x;
+  const int c = blockIdx.y;
+  const int bh = blockIdx.z;
+  const int b = bh / n_q_heads, hq = bh % n_q_heads;
+  const int unit = b * n_kv_heads + hq / (n_q_heads / n_kv_heads);
+  const int t0 = c * CH;
+  const int clen = min(CH, seq_len - t0);
+  extern __shared__ float smem[];
+  float* s_a = smem;                          // [CH][CH]
+  float* s_q = s_a + CH * CH;                 // [CH][DH + 1]
+  float* s_k = s_q + CH * (DH + 1);           // [CH][DH + 1]
+  const float* ablk = alpha + ((size_t)bh * n_chunks + c) * CH * CH;
+  for (int i = threadIdx.x; i < CH * CH / 4; i += blockDim.x)
+    reinterpret_cast<float4*>(s_a)[i] = reinterpret_cast<const float4*>(ablk)[i];
+  const size_t qrow0 = (size_t)bh * seq_len + t0;
+  const size_t krow0 = (size_t)unit * seq_len + t0;
+  for (int i = threadIdx.x; i < CH * DH; i += blockDim.x) {
+    const int ii = i / DH, d = i % DH;
+    s_q[ii * (DH + 1) + d] = ii < clen ? Elem<T>::load(q, (qrow0 + ii) * DH + d) : 0.f;
+    s_k[ii * (DH + 1) + d] = ii < clen ? Elem<T>::load(k, (krow0 + ii) * DH + d) : 0.f;
+  }
+  __syncthreads();
+  if (f >= DCAN) return;
+  int r, t;
+  const int kind = feat_decode(f, r, t);
+  float kf[CH];
+#pragma unroll
+  for (int j = 0; j < CH; ++j) {
+    const float* kr = s_k + j * (DH + 1);
+    kf[j] = kind == 0 ? 1.f : kind == 1 ? kr[r] : kr[r] * kr[t];
+  }
+  float acc = 0.f;
+  for (int i = 0; i < clen; ++i) {
+    const float* qr = s_q + i * (DH + 1);
+    const float qf = kind == 0 ? 1.f : kind == 1 ? qr[r] : qr[r] * qr[t];
+    const float4* ar = reinterpret_cast<const float4*>(s_a + i * CH);
+    float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+    for (int j4 = 0; j4 < CH / 4; ++j4) {
+      const float4 av = ar[j4];
+      s0 = fmaf(av.x, kf[4 * j4 + 0], s0);
+      s1 = fmaf(av.y, kf[4 * j4 + 1], s1);
+      s0 = fmaf(av.z, kf[4 * j4 + 2], s0);
+      s1 = fmaf(av.w, kf[4 * j4 + 3], s1);
+    }
+    acc = fmaf(qf, s0 + s1, acc);
+  }
+  dcp[((size_t)bh * n_chunks + c) * DS + f] += acc;
+}
+
+// Sum over chunks and batch, then (da, db, dC) of [OAL] Eq. 3: the record's
+// b' = b / sqrt(d_h) and c' = m C / d_h give db_r = dc_r / sqrt(d_h) and, for
+// either entry of the pair, dC_rt = dc_rt / d_h.
+__global__ void __launch_bounds__(256)
+k_bwd_dcoef(int batch, int n_q_heads, int n_chunks, const float* __restrict__ dcp,
+            float* __restrict__ da, float* __restrict__ db, float* __restrict__ dC) {
+  const int f = blockIdx.x * 256 + threadIdx.x;
+  const int hq = blockIdx.y;
+  if (f >= DCAN) return;
+  float s = 0.f;
+  for (int b = 0; b < batch; ++b) {
+    const float* p = dcp + ((size_t)b * n_q_heads + hq) * n_chunks * DS + f;
+    for (int c = 0; c < n_chunks; ++c) s += p[(size_t)c * DS];
+  }
+  int r, t;
+  const int kind = feat_decode(f, r, t);
+  if (kind == 0) {
+    da[hq] = s;
+  } else if (kind == 1) {
+    db[(size_t)hq * DH + r] = s * 0.125f;
+  } else {
+    const float x = s * (1.0f / 64.0f);
+    dC[(size_t)hq * DH * DH + r * DH + t] = x;
+    dC[(size_t)hq * DH * DH + t * DH + r] = x;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// (da, db, dC) -> dL through the grouped map of [OAL] §4.3: in the group sums the
+// kernel is eps + sum_uv M_uv s_u s_v, so dM_00 = da, dM_{0,g} = dM_{g,0} =
+// sum_{r in g} db_r, dM_{g,h} = sum_{r in g, t in h} dC_rt, and with M = L L^T,
+// dL = (dM + dM^T) L on the lower triangle of the leading (G+1) block.
+__global__ void __launch_bounds__(64)
+k_coeffs_bwd(int g_max, const int32_t* __restrict__ n_groups, const int32_t* __restrict__ group_map,
+             const float* __restrict__ Lin, const float* __restrict__ da,
+             const float* __restrict__ db, const float* __restrict__ dC, float* __restrict__ dL) {
+  const int h = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int ld = g_max + 1;
+  __shared__ int sg[DH];
+  __shared__ float sL[LDIM][LDIM];
+  __shared__ double sM[LDIM][LDIM];
+  __shared__ int sG;
+  if (tid == 0) {
+    const int G = n_groups[h];
+    sG = G < 1 ? 1 : (G > g_max ? g_max : G);
+  }
+  __syncthreads();
+  const int G = sG;
+  {
+    const int gr = group_map[(size_t)h * DH + tid];
+    sg[tid] = gr < 1 ? 1 : (gr > G ? G : gr);
+  }
+  if (tid < LDIM * LDIM) {
+    const int u = tid / LDIM, w = tid % LDIM;
+    sL[u][w] = (u <= G && w <= G && w <= u) ? Lin[(size_t)h * ld * ld + u * ld + w] : 0.f;
+  }
+  __syncthreads();
+  if (tid < LDIM * LDIM) {
+    const int u = tid / LDIM, w = tid % LDIM;
+    double m = 0.0;
+    if (u <= G && w <= G) {
+      if (u == 0 && w == 0) {
+        m = da[h];
+      } else if (u == 0 || w == 0) {
+        const int gam = u + w;
+        for (int r = 0; r < DH; ++r)
+          if (sg[r] == gam) m += db[(size_t)h * DH + r];
+      } else {
+        for (int r = 0; r < DH; ++r) {
+          if (sg[r] != u) continue;
+          for (int t = 0; t < DH; ++t)
+            if (sg[t] == w) m += dC[(size_t)h * DH * DH + r * DH + t];
+        }
+      }
+    }
+    sM[u][w] = m;
+  }
+  __syncthreads();
+  for (int i = tid; i < ld * ld; i += blockDim.x) {
+    const int u = i / ld, w = i % ld;
+    double x = 0.0;
+    if (u <= G && w <= u) {
+      for (int p = 0; p <= G; ++p) x += (sM[u][p] + sM[p][u]) * (double)sL[p][w];
+    }
+    dL[(size_t)h * ld * ld + i] = (float)x;
+  }
+}
+
+// ---------------------------------------------------------------------------
+
+oal_status launch_prefix_vec(int batch, int n_kv_heads, int seq_len, int chunk, oal_dtype in_dtype,
+                             const void* k, const void* v, float* hc, hipStream_t stream);
+
+template <typename T>
+static oal_status backward_typed(int batch, int n_q_heads, int n_kv_heads, int seq_len, int chunk,
+                                 oal_dtype in_dtype, const void* q, const void* k, const void* v,
+                                 const void* coeffs, const float* dy, float* dq, float* dk,
+                                 float* dv, float* da, float* db, float* dC, void* ws,
+                                 hipStream_t stream) {
+  const BwdWs w = bwd_ws(ws, batch, n_q_heads, n_kv_heads, seq_len, chunk);
+  const int units = batch * n_kv_heads;
+  const int n_chunks = (seq_len + chunk - 1) / chunk;
+  const T* qq = reinterpret_cast<const T*>(q);
+  const T* kk = reinterpret_cast<const T*>(k);
+  const T* vv = reinterpret_cast<const T*>(v);
+  const bool want_coef = da != nullptr;
+  oal_status st = launch_prefix_vec(batch, n_kv_heads, seq_len, chunk, in_dtype, k, v, w.hc, stream);
+  if (st != OAL_OK) return st;
+  {
+    const size_t smem = sizeof(float) * ((size_t)2 * chunk * (DH + 1) + 32 * WP + 32 + TB * (DH + 1) +
+                                         TB * WP + DH + DH * DH);
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&k_bwd_query<T>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem) != hipSuccess)
+      return set_error(OAL_ERR_HIP, "k_bwd_query: cannot reserve %zu bytes of LDS", smem);
+    ProfScope ps("k_bwd_query", stream);
+    hipLaunchKernelGGL(k_bwd_query<T>, dim3(n_chunks, n_q_heads, batch), dim3(chunk), smem, stream,
+                       n_q_heads, n_kv_heads, seq_len, chunk, n_chunks, qq, kk, vv, coeffs, dy, w.hc,
+                       w.gbuf, w.alpha, dq);
+    if ((st = check_launch("k_bwd_query")) != OAL_OK) return st;
+  }
+  {
+    ProfScope ps("k_bwd_rbuild", stream);
+    hipLaunchKernelGGL(k_bwd_rbuild<T>, dim3(NFB, n_chunks, units), dim3(256), 0, stream, n_q_heads,
+                       n_kv_heads, seq_len, chunk, n_chunks, qq, coeffs, w.gbuf, w.hc, w.rc,
+                       want_coef ? w.dcp : nullptr);
+    if ((st = check_launch("k_bwd_rbuild")) != OAL_OK) return st;
+  }
+  {
+    ProfScope ps("k_bwd_rscan", stream);
+    hipLaunchKernelGGL(k_bwd_rscan, dim3((unsigned)((STATE_FLOATS + 255) / 256), units), dim3(256), 0,
+                       stream, n_chunks, w.rc);
+    if ((st = check_launch("k_bwd_rscan")) != OAL_OK) return st;
+  }
+  {
+    const size_t smem = sizeof(float) * ((size_t)2 * chunk * (DH + 1) + 32 * WP + TB * (DH + 1) +
+                                         TB * WP + DH + DH * DH);
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&k_bwd_key<T>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem) != hipSuccess)
+      return set_error(OAL_ERR_HIP, "k_bwd_key: cannot reserve %zu bytes of LDS", smem);
+    ProfScope ps("k_bwd_key", stream);
+    hipLaunchKernelGGL(k_bwd_key<T>, dim3(n_chunks, units), dim3(chunk), smem, stream, n_q_heads,
+                       n_kv_heads, seq_len, chunk, n_chunks, qq, kk, vv, coeffs, w.gbuf, w.rc, dk, dv);
+    if ((st = check_launch("k_bwd_key")) != OAL_OK) return st;
+  }
+  if (!want_coef) return OAL_OK;
+  {
+    const size_t smem = sizeof(float) * ((size_t)chunk * chunk + 2 * chunk * (DH + 1));
+    const void* fn = chunk == 64 ? reinterpret_cast<const void*>(&k_bwd_dc_intra<T, 64>)
+                                 : reinterpret_cast<const void*>(&k_bwd_dc_intra<T, 128>);
+    if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem) != hipSuccess)
+      return set_error(OAL_ERR_HIP, "k_bwd_dc_intra: cannot reserve %zu bytes of LDS", smem);
+    ProfScope ps("k_bwd_dc_intra", stream);
+    const dim3 grid((DCAN + 255) / 256, n_chunks, batch * n_q_heads);
+    if (chunk == 64)
+      hipLaunchKernelGGL((k_bwd_dc_intra<T, 64>), grid, dim3(256), smem, stream, n_q_heads, n_kv_heads,
+                         seq_len, n_chunks, qq, kk, w.alpha, w.dcp);
+    else
+      hipLaunchKernelGGL((k_bwd_dc_intra<T, 128>), grid, dim3(256), smem, stream, n_q_heads, n_kv_heads,
+                         seq_len, n_chunks, qq, kk, w.alpha, w.dcp);
+    if ((st = check_launch("k_bwd_dc_intra")) != OAL_OK) return st;
+  }
+  ProfScope ps("k_bwd_dcoef", stream);
+  hipLaunchKernelGGL(k_bwd_dcoef, dim3((DCAN + 255) / 256, n_q_heads), dim3(256), 0, stream, batch,
+                     n_q_heads, n_chunks, w.dcp, da, db, dC);
+  return check_launch("k_bwd_dcoef");
+}
+
+oal_status launch_backward(int batch, int n_q_heads, int n_kv_heads, int seq_len, int chunk,
+                           oal_dtype in_dtype, const void* q, const void* k, const void* v,
+                           const void* coeffs, const float* dy, float* dq, float* dk, float* dv,
+                           float* da, float* db, float* dC, void* ws, hipStream_t stream) {
+  if (in_dtype == OAL_F32)
+    return backward_typed<float>(batch, n_q_heads, n_kv_heads, seq_len, chunk, in_dtype, q, k, v,
+                                 coeffs, dy, dq, dk, dv, da, db, dC, ws, stream);
+  return backward_typed<uint16_t>(batch, n_q_heads, n_kv_heads, seq_len, chunk, in_dtype, q, k, v,
+                                  coeffs, dy, dq, dk, dv, da, db, dC, ws, stream);
+}
+
+oal_status launch_coeffs_backward(int n_q_heads, int g_max, const int32_t* n_groups,
+                                  const int32_t* group_map, const float* L, const float* da,
+                                  const float* db, const float* dC, float* dL, hipStream_t stream) {
+  ProfScope ps("k_coeffs_bwd", stream);
+  hipLaunchKernelGGL(k_coeffs_bwd, dim3(n_q_heads), dim3(64), 0, stream, g_max, n_groups, group_map,
+                     L, da, db, dC, dL);
+  return check_launch("k_coeffs_bwd");
+}
+
+}  // namespace oal

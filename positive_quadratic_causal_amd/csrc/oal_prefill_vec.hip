@@ -339,6 +339,32 @@ oal_status launch_build_vec_chunks(int batch, int n_kv_heads, int seq_len, int c
   return check_launch("k_build_vec");
 }
 
+// Exclusive per-chunk prefix states H_{<c} of a sequence that starts empty:
+// hc[unit][c] = sum of phi_k(k_j) u_j^T over the chunks before c (fp32, the
+// state layout), for fp32 or bf16 k and v.
+oal_status launch_prefix_vec(int batch, int n_kv_heads, int seq_len, int chunk, oal_dtype in_dtype,
+                             const void* k, const void* v, float* hc, hipStream_t stream) {
+  const int units = batch * n_kv_heads;
+  const int n_chunks = (seq_len + chunk - 1) / chunk;
+  {
+    ProfScope ps("k_build_vec", stream);
+    if (in_dtype == OAL_F32)
+      hipLaunchKernelGGL(k_build_vec<float>, dim3(NFB, n_chunks, units), dim3(256), 0, stream,
+                         n_kv_heads, seq_len, chunk, n_chunks, reinterpret_cast<const float*>(k),
+                         reinterpret_cast<const float*>(v), hc, 0);
+    else
+      hipLaunchKernelGGL(k_build_vec<uint16_t>, dim3(NFB, n_chunks, units), dim3(256), 0, stream,
+                         n_kv_heads, seq_len, chunk, n_chunks, reinterpret_cast<const uint16_t*>(k),
+                         reinterpret_cast<const uint16_t*>(v), hc, 0);
+    oal_status st = check_launch("k_build_vec");
+    if (st != OAL_OK) return st;
+  }
+  ProfScope ps("k_scan_vec", stream);
+  hipLaunchKernelGGL(k_scan_vec, dim3((unsigned)((STATE_FLOATS + 255) / 256), units), dim3(256), 0,
+                     stream, n_chunks, hc, nullptr);
+  return check_launch("k_scan_vec");
+}
+
 size_t prefill_vec_workspace(int batch, int n_kv_heads, int seq_len, int chunk) {
   const size_t n_chunks = (size_t)((seq_len + chunk - 1) / chunk);
   return (size_t)batch * n_kv_heads * n_chunks * STATE_FLOATS * sizeof(float);

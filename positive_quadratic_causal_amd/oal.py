@@ -65,6 +65,10 @@ def _load() -> ctypes.CDLL:
         "oal_prefill_dim": (c_int, [c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_void,
                                     c_void, c_void, c_void, c_int, c_void, c_void, c_int, c_void,
                                     c_size, c_void]),
+        "oal_prefill_backward_workspace_bytes": (c_size, [c_int] * 7),
+        "oal_prefill_backward": (c_int, [c_int] * 7 + [c_void] * 5 + [c_int] + [c_void] * 6
+                                 + [c_void, c_size, c_void]),
+        "oal_coeffs_backward": (c_int, [c_int, c_int, c_int] + [c_void] * 7 + [c_void]),
         "oal_decode_step": (c_int, [c_int, c_int, c_int, c_int, c_int, c_int, c_void, c_void,
                                     c_void, c_void, c_void, c_void, c_int, c_void]),
         "oal_softmax_attention": (c_int, [c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_void,
@@ -89,6 +93,7 @@ EXPORTED = ("oal_coeffs_bytes", "oal_expand_coeffs", "oal_dim_coeffs", "oal_stat
             "oal_state_reset", "oal_state_free", "oal_state_copy", "oal_state_bytes",
             "oal_state_tokens", "oal_state_export", "oal_prefill_workspace_bytes", "oal_prefill",
             "oal_prefill_dim_workspace_bytes", "oal_prefill_dim",
+            "oal_prefill_backward_workspace_bytes", "oal_prefill_backward", "oal_coeffs_backward",
             "oal_decode_step", "oal_softmax_attention", "oal_profile_enable", "oal_profile_reset",
             "oal_profile_query",
             "oal_status_string", "oal_last_error")
@@ -291,6 +296,56 @@ def oal_prefill_dim(q: torch.Tensor | None, k: torch.Tensor, v: torch.Tensor,
                                 _ptr(y), out_dt, _ptr(workspace) if workspace is not None else None,
                                 workspace.numel() if workspace is not None else 0, _stream(k)))
     return y
+
+
+def oal_prefill_backward_workspace_bytes(batch: int, n_q_heads: int, n_kv_heads: int,
+                                         seq_len: int, chunk: int = 0) -> int:
+    return int(_lib.oal_prefill_backward_workspace_bytes(batch, n_q_heads, n_kv_heads, seq_len,
+                                                         D_H, D_V, chunk))
+
+
+def oal_prefill_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, coeffs: torch.Tensor,
+                         dy: torch.Tensor, chunk: int = 0, want_coeff_grad: bool = True,
+                         out: tuple | None = None, workspace: torch.Tensor | None = None):
+    """Gradients of sum(dy * y) for y = the prefill of (q, k, v) from an empty state.
+    q [B, Hq, N, 64], k/v [B, Hkv, N, 64] (fp32 or bf16), dy [B, Hq, N, 64] fp32.
+    Returns (dq, dk, dv, da, db, dC), all fp32 (the last three None unless
+    want_coeff_grad); out may supply the six output tensors."""
+    B, Hq, N, dh = q.shape
+    Hkv = k.shape[1]
+    dv_ = v.shape[-1]
+    assert dy.dtype == torch.float32 and dy.is_contiguous()
+    dev = q.device
+    if out is None:
+        f32 = dict(dtype=torch.float32, device=dev)
+        out = (torch.empty((B, Hq, N, dh), **f32), torch.empty((B, Hkv, N, dh), **f32),
+               torch.empty((B, Hkv, N, dv_), **f32),
+               torch.empty((Hq,), **f32) if want_coeff_grad else None,
+               torch.empty((Hq, dh), **f32) if want_coeff_grad else None,
+               torch.empty((Hq, dh, dh), **f32) if want_coeff_grad else None)
+    dq, dk, dv, da, db, dC = out
+    if workspace is None:
+        workspace = alloc_workspace(oal_prefill_backward_workspace_bytes(B, Hq, Hkv, N, chunk), dev)
+    _check(_lib.oal_prefill_backward(B, Hq, Hkv, N, dh, dv_, _dtype_code(q), _ptr(q), _ptr(k),
+                                     _ptr(v), _ptr(coeffs), _ptr(dy), chunk, _ptr(dq), _ptr(dk),
+                                     _ptr(dv), _ptr(da), _ptr(db), _ptr(dC),
+                                     _ptr(workspace) if workspace is not None else None,
+                                     workspace.numel() if workspace is not None else 0, _stream(q)))
+    return dq, dk, dv, da, db, dC
+
+
+def oal_coeffs_backward(n_groups: torch.Tensor, group_map: torch.Tensor, L: torch.Tensor,
+                        da: torch.Tensor, db: torch.Tensor, dC: torch.Tensor,
+                        dL: torch.Tensor | None = None) -> torch.Tensor:
+    """dL [Hq, g+1, g+1] from (da, db, dC) through the grouped map (L as for
+    oal_expand_coeffs)."""
+    Hq = n_groups.shape[0]
+    g_max = L.shape[-1] - 1
+    if dL is None:
+        dL = torch.empty_like(L)
+    _check(_lib.oal_coeffs_backward(Hq, D_H, g_max, _ptr(n_groups), _ptr(group_map), _ptr(L),
+                                    _ptr(da), _ptr(db), _ptr(dC), _ptr(dL), _stream(L)))
+    return dL
 
 
 def oal_decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, coeffs: torch.Tensor,

@@ -139,3 +139,27 @@ def test_softmax_rejects_invalid_arguments():
     assert lib.oal_softmax_attention(1, 14, 2, 16, 64, 64, 1, None, P, P, P, 1, None) == 1
     assert lib.oal_softmax_attention(1, 14, 2, -1, 64, 64, 1, P, P, P, P, 1, None) == 1
     assert lib.oal_softmax_attention(1, 14, 2, 0, 64, 64, 1, P, P, P, P, 1, None) == 0     # no-op
+
+
+def test_backward_entries_sizes_and_checks():
+    lib, oal = _lib()
+    assert lib.oal_prefill_backward_workspace_bytes(1, 14, 2, 300, 64, 64, 256) == 0
+    assert lib.oal_prefill_backward_workspace_bytes(1, 14, 2, 0, 64, 64, 128) == 0
+    ws = lib.oal_prefill_backward_workspace_bytes(1, 14, 2, 300, 64, 64, 128)
+    assert ws >= 2 * 2 * 3 * 65 * 2176 * 4
+    # batch, Hq, Hkv, N, d_h, d_v, in_dt, q, k, v, coeffs, dy, chunk, dq, dk, dv, da, db, dC, ws, wsb, stream
+    ok = (1, 14, 2, 16, 64, 64, 1, P, P, P, P, P, 0, P, P, P, P, P, P, P, 1 << 40, None)
+    def call(**kw):
+        args = list(ok)
+        for i, x in kw.items():
+            args[int(i[1:])] = x
+        return lib.oal_prefill_backward(*args)
+    assert call(a12=256) == 1                    # chunk 256 not supported by the backward
+    assert call(a2=3) == 1                       # Hq % Hkv
+    assert call(a4=32) == 2                      # d_h
+    assert call(a11=None) == 1                   # dy null
+    assert call(a17=None) == 1                   # coefficient outputs: all or none
+    assert call(a20=10) == 1                     # workspace too small
+    assert call(a19=ctypes.c_void_p(0x1010)) == 1  # misaligned workspace
+    assert lib.oal_coeffs_backward(2, 64, 7, P, P, P, P, P, P, P, None) == 2
+    assert lib.oal_coeffs_backward(2, 64, 6, P, P, None, P, P, P, P, None) == 1

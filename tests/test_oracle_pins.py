@@ -456,3 +456,18 @@ def test_p16_grouped_L_grad_matches_finite_differences(G):
     fd = _fd(lambda x: float(np.sum(dy * O.causal_attention(q, k, v, x, g, G, eps))), L)
     fd = np.tril(fd)          # entries above the diagonal do not enter (the oracle ignores them)
     np.testing.assert_allclose(dL, fd, rtol=1e-6, atol=1e-8)
+
+
+def test_p16_row_restriction_equals_zeroed_dy():
+    rng = np.random.default_rng(1620)
+    N, d = 12, 8
+    q, k, v = rng.normal(size=(N, d)), rng.normal(size=(N, d)), rng.normal(size=(N, 4))
+    dy = rng.normal(size=(N, 4))
+    a, b, C = _rand_dim(rng, d)
+    rows = [3, 7, 8, 11]
+    dz = np.zeros_like(dy)
+    dz[rows] = dy[rows]
+    full = O.causal_attention_dim_grad(q, k, v, a, b, C, dz)
+    part = O.causal_attention_dim_grad(q, k, v, a, b, C, dy, rows=rows)
+    for x, y in zip(full, part):
+        np.testing.assert_allclose(np.asarray(y), np.asarray(x), rtol=1e-12, atol=1e-14)
