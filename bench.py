@@ -254,6 +254,83 @@ def bench_prefill_dim(oal, w, chunk, steps, warmup, device):
             "kernels_ms": {k: round(v["avg_ms"], 5) for k, v in kt.items()}}
 
 
+BWD_KERNELS = ["k_build_vec", "k_scan_vec", "k_bwd_query", "k_bwd_rbuild", "k_bwd_rscan",
+               "k_bwd_key", "k_bwd_ksum", "k_bwd_dc_intra", "k_bwd_dcoef"]
+
+
+def backward_flops(w, chunk) -> dict:
+    """Algorithmic flops of the backward kernels (useful, unpadded).  Per causal
+    pair inside a chunk: kappa in packed form 64 + 2 (64 + 2080), its gradient
+    2 * 64 * 64 + 3 * 64 (S p and the product with k or q), and two 65-wide
+    products (alpha and the accumulation).  Per query or key row: two 2145 x 65
+    contractions with a state (recompute + H g, or R^T psi(k) + R u)."""
+    n, c = w.seq_len, chunk
+    pairs = 0
+    for t0 in range(0, n, c):
+        m = min(c, n - t0)
+        pairs += m * (m + 1) // 2
+    pairs *= w.batch * w.n_q_heads
+    D, Wc = 2145, 65
+    kap, grad = 64 + 2 * (64 + 2080), 2 * 64 * 64 + 3 * 64
+    nq = w.batch * w.n_q_heads * n
+    nk = w.batch * w.n_kv_heads * n
+    return {"k_bwd_query": nq * 4 * D * Wc + pairs * (kap + grad + 4 * Wc),
+            "k_bwd_key": nk * 4 * D * Wc + pairs * (kap + grad + 4 * Wc),
+            "k_bwd_rbuild": nq * 2 * D * Wc,
+            "k_bwd_dc_intra": pairs * 2 * D}
+
+
+def bench_backward(oal, w, chunk, steps, warmup, device):
+    """The prefill backward (dq, dk, dv, da, db, dC) for a seeded dy."""
+    import numpy as np
+    import torch
+
+    from positive_quadratic_causal_amd import synth
+    st = synth.structure(w)
+    x = gen_inputs(w, st, device, t1=w.seq_len)
+    coeffs = oal.oal_expand_coeffs(torch.from_numpy(st.n_groups).to(device),
+                                   torch.from_numpy(st.group_map).to(device),
+                                   torch.from_numpy(st.L).to(device), w.eps)
+    dy = torch.from_numpy(np.random.default_rng(7).standard_normal(
+        (w.batch, w.n_q_heads, w.seq_len, 64)).astype(np.float32)).to(device)
+    out = oal.oal_prefill_backward(x["q"], x["k"], x["v"], coeffs, dy, chunk=chunk)
+    ws = oal.alloc_workspace(oal.oal_prefill_backward_workspace_bytes(
+        w.batch, w.n_q_heads, w.n_kv_heads, w.seq_len, chunk), device)
+
+    def step():
+        oal.oal_prefill_backward(x["q"], x["k"], x["v"], coeffs, dy, chunk=chunk, out=out,
+                                 workspace=ws)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    oal.oal_profile_reset()
+    oal.oal_profile_enable(True)
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    oal.oal_profile_enable(False)
+    kt = kernel_times(oal, BWD_KERNELS)
+    fl = backward_flops(w, chunk)
+    dom = max((k for k in fl if k in kt), key=lambda k: kt[k]["avg_ms"])
+    kms = kt[dom]["avg_ms"]
+    del x, dy, out, ws
+    torch.cuda.empty_cache()
+    return {"workload": w.name, "chunk": chunk, "ms_per_step": round(ms, 5),
+            "tokens_per_s": round(w.batch * w.seq_len / (ms * 1e-3), 1),
+            "roofline": {"kernel": dom, "bound": "alu",
+                         "achieved": round(fl[dom] / (kms * 1e-3) / 1e12, 3),
+                         "peak": PEAK_F32_VECTOR_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(fl[dom] / (kms * 1e-3) / 1e12 / PEAK_F32_VECTOR_TFLOPS, 5),
+                         "algorithmic_flops": fl[dom]},
+            "kernels_ms": {k: round(v["avg_ms"], 5) for k, v in kt.items()}}
+
+
 def fidelity_report(oal, w, chunk, device):
     """[OAL] App. C, Eqs. 21-22: MSE and RelMSE of the OAL output against exact
     softmax attention on the same synthetic inputs, one sequence = all heads of a
@@ -566,7 +643,7 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-softmax", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "decode", "softmax", "prefill_dim"], default=None,
+    ap.add_argument("--only", choices=["prefill", "decode", "softmax", "prefill_dim", "backward"], default=None,
                     help="time one leg only (used to profile each workload on its own)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="after the legs, copy MIB MiB 5 times (reference for HBM counters)")
@@ -594,6 +671,10 @@ def main() -> int:
     if args.only == "softmax":
         res = bench_softmax(oal, w3, args.steps, args.warmup, device)
         print(json.dumps({"metric": METRIC, "softmax": res}), flush=True)
+        return 0
+    if args.only == "backward":
+        res = bench_backward(oal, synth.WORKLOADS[1], 64, args.steps, args.warmup, device)
+        print(json.dumps({"metric": METRIC, "backward": res}), flush=True)
         return 0
     if args.only == "prefill_dim":
         res = bench_prefill_dim(oal, synth.WORKLOADS[1], args.chunk, args.steps, args.warmup, device)
@@ -667,6 +748,9 @@ def main() -> int:
         log("general prefill (dimension-specific kernel): Qwen-shaped N = 2048")
         result["prefill_dim"] = bench_prefill_dim(oal, synth.WORKLOADS[1], args.chunk,
                                                   max(3, args.steps // 4), 2, device)
+        log("backward (dq, dk, dv, coefficient gradients): Qwen-shaped N = 2048")
+        result["backward"] = bench_backward(oal, synth.WORKLOADS[1], 64, max(3, args.steps // 4), 2,
+                                            device)
         log("fidelity: OAL vs softmax, MSE / RelMSE")
         result["fidelity"] = [fidelity_report(oal, synth.WORKLOADS[i], args.chunk, device)
                               for i in (1, 2)]

@@ -22,11 +22,12 @@
 //
 // Kernels, in launch order:
 //   prefix build + scan (oal_prefill_vec.hip)  H_{<c}
-//   k_bwd_query     one thread per query: recompute u~_i, g_i; dq_i; alpha rows
+//   k_bwd_query     two threads per query: recompute u~_i, g_i; dq_i; alpha rows
 //   k_bwd_rbuild    per chunk: sum_h c_f psi_f(q_i) g_i^T (suffix deltas) and the
 //                   state part of dc: sum_i psi_f(q_i) (H_{<c} g_i)_f
 //   k_bwd_rscan     exclusive suffix sums over chunks: R_{>c}
-//   k_bwd_key       one thread per key: dv_j, dk_j
+//   k_bwd_key       two threads per key and slot (a query head's pairs, or R_{>c}):
+//                   parts of dv_j, dk_j;  k_bwd_ksum adds the parts
 //   k_bwd_dc_intra  pair part of dc: sum_{i, j<=i in the chunk} alpha_ij psi_f(q_i) psi_f(k_j)
 //   k_bwd_dcoef     sum over chunks and batch; (da, db, dC) of [OAL] Eq. 3
 #include "oal_common.h"
@@ -86,15 +87,15 @@ __device__ __forceinline__ float dot_row(const float* row, const float (&x)[WP])
   float4 r4[WP / 4];
 #pragma unroll
   for (int i = 0; i < WP / 4; ++i) r4[i] = reinterpret_cast<const float4*>(row)[i];
-  float s0 = 0.f, s1 = 0.f;
+  float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;   // four independent chains
 #pragma unroll
   for (int i = 0; i < WP / 4; ++i) {
     s0 = fmaf(r4[i].x, x[4 * i + 0], s0);
     s1 = fmaf(r4[i].y, x[4 * i + 1], s1);
-    s0 = fmaf(r4[i].z, x[4 * i + 2], s0);
-    s1 = fmaf(r4[i].w, x[4 * i + 3], s1);
+    s2 = fmaf(r4[i].z, x[4 * i + 2], s2);
+    s3 = fmaf(r4[i].w, x[4 * i + 3], s3);
   }
-  return s0 + s1;
+  return (s0 + s1) + (s2 + s3);
 }
 
 // (S p)_r for the 64-float row r of S in LDS (16-byte aligned) and p in registers
@@ -102,15 +103,15 @@ __device__ __forceinline__ float srow_dot(const float* srow, const float (&p)[DH
   float4 s4[DH / 4];
 #pragma unroll
   for (int i = 0; i < DH / 4; ++i) s4[i] = reinterpret_cast<const float4*>(srow)[i];
-  float sa = 0.f, sb = 0.f;
+  float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;   // four independent chains
 #pragma unroll
   for (int i = 0; i < DH / 4; ++i) {
-    sa = fmaf(s4[i].x, p[4 * i + 0], sa);
-    sb = fmaf(s4[i].y, p[4 * i + 1], sb);
-    sa = fmaf(s4[i].z, p[4 * i + 2], sa);
-    sb = fmaf(s4[i].w, p[4 * i + 3], sb);
+    s0 = fmaf(s4[i].x, p[4 * i + 0], s0);
+    s1 = fmaf(s4[i].y, p[4 * i + 1], s1);
+    s2 = fmaf(s4[i].z, p[4 * i + 2], s2);
+    s3 = fmaf(s4[i].w, p[4 * i + 3], s3);
   }
-  return sa + sb;
+  return (s0 + s1) + (s2 + s3);
 }
 
 // kappa of one pair from a query row and a key row in LDS: a + sum_r p_r (b'_r + (S p)_r)
@@ -137,6 +138,7 @@ struct BwdWs {
   float* gbuf;    // [batch][Hq][n_chunks * chunk][WP] g rows (zero beyond seq_len)
   float* alpha;   // [batch][Hq][n_chunks][chunk][chunk] alpha_ij (zero for j > i)
   float* dcp;     // [batch][Hq][n_chunks][DS] per-chunk parts of dc
+  float* kpart;   // [units][2 (rep + 1)][n_chunks * chunk][128] parts of [dk | dv]
   size_t bytes;
 };
 
@@ -155,6 +157,7 @@ static BwdWs bwd_ws(void* base, int batch, int n_q_heads, int n_kv_heads, int se
   const size_t o_g = take(bh * nc * chunk * WP);
   const size_t o_a = take(bh * nc * chunk * chunk);
   const size_t o_d = take(bh * nc * DS);
+  const size_t o_k = take(units * (size_t)2 * (n_q_heads / n_kv_heads + 1) * nc * chunk * (DH + DV));
   BwdWs w;
   uint8_t* p = reinterpret_cast<uint8_t*>(base);
   w.hc = reinterpret_cast<float*>(p + o_h);
@@ -162,6 +165,7 @@ static BwdWs bwd_ws(void* base, int batch, int n_q_heads, int n_kv_heads, int se
   w.gbuf = reinterpret_cast<float*>(p + o_g);
   w.alpha = reinterpret_cast<float*>(p + o_a);
   w.dcp = reinterpret_cast<float*>(p + o_d);
+  w.kpart = reinterpret_cast<float*>(p + o_k);
   w.bytes = off;
   return w;
 }
@@ -171,9 +175,12 @@ size_t backward_workspace(int batch, int n_q_heads, int n_kv_heads, int seq_len,
 }
 
 // ---------------------------------------------------------------------------
-// Query side.  One block per (chunk, query head, batch), thread i = query t0 + i.
+// Query side.  One block per (chunk, query head, batch); two threads per query
+// (thread 2 i + h, h = 0, 1, for query t0 + i) split its features and its pairs
+// by parity; the halves of u~_i are added through LDS, g_i is shared the same
+// way, and each half keeps its own dq row, the two rows added at the end.
 template <typename T>
-__global__ void __launch_bounds__(128)
+__global__ void __launch_bounds__(256)
 k_bwd_query(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunks,
             const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
             const void* __restrict__ coeffs, const float* __restrict__ dy,
@@ -185,14 +192,17 @@ k_bwd_query(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunks,
   const int rep = n_q_heads / n_kv_heads;
   const int unit = b * n_kv_heads + hq / rep;
   const int tid = threadIdx.x;
+  const int nthr = blockDim.x;                // 2 * chunk
+  const int qx = tid >> 1;                    // query of the chunk
+  const int half = tid & 1;
   const int t0 = c * chunk;
   const int clen = min(chunk, seq_len - t0);
-  const bool active = tid < clen;
+  const bool active = qx < clen;
 
   extern __shared__ float smem[];
   float* s_q = smem;                          // [chunk][DH + 1]
-  float* s_dq = s_q + chunk * (DH + 1);       // [chunk][DH + 1]
-  float* s_H = s_dq + chunk * (DH + 1);       // [32][WP]
+  float* s_dq = s_q + chunk * (DH + 1);       // [2][chunk][DH + 1] (half 1's rows also pass u~, g)
+  float* s_H = s_dq + 2 * chunk * (DH + 1);   // [32][WP]
   float* s_cf = s_H + 32 * WP;                // [32]
   float* s_k = s_cf + 32;                     // [TB][DH + 1]
   float* s_u = s_k + TB * (DH + 1);           // [TB][WP]
@@ -202,30 +212,30 @@ k_bwd_query(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunks,
   const float* rec = coef_rec(coeffs, hq);
   const float a = rec[OAL_COEF_A];
   const size_t qrow0 = ((size_t)b * n_q_heads + hq) * seq_len + t0;
-  for (int i = tid; i < chunk * DH; i += blockDim.x) {
+  for (int i = tid; i < chunk * DH; i += nthr) {
     const int ii = i / DH, d = i % DH;
     s_q[ii * (DH + 1) + d] = ii < clen ? Elem<T>::load(q, (qrow0 + ii) * DH + d) : 0.f;
-    s_dq[ii * (DH + 1) + d] = 0.f;
   }
-  for (int i = tid; i < DH; i += blockDim.x) s_b[i] = rec[OAL_COEF_BP + i];
-  for (int i = tid; i < DH * DH; i += blockDim.x) s_S[i] = rec[OAL_COEF_CM + i];
-  for (int i = tid; i < 32 * (WP - W); i += blockDim.x) s_H[(i / (WP - W)) * WP + W + i % (WP - W)] = 0.f;
-  for (int i = tid; i < TB * (WP - W); i += blockDim.x) s_u[(i / (WP - W)) * WP + W + i % (WP - W)] = 0.f;
+  for (int i = tid; i < 2 * chunk * (DH + 1); i += nthr) s_dq[i] = 0.f;
+  for (int i = tid; i < DH; i += nthr) s_b[i] = rec[OAL_COEF_BP + i];
+  for (int i = tid; i < DH * DH; i += nthr) s_S[i] = rec[OAL_COEF_CM + i];
+  for (int i = tid; i < 32 * (WP - W); i += nthr) s_H[(i / (WP - W)) * WP + W + i % (WP - W)] = 0.f;
+  for (int i = tid; i < TB * (WP - W); i += nthr) s_u[(i / (WP - W)) * WP + W + i % (WP - W)] = 0.f;
   __syncthreads();
-  const float* qi = s_q + tid * (DH + 1);
-  float* dqi = s_dq + tid * (DH + 1);
+  const float* qi = s_q + qx * (DH + 1);
+  float* dqi = s_dq + (half * chunk + qx) * (DH + 1);
   const float* Hc = hc + ((size_t)unit * n_chunks + c) * STATE_FLOATS;
   const size_t kbase = (size_t)unit * seq_len + t0;
 
   auto stage_block = [&](int f0) {
-    for (int i = tid; i < 32 * W; i += blockDim.x) {
+    for (int i = tid; i < 32 * W; i += nthr) {
       const int w = i / 32, ff = i % 32;
       s_H[ff * WP + w] = Hc[(size_t)w * DS + f0 + ff];   // f0 + 31 < DS always
     }
     if (tid < 32) s_cf[tid] = coef_of(rec, f0 + tid);
   };
   auto stage_keys = [&](int j0, int nj) {
-    for (int i = tid; i < TB * DH; i += blockDim.x) {
+    for (int i = tid; i < TB * DH; i += nthr) {
       const int jj = i / DH, d = i % DH;
       float kv_ = 0.f, vv_ = 0.f;
       if (jj < nj) {
@@ -235,10 +245,10 @@ k_bwd_query(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunks,
       s_k[jj * (DH + 1) + d] = kv_;
       s_u[jj * WP + d] = vv_;
     }
-    for (int jj = tid; jj < TB; jj += blockDim.x) s_u[jj * WP + DV] = jj < nj ? 1.f : 0.f;
+    for (int jj = tid; jj < TB; jj += nthr) s_u[jj * WP + DV] = jj < nj ? 1.f : 0.f;
   };
 
-  // ---- 1. recompute u~_i: state part, then the pairs of the chunk
+  // ---- 1. recompute this half's share of u~_i: state part, then the chunk's pairs
   float acc[WP];
 #pragma unroll
   for (int w = 0; w < WP; ++w) acc[w] = 0.f;
@@ -248,7 +258,7 @@ k_bwd_query(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunks,
     __syncthreads();
     if (active) {
       const int nf = min(32, DCAN - f0);
-      for (int ff = 0; ff < nf; ++ff) {
+      for (int ff = half; ff < nf; ff += 2) {
         int r, t;
         const int kind = feat_decode(f0 + ff, r, t);
         const float psi = kind == 0 ? 1.f : kind == 1 ? qi[r] : qi[r] * qi[t];
@@ -262,44 +272,60 @@ k_bwd_query(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunks,
     stage_keys(j0, nj);
     __syncthreads();
     if (active) {
-      const int jmax = min(nj, tid - j0 + 1);
-      for (int jj = 0; jj < jmax; ++jj)
+      const int jmax = min(nj, qx - j0 + 1);
+      for (int jj = half; jj < jmax; jj += 2)
         axpy_row(acc, kappa_pair(a, qi, s_k + jj * (DH + 1), s_b, s_S), s_u + jj * WP);
     }
   }
 
-  // ---- 2. g_i (zero for rows beyond the sequence)
+  // ---- 2. u~_i = the two halves; g_i (zero for rows beyond the sequence), shared
+  float* xrow = s_dq + (chunk + qx) * (DH + 1);   // half 1's dq row, still unused
+  __syncthreads();
+  if (half == 1) {
+#pragma unroll
+    for (int w = 0; w < W; ++w) xrow[w] = acc[w];
+  }
+  __syncthreads();
   float g[WP];
 #pragma unroll
   for (int w = 0; w < WP; ++w) g[w] = 0.f;
-  if (active) {
-    const float inv = 1.0f / acc[DV];
-    const float* dyi = dy + (qrow0 + tid) * DV;
-    float ydot = 0.f;
+  if (half == 0) {
+    if (active) {
+      const float inv = 1.0f / (acc[DV] + xrow[DV]);
+      const float* dyi = dy + (qrow0 + qx) * DV;
+      float ydot = 0.f;
 #pragma unroll
-    for (int w = 0; w < DV; ++w) {
-      const float d = dyi[w];
-      g[w] = d * inv;
-      ydot = fmaf(d, acc[w] * inv, ydot);
+      for (int w = 0; w < DV; ++w) {
+        const float d = dyi[w];
+        g[w] = d * inv;
+        ydot = fmaf(d, (acc[w] + xrow[w]) * inv, ydot);
+      }
+      g[DV] = -ydot * inv;
     }
-    g[DV] = -ydot * inv;
-  }
-  {
-    float* gr = gbuf + (((size_t)b * n_q_heads + hq) * ((size_t)n_chunks * chunk) + t0 + tid) * WP;
+#pragma unroll
+    for (int w = 0; w < W; ++w) xrow[w] = g[w];
+    float* gr = gbuf + (((size_t)b * n_q_heads + hq) * ((size_t)n_chunks * chunk) + t0 + qx) * WP;
 #pragma unroll
     for (int i = 0; i < WP / 4; ++i)
       reinterpret_cast<float4*>(gr)[i] = make_float4(g[4 * i], g[4 * i + 1], g[4 * i + 2], g[4 * i + 3]);
   }
+  __syncthreads();
+  if (half == 1) {
+#pragma unroll
+    for (int w = 0; w < W; ++w) g[w] = xrow[w];
+#pragma unroll
+    for (int w = 0; w <= DH; ++w) xrow[w] = 0.f;   // back to a zero dq row (own row only)
+  }
 
   // ---- 3. the chunk's pairs: alpha_ij and dq_i += alpha_ij k_j o (b' + 2 S p)
-  float* arow = alpha + ((((size_t)b * n_q_heads + hq) * n_chunks + c) * chunk + tid) * chunk;
+  float* arow = alpha + ((((size_t)b * n_q_heads + hq) * n_chunks + c) * chunk + qx) * chunk;
   for (int j0 = 0; j0 < chunk; j0 += TB) {
     const int nj = max(0, min(TB, clen - j0));
     __syncthreads();
     stage_keys(j0, nj);
     __syncthreads();
-    const int jmax = active ? max(0, min(nj, tid - j0 + 1)) : 0;
-    for (int jj = 0; jj < jmax; ++jj) {
+    const int jmax = active ? max(0, min(nj, qx - j0 + 1)) : 0;
+    for (int jj = half; jj < jmax; jj += 2) {
       const float* kj = s_k + jj * (DH + 1);
       const float al = dot_row(s_u + jj * WP, g);
       arow[j0 + jj] = al;
@@ -310,7 +336,8 @@ k_bwd_query(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunks,
       for (int r = 0; r < DH; ++r)
         dqi[r] = fmaf(al * kj[r], s_b[r] + 2.f * srow_dot(s_S + r * DH, p), dqi[r]);
     }
-    for (int jj = jmax; jj < TB; ++jj) arow[j0 + jj] = 0.f;
+    for (int jj = half; jj < TB; jj += 2)
+      if (jj >= jmax) arow[j0 + jj] = 0.f;
   }
 
   // ---- 4. state part: d_f = H_{<c}[f] . g_i, then the monomials' derivatives
@@ -320,7 +347,7 @@ k_bwd_query(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunks,
     __syncthreads();
     if (active) {
       const int nf = min(32, DCAN - f0);
-      for (int ff = 0; ff < nf; ++ff) {
+      for (int ff = half; ff < nf; ff += 2) {
         int r, t;
         const int kind = feat_decode(f0 + ff, r, t);
         if (kind == 0) continue;
@@ -334,10 +361,13 @@ k_bwd_query(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunks,
       }
     }
   }
+  __syncthreads();
   if (active) {
-    float* o = dq + (qrow0 + tid) * DH;
+    const float* d0 = s_dq + qx * (DH + 1);
+    const float* d1 = s_dq + (chunk + qx) * (DH + 1);
+    float* o = dq + (qrow0 + qx) * DH + half * (DH / 2);
 #pragma unroll
-    for (int d = 0; d < DH; ++d) o[d] = dqi[d];
+    for (int d = 0; d < DH / 2; ++d) o[d] = d0[half * (DH / 2) + d] + d1[half * (DH / 2) + d];
   }
 }
 
@@ -440,65 +470,73 @@ k_bwd_rscan(int n_chunks, float* __restrict__ rc) {
 }
 
 // ---------------------------------------------------------------------------
-// Key side.  One block per (chunk, unit), thread j = key t0 + j.
+// Key side.  One block per (chunk, unit, slot): slot s < rep sums the chunk's
+// pairs of query head kv * rep + s, slot rep the later chunks through R_{>c}.
+// Two threads per key (thread 2 j + h for key t0 + j) split the pairs or the
+// features by parity; each thread writes its part of [dk_j | dv_j] to kpart
+// (part 2 slot + h), and k_bwd_ksum adds the 2 (rep + 1) parts in order.
 template <typename T>
-__global__ void __launch_bounds__(128)
+__global__ void __launch_bounds__(256)
 k_bwd_key(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunks,
           const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
           const void* __restrict__ coeffs, const float* __restrict__ gbuf,
-          const float* __restrict__ rc, float* __restrict__ dk, float* __restrict__ dv) {
+          const float* __restrict__ rc, float* __restrict__ kpart) {
   const int c = blockIdx.x;
-  const int unit = blockIdx.y;
-  const int b = unit / n_kv_heads, kv = unit % n_kv_heads;
   const int rep = n_q_heads / n_kv_heads;
+  const int unit = blockIdx.y / (rep + 1);
+  const int slot = blockIdx.y % (rep + 1);
+  const int b = unit / n_kv_heads, kv = unit % n_kv_heads;
   const int tid = threadIdx.x;
+  const int nthr = blockDim.x;                // 2 * chunk
+  const int jx = tid >> 1;                    // key of the chunk
+  const int half = tid & 1;
   const int t0 = c * chunk;
   const int clen = min(chunk, seq_len - t0);
-  const bool active = tid < clen;
+  const bool active = jx < clen;
 
   extern __shared__ float smem[];
   float* s_k = smem;                          // [chunk][DH + 1]
-  float* s_dk = s_k + chunk * (DH + 1);       // [chunk][DH + 1]
-  float* s_R = s_dk + chunk * (DH + 1);       // [32][WP]
+  float* s_dk = s_k + chunk * (DH + 1);       // [2][chunk][DH + 1]
+  float* s_R = s_dk + 2 * chunk * (DH + 1);   // [32][WP]
   float* s_q = s_R + 32 * WP;                 // [TB][DH + 1]
   float* s_g = s_q + TB * (DH + 1);           // [TB][WP]
   float* s_b = s_g + TB * WP;                 // [DH]
   float* s_S = s_b + DH;                      // [DH][DH]
 
   const size_t krow0 = (size_t)unit * seq_len + t0;
-  for (int i = tid; i < chunk * DH; i += blockDim.x) {
+  for (int i = tid; i < chunk * DH; i += nthr) {
     const int jj = i / DH, d = i % DH;
     s_k[jj * (DH + 1) + d] = jj < clen ? Elem<T>::load(k, (krow0 + jj) * DH + d) : 0.f;
-    s_dk[jj * (DH + 1) + d] = 0.f;
   }
-  for (int i = tid; i < 32 * (WP - W); i += blockDim.x) s_R[(i / (WP - W)) * WP + W + i % (WP - W)] = 0.f;
+  for (int i = tid; i < 2 * chunk * (DH + 1); i += nthr) s_dk[i] = 0.f;
+  for (int i = tid; i < 32 * (WP - W); i += nthr) s_R[(i / (WP - W)) * WP + W + i % (WP - W)] = 0.f;
   float uj[WP];
 #pragma unroll
   for (int w = 0; w < WP; ++w) uj[w] = 0.f;
   if (active) {
 #pragma unroll
-    for (int w = 0; w < DV; ++w) uj[w] = Elem<T>::load(v, (krow0 + tid) * DV + w);
+    for (int w = 0; w < DV; ++w) uj[w] = Elem<T>::load(v, (krow0 + jx) * DV + w);
     uj[DV] = 1.f;
   }
   __syncthreads();
-  const float* kj = s_k + tid * (DH + 1);
-  float* dkj = s_dk + tid * (DH + 1);
+  const float* kj = s_k + jx * (DH + 1);
+  float* dkj = s_dk + (half * chunk + jx) * (DH + 1);
   float du[WP];
 #pragma unroll
   for (int w = 0; w < WP; ++w) du[w] = 0.f;
 
   // ---- later chunks, through R_{>c}: du_j = R^T psi(k_j), d psi(k_j) = R u_j
   const float* Rs = rc + ((size_t)unit * n_chunks + c) * STATE_FLOATS;
-  for (int f0 = 0; f0 < DCAN; f0 += 32) {
+  for (int f0 = 0; slot == rep && f0 < DCAN; f0 += 32) {
     __syncthreads();
-    for (int i = tid; i < 32 * W; i += blockDim.x) {
+    for (int i = tid; i < 32 * W; i += nthr) {
       const int w = i / 32, ff = i % 32;
       s_R[ff * WP + w] = Rs[(size_t)w * DS + f0 + ff];
     }
     __syncthreads();
     if (active) {
       const int nf = min(32, DCAN - f0);
-      for (int ff = 0; ff < nf; ++ff) {
+      for (int ff = half; ff < nf; ff += 2) {
         int r, t;
         const int kind = feat_decode(f0 + ff, r, t);
         const float* row = s_R + ff * WP;
@@ -516,31 +554,32 @@ k_bwd_key(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunks,
     }
   }
 
-  // ---- the chunk's pairs (i >= j), every query head of the group
+  // ---- the chunk's pairs (i >= j) of this slot's query head
   const size_t npad = (size_t)n_chunks * chunk;
-  for (int hh = 0; hh < rep; ++hh) {
-    const int hq = kv * rep + hh;
+  if (slot < rep) {
+    const int hq = kv * rep + slot;
     const float* rec = coef_rec(coeffs, hq);
     const float a = rec[OAL_COEF_A];
     const size_t qrow0 = ((size_t)b * n_q_heads + hq) * seq_len;
     const size_t grow0 = ((size_t)b * n_q_heads + hq) * npad;
     __syncthreads();
-    for (int i = tid; i < DH; i += blockDim.x) s_b[i] = rec[OAL_COEF_BP + i];
-    for (int i = tid; i < DH * DH; i += blockDim.x) s_S[i] = rec[OAL_COEF_CM + i];
+    for (int i = tid; i < DH; i += nthr) s_b[i] = rec[OAL_COEF_BP + i];
+    for (int i = tid; i < DH * DH; i += nthr) s_S[i] = rec[OAL_COEF_CM + i];
     for (int i0 = 0; i0 < clen; i0 += TB) {
       const int ni = min(TB, clen - i0);
       __syncthreads();
-      for (int i = tid; i < TB * DH; i += blockDim.x) {
+      for (int i = tid; i < TB * DH; i += nthr) {
         const int ii = i / DH, d = i % DH;
         s_q[ii * (DH + 1) + d] = ii < ni ? Elem<T>::load(q, (qrow0 + t0 + i0 + ii) * DH + d) : 0.f;
       }
-      for (int i = tid; i < TB * WP; i += blockDim.x) {
+      for (int i = tid; i < TB * WP; i += nthr) {
         const int ii = i / WP, w = i % WP;
         s_g[ii * WP + w] = ii < ni ? gbuf[(grow0 + t0 + i0 + ii) * WP + w] : 0.f;
       }
       __syncthreads();
       if (active) {
-        for (int ii = max(0, tid - i0); ii < ni; ++ii) {
+        const int ii0 = max(0, jx - i0);
+        for (int ii = ii0 + ((ii0 ^ half) & 1); ii < ni; ii += 2) {
           const float* qi = s_q + ii * (DH + 1);
           const float* gi = s_g + ii * WP;
           const float al = dot_row(gi, uj);
@@ -560,13 +599,29 @@ k_bwd_key(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunks,
     }
   }
   if (active) {
-    float* ov = dv + (krow0 + tid) * DV;
-    float* ok = dk + (krow0 + tid) * DH;
+    float* o = kpart + (((size_t)unit * 2 * (rep + 1) + 2 * slot + half) * npad + t0 + jx) * (DH + DV);
 #pragma unroll
-    for (int w = 0; w < DV; ++w) ov[w] = du[w];
+    for (int d = 0; d < DH; ++d) o[d] = dkj[d];
 #pragma unroll
-    for (int d = 0; d < DH; ++d) ok[d] = dkj[d];
+    for (int w = 0; w < DV; ++w) o[DH + w] = du[w];
   }
+}
+
+// dk, dv = the sum of the 2 (rep + 1) parts of every key, in order.
+__global__ void __launch_bounds__(256)
+k_bwd_ksum(int n_kv_heads, int rep, int seq_len, int npad, const float* __restrict__ kpart,
+           float* __restrict__ dk, float* __restrict__ dv) {
+  const size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const size_t per_unit = (size_t)seq_len * (DH + DV);
+  const int unit = blockIdx.y;
+  if (e >= per_unit) return;
+  const size_t pos = e / (DH + DV);
+  const int comp = (int)(e % (DH + DV));
+  float s = 0.f;
+  for (int sl = 0; sl < 2 * (rep + 1); ++sl)
+    s += kpart[(((size_t)unit * 2 * (rep + 1) + sl) * npad + pos) * (DH + DV) + comp];
+  if (comp < DH) dk[((size_t)unit * seq_len + pos) * DH + comp] = s;
+  else dv[((size_t)unit * seq_len + pos) * DV + comp - DH] = s;
 }
 
 // ---------------------------------------------------------------------------
@@ -737,13 +792,13 @@ static oal_status backward_typed(int batch, int n_q_heads, int n_kv_heads, int s
   oal_status st = launch_prefix_vec(batch, n_kv_heads, seq_len, chunk, in_dtype, k, v, w.hc, stream);
   if (st != OAL_OK) return st;
   {
-    const size_t smem = sizeof(float) * ((size_t)2 * chunk * (DH + 1) + 32 * WP + 32 + TB * (DH + 1) +
+    const size_t smem = sizeof(float) * ((size_t)3 * chunk * (DH + 1) + 32 * WP + 32 + TB * (DH + 1) +
                                          TB * WP + DH + DH * DH);
     if (hipFuncSetAttribute(reinterpret_cast<const void*>(&k_bwd_query<T>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem) != hipSuccess)
       return set_error(OAL_ERR_HIP, "k_bwd_query: cannot reserve %zu bytes of LDS", smem);
     ProfScope ps("k_bwd_query", stream);
-    hipLaunchKernelGGL(k_bwd_query<T>, dim3(n_chunks, n_q_heads, batch), dim3(chunk), smem, stream,
+    hipLaunchKernelGGL(k_bwd_query<T>, dim3(n_chunks, n_q_heads, batch), dim3(2 * chunk), smem, stream,
                        n_q_heads, n_kv_heads, seq_len, chunk, n_chunks, qq, kk, vv, coeffs, dy, w.hc,
                        w.gbuf, w.alpha, dq);
     if ((st = check_launch("k_bwd_query")) != OAL_OK) return st;
@@ -762,15 +817,24 @@ static oal_status backward_typed(int batch, int n_q_heads, int n_kv_heads, int s
     if ((st = check_launch("k_bwd_rscan")) != OAL_OK) return st;
   }
   {
-    const size_t smem = sizeof(float) * ((size_t)2 * chunk * (DH + 1) + 32 * WP + TB * (DH + 1) +
+    const size_t smem = sizeof(float) * ((size_t)3 * chunk * (DH + 1) + 32 * WP + TB * (DH + 1) +
                                          TB * WP + DH + DH * DH);
     if (hipFuncSetAttribute(reinterpret_cast<const void*>(&k_bwd_key<T>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem) != hipSuccess)
       return set_error(OAL_ERR_HIP, "k_bwd_key: cannot reserve %zu bytes of LDS", smem);
-    ProfScope ps("k_bwd_key", stream);
-    hipLaunchKernelGGL(k_bwd_key<T>, dim3(n_chunks, units), dim3(chunk), smem, stream, n_q_heads,
-                       n_kv_heads, seq_len, chunk, n_chunks, qq, kk, vv, coeffs, w.gbuf, w.rc, dk, dv);
-    if ((st = check_launch("k_bwd_key")) != OAL_OK) return st;
+    const int rep = n_q_heads / n_kv_heads;
+    {
+      ProfScope ps("k_bwd_key", stream);
+      hipLaunchKernelGGL(k_bwd_key<T>, dim3(n_chunks, units * (rep + 1)), dim3(2 * chunk), smem, stream,
+                         n_q_heads, n_kv_heads, seq_len, chunk, n_chunks, qq, kk, vv, coeffs, w.gbuf,
+                         w.rc, w.kpart);
+      if ((st = check_launch("k_bwd_key")) != OAL_OK) return st;
+    }
+    ProfScope ps("k_bwd_ksum", stream);
+    const size_t per_unit = (size_t)seq_len * (DH + DV);
+    hipLaunchKernelGGL(k_bwd_ksum, dim3((unsigned)((per_unit + 255) / 256), units), dim3(256), 0,
+                       stream, n_kv_heads, rep, seq_len, n_chunks * chunk, w.kpart, dk, dv);
+    if ((st = check_launch("k_bwd_ksum")) != OAL_OK) return st;
   }
   if (!want_coef) return OAL_OK;
   {

@@ -248,15 +248,15 @@ k_readout_vec(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunk
             float4 s4[DH / 4];
 #pragma unroll
             for (int i = 0; i < DH / 4; ++i) s4[i] = reinterpret_cast<const float4*>(s_cm + r * DH)[i];
-            float sa = s_ell[r], sb = 0.f;   // two chains halve the dependent adds
+            float s0 = s_ell[r], s1 = 0.f, s2 = 0.f, s3 = 0.f;   // four independent chains
 #pragma unroll
             for (int i = 0; i < DH / 4; ++i) {
-              sa = fmaf(s4[i].x, pr[4 * i + 0], sa);
-              sb = fmaf(s4[i].y, pr[4 * i + 1], sb);
-              sa = fmaf(s4[i].z, pr[4 * i + 2], sa);
-              sb = fmaf(s4[i].w, pr[4 * i + 3], sb);
+              s0 = fmaf(s4[i].x, pr[4 * i + 0], s0);
+              s1 = fmaf(s4[i].y, pr[4 * i + 1], s1);
+              s2 = fmaf(s4[i].z, pr[4 * i + 2], s2);
+              s3 = fmaf(s4[i].w, pr[4 * i + 3], s3);
             }
-            kap = fmaf(sa + sb, qi[r] * kj[r], kap);
+            kap = fmaf((s0 + s1) + (s2 + s3), qi[r] * kj[r], kap);
           }
         } else {
           float tp[LDIM];
