@@ -233,6 +233,49 @@ oal_status oal_coeffs_backward(int n_q_heads, int d_h, int g_max, const int32_t*
                                const int32_t* group_map, const float* L, const float* da,
                                const float* db, const float* dC, float* dL, hipStream_t stream);
 
+/* ---- calibration of L by output matching ([OAL] App. B, Eq. 20) ------------ */
+
+/* Workspace of oal_calib_grad for n_pos sampled positions (0 if invalid). */
+size_t oal_calib_workspace_bytes(int n_q_heads, int n_pos);
+
+/* Loss and gradient of one calibration update for one sequence: per query head
+ * h, loss_h = (1 / (2 n_pos)) sum_{i in positions} ||y_i - y_ref_i||^2 (Eq. 20
+ * restricted to the sampled causal positions) with y the OAL output of the
+ * grouped kernel (L, g, eps as for oal_expand_coeffs), and dL_h its gradient with
+ * respect to L (lower triangle of the leading (G_h+1) block; zero elsewhere).
+ * The sampled rows are evaluated directly (each row's causal sum over its keys),
+ * not through a prefill.
+ *   q [n_q_heads][seq_len][d_h], k, v [n_kv_heads][seq_len][d_h / d_v]: one
+ *   sequence, fp32 or bf16; y_ref [n_q_heads][seq_len][d_v] fp32 (the softmax
+ *   output, e.g. from oal_softmax_attention); positions: device int32 [n_pos],
+ *   distinct, in 0..seq_len-1 (a position outside contributes nothing);
+ *   dL [n_q_heads][g_max+1][g_max+1], loss [n_q_heads] device fp32 out;
+ *   workspace >= oal_calib_workspace_bytes(), 256-byte aligned.  Deterministic. */
+oal_status oal_calib_grad(int n_q_heads, int n_kv_heads, int seq_len, int d_h, int d_v,
+                          oal_dtype in_dtype, const void* q, const void* k, const void* v,
+                          const float* y_ref, const int32_t* positions, int n_pos, int g_max,
+                          const int32_t* n_groups, const int32_t* group_map, const float* L,
+                          float eps, float* dL, float* loss, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream);
+
+/* One Adam update of L in place (Kingma and Ba, Algorithm 1; the calibration of
+ * [OAL] App. B uses Adam at lr 0.02 with the gradient norm clipped at 10): per
+ * head, the gradient dL is scaled to Euclidean norm <= clip_norm over the
+ * parameter entries (lower triangle of the leading (G_h+1) block), then
+ * m = beta1 m + (1 - beta1) g, v = beta2 v + (1 - beta2) g^2 and
+ * L -= lr (m / (1 - beta1^step)) / (sqrt(v / (1 - beta2^step)) + eps) on those
+ * entries; other entries are untouched.  L, dL, m, v: device fp32
+ * [n_q_heads][g_max+1][g_max+1] (m, v start at zero); step is 1-based. */
+oal_status oal_adam_step(int n_q_heads, int g_max, const int32_t* n_groups, float* L,
+                         const float* dL, float* m, float* v, int step, float lr, float beta1,
+                         float beta2, float eps, float clip_norm, hipStream_t stream);
+
+/* Per query head, the mean over batch, positions and channels of (y - y_ref)^2
+ * for y, y_ref [batch][n_q_heads][seq_len][d_v] fp32: the validation error of the
+ * calibration (and the MSE of [OAL] App. C, Eq. 21, per head). */
+oal_status oal_output_mse(int batch, int n_q_heads, int seq_len, int d_v, const float* y,
+                          const float* y_ref, float* mse, hipStream_t stream);
+
 /* Exact causal softmax attention, the reference OAL approximates ([OAL] §3:
  * y_i = sum_{j<=i} exp(s_ij) v_j / sum_{j<=i} exp(s_ij), s_ij = q_i . k_j / sqrt(d_h),
  * query head h reading KV head h / (n_q_heads / n_kv_heads)); used for the

@@ -28,6 +28,7 @@ SOURCES = [
     "oal_state_mfma.hip",
     "oal_softmax.hip",
     "oal_backward.hip",
+    "oal_calib.hip",
 ]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")

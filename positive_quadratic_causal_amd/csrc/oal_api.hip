@@ -95,6 +95,17 @@ void prof_end(int slot, hipStream_t stream) {
 }
 
 // kernels' launchers (one per source file)
+size_t calib_workspace(int n_q_heads, int n_pos);
+oal_status launch_calib_grad(int n_q_heads, int n_kv_heads, int seq_len, oal_dtype in_dtype,
+                             const void* q, const void* k, const void* v, const float* y_ref,
+                             const int32_t* positions, int n_pos, int g_max,
+                             const int32_t* n_groups, const int32_t* group_map, const float* L,
+                             float eps, float* dL, float* loss, void* ws, hipStream_t stream);
+oal_status launch_adam(int n_q_heads, int g_max, const int32_t* n_groups, float* L, const float* dL,
+                       float* m, float* v, int t, float lr, float beta1, float beta2, float eps,
+                       float clip, hipStream_t stream);
+oal_status launch_output_mse(int batch, int n_q_heads, int seq_len, int d_v, const float* y,
+                             const float* y_ref, float* mse, hipStream_t stream);
 size_t backward_workspace(int batch, int n_q_heads, int n_kv_heads, int seq_len, int chunk);
 oal_status launch_backward(int batch, int n_q_heads, int n_kv_heads, int seq_len, int chunk,
                            oal_dtype in_dtype, const void* q, const void* k, const void* v,
@@ -429,6 +440,60 @@ oal_status oal_coeffs_backward(int n_q_heads, int d_h, int g_max, const int32_t*
   if (!n_groups || !group_map || !L || !da || !db || !dC || !dL)
     return set_error(OAL_ERR_INVALID_ARG, "null pointer argument");
   return launch_coeffs_backward(n_q_heads, g_max, n_groups, group_map, L, da, db, dC, dL, stream);
+}
+
+size_t oal_calib_workspace_bytes(int n_q_heads, int n_pos) {
+  if (n_q_heads < 1 || n_pos < 1) return 0;
+  return calib_workspace(n_q_heads, n_pos);
+}
+
+oal_status oal_calib_grad(int n_q_heads, int n_kv_heads, int seq_len, int d_h, int d_v,
+                          oal_dtype in_dtype, const void* q, const void* k, const void* v,
+                          const float* y_ref, const int32_t* positions, int n_pos, int g_max,
+                          const int32_t* n_groups, const int32_t* group_map, const float* L,
+                          float eps, float* dL, float* loss, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream) {
+  oal_status st = check_heads(1, n_q_heads, n_kv_heads, d_h, d_v);
+  if (st != OAL_OK) return st;
+  if (!valid_dtype(in_dtype)) return set_error(OAL_ERR_INVALID_ARG, "unknown dtype");
+  if (seq_len < 1) return set_error(OAL_ERR_INVALID_ARG, "seq_len must be >= 1 (got %d)", seq_len);
+  if (n_pos < 1) return set_error(OAL_ERR_INVALID_ARG, "n_pos must be >= 1 (got %d)", n_pos);
+  if (g_max < 1 || g_max > GMAX)
+    return set_error(OAL_ERR_UNSUPPORTED, "g_max must be in 1..%d (got %d)", GMAX, g_max);
+  if (!(eps > 0.0f)) return set_error(OAL_ERR_INVALID_ARG, "eps must be > 0 (got %g)", (double)eps);
+  if (!q || !k || !v || !y_ref || !positions || !n_groups || !group_map || !L || !dL || !loss)
+    return set_error(OAL_ERR_INVALID_ARG, "null pointer argument");
+  const size_t need = calib_workspace(n_q_heads, n_pos);
+  if (!workspace || workspace_bytes < need)
+    return set_error(OAL_ERR_INVALID_ARG, "workspace too small: need %zu bytes, got %zu", need,
+                     workspace ? workspace_bytes : (size_t)0);
+  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+    return set_error(OAL_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  return launch_calib_grad(n_q_heads, n_kv_heads, seq_len, in_dtype, q, k, v, y_ref, positions, n_pos,
+                           g_max, n_groups, group_map, L, eps, dL, loss, workspace, stream);
+}
+
+oal_status oal_adam_step(int n_q_heads, int g_max, const int32_t* n_groups, float* L,
+                         const float* dL, float* m, float* v, int step, float lr, float beta1,
+                         float beta2, float eps, float clip_norm, hipStream_t stream) {
+  if (n_q_heads < 1) return set_error(OAL_ERR_INVALID_ARG, "n_q_heads must be >= 1");
+  if (g_max < 1 || g_max > GMAX)
+    return set_error(OAL_ERR_UNSUPPORTED, "g_max must be in 1..%d (got %d)", GMAX, g_max);
+  if (step < 1) return set_error(OAL_ERR_INVALID_ARG, "step is 1-based (got %d)", step);
+  if (!(lr > 0.0f) || !(beta1 >= 0.0f && beta1 < 1.0f) || !(beta2 >= 0.0f && beta2 < 1.0f) ||
+      !(eps > 0.0f) || !(clip_norm > 0.0f))
+    return set_error(OAL_ERR_INVALID_ARG, "invalid optimiser settings");
+  if (!n_groups || !L || !dL || !m || !v) return set_error(OAL_ERR_INVALID_ARG, "null pointer argument");
+  return launch_adam(n_q_heads, g_max, n_groups, L, dL, m, v, step, lr, beta1, beta2, eps, clip_norm,
+                     stream);
+}
+
+oal_status oal_output_mse(int batch, int n_q_heads, int seq_len, int d_v, const float* y,
+                          const float* y_ref, float* mse, hipStream_t stream) {
+  if (batch < 1 || n_q_heads < 1 || seq_len < 1 || d_v < 1)
+    return set_error(OAL_ERR_INVALID_ARG, "sizes must be >= 1");
+  if (!y || !y_ref || !mse) return set_error(OAL_ERR_INVALID_ARG, "null pointer argument");
+  return launch_output_mse(batch, n_q_heads, seq_len, d_v, y, y_ref, mse, stream);
 }
 
 oal_status oal_softmax_attention(int batch, int n_q_heads, int n_kv_heads, int seq_len, int d_h,

@@ -69,6 +69,11 @@ def _load() -> ctypes.CDLL:
         "oal_prefill_backward": (c_int, [c_int] * 7 + [c_void] * 5 + [c_int] + [c_void] * 6
                                  + [c_void, c_size, c_void]),
         "oal_coeffs_backward": (c_int, [c_int, c_int, c_int] + [c_void] * 7 + [c_void]),
+        "oal_calib_workspace_bytes": (c_size, [c_int, c_int]),
+        "oal_calib_grad": (c_int, [c_int] * 6 + [c_void] * 5 + [c_int, c_int] + [c_void] * 3
+                           + [c_float] + [c_void] * 3 + [c_size, c_void]),
+        "oal_adam_step": (c_int, [c_int, c_int] + [c_void] * 5 + [c_int] + [c_float] * 5 + [c_void]),
+        "oal_output_mse": (c_int, [c_int] * 4 + [c_void] * 3 + [c_void]),
         "oal_decode_step": (c_int, [c_int, c_int, c_int, c_int, c_int, c_int, c_void, c_void,
                                     c_void, c_void, c_void, c_void, c_int, c_void]),
         "oal_softmax_attention": (c_int, [c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_void,
@@ -94,6 +99,7 @@ EXPORTED = ("oal_coeffs_bytes", "oal_expand_coeffs", "oal_dim_coeffs", "oal_stat
             "oal_state_tokens", "oal_state_export", "oal_prefill_workspace_bytes", "oal_prefill",
             "oal_prefill_dim_workspace_bytes", "oal_prefill_dim",
             "oal_prefill_backward_workspace_bytes", "oal_prefill_backward", "oal_coeffs_backward",
+            "oal_calib_workspace_bytes", "oal_calib_grad", "oal_adam_step", "oal_output_mse",
             "oal_decode_step", "oal_softmax_attention", "oal_profile_enable", "oal_profile_reset",
             "oal_profile_query",
             "oal_status_string", "oal_last_error")
@@ -346,6 +352,56 @@ def oal_coeffs_backward(n_groups: torch.Tensor, group_map: torch.Tensor, L: torc
     _check(_lib.oal_coeffs_backward(Hq, D_H, g_max, _ptr(n_groups), _ptr(group_map), _ptr(L),
                                     _ptr(da), _ptr(db), _ptr(dC), _ptr(dL), _stream(L)))
     return dL
+
+
+def oal_calib_workspace_bytes(n_q_heads: int, n_pos: int) -> int:
+    return int(_lib.oal_calib_workspace_bytes(n_q_heads, n_pos))
+
+
+def oal_calib_grad(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, y_ref: torch.Tensor,
+                   positions: torch.Tensor, n_groups: torch.Tensor, group_map: torch.Tensor,
+                   L: torch.Tensor, eps: float, dL: torch.Tensor | None = None,
+                   loss: torch.Tensor | None = None, workspace: torch.Tensor | None = None):
+    """One sequence: q [Hq, N, 64], k/v [Hkv, N, 64] (or with a leading batch of 1),
+    y_ref [Hq, N, 64] fp32, positions int32 [n_pos].  Returns (dL, loss)."""
+    if q.dim() == 4:
+        q, k, v = q[0], k[0], v[0]
+    if y_ref.dim() == 4:
+        y_ref = y_ref[0]
+    Hq, N, dh = q.shape
+    Hkv = k.shape[0]
+    n_pos = positions.numel()
+    g_max = L.shape[-1] - 1
+    assert positions.dtype == torch.int32 and y_ref.dtype == torch.float32
+    if dL is None:
+        dL = torch.empty_like(L)
+    if loss is None:
+        loss = torch.empty((Hq,), dtype=torch.float32, device=L.device)
+    if workspace is None:
+        workspace = alloc_workspace(oal_calib_workspace_bytes(Hq, n_pos), L.device)
+    _check(_lib.oal_calib_grad(Hq, Hkv, N, dh, v.shape[-1], _dtype_code(q), _ptr(q), _ptr(k), _ptr(v),
+                               _ptr(y_ref), _ptr(positions), n_pos, g_max, _ptr(n_groups),
+                               _ptr(group_map), _ptr(L), float(eps), _ptr(dL), _ptr(loss),
+                               _ptr(workspace), workspace.numel(), _stream(L)))
+    return dL, loss
+
+
+def oal_adam_step(n_groups: torch.Tensor, L: torch.Tensor, dL: torch.Tensor, m: torch.Tensor,
+                  v: torch.Tensor, step: int, lr: float = 0.02, beta1: float = 0.9,
+                  beta2: float = 0.999, eps: float = 1e-8, clip_norm: float = 10.0) -> None:
+    """In place on L, m, v (all [Hq, g+1, g+1] fp32)."""
+    _check(_lib.oal_adam_step(n_groups.shape[0], L.shape[-1] - 1, _ptr(n_groups), _ptr(L), _ptr(dL),
+                              _ptr(m), _ptr(v), int(step), float(lr), float(beta1), float(beta2),
+                              float(eps), float(clip_norm), _stream(L)))
+
+
+def oal_output_mse(y: torch.Tensor, y_ref: torch.Tensor, mse: torch.Tensor | None = None) -> torch.Tensor:
+    """y, y_ref [B, Hq, N, d_v] fp32; returns the per-head MSE [Hq]."""
+    B, Hq, N, dv = y.shape
+    if mse is None:
+        mse = torch.empty((Hq,), dtype=torch.float32, device=y.device)
+    _check(_lib.oal_output_mse(B, Hq, N, dv, _ptr(y), _ptr(y_ref), _ptr(mse), _stream(y)))
+    return mse
 
 
 def oal_decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, coeffs: torch.Tensor,

@@ -163,3 +163,25 @@ def test_backward_entries_sizes_and_checks():
     assert call(a19=ctypes.c_void_p(0x1010)) == 1  # misaligned workspace
     assert lib.oal_coeffs_backward(2, 64, 7, P, P, P, P, P, P, P, None) == 2
     assert lib.oal_coeffs_backward(2, 64, 6, P, P, None, P, P, P, P, None) == 1
+
+
+def test_calibration_entries_checks():
+    lib, oal = _lib()
+    assert lib.oal_calib_workspace_bytes(14, 32) >= 14 * 32 * 49 * 4
+    assert lib.oal_calib_workspace_bytes(0, 32) == 0
+    # Hq, Hkv, N, d_h, d_v, in_dt, q, k, v, y_ref, pos, n_pos, g_max, ng, gm, L, eps, dL, loss, ws, wsb, stream
+    ok = [14, 2, 100, 64, 64, 1, P, P, P, P, P, 32, 6, P, P, P, 1e-6, P, P, P, 1 << 30, None]
+    def call(**kw):
+        args = list(ok)
+        for i, x in kw.items():
+            args[int(i[1:])] = x
+        return lib.oal_calib_grad(*args)
+    assert call(a1=3) == 1            # Hq % Hkv
+    assert call(a11=0) == 1           # n_pos
+    assert call(a12=7) == 2           # g_max
+    assert call(a16=0.0) == 1         # eps
+    assert call(a9=None) == 1         # y_ref
+    assert call(a20=8) == 1           # workspace too small
+    assert lib.oal_adam_step(2, 6, P, P, P, P, P, 0, 0.02, 0.9, 0.999, 1e-8, 10.0, None) == 1   # step 0
+    assert lib.oal_adam_step(2, 6, P, P, P, P, P, 1, 0.02, 1.0, 0.999, 1e-8, 10.0, None) == 1   # beta1
+    assert lib.oal_output_mse(1, 2, 0, 64, P, P, P, None) == 1
