@@ -20,8 +20,10 @@ Recipe (also stated in the design doc):
 * streams: ``numpy.random.default_rng(SeedSequence([20261202, wid, kind, b, h]))``
   with kind 0 = structure (shared by the whole workload), 1 = q, 2 = k, 3 = v;
 * q/k/v are standard normal float32, multiplied per dimension by the head's
-  outlier scales, then rounded to bfloat16 (round to nearest even) for the
-  bf16 workloads;
+  outlier scales (U[8, 20] unless a workload sets another range; U[2.5, 4.5]
+  gives the outlier dims about 43 % of sum_r |q_r k_r|, near the 46-49 % of
+  [OAL] Table 4, and a score spread of about 3), then rounded to bfloat16
+  (round to nearest even) for the bf16 workloads;
 * L per query head: (G+1)x(G+1) lower triangular, N(0, 0.3^2) entries, diagonal
   replaced by |.| + 0.5, zero above the diagonal; eps = 1e-6;
 * groups are labelled 1..G, group 1 being the bulk of non-outlier dimensions;
@@ -57,6 +59,7 @@ class Workload:
     decode_steps: int = 0   # single-token steps after the prefill
     eps: float = 1e-6
     grouping: str = "qwen"  # "tiny", "qwen" (G = 4) or "llama" (G in 2..6)
+    outlier_scale: tuple = (8.0, 20.0)   # U[lo, hi] factor of the outlier dims of q and k
     d_h: int = D_H
     d_v: int = D_V
     chunks: tuple = (128,)
@@ -174,9 +177,9 @@ def structure(w: Workload) -> Structure:
                 n_out = int(max(int(np.sum(s)) for s in sizes.values()))
             O = rng.choice(d, size=n_out, replace=False)
             outliers.append(sorted(int(x) for x in O))
-            k_scale[kv, O] = rng.uniform(8.0, 20.0, size=n_out)
+            k_scale[kv, O] = rng.uniform(*w.outlier_scale, size=n_out)
             for h in heads:
-                q_scale[h, O] = rng.uniform(8.0, 20.0, size=n_out)
+                q_scale[h, O] = rng.uniform(*w.outlier_scale, size=n_out)
                 s = sizes[h]
                 G = len(s) + 1
                 n_groups[h] = G
@@ -224,7 +227,9 @@ def full_tensor(w: Workload, st: Structure, kind: int, t0: int = 0,
 
 def small_workload(wid: int, name: str, batch: int, n_q_heads: int, n_kv_heads: int,
                    seq_len: int, dtype: str, grouping: str = "llama",
-                   decode_steps: int = 0, eps: float = 1e-6) -> Workload:
+                   decode_steps: int = 0, eps: float = 1e-6,
+                   outlier_scale: tuple = (8.0, 20.0)) -> Workload:
     """Ad-hoc workload (edge cases, ragged sizes) with its own seed id."""
     return Workload(wid, name, batch, n_q_heads, n_kv_heads, seq_len, dtype,
-                    decode_steps=decode_steps, eps=eps, grouping=grouping)
+                    decode_steps=decode_steps, eps=eps, grouping=grouping,
+                    outlier_scale=outlier_scale)
