@@ -671,11 +671,33 @@ def cpu_baseline_variants(w):
                                 C[0].astype(np.float64))
     # a row's cost grows with its position; the evenly spread rows average it
     t_dim = (time.perf_counter() - t0) / len(rows) * w.seq_len * w.n_q_heads * w.batch
+    # the gradient oracle on 16 evenly spread rows of one head (loss on those rows)
+    from oracle import calib_oracle as K
+    rows16 = np.linspace(0, w.seq_len - 1, 16).astype(np.int64)
+    dy = np.random.default_rng(7).standard_normal((w.seq_len, 64))
+    ag, bg, Cg = O.expand_coeffs(st.L[0].astype(np.float64), st.group_map[0], int(st.n_groups[0]),
+                                 w.eps)
+    t0 = time.perf_counter()
+    O.causal_attention_dim_grad(q, k, v, ag, bg, Cg, dy, rows=rows16)
+    t_bwd = (time.perf_counter() - t0) / len(rows16) * w.seq_len * w.n_q_heads * w.batch
+    # one calibration update of one head (32 positions), scaled to all heads
+    pos32 = np.sort(np.random.default_rng(8).choice(w.seq_len, size=32, replace=False))
+    y_ref = np.zeros((w.seq_len, 64))
+    t0 = time.perf_counter()
+    K.output_match_loss_grad(q, k, v, y_ref, pos32, st.L[0].astype(np.float64), st.group_map[0],
+                             int(st.n_groups[0]), w.eps)
+    t_cal = (time.perf_counter() - t0) * w.n_q_heads
     return {"softmax": {"value": round(w.batch * w.seq_len / t_sm, 3), "unit": "tokens/s",
                         "sample": f"query head 0 of {w.name}, all rows; scaled to {w.n_q_heads} heads"},
             "prefill_dim": {"value": round(w.batch * w.seq_len / t_dim, 3), "unit": "tokens/s",
                             "sample": f"64 evenly spread rows of query head 0 of {w.name}; "
-                                      f"scaled to all rows and {w.n_q_heads} heads"}}
+                                      f"scaled to all rows and {w.n_q_heads} heads"},
+            "backward": {"value": round(w.batch * w.seq_len / t_bwd, 3), "unit": "tokens/s",
+                         "sample": f"gradient of 16 evenly spread rows of query head 0 of {w.name}; "
+                                   f"scaled to all rows and {w.n_q_heads} heads"},
+            "calibration": {"value": round(1.0 / t_cal, 4), "unit": "updates/s",
+                            "sample": f"one 32-position update of query head 0 of {w.name}; "
+                                      f"scaled to {w.n_q_heads} heads"}}
 
 
 def measured_peaks(device):
