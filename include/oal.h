@@ -233,6 +233,46 @@ oal_status oal_coeffs_backward(int n_q_heads, int d_h, int g_max, const int32_t*
                                const int32_t* group_map, const float* L, const float* da,
                                const float* db, const float* dC, float* dL, hipStream_t stream);
 
+/* ---- dimension grouping ([OAL] §3.1 Eq. 2; App. B Eq. 16-19) -------------- */
+
+/* Contribution scores of Eq. 2: for prompt p and query head h,
+ *   chi_prompt[p][h][r] = mean over the causal pairs j <= i of the prompt of
+ *                         |q_ir k_jr| / sqrt(d_h)     (k from the head's KV head),
+ * and chi[h][r] = the equal-weight mean over the prompts (chi may be NULL).
+ *   q [n_q_heads][total_tokens][d_h], k [n_kv_heads][total_tokens][d_h] (fp32 or
+ *   bf16): the prompts concatenated; prompt p is tokens offsets[p] ..
+ *   offsets[p+1]-1 (offsets: device int32 [n_prompts+1], non-decreasing; values
+ *   are clamped into 0..total_tokens, an empty prompt scores 0).  Linear in the
+ *   tokens (the pair sum is sum_i |q_ir| sum_{j<=i} |k_jr|), double accumulation. */
+oal_status oal_contribution_scores(int n_q_heads, int n_kv_heads, int n_prompts, int total_tokens,
+                                  int d_h, oal_dtype in_dtype, const void* q, const void* k,
+                                  const int32_t* offsets, float* chi_prompt, float* chi,
+                                  hipStream_t stream);
+
+/* Bootstrap tail-cut grouping of App. B from the per-prompt scores: per head the
+ * dimensions are ordered by increasing chi (stable), candidate cuts are
+ * k = max(1, d_h - ceil(alpha d_h)) .. d_h - 1, rho_k = chi_{pi_{k+1}} /
+ * max(chi_{pi_k}, eps) (Eq. 16), S_k = the fraction of the n_boot replicates with
+ * min over the upper side >= tau max(max over the lower side, eps) of the
+ * replicate's mean scores in that fixed order (Eq. 17-18); cuts with rho_k >= tau
+ * and S_k >= gamma are kept and, below g_min groups, unused candidates are added
+ * by descending (S_k, rho_k) (ties: smaller k first); labels per Eq. 19 (group 1
+ * = the low-contribution bulk).  The pages use alpha 0.25 / 0.5, tau 1.5,
+ * gamma 0.9 / 0.5, g_min 2, 1000 replicates of 40 prompts.
+ *   chi_prompt [n_prompts][n_q_heads][d_h] (from oal_contribution_scores),
+ *   n_prompts <= 256; boot_idx: device int32 [n_boot][n_prompts], the prompt
+ *   indices of every replicate, drawn with replacement by the caller (clamped to
+ *   0..n_prompts-1);
+ *   group_map [n_q_heads][d_h] (labels 1..G), n_groups [n_q_heads] int32 out;
+ *   support, gap [n_q_heads][d_h] float out (S_k, rho_k at the candidate k, 0
+ *   elsewhere), or NULL.  G is not capped: oal_expand_coeffs accepts G <= 6.
+ * Decisions are taken in double precision; deterministic. */
+oal_status oal_bootstrap_grouping(int n_q_heads, int n_prompts, int d_h, const float* chi_prompt,
+                                  int n_boot, const int32_t* boot_idx, float alpha, float tau,
+                                  float gamma, int g_min, float eps, int32_t* group_map,
+                                  int32_t* n_groups, float* support, float* gap,
+                                  hipStream_t stream);
+
 /* ---- calibration of L by output matching ([OAL] App. B, Eq. 20) ------------ */
 
 /* Workspace of oal_calib_grad for n_pos sampled positions (0 if invalid). */

@@ -29,6 +29,7 @@ SOURCES = [
     "oal_softmax.hip",
     "oal_backward.hip",
     "oal_calib.hip",
+    "oal_grouping.hip",
 ]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")

@@ -95,6 +95,14 @@ void prof_end(int slot, hipStream_t stream) {
 }
 
 // kernels' launchers (one per source file)
+oal_status launch_contrib(int n_q_heads, int n_kv_heads, int n_prompts, int total,
+                          oal_dtype in_dtype, const void* q, const void* k, const int32_t* offsets,
+                          float* chi_prompt, float* chi, hipStream_t stream);
+oal_status launch_grouping(int n_q_heads, int n_prompts, const float* chi_prompt, int n_boot,
+                           const int32_t* boot_idx, float alpha, float tau, float gamma, int g_min,
+                           float eps, int32_t* group_map, int32_t* n_groups, float* support,
+                           float* gap, hipStream_t stream);
+int grouping_max_prompts();
 size_t calib_workspace(int n_q_heads, int n_pos);
 oal_status launch_calib_grad(int n_q_heads, int n_kv_heads, int seq_len, oal_dtype in_dtype,
                              const void* q, const void* k, const void* v, const float* y_ref,
@@ -494,6 +502,41 @@ oal_status oal_output_mse(int batch, int n_q_heads, int seq_len, int d_v, const 
     return set_error(OAL_ERR_INVALID_ARG, "sizes must be >= 1");
   if (!y || !y_ref || !mse) return set_error(OAL_ERR_INVALID_ARG, "null pointer argument");
   return launch_output_mse(batch, n_q_heads, seq_len, d_v, y, y_ref, mse, stream);
+}
+
+oal_status oal_contribution_scores(int n_q_heads, int n_kv_heads, int n_prompts, int total_tokens,
+                                  int d_h, oal_dtype in_dtype, const void* q, const void* k,
+                                  const int32_t* offsets, float* chi_prompt, float* chi,
+                                  hipStream_t stream) {
+  if (n_q_heads < 1 || n_kv_heads < 1 || n_q_heads % n_kv_heads != 0)
+    return set_error(OAL_ERR_INVALID_ARG, "n_q_heads must be a positive multiple of n_kv_heads");
+  if (d_h != DH) return set_error(OAL_ERR_UNSUPPORTED, "only d_h = 64 is supported (got %d)", d_h);
+  if (!valid_dtype(in_dtype)) return set_error(OAL_ERR_INVALID_ARG, "unknown dtype");
+  if (n_prompts < 1 || total_tokens < 0)
+    return set_error(OAL_ERR_INVALID_ARG, "n_prompts must be >= 1 and total_tokens >= 0");
+  if (!q || !k || !offsets || !chi_prompt) return set_error(OAL_ERR_INVALID_ARG, "null pointer argument");
+  return launch_contrib(n_q_heads, n_kv_heads, n_prompts, total_tokens, in_dtype, q, k, offsets,
+                        chi_prompt, chi, stream);
+}
+
+oal_status oal_bootstrap_grouping(int n_q_heads, int n_prompts, int d_h, const float* chi_prompt,
+                                  int n_boot, const int32_t* boot_idx, float alpha, float tau,
+                                  float gamma, int g_min, float eps, int32_t* group_map,
+                                  int32_t* n_groups, float* support, float* gap,
+                                  hipStream_t stream) {
+  if (n_q_heads < 1) return set_error(OAL_ERR_INVALID_ARG, "n_q_heads must be >= 1");
+  if (d_h != DH) return set_error(OAL_ERR_UNSUPPORTED, "only d_h = 64 is supported (got %d)", d_h);
+  if (n_prompts < 1 || n_prompts > grouping_max_prompts())
+    return set_error(OAL_ERR_UNSUPPORTED, "n_prompts must be in 1..%d (got %d)", grouping_max_prompts(),
+                     n_prompts);
+  if (n_boot < 1) return set_error(OAL_ERR_INVALID_ARG, "n_boot must be >= 1 (got %d)", n_boot);
+  if (!(alpha > 0.0f && alpha <= 1.0f) || !(tau > 0.0f) || !(gamma >= 0.0f && gamma <= 1.0f) ||
+      g_min < 1 || !(eps > 0.0f))
+    return set_error(OAL_ERR_INVALID_ARG, "invalid grouping settings");
+  if (!chi_prompt || !boot_idx || !group_map || !n_groups)
+    return set_error(OAL_ERR_INVALID_ARG, "null pointer argument");
+  return launch_grouping(n_q_heads, n_prompts, chi_prompt, n_boot, boot_idx, alpha, tau, gamma, g_min,
+                         eps, group_map, n_groups, support, gap, stream);
 }
 
 oal_status oal_softmax_attention(int batch, int n_q_heads, int n_kv_heads, int seq_len, int d_h,

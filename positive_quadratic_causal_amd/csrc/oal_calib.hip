@@ -265,25 +265,39 @@ k_adam(int g_max, const int32_t* __restrict__ n_groups, float* __restrict__ L,
 }
 
 // Per head: sum over batch, positions and channels of (y - y_ref)^2, divided by
-// their count.
-__global__ void __launch_bounds__(256)
+// their count.  One 1024-thread block per head, float4 loads when d_v is a
+// multiple of 4, a fixed-order tree at the end (deterministic).
+constexpr int MSE_T = 1024;
+__global__ void __launch_bounds__(MSE_T)
 k_output_mse(int batch, int n_q_heads, int seq_len, int d_v, const float* __restrict__ y,
              const float* __restrict__ y_ref, float* __restrict__ mse) {
   const int h = blockIdx.x;
   const int tid = threadIdx.x;
-  __shared__ float s_red[256];
+  __shared__ float s_red[MSE_T];
   const size_t per = (size_t)seq_len * d_v;
-  float acc = 0.f;
+  float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
   for (int b = 0; b < batch; ++b) {
     const float* a = y + ((size_t)b * n_q_heads + h) * per;
     const float* r = y_ref + ((size_t)b * n_q_heads + h) * per;
-    for (size_t e = tid; e < per; e += 256) {
-      const float d = a[e] - r[e];
-      acc = fmaf(d, d, acc);
+    if ((d_v & 3) == 0) {
+      const float4* a4 = reinterpret_cast<const float4*>(a);
+      const float4* r4 = reinterpret_cast<const float4*>(r);
+      for (size_t e = tid; e < per / 4; e += MSE_T) {
+        const float4 x = a4[e], z = r4[e];
+        a0 = fmaf(x.x - z.x, x.x - z.x, a0);
+        a1 = fmaf(x.y - z.y, x.y - z.y, a1);
+        a2 = fmaf(x.z - z.z, x.z - z.z, a2);
+        a3 = fmaf(x.w - z.w, x.w - z.w, a3);
+      }
+    } else {
+      for (size_t e = tid; e < per; e += MSE_T) {
+        const float d = a[e] - r[e];
+        a0 = fmaf(d, d, a0);
+      }
     }
   }
-  s_red[tid] = acc;
-  for (int stride = 128; stride > 0; stride >>= 1) {
+  s_red[tid] = (a0 + a1) + (a2 + a3);
+  for (int stride = MSE_T / 2; stride > 0; stride >>= 1) {
     __syncthreads();
     if (tid < stride) s_red[tid] += s_red[tid + stride];
   }
@@ -342,7 +356,7 @@ oal_status launch_adam(int n_q_heads, int g_max, const int32_t* n_groups, float*
 oal_status launch_output_mse(int batch, int n_q_heads, int seq_len, int d_v, const float* y,
                              const float* y_ref, float* mse, hipStream_t stream) {
   ProfScope ps("k_output_mse", stream);
-  hipLaunchKernelGGL(k_output_mse, dim3(n_q_heads), dim3(256), 0, stream, batch, n_q_heads, seq_len,
+  hipLaunchKernelGGL(k_output_mse, dim3(n_q_heads), dim3(MSE_T), 0, stream, batch, n_q_heads, seq_len,
                      d_v, y, y_ref, mse);
   return check_launch("k_output_mse");
 }

@@ -69,6 +69,9 @@ def _load() -> ctypes.CDLL:
         "oal_prefill_backward": (c_int, [c_int] * 7 + [c_void] * 5 + [c_int] + [c_void] * 6
                                  + [c_void, c_size, c_void]),
         "oal_coeffs_backward": (c_int, [c_int, c_int, c_int] + [c_void] * 7 + [c_void]),
+        "oal_contribution_scores": (c_int, [c_int] * 6 + [c_void] * 5 + [c_void]),
+        "oal_bootstrap_grouping": (c_int, [c_int] * 3 + [c_void, c_int, c_void] + [c_float] * 3
+                                   + [c_int, c_float] + [c_void] * 4 + [c_void]),
         "oal_calib_workspace_bytes": (c_size, [c_int, c_int]),
         "oal_calib_grad": (c_int, [c_int] * 6 + [c_void] * 5 + [c_int, c_int] + [c_void] * 3
                            + [c_float] + [c_void] * 3 + [c_size, c_void]),
@@ -100,6 +103,7 @@ EXPORTED = ("oal_coeffs_bytes", "oal_expand_coeffs", "oal_dim_coeffs", "oal_stat
             "oal_prefill_dim_workspace_bytes", "oal_prefill_dim",
             "oal_prefill_backward_workspace_bytes", "oal_prefill_backward", "oal_coeffs_backward",
             "oal_calib_workspace_bytes", "oal_calib_grad", "oal_adam_step", "oal_output_mse",
+            "oal_contribution_scores", "oal_bootstrap_grouping",
             "oal_decode_step", "oal_softmax_attention", "oal_profile_enable", "oal_profile_reset",
             "oal_profile_query",
             "oal_status_string", "oal_last_error")
@@ -352,6 +356,38 @@ def oal_coeffs_backward(n_groups: torch.Tensor, group_map: torch.Tensor, L: torc
     _check(_lib.oal_coeffs_backward(Hq, D_H, g_max, _ptr(n_groups), _ptr(group_map), _ptr(L),
                                     _ptr(da), _ptr(db), _ptr(dC), _ptr(dL), _stream(L)))
     return dL
+
+
+def oal_contribution_scores(q: torch.Tensor, k: torch.Tensor, offsets: torch.Tensor,
+                            want_mean: bool = True):
+    """q [Hq, T, 64], k [Hkv, T, 64] (prompts concatenated along T), offsets int32
+    [P+1].  Returns (chi_prompt [P, Hq, 64], chi [Hq, 64] or None)."""
+    Hq, T, dh = q.shape
+    P = offsets.numel() - 1
+    assert offsets.dtype == torch.int32
+    chi_p = torch.empty((P, Hq, dh), dtype=torch.float32, device=q.device)
+    chi = torch.empty((Hq, dh), dtype=torch.float32, device=q.device) if want_mean else None
+    _check(_lib.oal_contribution_scores(Hq, k.shape[0], P, T, dh, _dtype_code(q), _ptr(q), _ptr(k),
+                                        _ptr(offsets), _ptr(chi_p), _ptr(chi), _stream(q)))
+    return chi_p, chi
+
+
+def oal_bootstrap_grouping(chi_prompt: torch.Tensor, boot_idx: torch.Tensor, alpha: float = 0.25,
+                           tau: float = 1.5, gamma: float = 0.9, g_min: int = 2,
+                           eps: float = 1e-12, want_stats: bool = True):
+    """chi_prompt [P, Hq, 64], boot_idx int32 [B, P].  Returns (group_map int32
+    [Hq, 64], n_groups int32 [Hq], support [Hq, 64], gap [Hq, 64])."""
+    P, Hq, dh = chi_prompt.shape
+    assert boot_idx.dtype == torch.int32 and boot_idx.shape[1] == P
+    dev = chi_prompt.device
+    gm = torch.empty((Hq, dh), dtype=torch.int32, device=dev)
+    ng = torch.empty((Hq,), dtype=torch.int32, device=dev)
+    sup = torch.empty((Hq, dh), dtype=torch.float32, device=dev) if want_stats else None
+    gap = torch.empty((Hq, dh), dtype=torch.float32, device=dev) if want_stats else None
+    _check(_lib.oal_bootstrap_grouping(Hq, P, dh, _ptr(chi_prompt), boot_idx.shape[0], _ptr(boot_idx),
+                                       float(alpha), float(tau), float(gamma), int(g_min), float(eps),
+                                       _ptr(gm), _ptr(ng), _ptr(sup), _ptr(gap), _stream(chi_prompt)))
+    return gm, ng, sup, gap
 
 
 def oal_calib_workspace_bytes(n_q_heads: int, n_pos: int) -> int:

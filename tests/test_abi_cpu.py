@@ -185,3 +185,25 @@ def test_calibration_entries_checks():
     assert lib.oal_adam_step(2, 6, P, P, P, P, P, 0, 0.02, 0.9, 0.999, 1e-8, 10.0, None) == 1   # step 0
     assert lib.oal_adam_step(2, 6, P, P, P, P, P, 1, 0.02, 1.0, 0.999, 1e-8, 10.0, None) == 1   # beta1
     assert lib.oal_output_mse(1, 2, 0, 64, P, P, P, None) == 1
+
+
+def test_grouping_entries_checks():
+    lib, oal = _lib()
+    # Hq, Hkv, P, T, d_h, in_dt, q, k, offsets, chi_p, chi, stream
+    assert lib.oal_contribution_scores(6, 4, 3, 10, 64, 1, P, P, P, P, P, None) == 1   # Hq % Hkv
+    assert lib.oal_contribution_scores(6, 2, 0, 10, 64, 1, P, P, P, P, P, None) == 1   # no prompts
+    assert lib.oal_contribution_scores(6, 2, 3, 10, 32, 1, P, P, P, P, P, None) == 2   # d_h
+    assert lib.oal_contribution_scores(6, 2, 3, 10, 64, 1, P, None, P, P, P, None) == 1
+    # Hq, P, d_h, chi_p, B, boot, alpha, tau, gamma, g_min, eps, gm, ng, sup, gap, stream
+    ok = [6, 40, 64, P, 1000, P, 0.25, 1.5, 0.9, 2, 1e-12, P, P, None, None, None]
+    def call(**kw):
+        args = list(ok)
+        for i, x in kw.items():
+            args[int(i[1:])] = x
+        return lib.oal_bootstrap_grouping(*args)
+    assert call(a1=257) == 2          # more prompts than the kernel stages
+    assert call(a4=0) == 1            # no replicates
+    assert call(a6=0.0) == 1          # alpha
+    assert call(a8=1.5) == 1          # gamma
+    assert call(a9=0) == 1            # g_min
+    assert call(a12=None) == 1        # n_groups
