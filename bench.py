@@ -415,6 +415,66 @@ def bench_calibration(oal, device, max_updates=1000):
     return out
 
 
+def bench_grouping(oal, device, reps=20):
+    """Dimension grouping of a Qwen2.5-0.5B-shaped layer ([OAL] App. B settings:
+    40 calibration prompts, 1000 bootstrap replicates, tau 1.5, G_min 2, (alpha,
+    gamma) = (0.25, 0.9)): contribution scores of every head over the prompts,
+    then the grouping; prompt lengths 32..159 tokens (the pages' prompts are short)."""
+    import numpy as np
+    import torch
+
+    from positive_quadratic_causal_amd import synth
+    w = synth.small_workload(970, "Qwen2.5-0.5B-shaped layer 14/2, 40 prompts of 32-159 tokens, "
+                             "outlier scale U[2.5, 4.5]", 40, 14, 2, 1, "bf16", grouping="qwen",
+                             outlier_scale=(2.5, 4.5))
+    st = synth.structure(w)
+    lengths = list(np.random.default_rng(971).integers(32, 160, size=40))
+    q = np.concatenate([np.stack([synth.head_tensor(w, st, synth.KIND_Q, b, h, n)
+                                  for h in range(14)]) for b, n in enumerate(lengths)], axis=1)
+    k = np.concatenate([np.stack([synth.head_tensor(w, st, synth.KIND_K, b, h, n)
+                                  for h in range(2)]) for b, n in enumerate(lengths)], axis=1)
+    qd = torch.from_numpy(q).to(device).to(torch.bfloat16)
+    kd = torch.from_numpy(k).to(device).to(torch.bfloat16)
+    off = torch.from_numpy(np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)).to(device)
+    boot = torch.from_numpy(np.random.default_rng(972).integers(0, 40, size=(1000, 40))
+                            .astype(np.int32)).to(device)
+
+    def step():
+        chi_p, _ = oal.oal_contribution_scores(qd, kd, off, want_mean=False)
+        return oal.oal_bootstrap_grouping(chi_p, boot, 0.25, 1.5, 0.9, 2)
+
+    for _ in range(3):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        gm, ng, _, _ = step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / reps
+    oal.oal_profile_reset()
+    oal.oal_profile_enable(True)
+    for _ in range(reps):
+        step()
+    torch.cuda.synchronize()
+    oal.oal_profile_enable(False)
+    kt = kernel_times(oal, ["k_contrib", "k_group"])
+    ngs = ng.cpu().numpy()
+    recovered = sum(set(np.nonzero(gm[h].cpu().numpy() >= 2)[0]) == set(st.outliers[h // 7])
+                    for h in range(14))
+    tokens = int(sum(lengths))
+    cbytes = 14 * tokens * 64 * 2 + 2 * tokens * 64 * 2 + 40 * 14 * 64 * 4
+    kc = kt["k_contrib"]["avg_ms"]
+    return {"workload": w.name, "ms_per_layer": round(ms, 5), "tokens": tokens,
+            "groups_per_head": [int(x) for x in ngs],
+            "heads_with_outlier_set_recovered": int(recovered),
+            "roofline_k_contrib": {"bound": "hbm", "achieved": round(cbytes / (kc * 1e-3) / 1e9, 2),
+                                   "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                   "frac": round(cbytes / (kc * 1e-3) / 1e9 / PEAK_HBM_GBS, 5),
+                                   "algorithmic_bytes": cbytes,
+                                   "note": "one pass over q and k; latency-bound at this size"},
+            "kernels_ms": {k_: round(v["avg_ms"], 5) for k_, v in kt.items()}}
+
+
 def fidelity_report(oal, w, chunk, device):
     """[OAL] App. C, Eqs. 21-22: MSE and RelMSE of the OAL output against exact
     softmax attention on the same synthetic inputs, one sequence = all heads of a
@@ -687,6 +747,14 @@ def cpu_baseline_variants(w):
     K.output_match_loss_grad(q, k, v, y_ref, pos32, st.L[0].astype(np.float64), st.group_map[0],
                              int(st.n_groups[0]), w.eps)
     t_cal = (time.perf_counter() - t0) * w.n_q_heads
+    # grouping of one head: 40 prompts of 96 tokens, pair-by-pair scores, 1000 replicates
+    from oracle import grouping_oracle as GR
+    rg = np.random.default_rng(9)
+    t0 = time.perf_counter()
+    chi_p = np.stack([GR.contribution_prompt(q[96 * p:96 * p + 96], k[96 * p:96 * p + 96])
+                      for p in range(20)] * 2)
+    GR.group_head(chi_p, rg.integers(0, 40, size=(1000, 40)), 0.25, 1.5, 0.9, 2)
+    t_grp = (time.perf_counter() - t0) * w.n_q_heads
     return {"softmax": {"value": round(w.batch * w.seq_len / t_sm, 3), "unit": "tokens/s",
                         "sample": f"query head 0 of {w.name}, all rows; scaled to {w.n_q_heads} heads"},
             "prefill_dim": {"value": round(w.batch * w.seq_len / t_dim, 3), "unit": "tokens/s",
@@ -695,6 +763,9 @@ def cpu_baseline_variants(w):
             "backward": {"value": round(w.batch * w.seq_len / t_bwd, 3), "unit": "tokens/s",
                          "sample": f"gradient of 16 evenly spread rows of query head 0 of {w.name}; "
                                    f"scaled to all rows and {w.n_q_heads} heads"},
+            "grouping": {"value": round(1.0 / t_grp, 4), "unit": "layers/s",
+                         "sample": "one head: scores of 20 prompts of 96 tokens (each used twice), "
+                                   "1000 replicates; scaled to 14 heads"},
             "calibration": {"value": round(1.0 / t_cal, 4), "unit": "updates/s",
                             "sample": f"one 32-position update of query head 0 of {w.name}; "
                                       f"scaled to {w.n_q_heads} heads"}}
@@ -750,7 +821,7 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-softmax", action="store_true")
     ap.add_argument("--only", choices=["prefill", "decode", "softmax", "prefill_dim", "backward",
-                                                "calibration"], default=None,
+                                                "calibration", "grouping"], default=None,
                     help="time one leg only (used to profile each workload on its own)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="after the legs, copy MIB MiB 5 times (reference for HBM counters)")
@@ -782,6 +853,9 @@ def main() -> int:
     if args.only == "backward":
         res = bench_backward(oal, synth.WORKLOADS[1], 64, args.steps, args.warmup, device)
         print(json.dumps({"metric": METRIC, "backward": res}), flush=True)
+        return 0
+    if args.only == "grouping":
+        print(json.dumps({"metric": METRIC, "grouping": bench_grouping(oal, device)}), flush=True)
         return 0
     if args.only == "calibration":
         print(json.dumps({"metric": METRIC, "calibration": bench_calibration(oal, device)}), flush=True)
@@ -861,6 +935,8 @@ def main() -> int:
         log("backward (dq, dk, dv, coefficient gradients): Qwen-shaped N = 2048")
         result["backward"] = bench_backward(oal, synth.WORKLOADS[1], 64, max(3, args.steps // 4), 2,
                                             device)
+        log("dimension grouping: contribution scores and bootstrap cuts")
+        result["grouping"] = bench_grouping(oal, device)
         log("calibration of L by output matching (Taylor and perturbed starts)")
         result["calibration"] = bench_calibration(oal, device)
         log("fidelity: OAL vs softmax, MSE / RelMSE")

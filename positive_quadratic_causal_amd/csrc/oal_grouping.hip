@@ -20,7 +20,7 @@
 namespace oal {
 
 namespace {
-constexpr int GT = 256;          // threads of the grouping kernel
+constexpr int GT = 1024;         // threads of the grouping kernel (16 waves)
 constexpr int MAX_PROMPTS = 256; // per-prompt scores of one head staged in LDS
 }  // namespace
 
@@ -59,7 +59,21 @@ k_contrib_mean(int n_q_heads, int n_prompts, const float* __restrict__ chi_promp
   chi[(size_t)h * DH + r] = (float)(s / n_prompts);
 }
 
-// One block per head: order, gaps, bootstrap support, cuts and labels.
+// double-precision wave shuffles (two 32-bit halves)
+__device__ __forceinline__ double shfl_up_d(double x, int d) {
+  const int lo = __shfl_up(__double2loint(x), d, 64), hi = __shfl_up(__double2hiint(x), d, 64);
+  return __hiloint2double(hi, lo);
+}
+__device__ __forceinline__ double shfl_down_d(double x, int d) {
+  const int lo = __shfl_down(__double2loint(x), d, 64), hi = __shfl_down(__double2hiint(x), d, 64);
+  return __hiloint2double(hi, lo);
+}
+
+// One block per head: order, gaps, bootstrap support, cuts and labels.  The
+// bootstrap runs one replicate per wave at a time, lane u holding the u-th
+// dimension of the fixed order pi: the replicate's score sums, a prefix maximum
+// and a suffix minimum by wave scans, and lane k counts the replicates that keep
+// cut k (no atomics; the per-wave counts are added in wave order).
 __global__ void __launch_bounds__(GT)
 k_group(int n_q_heads, int n_prompts, const float* __restrict__ chi_prompt, int n_boot,
         const int32_t* __restrict__ boot_idx, float alpha, float tau, float gamma, int g_min,
@@ -67,16 +81,17 @@ k_group(int n_q_heads, int n_prompts, const float* __restrict__ chi_prompt, int 
         float* __restrict__ support_out, float* __restrict__ gap_out) {
   const int h = blockIdx.x;
   const int tid = threadIdx.x;
-  __shared__ float s_cp[MAX_PROMPTS][DH];   // this head's per-prompt scores
+  const int lane = tid & 63, wave = tid >> 6;
+  __shared__ float s_cp[MAX_PROMPTS][DH];   // this head's per-prompt scores, then in pi order
   __shared__ double s_chi[DH];
   __shared__ int s_pi[DH];
   __shared__ double s_rho[DH];
+  __shared__ int s_wcnt[GT / 64][DH];
   __shared__ int s_cnt[DH];
   const int m = (int)ceil((double)alpha * DH);
   const int kmin = max(1, DH - m);           // candidates kmin .. DH-1
   for (int i = tid; i < n_prompts * DH; i += GT)
     s_cp[i / DH][i % DH] = chi_prompt[((size_t)(i / DH) * n_q_heads + h) * DH + i % DH];
-  if (tid < DH) s_cnt[tid] = 0;
   __syncthreads();
   if (tid < DH) {
     double s = 0.0;
@@ -93,35 +108,50 @@ k_group(int n_q_heads, int n_prompts, const float* __restrict__ chi_prompt, int 
   __syncthreads();
   if (tid < DH)
     s_rho[tid] = tid >= kmin ? s_chi[s_pi[tid]] / fmax(s_chi[s_pi[tid - 1]], (double)eps) : 0.0;
-
-  // bootstrap: replicate b's mean scores in the fixed order pi, then the cut test
-  // min(upper) >= tau * max(max(lower), eps) for every candidate
-  for (int b = tid; b < n_boot; b += GT) {
-    double ord[DH];
+  {   // permute every prompt's row into pi order (through registers, one pass)
+    constexpr int PER = MAX_PROMPTS * DH / GT;
+    float tmp[PER];
 #pragma unroll
-    for (int t = 0; t < DH; ++t) ord[t] = 0.0;
+    for (int e = 0; e < PER; ++e) {
+      const int i = tid + e * GT;
+      tmp[e] = i < n_prompts * DH ? s_cp[i / DH][s_pi[i % DH]] : 0.f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      const int i = tid + e * GT;
+      if (i < n_prompts * DH) s_cp[i / DH][i % DH] = tmp[e];
+    }
+  }
+  __syncthreads();
+
+  // cut k at lane k: lower side = lanes 0..k-1, upper side = lanes k..63; both
+  // sums carry the factor 1 / n_prompts, which the ratio test does not need
+  int cnt = 0;
+  const double tau_d = tau, floor_d = (double)eps * n_prompts;
+  for (int b = wave; b < n_boot; b += GT / 64) {
     const int32_t* idx = boot_idx + (size_t)b * n_prompts;
+    double sum = 0.0;
     for (int t = 0; t < n_prompts; ++t) {
       const int p = min(max(idx[t], 0), n_prompts - 1);
-#pragma unroll
-      for (int u = 0; u < DH; ++u) ord[u] += s_cp[p][s_pi[u]];
+      sum += s_cp[p][lane];
     }
-    double sufmin[DH];
-    double run = ord[DH - 1];
-#pragma unroll
-    for (int u = DH - 1; u >= 0; --u) {
-      run = fmin(run, ord[u]);
-      sufmin[u] = run;
+    double pmax = sum, smin = sum;
+    for (int d = 1; d < 64; d <<= 1) {
+      const double up = shfl_up_d(pmax, d);
+      const double dn = shfl_down_d(smin, d);
+      if (lane >= d) pmax = fmax(pmax, up);
+      if (lane + d < 64) smin = fmin(smin, dn);
     }
-    double pmax = ord[0];
-#pragma unroll
-    for (int kk = 1; kk < DH; ++kk) {
-      // lower side pi_1..pi_k = ord[0..kk-1], upper side ord[kk..]; both sums carry
-      // the same factor 1 / n_prompts, which the ratio test does not need
-      if (kk >= kmin && sufmin[kk] >= (double)tau * fmax(pmax, (double)eps * n_prompts))
-        atomicAdd(&s_cnt[kk], 1);   // integer counts: exact in any order
-      pmax = fmax(pmax, ord[kk]);
-    }
+    const double lower = shfl_up_d(pmax, 1);   // max over lanes 0..lane-1
+    if (lane >= kmin && smin >= tau_d * fmax(lower, floor_d)) ++cnt;
+  }
+  s_wcnt[wave][lane] = cnt;
+  __syncthreads();
+  if (tid < DH) {
+    int c = 0;
+    for (int wv = 0; wv < GT / 64; ++wv) c += s_wcnt[wv][tid];
+    s_cnt[tid] = c;
   }
   __syncthreads();
 
