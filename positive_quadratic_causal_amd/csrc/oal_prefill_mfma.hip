@@ -565,6 +565,10 @@ k_readout_mfma(int n_q_heads, int n_kv_heads, int seq_len, int n_chunks, int n_h
       qr[nt][3] = hi[1];
     }
     const uint8_t* mgc = mgh + 32 * c;
+    // the 16 products of the half-slab at raised wave priority, so that a wave
+    // with its products ready issues them ahead of the co-resident waves' loads
+    // and feature arithmetic (about 1 % on this kernel, measured)
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       // qhat = q_t M_{g(r), g(t)} / d_h (scaled), recomputed when g(r) changes
@@ -583,6 +587,7 @@ k_readout_mfma(int n_q_heads, int n_kv_heads, int seq_len, int n_chunks, int n_h
         acc[mt][1] = mfma32h(af[i][mt], f1, acc[mt][1]);
       }
     }
+    __builtin_amdgcn_s_setprio(0);
   };
   // the merged half-slab of t-block c: K-step i holds rows 16 c + 8 + 2 i + half
   // against t = 16 c + 8 .. 16 c + 15 in both lane halves (multiplicity 1)

@@ -127,7 +127,9 @@ k_scan_vec(int n_chunks, float* __restrict__ ws, float* __restrict__ state) {
 // DIM: the record is dimension-specific (intra-chunk kappa from b', c');
 // otherwise it is grouped, and a record with NG = 0 (dimension-specific) makes
 // every output NaN instead of a silently wrong value.
-template <typename T, typename O, bool DIM>
+// SPLIT = 2: two threads per query (thread 2 i + h) split its features and its
+// pairs by parity and add their halves of u~_i through LDS at the end.
+template <typename T, typename O, bool DIM, int SPLIT>
 __global__ void __launch_bounds__(256)
 k_readout_vec(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunks,
               const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
@@ -139,6 +141,8 @@ k_readout_vec(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunk
   const int kv = hq / rep;
   const int unit = b * n_kv_heads + kv;
   const int tid = threadIdx.x;
+  const int nthr = blockDim.x;                // SPLIT * chunk
+  const int qx = tid / SPLIT, half = tid % SPLIT;
   const int t0 = c * chunk;
   const int clen = min(chunk, seq_len - t0);
 
@@ -158,34 +162,34 @@ k_readout_vec(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunk
   const float eps = rec[OAL_COEF_EPS];
   const int G = reinterpret_cast<const int32_t*>(rec)[OAL_COEF_NG];
 
-  for (int i = tid; i < chunk * DH; i += blockDim.x) {
+  for (int i = tid; i < chunk * DH; i += nthr) {
     int ii = i / DH, d = i % DH;
     s_q[ii * (DH + 1) + d] =
         ii < clen ? Elem<T>::load(q, (((size_t)b * n_q_heads + hq) * seq_len + t0 + ii) * DH + d) : 0.f;
   }
   if constexpr (DIM) {
-    for (int i = tid; i < DH; i += blockDim.x) s_ell[i] = rec[OAL_COEF_BP + i];
-    for (int i = tid; i < DH * DH; i += blockDim.x) s_cm[i] = rec[OAL_COEF_CM + i];
+    for (int i = tid; i < DH; i += nthr) s_ell[i] = rec[OAL_COEF_BP + i];
+    for (int i = tid; i < DH * DH; i += nthr) s_cm[i] = rec[OAL_COEF_CM + i];
   } else {
-    for (int i = tid; i < LDIM * DH; i += blockDim.x) s_ell[i] = rec[OAL_COEF_ELL + i];
+    for (int i = tid; i < LDIM * DH; i += nthr) s_ell[i] = rec[OAL_COEF_ELL + i];
     if (tid < LDIM) s_L0[tid] = rec[OAL_COEF_L + tid];   // row 0 of L: L_{0,p}
   }
   // the pad columns W..WP-1 of the H and u rows are never written again
-  for (int i = tid; i < 32 * (WP - W); i += blockDim.x) s_H[(i / (WP - W)) * WP + W + i % (WP - W)] = 0.f;
-  for (int i = tid; i < TB * (WP - W); i += blockDim.x) s_u[(i / (WP - W)) * WP + W + i % (WP - W)] = 0.f;
+  for (int i = tid; i < 32 * (WP - W); i += nthr) s_H[(i / (WP - W)) * WP + W + i % (WP - W)] = 0.f;
+  for (int i = tid; i < TB * (WP - W); i += nthr) s_u[(i / (WP - W)) * WP + W + i % (WP - W)] = 0.f;
   __syncthreads();
 
   float acc[WP];
 #pragma unroll
   for (int w = 0; w < WP; ++w) acc[w] = 0.f;
-  const bool active = tid < clen;
-  const float* qi = s_q + tid * (DH + 1);
+  const bool active = qx < clen;
+  const float* qi = s_q + qx * (DH + 1);
 
   // inter-chunk part: phi_q(q_i)^T H_{<c}
   const float* Hc = ws + ((size_t)unit * n_chunks + c) * STATE_FLOATS;
   for (int f0 = 0; f0 < DCAN; f0 += 32) {
     __syncthreads();
-    for (int i = tid; i < 32 * W; i += blockDim.x) {
+    for (int i = tid; i < 32 * W; i += nthr) {
       int w = i / 32, ff = i % 32;
       s_H[ff * WP + w] = Hc[(size_t)w * DS + f0 + ff];   // f0 + 31 < DS always
     }
@@ -200,7 +204,7 @@ k_readout_vec(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunk
     __syncthreads();
     if (active) {
       const int nf = min(32, DCAN - f0);
-      for (int ff = 0; ff < nf; ++ff) {
+      for (int ff = half; ff < nf; ff += SPLIT) {
         int f = f0 + ff;
         float phi;
         if (f == 0) phi = s_cf[ff];
@@ -219,7 +223,7 @@ k_readout_vec(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunk
   for (int j0 = 0; j0 < clen; j0 += TB) {
     const int nj = min(TB, clen - j0);
     __syncthreads();
-    for (int i = tid; i < TB * DH; i += blockDim.x) {
+    for (int i = tid; i < TB * DH; i += nthr) {
       int jj = i / DH, d = i % DH;
       float kv_ = 0.f, vv_ = 0.f;
       if (jj < nj) {
@@ -229,11 +233,11 @@ k_readout_vec(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunk
       s_k[jj * (DH + 1) + d] = kv_;
       s_u[jj * WP + d] = vv_;
     }
-    for (int jj = tid; jj < TB; jj += blockDim.x) s_u[jj * WP + DV] = 1.f;
+    for (int jj = tid; jj < TB; jj += nthr) s_u[jj * WP + DV] = 1.f;
     __syncthreads();
     if (active) {
-      const int jmax = min(nj, tid - j0 + 1);
-      for (int jj = 0; jj < jmax; ++jj) {
+      const int jmax = min(nj, qx - j0 + 1);
+      for (int jj = half; jj < jmax; jj += SPLIT) {
         const float* kj = s_k + jj * (DH + 1);
         float kap;
         if constexpr (DIM) {
@@ -277,9 +281,21 @@ k_readout_vec(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunk
     }
   }
 
+  if (SPLIT == 2) {   // half 1's share of u~_i through LDS (the query rows are done with)
+    float* xrow = s_q + qx * (DH + 1);
+    __syncthreads();
+    if (half == 1) {
+#pragma unroll
+      for (int w = 0; w < W; ++w) xrow[w] = acc[w];
+    }
+    __syncthreads();
+    if (half == 1) return;
+#pragma unroll
+    for (int w = 0; w < W; ++w) acc[w] += xrow[w];
+  }
   if (active) {
     const float inv = (DIM || G >= 1) ? 1.0f / acc[DV] : __builtin_nanf("");
-    O* yo = y + (((size_t)b * n_q_heads + hq) * seq_len + t0 + tid) * DV;
+    O* yo = y + (((size_t)b * n_q_heads + hq) * seq_len + t0 + qx) * DV;
 #pragma unroll
     for (int w = 0; w < DV; ++w) Elem<O>::store(yo, w, acc[w] * inv);
   }
@@ -318,13 +334,20 @@ static oal_status prefill_vec_typed(int batch, int n_q_heads, int n_kv_heads, in
   if (st != OAL_OK) return st;
   size_t smem = sizeof(float) * ((size_t)chunk * (DH + 1) + 32 * WP + 32 + TB * (DH + 1) + TB * WP +
                                  (DIM ? DH + DH * DH : LDIM * DH + LDIM));
-  if (hipFuncSetAttribute(reinterpret_cast<const void*>(&k_readout_vec<T, O, DIM>),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem) != hipSuccess)
+  const bool split = chunk <= 128;   // 2 threads per query up to 256 threads per block
+  const void* fn = split ? reinterpret_cast<const void*>(&k_readout_vec<T, O, DIM, 2>)
+                         : reinterpret_cast<const void*>(&k_readout_vec<T, O, DIM, 1>);
+  if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem) != hipSuccess)
     return set_error(OAL_ERR_HIP, "k_readout_vec: cannot reserve %zu bytes of LDS", smem);
   ProfScope ps("k_readout_vec", stream);
-  hipLaunchKernelGGL((k_readout_vec<T, O, DIM>), dim3(n_chunks, n_q_heads, batch), dim3(chunk), smem,
-                     stream, n_q_heads, n_kv_heads, seq_len, chunk, n_chunks,
-                     reinterpret_cast<const T*>(q), kk, vv, coeffs, ws, reinterpret_cast<O*>(y));
+  if (split)
+    hipLaunchKernelGGL((k_readout_vec<T, O, DIM, 2>), dim3(n_chunks, n_q_heads, batch), dim3(2 * chunk),
+                       smem, stream, n_q_heads, n_kv_heads, seq_len, chunk, n_chunks,
+                       reinterpret_cast<const T*>(q), kk, vv, coeffs, ws, reinterpret_cast<O*>(y));
+  else
+    hipLaunchKernelGGL((k_readout_vec<T, O, DIM, 1>), dim3(n_chunks, n_q_heads, batch), dim3(chunk), smem,
+                       stream, n_q_heads, n_kv_heads, seq_len, chunk, n_chunks,
+                       reinterpret_cast<const T*>(q), kk, vv, coeffs, ws, reinterpret_cast<O*>(y));
   return check_launch("k_readout_vec");
 }
 

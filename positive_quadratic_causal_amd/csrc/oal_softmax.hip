@@ -148,9 +148,13 @@ k_softmax(int n_q_heads, int n_kv_heads, int seq_len, int n_qb, int n_hg,
           if (key0 > qt0 + 31) continue;
           const SwRow& qr = nt ? qrow1 : qrow0;
           f32x16 s = splat16(0.f);
+          // products at raised wave priority: a wave with its operands ready issues
+          // them ahead of the co-resident waves' exponentials (about 1 %, measured)
+          __builtin_amdgcn_s_setprio(1);
 #pragma unroll
           for (int ks = 0; ks < 4; ++ks)
             s = mfma32(kr[ks], *reinterpret_cast<const bf16x8*>(qr.chunk(2 * ks + half)), s);
+          __builtin_amdgcn_s_setprio(0);
           // scores in base 2; keys after the query are masked
           const int query = qt0 + col;
           float tmax = -INFINITY;
@@ -175,6 +179,7 @@ k_softmax(int n_q_heads, int n_kv_heads, int seq_len, int n_qb, int n_hg,
           for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
             for (int i = 0; i < 16; ++i) acc[mt][nt][i] *= alpha;
+          __builtin_amdgcn_s_setprio(1);
 #pragma unroll
           for (int s2 = 0; s2 < 2; ++s2) {
             float x[8];
@@ -188,6 +193,7 @@ k_softmax(int n_q_heads, int n_kv_heads, int seq_len, int n_qb, int n_hg,
               acc[mt][nt] = mfma32(*reinterpret_cast<const bf16x8*>(vr.chunk(kc8)), pb, acc[mt][nt]);
             }
           }
+          __builtin_amdgcn_s_setprio(0);
         }
       }
     }
