@@ -282,11 +282,13 @@ BWD_KERNELS = ["k_build_vec", "k_scan_vec", "k_bwd_query", "k_bwd_rbuild", "k_bw
                "k_bwd_key", "k_bwd_ksum", "k_bwd_dc_intra", "k_bwd_dcoef"]
 
 
-def backward_flops(w, chunk) -> dict:
+def backward_flops(w, chunk, grouped=True) -> dict:
     """Algorithmic flops of the backward kernels (useful, unpadded).  Per causal
-    pair inside a chunk: kappa in packed form 64 + 2 (64 + 2080), its gradient
-    2 * 64 * 64 + 3 * 64 (S p and the product with k or q), and two 65-wide
-    products (alpha and the accumulation).  Per query or key row: two 2145 x 65
+    pair inside a chunk, for a grouped record: the 64 products q_r k_r, their
+    group sums (64), M s_bar (2 x 49), kappa (2 x 7), the gradient's 64
+    multiply-adds and two 65-wide products (alpha and the accumulation); for a
+    dimension-specific record kappa in packed form 64 + 2 (64 + 2080) and its
+    gradient 2 * 64 * 64 + 3 * 64 instead.  Per query or key row: two 2145 x 65
     contractions with a state (recompute + H g, or R^T psi(k) + R u)."""
     n, c = w.seq_len, chunk
     pairs = 0
@@ -295,7 +297,10 @@ def backward_flops(w, chunk) -> dict:
         pairs += m * (m + 1) // 2
     pairs *= w.batch * w.n_q_heads
     D, Wc = 2145, 65
-    kap, grad = 64 + 2 * (64 + 2080), 2 * 64 * 64 + 3 * 64
+    if grouped:
+        kap, grad = 64 + 64 + 2 * 49 + 2 * 7, 2 * 64
+    else:
+        kap, grad = 64 + 2 * (64 + 2080), 2 * 64 * 64 + 3 * 64
     nq = w.batch * w.n_q_heads * n
     nk = w.batch * w.n_kv_heads * n
     return {"k_bwd_query": nq * 4 * D * Wc + pairs * (kap + grad + 4 * Wc),

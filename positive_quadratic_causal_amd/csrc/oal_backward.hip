@@ -128,6 +128,87 @@ __device__ __forceinline__ float kappa_pair(float a, const float* qi, const floa
   return kap;
 }
 
+// Grouped records (NG >= 1): the kernel depends on a pair only through the group
+// sums s_bar = [1, s_1 .. s_G], s_g = sum_{r in g} q_r k_r / sqrt(d_h) ([OAL]
+// Eq. 7): kappa = eps + s_bar^T M s_bar, and the gradient of kappa with respect
+// to q_r is k_r w_{g(r)} with w = (2 / sqrt(d_h)) M s_bar (and q_r w_{g(r)} with
+// respect to k_r).  With few dims outside group 1 (at most 16, as the readout's
+// compact path) a pair costs one masked 64-wide sum, the outlier dims and a 7 x 7
+// product instead of the 64 x 64 S p of the general form.
+constexpr int MAX_OUT = 16;
+struct GroupTab {
+  float M[LDIM][LDIM];   // M = L L^T, zero beyond G
+  float bulk[DH];        // 1 on the dims of group 1, else 0
+  float eps;
+  int n_out;             // dims outside group 1
+  int dim[MAX_OUT];
+  int grp[MAX_OUT];
+};
+
+// every thread of the block calls it; a barrier must follow before use
+__device__ __forceinline__ void build_group_tab(GroupTab& gt, const float* rec, int tid) {
+  const int32_t* gmap = reinterpret_cast<const int32_t*>(rec) + OAL_COEF_GMAP;
+  if (tid < LDIM * LDIM) gt.M[tid / LDIM][tid % LDIM] = rec[OAL_COEF_M + tid];
+  if (tid < DH) gt.bulk[tid] = gmap[tid] <= 1 ? 1.f : 0.f;
+  if (tid == 0) {
+    gt.eps = rec[OAL_COEF_EPS];
+    int n = 0;
+    for (int r = 0; r < DH; ++r) {
+      if (gmap[r] <= 1) continue;
+      if (n < MAX_OUT) {
+        gt.dim[n] = r;
+        gt.grp[n] = gmap[r];
+      }
+      ++n;
+    }
+    gt.n_out = n;
+  }
+}
+
+// kappa of one pair (q row and k row in LDS) and w = (2 / sqrt d_h) M s_bar
+__device__ __forceinline__ float grouped_pair(const float* qi, const float* kj, const GroupTab& gt,
+                                              float (&w)[LDIM]) {
+  float s[LDIM];
+  float s1 = 0.f;
+#pragma unroll
+  for (int t = 0; t < DH; ++t) s1 = fmaf(gt.bulk[t], qi[t] * kj[t], s1);
+  s[0] = 1.f;
+  s[1] = s1 * 0.125f;
+#pragma unroll
+  for (int g = 2; g < LDIM; ++g) s[g] = 0.f;
+  for (int e = 0; e < gt.n_out; ++e) {
+    const int d = gt.dim[e], ge = gt.grp[e];
+    const float pe = qi[d] * kj[d] * 0.125f;
+#pragma unroll
+    for (int g = 2; g < LDIM; ++g) s[g] += ge == g ? pe : 0.f;
+  }
+  float kap = gt.eps;
+#pragma unroll
+  for (int u = 0; u < LDIM; ++u) {
+    float tu = 0.f;
+#pragma unroll
+    for (int v = 0; v < LDIM; ++v) tu = fmaf(gt.M[u][v], s[v], tu);
+    kap = fmaf(s[u], tu, kap);
+    w[u] = 0.25f * tu;
+  }
+  return kap;
+}
+
+// x[r] += a y[r] w_{g(r)} for an LDS row x (dq or dk) and a row y (k or q) in LDS
+__device__ __forceinline__ void grouped_grad(float* x, float a, const float* y, const GroupTab& gt,
+                                             const float (&w)[LDIM]) {
+  const float a1 = a * w[1];
+#pragma unroll
+  for (int r = 0; r < DH; ++r) x[r] = fmaf(a1 * gt.bulk[r], y[r], x[r]);
+  for (int e = 0; e < gt.n_out; ++e) {
+    const int d = gt.dim[e], ge = gt.grp[e];
+    float we = 0.f;
+#pragma unroll
+    for (int g = 2; g < LDIM; ++g) we = ge == g ? w[g] : we;
+    x[d] = fmaf(a * we, y[d], x[d]);
+  }
+}
+
 size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
 }  // namespace
 
@@ -199,7 +280,7 @@ k_bwd_query(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunks,
   const int clen = min(chunk, seq_len - t0);
   const bool active = qx < clen;
 
-  extern __shared__ float smem[];
+  extern __shared__ __attribute__((aligned(16))) float smem[];
   float* s_q = smem;                          // [chunk][DH + 1]
   float* s_dq = s_q + chunk * (DH + 1);       // [2][chunk][DH + 1] (half 1's rows also pass u~, g)
   float* s_H = s_dq + 2 * chunk * (DH + 1);   // [32][WP]
@@ -211,6 +292,9 @@ k_bwd_query(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunks,
 
   const float* rec = coef_rec(coeffs, hq);
   const float a = rec[OAL_COEF_A];
+  __shared__ __attribute__((aligned(16))) GroupTab gt;
+  const bool grouped = reinterpret_cast<const int32_t*>(rec)[OAL_COEF_NG] >= 1;
+  if (grouped) build_group_tab(gt, rec, tid);
   const size_t qrow0 = ((size_t)b * n_q_heads + hq) * seq_len + t0;
   for (int i = tid; i < chunk * DH; i += nthr) {
     const int ii = i / DH, d = i % DH;
@@ -222,6 +306,7 @@ k_bwd_query(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunks,
   for (int i = tid; i < 32 * (WP - W); i += nthr) s_H[(i / (WP - W)) * WP + W + i % (WP - W)] = 0.f;
   for (int i = tid; i < TB * (WP - W); i += nthr) s_u[(i / (WP - W)) * WP + W + i % (WP - W)] = 0.f;
   __syncthreads();
+  const bool fast = grouped && gt.n_out <= MAX_OUT;   // uniform over the block
   const float* qi = s_q + qx * (DH + 1);
   float* dqi = s_dq + (half * chunk + qx) * (DH + 1);
   const float* Hc = hc + ((size_t)unit * n_chunks + c) * STATE_FLOATS;
@@ -273,8 +358,12 @@ k_bwd_query(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunks,
     __syncthreads();
     if (active) {
       const int jmax = min(nj, qx - j0 + 1);
-      for (int jj = half; jj < jmax; jj += 2)
-        axpy_row(acc, kappa_pair(a, qi, s_k + jj * (DH + 1), s_b, s_S), s_u + jj * WP);
+      for (int jj = half; jj < jmax; jj += 2) {
+        float w[LDIM];
+        const float kap = fast ? grouped_pair(qi, s_k + jj * (DH + 1), gt, w)
+                               : kappa_pair(a, qi, s_k + jj * (DH + 1), s_b, s_S);
+        axpy_row(acc, kap, s_u + jj * WP);
+      }
     }
   }
 
@@ -329,6 +418,12 @@ k_bwd_query(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunks,
       const float* kj = s_k + jj * (DH + 1);
       const float al = dot_row(s_u + jj * WP, g);
       arow[j0 + jj] = al;
+      if (fast) {
+        float w[LDIM];
+        grouped_pair(qi, kj, gt, w);
+        grouped_grad(dqi, al, kj, gt, w);
+        continue;
+      }
       float p[DH];
 #pragma unroll
       for (int t = 0; t < DH; ++t) p[t] = qi[t] * kj[t];
@@ -494,7 +589,7 @@ k_bwd_key(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunks,
   const int clen = min(chunk, seq_len - t0);
   const bool active = jx < clen;
 
-  extern __shared__ float smem[];
+  extern __shared__ __attribute__((aligned(16))) float smem[];
   float* s_k = smem;                          // [chunk][DH + 1]
   float* s_dk = s_k + chunk * (DH + 1);       // [2][chunk][DH + 1]
   float* s_R = s_dk + 2 * chunk * (DH + 1);   // [32][WP]
@@ -556,13 +651,16 @@ k_bwd_key(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunks,
 
   // ---- the chunk's pairs (i >= j) of this slot's query head
   const size_t npad = (size_t)n_chunks * chunk;
+  __shared__ __attribute__((aligned(16))) GroupTab gt;
   if (slot < rep) {
     const int hq = kv * rep + slot;
     const float* rec = coef_rec(coeffs, hq);
     const float a = rec[OAL_COEF_A];
+    const bool grouped = reinterpret_cast<const int32_t*>(rec)[OAL_COEF_NG] >= 1;
     const size_t qrow0 = ((size_t)b * n_q_heads + hq) * seq_len;
     const size_t grow0 = ((size_t)b * n_q_heads + hq) * npad;
     __syncthreads();
+    if (grouped) build_group_tab(gt, rec, tid);
     for (int i = tid; i < DH; i += nthr) s_b[i] = rec[OAL_COEF_BP + i];
     for (int i = tid; i < DH * DH; i += nthr) s_S[i] = rec[OAL_COEF_CM + i];
     for (int i0 = 0; i0 < clen; i0 += TB) {
@@ -577,12 +675,20 @@ k_bwd_key(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunks,
         s_g[ii * WP + w] = ii < ni ? gbuf[(grow0 + t0 + i0 + ii) * WP + w] : 0.f;
       }
       __syncthreads();
+      const bool fast = grouped && gt.n_out <= MAX_OUT;   // uniform over the block
       if (active) {
         const int ii0 = max(0, jx - i0);
         for (int ii = ii0 + ((ii0 ^ half) & 1); ii < ni; ii += 2) {
           const float* qi = s_q + ii * (DH + 1);
           const float* gi = s_g + ii * WP;
           const float al = dot_row(gi, uj);
+          if (fast) {
+            float w[LDIM];
+            const float kap = grouped_pair(qi, kj, gt, w);
+            grouped_grad(dkj, al, qi, gt, w);
+            axpy_row(du, kap, gi);
+            continue;
+          }
           float p[DH];
 #pragma unroll
           for (int t = 0; t < DH; ++t) p[t] = qi[t] * kj[t];
@@ -639,7 +745,7 @@ k_bwd_dc_intra(int n_q_heads, int n_kv_heads, int seq_len, int n_chunks,
   const int unit = b * n_kv_heads + hq / (n_q_heads / n_kv_heads);
   const int t0 = c * CH;
   const int clen = min(CH, seq_len - t0);
-  extern __shared__ float smem[];
+  extern __shared__ __attribute__((aligned(16))) float smem[];
   float* s_a = smem;                          // [CH][CH]
   float* s_q = s_a + CH * CH;                 // [CH][DH + 1]
   float* s_k = s_q + CH * (DH + 1);           // [CH][DH + 1]

@@ -146,7 +146,7 @@ k_readout_vec(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunk
   const int t0 = c * chunk;
   const int clen = min(chunk, seq_len - t0);
 
-  extern __shared__ float smem[];
+  extern __shared__ __attribute__((aligned(16))) float smem[];
   // every array starts at a multiple of 4 floats (chunk and TB are multiples of 64)
   float* s_q = smem;                          // [chunk][DH + 1]
   float* s_H = s_q + chunk * (DH + 1);        // [32][WP]
