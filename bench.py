@@ -894,8 +894,7 @@ def main() -> int:
         print(json.dumps({"metric": METRIC, "prefill_dim": res}), flush=True)
         return 0
     log(f"prefill: {w3.name}, chunk {args.chunk}, {args.warmup} warmup + {args.steps} steps")
-    ms_eager, kt, ms_graph = bench_prefill(oal, w3, args.chunk, args.steps, args.warmup, device)
-    ms = ms_graph if ms_graph is not None else ms_eager
+    ms, kt, ms_graph = bench_prefill(oal, w3, args.chunk, args.steps, args.warmup, device)
     tokens = w3.batch * w3.seq_len
     result = {
         "metric": METRIC,
@@ -905,9 +904,9 @@ def main() -> int:
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 5),
-        "ms_per_step_eager": round(ms_eager, 5),
-        "launch": ("HIP graph replay of the step (checked equal to the eager step)"
-                   if ms_graph is not None else "eager launches"),
+        "ms_per_step_graph": round(ms_graph, 5) if ms_graph is not None else None,
+        "launch": "eager launches (ms_per_step_graph: the same step replayed from a HIP graph, "
+                  "checked equal to the eager step)",
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -933,19 +932,17 @@ def main() -> int:
                 sweep[str(c)] = round(ms, 5)
                 continue
             log(f"prefill chunk sweep: chunk {c}")
-            msc, _, msg = bench_prefill(oal, w3, c, max(3, args.steps // 4), 2, device)
-            sweep[str(c)] = round(msg if msg is not None else msc, 5)
+            msc, _, _ = bench_prefill(oal, w3, c, max(3, args.steps // 4), 2, device)
+            sweep[str(c)] = round(msc, 5)
         result["chunk_sweep_ms"] = sweep
         w1 = synth.WORKLOADS[1]
         log("linear-time check: N = 2048")
-        ms1e, _, ms1g = bench_prefill(oal, w1, args.chunk, args.steps, args.warmup, device)
-        ms1 = ms1g if ms1g is not None else ms1e
+        ms1, _, _ = bench_prefill(oal, w1, args.chunk, args.steps, args.warmup, device)
         result["linear_time_check"] = {"ms_n2048": round(ms1, 5), "ms_n32768": round(ms, 5),
                                        "ratio": round(ms / ms1, 3), "ideal_ratio": 16.0}
         w2 = synth.WORKLOADS[2]
         log(f"prefill: {w2.name}, chunk {args.chunk}")
-        ms2e, kt2, ms2g = bench_prefill(oal, w2, args.chunk, args.steps, args.warmup, device)
-        ms2 = ms2g if ms2g is not None else ms2e
+        ms2, kt2, _ = bench_prefill(oal, w2, args.chunk, args.steps, args.warmup, device)
         fl2 = prefill_flops_per_token(w2.n_q_heads, w2.n_kv_heads, args.chunk)["total"] * w2.batch * w2.seq_len
         result["prefill_llama_b4_n4096"] = {
             "workload": w2.name, "chunk": args.chunk, "ms_per_step": round(ms2, 5),
