@@ -406,30 +406,37 @@ def bench_calibration(oal, device, max_updates=1000):
             mse.append(err / e.size)
         return float(np.mean(mse)), float(np.mean(rel))
 
-    out = {"workload": w.name, "protocol": "Adam lr 0.02, clip 10, 32 positions per update, "
-           "validation every 100, patience 400, best checkpoint per head", "starts": {}}
+    out = {"workload": w.name, "protocol": "three starts (learned global embedded, Taylor, "
+           "perturbed global), each Adam lr 0.02, clip 10, 32 positions per update, validation "
+           "every 100, patience 400, best checkpoint per head; best start per head",
+           "starts": {}}
     L_seeded = torch.from_numpy(st.L).to(device)
     out["seeded_L"] = dict(zip(("mse", "rel_mse"), rel_mse(L_seeded)))
-    starts = {"taylor": cal.taylor_L(st.n_groups, 6)}
-    starts["taylor_perturbed"] = cal.perturbed(starts["taylor"], st.n_groups, 0.05, seed=951)
-    best_rel = None
-    for name, L0 in starts.items():
-        L0d = torch.from_numpy(L0).to(device)
-        before = rel_mse(L0d)
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        res = cal.calibrate(train, val, ng, gm, L0d, w.eps, max_updates=max_updates, seed=952)
-        secs = time.perf_counter() - t0
-        after = rel_mse(res.L)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    proto = cal.calibrate_protocol(train, val, ng, gm, w.eps, max_updates=max_updates, seed=952)
+    secs = time.perf_counter() - t0
+    res_all = proto.starts["results"]
+    total_updates = sum(r.updates for r in res_all.values())
+    for name, res in res_all.items():
         lh = res.loss_history.mean(axis=1)
-        out["starts"][name] = {"updates": res.updates, "seconds": round(secs, 3),
-                               "ms_per_update": round(secs * 1e3 / res.updates, 4),
-                               "train_loss_first_100": float(lh[:100].mean()),
-                               "train_loss_last_100": float(lh[-100:].mean()),
-                               "val_mse_history": [[t, float(np.mean(m))] for t, m in res.val_history],
-                               "before": {"mse": before[0], "rel_mse": before[1]},
-                               "after": {"mse": after[0], "rel_mse": after[1]}}
-        best_rel = after[1] if best_rel is None else min(best_rel, after[1])
+        entry = {"updates": res.updates,
+                 "train_loss_first_100": float(lh[:100].mean()),
+                 "train_loss_last_100": float(lh[-100:].mean()),
+                 "val_mse_history": [[t, float(np.mean(m))] for t, m in res.val_history]}
+        if name in proto.starts["starts"]:
+            b = rel_mse(proto.starts["starts"][name])
+            a = rel_mse(res.L)
+            entry["before"] = {"mse": b[0], "rel_mse": b[1]}
+            entry["after"] = {"mse": a[0], "rel_mse": a[1]}
+        out["starts"][name] = entry
+    final = rel_mse(proto.L)
+    out["selected"] = {"mse": final[0], "rel_mse": final[1],
+                       "start_per_head": proto.chosen}
+    out["seconds"] = round(secs, 3)
+    out["ms_per_update"] = round(secs * 1e3 / total_updates, 4)
+    best_rel = final[1]
+    starts = {"taylor": cal.taylor_L(st.n_groups, 6)}
     # one update's kernels alone (no validation), timed with the profiler events
     oal.oal_profile_reset()
     oal.oal_profile_enable(True)

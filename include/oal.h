@@ -310,6 +310,17 @@ oal_status oal_adam_step(int n_q_heads, int g_max, const int32_t* n_groups, floa
                          const float* dL, float* m, float* v, int step, float lr, float beta1,
                          float beta2, float eps, float clip_norm, hipStream_t stream);
 
+/* The learned global quadratic embedded into the grouped form ([OAL] App. D,
+ * Eq. 23: eps + [1 s] M_g [1 s]^T with s = q . k / sqrt(d_h); M_00 = m00,
+ * M_{0g} = M_{g0} = m01, M_{gh} = m11 for every group), the start of a grouped
+ * calibration from a calibrated global kernel.  L_global: device fp32
+ * [n_q_heads][g_ld][g_ld], of which the lower triangle of the leading 2 x 2 block
+ * is M_g's factor (a G = 1 calibration's L, g_ld = its g_max + 1); L: device fp32
+ * out [n_q_heads][g_max+1][g_max+1], rows 1..G_h = (l10, l11, 0, ..), row 0 =
+ * (l00, 0, ..), l00 = sqrt(m00), l10 = m01 / l00, l11 = sqrt(max(m11 - l10^2, 0)). */
+oal_status oal_embed_global(int n_q_heads, int g_max, const int32_t* n_groups, int g_ld,
+                            const float* L_global, float* L, hipStream_t stream);
+
 /* Per query head, the mean over batch, positions and channels of (y - y_ref)^2
  * for y, y_ref [batch][n_q_heads][seq_len][d_v] fp32: the validation error of the
  * calibration (and the MSE of [OAL] App. C, Eq. 21, per head). */

@@ -5,8 +5,9 @@ positions from a seeded generator, runs validation every ``val_every`` updates,
 keeps each head's best L and stops early.  Every arithmetic step runs in the
 library's kernels: the sampled rows' loss and gradient (``oal_calib_grad``), the
 clipped Adam step (``oal_adam_step``), the softmax targets
-(``oal_softmax_attention``) and the validation outputs and errors
-(``oal_expand_coeffs``, ``oal_prefill``, ``oal_output_mse``).
+(``oal_softmax_attention``), the validation outputs and errors
+(``oal_expand_coeffs``, ``oal_prefill``, ``oal_output_mse``) and the embedding of
+the learned global kernel (``oal_embed_global``).
 
 Protocol of the pages (App. B "Coefficient-calibration settings"): Adam at
 learning rate 0.02 without a scheduler, up to 1000 updates per initialisation,
@@ -27,7 +28,8 @@ import torch
 
 from positive_quadratic_causal_amd import oal
 
-__all__ = ["Sequence", "taylor_L", "perturbed", "softmax_targets", "validation_mse", "calibrate"]
+__all__ = ["Sequence", "taylor_L", "perturbed", "softmax_targets", "validation_mse", "calibrate",
+           "learned_global", "calibrate_protocol"]
 
 
 @dataclass
@@ -134,3 +136,53 @@ def calibrate(train: list[Sequence], val: list[Sequence], n_groups: torch.Tensor
                 break
     torch.cuda.synchronize()
     return CalibResult(best_L, best, t, history, losses[:t].cpu().numpy())
+
+
+def learned_global(train: list[Sequence], val: list[Sequence], n_q_heads: int, eps: float,
+                   **kw) -> CalibResult:
+    """The learned global quadratic ([OAL] App. D): the same calibration with every
+    dimension in one group (G = 1, L 2 x 2), from its Taylor start."""
+    dev = train[0].q.device
+    ng1 = torch.ones((n_q_heads,), dtype=torch.int32, device=dev)
+    gm1 = torch.ones((n_q_heads, 64), dtype=torch.int32, device=dev)
+    L1 = torch.from_numpy(taylor_L(np.ones(n_q_heads, dtype=np.int64), 1)).to(dev)
+    return calibrate(train, val, ng1, gm1, L1, eps, **kw)
+
+
+@dataclass
+class ProtocolResult:
+    L: torch.Tensor                      # per head the best of the starts
+    best_mse: np.ndarray                 # its validation MSE
+    chosen: list                         # per head the name of the winning start
+    starts: dict                         # name -> CalibResult (and the start L)
+
+
+def calibrate_protocol(train: list[Sequence], val: list[Sequence], n_groups: torch.Tensor,
+                       group_map: torch.Tensor, eps: float, *, g_max: int = 6,
+                       sigma: float = 0.05, seed: int = 0, **kw) -> ProtocolResult:
+    """The three starts of [OAL] App. B: the learned global quadratic embedded into
+    the grouped form (``oal_embed_global``), the second-order Taylor start, and a
+    Gaussian perturbation of the embedded global start; each calibrated with
+    ``calibrate`` and the best start kept per head by validation MSE."""
+    Hq = n_groups.shape[0]
+    dev = n_groups.device
+    ng_host = n_groups.cpu().numpy()
+    glob = learned_global(train, val, Hq, eps, seed=seed, **kw)
+    emb = oal.oal_embed_global(n_groups, glob.L, g_max)
+    starts = {"global_embedding": emb,
+              "taylor": torch.from_numpy(taylor_L(ng_host, g_max)).to(dev),
+              "global_perturbed": torch.from_numpy(perturbed(emb.cpu().numpy(), ng_host, sigma,
+                                                             seed + 1)).to(dev)}
+    results = {"learned_global_G1": glob}
+    best_L, best, chosen = None, None, None
+    for i, (name, L0) in enumerate(starts.items()):
+        res = calibrate(train, val, n_groups, group_map, L0, eps, seed=seed + 10 + i, **kw)
+        results[name] = res
+        if best is None:
+            best_L, best, chosen = res.L.clone(), res.best_mse.copy(), [name] * Hq
+            continue
+        for h in np.nonzero(res.best_mse < best)[0]:
+            best_L[h] = res.L[h]
+            best[h] = res.best_mse[h]
+            chosen[h] = name
+    return ProtocolResult(best_L, best, chosen, {"results": results, "starts": starts})

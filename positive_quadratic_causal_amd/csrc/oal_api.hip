@@ -104,6 +104,8 @@ oal_status launch_grouping(int n_q_heads, int n_prompts, const float* chi_prompt
                            float* gap, hipStream_t stream);
 int grouping_max_prompts();
 size_t calib_workspace(int n_q_heads, int n_pos);
+oal_status launch_embed_global(int n_q_heads, int g_max, int g_ld, const int32_t* n_groups,
+                               const float* Lg, float* L, hipStream_t stream);
 oal_status launch_calib_grad(int n_q_heads, int n_kv_heads, int seq_len, oal_dtype in_dtype,
                              const void* q, const void* k, const void* v, const float* y_ref,
                              const int32_t* positions, int n_pos, int g_max,
@@ -494,6 +496,16 @@ oal_status oal_adam_step(int n_q_heads, int g_max, const int32_t* n_groups, floa
   if (!n_groups || !L || !dL || !m || !v) return set_error(OAL_ERR_INVALID_ARG, "null pointer argument");
   return launch_adam(n_q_heads, g_max, n_groups, L, dL, m, v, step, lr, beta1, beta2, eps, clip_norm,
                      stream);
+}
+
+oal_status oal_embed_global(int n_q_heads, int g_max, const int32_t* n_groups, int g_ld,
+                            const float* L_global, float* L, hipStream_t stream) {
+  if (n_q_heads < 1) return set_error(OAL_ERR_INVALID_ARG, "n_q_heads must be >= 1");
+  if (g_max < 1 || g_max > GMAX)
+    return set_error(OAL_ERR_UNSUPPORTED, "g_max must be in 1..%d (got %d)", GMAX, g_max);
+  if (g_ld < 2 || g_ld > LDIM) return set_error(OAL_ERR_INVALID_ARG, "g_ld must be in 2..%d", LDIM);
+  if (!n_groups || !L_global || !L) return set_error(OAL_ERR_INVALID_ARG, "null pointer argument");
+  return launch_embed_global(n_q_heads, g_max, g_ld, n_groups, L_global, L, stream);
 }
 
 oal_status oal_output_mse(int batch, int n_q_heads, int seq_len, int d_v, const float* y,

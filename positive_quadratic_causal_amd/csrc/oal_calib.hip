@@ -304,6 +304,43 @@ k_output_mse(int batch, int n_q_heads, int seq_len, int d_v, const float* __rest
   if (tid == 0) mse[h] = s_red[0] / (float)((size_t)batch * per);
 }
 
+// The learned global quadratic ([OAL] App. D, Eq. 23: eps + [1 s] M_g [1 s]^T,
+// s = q . k / sqrt(d_h)) embedded into the grouped parameterisation: M_00 = m00,
+// M_{0g} = M_{g0} = m01, M_{gh} = m11 for all groups 1..G, factored as L with
+// row 0 = (l00, 0, ..) and rows 1..G = (l10, l11, 0, ..), l00 = sqrt(m00),
+// l10 = m01 / l00, l11 = sqrt(max(m11 - l10^2, 0)); M_g = L_g L_g^T from the
+// 2 x 2 lower triangle L_g of each head (the G = 1 calibration's L).
+__global__ void __launch_bounds__(64)
+k_embed_global(int g_max, int g_ld, const int32_t* __restrict__ n_groups,
+               const float* __restrict__ Lg, float* __restrict__ L) {
+  const int h = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int ld = g_max + 1;
+  int G = n_groups[h];
+  G = G < 1 ? 1 : (G > g_max ? g_max : G);
+  const float* lg = Lg + (size_t)h * g_ld * g_ld;
+  const double a = lg[0], b = lg[g_ld], c = lg[g_ld + 1];   // lower triangle of L_g
+  const double m00 = a * a, m01 = a * b, m11 = b * b + c * c;
+  const double l00 = sqrt(m00);
+  const double l10 = l00 > 0.0 ? m01 / l00 : 0.0;
+  const double l11 = sqrt(fmax(m11 - l10 * l10, 0.0));
+  if (tid < ld * ld) {
+    const int u = tid / ld, w = tid % ld;
+    float x = 0.f;
+    if (u == 0 && w == 0) x = (float)l00;
+    else if (u >= 1 && u <= G && w == 0) x = (float)l10;
+    else if (u >= 1 && u <= G && w == 1) x = (float)l11;
+    L[(size_t)h * ld * ld + tid] = x;
+  }
+}
+
+oal_status launch_embed_global(int n_q_heads, int g_max, int g_ld, const int32_t* n_groups,
+                               const float* Lg, float* L, hipStream_t stream) {
+  ProfScope ps("k_embed_global", stream);
+  hipLaunchKernelGGL(k_embed_global, dim3(n_q_heads), dim3(64), 0, stream, g_max, g_ld, n_groups, Lg, L);
+  return check_launch("k_embed_global");
+}
+
 // ---------------------------------------------------------------------------
 
 size_t calib_workspace(int n_q_heads, int n_pos) {

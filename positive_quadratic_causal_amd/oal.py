@@ -77,6 +77,7 @@ def _load() -> ctypes.CDLL:
                            + [c_float] + [c_void] * 3 + [c_size, c_void]),
         "oal_adam_step": (c_int, [c_int, c_int] + [c_void] * 5 + [c_int] + [c_float] * 5 + [c_void]),
         "oal_output_mse": (c_int, [c_int] * 4 + [c_void] * 3 + [c_void]),
+        "oal_embed_global": (c_int, [c_int, c_int, c_void, c_int, c_void, c_void, c_void]),
         "oal_decode_step": (c_int, [c_int, c_int, c_int, c_int, c_int, c_int, c_void, c_void,
                                     c_void, c_void, c_void, c_void, c_int, c_void]),
         "oal_softmax_attention": (c_int, [c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_void,
@@ -103,6 +104,7 @@ EXPORTED = ("oal_coeffs_bytes", "oal_expand_coeffs", "oal_dim_coeffs", "oal_stat
             "oal_prefill_dim_workspace_bytes", "oal_prefill_dim",
             "oal_prefill_backward_workspace_bytes", "oal_prefill_backward", "oal_coeffs_backward",
             "oal_calib_workspace_bytes", "oal_calib_grad", "oal_adam_step", "oal_output_mse",
+            "oal_embed_global",
             "oal_contribution_scores", "oal_bootstrap_grouping",
             "oal_decode_step", "oal_softmax_attention", "oal_profile_enable", "oal_profile_reset",
             "oal_profile_query",
@@ -429,6 +431,18 @@ def oal_adam_step(n_groups: torch.Tensor, L: torch.Tensor, dL: torch.Tensor, m: 
     _check(_lib.oal_adam_step(n_groups.shape[0], L.shape[-1] - 1, _ptr(n_groups), _ptr(L), _ptr(dL),
                               _ptr(m), _ptr(v), int(step), float(lr), float(beta1), float(beta2),
                               float(eps), float(clip_norm), _stream(L)))
+
+
+def oal_embed_global(n_groups: torch.Tensor, L_global: torch.Tensor, g_max: int = 6,
+                     L: torch.Tensor | None = None) -> torch.Tensor:
+    """L_global [Hq, g+1, g+1] (a G = 1 calibration's L); returns the grouped start
+    L [Hq, g_max+1, g_max+1]."""
+    Hq = n_groups.shape[0]
+    if L is None:
+        L = torch.empty((Hq, g_max + 1, g_max + 1), dtype=torch.float32, device=L_global.device)
+    _check(_lib.oal_embed_global(Hq, g_max, _ptr(n_groups), L_global.shape[-1], _ptr(L_global), _ptr(L),
+                                 _stream(L)))
+    return L
 
 
 def oal_output_mse(y: torch.Tensor, y_ref: torch.Tensor, mse: torch.Tensor | None = None) -> torch.Tensor:

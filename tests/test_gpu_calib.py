@@ -109,3 +109,22 @@ def test_update_schedule_matches_oracle(oal):
         Ls, _ = K.calibrate(train, L0[h].astype(np.float64), case.st.group_map[h], G, w.eps, sched)
         assert rel_l2(got[h], Ls[-1]) <= 1e-4, h
         assert rel_l2(Ls[-1], L0[h]) > 1e-3       # the schedule really moved L
+
+
+def test_embed_global_matches_oracle(oal):
+    """oal_embed_global against the oracle's embedding of Eq. 23, and the embedded
+    grouped kernel equal to the global one on a pair."""
+    announce("learned-global embedding, 5 heads")
+    rng = np.random.default_rng(940)
+    n_groups = np.array([1, 2, 4, 6, 3], dtype=np.int32)
+    Lg = np.zeros((5, 2, 2), dtype=np.float32)
+    Lg[:, 0, 0] = rng.uniform(0.5, 1.5, size=5)
+    Lg[:, 1, 0] = rng.normal(size=5)
+    Lg[:, 1, 1] = rng.uniform(0.2, 1.0, size=5)
+    L = oal.oal_embed_global(torch.from_numpy(n_groups).cuda(), torch.from_numpy(Lg).cuda(), 6)
+    torch.cuda.synchronize()
+    got = L.cpu().numpy()
+    for h in range(5):
+        Lg64 = Lg[h].astype(np.float64)
+        ref = K.global_embedding_L(Lg64 @ Lg64.T, int(n_groups[h]), 6)
+        np.testing.assert_allclose(got[h], ref, rtol=1e-6, atol=1e-7)
