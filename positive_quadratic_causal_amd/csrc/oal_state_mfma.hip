@@ -421,8 +421,8 @@ k_state_mfma(int seq_len, int chunk, int n_chunks, int n_seg, int cps, int n_blk
           acc[m][nt][i] = MODE == 1 ? (float)__builtin_bit_cast(_Float16, pslot[(size_t)((m * 2 + nt) * 16 + i) * 64 + lane]) * rescale
                                     : 0.f;
     const float wscale = unscale * tscale;   // accumulator -> tile entry
-    // tile stores per chunk start: every row of every tile, 4 rows per store
-    constexpr int NST = st::QTILES * 2 * 4;
+    // tile stores per chunk start: every tile, one 16-byte store per (tile, column half, K-step)
+    constexpr int NST = st::QTILES * 2 * 2;   // store instructions per tile store (per lane)
     auto stores_at = [&](int b) { return (MODE == 1 && b >= 0 && (b * st::TB) % chunk == 0) ? NST : 0; };
 
     auto body = [&](int bi, const uint8_t* cur, uint8_t* nxt) {
@@ -443,13 +443,22 @@ k_state_mfma(int seq_len, int chunk, int n_chunks, int n_seg, int cps, int n_blk
 #pragma unroll
           for (int nt = 0; nt < 2; ++nt) {
             const int w = 32 * nt + col;
+            // K-step ks0 + kk holds rows 8 kk .. 8 kk + 7 of the lane pair (lane,
+            // lane ^ 32): elements 4 half .. + 3 and 8 + 4 half .. + 3 of the 16 of
+            // column w.  One exchange gives each lane 8 contiguous elements, so that
+            // every store writes 16 contiguous bytes (the pass is about 9 % faster
+            // than with two 8-byte stores per lane, measured)
 #pragma unroll
-            for (int gq = 0; gq < 4; ++gq) {
-              const int ks_ = ks0[m] + (gq >> 1);
-              const int el = 8 * (gq & 1) + 4 * half;
-              *reinterpret_cast<uint2*>(tl + (size_t)ks_ * 1024 + w * 16 + el) =
-                  pack4_f16(acc[m][nt][4 * gq], acc[m][nt][4 * gq + 1], acc[m][nt][4 * gq + 2],
-                            acc[m][nt][4 * gq + 3], wscale);
+            for (int kk = 0; kk < 2; ++kk) {
+              const int ks_ = ks0[m] + kk;
+              const uint2 A = pack4_f16(acc[m][nt][8 * kk], acc[m][nt][8 * kk + 1], acc[m][nt][8 * kk + 2],
+                                        acc[m][nt][8 * kk + 3], wscale);
+              const uint2 B = pack4_f16(acc[m][nt][8 * kk + 4], acc[m][nt][8 * kk + 5],
+                                        acc[m][nt][8 * kk + 6], acc[m][nt][8 * kk + 7], wscale);
+              const uint2 X = half ? A : B;   // the half the partner lane stores
+              const uint2 Y = make_uint2(__shfl_xor((int)X.x, 32, 64), __shfl_xor((int)X.y, 32, 64));
+              const uint4 out = half ? make_uint4(Y.x, Y.y, B.x, B.y) : make_uint4(A.x, A.y, Y.x, Y.y);
+              *reinterpret_cast<uint4*>(tl + (size_t)ks_ * 1024 + w * 16 + 8 * half) = out;
             }
             asm volatile("" ::: "memory");   // keep the conversions next to their stores
           }
