@@ -117,6 +117,8 @@ k_readout_mfma(int n_q_heads, int n_kv_heads, int seq_len, int n_chunks, int n_h
   __shared__ __attribute__((aligned(16))) float s_ht[Cfg::HPW * htab::FLOATS];
   __shared__ float s_red[16];
   __shared__ __attribute__((aligned(16))) float s_h0[DV];   // H0 of the chunk's prefix
+  // inter-chunk denominators of the mirror waves' tokens, per (head, wave pair)
+  __shared__ float s_dx[Cfg::HPW * (Cfg::WPH > 1 ? Cfg::WPH / 2 : 1) * 64];
   // k rows (64 per array) and v^T rows (64 keys per array) of the chunk
   auto k_arr = [&](int i) -> uint8_t* { return pick4(i, s_b0, s_b1, s_b2, s_b3); };
   auto v_arr = [&](int i) -> uint8_t* {
@@ -341,6 +343,86 @@ k_readout_mfma(int n_q_heads, int n_kv_heads, int seq_len, int n_chunks, int n_h
     for (int i = 0; i < 2; ++i) load_lds16(tile_rsrc, dst + i * 1024, dma_off[i], soff);
   };
 
+  // ---- inter-chunk denominator: a z0 + sum_r q_r (b'_r z1_r + ((C / d_h o Z) q)_r),
+  //      T = b' o z1 + (C/d_h o Z) q^T on the matrix cores (the first term as the
+  //      accumulator seed); C/d_h from the head's M_{g(n),g(t)}/d_h 2^-e_M table.
+  //      The waves of a head have unequal intra-chunk parts (wave sub meets
+  //      2 sub + 2 key tiles), and the barrier behind that part waits for the
+  //      longest.  So wave sub < WPH / 2 computes the denominators of its own
+  //      tokens and of the mirror wave WPH - 1 - sub before its intra-chunk part
+  //      (one Z operand serves both), handing the latter over through LDS; the
+  //      mirror waves compute none.  With one wave per head (no imbalance) the
+  //      wave computes its own after the barrier, while the first half-slabs load.
+  constexpr bool PAIRED = Cfg::WPH > 1;
+  const bool den_giver = !PAIRED || sub < Cfg::WPH / 2;
+  const int msub = Cfg::WPH - 1 - sub;   // the mirror wave of a giver
+  float* dx = s_dx + (hslot * (PAIRED ? Cfg::WPH / 2 : 1) + min(sub, msub)) * 64;   // this pair's slots
+  auto denominator = [&](auto two_t) {
+    constexpr bool TWO = decltype(two_t)::value;
+    constexpr int NT = TWO ? 4 : 2;
+    const SwRow rows[4] = {qrow0, qrow1, SwRow(qw, 64 * msub + col), SwRow(qw, 64 * msub + 32 + col)};
+    const float* Zs = ts_side + tile::SIDE_Z;
+    float dd[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) dd[nt] = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      const int n = 32 * mt + col;
+      const int gn = __shfl(gl, n, 64);   // g(n)
+      const _Float16* mrow = s_mg + (hslot * LDIM + gn) * DH + 8 * half;
+      f32x16 T[NT];
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const float4 bz = *reinterpret_cast<const float4*>(ht + htab::BZ + 32 * mt + 8 * g4 + 4 * half);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          T[nt][4 * g4 + 0] = bz.x;
+          T[nt][4 * g4 + 1] = bz.y;
+          T[nt][4 * g4 + 2] = bz.z;
+          T[nt][4 * g4 + 3] = bz.w;
+        }
+      }
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const float4 z0 = *reinterpret_cast<const float4*>(Zs + n * DH + 16 * ks + 8 * half);
+        const float4 z1 = *reinterpret_cast<const float4*>(Zs + n * DH + 16 * ks + 8 * half + 4);
+        const f16x8 m8 = *reinterpret_cast<const f16x8*>(mrow + 16 * ks);
+        const float x[8] = {z0.x * (float)m8[0], z0.y * (float)m8[1], z0.z * (float)m8[2], z0.w * (float)m8[3],
+                            z1.x * (float)m8[4], z1.y * (float)m8[5], z1.z * (float)m8[6], z1.w * (float)m8[7]};
+        const bf16x8 az = pack8(x);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+          T[nt] = mfma32(az, *reinterpret_cast<const bf16x8*>(rows[nt].chunk(2 * ks + half)), T[nt]);
+      }
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        float d = 0.f;
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {   // rows 32 mt + 8 g4 + 4 half + e, e = 0..3
+          const uint2 u = *reinterpret_cast<const uint2*>(rows[nt].elem(32 * mt + 8 * g4 + 4 * half));
+          d = fmaf(__uint_as_float(u.x << 16), T[nt][4 * g4 + 0], d);
+          d = fmaf(__uint_as_float(u.x & 0xffff0000u), T[nt][4 * g4 + 1], d);
+          d = fmaf(__uint_as_float(u.y << 16), T[nt][4 * g4 + 2], d);
+          d = fmaf(__uint_as_float(u.y & 0xffff0000u), T[nt][4 * g4 + 3], d);
+        }
+        dd[nt] += d;
+      }
+    }
+    const float az0 = half == 0 ? rec[OAL_COEF_A] * ts_side[tile::SIDE_Z0] : 0.f;
+    const float sc = ldexpf(F, e_m);
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) den[nt] += dd[nt] * sc + az0 * F;
+    if (TWO) {
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {   // whole sums (both lane halves) of the mirror's tokens
+        float x = dd[NT - 2 + nt] * sc + az0 * F;
+        x += __shfl_xor(x, 32, 64);
+        if (half == 0) dx[32 * nt + col] = x;
+      }
+    }
+  };
+  if (PAIRED && head_ok && den_giver) denominator(bool_t<true>{});
+
   // ================= intra-chunk part ======================================
   // kappa^T[key][tok] F = eps F + sum_p t_p^2,  t_p = sqrt(F) (L_0p + sum_r ell_p[r] q_r k_r),
   // then the causal mask and u~^T += [V; 1]^T kappa^T (values on the matrix cores,
@@ -477,58 +559,7 @@ k_readout_mfma(int n_q_heads, int n_kv_heads, int seq_len, int n_chunks, int n_h
   issue(0, buf(0));
   issue(1, buf(1));
   issue(2, buf(2));
-
-  // ---- inter-chunk denominator: a z0 + sum_r q_r (b'_r z1_r + ((C / d_h o Z) q)_r),
-  //      T = b' o z1 + (C/d_h o Z) q^T on the matrix cores (the first term as the
-  //      accumulator seed); C/d_h from the head's M_{g(n),g(t)}/d_h 2^-e_M table
-  if (head_ok) {
-    const float* Zs = ts_side + tile::SIDE_Z;
-    float dd[2] = {0.f, 0.f};
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      const int n = 32 * mt + col;
-      const int gn = __shfl(gl, n, 64);   // g(n)
-      const _Float16* mrow = s_mg + (hslot * LDIM + gn) * DH + 8 * half;
-      f32x16 T[2];
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const float4 bz = *reinterpret_cast<const float4*>(ht + htab::BZ + 32 * mt + 8 * g4 + 4 * half);
-        T[0][4 * g4 + 0] = T[1][4 * g4 + 0] = bz.x;
-        T[0][4 * g4 + 1] = T[1][4 * g4 + 1] = bz.y;
-        T[0][4 * g4 + 2] = T[1][4 * g4 + 2] = bz.z;
-        T[0][4 * g4 + 3] = T[1][4 * g4 + 3] = bz.w;
-      }
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const float4 z0 = *reinterpret_cast<const float4*>(Zs + n * DH + 16 * ks + 8 * half);
-        const float4 z1 = *reinterpret_cast<const float4*>(Zs + n * DH + 16 * ks + 8 * half + 4);
-        const f16x8 m8 = *reinterpret_cast<const f16x8*>(mrow + 16 * ks);
-        const float x[8] = {z0.x * (float)m8[0], z0.y * (float)m8[1], z0.z * (float)m8[2], z0.w * (float)m8[3],
-                            z1.x * (float)m8[4], z1.y * (float)m8[5], z1.z * (float)m8[6], z1.w * (float)m8[7]};
-        const bf16x8 az = pack8(x);
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt) T[nt] = mfma32(az, qfrag(nt, ks), T[nt]);
-      }
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        const SwRow& qr = nt ? qrow1 : qrow0;
-        float d = 0.f;
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {   // rows 32 mt + 8 g4 + 4 half + e, e = 0..3
-          const uint2 u = *reinterpret_cast<const uint2*>(qr.elem(32 * mt + 8 * g4 + 4 * half));
-          d = fmaf(__uint_as_float(u.x << 16), T[nt][4 * g4 + 0], d);
-          d = fmaf(__uint_as_float(u.x & 0xffff0000u), T[nt][4 * g4 + 1], d);
-          d = fmaf(__uint_as_float(u.y << 16), T[nt][4 * g4 + 2], d);
-          d = fmaf(__uint_as_float(u.y & 0xffff0000u), T[nt][4 * g4 + 3], d);
-        }
-        dd[nt] += d;
-      }
-    }
-    const float az0 = half == 0 ? rec[OAL_COEF_A] * ts_side[tile::SIDE_Z0] : 0.f;
-    const float sc = ldexpf(F, e_m);
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt) den[nt] += dd[nt] * sc + az0 * F;
-  }
+  if (!PAIRED && head_ok) denominator(bool_t<false>{});
 
   // ---- main K loop over the 37 half-slabs: 1 linear, then 4 c + 3 per t-block c
   //      (the last of them the merged rows of the diagonal block); half-slab hs
@@ -696,7 +727,10 @@ k_readout_mfma(int n_q_heads, int n_kv_heads, int seq_len, int n_chunks, int n_h
   // ================= epilogue: + a F H0, normalise, store ======================
   if (!head_ok) return;
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt) den[nt] += __shfl_xor(den[nt], 32, 64);
+  for (int nt = 0; nt < 2; ++nt) {
+    den[nt] += __shfl_xor(den[nt], 32, 64);
+    if (!den_giver) den[nt] += dx[32 * nt + col];   // written before the intra-chunk barrier
+  }
   const float aF = rec[OAL_COEF_A] * F;
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt) {
