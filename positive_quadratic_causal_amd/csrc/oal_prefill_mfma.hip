@@ -316,8 +316,8 @@ k_readout_mfma(int n_q_heads, int n_kv_heads, int seq_len, int n_chunks, int n_h
     for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = splat16(0.f);
 
   // Half-slab hs of the tile goes to buffer hs % 4 by direct-to-LDS buffer loads,
-  // three half-slabs ahead of the one being read (the buffers hold k and v^T
-  // until the intra-chunk part is done).  Each wave moves two 1 KB pieces of a
+  // issued while half-slab hs - 4 is multiplied from registers (the buffers hold
+  // k and v^T until the intra-chunk part is done).  Each wave moves two 1 KB pieces of a
   // half-slab, lane l writing bytes 16 l .. 16 l + 15 of a piece,
   // fetched from the tile position that the swizzle of slab_off puts there.
   // The loads are issued from inline assembly: the compiler then neither waits
@@ -559,6 +559,7 @@ k_readout_mfma(int n_q_heads, int n_kv_heads, int seq_len, int n_chunks, int n_h
   issue(0, buf(0));
   issue(1, buf(1));
   issue(2, buf(2));
+  issue(3, buf(3));
   if (!PAIRED && head_ok) denominator(bool_t<false>{});
 
   // ---- main K loop over the 37 half-slabs: 1 linear, then 4 c + 3 per t-block c
@@ -568,34 +569,51 @@ k_readout_mfma(int n_q_heads, int n_kv_heads, int seq_len, int n_chunks, int n_h
   const uint8_t* mgh = mgh0 + 16 * half;
   f16x8 qt[2], qh[2];
   int cur = -1;
-  // one half-slab of rows r0 .. r0 + 3 of t-block c: K-steps (r0 + i, c)
-  auto quad = [&](int c, int h, const uint8_t* sb) {
-    const int r0 = 4 * h;
-    // the state fragments of all four K-steps first, so that their LDS latency
-    // overlaps the feature arithmetic below
-    f16x8 af[4][2];
+  // The state fragments of a half-slab in registers: K-step i, rows 32 mt + col.
+  using AFrag = f16x8[4][2];
+  auto load_af = [&](AFrag& af, const uint8_t* sb) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
         af[i][mt] = *reinterpret_cast<const f16x8*>(sb + slab_off(i, 32 * mt + col, half));
+  };
+  // Every product step first issues its own LDS reads (q rows, M rows), then the
+  // reads of the next half-slab's fragments (nx from nsb, when pf), then its
+  // products: LDS reads return in order, so the products wait only for their own
+  // operands and the next fragments arrive behind them.
+  // one half-slab of rows r0 .. r0 + 3 of t-block c: K-steps (r0 + i, c)
+  auto quad = [&](int c, int h, const AFrag& af, AFrag& nx, const uint8_t* nsb, bool pf) {
+    const int r0 = 4 * h;
+    uint2 u[2];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) u[nt] = *reinterpret_cast<const uint2*>((nt ? qrow1 : qrow0).elem(r0));
+    const uint8_t* mgc = mgh + 32 * c;
+    int gi[4];
+    f16x8 m8[4];   // M_{g(r), g(t)} / d_h (scaled) of the four rows
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      gi[i] = __builtin_amdgcn_readlane(gl, r0 + i);
+      m8[i] = *reinterpret_cast<const f16x8*>(mgc + gi[i] * (DH * 2));
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (pf) load_af(nx, nsb);
+    __builtin_amdgcn_sched_barrier(0);
     // m q_r of r0 .. r0 + 3, scaled, as fp16: m = 2 off the diagonal 16-block and
     // for its upper t-half (whose mirrored pairs are not stored), 1 otherwise
     const float qs = (r0 < 16 * c || half == 1) ? 2.0f * qr_scale : qr_scale;
     _Float16 qr[2][4];
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
-      const uint2 u = *reinterpret_cast<const uint2*>((nt ? qrow1 : qrow0).elem(r0));
       const f16x2 lo = __builtin_convertvector(
-          (f32x2){__uint_as_float(u.x << 16) * qs, __uint_as_float(u.x & 0xffff0000u) * qs}, f16x2);
+          (f32x2){__uint_as_float(u[nt].x << 16) * qs, __uint_as_float(u[nt].x & 0xffff0000u) * qs}, f16x2);
       const f16x2 hi = __builtin_convertvector(
-          (f32x2){__uint_as_float(u.y << 16) * qs, __uint_as_float(u.y & 0xffff0000u) * qs}, f16x2);
+          (f32x2){__uint_as_float(u[nt].y << 16) * qs, __uint_as_float(u[nt].y & 0xffff0000u) * qs}, f16x2);
       qr[nt][0] = lo[0];
       qr[nt][1] = lo[1];
       qr[nt][2] = hi[0];
       qr[nt][3] = hi[1];
     }
-    const uint8_t* mgc = mgh + 32 * c;
     // the 16 products of the half-slab at raised wave priority, so that a wave
     // with its products ready issues them ahead of the co-resident waves' loads
     // and feature arithmetic (about 1 % on this kernel, measured)
@@ -603,12 +621,10 @@ k_readout_mfma(int n_q_heads, int n_kv_heads, int seq_len, int n_chunks, int n_h
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       // qhat = q_t M_{g(r), g(t)} / d_h (scaled), recomputed when g(r) changes
-      const int g = __builtin_amdgcn_readlane(gl, r0 + i);
-      if (g != cur) {
-        cur = g;
-        const f16x8 m8 = *reinterpret_cast<const f16x8*>(mgc + g * (DH * 2));
-        qh[0] = qt[0] * m8;
-        qh[1] = qt[1] * m8;
+      if (gi[i] != cur) {
+        cur = gi[i];
+        qh[0] = qt[0] * m8[i];
+        qh[1] = qt[1] * m8[i];
       }
       const f16x8 f0 = qh[0] * qr[0][i];
       const f16x8 f1 = qh[1] * qr[1][i];
@@ -622,35 +638,38 @@ k_readout_mfma(int n_q_heads, int n_kv_heads, int seq_len, int n_chunks, int n_h
   };
   // the merged half-slab of t-block c: K-step i holds rows 16 c + 8 + 2 i + half
   // against t = 16 c + 8 .. 16 c + 15 in both lane halves (multiplicity 1)
-  auto quad_merged = [&](int c, const uint8_t* sb) {
-    f16x8 af[4][2];
+  auto quad_merged = [&](int c, const AFrag& af, AFrag& nx, const uint8_t* nsb, bool pf) {
+    bf16x8 qv[2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-        af[i][mt] = *reinterpret_cast<const f16x8*>(sb + slab_off(i, 32 * mt + col, half));
-    f16x8 qu[2];          // q_t, t = 16 c + 8 .. + 7, times qt_scale
-    _Float16 qr[2][4];    // q_r, r = 16 c + 8 + 2 i + half, times qr_scale
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      const bf16x8 qv = *reinterpret_cast<const bf16x8*>((nt ? qrow1 : qrow0).chunk(2 * c + 1));
-#pragma unroll
-      for (int j = 0; j < 8; j += 2) {
-        const f16x2 hv = __builtin_convertvector((f32x2){bf(qv[j]) * qt_scale, bf(qv[j + 1]) * qt_scale}, f16x2);
-        qu[nt][j] = hv[0];
-        qu[nt][j + 1] = hv[1];
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) qr[nt][i] = (_Float16)(bf(half ? qv[2 * i + 1] : qv[2 * i]) * qr_scale);
-    }
+    for (int nt = 0; nt < 2; ++nt) qv[nt] = *reinterpret_cast<const bf16x8*>((nt ? qrow1 : qrow0).chunk(2 * c + 1));
     const uint8_t* mgc = mgh0 + 32 * c + 16;   // M rows at t = 16 c + 8 .. + 7
+    f16x8 m8[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int g0 = __builtin_amdgcn_readlane(gl, 16 * c + 8 + 2 * i);
       const int g1 = __builtin_amdgcn_readlane(gl, 16 * c + 9 + 2 * i);
-      const f16x8 m8 = *reinterpret_cast<const f16x8*>(mgc + (half ? g1 : g0) * (DH * 2));
-      const f16x8 f0 = (qu[0] * m8) * qr[0][i];
-      const f16x8 f1 = (qu[1] * m8) * qr[1][i];
+      m8[i] = *reinterpret_cast<const f16x8*>(mgc + (half ? g1 : g0) * (DH * 2));
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (pf) load_af(nx, nsb);
+    __builtin_amdgcn_sched_barrier(0);
+    f16x8 qu[2];          // q_t, t = 16 c + 8 .. + 7, times qt_scale
+    _Float16 qr[2][4];    // q_r, r = 16 c + 8 + 2 i + half, times qr_scale
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+#pragma unroll
+      for (int j = 0; j < 8; j += 2) {
+        const f16x2 hv = __builtin_convertvector((f32x2){bf(qv[nt][j]) * qt_scale, bf(qv[nt][j + 1]) * qt_scale}, f16x2);
+        qu[nt][j] = hv[0];
+        qu[nt][j + 1] = hv[1];
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) qr[nt][i] = (_Float16)(bf(half ? qv[nt][2 * i + 1] : qv[nt][2 * i]) * qr_scale);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const f16x8 f0 = (qu[0] * m8[i]) * qr[0][i];
+      const f16x8 f1 = (qu[1] * m8[i]) * qr[1][i];
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt) {
         acc[mt][0] = mfma32h(af[i][mt], f0, acc[mt][0]);
@@ -658,12 +677,24 @@ k_readout_mfma(int n_q_heads, int n_kv_heads, int seq_len, int n_chunks, int n_h
       }
     }
   };
+  // Step hs of the half-slab ring: every wave holds the fragments of half-slab hs
+  // in registers (read during step hs - 1) and half-slab hs + 1 has landed; the
+  // buffer of hs is then refilled with hs + 4 while the products of hs run.  The
+  // wait also covers this wave's LDS reads, so no buffer is refilled while a read
+  // of it is in flight.
+  auto ring_step = [&](int hs) {
+    wait_vmcnt<4, true>();   // hs + 1 landed; hs + 2, hs + 3 may be in flight
+    barrier_nofence();
+    issue(hs + 4, buf(hs));
+  };
   auto main_loop = [&](auto compute_t) {
     constexpr bool COMPUTE = decltype(compute_t)::value;
-    // linear half-slab (buffer 0): phi = b'_r F_f q_r, r = 16 ks + 8 half + j
-    wait_vmcnt<4>();
+    AFrag afa, afb;
+    wait_vmcnt<6, true>();   // half-slab 0 landed
     barrier_nofence();
-    issue(3, buf(3));
+    if (COMPUTE) load_af(afa, buf(0));
+    // linear half-slab 0: phi = b'_r F_f q_r, r = 16 ks + 8 half + j
+    ring_step(0);
     if (COMPUTE) {
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
@@ -683,14 +714,16 @@ k_readout_mfma(int n_q_heads, int n_kv_heads, int seq_len, int n_chunks, int n_h
         }
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) {
-          const f16x8 af = *reinterpret_cast<const f16x8*>(buf(0) + slab_off(ks, 32 * mt + col, half));
-          acc[mt][0] = mfma32h(af, fb[0], acc[mt][0]);
-          acc[mt][1] = mfma32h(af, fb[1], acc[mt][1]);
+          acc[mt][0] = mfma32h(afa[ks][mt], fb[0], acc[mt][0]);
+          acc[mt][1] = mfma32h(afa[ks][mt], fb[1], acc[mt][1]);
         }
       }
+      __builtin_amdgcn_sched_barrier(0);
+      load_af(afb, buf(1));
     }
-    int hs = 1;
-    for (int c = 0; c < 4; ++c) {
+    // t-block c: 4 c + 2 half-slabs of 4 c rows, then the merged one; its first
+    // half-slab hs0 has its fragments in X
+    auto cblock = [&](int c, int hs0, AFrag& X, AFrag& Y) {
       if (COMPUTE) {
         // q_t of this lane's 8 t's of block c, times qt_scale, as fp16
 #pragma unroll
@@ -705,18 +738,21 @@ k_readout_mfma(int n_q_heads, int n_kv_heads, int seq_len, int n_chunks, int n_h
         }
         cur = -1;
       }
-      for (int h = 0; h < 4 * c + 2; ++h, ++hs) {
-        wait_vmcnt<4>();
-        barrier_nofence();
-        issue(hs + 3, buf(hs + 3));
-        if (COMPUTE) quad(c, h, buf(hs));
+      for (int pr = 0; pr < 2 * c + 1; ++pr) {
+        const int hs = hs0 + 2 * pr;
+        ring_step(hs);
+        if (COMPUTE) quad(c, 2 * pr, X, Y, buf(hs + 1), true);
+        ring_step(hs + 1);
+        if (COMPUTE) quad(c, 2 * pr + 1, Y, X, buf(hs + 2), true);
       }
-      wait_vmcnt<4>();
-      barrier_nofence();
-      issue(hs + 3, buf(hs + 3));
-      if (COMPUTE) quad_merged(c, buf(hs));
-      ++hs;
-    }
+      const int hs = hs0 + 4 * c + 2;
+      ring_step(hs);
+      if (COMPUTE) quad_merged(c, X, Y, buf(hs + 1), hs + 1 < Cfg::NHS);
+    };
+    cblock(0, 1, afb, afa);
+    cblock(1, 4, afa, afb);
+    cblock(2, 11, afb, afa);
+    cblock(3, 22, afa, afb);
     wait_vmcnt<0>();   // the last (repeated) prefetches
   };
   if (head_ok)
