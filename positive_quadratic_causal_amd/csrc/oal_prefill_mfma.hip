@@ -590,11 +590,13 @@ k_readout_mfma(int n_q_heads, int n_kv_heads, int seq_len, int n_chunks, int n_h
     for (int nt = 0; nt < 2; ++nt) u[nt] = *reinterpret_cast<const uint2*>((nt ? qrow1 : qrow0).elem(r0));
     const uint8_t* mgc = mgh + 32 * c;
     int gi[4];
-    f16x8 m8[4];   // M_{g(r), g(t)} / d_h (scaled) of the four rows
+    f16x8 m8[4];   // M_{g(r), g(t)} / d_h (scaled), read only for a row whose group differs from the row before
+    int pg = cur;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       gi[i] = __builtin_amdgcn_readlane(gl, r0 + i);
-      m8[i] = *reinterpret_cast<const f16x8*>(mgc + gi[i] * (DH * 2));
+      if (gi[i] != pg) m8[i] = *reinterpret_cast<const f16x8*>(mgc + gi[i] * (DH * 2));
+      pg = gi[i];
     }
     __builtin_amdgcn_sched_barrier(0);
     if (pf) load_af(nx, nsb);
