@@ -182,9 +182,30 @@ __device__ __forceinline__ uint2 pack4_f16(float a, float b, float c, float d, f
 // sums of beta, then [units][nip] partial maxima of |H_init|.
 __device__ __forceinline__ int tile_scale_exp(const float* bound, int units, int n_blk, int nip,
                                               int unit, int lane) {
+  // 8 loads in flight per lane and round (a rolled loop of single loads waits out
+  // the memory latency once per 64 entries); the sum keeps the entry order
+  constexpr int R = 8;
   float sum = 0.f, mx = 0.f;
-  for (int i = lane; i < n_blk; i += 64) sum += bound[(size_t)unit * n_blk + i];
-  for (int i = lane; i < nip; i += 64) mx = fmaxf(mx, bound[(size_t)units * n_blk + (size_t)unit * nip + i]);
+  for (int i0 = lane; i0 < n_blk; i0 += 64 * R) {
+    float x[R];
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+      const int i = i0 + 64 * j;
+      x[j] = i < n_blk ? bound[(size_t)unit * n_blk + i] : 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < R; ++j) sum += x[j];
+  }
+  for (int i0 = lane; i0 < nip; i0 += 64 * R) {
+    float x[R];
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+      const int i = i0 + 64 * j;
+      x[j] = i < nip ? bound[(size_t)units * n_blk + (size_t)unit * nip + i] : 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < R; ++j) mx = fmaxf(mx, x[j]);
+  }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) {
     sum += __shfl_xor(sum, o, 64);
