@@ -10,10 +10,13 @@ Also reported: batched decode (Llama-3.2-1B-shaped 32/8, batch 64, state
 prefilled from 8192 tokens, 256 single-token steps; ``decode``), a chunk-size
 sweep, the linear-time check against N = 2048, the roofline of the dominant
 kernel of each path (algorithmic flops or bytes per launch over the launch's
-average duration, from HIP events recorded on the launch stream around every
-launch of a second timed pass over the same steps: the events would widen the
-gaps between launches of the pass that gives ``value``), and the float64 CPU
-oracle timed on a bounded sample of the prefill workload (``cpu_baseline``).
+average duration; for the prefill, HIP events recorded on the launch stream
+around that kernel's launches inside the timed steps that give ``value``, about
+1 % of a step; for decode, whose step is that one kernel, around every launch
+of a second pass over the same steps), a per-kernel breakdown (events around
+every launch of another pass: they widen the gaps between launches, so that
+pass is kept out of the timed one), and the float64 CPU oracle timed on a
+bounded sample of the prefill workload (``cpu_baseline``).
 
 Inputs are synthetic (seeded generator in positive_quadratic_causal_amd.synth)
 and resident in HBM before the timed region starts.
@@ -119,13 +122,21 @@ def bench_prefill(oal, w, chunk, steps, warmup, device):
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
+    # the timed steps, with HIP events around the dominant kernel's launches only
+    dominant = "k_readout_mfma" if x["q"].dtype == torch.bfloat16 else "k_readout_vec"
+    oal.oal_profile_reset()
+    oal.oal_profile_filter(dominant)
+    oal.oal_profile_enable(True)
     t0 = time.perf_counter()
     for _ in range(steps):
         step()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    oal.oal_profile_enable(False)
+    oal.oal_profile_filter(None)
+    kt_timed = kernel_times(oal, [dominant])
     ms = (t1 - t0) * 1e3 / steps
-    # per-kernel durations: the same steps again with HIP events around every
+    # per-kernel breakdown: the same steps again with HIP events around every
     # launch (kept out of the timed steps above, whose gaps the events would widen)
     oal.oal_profile_reset()
     oal.oal_profile_enable(True)
@@ -161,7 +172,7 @@ def bench_prefill(oal, w, chunk, steps, warmup, device):
     del graph, y_eager, ws, y, x
     state.free()
     torch.cuda.empty_cache()
-    return ms, kt, (ms_graph if graph_ok else None)
+    return ms, kt, kt_timed, (ms_graph if graph_ok else None)
 
 
 def softmax_flops(w) -> int:
@@ -601,10 +612,13 @@ def copy_probe(mib):
     log(f"copy probe: {mib} MiB x 5")
 
 
-def roofline_prefill(kt, w, chunk):
-    """Roofline of the prefill's dominant kernel (largest total time)."""
+def roofline_prefill(kt, kt_timed, w, chunk):
+    """Roofline of the prefill's dominant kernel (largest total time in the
+    per-kernel breakdown), its launch duration from the timed steps' events."""
     prefill_kernels = {k: v for k, v in kt.items() if k not in ("k_expand", "k_fill_zero")}
     name = max(prefill_kernels, key=lambda k: prefill_kernels[k]["total_ms"])
+    if name in kt_timed:
+        prefill_kernels[name] = kt_timed[name]
     fl = prefill_flops_per_token(w.n_q_heads, w.n_kv_heads, chunk)
     tokens = w.batch * w.seq_len
     bound, peak, unit = KERNEL_BOUND.get(name, ("mfma", PEAK_BF16_TFLOPS, "TFLOP/s"))
@@ -901,7 +915,7 @@ def main() -> int:
         print(json.dumps({"metric": METRIC, "prefill_dim": res}), flush=True)
         return 0
     log(f"prefill: {w3.name}, chunk {args.chunk}, {args.warmup} warmup + {args.steps} steps")
-    ms, kt, ms_graph = bench_prefill(oal, w3, args.chunk, args.steps, args.warmup, device)
+    ms, kt, kt_timed, ms_graph = bench_prefill(oal, w3, args.chunk, args.steps, args.warmup, device)
     tokens = w3.batch * w3.seq_len
     result = {
         "metric": METRIC,
@@ -923,7 +937,7 @@ def main() -> int:
                    "n_kv_heads": w3.n_kv_heads, "seq_len": w3.seq_len, "d_h": 64, "d_v": 64,
                    "groups_per_head": 4, "chunk": args.chunk, "state": "fp32",
                    "parallelism": "single GPU"},
-        "roofline": roofline_prefill(kt, w3, args.chunk),
+        "roofline": roofline_prefill(kt, kt_timed, w3, args.chunk),
         "kernels_ms": {k: round(v["avg_ms"], 5) for k, v in kt.items()},
     }
     fl = prefill_flops_per_token(w3.n_q_heads, w3.n_kv_heads, args.chunk)
@@ -939,17 +953,17 @@ def main() -> int:
                 sweep[str(c)] = round(ms, 5)
                 continue
             log(f"prefill chunk sweep: chunk {c}")
-            msc, _, _ = bench_prefill(oal, w3, c, max(3, args.steps // 4), 2, device)
+            msc, _, _, _ = bench_prefill(oal, w3, c, max(3, args.steps // 4), 2, device)
             sweep[str(c)] = round(msc, 5)
         result["chunk_sweep_ms"] = sweep
         w1 = synth.WORKLOADS[1]
         log("linear-time check: N = 2048")
-        ms1, _, _ = bench_prefill(oal, w1, args.chunk, args.steps, args.warmup, device)
+        ms1, _, _, _ = bench_prefill(oal, w1, args.chunk, args.steps, args.warmup, device)
         result["linear_time_check"] = {"ms_n2048": round(ms1, 5), "ms_n32768": round(ms, 5),
                                        "ratio": round(ms / ms1, 3), "ideal_ratio": 16.0}
         w2 = synth.WORKLOADS[2]
         log(f"prefill: {w2.name}, chunk {args.chunk}")
-        ms2, kt2, _ = bench_prefill(oal, w2, args.chunk, args.steps, args.warmup, device)
+        ms2, kt2, _, _ = bench_prefill(oal, w2, args.chunk, args.steps, args.warmup, device)
         fl2 = prefill_flops_per_token(w2.n_q_heads, w2.n_kv_heads, args.chunk)["total"] * w2.batch * w2.seq_len
         result["prefill_llama_b4_n4096"] = {
             "workload": w2.name, "chunk": args.chunk, "ms_per_step": round(ms2, 5),

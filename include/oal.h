@@ -343,9 +343,13 @@ oal_status oal_softmax_attention(int batch, int n_q_heads, int n_kv_heads, int s
  * records a pair of HIP events on the launch stream around every kernel it
  * launches.  oal_profile_query waits for the pending events of the named kernel
  * ("k_decode", "k_readout_vec", ...; NULL = all kernels) and returns their total
- * duration and launch count since the last reset.  Host-global, not thread-safe
- * against concurrent launches from several threads. */
+ * duration and launch count since the last reset.  oal_profile_filter restricts
+ * the events to the kernel of that name (NULL: every kernel again), so that one
+ * kernel can be timed inside a sequence of launches without widening the gaps
+ * between the others.  Host-global, not thread-safe against concurrent launches
+ * from several threads. */
 oal_status oal_profile_enable(int enable);
+oal_status oal_profile_filter(const char* kernel);
 oal_status oal_profile_reset(void);
 oal_status oal_profile_query(const char* kernel, double* total_ms, int64_t* launches);
 

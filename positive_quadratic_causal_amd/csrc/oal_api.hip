@@ -44,6 +44,7 @@ struct ProfTotals {
 };
 std::mutex g_prof_mu;
 bool g_prof_on = false;
+std::string g_prof_only;   // when not empty: the one kernel that gets events
 std::vector<ProfEntry> g_prof_pending;
 std::vector<hipEvent_t> g_prof_pool;
 std::map<std::string, ProfTotals> g_prof_totals;
@@ -81,6 +82,7 @@ oal_status prof_drain() {
 int prof_begin(const char* kernel, hipStream_t stream) {
   std::lock_guard<std::mutex> lk(g_prof_mu);
   if (!g_prof_on) return -1;
+  if (!g_prof_only.empty() && g_prof_only != kernel) return -1;
   hipEvent_t a = prof_event(), b = prof_event();
   if (!a || !b) return -1;
   if (hipEventRecord(a, stream) != hipSuccess) return -1;
@@ -188,6 +190,12 @@ const char* oal_last_error(void) { return g_last_error; }
 oal_status oal_profile_enable(int enable) {
   std::lock_guard<std::mutex> lk(g_prof_mu);
   g_prof_on = enable != 0;
+  return OAL_OK;
+}
+
+oal_status oal_profile_filter(const char* kernel) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  g_prof_only = kernel ? kernel : "";
   return OAL_OK;
 }
 

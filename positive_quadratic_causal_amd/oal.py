@@ -83,6 +83,7 @@ def _load() -> ctypes.CDLL:
         "oal_softmax_attention": (c_int, [c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_void,
                                           c_void, c_void, c_void, c_int, c_void]),
         "oal_profile_enable": (c_int, [c_int]),
+        "oal_profile_filter": (c_int, [ctypes.c_char_p]),
         "oal_profile_reset": (c_int, []),
         "oal_profile_query": (c_int, [ctypes.c_char_p, ctypes.POINTER(ctypes.c_double),
                                       ctypes.POINTER(ctypes.c_int64)]),
@@ -107,7 +108,7 @@ EXPORTED = ("oal_coeffs_bytes", "oal_expand_coeffs", "oal_dim_coeffs", "oal_stat
             "oal_embed_global",
             "oal_contribution_scores", "oal_bootstrap_grouping",
             "oal_decode_step", "oal_softmax_attention", "oal_profile_enable", "oal_profile_reset",
-            "oal_profile_query",
+            "oal_profile_query", "oal_profile_filter",
             "oal_status_string", "oal_last_error")
 
 
@@ -499,6 +500,11 @@ def oal_state_tokens(state: OalState) -> int:
 
 def oal_profile_enable(enable: bool = True) -> None:
     _check(_lib.oal_profile_enable(1 if enable else 0))
+
+
+def oal_profile_filter(kernel: str | None = None) -> None:
+    """Record profiling events around the named kernel only (None: every kernel)."""
+    _check(_lib.oal_profile_filter(kernel.encode() if kernel else None))
 
 
 def oal_profile_reset() -> None:
