@@ -119,6 +119,36 @@ def test_prefill_ragged(oal, n, chunk, dtype):
     _check_heads(case, y, [(b, h) for b in range(2) for h in range(6)], tol_for(w))
 
 
+@pytest.mark.parametrize("chunk", [64, 128, 256])
+def test_prefill_mha_bf16(oal, chunk):
+    """One query head per KV head (rep = 1): at chunk 128 every head group of the
+    matrix-core readout holds one head and one idle slot."""
+    w = synth.small_workload(310 + chunk, "mha", 2, 3, 3, 300, "bf16")
+    announce(f"prefill MHA B=2 3/3 N=300 chunk={chunk} bf16")
+    case = Case(w)
+    y = _prefill(oal, case, chunk)
+    torch.cuda.synchronize()
+    _check_heads(case, y, [(b, h) for b in range(2) for h in range(3)], tol_for(w))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_prefill_zero_length_is_a_no_op(oal, dtype):
+    """seq_len = 0 returns OK and leaves the state (values and token count) as it was."""
+    w = synth.small_workload(320, "zero length", 1, 4, 2, 90, dtype)
+    announce(f"prefill of zero tokens after 90 {dtype}")
+    case = Case(w)
+    st = oal.oal_state_alloc(1, 2)
+    _prefill(oal, case, 64, state=st)
+    before = oal.oal_state_export(st).clone()
+    empty_q = case.q[:, :, :0].contiguous()
+    empty_kv = case.k[:, :, :0].contiguous(), case.v[:, :, :0].contiguous()
+    y = oal.oal_prefill(empty_q, *empty_kv, case.coeffs(), chunk=128, state=st)
+    torch.cuda.synchronize()
+    assert y.shape == (1, 4, 0, 64)
+    assert st.tokens == 90
+    assert torch.equal(oal.oal_state_export(st), before)
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_prefill_continues_from_state(oal, dtype):
     """prefill(N1) then prefill(N2) from the state == the last N2 outputs of
