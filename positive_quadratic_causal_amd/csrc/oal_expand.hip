@@ -17,36 +17,26 @@ k_expand(int g_max, const int32_t* __restrict__ n_groups, const int32_t* __restr
   __shared__ float sL[LDIM][LDIM];
   __shared__ float sM[LDIM][LDIM];
   __shared__ int sg[DH];
-  __shared__ int sG;
   float* rec = coeffs + (size_t)h * OAL_COEF_WORDS;
 
-  if (tid == 0) {
-    int G = n_groups[h];
-    sG = G < 1 ? 1 : (G > g_max ? g_max : G);
-  }
-  __syncthreads();
-  const int G = sG;
-  if (tid < LDIM * LDIM) {
-    int u = tid / LDIM, v = tid % LDIM;
-    float x = 0.f;
-    if (u <= G && v <= G && v <= u) x = Lin[(size_t)h * ld * ld + u * ld + v];
-    sL[u][v] = x;
-  }
-  if (tid < DH) {
-    int gr = group_map[(size_t)h * DH + tid];
-    sg[tid] = gr < 1 ? 1 : (gr > G ? G : gr);
-  }
-  __syncthreads();
-  if (tid < LDIM * LDIM) {
-    int u = tid / LDIM, v = tid % LDIM;
-    double m = 0.0;
-    for (int p = 0; p < LDIM; ++p) m += (double)sL[u][p] * (double)sL[v][p];
-    sM[u][v] = (float)m;
-  }
-  __syncthreads();
-
-  // zero the whole record first so padding words are defined
+  // Every input load and the zeroing of the record (so that padding words are
+  // defined) are issued before the first barrier: the chain of global round
+  // trips is one deep.  L is read only inside the g_max + 1 square of the head.
+  const int G_in = n_groups[h];
+  float lval = 0.f;
+  const int lu = tid / LDIM, lv = tid % LDIM;
+  if (tid < LDIM * LDIM && lu <= g_max && lv <= g_max) lval = Lin[(size_t)h * ld * ld + lu * ld + lv];
+  const int gr_in = tid < DH ? group_map[(size_t)h * DH + tid] : 1;
   for (int i = tid; i < OAL_COEF_WORDS; i += blockDim.x) rec[i] = 0.f;
+  const int G = G_in < 1 ? 1 : (G_in > g_max ? g_max : G_in);
+  if (tid < LDIM * LDIM) sL[lu][lv] = (lu <= G && lv <= G && lv <= lu) ? lval : 0.f;
+  if (tid < DH) sg[tid] = gr_in < 1 ? 1 : (gr_in > G ? G : gr_in);
+  __syncthreads();   // also orders the zeroing before the stores below
+  if (tid < LDIM * LDIM) {
+    double m = 0.0;
+    for (int p = 0; p < LDIM; ++p) m += (double)sL[lu][p] * (double)sL[lv][p];
+    sM[lu][lv] = (float)m;
+  }
   __syncthreads();
 
   const float inv_sqrt_d = 0.125f;   // 1 / sqrt(64)
