@@ -271,7 +271,7 @@ k_readout_mfma(int n_q_heads, int n_kv_heads, int seq_len, int n_chunks, int n_h
   float* ht = s_ht + hslot * htab::FLOATS;
   const uint64_t cmask = __ballot(gl >= 2);   // dims of the groups 2..G
   const int n_out = __popcll(cmask);
-  const bool compact = n_out <= 16;            // t_p, p >= 2, from one 16-deep K-step
+  const bool compact = n_out <= 14;            // t_p from one 16-deep K-step (+ 2 constant slots)
   if (head_ok) {
 #pragma unroll
     for (int p = 0; p < LDIM; ++p) ht[htab::ELL + p * DH + lane] = ellv[p] * sroot;
@@ -281,9 +281,13 @@ k_readout_mfma(int n_q_heads, int n_kv_heads, int seq_len, int n_chunks, int n_h
     ht[htab::BZ + lane] = bval * z1v * ldexpf(1.0f, -e_m);
     if (compact) {
       int* cidx = reinterpret_cast<int*>(ht + htab::CIDX);
-      float c1[LDIM];   // L_{1,p} / sqrt(d_h), read across lanes before the branch below
+      float c1[LDIM];   // L_{1,p} / sqrt(d_h), read across lanes before the branches below
+      float l0s[LDIM];  // L_{0,p} 2^(E/2)
 #pragma unroll
-      for (int p = 0; p < LDIM; ++p) c1[p] = __shfl(l1v, p, 64) * 0.125f;
+      for (int p = 0; p < LDIM; ++p) {
+        c1[p] = __shfl(l1v, p, 64) * 0.125f;
+        l0s[p] = __shfl(l0v, p, 64) * sroot;
+      }
       if (gl >= 2) {
         const int rank = __builtin_amdgcn_mbcnt_hi((uint32_t)(cmask >> 32),
                                                    __builtin_amdgcn_mbcnt_lo((uint32_t)cmask, 0));
@@ -293,9 +297,14 @@ k_readout_mfma(int n_q_heads, int n_kv_heads, int seq_len, int n_chunks, int n_h
           ht[htab::ELLC + p * 16 + rank] = (ellv[p] - c1[p]) * sroot;
       }
       if (lane >= n_out && lane < 16) {
+        // slots 14 and 15 carry L_{0,p} (a bf16-exact high part and the rest)
+        // against key and query entries of 1: the product's constant term
         cidx[lane] = 0;
 #pragma unroll
-        for (int p = 0; p < LDIM; ++p) ht[htab::ELLC + p * 16 + lane] = 0.f;
+        for (int p = 0; p < LDIM; ++p) {
+          const float hi = __uint_as_float(__float_as_uint(l0s[p]) & 0xffff0000u);
+          ht[htab::ELLC + p * 16 + lane] = lane == 14 ? hi : lane == 15 ? l0s[p] - hi : 0.f;
+        }
       }
     }
   }
@@ -429,10 +438,10 @@ k_readout_mfma(int n_q_heads, int n_kv_heads, int seq_len, int n_chunks, int n_h
   // the ones channel as column sums into the denominator).  ell_p[r] = L_{g(r),p} /
   // sqrt(d_h) equals c_p = L_{1,p} / sqrt(d_h) on group 1, so with S = q . k
   //   t_p = sqrt(F) (L_0p + c_p S + sum_{g(r) >= 2} (ell_p[r] - c_p) q_r k_r);
-  // when at most 16 dims lie outside group 1 (compact), S is one 64-deep product of
-  // the raw inputs and each t_p one 16-deep product over the gathered outlier dims,
-  // seeded with L_0p + c_p S.  Otherwise each t_p is a 64-deep product with
-  // A = k o ell_p.
+  // when at most 14 dims lie outside group 1 (compact), S is one 64-deep product of
+  // the raw inputs and each t_p one 16-deep product over the gathered outlier dims
+  // plus two constant slots that add L_0p, seeded with c_p S (zero for p >= 2).
+  // Otherwise each t_p is a 64-deep product with A = k o ell_p, seeded with L_0p.
   if (head_ok) {
     const float epsF = rec[OAL_COEF_EPS] * F;
     const int* cidx = reinterpret_cast<const int*>(ht + htab::CIDX) + 8 * half;
@@ -441,8 +450,9 @@ k_readout_mfma(int n_q_heads, int n_kv_heads, int seq_len, int n_chunks, int n_h
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int d = cidx[j];
-        qc[0][j] = *qrow0.elem(d);
-        qc[1][j] = *qrow1.elem(d);
+        const bool one = half && j >= 6;           // the constant slots 14, 15
+        qc[0][j] = one ? (__bf16)1.0f : *qrow0.elem(d);
+        qc[1][j] = one ? (__bf16)1.0f : *qrow1.elem(d);
       }
     }
     // One 32-key tile.  DO0: token tile 0 is not entirely masked; MASKn: token
@@ -466,7 +476,7 @@ k_readout_mfma(int n_q_heads, int n_kv_heads, int seq_len, int n_chunks, int n_h
         }
         float kc[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) kc[j] = bf(*krow.elem(cidx[j]));
+        for (int j = 0; j < 8; ++j) kc[j] = (half && j >= 6) ? 1.0f : bf(*krow.elem(cidx[j]));
         for (int p = 0; p <= G; ++p) {
           const float* ec = ht + htab::ELLC + p * 16 + 8 * half;
           const float4 e0 = *reinterpret_cast<const float4*>(ec);
@@ -474,16 +484,16 @@ k_readout_mfma(int n_q_heads, int n_kv_heads, int seq_len, int n_chunks, int n_h
           const float x[8] = {kc[0] * e0.x, kc[1] * e0.y, kc[2] * e0.z, kc[3] * e0.w,
                               kc[4] * e1.x, kc[5] * e1.y, kc[6] * e1.z, kc[7] * e1.w};
           const bf16x8 akc = pack8(x);
-          const float l0 = ht[htab::L0 + p], cp = ht[htab::CP + p];
+          const float cp = ht[htab::CP + p];
 #pragma unroll
           for (int nt = 0; nt < 2; ++nt) {
             if (nt == 0 && !DO0) continue;
-            f32x16 seed;
+            f32x16 seed;   // L_{0,p} comes from the constant slots
             if (p <= 1) {
 #pragma unroll
-              for (int i = 0; i < 16; ++i) seed[i] = fmaf(cp, S[nt][i], l0);
+              for (int i = 0; i < 16; ++i) seed[i] = cp * S[nt][i];
             } else {
-              seed = splat16(l0);   // c_p = 0 for p >= 2 (L is lower triangular)
+              seed = splat16(0.f);   // c_p = 0 for p >= 2 (L is lower triangular)
             }
             const f32x16 t = mfma32(akc, qc[nt], seed);
 #pragma unroll
