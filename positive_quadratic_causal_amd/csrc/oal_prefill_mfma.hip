@@ -18,7 +18,9 @@ namespace oal {
 
 // ---------------------------------------------------------------------------
 // Readout.  Workgroup = 4 waves = (256 / C) query heads of one KV group x C
-// tokens of one chunk; wave = one head x 64 tokens.  In the u~^T orientation
+// tokens of one chunk; wave = one head x 64 tokens (token tiles sub and
+// 2 WPH - 1 - sub of 32 tokens, sub = the wave's index within its head, so that
+// each wave meets an equal share of the causal triangle).  In the u~^T orientation
 // (rows = value channel w, columns = tokens) each wave owns a 64 x 64 tile of
 // fp32 accumulators (2 x 2 MFMA tiles).
 //
@@ -117,8 +119,6 @@ k_readout_mfma(int n_q_heads, int n_kv_heads, int seq_len, int n_chunks, int n_h
   __shared__ __attribute__((aligned(16))) float s_ht[Cfg::HPW * htab::FLOATS];
   __shared__ float s_red[16];
   __shared__ __attribute__((aligned(16))) float s_h0[DV];   // H0 of the chunk's prefix
-  // inter-chunk denominators of the mirror waves' tokens, per (head, wave pair)
-  __shared__ float s_dx[Cfg::HPW * (Cfg::WPH > 1 ? Cfg::WPH / 2 : 1) * 64];
   // k rows (64 per array) and v^T rows (64 keys per array) of the chunk
   auto k_arr = [&](int i) -> uint8_t* { return pick4(i, s_b0, s_b1, s_b2, s_b3); };
   auto v_arr = [&](int i) -> uint8_t* {
@@ -189,6 +189,25 @@ k_readout_mfma(int n_q_heads, int n_kv_heads, int seq_len, int n_chunks, int n_h
   const float z1v = ts_side[tile::SIDE_Z1 + lane];
   const float h0v = ts_side[tile::SIDE_H0 + lane];   // read in the epilogue, from LDS
   const float esv = ts_side[tile::SIDE_SEXP];
+  // Z rows 32 mt + col, columns 16 ks + 8 half .. + 7: the inter-chunk
+  // denominator's operand.  With several waves per head (C >= 128) it is loaded
+  // once the staging's loads are consumed, so that its latency overlaps the
+  // reductions, barrier and tables, and the denominator is computed before the
+  // intra-chunk part; with one (C = 64, four
+  // heads staged, where holding it would spill) it is loaded in place, after the
+  // intra-chunk barrier, while the first half-slabs load.
+  constexpr bool ZPRE = Cfg::WPH > 1;
+  float4 zv[2][4][2];
+  auto load_z = [&]() {
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int e = 0; e < 2; ++e)
+          zv[mt][ks][e] = *reinterpret_cast<const float4*>(ts_side + tile::SIDE_Z + (32 * mt + col) * DH +
+                                                           16 * ks + 8 * half + 4 * e);
+  };
 
   // ---- q tile, with each thread's max |q| per head
   uint32_t qmax[Cfg::HPW];
@@ -231,6 +250,10 @@ k_readout_mfma(int n_q_heads, int n_kv_heads, int seq_len, int n_chunks, int n_h
     }
   }
 
+  // (after the staging's last use of its loads: memory operations complete in
+  // order, so no later wait of the staging waits for these)
+  __builtin_amdgcn_sched_barrier(0);
+  if (ZPRE) load_z();
   // ---- this head's coefficient magnitudes (wave-uniform)
   const int e_m = exp_above(wave_max(lane < LDIM * LDIM ? fabsf(mval) * (1.0f / DH) : 0.f));
   const int e_b = exp_above(wave_max(fabsf(bval)));
@@ -309,9 +332,11 @@ k_readout_mfma(int n_q_heads, int n_kv_heads, int seq_len, int n_chunks, int n_h
     }
   }
 
-  const int tok0 = sub * 64;                 // first token of this wave in the chunk
+  // token tiles of this wave (32 tokens each): sub and 2 WPH - 1 - sub, so that
+  // the waves of a head meet equal parts of the causal triangle inside the chunk
+  const int T0 = sub, T1 = 2 * Cfg::WPH - 1 - sub;
   const uint8_t* qw = s_q + hslot * CH * 128;
-  const SwRow qrow0(qw, tok0 + col), qrow1(qw, tok0 + 32 + col);   // tokens of N-tiles 0, 1
+  const SwRow qrow0(qw, 32 * T0 + col), qrow1(qw, 32 * T1 + col);   // tokens of N-tiles 0, 1
   // q fragment (B operand, columns = tokens, K = head dims): exact bf16 inputs
   auto qfrag = [&](int nt, int ks) {
     return *reinterpret_cast<const bf16x8*>((nt ? qrow1 : qrow0).chunk(2 * ks + half));
@@ -354,37 +379,21 @@ k_readout_mfma(int n_q_heads, int n_kv_heads, int seq_len, int n_chunks, int n_h
 
   // ---- inter-chunk denominator: a z0 + sum_r q_r (b'_r z1_r + ((C / d_h o Z) q)_r),
   //      T = b' o z1 + (C/d_h o Z) q^T on the matrix cores (the first term as the
-  //      accumulator seed); C/d_h from the head's M_{g(n),g(t)}/d_h 2^-e_M table.
-  //      The waves of a head have unequal intra-chunk parts (wave sub meets
-  //      2 sub + 2 key tiles), and the barrier behind that part waits for the
-  //      longest.  So wave sub < WPH / 2 computes the denominators of its own
-  //      tokens and of the mirror wave WPH - 1 - sub before its intra-chunk part
-  //      (one Z operand serves both), handing the latter over through LDS; the
-  //      mirror waves compute none.  With one wave per head (no imbalance) the
-  //      wave computes its own after the barrier, while the first half-slabs load.
-  constexpr bool PAIRED = Cfg::WPH > 1;
-  const bool den_giver = !PAIRED || sub < Cfg::WPH / 2;
-  const int msub = Cfg::WPH - 1 - sub;   // the mirror wave of a giver
-  float* dx = s_dx + (hslot * (PAIRED ? Cfg::WPH / 2 : 1) + min(sub, msub)) * 64;   // this pair's slots
-  auto denominator = [&](auto two_t) {
-    constexpr bool TWO = decltype(two_t)::value;
-    constexpr int NT = TWO ? 4 : 2;
-    const SwRow rows[4] = {qrow0, qrow1, SwRow(qw, 64 * msub + col), SwRow(qw, 64 * msub + 32 + col)};
-    const float* Zs = ts_side + tile::SIDE_Z;
-    float dd[NT];
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) dd[nt] = 0.f;
+  //      accumulator seed); C/d_h from the head's M_{g(n),g(t)}/d_h 2^-e_M table
+  auto denominator = [&]() {
+    if (!ZPRE) load_z();
+    float dd[2] = {0.f, 0.f};
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
       const int n = 32 * mt + col;
       const int gn = __shfl(gl, n, 64);   // g(n)
       const _Float16* mrow = s_mg + (hslot * LDIM + gn) * DH + 8 * half;
-      f32x16 T[NT];
+      f32x16 T[2];
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         const float4 bz = *reinterpret_cast<const float4*>(ht + htab::BZ + 32 * mt + 8 * g4 + 4 * half);
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
+        for (int nt = 0; nt < 2; ++nt) {
           T[nt][4 * g4 + 0] = bz.x;
           T[nt][4 * g4 + 1] = bz.y;
           T[nt][4 * g4 + 2] = bz.z;
@@ -393,22 +402,21 @@ k_readout_mfma(int n_q_heads, int n_kv_heads, int seq_len, int n_chunks, int n_h
       }
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        const float4 z0 = *reinterpret_cast<const float4*>(Zs + n * DH + 16 * ks + 8 * half);
-        const float4 z1 = *reinterpret_cast<const float4*>(Zs + n * DH + 16 * ks + 8 * half + 4);
+        const float4 z0 = zv[mt][ks][0], z1 = zv[mt][ks][1];
         const f16x8 m8 = *reinterpret_cast<const f16x8*>(mrow + 16 * ks);
         const float x[8] = {z0.x * (float)m8[0], z0.y * (float)m8[1], z0.z * (float)m8[2], z0.w * (float)m8[3],
                             z1.x * (float)m8[4], z1.y * (float)m8[5], z1.z * (float)m8[6], z1.w * (float)m8[7]};
         const bf16x8 az = pack8(x);
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
-          T[nt] = mfma32(az, *reinterpret_cast<const bf16x8*>(rows[nt].chunk(2 * ks + half)), T[nt]);
+        for (int nt = 0; nt < 2; ++nt) T[nt] = mfma32(az, qfrag(nt, ks), T[nt]);
       }
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
+      for (int nt = 0; nt < 2; ++nt) {
+        const SwRow& qr = nt ? qrow1 : qrow0;
         float d = 0.f;
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {   // rows 32 mt + 8 g4 + 4 half + e, e = 0..3
-          const uint2 u = *reinterpret_cast<const uint2*>(rows[nt].elem(32 * mt + 8 * g4 + 4 * half));
+          const uint2 u = *reinterpret_cast<const uint2*>(qr.elem(32 * mt + 8 * g4 + 4 * half));
           d = fmaf(__uint_as_float(u.x << 16), T[nt][4 * g4 + 0], d);
           d = fmaf(__uint_as_float(u.x & 0xffff0000u), T[nt][4 * g4 + 1], d);
           d = fmaf(__uint_as_float(u.y << 16), T[nt][4 * g4 + 2], d);
@@ -421,16 +429,8 @@ k_readout_mfma(int n_q_heads, int n_kv_heads, int seq_len, int n_chunks, int n_h
     const float sc = ldexpf(F, e_m);
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) den[nt] += dd[nt] * sc + az0 * F;
-    if (TWO) {
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {   // whole sums (both lane halves) of the mirror's tokens
-        float x = dd[NT - 2 + nt] * sc + az0 * F;
-        x += __shfl_xor(x, 32, 64);
-        if (half == 0) dx[32 * nt + col] = x;
-      }
-    }
   };
-  if (PAIRED && head_ok && den_giver) denominator(bool_t<true>{});
+  if (ZPRE && head_ok) denominator();
 
   // ================= intra-chunk part ======================================
   // kappa^T[key][tok] F = eps F + sum_p t_p^2,  t_p = sqrt(F) (L_0p + sum_r ell_p[r] q_r k_r),
@@ -559,9 +559,12 @@ k_readout_mfma(int n_q_heads, int n_kv_heads, int seq_len, int n_chunks, int n_h
         }
       }
     };
-    for (int kt = 0; kt < 2 * sub; ++kt) key_tile(kt, bool_t<true>{}, bool_t<false>{}, bool_t<false>{});
-    key_tile(2 * sub, bool_t<true>{}, bool_t<true>{}, bool_t<false>{});
-    key_tile(2 * sub + 1, bool_t<false>{}, bool_t<false>{}, bool_t<true>{});
+    // key tiles 0 .. T1: both token tiles up to T0 (T0 the diagonal one of N-tile
+    // 0), then N-tile 1 alone (T1 its diagonal one)
+    for (int kt = 0; kt < T0; ++kt) key_tile(kt, bool_t<true>{}, bool_t<false>{}, bool_t<false>{});
+    key_tile(T0, bool_t<true>{}, bool_t<true>{}, bool_t<false>{});
+    for (int kt = T0 + 1; kt < T1; ++kt) key_tile(kt, bool_t<false>{}, bool_t<false>{}, bool_t<false>{});
+    key_tile(T1, bool_t<false>{}, bool_t<false>{}, bool_t<true>{});
   }
 
   // ================= inter-chunk part ======================================
@@ -570,7 +573,7 @@ k_readout_mfma(int n_q_heads, int n_kv_heads, int seq_len, int n_chunks, int n_h
   issue(1, buf(1));
   issue(2, buf(2));
   issue(3, buf(3));
-  if (!PAIRED && head_ok) denominator(bool_t<false>{});
+  if (!ZPRE && head_ok) denominator();
 
   // ---- main K loop over the 37 half-slabs: 1 linear, then 4 c + 3 per t-block c
   //      (the last of them the merged rows of the diagonal block); half-slab hs
@@ -777,12 +780,11 @@ k_readout_mfma(int n_q_heads, int n_kv_heads, int seq_len, int n_chunks, int n_h
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt) {
     den[nt] += __shfl_xor(den[nt], 32, 64);
-    if (!den_giver) den[nt] += dx[32 * nt + col];   // written before the intra-chunk barrier
   }
   const float aF = rec[OAL_COEF_A] * F;
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt) {
-    const int tok = tok0 + 32 * nt + col;
+    const int tok = 32 * (nt ? T1 : T0) + col;
     if (tok >= clen) continue;
     // NG = 0 marks a dimension-specific record, which this grouped readout
     // cannot evaluate: its outputs are made NaN rather than silently wrong
