@@ -119,6 +119,8 @@ k_readout_mfma(int n_q_heads, int n_kv_heads, int seq_len, int n_chunks, int n_h
   __shared__ __attribute__((aligned(16))) float s_ht[Cfg::HPW * htab::FLOATS];
   __shared__ float s_red[16];
   __shared__ __attribute__((aligned(16))) float s_h0[DV];   // H0 of the chunk's prefix
+  // inter-chunk denominators handed to the mirror waves, per (head, wave pair)
+  __shared__ float s_dx[Cfg::HPW * (Cfg::WPH > 1 ? Cfg::WPH / 2 : 1) * 64];
   // k rows (64 per array) and v^T rows (64 keys per array) of the chunk
   auto k_arr = [&](int i) -> uint8_t* { return pick4(i, s_b0, s_b1, s_b2, s_b3); };
   auto v_arr = [&](int i) -> uint8_t* {
@@ -142,6 +144,12 @@ k_readout_mfma(int n_q_heads, int n_kv_heads, int seq_len, int n_chunks, int n_h
   const int lane = tid & 63;
   const int col = lane & 31, half = lane >> 5;
   const int hslot = wave / Cfg::WPH, sub = wave % Cfg::WPH;
+  // Wave sub >= WPH / 2 meets one key tile fewer inside the chunk than its
+  // mirror WPH - 1 - sub (token tiles below): it computes the inter-chunk
+  // denominators of both (one Z operand) and hands the mirror's over through LDS.
+  constexpr bool PAIRED = Cfg::WPH > 1;
+  const bool den_giver = !PAIRED || sub >= Cfg::WPH / 2;
+  const int msub = Cfg::WPH - 1 - sub;
   const int hl = hg * Cfg::HPW + hslot;
   const bool head_ok = hl < rep;
   const int hq = kv * rep + (head_ok ? hl : 0);
@@ -253,7 +261,7 @@ k_readout_mfma(int n_q_heads, int n_kv_heads, int seq_len, int n_chunks, int n_h
   // (after the staging's last use of its loads: memory operations complete in
   // order, so no later wait of the staging waits for these)
   __builtin_amdgcn_sched_barrier(0);
-  if (ZPRE) load_z();
+  if (ZPRE && den_giver) load_z();
   // ---- this head's coefficient magnitudes (wave-uniform)
   const int e_m = exp_above(wave_max(lane < LDIM * LDIM ? fabsf(mval) * (1.0f / DH) : 0.f));
   const int e_b = exp_above(wave_max(fabsf(bval)));
@@ -380,20 +388,27 @@ k_readout_mfma(int n_q_heads, int n_kv_heads, int seq_len, int n_chunks, int n_h
   // ---- inter-chunk denominator: a z0 + sum_r q_r (b'_r z1_r + ((C / d_h o Z) q)_r),
   //      T = b' o z1 + (C/d_h o Z) q^T on the matrix cores (the first term as the
   //      accumulator seed); C/d_h from the head's M_{g(n),g(t)}/d_h 2^-e_M table
-  auto denominator = [&]() {
+  float* dx = s_dx + (hslot * (PAIRED ? Cfg::WPH / 2 : 1) + min(sub, msub)) * 64;   // this pair's slots
+  auto denominator = [&](auto two_t) {
+    constexpr bool TWO = decltype(two_t)::value;
+    constexpr int NT = TWO ? 4 : 2;
     if (!ZPRE) load_z();
-    float dd[2] = {0.f, 0.f};
+    // N-tiles 0, 1 of this wave, then (TWO) those of its mirror
+    const SwRow rows[4] = {qrow0, qrow1, SwRow(qw, 32 * msub + col), SwRow(qw, 32 * (2 * Cfg::WPH - 1 - msub) + col)};
+    float dd[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) dd[nt] = 0.f;
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
       const int n = 32 * mt + col;
       const int gn = __shfl(gl, n, 64);   // g(n)
       const _Float16* mrow = s_mg + (hslot * LDIM + gn) * DH + 8 * half;
-      f32x16 T[2];
+      f32x16 T[NT];
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         const float4 bz = *reinterpret_cast<const float4*>(ht + htab::BZ + 32 * mt + 8 * g4 + 4 * half);
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
+        for (int nt = 0; nt < NT; ++nt) {
           T[nt][4 * g4 + 0] = bz.x;
           T[nt][4 * g4 + 1] = bz.y;
           T[nt][4 * g4 + 2] = bz.z;
@@ -408,15 +423,15 @@ k_readout_mfma(int n_q_heads, int n_kv_heads, int seq_len, int n_chunks, int n_h
                             z1.x * (float)m8[4], z1.y * (float)m8[5], z1.z * (float)m8[6], z1.w * (float)m8[7]};
         const bf16x8 az = pack8(x);
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) T[nt] = mfma32(az, qfrag(nt, ks), T[nt]);
+        for (int nt = 0; nt < NT; ++nt)
+          T[nt] = mfma32(az, *reinterpret_cast<const bf16x8*>(rows[nt].chunk(2 * ks + half)), T[nt]);
       }
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        const SwRow& qr = nt ? qrow1 : qrow0;
+      for (int nt = 0; nt < NT; ++nt) {
         float d = 0.f;
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {   // rows 32 mt + 8 g4 + 4 half + e, e = 0..3
-          const uint2 u = *reinterpret_cast<const uint2*>(qr.elem(32 * mt + 8 * g4 + 4 * half));
+          const uint2 u = *reinterpret_cast<const uint2*>(rows[nt].elem(32 * mt + 8 * g4 + 4 * half));
           d = fmaf(__uint_as_float(u.x << 16), T[nt][4 * g4 + 0], d);
           d = fmaf(__uint_as_float(u.x & 0xffff0000u), T[nt][4 * g4 + 1], d);
           d = fmaf(__uint_as_float(u.y << 16), T[nt][4 * g4 + 2], d);
@@ -429,8 +444,16 @@ k_readout_mfma(int n_q_heads, int n_kv_heads, int seq_len, int n_chunks, int n_h
     const float sc = ldexpf(F, e_m);
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) den[nt] += dd[nt] * sc + az0 * F;
+    if (TWO) {
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {   // whole sums (both lane halves) of the mirror's tokens
+        float xm = dd[NT - 2 + nt] * sc + az0 * F;
+        xm += __shfl_xor(xm, 32, 64);
+        if (half == 0) dx[32 * nt + col] = xm;
+      }
+    }
   };
-  if (ZPRE && head_ok) denominator();
+  if (ZPRE && head_ok && den_giver) denominator(bool_t<PAIRED>{});
 
   // ================= intra-chunk part ======================================
   // kappa^T[key][tok] F = eps F + sum_p t_p^2,  t_p = sqrt(F) (L_0p + sum_r ell_p[r] q_r k_r),
@@ -573,7 +596,7 @@ k_readout_mfma(int n_q_heads, int n_kv_heads, int seq_len, int n_chunks, int n_h
   issue(1, buf(1));
   issue(2, buf(2));
   issue(3, buf(3));
-  if (!ZPRE && head_ok) denominator();
+  if (!ZPRE && head_ok) denominator(bool_t<false>{});
 
   // ---- main K loop over the 37 half-slabs: 1 linear, then 4 c + 3 per t-block c
   //      (the last of them the merged rows of the diagonal block); half-slab hs
@@ -780,6 +803,7 @@ k_readout_mfma(int n_q_heads, int n_kv_heads, int seq_len, int n_chunks, int n_h
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt) {
     den[nt] += __shfl_xor(den[nt], 32, 64);
+    if (!den_giver) den[nt] += dx[32 * nt + col];   // written before the intra-chunk barrier
   }
   const float aF = rec[OAL_COEF_A] * F;
 #pragma unroll
