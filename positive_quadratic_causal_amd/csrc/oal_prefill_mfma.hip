@@ -806,9 +806,13 @@ k_readout_mfma(int n_q_heads, int n_kv_heads, int seq_len, int n_chunks, int n_h
     if (!den_giver) den[nt] += dx[32 * nt + col];   // written before the intra-chunk barrier
   }
   const float aF = rec[OAL_COEF_A] * F;
+  // the lane's column taken afresh: the compiler would otherwise compute the
+  // token offsets before the main loop and keep them spilled across it
+  int col_e = (int)(threadIdx.x & 31);
+  asm volatile("" : "+v"(col_e));
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt) {
-    const int tok = 32 * (nt ? T1 : T0) + col;
+    const int tok = 32 * (nt ? T1 : T0) + col_e;
     if (tok >= clen) continue;
     // NG = 0 marks a dimension-specific record, which this grouped readout
     // cannot evaluate: its outputs are made NaN rather than silently wrong
