@@ -68,6 +68,16 @@ def prefill_flops_per_token(n_q: int, n_kv: int, chunk: int) -> dict:
             "total": build + readout + intra}
 
 
+def decode_bytes_per_step(batch: int, n_q: int, n_kv: int) -> int:
+    """Algorithmic HBM bytes of one decode step: the fp32 state of every (batch,
+    KV head) unit read and written once, bf16 q, k, v in and bf16 y out."""
+    units = batch * n_kv
+    return (units * 2 * D_CANON * W * 4         # state read + write
+            + 2 * (batch * n_q * 64)            # q in (bf16)
+            + 2 * 2 * (units * 64)              # k, v in (bf16)
+            + 2 * (batch * n_q * 64))           # y out (bf16)
+
+
 def gen_inputs(w, st, device, kinds=("q", "k", "v"), t0=0, t1=None):
     import torch
 
@@ -687,11 +697,7 @@ def bench_decode(oal, w, reps, n_steps, device):
     oal.oal_profile_enable(False)
     kt = kernel_times(oal, ["k_decode"])
     ms_step = total * 1e3 / (reps * n_steps)
-    units = w.batch * w.n_kv_heads
-    bytes_launch = (units * 2 * D_CANON * W * 4            # state read + write
-                    + 2 * (w.batch * w.n_q_heads * 64)     # q in (bf16)
-                    + 2 * 2 * (units * 64)                 # k, v in (bf16)
-                    + 2 * (w.batch * w.n_q_heads * 64))    # y out (bf16)
+    bytes_launch = decode_bytes_per_step(w.batch, w.n_q_heads, w.n_kv_heads)
     avg_s = kt["k_decode"]["avg_ms"] * 1e-3
     achieved = bytes_launch / avg_s / 1e9
     base.free()
@@ -878,9 +884,10 @@ def main() -> int:
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU only: every box here has a single MI355X and the "
-              "OAL path has no multi-GPU leg (each (batch, KV head) unit is independent; "
-              "see DESIGN.md for how it would shard).", file=sys.stderr)
+        print("bench.py measures one GPU only: the OAL path has no multi-GPU leg (each "
+              "(batch, KV head) unit is independent, so several GPUs would split the units "
+              "with no communication, or a long sequence by segments with one prefix "
+              "exchange).", file=sys.stderr)
         return 2
 
     import torch

@@ -18,7 +18,7 @@ Sources:
 * Adam: Kingma and Ba, "Adam: A Method for Stochastic Optimization" (ICLR 2015),
   Algorithm 1 (bias-corrected first and second moment estimates).
 
-Readings (also in the design doc): the per-update objective is Eq. 20 restricted to
+Readings: the per-update objective is Eq. 20 restricted to
 the sampled positions S of one sequence, averaged over them:
 loss = (1 / (2 |S|)) sum_{i in S} ||y^_i - y_i^softmax||^2; the clipping norm is
 the Euclidean norm of one head's gradient over the entries of L that are

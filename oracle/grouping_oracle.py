@@ -13,7 +13,7 @@ the P calibration inputs) and App. B "Dimension grouping" (sorting, the tail of
 candidate cuts, Eq. 16 gap, Eq. 17 bootstrap separation, Eq. 18 support, natural
 cuts, the G_min fallback, Eq. 19 groups).
 
-Readings (also in the design doc): Eq. 2 takes |q_{p,i,r} k_{p,j,r}| (the absolute
+Readings: Eq. 2 takes |q_{p,i,r} k_{p,j,r}| (the absolute
 value that the HTML rendering and the second record show; the first PDF record
 lost it); positions and dimensions are 0-based here, the cut k of the pages
 (1-based, separating pi_1..pi_k from pi_{k+1}..pi_d) is the same integer k; the

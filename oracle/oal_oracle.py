@@ -19,7 +19,7 @@ per-dimension contribution is x_r = q_r k_r / sqrt(d_h) ([OAL] §4.1), groups ar
 labelled 1..G by a map g(r) ([OAL] §4.2) and s_bar = [1, s_1, .., s_G] with
 s_g = sum_{r in group g} x_r ([OAL] §4.3).
 
-Readings of the pages that this module fixes (each also listed in the design doc):
+Readings of the pages that this module fixes:
 
 * causal sums include the current position j = i ([OAL] Eq. 5 sums over j <= i;
   Algorithm 1 adds token i to the states before its readout; [GLOSSARY] running

@@ -15,7 +15,7 @@ per-head outlier dimensions scaled by 8-20 (x12 in the tiny case), v ~ N(0, 1).
 They stand in for the real Qwen/Llama attention states and WikiText prompts of
 the paper, which are not available here.
 
-Recipe (also stated in the design doc):
+Recipe:
 
 * streams: ``numpy.random.default_rng(SeedSequence([20261202, wid, kind, b, h]))``
   with kind 0 = structure (shared by the whole workload), 1 = q, 2 = k, 3 = v;
