@@ -123,6 +123,11 @@ k_scan_vec(int n_chunks, float* __restrict__ ws, float* __restrict__ state) {
   if (state) state[(size_t)unit * STATE_FLOATS + e] = run;
 }
 
+// Upper-triangle 4 x 4 blocks of a 64 x 64 symmetric matrix: block row br, block
+// column bc >= br, row-major, at index sblk(br, bc) (compile-time once unrolled).
+constexpr int NSB = (DH / 4) * (DH / 4 + 1) / 2;   // 136
+__host__ __device__ constexpr int sblk(int br, int bc) { return (DH / 4) * br - br * (br - 1) / 2 + (bc - br); }
+
 // One block per (chunk, query head, batch); thread i owns token i of the chunk.
 // DIM: the record is dimension-specific (intra-chunk kappa from b', c');
 // otherwise it is grouped, and a record with NG = 0 (dimension-specific) makes
@@ -155,7 +160,7 @@ k_readout_vec(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunk
   float* s_u = s_k + TB * (DH + 1);           // [TB][WP]
   float* s_ell = s_u + TB * WP;               // grouped: [LDIM][DH]; DIM: b' [DH]
   float* s_L0 = s_ell + LDIM * DH;            // grouped: [LDIM]
-  float* s_cm = s_ell + DH;                   // DIM: S = C / d_h [DH][DH]
+  float* s_st = s_ell + DH;                   // DIM: S = C / d_h, upper 4 x 4 blocks [NSB][16]
 
   const float* rec = coef_rec(coeffs, hq);
   const float a = rec[OAL_COEF_A];
@@ -169,7 +174,14 @@ k_readout_vec(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunk
   }
   if constexpr (DIM) {
     for (int i = tid; i < DH; i += nthr) s_ell[i] = rec[OAL_COEF_BP + i];
-    for (int i = tid; i < DH * DH; i += nthr) s_cm[i] = rec[OAL_COEF_CM + i];
+    // block (br, bc), bc >= br, of S at sblk(br, bc): rows 4 br .., columns 4 bc ..,
+    // the blocks above the diagonal doubled (they stand for their mirrors as well)
+    for (int i = tid; i < NSB * 16; i += nthr) {
+      int br = 0, base = 0;
+      while (base + (16 - br) <= i / 16) base += 16 - br++;
+      const int bc = br + (i / 16 - base), e = i % 16;
+      s_st[i] = (bc > br ? 2.0f : 1.0f) * rec[OAL_COEF_CM + (4 * br + e / 4) * DH + 4 * bc + e % 4];
+    }
   } else {
     for (int i = tid; i < LDIM * DH; i += nthr) s_ell[i] = rec[OAL_COEF_ELL + i];
     if (tid < LDIM) s_L0[tid] = rec[OAL_COEF_L + tid];   // row 0 of L: L_{0,p}
@@ -244,24 +256,36 @@ k_readout_vec(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunk
           float pr[DH];
 #pragma unroll
           for (int t = 0; t < DH; ++t) pr[t] = qi[t] * kj[t];
-          kap = a;
-          // rows of S stream from LDS (one broadcast row per r); a rolled r loop
-          // keeps the 4096 coefficients out of registers
-#pragma unroll 1
-          for (int r = 0; r < DH; ++r) {
-            float4 s4[DH / 4];
+          // kappa = a + b' . p + p^T S p over the upper triangle of 4 x 4 blocks of
+          // S (2240 multiply-adds instead of 4160), the blocks streamed from LDS as
+          // broadcast reads; four row partials per block row
+          float kl = a;
 #pragma unroll
-            for (int i = 0; i < DH / 4; ++i) s4[i] = reinterpret_cast<const float4*>(s_cm + r * DH)[i];
-            float s0 = s_ell[r], s1 = 0.f, s2 = 0.f, s3 = 0.f;   // four independent chains
-#pragma unroll
-            for (int i = 0; i < DH / 4; ++i) {
-              s0 = fmaf(s4[i].x, pr[4 * i + 0], s0);
-              s1 = fmaf(s4[i].y, pr[4 * i + 1], s1);
-              s2 = fmaf(s4[i].z, pr[4 * i + 2], s2);
-              s3 = fmaf(s4[i].w, pr[4 * i + 3], s3);
-            }
-            kap = fmaf((s0 + s1) + (s2 + s3), qi[r] * kj[r], kap);
+          for (int i = 0; i < DH / 4; ++i) {
+            const float4 b4 = reinterpret_cast<const float4*>(s_ell)[i];
+            kl = fmaf(b4.x, pr[4 * i], fmaf(b4.y, pr[4 * i + 1], fmaf(b4.z, pr[4 * i + 2], fmaf(b4.w, pr[4 * i + 3], kl))));
           }
+          // the table pointer taken afresh per pair, so that the compiler does
+          // not hoist the 544 block reads out of the pair loop into registers
+          const float* stp = s_st;
+          asm volatile("" : "+v"(stp));
+          float kq = 0.f;
+#pragma unroll
+          for (int br = 0; br < DH / 4; ++br) {
+            float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+#pragma unroll
+            for (int bc = br; bc < DH / 4; ++bc) {
+              const float4* blk = reinterpret_cast<const float4*>(stp + sblk(br, bc) * 16);
+              const float4 b0 = blk[0], b1 = blk[1], b2 = blk[2], b3 = blk[3];
+              const float p0 = pr[4 * bc], p1 = pr[4 * bc + 1], p2 = pr[4 * bc + 2], p3 = pr[4 * bc + 3];
+              s0 = fmaf(b0.x, p0, fmaf(b0.y, p1, fmaf(b0.z, p2, fmaf(b0.w, p3, s0))));
+              s1 = fmaf(b1.x, p0, fmaf(b1.y, p1, fmaf(b1.z, p2, fmaf(b1.w, p3, s1))));
+              s2 = fmaf(b2.x, p0, fmaf(b2.y, p1, fmaf(b2.z, p2, fmaf(b2.w, p3, s2))));
+              s3 = fmaf(b3.x, p0, fmaf(b3.y, p1, fmaf(b3.z, p2, fmaf(b3.w, p3, s3))));
+            }
+            kq = fmaf(s0, pr[4 * br], fmaf(s1, pr[4 * br + 1], fmaf(s2, pr[4 * br + 2], fmaf(s3, pr[4 * br + 3], kq))));
+          }
+          kap = kl + kq;
         } else {
           float tp[LDIM];
 #pragma unroll
@@ -333,7 +357,7 @@ static oal_status prefill_vec_typed(int batch, int n_q_heads, int n_kv_heads, in
   }
   if (st != OAL_OK) return st;
   size_t smem = sizeof(float) * ((size_t)chunk * (DH + 1) + 32 * WP + 32 + TB * (DH + 1) + TB * WP +
-                                 (DIM ? DH + DH * DH : LDIM * DH + LDIM));
+                                 (DIM ? DH + NSB * 16 : LDIM * DH + LDIM));
   const bool split = chunk <= 128;   // 2 threads per query up to 256 threads per block
   const void* fn = split ? reinterpret_cast<const void*>(&k_readout_vec<T, O, DIM, 2>)
                          : reinterpret_cast<const void*>(&k_readout_vec<T, O, DIM, 1>);
