@@ -132,10 +132,11 @@ __host__ __device__ constexpr int sblk(int br, int bc) { return (DH / 4) * br - 
 // DIM: the record is dimension-specific (intra-chunk kappa from b', c');
 // otherwise it is grouped, and a record with NG = 0 (dimension-specific) makes
 // every output NaN instead of a silently wrong value.
-// SPLIT = 2: two threads per query (thread 2 i + h) split its features and its
-// pairs by parity and add their halves of u~_i through LDS at the end.
+// SPLIT = 2 or 4: that many threads per query (thread SPLIT i + h) split its
+// features and its pairs round robin and add their parts of u~_i through LDS at
+// the end.
 template <typename T, typename O, bool DIM, int SPLIT>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(SPLIT == 4 ? 512 : 256)
 k_readout_vec(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunks,
               const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
               const void* __restrict__ coeffs, const float* __restrict__ ws, O* __restrict__ y) {
@@ -305,6 +306,32 @@ k_readout_vec(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunk
     }
   }
 
+  if (SPLIT == 4) {   // parts 2, 3 onto 0, 1, then 1 onto 0, through the query rows and
+                      // the H, k and u staging (chunk x (DH + 1) floats each; done with)
+    float* xa = s_q + qx * (DH + 1);
+    float* xb = s_H + qx * (DH + 1);
+    __syncthreads();
+    if (half >= 2) {
+      float* xr = half == 2 ? xa : xb;
+#pragma unroll
+      for (int w = 0; w < W; ++w) xr[w] = acc[w];
+    }
+    __syncthreads();
+    if (half < 2) {
+      const float* xr = half == 0 ? xa : xb;
+#pragma unroll
+      for (int w = 0; w < W; ++w) acc[w] += xr[w];
+    }
+    __syncthreads();
+    if (half == 1) {
+#pragma unroll
+      for (int w = 0; w < W; ++w) xa[w] = acc[w];
+    }
+    __syncthreads();
+    if (half != 0) return;
+#pragma unroll
+    for (int w = 0; w < W; ++w) acc[w] += xa[w];
+  }
   if (SPLIT == 2) {   // half 1's share of u~_i through LDS (the query rows are done with)
     float* xrow = s_q + qx * (DH + 1);
     __syncthreads();
@@ -358,14 +385,17 @@ static oal_status prefill_vec_typed(int batch, int n_q_heads, int n_kv_heads, in
   if (st != OAL_OK) return st;
   size_t smem = sizeof(float) * ((size_t)chunk * (DH + 1) + 32 * WP + 32 + TB * (DH + 1) + TB * WP +
                                  (DIM ? DH + NSB * 16 : LDIM * DH + LDIM));
-  const bool split = chunk <= 128;   // 2 threads per query up to 256 threads per block
-  const void* fn = split ? reinterpret_cast<const void*>(&k_readout_vec<T, O, DIM, 2>)
+  // threads per query: 4 for dimension-specific records (their per-pair work is
+  // the larger) and 2 for grouped ones up to chunk 128, 1 at chunk 256
+  constexpr int SP = DIM ? 4 : 2;
+  const bool split = chunk <= 128;
+  const void* fn = split ? reinterpret_cast<const void*>(&k_readout_vec<T, O, DIM, SP>)
                          : reinterpret_cast<const void*>(&k_readout_vec<T, O, DIM, 1>);
   if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem) != hipSuccess)
     return set_error(OAL_ERR_HIP, "k_readout_vec: cannot reserve %zu bytes of LDS", smem);
   ProfScope ps("k_readout_vec", stream);
   if (split)
-    hipLaunchKernelGGL((k_readout_vec<T, O, DIM, 2>), dim3(n_chunks, n_q_heads, batch), dim3(2 * chunk),
+    hipLaunchKernelGGL((k_readout_vec<T, O, DIM, SP>), dim3(n_chunks, n_q_heads, batch), dim3(SP * chunk),
                        smem, stream, n_q_heads, n_kv_heads, seq_len, chunk, n_chunks,
                        reinterpret_cast<const T*>(q), kk, vv, coeffs, ws, reinterpret_cast<O*>(y));
   else
