@@ -22,7 +22,7 @@
 //
 // Kernels, in launch order:
 //   prefix build + scan (oal_prefill_vec.hip)  H_{<c}
-//   k_bwd_query     two threads per query: recompute u~_i, g_i; dq_i; alpha rows
+//   k_bwd_query     four (chunk 64) or two threads per query: recompute u~_i, g_i; dq_i; alpha rows
 //   k_bwd_rbuild    per chunk: sum_h c_f psi_f(q_i) g_i^T (suffix deltas) and the
 //                   state part of dc: sum_i psi_f(q_i) (H_{<c} g_i)_f
 //   k_bwd_rscan     exclusive suffix sums over chunks: R_{>c}
@@ -256,11 +256,12 @@ size_t backward_workspace(int batch, int n_q_heads, int n_kv_heads, int seq_len,
 }
 
 // ---------------------------------------------------------------------------
-// Query side.  One block per (chunk, query head, batch); two threads per query
-// (thread 2 i + h, h = 0, 1, for query t0 + i) split its features and its pairs
-// by parity; the halves of u~_i are added through LDS, g_i is shared the same
-// way, and each half keeps its own dq row, the two rows added at the end.
-template <typename T>
+// Query side.  One block per (chunk, query head, batch); SP threads per query
+// (thread SP i + h, h = 0 .. SP - 1, for query t0 + i; SP = 4 at chunk 64, 2 at
+// chunk 128) split its features and its pairs round robin; the parts of u~_i are
+// added through LDS, g_i is shared the same way, and each part keeps its own dq
+// row, the rows added in a fixed order at the end.
+template <typename T, int SP>
 __global__ void __launch_bounds__(256)
 k_bwd_query(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunks,
             const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
@@ -273,17 +274,17 @@ k_bwd_query(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunks,
   const int rep = n_q_heads / n_kv_heads;
   const int unit = b * n_kv_heads + hq / rep;
   const int tid = threadIdx.x;
-  const int nthr = blockDim.x;                // 2 * chunk
-  const int qx = tid >> 1;                    // query of the chunk
-  const int half = tid & 1;
+  const int nthr = blockDim.x;                // SP * chunk
+  const int qx = tid / SP;                    // query of the chunk
+  const int half = tid % SP;                  // this thread's part
   const int t0 = c * chunk;
   const int clen = min(chunk, seq_len - t0);
   const bool active = qx < clen;
 
   extern __shared__ __attribute__((aligned(16))) float smem[];
   float* s_q = smem;                          // [chunk][DH + 1]
-  float* s_dq = s_q + chunk * (DH + 1);       // [2][chunk][DH + 1] (half 1's rows also pass u~, g)
-  float* s_H = s_dq + 2 * chunk * (DH + 1);   // [32][WP]
+  float* s_dq = s_q + chunk * (DH + 1);       // [SP][chunk][DH + 1] (parts >= 1 also pass u~, g)
+  float* s_H = s_dq + SP * chunk * (DH + 1);  // [32][WP]
   float* s_cf = s_H + 32 * WP;                // [32]
   float* s_k = s_cf + 32;                     // [TB][DH + 1]
   float* s_u = s_k + TB * (DH + 1);           // [TB][WP]
@@ -300,7 +301,7 @@ k_bwd_query(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunks,
     const int ii = i / DH, d = i % DH;
     s_q[ii * (DH + 1) + d] = ii < clen ? Elem<T>::load(q, (qrow0 + ii) * DH + d) : 0.f;
   }
-  for (int i = tid; i < 2 * chunk * (DH + 1); i += nthr) s_dq[i] = 0.f;
+  for (int i = tid; i < SP * chunk * (DH + 1); i += nthr) s_dq[i] = 0.f;
   for (int i = tid; i < DH; i += nthr) s_b[i] = rec[OAL_COEF_BP + i];
   for (int i = tid; i < DH * DH; i += nthr) s_S[i] = rec[OAL_COEF_CM + i];
   for (int i = tid; i < 32 * (WP - W); i += nthr) s_H[(i / (WP - W)) * WP + W + i % (WP - W)] = 0.f;
@@ -343,7 +344,7 @@ k_bwd_query(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunks,
     __syncthreads();
     if (active) {
       const int nf = min(32, DCAN - f0);
-      for (int ff = half; ff < nf; ff += 2) {
+      for (int ff = half; ff < nf; ff += SP) {
         int r, t;
         const int kind = feat_decode(f0 + ff, r, t);
         const float psi = kind == 0 ? 1.f : kind == 1 ? qi[r] : qi[r] * qi[t];
@@ -358,7 +359,7 @@ k_bwd_query(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunks,
     __syncthreads();
     if (active) {
       const int jmax = min(nj, qx - j0 + 1);
-      for (int jj = half; jj < jmax; jj += 2) {
+      for (int jj = half; jj < jmax; jj += SP) {
         float w[LDIM];
         const float kap = fast ? grouped_pair(qi, s_k + jj * (DH + 1), gt, w)
                                : kappa_pair(a, qi, s_k + jj * (DH + 1), s_b, s_S);
@@ -367,10 +368,11 @@ k_bwd_query(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunks,
     }
   }
 
-  // ---- 2. u~_i = the two halves; g_i (zero for rows beyond the sequence), shared
-  float* xrow = s_dq + (chunk + qx) * (DH + 1);   // half 1's dq row, still unused
+  // ---- 2. u~_i = the parts' sum; g_i (zero for rows beyond the sequence), shared
+  // through the dq rows of parts 1 .. SP - 1, still unused
+  float* xrow = s_dq + (half * chunk + qx) * (DH + 1);   // this part's dq row
   __syncthreads();
-  if (half == 1) {
+  if (half >= 1) {
 #pragma unroll
     for (int w = 0; w < W; ++w) xrow[w] = acc[w];
   }
@@ -379,27 +381,37 @@ k_bwd_query(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunks,
 #pragma unroll
   for (int w = 0; w < WP; ++w) g[w] = 0.f;
   if (half == 0) {
+#pragma unroll
+    for (int h = 1; h < SP; ++h) {   // the parts in a fixed order
+      const float* pr = s_dq + (h * chunk + qx) * (DH + 1);
+#pragma unroll
+      for (int w = 0; w < W; ++w) acc[w] += pr[w];
+    }
     if (active) {
-      const float inv = 1.0f / (acc[DV] + xrow[DV]);
+      const float inv = 1.0f / acc[DV];
       const float* dyi = dy + (qrow0 + qx) * DV;
       float ydot = 0.f;
 #pragma unroll
       for (int w = 0; w < DV; ++w) {
         const float d = dyi[w];
         g[w] = d * inv;
-        ydot = fmaf(d, (acc[w] + xrow[w]) * inv, ydot);
+        ydot = fmaf(d, acc[w] * inv, ydot);
       }
       g[DV] = -ydot * inv;
     }
 #pragma unroll
-    for (int w = 0; w < W; ++w) xrow[w] = g[w];
+    for (int h = 1; h < SP; ++h) {   // g into every other part's own row
+      float* pr = s_dq + (h * chunk + qx) * (DH + 1);
+#pragma unroll
+      for (int w = 0; w < W; ++w) pr[w] = g[w];
+    }
     float* gr = gbuf + (((size_t)b * n_q_heads + hq) * ((size_t)n_chunks * chunk) + t0 + qx) * WP;
 #pragma unroll
     for (int i = 0; i < WP / 4; ++i)
       reinterpret_cast<float4*>(gr)[i] = make_float4(g[4 * i], g[4 * i + 1], g[4 * i + 2], g[4 * i + 3]);
   }
   __syncthreads();
-  if (half == 1) {
+  if (half >= 1) {
 #pragma unroll
     for (int w = 0; w < W; ++w) g[w] = xrow[w];
 #pragma unroll
@@ -414,7 +426,7 @@ k_bwd_query(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunks,
     stage_keys(j0, nj);
     __syncthreads();
     const int jmax = active ? max(0, min(nj, qx - j0 + 1)) : 0;
-    for (int jj = half; jj < jmax; jj += 2) {
+    for (int jj = half; jj < jmax; jj += SP) {
       const float* kj = s_k + jj * (DH + 1);
       const float al = dot_row(s_u + jj * WP, g);
       arow[j0 + jj] = al;
@@ -431,7 +443,7 @@ k_bwd_query(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunks,
       for (int r = 0; r < DH; ++r)
         dqi[r] = fmaf(al * kj[r], s_b[r] + 2.f * srow_dot(s_S + r * DH, p), dqi[r]);
     }
-    for (int jj = half; jj < TB; jj += 2)
+    for (int jj = half; jj < TB; jj += SP)
       if (jj >= jmax) arow[j0 + jj] = 0.f;
   }
 
@@ -442,7 +454,7 @@ k_bwd_query(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunks,
     __syncthreads();
     if (active) {
       const int nf = min(32, DCAN - f0);
-      for (int ff = half; ff < nf; ff += 2) {
+      for (int ff = half; ff < nf; ff += SP) {
         int r, t;
         const int kind = feat_decode(f0 + ff, r, t);
         if (kind == 0) continue;
@@ -457,12 +469,15 @@ k_bwd_query(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunks,
     }
   }
   __syncthreads();
-  if (active) {
-    const float* d0 = s_dq + qx * (DH + 1);
-    const float* d1 = s_dq + (chunk + qx) * (DH + 1);
-    float* o = dq + (qrow0 + qx) * DH + half * (DH / 2);
+  if (active) {   // each part writes DH / SP entries, the parts' rows added in order
+    float* o = dq + (qrow0 + qx) * DH + half * (DH / SP);
 #pragma unroll
-    for (int d = 0; d < DH / 2; ++d) o[d] = d0[half * (DH / 2) + d] + d1[half * (DH / 2) + d];
+    for (int d = 0; d < DH / SP; ++d) {
+      float x = 0.f;
+#pragma unroll
+      for (int h = 0; h < SP; ++h) x += s_dq[(h * chunk + qx) * (DH + 1) + half * (DH / SP) + d];
+      o[d] = x;
+    }
   }
 }
 
@@ -898,15 +913,23 @@ static oal_status backward_typed(int batch, int n_q_heads, int n_kv_heads, int s
   oal_status st = launch_prefix_vec(batch, n_kv_heads, seq_len, chunk, in_dtype, k, v, w.hc, stream);
   if (st != OAL_OK) return st;
   {
-    const size_t smem = sizeof(float) * ((size_t)3 * chunk * (DH + 1) + 32 * WP + 32 + TB * (DH + 1) +
-                                         TB * WP + DH + DH * DH);
-    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&k_bwd_query<T>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem) != hipSuccess)
+    // four threads per query at chunk 64 (256 threads, 143 KB of LDS), two at 128
+    const int sp = chunk <= 64 ? 4 : 2;
+    const size_t smem = sizeof(float) * ((size_t)(1 + sp) * chunk * (DH + 1) + 32 * WP + 32 +
+                                         TB * (DH + 1) + TB * WP + DH + DH * DH);
+    const void* fn = sp == 4 ? reinterpret_cast<const void*>(&k_bwd_query<T, 4>)
+                             : reinterpret_cast<const void*>(&k_bwd_query<T, 2>);
+    if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem) != hipSuccess)
       return set_error(OAL_ERR_HIP, "k_bwd_query: cannot reserve %zu bytes of LDS", smem);
     ProfScope ps("k_bwd_query", stream);
-    hipLaunchKernelGGL(k_bwd_query<T>, dim3(n_chunks, n_q_heads, batch), dim3(2 * chunk), smem, stream,
-                       n_q_heads, n_kv_heads, seq_len, chunk, n_chunks, qq, kk, vv, coeffs, dy, w.hc,
-                       w.gbuf, w.alpha, dq);
+    if (sp == 4)
+      hipLaunchKernelGGL((k_bwd_query<T, 4>), dim3(n_chunks, n_q_heads, batch), dim3(4 * chunk), smem,
+                         stream, n_q_heads, n_kv_heads, seq_len, chunk, n_chunks, qq, kk, vv, coeffs, dy,
+                         w.hc, w.gbuf, w.alpha, dq);
+    else
+      hipLaunchKernelGGL((k_bwd_query<T, 2>), dim3(n_chunks, n_q_heads, batch), dim3(2 * chunk), smem,
+                         stream, n_q_heads, n_kv_heads, seq_len, chunk, n_chunks, qq, kk, vv, coeffs, dy,
+                         w.hc, w.gbuf, w.alpha, dq);
     if ((st = check_launch("k_bwd_query")) != OAL_OK) return st;
   }
   {
