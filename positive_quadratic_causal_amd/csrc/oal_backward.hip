@@ -26,7 +26,7 @@
 //   k_bwd_rbuild    per chunk: sum_h c_f psi_f(q_i) g_i^T (suffix deltas) and the
 //                   state part of dc: sum_i psi_f(q_i) (H_{<c} g_i)_f
 //   k_bwd_rscan     exclusive suffix sums over chunks: R_{>c}
-//   k_bwd_key       two threads per key and slot (a query head's pairs, or R_{>c}):
+//   k_bwd_key       four (chunk 64) or two threads per key and slot (a query head's pairs, or R_{>c}):
 //                   parts of dv_j, dk_j;  k_bwd_ksum adds the parts
 //   k_bwd_dc_intra  pair part of dc: sum_{i, j<=i in the chunk} alpha_ij psi_f(q_i) psi_f(k_j)
 //   k_bwd_dcoef     sum over chunks and batch; (da, db, dC) of [OAL] Eq. 3
@@ -219,9 +219,13 @@ struct BwdWs {
   float* gbuf;    // [batch][Hq][n_chunks * chunk][WP] g rows (zero beyond seq_len)
   float* alpha;   // [batch][Hq][n_chunks][chunk][chunk] alpha_ij (zero for j > i)
   float* dcp;     // [batch][Hq][n_chunks][DS] per-chunk parts of dc
-  float* kpart;   // [units][2 (rep + 1)][n_chunks * chunk][128] parts of [dk | dv]
+  float* kpart;   // [units][KS (rep + 1)][n_chunks * chunk][128] parts of [dk | dv]
   size_t bytes;
 };
+
+// Threads per key of the key-side kernel (and parts per slot in kpart): four at
+// chunk 64 (256 threads, 143 KB of LDS per block), two at chunk 128.
+static int key_split(int chunk) { return chunk <= 64 ? 4 : 2; }
 
 static BwdWs bwd_ws(void* base, int batch, int n_q_heads, int n_kv_heads, int seq_len, int chunk) {
   const size_t units = (size_t)batch * n_kv_heads;
@@ -238,7 +242,8 @@ static BwdWs bwd_ws(void* base, int batch, int n_q_heads, int n_kv_heads, int se
   const size_t o_g = take(bh * nc * chunk * WP);
   const size_t o_a = take(bh * nc * chunk * chunk);
   const size_t o_d = take(bh * nc * DS);
-  const size_t o_k = take(units * (size_t)2 * (n_q_heads / n_kv_heads + 1) * nc * chunk * (DH + DV));
+  const size_t o_k = take(units * (size_t)key_split(chunk) * (n_q_heads / n_kv_heads + 1) * nc * chunk *
+                          (DH + DV));
   BwdWs w;
   uint8_t* p = reinterpret_cast<uint8_t*>(base);
   w.hc = reinterpret_cast<float*>(p + o_h);
@@ -582,10 +587,11 @@ k_bwd_rscan(int n_chunks, float* __restrict__ rc) {
 // ---------------------------------------------------------------------------
 // Key side.  One block per (chunk, unit, slot): slot s < rep sums the chunk's
 // pairs of query head kv * rep + s, slot rep the later chunks through R_{>c}.
-// Two threads per key (thread 2 j + h for key t0 + j) split the pairs or the
-// features by parity; each thread writes its part of [dk_j | dv_j] to kpart
-// (part 2 slot + h), and k_bwd_ksum adds the 2 (rep + 1) parts in order.
-template <typename T>
+// SP threads per key (thread SP j + h for key t0 + j) split the pairs (by query
+// index mod SP) or the features round robin; each thread writes its part of
+// [dk_j | dv_j] to kpart (part SP slot + h), and k_bwd_ksum adds the SP (rep + 1)
+// parts in order.
+template <typename T, int SP>
 __global__ void __launch_bounds__(256)
 k_bwd_key(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunks,
           const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
@@ -597,17 +603,17 @@ k_bwd_key(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunks,
   const int slot = blockIdx.y % (rep + 1);
   const int b = unit / n_kv_heads, kv = unit % n_kv_heads;
   const int tid = threadIdx.x;
-  const int nthr = blockDim.x;                // 2 * chunk
-  const int jx = tid >> 1;                    // key of the chunk
-  const int half = tid & 1;
+  const int nthr = blockDim.x;                // SP * chunk
+  const int jx = tid / SP;                    // key of the chunk
+  const int half = tid % SP;                  // this thread's part
   const int t0 = c * chunk;
   const int clen = min(chunk, seq_len - t0);
   const bool active = jx < clen;
 
   extern __shared__ __attribute__((aligned(16))) float smem[];
   float* s_k = smem;                          // [chunk][DH + 1]
-  float* s_dk = s_k + chunk * (DH + 1);       // [2][chunk][DH + 1]
-  float* s_R = s_dk + 2 * chunk * (DH + 1);   // [32][WP]
+  float* s_dk = s_k + chunk * (DH + 1);       // [SP][chunk][DH + 1]
+  float* s_R = s_dk + SP * chunk * (DH + 1);  // [32][WP]
   float* s_q = s_R + 32 * WP;                 // [TB][DH + 1]
   float* s_g = s_q + TB * (DH + 1);           // [TB][WP]
   float* s_b = s_g + TB * WP;                 // [DH]
@@ -618,7 +624,7 @@ k_bwd_key(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunks,
     const int jj = i / DH, d = i % DH;
     s_k[jj * (DH + 1) + d] = jj < clen ? Elem<T>::load(k, (krow0 + jj) * DH + d) : 0.f;
   }
-  for (int i = tid; i < 2 * chunk * (DH + 1); i += nthr) s_dk[i] = 0.f;
+  for (int i = tid; i < SP * chunk * (DH + 1); i += nthr) s_dk[i] = 0.f;
   for (int i = tid; i < 32 * (WP - W); i += nthr) s_R[(i / (WP - W)) * WP + W + i % (WP - W)] = 0.f;
   float uj[WP];
 #pragma unroll
@@ -646,7 +652,7 @@ k_bwd_key(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunks,
     __syncthreads();
     if (active) {
       const int nf = min(32, DCAN - f0);
-      for (int ff = half; ff < nf; ff += 2) {
+      for (int ff = half; ff < nf; ff += SP) {
         int r, t;
         const int kind = feat_decode(f0 + ff, r, t);
         const float* row = s_R + ff * WP;
@@ -693,7 +699,7 @@ k_bwd_key(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunks,
       const bool fast = grouped && gt.n_out <= MAX_OUT;   // uniform over the block
       if (active) {
         const int ii0 = max(0, jx - i0);
-        for (int ii = ii0 + ((ii0 ^ half) & 1); ii < ni; ii += 2) {
+        for (int ii = ii0 + (((half - ii0) % SP) + SP) % SP; ii < ni; ii += SP) {
           const float* qi = s_q + ii * (DH + 1);
           const float* gi = s_g + ii * WP;
           const float al = dot_row(gi, uj);
@@ -720,7 +726,7 @@ k_bwd_key(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunks,
     }
   }
   if (active) {
-    float* o = kpart + (((size_t)unit * 2 * (rep + 1) + 2 * slot + half) * npad + t0 + jx) * (DH + DV);
+    float* o = kpart + (((size_t)unit * SP * (rep + 1) + SP * slot + half) * npad + t0 + jx) * (DH + DV);
 #pragma unroll
     for (int d = 0; d < DH; ++d) o[d] = dkj[d];
 #pragma unroll
@@ -728,9 +734,9 @@ k_bwd_key(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunks,
   }
 }
 
-// dk, dv = the sum of the 2 (rep + 1) parts of every key, in order.
+// dk, dv = the sum of the nparts parts of every key, in order.
 __global__ void __launch_bounds__(256)
-k_bwd_ksum(int n_kv_heads, int rep, int seq_len, int npad, const float* __restrict__ kpart,
+k_bwd_ksum(int n_kv_heads, int nparts, int seq_len, int npad, const float* __restrict__ kpart,
            float* __restrict__ dk, float* __restrict__ dv) {
   const size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   const size_t per_unit = (size_t)seq_len * (DH + DV);
@@ -739,8 +745,8 @@ k_bwd_ksum(int n_kv_heads, int rep, int seq_len, int npad, const float* __restri
   const size_t pos = e / (DH + DV);
   const int comp = (int)(e % (DH + DV));
   float s = 0.f;
-  for (int sl = 0; sl < 2 * (rep + 1); ++sl)
-    s += kpart[(((size_t)unit * 2 * (rep + 1) + sl) * npad + pos) * (DH + DV) + comp];
+  for (int sl = 0; sl < nparts; ++sl)
+    s += kpart[(((size_t)unit * nparts + sl) * npad + pos) * (DH + DV) + comp];
   if (comp < DH) dk[((size_t)unit * seq_len + pos) * DH + comp] = s;
   else dv[((size_t)unit * seq_len + pos) * DV + comp - DH] = s;
 }
@@ -946,23 +952,30 @@ static oal_status backward_typed(int batch, int n_q_heads, int n_kv_heads, int s
     if ((st = check_launch("k_bwd_rscan")) != OAL_OK) return st;
   }
   {
-    const size_t smem = sizeof(float) * ((size_t)3 * chunk * (DH + 1) + 32 * WP + TB * (DH + 1) +
+    const int ks = key_split(chunk);
+    const size_t smem = sizeof(float) * ((size_t)(1 + ks) * chunk * (DH + 1) + 32 * WP + TB * (DH + 1) +
                                          TB * WP + DH + DH * DH);
-    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&k_bwd_key<T>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem) != hipSuccess)
+    const void* fn = ks == 4 ? reinterpret_cast<const void*>(&k_bwd_key<T, 4>)
+                             : reinterpret_cast<const void*>(&k_bwd_key<T, 2>);
+    if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem) != hipSuccess)
       return set_error(OAL_ERR_HIP, "k_bwd_key: cannot reserve %zu bytes of LDS", smem);
     const int rep = n_q_heads / n_kv_heads;
     {
       ProfScope ps("k_bwd_key", stream);
-      hipLaunchKernelGGL(k_bwd_key<T>, dim3(n_chunks, units * (rep + 1)), dim3(2 * chunk), smem, stream,
-                         n_q_heads, n_kv_heads, seq_len, chunk, n_chunks, qq, kk, vv, coeffs, w.gbuf,
-                         w.rc, w.kpart);
+      if (ks == 4)
+        hipLaunchKernelGGL((k_bwd_key<T, 4>), dim3(n_chunks, units * (rep + 1)), dim3(4 * chunk), smem,
+                           stream, n_q_heads, n_kv_heads, seq_len, chunk, n_chunks, qq, kk, vv, coeffs,
+                           w.gbuf, w.rc, w.kpart);
+      else
+        hipLaunchKernelGGL((k_bwd_key<T, 2>), dim3(n_chunks, units * (rep + 1)), dim3(2 * chunk), smem,
+                           stream, n_q_heads, n_kv_heads, seq_len, chunk, n_chunks, qq, kk, vv, coeffs,
+                           w.gbuf, w.rc, w.kpart);
       if ((st = check_launch("k_bwd_key")) != OAL_OK) return st;
     }
     ProfScope ps("k_bwd_ksum", stream);
     const size_t per_unit = (size_t)seq_len * (DH + DV);
     hipLaunchKernelGGL(k_bwd_ksum, dim3((unsigned)((per_unit + 255) / 256), units), dim3(256), 0,
-                       stream, n_kv_heads, rep, seq_len, n_chunks * chunk, w.kpart, dk, dv);
+                       stream, n_kv_heads, ks * (rep + 1), seq_len, n_chunks * chunk, w.kpart, dk, dv);
     if ((st = check_launch("k_bwd_ksum")) != OAL_OK) return st;
   }
   if (!want_coef) return OAL_OK;
