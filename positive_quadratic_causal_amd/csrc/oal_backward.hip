@@ -488,7 +488,8 @@ k_bwd_query(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunks,
 
 // ---------------------------------------------------------------------------
 // Suffix deltas and the state part of dc.  Block (feature block, chunk, unit);
-// thread: feature f = 64 fb + (tid & 63), columns w = (tid >> 6) + 4 j.
+// thread: feature f = 64 fb + (tid & 63), columns w = 16 (tid >> 6) + j, j < 16, and
+// the all-ones channel on the fourth wave.
 template <typename T>
 __global__ void __launch_bounds__(256)
 k_bwd_rbuild(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunks,
@@ -504,16 +505,19 @@ k_bwd_rbuild(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunks
   const int f = fb * FB + (tid & 63);
   const int wq = tid >> 6;
   __shared__ float s_q[TB][DH + 1];
-  __shared__ float s_g[TB][WP];
+  __shared__ __attribute__((aligned(16))) float s_g[TB][WP];
   __shared__ float s_red[4][FB];
   int r, t;
   const int kind = feat_decode(f, r, t);
   const size_t slot = ((size_t)unit * n_chunks + c) * STATE_FLOATS;
+  // columns of this thread: 16 wq .. 16 wq + 15 (read as four 16-byte rows of g),
+  // and the all-ones channel W - 1 on wave 3
+  auto col_of = [&](int j) { return j < 16 ? 16 * wq + j : (wq == 3 ? W - 1 : -1); };
   float hval[WPT], rd[WPT];
 #pragma unroll
   for (int j = 0; j < WPT; ++j) {
-    const int w = wq + 4 * j;
-    hval[j] = w < W ? hc[slot + (size_t)w * DS + f] : 0.f;
+    const int w = col_of(j);
+    hval[j] = w >= 0 ? hc[slot + (size_t)w * DS + f] : 0.f;
     rd[j] = 0.f;
   }
   const int t0 = c * chunk;
@@ -541,11 +545,16 @@ k_bwd_rbuild(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunks
       __syncthreads();
       for (int ii = 0; ii < ni; ++ii) {
         const float psi = kind == 0 ? 1.f : kind == 1 ? s_q[ii][r] : kind == 2 ? s_q[ii][r] * s_q[ii][t] : 0.f;
+        const float4* gr = reinterpret_cast<const float4*>(&s_g[ii][16 * wq]);
 #pragma unroll
-        for (int j = 0; j < WPT; ++j) {
-          const int w = wq + 4 * j;
-          if (w < W) acc[j] = fmaf(psi, s_g[ii][w], acc[j]);
+        for (int j4 = 0; j4 < 4; ++j4) {
+          const float4 g4 = gr[j4];
+          acc[4 * j4 + 0] = fmaf(psi, g4.x, acc[4 * j4 + 0]);
+          acc[4 * j4 + 1] = fmaf(psi, g4.y, acc[4 * j4 + 1]);
+          acc[4 * j4 + 2] = fmaf(psi, g4.z, acc[4 * j4 + 2]);
+          acc[4 * j4 + 3] = fmaf(psi, g4.w, acc[4 * j4 + 3]);
         }
+        if (wq == 3) acc[16] = fmaf(psi, s_g[ii][W - 1], acc[16]);
       }
     }
     float part = 0.f;
@@ -564,8 +573,8 @@ k_bwd_rbuild(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunks
   }
 #pragma unroll
   for (int j = 0; j < WPT; ++j) {
-    const int w = wq + 4 * j;
-    if (w < W) rc[slot + (size_t)w * DS + f] = rd[j];
+    const int w = col_of(j);
+    if (w >= 0) rc[slot + (size_t)w * DS + f] = rd[j];
   }
 }
 
