@@ -55,7 +55,10 @@ k_build_vec(int n_kv_heads, int seq_len, int chunk, int n_chunks, const T* __res
   const int f = fb * FB + (tid & 63);
   const int wq = tid >> 6;
   __shared__ float s_k[TB][DH + 1];
-  __shared__ float s_u[TB][W];
+  __shared__ __attribute__((aligned(16))) float s_u[TB][WP];   // [v; 1] rows, 16-byte aligned
+  // columns of this thread: 16 wq .. 16 wq + 15 (four 16-byte reads of a u row),
+  // and the all-ones channel W - 1 on wave 3
+  auto col_of = [&](int j) { return j < 16 ? 16 * wq + j : (wq == 3 ? W - 1 : -1); };
 
   int r = 0, t = 0, kind;
   if (f == 0) kind = 0;
@@ -87,19 +90,24 @@ k_build_vec(int n_kv_heads, int seq_len, int chunk, int n_chunks, const T* __res
     __syncthreads();
     for (int jj = 0; jj < nj; ++jj) {
       float phi = kind == 0 ? 1.f : kind == 1 ? s_k[jj][r] : kind == 2 ? s_k[jj][r] * s_k[jj][t] : 0.f;
+      const float4* ur = reinterpret_cast<const float4*>(&s_u[jj][16 * wq]);
 #pragma unroll
-      for (int j = 0; j < WPT; ++j) {
-        int w = wq + 4 * j;
-        if (w < W) acc[j] = fmaf(phi, s_u[jj][w], acc[j]);
+      for (int j4 = 0; j4 < 4; ++j4) {
+        const float4 u4 = ur[j4];
+        acc[4 * j4 + 0] = fmaf(phi, u4.x, acc[4 * j4 + 0]);
+        acc[4 * j4 + 1] = fmaf(phi, u4.y, acc[4 * j4 + 1]);
+        acc[4 * j4 + 2] = fmaf(phi, u4.z, acc[4 * j4 + 2]);
+        acc[4 * j4 + 3] = fmaf(phi, u4.w, acc[4 * j4 + 3]);
       }
+      if (wq == 3) acc[16] = fmaf(phi, s_u[jj][W - 1], acc[16]);
     }
   }
   float* o = out + (mode == 0 ? ((size_t)unit * n_chunks + c) * STATE_FLOATS
                               : (size_t)unit * STATE_FLOATS);
 #pragma unroll
   for (int j = 0; j < WPT; ++j) {
-    int w = wq + 4 * j;
-    if (w < W) {
+    const int w = col_of(j);
+    if (w >= 0) {
       float* p = o + (size_t)w * DS + f;
       if (mode == 0) *p = acc[j];
       else *p += acc[j];
