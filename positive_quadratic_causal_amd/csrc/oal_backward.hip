@@ -799,21 +799,27 @@ k_bwd_dc_intra(int n_q_heads, int n_kv_heads, int seq_len, int n_chunks,
     const float* kr = s_k + j * (DH + 1);
     kf[j] = kind == 0 ? 1.f : kind == 1 ? kr[r] : kr[r] * kr[t];
   }
+  // alpha_ij = 0 for j > i: the rows of band B (16 B .. 16 B + 15) stop at key
+  // 16 B + 15 (a compile-time bound, so kf stays in registers)
   float acc = 0.f;
-  for (int i = 0; i < clen; ++i) {
-    const float* qr = s_q + i * (DH + 1);
-    const float qf = kind == 0 ? 1.f : kind == 1 ? qr[r] : qr[r] * qr[t];
-    const float4* ar = reinterpret_cast<const float4*>(s_a + i * CH);
-    float s0 = 0.f, s1 = 0.f;
 #pragma unroll
-    for (int j4 = 0; j4 < CH / 4; ++j4) {
-      const float4 av = ar[j4];
-      s0 = fmaf(av.x, kf[4 * j4 + 0], s0);
-      s1 = fmaf(av.y, kf[4 * j4 + 1], s1);
-      s0 = fmaf(av.z, kf[4 * j4 + 2], s0);
-      s1 = fmaf(av.w, kf[4 * j4 + 3], s1);
+  for (int B = 0; B < CH / 16; ++B) {
+    const int ie = min(16 * B + 16, clen);
+    for (int i = 16 * B; i < ie; ++i) {
+      const float* qr = s_q + i * (DH + 1);
+      const float qf = kind == 0 ? 1.f : kind == 1 ? qr[r] : qr[r] * qr[t];
+      const float4* ar = reinterpret_cast<const float4*>(s_a + i * CH);
+      float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+      for (int j4 = 0; j4 < 4 * B + 4; ++j4) {
+        const float4 av = ar[j4];
+        s0 = fmaf(av.x, kf[4 * j4 + 0], s0);
+        s1 = fmaf(av.y, kf[4 * j4 + 1], s1);
+        s0 = fmaf(av.z, kf[4 * j4 + 2], s0);
+        s1 = fmaf(av.w, kf[4 * j4 + 3], s1);
+      }
+      acc = fmaf(qf, s0 + s1, acc);
     }
-    acc = fmaf(qf, s0 + s1, acc);
   }
   dcp[((size_t)bh * n_chunks + c) * DS + f] += acc;
 }
