@@ -318,12 +318,26 @@ k_bwd_query(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunks,
   const float* Hc = hc + ((size_t)unit * n_chunks + c) * STATE_FLOATS;
   const size_t kbase = (size_t)unit * seq_len + t0;
 
-  auto stage_block = [&](int f0) {
-    for (int i = tid; i < 32 * W; i += nthr) {
-      const int w = i / 32, ff = i % 32;
-      s_H[ff * WP + w] = Hc[(size_t)w * DS + f0 + ff];   // f0 + 31 < DS always
+  // the state blocks of 32 features pass through registers one block ahead of
+  // the LDS copy the threads work on (nthr = 256: 9 values per thread at most)
+  constexpr int PB = (32 * W + 255) / 256;
+  float pre[PB], pcf = 0.f;
+  auto fetch_block = [&](int f0) {
+#pragma unroll
+    for (int e = 0; e < PB; ++e) {
+      const int i = tid + e * 256;
+      if (i < 32 * W) pre[e] = Hc[(size_t)(i / 32) * DS + f0 + i % 32];   // f0 + 31 < DS always
     }
-    if (tid < 32) s_cf[tid] = coef_of(rec, f0 + tid);
+    if (tid < 32) pcf = coef_of(rec, f0 + tid);
+  };
+  auto stage_block = [&](int f0) {
+#pragma unroll
+    for (int e = 0; e < PB; ++e) {
+      const int i = tid + e * 256;
+      if (i < 32 * W) s_H[(i % 32) * WP + i / 32] = pre[e];
+    }
+    if (tid < 32) s_cf[tid] = pcf;
+    if (f0 + 32 < DCAN) fetch_block(f0 + 32);
   };
   auto stage_keys = [&](int j0, int nj) {
     for (int i = tid; i < TB * DH; i += nthr) {
@@ -343,6 +357,7 @@ k_bwd_query(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunks,
   float acc[WP];
 #pragma unroll
   for (int w = 0; w < WP; ++w) acc[w] = 0.f;
+  fetch_block(0);
   for (int f0 = 0; f0 < DCAN; f0 += 32) {
     __syncthreads();
     stage_block(f0);
@@ -453,6 +468,7 @@ k_bwd_query(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunks,
   }
 
   // ---- 4. state part: d_f = H_{<c}[f] . g_i, then the monomials' derivatives
+  fetch_block(0);
   for (int f0 = 0; f0 < DCAN; f0 += 32) {
     __syncthreads();
     stage_block(f0);
@@ -934,8 +950,10 @@ static oal_status backward_typed(int batch, int n_q_heads, int n_kv_heads, int s
   oal_status st = launch_prefix_vec(batch, n_kv_heads, seq_len, chunk, in_dtype, k, v, w.hc, stream);
   if (st != OAL_OK) return st;
   {
-    // four threads per query at chunk 64 (256 threads, 143 KB of LDS), two at 128
+    // four threads per query at chunk 64 (256 threads, 143 KB of LDS), two at 128;
+    // the kernel's state staging assumes SP * chunk = 256
     const int sp = chunk <= 64 ? 4 : 2;
+    if (sp * chunk != 256) return set_error(OAL_ERR_INVALID_ARG, "k_bwd_query: chunk %d", chunk);
     const size_t smem = sizeof(float) * ((size_t)(1 + sp) * chunk * (DH + 1) + 32 * WP + 32 +
                                          TB * (DH + 1) + TB * WP + DH + DH * DH);
     const void* fn = sp == 4 ? reinterpret_cast<const void*>(&k_bwd_query<T, 4>)
