@@ -667,13 +667,27 @@ k_bwd_key(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunks,
   for (int w = 0; w < WP; ++w) du[w] = 0.f;
 
   // ---- later chunks, through R_{>c}: du_j = R^T psi(k_j), d psi(k_j) = R u_j
+  // (the next 32-feature block of R is fetched into registers while the current
+  // one is used; nthr = 256: 9 values per thread at most)
   const float* Rs = rc + ((size_t)unit * n_chunks + c) * STATE_FLOATS;
+  constexpr int PB = (32 * W + 255) / 256;
+  float pre[PB];
+  auto fetch_block = [&](int f0) {
+#pragma unroll
+    for (int e = 0; e < PB; ++e) {
+      const int i = tid + e * 256;
+      if (i < 32 * W) pre[e] = Rs[(size_t)(i / 32) * DS + f0 + i % 32];   // f0 + 31 < DS always
+    }
+  };
+  if (slot == rep) fetch_block(0);
   for (int f0 = 0; slot == rep && f0 < DCAN; f0 += 32) {
     __syncthreads();
-    for (int i = tid; i < 32 * W; i += nthr) {
-      const int w = i / 32, ff = i % 32;
-      s_R[ff * WP + w] = Rs[(size_t)w * DS + f0 + ff];
+#pragma unroll
+    for (int e = 0; e < PB; ++e) {
+      const int i = tid + e * 256;
+      if (i < 32 * W) s_R[(i % 32) * WP + i / 32] = pre[e];
     }
+    if (f0 + 32 < DCAN) fetch_block(f0 + 32);
     __syncthreads();
     if (active) {
       const int nf = min(32, DCAN - f0);
@@ -986,6 +1000,7 @@ static oal_status backward_typed(int batch, int n_q_heads, int n_kv_heads, int s
   }
   {
     const int ks = key_split(chunk);
+    if (ks * chunk != 256) return set_error(OAL_ERR_INVALID_ARG, "k_bwd_key: chunk %d", chunk);
     const size_t smem = sizeof(float) * ((size_t)(1 + ks) * chunk * (DH + 1) + 32 * WP + TB * (DH + 1) +
                                          TB * WP + DH + DH * DH);
     const void* fn = ks == 4 ? reinterpret_cast<const void*>(&k_bwd_key<T, 4>)
