@@ -207,13 +207,27 @@ k_readout_vec(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunk
   const float* qi = s_q + qx * (DH + 1);
 
   // inter-chunk part: phi_q(q_i)^T H_{<c}
+  // (the next 32-feature block is fetched into registers while the current one is
+  // used; nthr is at least 128 threads with SPLIT 2, 256 otherwise)
   const float* Hc = ws + ((size_t)unit * n_chunks + c) * STATE_FLOATS;
+  constexpr int PB = (32 * W + (SPLIT == 2 ? 128 : 256) - 1) / (SPLIT == 2 ? 128 : 256);
+  float pre[PB];
+  auto fetch_block = [&](int f0) {
+#pragma unroll
+    for (int e = 0; e < PB; ++e) {
+      const int i = tid + e * nthr;
+      if (i < 32 * W) pre[e] = Hc[(size_t)(i / 32) * DS + f0 + i % 32];   // f0 + 31 < DS always
+    }
+  };
+  fetch_block(0);
   for (int f0 = 0; f0 < DCAN; f0 += 32) {
     __syncthreads();
-    for (int i = tid; i < 32 * W; i += nthr) {
-      int w = i / 32, ff = i % 32;
-      s_H[ff * WP + w] = Hc[(size_t)w * DS + f0 + ff];   // f0 + 31 < DS always
+#pragma unroll
+    for (int e = 0; e < PB; ++e) {
+      const int i = tid + e * nthr;
+      if (i < 32 * W) s_H[(i % 32) * WP + i / 32] = pre[e];
     }
+    if (f0 + 32 < DCAN) fetch_block(f0 + 32);
     if (tid < 32) {
       int f = f0 + tid;
       float cf = 0.f;
@@ -397,6 +411,8 @@ static oal_status prefill_vec_typed(int batch, int n_q_heads, int n_kv_heads, in
   // the larger) and 2 for grouped ones up to chunk 128, 1 at chunk 256
   constexpr int SP = DIM ? 4 : 2;
   const bool split = chunk <= 128;
+  if (chunk != 64 && chunk != 128 && chunk != 256)   // the state staging's thread counts
+    return set_error(OAL_ERR_INVALID_ARG, "k_readout_vec: chunk %d", chunk);
   const void* fn = split ? reinterpret_cast<const void*>(&k_readout_vec<T, O, DIM, SP>)
                          : reinterpret_cast<const void*>(&k_readout_vec<T, O, DIM, 1>);
   if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem) != hipSuccess)
