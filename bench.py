@@ -717,50 +717,93 @@ def bench_decode(oal, w, reps, n_steps, device):
     }
 
 
-def cpu_baseline(w, seconds):
-    """The float64 oracle on stratified row blocks of query head 0, scaled to the
-    whole workload (every query head, every row)."""
+_CPU_CACHE = {}
+
+
+def _cpu_worker_init(wid):
+    """One BLAS thread per worker process (the pool supplies the parallelism), and
+    every head's float64 inputs regenerated from the seeded streams up front, so
+    that the timed tasks run the oracle only."""
+    try:
+        import threadpoolctl
+        threadpoolctl.threadpool_limits(1)
+    except Exception:
+        pass
+    import numpy as np
+
+    from positive_quadratic_causal_amd import synth
+    w = synth.WORKLOADS[wid]
+    st = synth.structure(w)
+    rep = w.n_q_heads // w.n_kv_heads
+
+    def f64(kind, b, h):
+        return synth.head_tensor(w, st, kind, b, h, w.seq_len).astype(np.float64)
+    for b in range(w.batch):
+        kv = {j: (f64(synth.KIND_K, b, j), f64(synth.KIND_V, b, j)) for j in range(w.n_kv_heads)}
+        for h in range(w.n_q_heads):
+            _CPU_CACHE[(wid, b, h)] = (w, st, f64(synth.KIND_Q, b, h), *kv[h // rep])
+
+
+def _cpu_block(task):
+    """Worker: the float64 oracle on one block of query rows of one (batch, query
+    head).  Returns (task, seconds)."""
     import numpy as np
 
     from oracle import oal_oracle as O
-    from positive_quadratic_causal_amd import synth
-    try:
-        import threadpoolctl
-        info = threadpoolctl.threadpool_info()
-        threads = max([i.get("num_threads", 1) for i in info] or [1])
-    except Exception:
-        threads = len(os.sched_getaffinity(0))
-    st = synth.structure(w)
-    q = synth.head_tensor(w, st, synth.KIND_Q, 0, 0, w.seq_len).astype(np.float64)
-    k = synth.head_tensor(w, st, synth.KIND_K, 0, 0, w.seq_len).astype(np.float64)
-    v = synth.head_tensor(w, st, synth.KIND_V, 0, 0, w.seq_len).astype(np.float64)
+    wid, b, h, i0, i1 = task
+    w, st, q, k, v = _CPU_CACHE[(wid, b, h)]
+    t0 = time.perf_counter()
+    O.causal_attention_rows(q[i0:i1], np.arange(i0, i1), k[:i1], v[:i1], st.L[h].astype(np.float64),
+                            st.group_map[h], int(st.n_groups[h]), w.eps)
+    return task, time.perf_counter() - t0
+
+
+def cpu_baseline(w, seconds):
+    """The float64 oracle timed on the host's cores: a process pool (one BLAS
+    thread each, as many workers as cores available to the job, at most 16, the
+    CPU share of one GPU) over (query head, row block) tasks of every query head of
+    the workload.  The rows are sampled: whole rounds of one row block per head,
+    the blocks spread evenly over the sequence in bit-reversed order (any number of
+    rounds covers it evenly), as many rounds as fit the time budget.  A block costs
+    its rows times the keys they see; tokens/s = the workload's tokens over the
+    measured wall time scaled by the work of all blocks over that of the sampled
+    ones."""
+    import multiprocessing as mp
+
+    cores = max(1, min(len(os.sched_getaffinity(0)), 16))
     blk = 256
     n_blocks = -(-w.seq_len // blk)
-    # 16 strata of the sequence, visited in bit-reversed order so that any prefix
-    # of the visit order is spread over the whole sequence
-    n_strata = 16
-    width = max(1, n_blocks // n_strata)
-    order = [width // 2 + width * int(f"{i:04b}"[::-1], 2) for i in range(n_strata)]
+    nbits = max(1, (n_blocks - 1).bit_length())
+    order = [int(f"{i:0{nbits}b}"[::-1], 2) for i in range(1 << nbits)]
     order = [bi for bi in order if bi < n_blocks]
-    done, t_spent = 0, 0.0
-    for bi in order:
-        i0, i1 = bi * blk, min(w.seq_len, bi * blk + blk)
+    heads = [(b, h) for b in range(w.batch) for h in range(w.n_q_heads)]
+
+    def tasks(blocks):
+        return [(w.wid, b, h, bi * blk, min(w.seq_len, bi * blk + blk)) for bi in blocks for b, h in heads]
+
+    ctx = mp.get_context("spawn")   # fresh interpreters: nothing of this process's GPU context
+    with ctx.Pool(cores, initializer=_cpu_worker_init, initargs=(w.wid,)) as pool:
+        pool.map(_cpu_block, [(w.wid, 0, 0, 0, 8)] * cores, chunksize=1)   # start-up done
+        # the first round takes the middle block (bit-reversed order puts it second):
+        # a block's cost grows with its position, so it costs about an average round
         t0 = time.perf_counter()
-        O.causal_attention_rows(q[i0:i1], np.arange(i0, i1), k, v, st.L[0].astype(np.float64),
-                                st.group_map[0], int(st.n_groups[0]), w.eps)
-        t_spent += time.perf_counter() - t0
-        done += 1
-        if t_spent >= seconds:
-            break
-    # the sampled blocks are spread evenly over the sequence, so their mean cost
-    # is the mean cost of a block of the whole head
-    t_head = t_spent / done * n_blocks
-    t_all = t_head * w.n_q_heads * w.batch
-    return {"value": round(w.batch * w.seq_len / t_all, 3), "unit": "tokens/s", "cores": threads,
+        pool.map(_cpu_block, tasks(order[1:2] if len(order) > 1 else order), chunksize=1)
+        t_round = time.perf_counter() - t0
+        rounds = int(min(len(order), max(2, seconds / max(t_round, 1e-3))))
+        pool.map(_cpu_block, tasks([order[0]] + order[2:rounds]), chunksize=1)
+        t_wall = time.perf_counter() - t0
+    # a block's cost is proportional to its rows times the keys they see (its end
+    # position): scale the measured wall time by that work, all blocks over sampled
+    def work(bi):
+        i1 = min(w.seq_len, bi * blk + blk)
+        return (i1 - bi * blk) * i1
+    t_all = t_wall * sum(work(bi) for bi in range(n_blocks)) / sum(work(bi) for bi in order[:rounds])
+    return {"value": round(w.batch * w.seq_len / t_all, 3), "unit": "tokens/s", "cores": cores,
             "kind": "oracle",
-            "sample": (f"{done} of {n_blocks} row blocks ({blk} rows each, evenly spread) of query "
-                       f"head 0 of the {w.name} workload, direct float64 sum, {t_spent:.1f} s; "
-                       f"scaled to all {w.n_q_heads} query heads x {w.seq_len} rows")}
+            "sample": (f"{rounds} of {n_blocks} row blocks ({blk} rows each, spread evenly over the "
+                       f"sequence) of every one of the {len(heads)} query heads of the {w.name} workload, "
+                       f"direct float64 sum, {cores} worker processes with one BLAS thread each, "
+                       f"{t_wall:.1f} s wall; scaled to all {n_blocks} blocks by their work (rows x keys)")}
 
 
 def cpu_baseline_variants(w):

@@ -129,7 +129,7 @@ def _stream(t: torch.Tensor | None = None):
 def _ptr(t: torch.Tensor | None):
     if t is None:
         return None
-    if not t.is_cuda:
+    if not _on_gpu(t):
         raise ValueError("tensor must be on the GPU")
     if not t.is_contiguous():
         raise ValueError("tensor must be contiguous")
@@ -144,6 +144,66 @@ def _dtype_code(t: torch.Tensor) -> int:
     raise ValueError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
 
 
+def _on_gpu(t: torch.Tensor) -> bool:
+    return t.is_cuda
+
+
+def _expect(t: torch.Tensor | None, name: str, shape: tuple | None = None, dtypes=None,
+            device: torch.device | None = None, optional: bool = False) -> None:
+    """Raises ValueError unless t is a contiguous GPU tensor of the given shape
+    (None entries match any size), one of the given dtypes and on the given device.
+    Every check runs before any device pointer is handed to the library, so a
+    mismatched tensor never reaches a kernel."""
+    if t is None:
+        if optional:
+            return
+        raise ValueError(f"{name} is required")
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch tensor")
+    if not _on_gpu(t):
+        raise ValueError(f"{name} must be on the GPU")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtypes is not None and t.dtype not in dtypes:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected one of {tuple(dtypes)}")
+    if shape is not None:
+        if t.dim() != len(shape) or any(e is not None and int(d) != e for d, e in zip(t.shape, shape)):
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected "
+                             f"{tuple('*' if e is None else e for e in shape)}")
+
+
+_IN_DTYPES = (torch.float32, torch.bfloat16)
+_F32 = (torch.float32,)
+_I32 = (torch.int32,)
+
+
+def _expect_coeffs(coeffs: torch.Tensor | None, n_q_heads: int, device, optional: bool = False) -> None:
+    _expect(coeffs, "coeffs", None, _F32, device, optional)
+    if coeffs is not None and (coeffs.dim() != 2 or coeffs.shape[0] < n_q_heads
+                               or coeffs.shape[1] != COEF_WORDS):
+        raise ValueError(f"coeffs has shape {tuple(coeffs.shape)}, expected ({n_q_heads}, {COEF_WORDS})")
+
+
+def _expect_state(state, batch: int, n_kv_heads: int) -> None:
+    if state is None:
+        return
+    if not isinstance(state, OalState) or not state.handle:
+        raise ValueError("state must be a live OalState")
+    if state.batch != batch or state.n_kv_heads != n_kv_heads:
+        raise ValueError(f"state holds ({state.batch}, {state.n_kv_heads}) units, "
+                         f"expected ({batch}, {n_kv_heads})")
+
+
+def _expect_workspace(ws: torch.Tensor | None, nbytes: int, device) -> None:
+    if ws is None:
+        return
+    _expect(ws, "workspace", None, (torch.uint8,), device)
+    if ws.numel() < nbytes:
+        raise ValueError(f"workspace holds {ws.numel()} bytes, {nbytes} needed")
+
+
 # ---------------------------------------------------------------------------
 
 
@@ -155,14 +215,15 @@ def oal_expand_coeffs(n_groups: torch.Tensor, group_map: torch.Tensor, L: torch.
                       eps: float, coeffs: torch.Tensor | None = None) -> torch.Tensor:
     """n_groups int32 [Hq], group_map int32 [Hq, 64], L float32 [Hq, g+1, g+1].
     Returns (or fills) the coefficient buffer as a float32 tensor [Hq, COEF_WORDS]."""
-    Hq = n_groups.shape[0]
-    g_max = L.shape[-1] - 1
+    _expect(L, "L", (None, None, None), _F32)
+    Hq, g_max = L.shape[0], L.shape[-1] - 1
+    dev = L.device
+    _expect(L, "L", (Hq, g_max + 1, g_max + 1))
+    _expect(n_groups, "n_groups", (Hq,), _I32, dev)
+    _expect(group_map, "group_map", (Hq, D_H), _I32, dev)
     if coeffs is None:
-        coeffs = torch.empty((Hq, COEF_WORDS), dtype=torch.float32, device=L.device)
-    if coeffs.numel() * 4 < oal_coeffs_bytes(Hq, D_H, g_max):
-        raise ValueError("coeffs buffer too small")
-    assert n_groups.dtype == torch.int32 and group_map.dtype == torch.int32
-    assert L.dtype == torch.float32
+        coeffs = torch.empty((Hq, COEF_WORDS), dtype=torch.float32, device=dev)
+    _expect_coeffs(coeffs, Hq, dev)
     _check(_lib.oal_expand_coeffs(Hq, group_map.shape[-1], g_max, _ptr(n_groups), _ptr(group_map),
                                   _ptr(L), float(eps), _ptr(coeffs), _stream(L)))
     return coeffs
@@ -173,14 +234,13 @@ def oal_dim_coeffs(a: torch.Tensor, b: torch.Tensor, C: torch.Tensor,
     """Dimension-specific coefficients: a float32 [Hq], b float32 [Hq, 64],
     C float32 [Hq, 64, 64].  Returns (or fills) a coefficient buffer [Hq, COEF_WORDS]
     for oal_prefill_dim and oal_decode_step."""
-    Hq = a.shape[0]
-    assert a.dtype == b.dtype == C.dtype == torch.float32
-    assert tuple(b.shape) == (Hq, D_H) and tuple(C.shape) == (Hq, D_H, D_H)
-    assert a.is_contiguous() and b.is_contiguous() and C.is_contiguous()
+    _expect(a, "a", (None,), _F32)
+    Hq, dev = a.shape[0], a.device
+    _expect(b, "b", (Hq, D_H), _F32, dev)
+    _expect(C, "C", (Hq, D_H, D_H), _F32, dev)
     if coeffs is None:
-        coeffs = torch.empty((Hq, COEF_WORDS), dtype=torch.float32, device=a.device)
-    if coeffs.numel() * 4 < oal_coeffs_bytes(Hq, D_H, 1):
-        raise ValueError("coeffs buffer too small")
+        coeffs = torch.empty((Hq, COEF_WORDS), dtype=torch.float32, device=dev)
+    _expect_coeffs(coeffs, Hq, dev)
     _check(_lib.oal_dim_coeffs(Hq, D_H, _ptr(a), _ptr(b), _ptr(C), _ptr(coeffs), _stream(a)))
     return coeffs
 
@@ -221,6 +281,7 @@ def oal_state_alloc(batch: int, n_kv_heads: int, d_h: int = D_H, d_v: int = D_V)
 
 
 def oal_state_reset(state: OalState) -> None:
+    _expect_state(state, getattr(state, "batch", -1), getattr(state, "n_kv_heads", -1))
     _check(_lib.oal_state_reset(state.handle, _stream()))
 
 
@@ -229,15 +290,19 @@ def oal_state_free(state: OalState) -> None:
 
 
 def oal_state_copy(dst: OalState, src: OalState) -> None:
+    _expect_state(src, getattr(src, "batch", -1), getattr(src, "n_kv_heads", -1))
+    _expect_state(dst, src.batch, src.n_kv_heads)
     _check(_lib.oal_state_copy(dst.handle, src.handle, _stream()))
 
 
 def oal_state_export(state: OalState, out: torch.Tensor | None = None,
                      device: str | torch.device = "cuda") -> torch.Tensor:
     """Canonical packed state, float32 [B, Hkv, 2145, 65]."""
+    _expect_state(state, getattr(state, "batch", -1), getattr(state, "n_kv_heads", -1))
     if out is None:
         out = torch.empty((state.batch, state.n_kv_heads, D_CANON, D_V + 1), dtype=torch.float32,
                           device=device)
+    _expect(out, "out", (state.batch, state.n_kv_heads, D_CANON, D_V + 1), _F32)
     _check(_lib.oal_state_export(state.handle, _ptr(out), _stream(out)))
     return out
 
@@ -256,26 +321,44 @@ def alloc_workspace(nbytes: int, device="cuda") -> torch.Tensor | None:
     return torch.empty(nbytes, dtype=torch.uint8, device=device)
 
 
+def _prefill_args(q, k, v, coeffs, state, y, want_output):
+    """Shapes of a prefill call, checked: k, v [B, Hkv, N, 64] of one input dtype;
+    q [B, Hq, N, 64] of that dtype and coeffs [Hq, COEF_WORDS] when outputs are
+    wanted; y [B, Hq, N, 64] fp32 or bf16 (allocated in q's dtype if not given)."""
+    _expect(k, "k", (None, None, None, D_H), _IN_DTYPES)
+    B, Hkv, N, _ = k.shape
+    dev = k.device
+    _expect(v, "v", (B, Hkv, N, D_V), (k.dtype,), dev)
+    if want_output or q is not None:
+        _expect(q, "q", (B, None, N, D_H), (k.dtype,), dev)
+        Hq = q.shape[1]
+        _expect_coeffs(coeffs, Hq, dev, optional=not want_output)
+    else:
+        Hq = coeffs.shape[0] if coeffs is not None else Hkv
+        _expect_coeffs(coeffs, Hq, dev, optional=True)
+    _expect_state(state, B, Hkv)
+    if want_output:
+        if y is None:
+            y = torch.empty((B, Hq, N, D_V), dtype=q.dtype, device=dev)
+        _expect(y, "y", (B, Hq, N, D_V), _IN_DTYPES, dev)
+    elif y is not None:
+        raise ValueError("y given with want_output=False")
+    return B, Hkv, N, Hq, y
+
+
 def oal_prefill(q: torch.Tensor | None, k: torch.Tensor, v: torch.Tensor, coeffs: torch.Tensor | None,
                 chunk: int = 0, state: OalState | None = None, y: torch.Tensor | None = None,
                 workspace: torch.Tensor | None = None, want_output: bool = True) -> torch.Tensor | None:
     """q [B, Hq, N, 64] (or None with want_output=False), k/v [B, Hkv, N, 64].
     Returns y [B, Hq, N, 64] in q's dtype unless y is given or want_output is False."""
-    B, Hkv, N, dh = k.shape
-    dv = v.shape[-1]
-    if q is not None:
-        Hq = q.shape[1]
-    elif coeffs is not None:
-        Hq = coeffs.shape[0]
-    else:
-        Hq = Hkv
+    B, Hkv, N, Hq, y = _prefill_args(q, k, v, coeffs, state, y, want_output)
+    dh, dv = D_H, D_V
     in_dt = _dtype_code(k)
-    if want_output and y is None:
-        y = torch.empty((B, Hq, N, dv), dtype=q.dtype, device=q.device)
     out_dt = _dtype_code(y) if y is not None else OAL_F32
     ws_bytes = oal_prefill_workspace_bytes(B, Hq, Hkv, N, chunk, in_dt, y is not None)
     if workspace is None:
         workspace = alloc_workspace(ws_bytes, k.device)
+    _expect_workspace(workspace, ws_bytes, k.device)
     _check(_lib.oal_prefill(B, Hq, Hkv, N, dh, dv, in_dt, _ptr(q), _ptr(k), _ptr(v), _ptr(coeffs),
                             chunk, state.handle if state is not None else None, _ptr(y), out_dt,
                             _ptr(workspace) if workspace is not None else None,
@@ -295,15 +378,13 @@ def oal_prefill_dim(q: torch.Tensor | None, k: torch.Tensor, v: torch.Tensor,
                     want_output: bool = True) -> torch.Tensor | None:
     """Prefill for any coefficient record (dimension-specific ones included); same
     shapes and semantics as oal_prefill."""
-    B, Hkv, N, dh = k.shape
-    dv = v.shape[-1]
-    Hq = q.shape[1] if q is not None else (coeffs.shape[0] if coeffs is not None else Hkv)
-    if want_output and y is None:
-        y = torch.empty((B, Hq, N, dv), dtype=q.dtype, device=q.device)
+    B, Hkv, N, Hq, y = _prefill_args(q, k, v, coeffs, state, y, want_output)
+    dh, dv = D_H, D_V
     out_dt = _dtype_code(y) if y is not None else OAL_F32
+    ws_bytes = oal_prefill_dim_workspace_bytes(B, Hq, Hkv, N, chunk, y is not None)
     if workspace is None:
-        workspace = alloc_workspace(oal_prefill_dim_workspace_bytes(B, Hq, Hkv, N, chunk, y is not None),
-                                    k.device)
+        workspace = alloc_workspace(ws_bytes, k.device)
+    _expect_workspace(workspace, ws_bytes, k.device)
     _check(_lib.oal_prefill_dim(B, Hq, Hkv, N, dh, dv, _dtype_code(k), _ptr(q), _ptr(k), _ptr(v),
                                 _ptr(coeffs), chunk, state.handle if state is not None else None,
                                 _ptr(y), out_dt, _ptr(workspace) if workspace is not None else None,
@@ -324,11 +405,15 @@ def oal_prefill_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, coef
     q [B, Hq, N, 64], k/v [B, Hkv, N, 64] (fp32 or bf16), dy [B, Hq, N, 64] fp32.
     Returns (dq, dk, dv, da, db, dC), all fp32 (the last three None unless
     want_coeff_grad); out may supply the six output tensors."""
+    _expect(q, "q", (None, None, None, D_H), _IN_DTYPES)
     B, Hq, N, dh = q.shape
-    Hkv = k.shape[1]
-    dv_ = v.shape[-1]
-    assert dy.dtype == torch.float32 and dy.is_contiguous()
     dev = q.device
+    _expect(k, "k", (B, None, N, D_H), (q.dtype,), dev)
+    Hkv = k.shape[1]
+    dv_ = D_V
+    _expect(v, "v", (B, Hkv, N, D_V), (q.dtype,), dev)
+    _expect_coeffs(coeffs, Hq, dev)
+    _expect(dy, "dy", (B, Hq, N, D_V), _F32, dev)
     if out is None:
         f32 = dict(dtype=torch.float32, device=dev)
         out = (torch.empty((B, Hq, N, dh), **f32), torch.empty((B, Hkv, N, dh), **f32),
@@ -337,8 +422,18 @@ def oal_prefill_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, coef
                torch.empty((Hq, dh), **f32) if want_coeff_grad else None,
                torch.empty((Hq, dh, dh), **f32) if want_coeff_grad else None)
     dq, dk, dv, da, db, dC = out
+    _expect(dq, "dq", (B, Hq, N, D_H), _F32, dev)
+    _expect(dk, "dk", (B, Hkv, N, D_H), _F32, dev)
+    _expect(dv, "dv", (B, Hkv, N, D_V), _F32, dev)
+    _expect(da, "da", (Hq,), _F32, dev, optional=True)
+    _expect(db, "db", (Hq, D_H), _F32, dev, optional=True)
+    _expect(dC, "dC", (Hq, D_H, D_H), _F32, dev, optional=True)
+    if not ((da is None) == (db is None) == (dC is None)):
+        raise ValueError("da, db and dC are given together or not at all")
+    ws_bytes = oal_prefill_backward_workspace_bytes(B, Hq, Hkv, N, chunk)
     if workspace is None:
-        workspace = alloc_workspace(oal_prefill_backward_workspace_bytes(B, Hq, Hkv, N, chunk), dev)
+        workspace = alloc_workspace(ws_bytes, dev)
+    _expect_workspace(workspace, ws_bytes, dev)
     _check(_lib.oal_prefill_backward(B, Hq, Hkv, N, dh, dv_, _dtype_code(q), _ptr(q), _ptr(k),
                                      _ptr(v), _ptr(coeffs), _ptr(dy), chunk, _ptr(dq), _ptr(dk),
                                      _ptr(dv), _ptr(da), _ptr(db), _ptr(dC),
@@ -352,10 +447,17 @@ def oal_coeffs_backward(n_groups: torch.Tensor, group_map: torch.Tensor, L: torc
                         dL: torch.Tensor | None = None) -> torch.Tensor:
     """dL [Hq, g+1, g+1] from (da, db, dC) through the grouped map (L as for
     oal_expand_coeffs)."""
-    Hq = n_groups.shape[0]
-    g_max = L.shape[-1] - 1
+    _expect(L, "L", (None, None, None), _F32)
+    Hq, g_max, dev = L.shape[0], L.shape[-1] - 1, L.device
+    _expect(L, "L", (Hq, g_max + 1, g_max + 1))
+    _expect(n_groups, "n_groups", (Hq,), _I32, dev)
+    _expect(group_map, "group_map", (Hq, D_H), _I32, dev)
+    _expect(da, "da", (Hq,), _F32, dev)
+    _expect(db, "db", (Hq, D_H), _F32, dev)
+    _expect(dC, "dC", (Hq, D_H, D_H), _F32, dev)
     if dL is None:
         dL = torch.empty_like(L)
+    _expect(dL, "dL", tuple(L.shape), _F32, dev)
     _check(_lib.oal_coeffs_backward(Hq, D_H, g_max, _ptr(n_groups), _ptr(group_map), _ptr(L),
                                     _ptr(da), _ptr(db), _ptr(dC), _ptr(dL), _stream(L)))
     return dL
@@ -365,9 +467,11 @@ def oal_contribution_scores(q: torch.Tensor, k: torch.Tensor, offsets: torch.Ten
                             want_mean: bool = True):
     """q [Hq, T, 64], k [Hkv, T, 64] (prompts concatenated along T), offsets int32
     [P+1].  Returns (chi_prompt [P, Hq, 64], chi [Hq, 64] or None)."""
+    _expect(q, "q", (None, None, D_H), _IN_DTYPES)
     Hq, T, dh = q.shape
+    _expect(k, "k", (None, T, D_H), (q.dtype,), q.device)
+    _expect(offsets, "offsets", (None,), _I32, q.device)
     P = offsets.numel() - 1
-    assert offsets.dtype == torch.int32
     chi_p = torch.empty((P, Hq, dh), dtype=torch.float32, device=q.device)
     chi = torch.empty((Hq, dh), dtype=torch.float32, device=q.device) if want_mean else None
     _check(_lib.oal_contribution_scores(Hq, k.shape[0], P, T, dh, _dtype_code(q), _ptr(q), _ptr(k),
@@ -380,9 +484,10 @@ def oal_bootstrap_grouping(chi_prompt: torch.Tensor, boot_idx: torch.Tensor, alp
                            eps: float = 1e-12, want_stats: bool = True):
     """chi_prompt [P, Hq, 64], boot_idx int32 [B, P].  Returns (group_map int32
     [Hq, 64], n_groups int32 [Hq], support [Hq, 64], gap [Hq, 64])."""
+    _expect(chi_prompt, "chi_prompt", (None, None, D_H), _F32)
     P, Hq, dh = chi_prompt.shape
-    assert boot_idx.dtype == torch.int32 and boot_idx.shape[1] == P
     dev = chi_prompt.device
+    _expect(boot_idx, "boot_idx", (None, P), _I32, dev)
     gm = torch.empty((Hq, dh), dtype=torch.int32, device=dev)
     ng = torch.empty((Hq,), dtype=torch.int32, device=dev)
     sup = torch.empty((Hq, dh), dtype=torch.float32, device=dev) if want_stats else None
@@ -407,17 +512,30 @@ def oal_calib_grad(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, y_ref: tor
         q, k, v = q[0], k[0], v[0]
     if y_ref.dim() == 4:
         y_ref = y_ref[0]
+    _expect(q, "q", (None, None, D_H), _IN_DTYPES)
     Hq, N, dh = q.shape
+    dev = q.device
+    _expect(k, "k", (None, N, D_H), (q.dtype,), dev)
     Hkv = k.shape[0]
+    _expect(v, "v", (Hkv, N, D_V), (q.dtype,), dev)
+    _expect(y_ref, "y_ref", (Hq, N, D_V), _F32, dev)
+    _expect(positions, "positions", (None,), _I32, dev)
     n_pos = positions.numel()
+    _expect(L, "L", (Hq, None, None), _F32, dev)
     g_max = L.shape[-1] - 1
-    assert positions.dtype == torch.int32 and y_ref.dtype == torch.float32
+    _expect(L, "L", (Hq, g_max + 1, g_max + 1))
+    _expect(n_groups, "n_groups", (Hq,), _I32, dev)
+    _expect(group_map, "group_map", (Hq, D_H), _I32, dev)
     if dL is None:
         dL = torch.empty_like(L)
+    _expect(dL, "dL", tuple(L.shape), _F32, dev)
     if loss is None:
         loss = torch.empty((Hq,), dtype=torch.float32, device=L.device)
+    _expect(loss, "loss", (Hq,), _F32, dev)
+    ws_bytes = oal_calib_workspace_bytes(Hq, n_pos)
     if workspace is None:
-        workspace = alloc_workspace(oal_calib_workspace_bytes(Hq, n_pos), L.device)
+        workspace = alloc_workspace(ws_bytes, L.device)
+    _expect_workspace(workspace, ws_bytes, dev)
     _check(_lib.oal_calib_grad(Hq, Hkv, N, dh, v.shape[-1], _dtype_code(q), _ptr(q), _ptr(k), _ptr(v),
                                _ptr(y_ref), _ptr(positions), n_pos, g_max, _ptr(n_groups),
                                _ptr(group_map), _ptr(L), float(eps), _ptr(dL), _ptr(loss),
@@ -429,6 +547,11 @@ def oal_adam_step(n_groups: torch.Tensor, L: torch.Tensor, dL: torch.Tensor, m: 
                   v: torch.Tensor, step: int, lr: float = 0.02, beta1: float = 0.9,
                   beta2: float = 0.999, eps: float = 1e-8, clip_norm: float = 10.0) -> None:
     """In place on L, m, v (all [Hq, g+1, g+1] fp32)."""
+    _expect(L, "L", (None, None, None), _F32)
+    dev = L.device
+    _expect(n_groups, "n_groups", (L.shape[0],), _I32, dev)
+    for t, nm in ((dL, "dL"), (m, "m"), (v, "v")):
+        _expect(t, nm, tuple(L.shape), _F32, dev)
     _check(_lib.oal_adam_step(n_groups.shape[0], L.shape[-1] - 1, _ptr(n_groups), _ptr(L), _ptr(dL),
                               _ptr(m), _ptr(v), int(step), float(lr), float(beta1), float(beta2),
                               float(eps), float(clip_norm), _stream(L)))
@@ -438,9 +561,12 @@ def oal_embed_global(n_groups: torch.Tensor, L_global: torch.Tensor, g_max: int 
                      L: torch.Tensor | None = None) -> torch.Tensor:
     """L_global [Hq, g+1, g+1] (a G = 1 calibration's L); returns the grouped start
     L [Hq, g_max+1, g_max+1]."""
+    _expect(n_groups, "n_groups", (None,), _I32)
     Hq = n_groups.shape[0]
+    _expect(L_global, "L_global", (Hq, None, None), _F32, n_groups.device)
     if L is None:
         L = torch.empty((Hq, g_max + 1, g_max + 1), dtype=torch.float32, device=L_global.device)
+    _expect(L, "L", (Hq, g_max + 1, g_max + 1), _F32, n_groups.device)
     _check(_lib.oal_embed_global(Hq, g_max, _ptr(n_groups), L_global.shape[-1], _ptr(L_global), _ptr(L),
                                  _stream(L)))
     return L
@@ -448,9 +574,12 @@ def oal_embed_global(n_groups: torch.Tensor, L_global: torch.Tensor, g_max: int 
 
 def oal_output_mse(y: torch.Tensor, y_ref: torch.Tensor, mse: torch.Tensor | None = None) -> torch.Tensor:
     """y, y_ref [B, Hq, N, d_v] fp32; returns the per-head MSE [Hq]."""
+    _expect(y, "y", (None, None, None, D_V), _F32)
     B, Hq, N, dv = y.shape
+    _expect(y_ref, "y_ref", tuple(y.shape), _F32, y.device)
     if mse is None:
         mse = torch.empty((Hq,), dtype=torch.float32, device=y.device)
+    _expect(mse, "mse", (Hq,), _F32, y.device)
     _check(_lib.oal_output_mse(B, Hq, N, dv, _ptr(y), _ptr(y_ref), _ptr(mse), _stream(y)))
     return mse
 
@@ -458,11 +587,20 @@ def oal_output_mse(y: torch.Tensor, y_ref: torch.Tensor, mse: torch.Tensor | Non
 def oal_decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, coeffs: torch.Tensor,
                     state: OalState, y: torch.Tensor | None = None) -> torch.Tensor:
     """q [B, Hq, 64], k/v [B, Hkv, 64]; returns y [B, Hq, 64]."""
+    _expect(q, "q", (None, None, D_H), _IN_DTYPES)
     B, Hq, dh = q.shape
+    dev = q.device
+    _expect(k, "k", (B, None, D_H), (q.dtype,), dev)
     Hkv = k.shape[1]
-    dv = v.shape[-1]
+    dv = D_V
+    _expect(v, "v", (B, Hkv, D_V), (q.dtype,), dev)
+    _expect_coeffs(coeffs, Hq, dev)
+    if state is None:
+        raise ValueError("state is required")
+    _expect_state(state, B, Hkv)
     if y is None:
         y = torch.empty((B, Hq, dv), dtype=q.dtype, device=q.device)
+    _expect(y, "y", (B, Hq, D_V), _IN_DTYPES, dev)
     _check(_lib.oal_decode_step(B, Hq, Hkv, dh, dv, _dtype_code(q), _ptr(q), _ptr(k), _ptr(v),
                                 _ptr(coeffs), state.handle, _ptr(y), _dtype_code(y), _stream(q)))
     return y
@@ -472,11 +610,16 @@ def oal_softmax_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                           y: torch.Tensor | None = None) -> torch.Tensor:
     """Exact causal softmax attention (the reference OAL approximates): q [B, Hq, N, 64],
     k/v [B, Hkv, N, 64] in bf16; returns y [B, Hq, N, 64] in q's dtype unless y is given."""
+    _expect(q, "q", (None, None, None, D_H), _IN_DTYPES)
     B, Hq, N, dh = q.shape
+    dev = q.device
+    _expect(k, "k", (B, None, N, D_H), (q.dtype,), dev)
     Hkv = k.shape[1]
-    dv = v.shape[-1]
+    dv = D_V
+    _expect(v, "v", (B, Hkv, N, D_V), (q.dtype,), dev)
     if y is None:
         y = torch.empty((B, Hq, N, dv), dtype=q.dtype, device=q.device)
+    _expect(y, "y", (B, Hq, N, D_V), _IN_DTYPES, dev)
     _check(_lib.oal_softmax_attention(B, Hq, Hkv, N, dh, dv, _dtype_code(q), _ptr(q), _ptr(k), _ptr(v),
                                       _ptr(y), _dtype_code(y), _stream(q)))
     return y

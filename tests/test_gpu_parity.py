@@ -28,15 +28,31 @@ def _prefill(oal, case, chunk=128, state=None, y=True):
                            state=state, want_output=y)
 
 
+def _row_errors(y, ref):
+    """rel-L2 of each output row (token) against the reference."""
+    y = np.asarray(y, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    return np.linalg.norm(y - ref, axis=-1) / np.maximum(np.linalg.norm(ref, axis=-1), 1e-30)
+
+
+def _check_rows(y, ref, tol, what):
+    """rel-L2 over the rows together and every row on its own within tol, so that
+    an error confined to a few rows (a chunk edge, a segment hand-over) cannot hide
+    inside the norm of a whole head."""
+    err = rel_l2(y, ref)
+    rows = _row_errors(y, ref)
+    assert err <= tol, (what, err)
+    assert rows.max() <= tol, (what, int(np.argmax(rows)), float(rows.max()))
+    return err
+
+
 def _check_heads(case, y_gpu, heads, tol):
     y = y_gpu.float().cpu().numpy()
     assert np.all(np.isfinite(y))
     worst = 0.0
     for b, h in heads:
         ref = case.oracle_head(b, h)
-        err = rel_l2(y[b, h], ref)
-        worst = max(worst, err)
-        assert err <= tol, (b, h, err)
+        worst = max(worst, _check_rows(y[b, h], ref, tol, (b, h)))
     return worst
 
 
@@ -168,8 +184,8 @@ def test_prefill_continues_from_state(oal, dtype):
     y = torch.cat([y1, y2], dim=2).float().cpu().numpy()
     for h in range(4):
         ref = case.oracle_head(0, h)
-        assert rel_l2(y[0, h], ref) <= tol_for(w)
-        assert rel_l2(y[0, h, n1:], ref[n1:]) <= tol_for(w)
+        _check_rows(y[0, h], ref, tol_for(w), h)
+        _check_rows(y[0, h, n1:], ref[n1:], tol_for(w), h)
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
@@ -181,10 +197,10 @@ def test_state_export_matches_oracle_state(oal, dtype):
     st = oal.oal_state_alloc(2, 2)
     oal.oal_prefill(None, case.k, case.v, None, chunk=128, state=st, want_output=False)
     exp = oal.oal_state_export(st).cpu().numpy()
-    # bf16 inputs: the matrix-core build rounds each key feature k_r k_t to bf16
-    # (unit roundoff 2^-9, about 1.1e-3 RMS relative per product), so the fp32
-    # state carries ~1e-3 relative error; the bar is 2^-8.
-    tol = 1e-5 if dtype == "f32" else 2.0 ** -8
+    # bf16 inputs: the matrix-core build forms each key product k_r k_t in fp16
+    # (unit roundoff 2^-11, about 2.8e-4 RMS relative per product) before the fp32
+    # accumulation; k, v and the linear rows are exact.  The bar is 1e-3.
+    tol = 1e-5 if dtype == "f32" else 1e-3
     for b in range(2):
         for kv in range(2):
             _, k, v = case.head_qkv(b, kv * 2, n)
@@ -194,7 +210,9 @@ def test_state_export_matches_oracle_state(oal, dtype):
     st2 = oal.oal_state_alloc(2, 2)
     _prefill(oal, case, 64, state=st2)
     exp2 = oal.oal_state_export(st2).cpu().numpy()
-    assert rel_l2(exp2, exp) <= (1e-6 if dtype == "f32" else 1e-5)
+    # the two calls split the sequence into builder segments differently (chunk 128
+    # against 64): only the fp32 summation order differs
+    assert rel_l2(exp2, exp) <= 1e-6
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
@@ -219,7 +237,7 @@ def test_decode_after_prefill(oal, dtype):
     for b in range(2):
         for h in range(8):
             ref = case.oracle_rows(b, h, np.arange(n0, n0 + steps))
-            assert rel_l2(y[b, h], ref) <= tol_for(w), (b, h)
+            _check_rows(y[b, h], ref, tol_for(w), (b, h))
 
 
 def test_decode_from_empty_state(oal):
@@ -248,7 +266,7 @@ def test_prefill_chunk_invariance_and_determinism(oal):
     ref = [case.oracle_head(0, h) for h in range(4)]
     for c in ys:
         for h in range(4):
-            assert rel_l2(ys[c][0, h], ref[h]) <= tol_for(w)
+            _check_rows(ys[c][0, h], ref[h], tol_for(w), (c, h))
 
 
 # The bf16 path rounds the intra-chunk weights kappa to bf16 for the P V product
@@ -280,7 +298,9 @@ def test_prefill_llama_4096_sampled_heads(oal):
     yc = y.float().cpu().numpy()
     assert np.all(np.isfinite(yc))
     rng = np.random.default_rng(2)
-    heads = [(int(rng.integers(4)), int(rng.integers(32))) for _ in range(5)] + [(3, 31), (0, 0)]
+    # two query heads of every KV head (the first and the last slot of each GQA
+    # group), each in a random sequence of the batch, plus the two corners
+    heads = [(int(rng.integers(4)), 4 * kv + s) for kv in range(8) for s in (0, 3)] + [(3, 31), (0, 0)]
     _check_heads(case, y, heads, tol_for(w))
 
 
@@ -294,10 +314,16 @@ def test_prefill_long_32768_sampled_rows(oal, chunk):
     yc = y.float().cpu().numpy()
     assert np.all(np.isfinite(yc))
     rng = np.random.default_rng(3)
-    rows = np.unique(np.concatenate([rng.integers(0, 32768, 40), [0, 1, 127, 128, 32767]]))
+    # random rows; both sides of every 64-, 128- and 256-token chunk edge in the first
+    # 1024 tokens; the first row of every state-builder segment and the row before it
+    # (segments start at multiples of 960 or 1024 tokens at this length); the ends
+    edges = np.concatenate([[63, 64, 127, 128, 191, 192, 255, 256, 511, 512, 767, 768, 1023, 1024],
+                            np.arange(960, 32768, 960), np.arange(960, 32768, 960) - 1,
+                            np.arange(1024, 32768, 1024), np.arange(1024, 32768, 1024) - 1])
+    rows = np.unique(np.concatenate([rng.integers(0, 32768, 40), [0, 1, 2, 32766, 32767], edges]))
     for h in (0, 6, 7, 13):
         ref = case.oracle_rows(0, h, rows)
-        assert rel_l2(yc[0, h, rows], ref) <= tol_for(w), h
+        _check_rows(yc[0, h, rows], ref, tol_for(w), h)
 
 
 # Powers of two: exact in bf16, so the oracle sees the same values scaled.
@@ -330,7 +356,7 @@ def test_prefill_magnitude_range(oal, sq, sk, sv):
         q, k, v = case.head_qkv(0, h)
         ref = O.causal_attention(q * sq, k * sk, v * sv, case.st.L[h].astype(np.float64),
                                  case.st.group_map[h], int(case.st.n_groups[h]), w.eps)
-        assert rel_l2(y[0, h], ref) <= tol_for(w), h
+        _check_rows(y[0, h], ref, tol_for(w), h)
 
 
 def test_prefill_many_outlier_dims(oal):
@@ -387,4 +413,4 @@ def test_learned_global_single_group(oal, dtype):
     assert np.all(np.isfinite(yd))
     for h in range(4):
         ref = case.oracle_head(0, h)[n0:]
-        assert rel_l2(yd[0, h], ref) <= tol_for(w), h
+        _check_rows(yd[0, h], ref, tol_for(w), h)
