@@ -12,7 +12,7 @@ import torch
 from oracle import oal_oracle as O
 from positive_quadratic_causal_amd import synth
 
-from gpu_util import Case, announce, rel_l2, tol_for
+from gpu_util import TOL_BF16, Case, announce, rel_l2, tol_for
 
 pytestmark = pytest.mark.gpu
 
@@ -35,24 +35,25 @@ def _row_errors(y, ref):
     return np.linalg.norm(y - ref, axis=-1) / np.maximum(np.linalg.norm(ref, axis=-1), 1e-30)
 
 
-def _check_rows(y, ref, tol, what):
-    """rel-L2 over the rows together and every row on its own within tol, so that
-    an error confined to a few rows (a chunk edge, a segment hand-over) cannot hide
-    inside the norm of a whole head."""
+def _check_rows(y, ref, tol, what, row_tol=None):
+    """rel-L2 over the rows together within tol and every row on its own within
+    row_tol (default tol), so that an error confined to a few rows (a chunk edge, a
+    segment hand-over) cannot hide inside the norm of a whole head."""
     err = rel_l2(y, ref)
     rows = _row_errors(y, ref)
+    row_tol = tol if row_tol is None else row_tol
     assert err <= tol, (what, err)
-    assert rows.max() <= tol, (what, int(np.argmax(rows)), float(rows.max()))
+    assert rows.max() <= row_tol, (what, int(np.argmax(rows)), float(rows.max()))
     return err
 
 
-def _check_heads(case, y_gpu, heads, tol):
+def _check_heads(case, y_gpu, heads, tol, row_tol=None):
     y = y_gpu.float().cpu().numpy()
     assert np.all(np.isfinite(y))
     worst = 0.0
     for b, h in heads:
         ref = case.oracle_head(b, h)
-        worst = max(worst, _check_rows(y[b, h], ref, tol, (b, h)))
+        worst = max(worst, _check_rows(y[b, h], ref, tol, (b, h), row_tol))
     return worst
 
 
@@ -274,7 +275,8 @@ def test_prefill_chunk_invariance_and_determinism(oal):
 # (2^-11); the expected rel-L2 of an fp32 output is therefore about 2e-3.  A
 # bound three times that, well inside the 2e-2 bar, catches a structural slip
 # (a wrong multiplicity or a lost block of pairs) that the bar alone could let
-# through.
+# through.  It bounds each head's rows together; a single row averages over fewer
+# weights (row 5 sees six keys), so each row is held to the 2e-2 accuracy target.
 MARGIN_F32_OUT = 6e-3
 
 
@@ -286,7 +288,7 @@ def test_prefill_precision_margin(oal, chunk):
     y = torch.empty(case.q.shape, dtype=torch.float32, device="cuda")
     oal.oal_prefill(case.q, case.k, case.v, case.coeffs(), chunk=chunk, y=y)
     torch.cuda.synchronize()
-    _check_heads(case, y, [(0, h) for h in (0, 3, 6, 7, 10, 13)], MARGIN_F32_OUT)
+    _check_heads(case, y, [(0, h) for h in (0, 3, 6, 7, 10, 13)], MARGIN_F32_OUT, row_tol=TOL_BF16)
 
 
 def test_prefill_llama_4096_sampled_heads(oal):
