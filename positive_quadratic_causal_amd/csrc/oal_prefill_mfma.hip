@@ -48,7 +48,13 @@ struct ReadoutCfg {
   static constexpr int HS_BYTES = 4 * tile::KS_BYTES;   // one half-slab = 4 K-steps = 8 KB
   static constexpr int NHS = tile::NKS / 4;         // 37 half-slabs per tile
   static constexpr int Q_BYTES = HPW * CH * 128;    // = 32 KB
-  static constexpr int XB = CH == 256 ? HS_BYTES : 16;   // extra staging arrays (C = 256)
+  // The chunk's keys are staged for the intra-chunk part in the half-slab buffers,
+  // 128 at a time (k rows in buffers 0, 1, v^T rows in 2, 3): one pass up to
+  // C = 128, two at C = 256 (which keeps the workgroup's LDS below 80 KB, so that
+  // two workgroups fit a CU).
+  static constexpr int KPASS = CH < 128 ? CH : 128;  // keys per staging pass
+  static constexpr int NPASS = CH / KPASS;
+  static constexpr int KIT = KPASS / 64;             // token pairs per thread and pass
 };
 
 // Per-head table (floats), written from the coefficient record with the head's
@@ -100,7 +106,7 @@ __device__ __forceinline__ uint8_t* pick4(int i, uint8_t* a, uint8_t* b, uint8_t
 }
 
 template <int CH, typename O>
-__global__ void __launch_bounds__(256, CH == 256 ? 1 : 2)   // C = 256: LDS allows one
+__global__ void __launch_bounds__(256, 2)
 k_readout_mfma(int n_q_heads, int n_kv_heads, int seq_len, int n_chunks, int n_hg, int n_uc,
                const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                const uint16_t* __restrict__ v, const float* __restrict__ coeffs,
@@ -111,21 +117,16 @@ k_readout_mfma(int n_q_heads, int n_kv_heads, int seq_len, int n_chunks, int n_h
   __shared__ __attribute__((aligned(16))) uint8_t s_b1[Cfg::HS_BYTES];
   __shared__ __attribute__((aligned(16))) uint8_t s_b2[Cfg::HS_BYTES];
   __shared__ __attribute__((aligned(16))) uint8_t s_b3[Cfg::HS_BYTES];
-  __shared__ __attribute__((aligned(16))) uint8_t s_x0[Cfg::XB];
-  __shared__ __attribute__((aligned(16))) uint8_t s_x1[Cfg::XB];
-  __shared__ __attribute__((aligned(16))) uint8_t s_x2[Cfg::XB];
-  __shared__ __attribute__((aligned(16))) uint8_t s_x3[Cfg::XB];
   __shared__ __attribute__((aligned(16))) _Float16 s_mg[Cfg::HPW * LDIM * DH];
   __shared__ __attribute__((aligned(16))) float s_ht[Cfg::HPW * htab::FLOATS];
   __shared__ float s_red[16];
   __shared__ __attribute__((aligned(16))) float s_h0[DV];   // H0 of the chunk's prefix
   // inter-chunk denominators handed to the mirror waves, per (head, wave pair)
   __shared__ float s_dx[Cfg::HPW * (Cfg::WPH > 1 ? Cfg::WPH / 2 : 1) * 64];
-  // k rows (64 per array) and v^T rows (64 keys per array) of the chunk
-  auto k_arr = [&](int i) -> uint8_t* { return pick4(i, s_b0, s_b1, s_b2, s_b3); };
-  auto v_arr = [&](int i) -> uint8_t* {
-    return CH == 256 ? pick4(i, s_x0, s_x1, s_x2, s_x3) : pick4(i, s_b2, s_b3, s_b2, s_b3);
-  };
+  // k rows (64 per array) and v^T rows (64 keys per array) of the keys staged
+  // by one pass (i: 64-key block inside the pass)
+  auto k_arr = [&](int i) -> uint8_t* { return i == 0 ? s_b0 : s_b1; };
+  auto v_arr = [&](int i) -> uint8_t* { return i == 0 ? s_b2 : s_b3; };
 
   // ---- which (unit, chunk, head group): the head groups of one (unit, chunk)
   //      share an XCD (blockIdx % 8) so they hit the same L2 for the state.
@@ -161,7 +162,7 @@ k_readout_mfma(int n_q_heads, int n_kv_heads, int seq_len, int n_chunks, int n_h
   //      clamping the address and zeroing the value afterwards): q of all heads
   //      of the group, k and v of the chunk, and this wave's coefficients
   constexpr int QIT = Cfg::HPW * CH * 8 / 256;   // 16-byte q pieces per thread
-  constexpr int KIT = CH / 64;                   // token pairs per thread
+  constexpr int KIT = Cfg::KIT;                  // token pairs per thread and pass
   uint4 qv[QIT];
 #pragma unroll
   for (int it = 0; it < QIT; ++it) {
@@ -171,18 +172,22 @@ k_readout_mfma(int n_q_heads, int n_kv_heads, int seq_len, int n_chunks, int n_h
     const size_t row = ((size_t)b * n_q_heads + kv * rep + hh) * seq_len + t0 + min(tok, clen - 1);
     qv[it] = reinterpret_cast<const uint4*>(q + row * DH)[part];
   }
-  // k and v: thread t holds dims 8 (t & 7) .. + 7 of the tokens 64 it + 2 (t >> 3) + e
+  // k and v of a staging pass: thread t holds dims 8 (t & 7) .. + 7 of the tokens
+  // KPASS pass + 64 it + 2 (t >> 3) + e
   const size_t kvrow0 = (size_t)unit * seq_len + t0;
   const int kpart = tid & 7, kpair = tid >> 3;
   uint4 kq[KIT][2], vq[KIT][2];
+  auto load_kv = [&](int pass) {
 #pragma unroll
-  for (int it = 0; it < KIT; ++it)
+    for (int it = 0; it < KIT; ++it)
 #pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const size_t row = kvrow0 + min(64 * it + 2 * kpair + e, clen - 1);
-      kq[it][e] = reinterpret_cast<const uint4*>(k + row * DH)[kpart];
-      vq[it][e] = reinterpret_cast<const uint4*>(v + row * DV)[kpart];
-    }
+      for (int e = 0; e < 2; ++e) {
+        const size_t row = kvrow0 + min(Cfg::KPASS * pass + 64 * it + 2 * kpair + e, clen - 1);
+        kq[it][e] = reinterpret_cast<const uint4*>(k + row * DH)[kpart];
+        vq[it][e] = reinterpret_cast<const uint4*>(v + row * DV)[kpart];
+      }
+  };
+  load_kv(0);
   const float mval = rec[OAL_COEF_M + min(lane, LDIM * LDIM - 1)];
   const float bval = rec[OAL_COEF_BP + lane];
   const int gl = reinterpret_cast<const int32_t*>(rec)[OAL_COEF_GMAP + lane];   // g(r), lane r
@@ -232,18 +237,25 @@ k_readout_mfma(int n_q_heads, int n_kv_heads, int seq_len, int n_chunks, int n_h
   }
   // ---- k rows, and v^T rows with the keys of each 16-block permuted: position
   //      8h + 4a + e holds key 8a + 4h + e (the key order of the kappa accumulator
-  //      rows); the two tokens of a thread are adjacent there (one 32-bit write)
+  //      rows); the two tokens of a thread are adjacent there (one 32-bit write).
+  //      tok: the key inside the pass, KPASS pass + tok inside the chunk.
+  auto stage_kv = [&](int pass) {
+  // the thread's indices taken afresh: the compiler would otherwise keep the first
+  // pass's LDS addresses live (spilled) across the intra-chunk part for the second
+  int kpair_ = kpair, kpart_ = kpart;
+  asm volatile("" : "+v"(kpair_), "+v"(kpart_));
 #pragma unroll
   for (int it = 0; it < KIT; ++it) {
-    const int tok = 64 * it + 2 * kpair;       // even; tok + 1 is the pair's second token
-    const bool ok0 = tok < clen, ok1 = tok + 1 < clen;
+    const int tok = 64 * it + 2 * kpair_;      // even; tok + 1 is the pair's second token
+    const int ctok = Cfg::KPASS * pass + tok;
+    const bool ok0 = ctok < clen, ok1 = ctok + 1 < clen;
     const uint4 k0 = ok0 ? kq[it][0] : make_uint4(0, 0, 0, 0);
     const uint4 k1 = ok1 ? kq[it][1] : make_uint4(0, 0, 0, 0);
     const uint4 v0 = ok0 ? vq[it][0] : make_uint4(0, 0, 0, 0);
     const uint4 v1 = ok1 ? vq[it][1] : make_uint4(0, 0, 0, 0);
     uint8_t* ka = k_arr(tok >> 6);
-    *reinterpret_cast<uint4*>(ka + (tok & 63) * 128 + ((kpart ^ row_key(tok & 63)) << 4)) = k0;
-    *reinterpret_cast<uint4*>(ka + ((tok + 1) & 63) * 128 + ((kpart ^ row_key((tok + 1) & 63)) << 4)) = k1;
+    *reinterpret_cast<uint4*>(ka + (tok & 63) * 128 + ((kpart_ ^ row_key(tok & 63)) << 4)) = k0;
+    *reinterpret_cast<uint4*>(ka + ((tok + 1) & 63) * 128 + ((kpart_ ^ row_key((tok + 1) & 63)) << 4)) = k1;
     const int pos = (tok & ~15) | (((tok >> 2) & 1) << 3) | (((tok >> 3) & 1) << 2) | (tok & 3);
     uint8_t* va = v_arr(pos >> 6);
     const int pk = pos & 63;
@@ -251,12 +263,14 @@ k_readout_mfma(int n_q_heads, int n_kv_heads, int seq_len, int n_chunks, int n_h
     const uint32_t* a1 = reinterpret_cast<const uint32_t*>(&v1);
 #pragma unroll
     for (int x = 0; x < 8; ++x) {
-      const int w = kpart * 8 + x;
+      const int w = kpart_ * 8 + x;
       const uint32_t word = (x & 1) ? (a0[x >> 1] >> 16) | (a1[x >> 1] & 0xffff0000u)
                                     : (a0[x >> 1] & 0xffffu) | (a1[x >> 1] << 16);
       *reinterpret_cast<uint32_t*>(va + w * 128 + (((pk >> 3) ^ row_key(w)) << 4) + ((pk & 7) << 1)) = word;
     }
   }
+  };
+  stage_kv(0);
 
   // (after the staging's last use of its loads: memory operations complete in
   // order, so no later wait of the staging waits for these)
@@ -465,7 +479,8 @@ k_readout_mfma(int n_q_heads, int n_kv_heads, int seq_len, int n_chunks, int n_h
   // the raw inputs and each t_p one 16-deep product over the gathered outlier dims
   // plus two constant slots that add L_0p, seeded with c_p S (zero for p >= 2).
   // Otherwise each t_p is a 64-deep product with A = k o ell_p, seeded with L_0p.
-  if (head_ok) {
+  // Key tiles are addressed inside the staged pass (kt - 4 pass).
+  {
     const float epsF = rec[OAL_COEF_EPS] * F;
     const int* cidx = reinterpret_cast<const int*>(ht + htab::CIDX) + 8 * half;
     bf16x8 qc[2];                              // compact q (B operand) of the wave's tokens
@@ -583,11 +598,28 @@ k_readout_mfma(int n_q_heads, int n_kv_heads, int seq_len, int n_chunks, int n_h
       }
     };
     // key tiles 0 .. T1: both token tiles up to T0 (T0 the diagonal one of N-tile
-    // 0), then N-tile 1 alone (T1 its diagonal one)
-    for (int kt = 0; kt < T0; ++kt) key_tile(kt, bool_t<true>{}, bool_t<false>{}, bool_t<false>{});
-    key_tile(T0, bool_t<true>{}, bool_t<true>{}, bool_t<false>{});
-    for (int kt = T0 + 1; kt < T1; ++kt) key_tile(kt, bool_t<false>{}, bool_t<false>{}, bool_t<false>{});
-    key_tile(T1, bool_t<false>{}, bool_t<false>{}, bool_t<true>{});
+    // 0), then N-tile 1 alone (T1 its diagonal one).  With two passes T0 < 4 <= T1:
+    // the first pass holds key tiles 0..3, the second 4..7.
+    if (head_ok) {
+      for (int kt = 0; kt < T0; ++kt) key_tile(kt, bool_t<true>{}, bool_t<false>{}, bool_t<false>{});
+      key_tile(T0, bool_t<true>{}, bool_t<true>{}, bool_t<false>{});
+      if (Cfg::NPASS == 1) {
+        for (int kt = T0 + 1; kt < T1; ++kt) key_tile(kt, bool_t<false>{}, bool_t<false>{}, bool_t<false>{});
+        key_tile(T1, bool_t<false>{}, bool_t<false>{}, bool_t<true>{});
+      } else {
+        for (int kt = T0 + 1; kt < 4; ++kt) key_tile(kt, bool_t<false>{}, bool_t<false>{}, bool_t<false>{});
+      }
+    }
+    if (Cfg::NPASS > 1) {
+      load_kv(1);        // (issued here: in flight during the first pass they would spill)
+      __syncthreads();   // every wave is done with the first pass's keys
+      stage_kv(1);
+      __syncthreads();
+      if (head_ok) {
+        for (int kt = 4; kt < T1; ++kt) key_tile(kt - 4, bool_t<false>{}, bool_t<false>{}, bool_t<false>{});
+        key_tile(T1 - 4, bool_t<false>{}, bool_t<false>{}, bool_t<true>{});
+      }
+    }
   }
 
   // ================= inter-chunk part ======================================
