@@ -157,6 +157,25 @@ oal_status oal_prefill(int batch, int n_q_heads, int n_kv_heads, int seq_len, in
                        oal_dtype out_dtype, void* workspace, size_t workspace_bytes,
                        hipStream_t stream);
 
+/* ---- allocation-free prefill ----------------------------------------------
+ * For callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): oal_prefill with the
+ * same arguments except the workspace, which comes from a static device array of
+ * OAL_NOALLOC_SCRATCH_BYTES (128 MiB) that the library holds on every GPU it runs
+ * on until the process ends.  The call allocates nothing (no hipMalloc, hipFree
+ * or allocating library routine); its first call on a device looks the array's
+ * address up.  Sizes whose workspace (oal_prefill_workspace_bytes) exceeds the
+ * array return OAL_ERR_UNSUPPORTED before any HIP call; other errors are those of
+ * oal_prefill.  Every call on a GPU shares that GPU's array, so calls that overlap
+ * on one GPU (concurrent streams, or host threads) race and must be serialised by
+ * the caller; nothing in the array needs to start at zero. */
+#define OAL_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+size_t oal_prefill_noalloc_scratch_bytes(void);
+oal_status oal_prefill_noalloc(int batch, int n_q_heads, int n_kv_heads, int seq_len, int d_h,
+                               int d_v, oal_dtype in_dtype, const void* q, const void* k,
+                               const void* v, const void* coeffs, int chunk, oal_state* state,
+                               void* y, oal_dtype out_dtype, hipStream_t stream);
+
 /* Device workspace oal_prefill_dim needs (same conventions as
  * oal_prefill_workspace_bytes; the size does not depend on the input dtype). */
 size_t oal_prefill_dim_workspace_bytes(int batch, int n_q_heads, int n_kv_heads, int seq_len,

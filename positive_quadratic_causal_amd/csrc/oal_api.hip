@@ -379,6 +379,68 @@ oal_status oal_prefill(int batch, int n_q_heads, int n_kv_heads, int seq_len, in
   return st;
 }
 
+// ---- allocation-free prefill -------------------------------------------------
+// The scratch of oal_prefill_noalloc: a file-scope device array (one copy on every
+// GPU the library runs on, held until the process ends).  Host code never passes
+// the array's name to a kernel (on the host it is only a stand-in): the device
+// address of each GPU's copy is looked up once per device with
+// hipGetSymbolAddress and kept here.
+namespace {
+__device__ __align__(256) uint8_t scratch[OAL_NOALLOC_SCRATCH_BYTES];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+oal_status scratch_ptr(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return set_error(OAL_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return set_error(OAL_ERR_UNSUPPORTED, "device %d beyond the %d the scratch table holds", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr)
+      return set_error(OAL_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev,
+                       hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return OAL_OK;
+}
+}  // namespace
+
+size_t oal_prefill_noalloc_scratch_bytes(void) { return OAL_NOALLOC_SCRATCH_BYTES; }
+
+oal_status oal_prefill_noalloc(int batch, int n_q_heads, int n_kv_heads, int seq_len, int d_h,
+                               int d_v, oal_dtype in_dtype, const void* q, const void* k,
+                               const void* v, const void* coeffs, int chunk, oal_state* state,
+                               void* y, oal_dtype out_dtype, hipStream_t stream) {
+  chunk = resolve_chunk(chunk);
+  const size_t need = oal_prefill_workspace_bytes(batch, n_q_heads, n_kv_heads, seq_len, d_h, d_v,
+                                                  chunk, in_dtype, y != nullptr);
+  if (need > OAL_NOALLOC_SCRATCH_BYTES)
+    return set_error(OAL_ERR_UNSUPPORTED,
+                     "oal_prefill_noalloc: these sizes need %zu bytes of scratch, the static buffer "
+                     "holds %zu (use oal_prefill with a workspace)", need,
+                     (size_t)OAL_NOALLOC_SCRATCH_BYTES);
+  // the same checks as oal_prefill (with a stand-in for the workspace) before any
+  // HIP call, so that invalid arguments fail the same way
+  oal_status st = prefill_checks(batch, n_q_heads, n_kv_heads, seq_len, d_h, d_v, in_dtype, q, k, v,
+                                 coeffs, chunk, state, y, out_dtype,
+                                 need > 0 ? reinterpret_cast<void*>(256) : nullptr,
+                                 OAL_NOALLOC_SCRATCH_BYTES, need);
+  if (st != OAL_OK || seq_len == 0) return st;
+  void* ws = nullptr;
+  if (need > 0) {
+    st = scratch_ptr(&ws);
+    if (st != OAL_OK) return st;
+  }
+  return oal_prefill(batch, n_q_heads, n_kv_heads, seq_len, d_h, d_v, in_dtype, q, k, v, coeffs,
+                     chunk, state, y, out_dtype, ws, need > 0 ? OAL_NOALLOC_SCRATCH_BYTES : 0, stream);
+}
+
 size_t oal_prefill_dim_workspace_bytes(int batch, int n_q_heads, int n_kv_heads, int seq_len,
                                        int d_h, int d_v, int chunk, int with_output) {
   if (check_heads(batch, n_q_heads, n_kv_heads, d_h, d_v) != OAL_OK) return 0;

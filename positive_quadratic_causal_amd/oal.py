@@ -60,6 +60,10 @@ def _load() -> ctypes.CDLL:
         "oal_prefill": (c_int, [c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_void, c_void,
                                 c_void, c_void, c_int, c_void, c_void, c_int, c_void, c_size,
                                 c_void]),
+        "oal_prefill_noalloc_scratch_bytes": (c_size, []),
+        "oal_prefill_noalloc": (c_int, [c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_void,
+                                        c_void, c_void, c_void, c_int, c_void, c_void, c_int,
+                                        c_void]),
         "oal_prefill_dim_workspace_bytes": (c_size, [c_int, c_int, c_int, c_int, c_int, c_int,
                                                      c_int, c_int]),
         "oal_prefill_dim": (c_int, [c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_void,
@@ -102,6 +106,7 @@ _lib = _load()
 EXPORTED = ("oal_coeffs_bytes", "oal_expand_coeffs", "oal_dim_coeffs", "oal_state_alloc",
             "oal_state_reset", "oal_state_free", "oal_state_copy", "oal_state_bytes",
             "oal_state_tokens", "oal_state_export", "oal_prefill_workspace_bytes", "oal_prefill",
+            "oal_prefill_noalloc_scratch_bytes", "oal_prefill_noalloc",
             "oal_prefill_dim_workspace_bytes", "oal_prefill_dim",
             "oal_prefill_backward_workspace_bytes", "oal_prefill_backward", "oal_coeffs_backward",
             "oal_calib_workspace_bytes", "oal_calib_grad", "oal_adam_step", "oal_output_mse",
@@ -363,6 +368,26 @@ def oal_prefill(q: torch.Tensor | None, k: torch.Tensor, v: torch.Tensor, coeffs
                             chunk, state.handle if state is not None else None, _ptr(y), out_dt,
                             _ptr(workspace) if workspace is not None else None,
                             workspace.numel() if workspace is not None else 0, _stream(k)))
+    return y
+
+
+def oal_prefill_noalloc_scratch_bytes() -> int:
+    return int(_lib.oal_prefill_noalloc_scratch_bytes())
+
+
+def oal_prefill_noalloc(q: torch.Tensor | None, k: torch.Tensor, v: torch.Tensor,
+                        coeffs: torch.Tensor | None, chunk: int = 0, state: OalState | None = None,
+                        y: torch.Tensor | None = None, want_output: bool = True) -> torch.Tensor | None:
+    """oal_prefill without a workspace argument: the library's static scratch array
+    serves instead, and the call allocates nothing.  y must be given when outputs
+    are wanted (the caller owns every buffer)."""
+    if want_output and y is None:
+        raise ValueError("oal_prefill_noalloc allocates nothing: pass y")
+    B, Hkv, N, Hq, y = _prefill_args(q, k, v, coeffs, state, y, want_output)
+    out_dt = _dtype_code(y) if y is not None else OAL_F32
+    _check(_lib.oal_prefill_noalloc(B, Hq, Hkv, N, D_H, D_V, _dtype_code(k), _ptr(q), _ptr(k), _ptr(v),
+                                    _ptr(coeffs), chunk, state.handle if state is not None else None,
+                                    _ptr(y), out_dt, _stream(k)))
     return y
 
 

@@ -207,3 +207,17 @@ def test_grouping_entries_checks():
     assert call(a8=1.5) == 1          # gamma
     assert call(a9=0) == 1            # g_min
     assert call(a12=None) == 1        # n_groups
+
+
+def test_noalloc_prefill_rejects_oversized_calls_on_the_host():
+    """oal_prefill_noalloc checks its scratch limit before any HIP call (so this
+    runs without a GPU): a workspace beyond the static array is refused."""
+    lib, oal = _lib()
+    cap = lib.oal_prefill_noalloc_scratch_bytes()
+    assert cap == 128 << 20
+    need = lib.oal_prefill_workspace_bytes(1, 14, 2, 32768, 64, 64, 128, oal.OAL_BF16, 1)
+    assert need > cap
+    st = lib.oal_prefill_noalloc(1, 14, 2, 32768, 64, 64, oal.OAL_BF16, P, P, P, P, 128, None, P,
+                                 oal.OAL_BF16, None)
+    assert st == oal.OAL_ERR_UNSUPPORTED
+    assert b"scratch" in lib.oal_last_error()
