@@ -568,14 +568,16 @@ def fidelity_report(oal, w, chunk, device):
 # counters scaled against a plain copy of known size (profiles/*_traffic.txt).
 # The figure is used only while the kernel's sources are unchanged since the
 # counters were taken (sha256 over the listed sources).
+_READOUT_SRCS = ["positive_quadratic_causal_amd/csrc/oal_prefill_mfma.hip",
+                 "positive_quadratic_causal_amd/csrc/oal_tile.h",
+                 "positive_quadratic_causal_amd/csrc/oal_common.h"]
+# (kernel, chunk) -> (traffic summary, the sources whose hash it records)
 TRAFFIC_FILES = {
-    "k_readout_mfma": ("profiles/k_readout_mfma_qwen14x2_n32768_c128_traffic.txt",
-                       ["positive_quadratic_causal_amd/csrc/oal_prefill_mfma.hip",
-                        "positive_quadratic_causal_amd/csrc/oal_tile.h",
-                        "positive_quadratic_causal_amd/csrc/oal_common.h"]),
-    "k_decode": ("profiles/k_decode_llama32x8_b64_traffic.txt",
-                 ["positive_quadratic_causal_amd/csrc/oal_decode.hip",
-                  "positive_quadratic_causal_amd/csrc/oal_common.h"]),
+    ("k_readout_mfma", 128): ("profiles/k_readout_mfma_qwen14x2_n32768_c128_traffic.txt", _READOUT_SRCS),
+    ("k_readout_mfma", 256): ("profiles/k_readout_mfma_qwen14x2_n32768_c256_traffic.txt", _READOUT_SRCS),
+    ("k_decode", None): ("profiles/k_decode_llama32x8_b64_traffic.txt",
+                         ["positive_quadratic_causal_amd/csrc/oal_decode.hip",
+                          "positive_quadratic_causal_amd/csrc/oal_common.h"]),
 }
 
 
@@ -588,12 +590,12 @@ def sources_sha256(paths):
     return h.hexdigest()
 
 
-def measured_traffic(kernel):
+def measured_traffic(kernel, chunk=None):
     """Bytes per launch from the kernel's traffic summary, or None when there is
     none or the kernel's sources changed since it was taken."""
-    if kernel not in TRAFFIC_FILES:
+    if (kernel, chunk) not in TRAFFIC_FILES:
         return None
-    path, srcs = TRAFFIC_FILES[kernel]
+    path, srcs = TRAFFIC_FILES[(kernel, chunk)]
     try:
         fields = {}
         with open(os.path.join(ROOT, path)) as f:
@@ -645,7 +647,7 @@ def roofline_prefill(kt, kt_timed, w, chunk):
     else:
         achieved = work / avg_s / 1e9
     return {"kernel": name, "bound": bound, "achieved": round(achieved, 3), "peak": peak,
-            "unit": unit, "frac": round(achieved / peak, 5), "traffic": measured_traffic(name),
+            "unit": unit, "frac": round(achieved / peak, 5), "traffic": measured_traffic(name, chunk),
             "work_per_launch": work, "avg_launch_ms": round(prefill_kernels[name]["avg_ms"], 5)}
 
 
