@@ -493,57 +493,125 @@ k_readout_mfma(int n_q_heads, int n_kv_heads, int seq_len, int n_chunks, int n_h
         qc[1][j] = one ? (__bf16)1.0f : *qrow1.elem(d);
       }
     }
-    // One 32-key tile.  DO0: token tile 0 is not entirely masked; MASKn: token
-    // tile n is the diagonal one (key row acc_row(i, h) visible iff <= col).
-    auto key_tile = [&](int kt, auto do0_t, auto mask0_t, auto mask1_t) {
-      constexpr bool DO0 = decltype(do0_t)::value;
+    // One unit of the intra-chunk work: two products of a 32-key tile with a
+    // 32-token tile, in slots x = 0, 1, that share their operand reads and run as
+    // independent chains (so that their latencies overlap).  MODE 1: key tile kt
+    // against token tiles 0 and 1; MODE 0: slot 1 only, kt against token tile 1;
+    // MODE 2 (compact path only): key tiles kt and kt + 1 against token tile 1.
+    // MASKx: slot x's key tile is the diagonal one of its token tile (key row
+    // acc_row(i, h) visible iff <= col).
+    auto unit = [&](int kt, auto mode_t, auto mask0_t, auto mask1_t) __attribute__((always_inline)) {
+      constexpr int MODE = decltype(mode_t)::value;
       constexpr bool MASK[2] = {decltype(mask0_t)::value, decltype(mask1_t)::value};
+      constexpr bool USE[2] = {MODE != 0, true};
+      constexpr int NT[2] = {MODE == 1 ? 0 : 1, 1};   // token tile of slot x
+      constexpr int NK = MODE == 2 ? 2 : 1;            // distinct key tiles
+      constexpr int KX[2] = {0, MODE == 2 ? 1 : 0};    // key tile (of the NK) of slot x
       f32x16 kap[2] = {splat16(epsF), splat16(epsF)};
-      const SwRow krow(k_arr(kt >> 1), (32 * kt + col) & 63);
-      bf16x8 kr[4];
+      const SwRow krow[2] = {SwRow(k_arr(kt >> 1), (32 * kt + col) & 63),
+                             SwRow(k_arr((kt + NK - 1) >> 1), (32 * (kt + NK - 1) + col) & 63)};
+      bf16x8 kr[NK][4];
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) kr[ks] = *reinterpret_cast<const bf16x8*>(krow.chunk(2 * ks + half));
+      for (int j = 0; j < NK; ++j)
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) kr[j][ks] = *reinterpret_cast<const bf16x8*>(krow[j].chunk(2 * ks + half));
       if (compact) {
         f32x16 S[2];
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-          if (nt == 0 && !DO0) continue;
-          S[nt] = splat16(0.f);
+        for (int x = 0; x < 2; ++x) {
+          if (!USE[x]) continue;
+          S[x] = splat16(0.f);
 #pragma unroll
-          for (int ks = 0; ks < 4; ++ks) S[nt] = mfma32(kr[ks], qfrag(nt, ks), S[nt]);
+          for (int ks = 0; ks < 4; ++ks) S[x] = mfma32(kr[KX[x]][ks], qfrag(NT[x], ks), S[x]);
         }
-        float kc[8];
+        float kc[NK][8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) kc[j] = (half && j >= 6) ? 1.0f : bf(*krow.elem(cidx[j]));
-        for (int p = 0; p <= G; ++p) {
+        for (int j = 0; j < NK; ++j)
+#pragma unroll
+          for (int i = 0; i < 8; ++i) kc[j][i] = (half && i >= 6) ? 1.0f : bf(*krow[j].elem(cidx[i]));
+        // A operand of t_p for key tile j: the compact key entries times (ell_p - c_p) 2^(E/2)
+        auto akc_of = [&](int j, int p) __attribute__((always_inline)) {
           const float* ec = ht + htab::ELLC + p * 16 + 8 * half;
           const float4 e0 = *reinterpret_cast<const float4*>(ec);
           const float4 e1 = *reinterpret_cast<const float4*>(ec + 4);
-          const float x[8] = {kc[0] * e0.x, kc[1] * e0.y, kc[2] * e0.z, kc[3] * e0.w,
-                              kc[4] * e1.x, kc[5] * e1.y, kc[6] * e1.z, kc[7] * e1.w};
-          const bf16x8 akc = pack8(x);
-          const float cp = ht[htab::CP + p];
+          const float x[8] = {kc[j][0] * e0.x, kc[j][1] * e0.y, kc[j][2] * e0.z, kc[j][3] * e0.w,
+                              kc[j][4] * e1.x, kc[j][5] * e1.y, kc[j][6] * e1.z, kc[j][7] * e1.w};
+          return pack8(x);
+        };
+        // The terms go two at a time, so that up to four independent products are
+        // in flight before their squares are summed: p = 0, 1 (seeded with c_p S),
+        // then pairs of p >= 2 (c_p = 0 there: L is lower triangular), then a
+        // single last term when G + 1 is odd.
+        {
+          bf16x8 a[NK][2];
 #pragma unroll
-          for (int nt = 0; nt < 2; ++nt) {
-            if (nt == 0 && !DO0) continue;
-            f32x16 seed;   // L_{0,p} comes from the constant slots
-            if (p <= 1) {
+          for (int j = 0; j < NK; ++j) {
+            a[j][0] = akc_of(j, 0);
+            a[j][1] = akc_of(j, 1);
+          }
+          const float c0 = ht[htab::CP + 0], c1 = ht[htab::CP + 1];
+          f32x16 t[2][2];
 #pragma unroll
-              for (int i = 0; i < 16; ++i) seed[i] = cp * S[nt][i];
-            } else {
-              seed = splat16(0.f);   // c_p = 0 for p >= 2 (L is lower triangular)
+          for (int x = 0; x < 2; ++x) {
+            if (!USE[x]) continue;
+            f32x16 s0, s1;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              s0[i] = c0 * S[x][i];
+              s1[i] = c1 * S[x][i];
             }
-            const f32x16 t = mfma32(akc, qc[nt], seed);
+            t[x][0] = mfma32(a[KX[x]][0], qc[NT[x]], s0);
+            t[x][1] = mfma32(a[KX[x]][1], qc[NT[x]], s1);
+          }
 #pragma unroll
-            for (int i = 0; i < 16; ++i) kap[nt][i] = fmaf(t[i], t[i], kap[nt][i]);
+          for (int x = 0; x < 2; ++x) {
+            if (!USE[x]) continue;
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+              kap[x][i] = fmaf(t[x][0][i], t[x][0][i], fmaf(t[x][1][i], t[x][1][i], kap[x][i]));
           }
         }
-      } else {
+        int p = 2;
+        for (; p + 1 <= G; p += 2) {
+          bf16x8 a[NK][2];
+#pragma unroll
+          for (int j = 0; j < NK; ++j) {
+            a[j][0] = akc_of(j, p);
+            a[j][1] = akc_of(j, p + 1);
+          }
+          f32x16 t[2][2];
+#pragma unroll
+          for (int x = 0; x < 2; ++x) {
+            if (!USE[x]) continue;
+            t[x][0] = mfma32(a[KX[x]][0], qc[NT[x]], splat16(0.f));
+            t[x][1] = mfma32(a[KX[x]][1], qc[NT[x]], splat16(0.f));
+          }
+#pragma unroll
+          for (int x = 0; x < 2; ++x) {
+            if (!USE[x]) continue;
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+              kap[x][i] = fmaf(t[x][0][i], t[x][0][i], fmaf(t[x][1][i], t[x][1][i], kap[x][i]));
+          }
+        }
+        if (p <= G) {
+          bf16x8 a[NK];
+#pragma unroll
+          for (int j = 0; j < NK; ++j) a[j] = akc_of(j, p);
+#pragma unroll
+          for (int x = 0; x < 2; ++x) {
+            if (!USE[x]) continue;
+            const f32x16 t = mfma32(a[KX[x]], qc[NT[x]], splat16(0.f));
+#pragma unroll
+            for (int i = 0; i < 16; ++i) kap[x][i] = fmaf(t[i], t[i], kap[x][i]);
+          }
+        }
+      } else if constexpr (MODE != 2) {
         float kf[4][8];
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-          for (int j = 0; j < 8; ++j) kf[ks][j] = bf(kr[ks][j]);
+          for (int j = 0; j < 8; ++j) kf[ks][j] = bf(kr[0][ks][j]);
         for (int p = 0; p <= G; ++p) {
           const float* ell = ht + htab::ELL + p * DH + 8 * half;
           bf16x8 ak[4];
@@ -557,68 +625,85 @@ k_readout_mfma(int n_q_heads, int n_kv_heads, int seq_len, int n_chunks, int n_h
           }
           const float l0 = ht[htab::L0 + p];
 #pragma unroll
-          for (int nt = 0; nt < 2; ++nt) {
-            if (nt == 0 && !DO0) continue;
+          for (int x = 0; x < 2; ++x) {
+            if (!USE[x]) continue;
             f32x16 sacc = splat16(l0);
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) sacc = mfma32(ak[ks], qfrag(nt, ks), sacc);
+            for (int ks = 0; ks < 4; ++ks) sacc = mfma32(ak[ks], qfrag(NT[x], ks), sacc);
 #pragma unroll
-            for (int i = 0; i < 16; ++i) kap[nt][i] = fmaf(sacc[i], sacc[i], kap[nt][i]);
+            for (int i = 0; i < 16; ++i) kap[x][i] = fmaf(sacc[i], sacc[i], kap[x][i]);
           }
         }
       }
       // causal mask, denominators, and P [V; 1]
-      const uint8_t* va = v_arr(kt >> 1);
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        if (nt == 0 && !DO0) continue;
-        if (MASK[nt]) {
+      for (int x = 0; x < 2; ++x) {
+        if (!USE[x]) continue;
+        const int ktx = kt + KX[x];
+        const uint8_t* va = v_arr(ktx >> 1);
+        if (MASK[x]) {
 #pragma unroll
           for (int i = 0; i < 16; ++i)
-            if (acc_row(i, half) > col) kap[nt][i] = 0.f;
+            if (acc_row(i, half) > col) kap[x][i] = 0.f;
         }
         float ds = 0.f;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) ds += kap[nt][i];
-        den[nt] += ds;
+        for (int i = 0; i < 16; ++i) ds += kap[x][i];
+        den[NT[x]] += ds;
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
-          float x[8];
+          float xv[8];
 #pragma unroll
-          for (int j = 0; j < 8; ++j) x[j] = kap[nt][8 * s2 + j];
-          const bf16x8 pb = pack8(x);
-          const int kc8 = (4 * (kt & 1) + 2 * s2 + half);   // 16-byte chunk of the v^T row
+          for (int j = 0; j < 8; ++j) xv[j] = kap[x][8 * s2 + j];
+          const bf16x8 pb = pack8(xv);
+          const int kc8 = (4 * (ktx & 1) + 2 * s2 + half);   // 16-byte chunk of the v^T row
 #pragma unroll
           for (int mt = 0; mt < 2; ++mt) {
             const SwRow vr(va, 32 * mt + col);
             const bf16x8 av = *reinterpret_cast<const bf16x8*>(vr.chunk(kc8));
-            acc[mt][nt] = mfma32(av, pb, acc[mt][nt]);
+            acc[mt][NT[x]] = mfma32(av, pb, acc[mt][NT[x]]);
           }
         }
+      }
+    };
+    using M0 = std::integral_constant<int, 0>;
+    using M1 = std::integral_constant<int, 1>;
+    using M2 = std::integral_constant<int, 2>;
+    using F_ = bool_t<false>;
+    // key tiles lo .. hi - 1 (staged indices) against token tile 1 alone, the last
+    // one masked when ML; two at a time on the compact path
+    auto singles = [&](int lo, int hi, auto ml_t) __attribute__((always_inline)) {
+      using ML = decltype(ml_t);
+      if (lo >= hi) return;
+      if (compact) {
+        int kt = lo;
+        for (; kt + 2 < hi; kt += 2) unit(kt, M2{}, F_{}, F_{});
+        if (kt + 2 == hi)
+          unit(kt, M2{}, F_{}, ML{});
+        else
+          unit(kt, M0{}, F_{}, ML{});
+      } else {
+        for (int kt = lo; kt + 1 < hi; ++kt) unit(kt, M0{}, F_{}, F_{});
+        unit(hi - 1, M0{}, F_{}, ML{});
       }
     };
     // key tiles 0 .. T1: both token tiles up to T0 (T0 the diagonal one of N-tile
     // 0), then N-tile 1 alone (T1 its diagonal one).  With two passes T0 < 4 <= T1:
     // the first pass holds key tiles 0..3, the second 4..7.
     if (head_ok) {
-      for (int kt = 0; kt < T0; ++kt) key_tile(kt, bool_t<true>{}, bool_t<false>{}, bool_t<false>{});
-      key_tile(T0, bool_t<true>{}, bool_t<true>{}, bool_t<false>{});
-      if (Cfg::NPASS == 1) {
-        for (int kt = T0 + 1; kt < T1; ++kt) key_tile(kt, bool_t<false>{}, bool_t<false>{}, bool_t<false>{});
-        key_tile(T1, bool_t<false>{}, bool_t<false>{}, bool_t<true>{});
-      } else {
-        for (int kt = T0 + 1; kt < 4; ++kt) key_tile(kt, bool_t<false>{}, bool_t<false>{}, bool_t<false>{});
-      }
+      for (int kt = 0; kt < T0; ++kt) unit(kt, M1{}, F_{}, F_{});
+      unit(T0, M1{}, bool_t<true>{}, F_{});
+      if (Cfg::NPASS == 1)
+        singles(T0 + 1, T1 + 1, bool_t<true>{});
+      else
+        singles(T0 + 1, 4, F_{});
     }
     if (Cfg::NPASS > 1) {
       load_kv(1);        // (issued here: in flight during the first pass they would spill)
       __syncthreads();   // every wave is done with the first pass's keys
       stage_kv(1);
       __syncthreads();
-      if (head_ok) {
-        for (int kt = 4; kt < T1; ++kt) key_tile(kt - 4, bool_t<false>{}, bool_t<false>{}, bool_t<false>{});
-        key_tile(T1 - 4, bool_t<false>{}, bool_t<false>{}, bool_t<true>{});
-      }
+      if (head_ok) singles(0, T1 - 4 + 1, bool_t<true>{});
     }
   }
 
