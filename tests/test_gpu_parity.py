@@ -73,9 +73,18 @@ def test_expand_coeffs(oal):
         Lh = rng.normal(0, 0.5, size=(7, 7)).astype(np.float32)   # junk outside the block too
         L[h] = Lh
     dev = "cuda"
-    coeffs = oal.oal_expand_coeffs(torch.from_numpy(n_groups).to(dev), torch.from_numpy(gmap).to(dev),
-                                   torch.from_numpy(L).to(dev), 1e-3)
+    # written into a buffer full of NaN: every word of every record must be set
+    coeffs = torch.full((Hq, oal.COEF_WORDS), float("nan"), dtype=torch.float32, device=dev)
+    oal.oal_expand_coeffs(torch.from_numpy(n_groups).to(dev), torch.from_numpy(gmap).to(dev),
+                          torch.from_numpy(L).to(dev), 1e-3, coeffs)
     cf = coeffs.cpu().numpy()
+    assert not np.isnan(cf).any(), "words of the record left unwritten"
+    fields = [(oal.COEF_A, 3), (oal.COEF_BP, 64), (oal.COEF_GMAP, 64), (oal.COEF_M, 49),
+              (oal.COEF_L, 49), (oal.COEF_ELL, 7 * 64), (oal.COEF_CM, 4096), (oal.COEF_CP, 2080),
+              (oal.COEF_MG, 7 * 64), (oal.COEF_GPACK, 8)]
+    pad = np.ones(oal.COEF_WORDS, dtype=bool)
+    for off, n in fields:
+        pad[off:off + n] = False
     pairs = O.packed_pairs(64)
     r_ = np.array([p[0] for p in pairs]); t_ = np.array([p[1] for p in pairs])
     for h in range(Hq):
@@ -100,6 +109,20 @@ def test_expand_coeffs(oal):
         assert np.all(ell[G + 1:] == 0)
         mg = rec[oal.COEF_MG:oal.COEF_MG + 7 * 64].reshape(7, 64)
         np.testing.assert_allclose(mg[: G + 1], M[:, gmap[h]] / 64.0, rtol=1e-6, atol=1e-8)
+        assert np.all(mg[G + 1:] == 0)
+        # the encodings of the inputs, bit for bit: g(r), its 4-bit packing, L (lower
+        # triangle of the G + 1 block), and M and L zero outside that block
+        assert np.array_equal(rec[oal.COEF_GMAP:oal.COEF_GMAP + 64].view(np.int32), gmap[h])
+        packed = rec[oal.COEF_GPACK:oal.COEF_GPACK + 8].view(np.uint32)
+        for r in range(64):
+            assert (int(packed[r // 8]) >> (4 * (r % 8))) & 15 == gmap[h][r]
+        Lrec = rec[oal.COEF_L:oal.COEF_L + 49].reshape(7, 7)
+        assert np.array_equal(Lrec[: G + 1, : G + 1], np.tril(L[h][: G + 1, : G + 1]))
+        Mrec = rec[oal.COEF_M:oal.COEF_M + 49].reshape(7, 7)
+        for X in (Lrec, Mrec):
+            assert np.all(X[G + 1:, :] == 0) and np.all(X[:, G + 1:] == 0)
+        assert rec[oal.COEF_EPS] == np.float32(1e-3)
+        assert np.all(rec[pad] == 0), "padding words not zero"
 
 
 @pytest.mark.parametrize("chunk", [64, 128, 256])
