@@ -57,6 +57,25 @@ def log(msg: str) -> None:
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+WARM_SECONDS = 0.3
+
+
+def warm_up(step, n, seconds=WARM_SECONDS):
+    """Untimed warmup: n calls of step, then more until `seconds` of them have run.
+    From idle the GPU needs tens of milliseconds of work (about 60 steps of the
+    long prefill) to reach its steady clock; a fixed small step count alone would
+    leave part of that ramp inside the timed steps."""
+    import torch
+    for _ in range(n):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(4):
+            step()
+        torch.cuda.synchronize()
+
+
 def prefill_flops_per_token(n_q: int, n_kv: int, chunk: int) -> dict:
     """Algorithmic (useful, unpadded) flops per token: state build 2*D*W per KV
     head, inter-chunk readout 2*D*W per query head, intra-chunk causal triangle
@@ -129,9 +148,7 @@ def bench_prefill(oal, w, chunk, steps, warmup, device):
         oal.oal_prefill(x["q"], x["k"], x["v"], coeffs, chunk=chunk, state=state, y=y,
                         workspace=ws)
 
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
+    warm_up(step, warmup)
     # the timed steps, with HIP events around the dominant kernel's launches only
     dominant = "k_readout_mfma" if x["q"].dtype == torch.bfloat16 else "k_readout_vec"
     oal.oal_profile_reset()
@@ -171,9 +188,7 @@ def bench_prefill(oal, w, chunk, steps, warmup, device):
     graph.replay()
     torch.cuda.synchronize()
     graph_ok = bool(torch.equal(y, y_eager))
-    for _ in range(warmup):
-        graph.replay()
-    torch.cuda.synchronize()
+    warm_up(graph.replay, warmup)
     t0 = time.perf_counter()
     for _ in range(steps):
         graph.replay()
@@ -204,9 +219,7 @@ def bench_softmax(oal, w, steps, warmup, device):
     def step():
         oal.oal_softmax_attention(x["q"], x["k"], x["v"], y)
 
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
+    warm_up(step, warmup)
     t0 = time.perf_counter()
     for _ in range(steps):
         step()
@@ -269,9 +282,7 @@ def bench_prefill_dim(oal, w, chunk, steps, warmup, device):
         oal.oal_prefill_dim(x["q"], x["k"], x["v"], coeffs, chunk=chunk, state=state, y=y,
                             workspace=ws)
 
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
+    warm_up(step, warmup)
     t0 = time.perf_counter()
     for _ in range(steps):
         step()
@@ -351,9 +362,7 @@ def bench_backward(oal, w, chunk, steps, warmup, device):
         oal.oal_prefill_backward(x["q"], x["k"], x["v"], coeffs, dy, chunk=chunk, out=out,
                                  workspace=ws)
 
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
+    warm_up(step, warmup)
     t0 = time.perf_counter()
     for _ in range(steps):
         step()
@@ -679,8 +688,7 @@ def bench_decode(oal, w, reps, n_steps, device):
             oal.oal_decode_step(steps_q[s], steps_k[s], steps_v[s], coeffs, state, y)
 
     oal.oal_state_copy(state, base)
-    rep_once()      # warmup
-    torch.cuda.synchronize()
+    warm_up(rep_once, 1)
     total = 0.0
     for _ in range(reps):
         oal.oal_state_copy(state, base)
@@ -912,7 +920,7 @@ def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--chunk", type=int, default=128)
     ap.add_argument("--decode-steps", type=int, default=256)
     ap.add_argument("--decode-reps", type=int, default=3)
@@ -999,14 +1007,15 @@ def main() -> int:
         "frac_bf16_peak": round(fl["total"] * tokens / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 5),
     }
     if not args.no_sweep and args.only is None:
+        # every chunk size timed alike (the headline chunk again too, so that all
+        # three come from the same conditions), in two interleaved rounds, the
+        # faster of the two kept per size
         sweep = {}
-        for c in (64, 128, 256):
-            if c == args.chunk:
-                sweep[str(c)] = round(ms, 5)
-                continue
-            log(f"prefill chunk sweep: chunk {c}")
-            msc, _, _, _ = bench_prefill(oal, w3, c, max(3, args.steps // 4), 2, device)
-            sweep[str(c)] = round(msc, 5)
+        for rnd in range(2):
+            for c in (64, 128, 256):
+                log(f"prefill chunk sweep: chunk {c}, round {rnd + 1}")
+                msc, _, _, _ = bench_prefill(oal, w3, c, args.steps, args.warmup, device)
+                sweep[str(c)] = round(min(msc, sweep.get(str(c), msc)), 5)
         result["chunk_sweep_ms"] = sweep
         w1 = synth.WORKLOADS[1]
         log("linear-time check: N = 2048")
