@@ -25,6 +25,7 @@ and resident in HBM before the timed region starts.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import json
 import os
 import sys
@@ -60,20 +61,25 @@ def log(msg: str) -> None:
 WARM_SECONDS = 0.3
 
 
-def warm_up(step, n, seconds=WARM_SECONDS):
+def warm_up(step, n, seconds=None):
     """Untimed warmup: n calls of step, then more until `seconds` of them have run.
     From idle the GPU needs tens of milliseconds of work (about 60 steps of the
     long prefill) to reach its steady clock; a fixed small step count alone would
-    leave part of that ramp inside the timed steps."""
+    leave part of that ramp inside the timed steps.  Returns the steps run."""
     import torch
+    if seconds is None:
+        seconds = WARM_SECONDS
     for _ in range(n):
         step()
     torch.cuda.synchronize()
+    done = n
     t0 = time.perf_counter()
     while time.perf_counter() - t0 < seconds:
         for _ in range(4):
             step()
         torch.cuda.synchronize()
+        done += 4
+    return done
 
 
 def prefill_flops_per_token(n_q: int, n_kv: int, chunk: int) -> dict:
@@ -148,7 +154,8 @@ def bench_prefill(oal, w, chunk, steps, warmup, device):
         oal.oal_prefill(x["q"], x["k"], x["v"], coeffs, chunk=chunk, state=state, y=y,
                         workspace=ws)
 
-    warm_up(step, warmup)
+    n_warm = warm_up(step, warmup)
+    log(f"prefill warmup: {n_warm} steps ({w.name}, chunk {chunk})")
     # the timed steps, with HIP events around the dominant kernel's launches only
     dominant = "k_readout_mfma" if x["q"].dtype == torch.bfloat16 else "k_readout_vec"
     oal.oal_profile_reset()
@@ -917,10 +924,13 @@ def measured_peaks(device):
 
 
 def main() -> int:
+    global WARM_SECONDS
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--warm-seconds", type=float, default=WARM_SECONDS,
+                    help="untimed warmup time floor per timed leg (seconds)")
     ap.add_argument("--chunk", type=int, default=128)
     ap.add_argument("--decode-steps", type=int, default=256)
     ap.add_argument("--decode-reps", type=int, default=3)
@@ -935,6 +945,7 @@ def main() -> int:
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="after the legs, copy MIB MiB 5 times (reference for HBM counters)")
     args = ap.parse_args()
+    WARM_SECONDS = args.warm_seconds
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU only: the OAL path has no multi-GPU leg (each "
@@ -1022,6 +1033,20 @@ def main() -> int:
         ms1, _, _, _ = bench_prefill(oal, w1, args.chunk, args.steps, args.warmup, device)
         result["linear_time_check"] = {"ms_n2048": round(ms1, 5), "ms_n32768": round(ms, 5),
                                        "ratio": round(ms / ms1, 3), "ideal_ratio": 16.0}
+        # the long prefill's first N tokens, N doubling up to the full length:
+        # ms per step and the ratio to the half length (2 for linear time)
+        curve = {}
+        for n in (2048, 4096, 8192, 16384):
+            log(f"length scaling: first {n} tokens")
+            wn = dataclasses.replace(w3, seq_len=n)
+            curve[n] = bench_prefill(oal, wn, args.chunk, args.steps, args.warmup, device)[0]
+        curve[w3.seq_len] = ms
+        ns = sorted(curve)
+        result["length_scaling"] = {
+            "workload": f"{w3.name}, first N tokens", "chunk": args.chunk,
+            "ms_per_step": {str(n): round(curve[n], 5) for n in ns},
+            "ratio_to_half_length": {str(n): round(curve[n] / curve[n // 2], 3) for n in ns[1:]},
+            "tokens_per_s": {str(n): round(n * w3.batch / (curve[n] * 1e-3), 1) for n in ns}}
         w2 = synth.WORKLOADS[2]
         log(f"prefill: {w2.name}, chunk {args.chunk}")
         ms2, kt2, _, _ = bench_prefill(oal, w2, args.chunk, args.steps, args.warmup, device)
