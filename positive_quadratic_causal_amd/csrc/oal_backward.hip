@@ -35,12 +35,20 @@
 namespace oal {
 
 namespace {
-__constant__ PairTable c_bwd_pairs = PairTable();
 constexpr int WP = 68;                 // rows of H, R, u and g padded to 16 bytes
 constexpr int TB = 64;                 // tokens per staged tile
 constexpr int FB = 64;                 // feature rows per build block
 constexpr int NFB = DS / FB;           // 34
 constexpr int WPT = (W + 3) / 4;       // 17 columns per thread in the build
+
+// fp32 matrix-core product v_mfma_f32_32x32x2_f32: A 32 x 2 (lane l holds
+// A[l % 32][l / 32]), B 2 x 32 (lane l holds B[l / 32][l % 32]), D 32 x 32 (lane l,
+// register i holds D[8 (i / 4) + 4 (l / 32) + i % 4][l % 32]).
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float fx16;
+__device__ __forceinline__ fx16 mfma_f32(float a, float b, fx16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ int mrow(int i, int h) { return 8 * (i >> 2) + 4 * h + (i & 3); }
 
 // feature f of the canonical order: kind 0 constant, 1 linear x_r, 2 pair x_r x_t,
 // 3 padding
@@ -53,13 +61,22 @@ __device__ __forceinline__ int feat_decode(int f, int& r, int& t) {
     return 1;
   }
   if (f < DCAN) {
-    const uint16_t rt = c_bwd_pairs.rt[f - 1 - DH];
-    r = rt >> 8;
-    t = rt & 0xff;
+    // pair p = pair_index(r, t): row r starts at S(r) = r (2 DH + 1 - r) / 2, so r is
+    // the floor of the smaller root of S(r) = p, corrected by one either way for the
+    // rounding of the square root (exact for all 2080 pairs; no table read)
+    const int p = f - 1 - DH;
+    int rr = (int)((129.f - __builtin_sqrtf(16641.f - 8.f * (float)p)) * 0.5f);
+    if (rr * (129 - rr) / 2 > p)
+      --rr;
+    else if ((rr + 1) * (128 - rr) / 2 <= p)
+      ++rr;
+    r = rr;
+    t = p - rr * (129 - rr) / 2 + rr;
     return 2;
   }
   return 3;
 }
+static_assert(DH == 64, "the pair decode's constants are for d_h = 64");
 
 __device__ __forceinline__ float coef_of(const float* rec, int f) {
   if (f == 0) return rec[OAL_COEF_A];
@@ -268,16 +285,20 @@ size_t backward_workspace(int batch, int n_q_heads, int n_kv_heads, int seq_len,
 // row, the rows added in a fixed order at the end.
 template <typename T, int SP>
 __global__ void __launch_bounds__(256)
-k_bwd_query(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunks,
+k_bwd_query(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunks, int n_units,
             const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
             const void* __restrict__ coeffs, const float* __restrict__ dy,
             const float* __restrict__ hc, float* __restrict__ gbuf, float* __restrict__ alpha,
             float* __restrict__ dq) {
-  const int c = blockIdx.x;
-  const int hq = blockIdx.y;
-  const int b = blockIdx.z;
+  // the query heads of one (unit, chunk) in consecutive slots of one XCD
+  // (workgroup id % 8), so that they read that chunk's prefix state through one L2
   const int rep = n_q_heads / n_kv_heads;
-  const int unit = b * n_kv_heads + hq / rep;
+  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  const int uc = (slot / rep) * 8 + xcd;
+  if (uc >= n_units * n_chunks) return;
+  const int unit = uc / n_chunks, c = uc % n_chunks;
+  const int b = unit / n_kv_heads;
+  const int hq = (unit % n_kv_heads) * rep + slot % rep;
   const int tid = threadIdx.x;
   const int nthr = blockDim.x;                // SP * chunk
   const int qx = tid / SP;                    // query of the chunk
@@ -299,6 +320,7 @@ k_bwd_query(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunks,
   const float* rec = coef_rec(coeffs, hq);
   const float a = rec[OAL_COEF_A];
   __shared__ __attribute__((aligned(16))) GroupTab gt;
+  __shared__ int s_fdec[32];   // kind | r << 8 | t << 16 of the staged block's features
   const bool grouped = reinterpret_cast<const int32_t*>(rec)[OAL_COEF_NG] >= 1;
   if (grouped) build_group_tab(gt, rec, tid);
   const size_t qrow0 = ((size_t)b * n_q_heads + hq) * seq_len + t0;
@@ -306,7 +328,22 @@ k_bwd_query(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunks,
     const int ii = i / DH, d = i % DH;
     s_q[ii * (DH + 1) + d] = ii < clen ? Elem<T>::load(q, (qrow0 + ii) * DH + d) : 0.f;
   }
+  for (int i = tid; i < chunk; i += nthr) s_q[i * (DH + 1) + DH] = 1.f;   // psi's constant slot
   for (int i = tid; i < SP * chunk * (DH + 1); i += nthr) s_dq[i] = 0.f;
+  // feature descriptors for the state part of step 1, in the staged keys' rows
+  // (free until the pairs of step 1): psi_f(q) = q~[ia] q~[ib] with q~ = (q, 1),
+  // i.e. (64, 64) for the constant, (r, 64) for x_r, (r, t) for a pair; and c_f
+  // (zero on the padding rows DCAN .. DS - 1)
+  uint16_t* s_fd = reinterpret_cast<uint16_t*>(s_k);
+  float* s_fc = s_k + DS / 2;
+  static_assert(DS / 2 + DS <= TB * (DH + 1), "descriptors fit the staged keys' rows");
+  for (int f = tid; f < DS; f += nthr) {
+    int r, t;
+    const int kind = feat_decode(f, r, t);
+    const int ia = kind == 0 ? DH : r, ib = kind == 2 ? t : DH;
+    s_fd[f] = (uint16_t)(ia | (ib << 8));
+    s_fc[f] = f < DCAN ? coef_of(rec, f) : 0.f;
+  }
   for (int i = tid; i < DH; i += nthr) s_b[i] = rec[OAL_COEF_BP + i];
   for (int i = tid; i < DH * DH; i += nthr) s_S[i] = rec[OAL_COEF_CM + i];
   for (int i = tid; i < 32 * (WP - W); i += nthr) s_H[(i / (WP - W)) * WP + W + i % (WP - W)] = 0.f;
@@ -336,7 +373,12 @@ k_bwd_query(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunks,
       const int i = tid + e * 256;
       if (i < 32 * W) s_H[(i % 32) * WP + i / 32] = pre[e];
     }
-    if (tid < 32) s_cf[tid] = pcf;
+    if (tid < 32) {
+      s_cf[tid] = pcf;
+      int r, t;
+      const int kind = feat_decode(f0 + tid, r, t);
+      s_fdec[tid] = kind | (r << 8) | (t << 16);
+    }
     if (f0 + 32 < DCAN) fetch_block(f0 + 32);
   };
   auto stage_keys = [&](int j0, int nj) {
@@ -353,25 +395,118 @@ k_bwd_query(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunks,
     for (int jj = tid; jj < TB; jj += nthr) s_u[jj * WP + DV] = jj < nj ? 1.f : 0.f;
   };
 
-  // ---- 1. recompute this half's share of u~_i: state part, then the chunk's pairs
+  // ---- 1. recompute u~_i.  State part on the fp32 matrix cores:
+  //   U[tok][w] = sum_f c_f psi_f(q_tok) H_{<c}[f][w],  w < 64,
+  // over staged 64-feature blocks, two features per product; token tiles of 32
+  // rows (A: lane l forms c_f psi_f(q) of token 32 TT + l % 32 and feature
+  // f0 + 2 j + l / 32 in place) against channel tiles of 32 (B: the staged block).
+  // Chunk 64 (SP 4): wave = (token tile wave % 2, channel tile wave / 2); chunk 128
+  // (SP 2): wave = token tile, both channel tiles.  The all-ones channel w = 64 is a
+  // multiply-add per product (kept from the waves of channel tile 0).  U and that channel go
+  // to part 0's dq rows (unused until step 3) and are added in step 2.
+  constexpr int NCT = SP == 4 ? 1 : 2;            // channel tiles per wave
+  static_assert(SP * 64 == 256 || SP * 128 == 256, "chunk 64 or 128");
+  {
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+    const int TT = SP == 4 ? (wave & 1) : wave;
+    const int CT0 = SP == 4 ? (wave >> 1) : 0;
+    const int kpar = lane >> 5;
+    fx16 U[2][NCT];   // two chains (even and odd products), added at the end
+#pragma unroll
+    for (int x = 0; x < 2; ++x)
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) U[x][ct][i] = 0.f;
+    float dpart = 0.f;
+    // 64-feature blocks of H_{<c} staged in the value rows s_u (64 x WP, free until
+    // the pairs), each fetched into registers one block ahead
+    constexpr int FB1 = 64;
+    constexpr int PB1 = (FB1 * W + 255) / 256;
+    float pre1[PB1];
+    auto fetch1 = [&](int f0) {
+#pragma unroll
+      for (int e = 0; e < PB1; ++e) {
+        const int i = tid + e * 256;
+        if (i < FB1 * W) pre1[e] = Hc[(size_t)(i / FB1) * DS + f0 + i % FB1];   // f0 + 63 < DS
+      }
+    };
+    // the block's A operand c_f psi_f(q_tok), formed by all threads into part 1's dq
+    // rows (free until step 2) as [feature][token], the token index XOR 32 on odd
+    // features so that the two lane halves of a product read distinct banks
+    float* s_A = s_dq + chunk * (DH + 1);
+    static_assert(FB1 <= DH + 1, "the A tile fits one part's dq rows");
+    constexpr int NA = FB1 * 256 / SP / 256;   // A values per thread: FB1 x chunk / 256
+    fetch1(0);
+    for (int f0 = 0; f0 < DCAN; f0 += FB1) {
+      __syncthreads();
+#pragma unroll
+      for (int e = 0; e < PB1; ++e) {
+        const int i = tid + e * 256;
+        if (i < FB1 * W) s_u[(i % FB1) * WP + i / FB1] = pre1[e];
+      }
+      if (f0 + FB1 < DCAN) fetch1(f0 + FB1);
+#pragma unroll
+      for (int e = 0; e < NA; ++e) {
+        const int v = tid + 256 * e, ff = v / chunk, tok = v % chunk;
+        const int d = s_fd[f0 + ff];
+        const float* qt = s_q + tok * (DH + 1);
+        s_A[ff * chunk + (tok ^ ((ff & 1) << 5))] = s_fc[f0 + ff] * qt[d & 255] * qt[d >> 8];
+      }
+      __syncthreads();
+      const float* arow = s_A + kpar * chunk + ((32 * TT + (lane & 31)) ^ (kpar << 5));
+      const float* hrow = s_u + kpar * WP;   // feature kpar of the block; + 2 j WP for product j
+      // straight-line groups of 8 products, each group's LDS reads issued before its
+      // products; every wave also forms the all-ones channel (kept by channel tile 0)
+      auto products = [&](auto check_t) __attribute__((always_inline)) {
+        constexpr bool CHECK = decltype(check_t)::value;   // the last block: rows past DCAN
+#pragma unroll
+        for (int j0 = 0; j0 < FB1 / 2; j0 += 8) {
+          float av[8], bv[8][NCT], hv[8];
+#pragma unroll
+          for (int jj = 0; jj < 8; ++jj) {
+            const int j = j0 + jj;
+            av[jj] = arow[2 * j * chunk];
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) bv[jj][ct] = hrow[2 * j * WP + 32 * (CT0 + ct) + (lane & 31)];
+            hv[jj] = hrow[2 * j * WP + DV];
+            if (CHECK && f0 + 2 * j + kpar >= DCAN) {
+              av[jj] = 0.f;
+              hv[jj] = 0.f;
+#pragma unroll
+              for (int ct = 0; ct < NCT; ++ct) bv[jj][ct] = 0.f;
+            }
+          }
+#pragma unroll
+          for (int jj = 0; jj < 8; ++jj) {
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) U[jj & 1][ct] = mfma_f32(av[jj], bv[jj][ct], U[jj & 1][ct]);
+            dpart = fmaf(av[jj], hv[jj], dpart);
+          }
+        }
+      };
+      if (f0 + FB1 <= DCAN)
+        products(std::integral_constant<bool, false>{});
+      else
+        products(std::integral_constant<bool, true>{});
+    }
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) U[0][ct][i] += U[1][ct][i];
+    float* urow0 = s_dq + 32 * TT * (DH + 1);   // part 0's rows of token tile TT
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        urow0[mrow(i, kpar) * (DH + 1) + 32 * (CT0 + ct) + (lane & 31)] = U[0][ct][i];
+    dpart += __shfl_xor(dpart, 32, 64);
+    if (CT0 == 0 && kpar == 0) urow0[(lane & 31) * (DH + 1) + DV] = dpart;   // channel tile 0's
+  }
+  // the chunk's pairs, on the vector ALUs: this part's share
   float acc[WP];
 #pragma unroll
   for (int w = 0; w < WP; ++w) acc[w] = 0.f;
-  fetch_block(0);
-  for (int f0 = 0; f0 < DCAN; f0 += 32) {
-    __syncthreads();
-    stage_block(f0);
-    __syncthreads();
-    if (active) {
-      const int nf = min(32, DCAN - f0);
-      for (int ff = half; ff < nf; ff += SP) {
-        int r, t;
-        const int kind = feat_decode(f0 + ff, r, t);
-        const float psi = kind == 0 ? 1.f : kind == 1 ? qi[r] : qi[r] * qi[t];
-        axpy_row(acc, s_cf[ff] * psi, s_H + ff * WP);
-      }
-    }
-  }
   for (int j0 = 0; j0 < clen; j0 += TB) {
     const int nj = min(TB, clen - j0);
     __syncthreads();
@@ -406,6 +541,13 @@ k_bwd_query(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunks,
       const float* pr = s_dq + (h * chunk + qx) * (DH + 1);
 #pragma unroll
       for (int w = 0; w < W; ++w) acc[w] += pr[w];
+    }
+    // + the state part (this part's own row, written in step 1), the row cleared
+    // for the dq sums of step 3
+#pragma unroll
+    for (int w = 0; w < W; ++w) {
+      acc[w] += xrow[w];
+      xrow[w] = 0.f;
     }
     if (active) {
       const float inv = 1.0f / acc[DV];
@@ -467,24 +609,82 @@ k_bwd_query(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunks,
       if (jj >= jmax) arow[j0 + jj] = 0.f;
   }
 
-  // ---- 4. state part: d_f = H_{<c}[f] . g_i, then the monomials' derivatives
-  fetch_block(0);
-  for (int f0 = 0; f0 < DCAN; f0 += 32) {
+  // ---- 4. state part of dq: per 32-feature block,
+  //   D[f][tok] = sum_w H_{<c}[f][w] g_tok[w]   on the fp32 matrix cores
+  // (M = features, N = tokens, K = channels; g of the chunk read once into registers
+  // as B operands), c_f D to an LDS tile E[f][tok], then each part adds
+  // c_f D d psi_f / dq into its own dq row for its share of the block's features.
+  // Chunk 64: wave = (token tile wave % 2, channel half wave / 2), the halves' partial
+  // D in two tiles; chunk 128: wave = token tile, all channels.
+  {
+    constexpr int GS = W + 1;                    // g row: channels 0..64 and a zero
+    constexpr int NJ = SP == 4 ? 17 : 33;        // channel pairs per wave (the first half: 16)
+    constexpr int NE = SP == 4 ? 2 : 1;          // E tiles (one per channel half)
+    float* s_g = s_k;
+    float* s_E = s_k;                            // [NE][32][chunk], after g is in registers
+    static_assert((256 / SP) * GS <= TB * (DH + 1) + TB * WP, "the g tile fits the staged rows");
+    static_assert(NE * 32 * (256 / SP) <= TB * (DH + 1) + TB * WP, "the E tiles fit the staged rows");
+    __syncthreads();   // step 3's reads of the staged keys and values are done
+    if (half == 0) {
+#pragma unroll
+      for (int w = 0; w < W; ++w) s_g[qx * GS + w] = g[w];
+      s_g[qx * GS + W] = 0.f;
+    }
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+    const int TT = SP == 4 ? (wave & 1) : wave;
+    const int KH = SP == 4 ? (wave >> 1) : 0;
+    const int j_begin = SP == 4 ? 16 * KH : 0;
+    const int j_end = SP == 4 ? (KH ? 33 : 16) : 33;
+    const int hout = lane >> 5;
+    const int tok = 32 * TT + (lane & 31);
     __syncthreads();
-    stage_block(f0);
-    __syncthreads();
-    if (active) {
-      const int nf = min(32, DCAN - f0);
-      for (int ff = half; ff < nf; ff += SP) {
-        int r, t;
-        const int kind = feat_decode(f0 + ff, r, t);
-        if (kind == 0) continue;
-        const float cd = s_cf[ff] * dot_row(s_H + ff * WP, g);
-        if (kind == 1) {
-          dqi[r] += cd;
-        } else {
-          dqi[r] = fmaf(cd, qi[t], dqi[r]);
-          dqi[t] = fmaf(cd, qi[r], dqi[t]);
+    float gv[NJ];   // B operands: g[tok][2 j + lane / 32] over this wave's channel pairs
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int jj = j_begin + j;
+      gv[j] = jj < j_end ? s_g[tok * GS + 2 * jj + hout] : 0.f;
+    }
+    const float* hrow = s_H + (lane & 31) * WP + hout;   // A: H[f0 + lane % 32][2 j + lane / 32]
+    float* erow = s_E + KH * 32 * chunk + tok;          // E[kh][row][tok]
+    fetch_block(0);
+    for (int f0 = 0; f0 < DCAN; f0 += 32) {
+      __syncthreads();   // also: the last block's E tiles have been read
+      stage_block(f0);
+      __syncthreads();
+      fx16 D[2];
+#pragma unroll
+      for (int x = 0; x < 2; ++x)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) D[x][i] = 0.f;
+#pragma unroll
+      for (int j0 = 0; j0 < NJ; j0 += 8) {
+        float av[8];
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj)
+          if (j0 + jj < NJ) av[jj] = j_begin + j0 + jj < j_end ? hrow[2 * (j_begin + j0 + jj)] : 0.f;
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj)
+          if (j0 + jj < NJ) D[jj & 1] = mfma_f32(av[jj], gv[j0 + jj], D[jj & 1]);
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int row = mrow(i, hout);
+        erow[row * chunk] = s_cf[row] * (D[0][i] + D[1][i]);
+      }
+      __syncthreads();
+      if (active) {
+        const int nf = min(32, DCAN - f0);
+        for (int ff = half; ff < nf; ff += SP) {
+          const int dec = s_fdec[ff];
+          const int kind = dec & 3, r = (dec >> 8) & 255, t = dec >> 16;
+          float cd = s_E[ff * chunk + qx];
+          if (NE == 2) cd += s_E[(32 + ff) * chunk + qx];
+          if (kind == 1) {
+            dqi[r] += cd;
+          } else if (kind == 2) {
+            dqi[r] = fmaf(cd, qi[t], dqi[r]);
+            dqi[t] = fmaf(cd, qi[r], dqi[t]);
+          }
         }
       }
     }
@@ -974,14 +1174,15 @@ static oal_status backward_typed(int batch, int n_q_heads, int n_kv_heads, int s
                              : reinterpret_cast<const void*>(&k_bwd_query<T, 2>);
     if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem) != hipSuccess)
       return set_error(OAL_ERR_HIP, "k_bwd_query: cannot reserve %zu bytes of LDS", smem);
+    const dim3 grid_q((unsigned)(((size_t)units * n_chunks + 7) / 8 * 8 * (size_t)(n_q_heads / n_kv_heads)));
     ProfScope ps("k_bwd_query", stream);
     if (sp == 4)
-      hipLaunchKernelGGL((k_bwd_query<T, 4>), dim3(n_chunks, n_q_heads, batch), dim3(4 * chunk), smem,
-                         stream, n_q_heads, n_kv_heads, seq_len, chunk, n_chunks, qq, kk, vv, coeffs, dy,
+      hipLaunchKernelGGL((k_bwd_query<T, 4>), grid_q, dim3(4 * chunk), smem,
+                         stream, n_q_heads, n_kv_heads, seq_len, chunk, n_chunks, units, qq, kk, vv, coeffs, dy,
                          w.hc, w.gbuf, w.alpha, dq);
     else
-      hipLaunchKernelGGL((k_bwd_query<T, 2>), dim3(n_chunks, n_q_heads, batch), dim3(2 * chunk), smem,
-                         stream, n_q_heads, n_kv_heads, seq_len, chunk, n_chunks, qq, kk, vv, coeffs, dy,
+      hipLaunchKernelGGL((k_bwd_query<T, 2>), grid_q, dim3(2 * chunk), smem,
+                         stream, n_q_heads, n_kv_heads, seq_len, chunk, n_chunks, units, qq, kk, vv, coeffs, dy,
                          w.hc, w.gbuf, w.alpha, dq);
     if ((st = check_launch("k_bwd_query")) != OAL_OK) return st;
   }
