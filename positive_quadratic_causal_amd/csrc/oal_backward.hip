@@ -244,6 +244,12 @@ struct BwdWs {
 // chunk 64 (256 threads, 143 KB of LDS per block), two at chunk 128.
 static int key_split(int chunk) { return chunk <= 64 ? 4 : 2; }
 
+// The suffix-state slot of the key-side kernel is cut into this many feature
+// ranges, one workgroup (and one set of parts) each: it walks all 2145 features
+// while the pair slots meet one chunk of queries, and would otherwise set the
+// kernel's length alone.
+constexpr int KEY_RSPLIT = 4;
+
 static BwdWs bwd_ws(void* base, int batch, int n_q_heads, int n_kv_heads, int seq_len, int chunk) {
   const size_t units = (size_t)batch * n_kv_heads;
   const size_t nc = (size_t)((seq_len + chunk - 1) / chunk);
@@ -259,7 +265,7 @@ static BwdWs bwd_ws(void* base, int batch, int n_q_heads, int n_kv_heads, int se
   const size_t o_g = take(bh * nc * chunk * WP);
   const size_t o_a = take(bh * nc * chunk * chunk);
   const size_t o_d = take(bh * nc * DS);
-  const size_t o_k = take(units * (size_t)key_split(chunk) * (n_q_heads / n_kv_heads + 1) * nc * chunk *
+  const size_t o_k = take(units * (size_t)key_split(chunk) * (n_q_heads / n_kv_heads + KEY_RSPLIT) * nc * chunk *
                           (DH + DV));
   BwdWs w;
   uint8_t* p = reinterpret_cast<uint8_t*>(base);
@@ -673,17 +679,47 @@ k_bwd_query(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunks,
       }
       __syncthreads();
       if (active) {
-        const int nf = min(32, DCAN - f0);
-        for (int ff = half; ff < nf; ff += SP) {
-          const int dec = s_fdec[ff];
-          const int kind = dec & 3, r = (dec >> 8) & 255, t = dec >> 16;
-          float cd = s_E[ff * chunk + qx];
-          if (NE == 2) cd += s_E[(32 + ff) * chunk + qx];
-          if (kind == 1) {
-            dqi[r] += cd;
-          } else if (kind == 2) {
-            dqi[r] = fmaf(cd, qi[t], dqi[r]);
-            dqi[t] = fmaf(cd, qi[r], dqi[t]);
+        constexpr int NPT = 32 / SP;   // this part's features of the block: ff = half + SP k
+        const int d_first = s_fdec[half], d_last = s_fdec[half + SP * (NPT - 1)];
+        // a block of pairs only, whose features of this part share one r: their t's
+        // are distinct, so the t-side updates go as one batch of reads and one of
+        // writes, and the r-side sums in a register (the pair (r, r) included: its
+        // t-side write lands before the r-side read-modify-write)
+        const bool one_run = f0 >= 1 + DH && f0 + 31 < DCAN &&
+                             ((d_first >> 8) & 255) == ((d_last >> 8) & 255);
+        if (one_run) {
+          const int r = (d_first >> 8) & 255;
+          const float qr = qi[r];
+          int tk[NPT];
+          float cdk[NPT], dv[NPT];
+          float accr = 0.f;
+#pragma unroll
+          for (int k = 0; k < NPT; ++k) {
+            const int ff = half + SP * k;
+            tk[k] = s_fdec[ff] >> 16;
+            float cd = s_E[ff * chunk + qx];
+            if (NE == 2) cd += s_E[(32 + ff) * chunk + qx];
+            cdk[k] = cd;
+            accr = fmaf(cd, qi[tk[k]], accr);
+          }
+#pragma unroll
+          for (int k = 0; k < NPT; ++k) dv[k] = dqi[tk[k]];
+#pragma unroll
+          for (int k = 0; k < NPT; ++k) dqi[tk[k]] = fmaf(cdk[k], qr, dv[k]);
+          dqi[r] += accr;
+        } else {
+          const int nf = min(32, DCAN - f0);
+          for (int ff = half; ff < nf; ff += SP) {
+            const int dec = s_fdec[ff];
+            const int kind = dec & 3, r = (dec >> 8) & 255, t = dec >> 16;
+            float cd = s_E[ff * chunk + qx];
+            if (NE == 2) cd += s_E[(32 + ff) * chunk + qx];
+            if (kind == 1) {
+              dqi[r] += cd;
+            } else if (kind == 2) {
+              dqi[r] = fmaf(cd, qi[t], dqi[r]);
+              dqi[t] = fmaf(cd, qi[r], dqi[t]);
+            }
           }
         }
       }
@@ -703,9 +739,15 @@ k_bwd_query(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunks,
 }
 
 // ---------------------------------------------------------------------------
-// Suffix deltas and the state part of dc.  Block (feature block, chunk, unit);
-// thread: feature f = 64 fb + (tid & 63), columns w = 16 (tid >> 6) + j, j < 16, and
-// the all-ones channel on the fourth wave.
+// Suffix deltas and the state part of dc.  Block (feature block, chunk, unit).
+// Per query head of the unit, the tile R_h[f][w] = sum_i psi_f(q_i) g_i[w] of the
+// block's 64 features is formed on the fp32 matrix cores (M = features, N =
+// channels, K = tokens; wave = (feature half wave % 2, channel half wave / 2); A =
+// psi_f(q) of the lane's own feature, B = the staged g rows; the all-ones channel
+// as a multiply-add per product on the waves of channel half 0) and passed through
+// LDS to the thread layout below: thread feature f = 64 fb + (tid & 63), columns
+// w = 16 (tid >> 6) + j, j < 16, and the all-ones channel on the fourth wave, which
+// adds c_f R_h into the suffix delta and H_{<c} . R_h into the state part of dc.
 template <typename T>
 __global__ void __launch_bounds__(256)
 k_bwd_rbuild(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunks,
@@ -720,8 +762,9 @@ k_bwd_rbuild(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunks
   const int tid = threadIdx.x;
   const int f = fb * FB + (tid & 63);
   const int wq = tid >> 6;
-  __shared__ float s_q[TB][DH + 1];
+  __shared__ float s_q[TB][DH + 1];                          // q~ = (q, 1) rows, zero past the sequence
   __shared__ __attribute__((aligned(16))) float s_g[TB][WP];
+  __shared__ __attribute__((aligned(16))) float s_R[FB][WP];  // R_h of the block
   __shared__ float s_red[4][FB];
   int r, t;
   const int kind = feat_decode(f, r, t);
@@ -736,15 +779,26 @@ k_bwd_rbuild(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunks
     hval[j] = w >= 0 ? hc[slot + (size_t)w * DS + f] : 0.f;
     rd[j] = 0.f;
   }
+  // the matrix-core roles: this lane's feature (A rows) and channel column (B)
+  const int wave = __builtin_amdgcn_readfirstlane(wq), lane = tid & 63;
+  const int FT = wave & 1, WT = wave >> 1, kpar = lane >> 5;
+  const int fa = fb * FB + 32 * FT + (lane & 31);
+  int ra, ta;
+  const int kinda = feat_decode(fa, ra, ta);
+  const int ia = kinda == 0 ? DH : ra, ib = kinda == 2 ? ta : DH;   // psi = q~[ia] q~[ib]
+  const float amask = kinda == 3 ? 0.f : 1.f;
   const int t0 = c * chunk;
   const int t1 = min(seq_len, t0 + chunk);
   const size_t npad = (size_t)n_chunks * chunk;
   for (int hh = 0; hh < rep; ++hh) {
     const int hq = kv * rep + hh;
     const float cf = coef_of(coef_rec(coeffs, hq), f);
-    float acc[WPT];
+    fx16 D[2];
 #pragma unroll
-    for (int j = 0; j < WPT; ++j) acc[j] = 0.f;
+    for (int x = 0; x < 2; ++x)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) D[x][i] = 0.f;
+    float d64 = 0.f;   // all-ones channel of the lane's feature, its tokens of parity kpar
     const size_t qrow0 = ((size_t)b * n_q_heads + hq) * seq_len;
     const size_t grow0 = ((size_t)b * n_q_heads + hq) * npad;
     for (int i0 = t0; i0 < t1; i0 += TB) {
@@ -754,30 +808,42 @@ k_bwd_rbuild(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunks
         const int ii = i / DH, d = i % DH;
         s_q[ii][d] = ii < ni ? Elem<T>::load(q, (qrow0 + i0 + ii) * DH + d) : 0.f;
       }
+      for (int i = tid; i < TB; i += blockDim.x) s_q[i][DH] = i < ni ? 1.f : 0.f;
       for (int i = tid; i < TB * WP; i += blockDim.x) {
         const int ii = i / WP, w = i % WP;
         s_g[ii][w] = ii < ni ? gbuf[(grow0 + i0 + ii) * WP + w] : 0.f;
       }
       __syncthreads();
-      for (int ii = 0; ii < ni; ++ii) {
-        const float psi = kind == 0 ? 1.f : kind == 1 ? s_q[ii][r] : kind == 2 ? s_q[ii][r] * s_q[ii][t] : 0.f;
-        const float4* gr = reinterpret_cast<const float4*>(&s_g[ii][16 * wq]);
 #pragma unroll
-        for (int j4 = 0; j4 < 4; ++j4) {
-          const float4 g4 = gr[j4];
-          acc[4 * j4 + 0] = fmaf(psi, g4.x, acc[4 * j4 + 0]);
-          acc[4 * j4 + 1] = fmaf(psi, g4.y, acc[4 * j4 + 1]);
-          acc[4 * j4 + 2] = fmaf(psi, g4.z, acc[4 * j4 + 2]);
-          acc[4 * j4 + 3] = fmaf(psi, g4.w, acc[4 * j4 + 3]);
+      for (int j0 = 0; j0 < TB / 2; j0 += 8) {
+        float av[8], bv[8], gv[8];
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) {
+          const int tok = 2 * (j0 + jj) + kpar;
+          av[jj] = amask * s_q[tok][ia] * s_q[tok][ib];
+          bv[jj] = s_g[tok][32 * WT + (lane & 31)];
+          gv[jj] = s_g[tok][W - 1];
         }
-        if (wq == 3) acc[16] = fmaf(psi, s_g[ii][W - 1], acc[16]);
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) {
+          D[jj & 1] = mfma_f32(av[jj], bv[jj], D[jj & 1]);
+          d64 = fmaf(av[jj], gv[jj], d64);
+        }
       }
     }
+    // R_h to LDS (the previous head's readers are done: the token loop's barrier)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s_R[32 * FT + mrow(i, kpar)][32 * WT + (lane & 31)] = D[0][i] + D[1][i];
+    d64 += __shfl_xor(d64, 32, 64);
+    if (WT == 0 && kpar == 0) s_R[32 * FT + (lane & 31)][W - 1] = d64;
+    __syncthreads();
     float part = 0.f;
 #pragma unroll
     for (int j = 0; j < WPT; ++j) {
-      rd[j] = fmaf(cf, acc[j], rd[j]);
-      part = fmaf(hval[j], acc[j], part);
+      const int w = col_of(j);
+      const float x = w >= 0 ? s_R[tid & 63][w] : 0.f;
+      rd[j] = fmaf(cf, x, rd[j]);
+      part = fmaf(hval[j], x, part);
     }
     if (dcp != nullptr) {
       s_red[wq][tid & 63] = part;
@@ -824,8 +890,8 @@ k_bwd_key(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunks,
           const float* __restrict__ rc, float* __restrict__ kpart) {
   const int c = blockIdx.x;
   const int rep = n_q_heads / n_kv_heads;
-  const int unit = blockIdx.y / (rep + 1);
-  const int slot = blockIdx.y % (rep + 1);
+  const int unit = blockIdx.y / (rep + KEY_RSPLIT);
+  const int slot = blockIdx.y % (rep + KEY_RSPLIT);   // >= rep: suffix states, feature range slot - rep
   const int b = unit / n_kv_heads, kv = unit % n_kv_heads;
   const int tid = threadIdx.x;
   const int nthr = blockDim.x;                // SP * chunk
@@ -879,15 +945,20 @@ k_bwd_key(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunks,
       if (i < 32 * W) pre[e] = Rs[(size_t)(i / 32) * DS + f0 + i % 32];   // f0 + 31 < DS always
     }
   };
-  if (slot == rep) fetch_block(0);
-  for (int f0 = 0; slot == rep && f0 < DCAN; f0 += 32) {
+  // this slot's range of 32-feature blocks
+  constexpr int NBLK = (DCAN + 31) / 32;
+  const int rq = slot - rep;
+  const int fbeg = rq < 0 ? DCAN : 32 * ((NBLK * rq) / KEY_RSPLIT);
+  const int fend = rq < 0 ? DCAN : min(DCAN, 32 * ((NBLK * (rq + 1)) / KEY_RSPLIT));
+  if (fbeg < fend) fetch_block(fbeg);
+  for (int f0 = fbeg; f0 < fend; f0 += 32) {
     __syncthreads();
 #pragma unroll
     for (int e = 0; e < PB; ++e) {
       const int i = tid + e * 256;
       if (i < 32 * W) s_R[(i % 32) * WP + i / 32] = pre[e];
     }
-    if (f0 + 32 < DCAN) fetch_block(f0 + 32);
+    if (f0 + 32 < fend) fetch_block(f0 + 32);
     __syncthreads();
     if (active) {
       const int nf = min(32, DCAN - f0);
@@ -965,7 +1036,7 @@ k_bwd_key(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunks,
     }
   }
   if (active) {
-    float* o = kpart + (((size_t)unit * SP * (rep + 1) + SP * slot + half) * npad + t0 + jx) * (DH + DV);
+    float* o = kpart + (((size_t)unit * SP * (rep + KEY_RSPLIT) + SP * slot + half) * npad + t0 + jx) * (DH + DV);
 #pragma unroll
     for (int d = 0; d < DH; ++d) o[d] = dkj[d];
 #pragma unroll
@@ -1212,11 +1283,11 @@ static oal_status backward_typed(int batch, int n_q_heads, int n_kv_heads, int s
     {
       ProfScope ps("k_bwd_key", stream);
       if (ks == 4)
-        hipLaunchKernelGGL((k_bwd_key<T, 4>), dim3(n_chunks, units * (rep + 1)), dim3(4 * chunk), smem,
+        hipLaunchKernelGGL((k_bwd_key<T, 4>), dim3(n_chunks, units * (rep + KEY_RSPLIT)), dim3(4 * chunk), smem,
                            stream, n_q_heads, n_kv_heads, seq_len, chunk, n_chunks, qq, kk, vv, coeffs,
                            w.gbuf, w.rc, w.kpart);
       else
-        hipLaunchKernelGGL((k_bwd_key<T, 2>), dim3(n_chunks, units * (rep + 1)), dim3(2 * chunk), smem,
+        hipLaunchKernelGGL((k_bwd_key<T, 2>), dim3(n_chunks, units * (rep + KEY_RSPLIT)), dim3(2 * chunk), smem,
                            stream, n_q_heads, n_kv_heads, seq_len, chunk, n_chunks, qq, kk, vv, coeffs,
                            w.gbuf, w.rc, w.kpart);
       if ((st = check_launch("k_bwd_key")) != OAL_OK) return st;
@@ -1224,7 +1295,7 @@ static oal_status backward_typed(int batch, int n_q_heads, int n_kv_heads, int s
     ProfScope ps("k_bwd_ksum", stream);
     const size_t per_unit = (size_t)seq_len * (DH + DV);
     hipLaunchKernelGGL(k_bwd_ksum, dim3((unsigned)((per_unit + 255) / 256), units), dim3(256), 0,
-                       stream, n_kv_heads, ks * (rep + 1), seq_len, n_chunks * chunk, w.kpart, dk, dv);
+                       stream, n_kv_heads, ks * (rep + KEY_RSPLIT), seq_len, n_chunks * chunk, w.kpart, dk, dv);
     if ((st = check_launch("k_bwd_ksum")) != OAL_OK) return st;
   }
   if (!want_coef) return OAL_OK;
