@@ -1062,67 +1062,84 @@ k_bwd_ksum(int n_kv_heads, int nparts, int seq_len, int npad, const float* __res
 }
 
 // ---------------------------------------------------------------------------
-// Pair part of dc: block (feature block of 256, chunk, batch x query head);
-// thread f holds psi_f(k_j) for the chunk's keys in registers.
+// Pair part of dc: dc_f += sum_i psi_f(q_i) Y[i][f] with Y = alpha Psi(K) over the
+// chunk's keys (alpha_ij = 0 for j > i).  One block per (chunk, query head); Y on
+// the fp32 matrix cores one 32-feature tile at a time (wave w takes tiles w, w + 4,
+// ...): token tiles of 32 rows (A = alpha rows), K = keys two per product, B =
+// psi_f(k_j) of the lane's own feature formed in place (psi = k~[ia] k~[ib] with
+// k~ = (k, 1)), key steps past a token tile's diagonal skipped; the weighted row
+// sum in registers, the two lane halves added at the end.
 template <typename T, int CH>
 __global__ void __launch_bounds__(256)
 k_bwd_dc_intra(int n_q_heads, int n_kv_heads, int seq_len, int n_chunks,
                const T* __restrict__ q, const T* __restrict__ k, const float* __restrict__ alpha,
                float* __restrict__ dcp) {
-  const int f = blockIdx.x * 256 + threadIdx.x;
-  const int c = blockIdx.y;
-  const int bh = blockIdx.z;
+  const int c = blockIdx.x;
+  const int bh = blockIdx.y;
   const int b = bh / n_q_heads, hq = bh % n_q_heads;
   const int unit = b * n_kv_heads + hq / (n_q_heads / n_kv_heads);
   const int t0 = c * CH;
   const int clen = min(CH, seq_len - t0);
+  const int tid = threadIdx.x;
   extern __shared__ __attribute__((aligned(16))) float smem[];
-  float* s_a = smem;                          // [CH][CH]
-  float* s_q = s_a + CH * CH;                 // [CH][DH + 1]
-  float* s_k = s_q + CH * (DH + 1);           // [CH][DH + 1]
+  float* s_a = smem;                          // [CH][CH + 1] (rows padded: the lanes of a
+                                              // product read 32 rows at one column)
+  float* s_q = s_a + CH * (CH + 1);           // [CH][DH + 1]: q~ = (q, 1), zero past the sequence
+  float* s_k = s_q + CH * (DH + 1);           // [CH][DH + 1]: k~ = (k, 1), likewise
   const float* ablk = alpha + ((size_t)bh * n_chunks + c) * CH * CH;
-  for (int i = threadIdx.x; i < CH * CH / 4; i += blockDim.x)
-    reinterpret_cast<float4*>(s_a)[i] = reinterpret_cast<const float4*>(ablk)[i];
+  for (int i = tid; i < CH * CH; i += blockDim.x) s_a[(i / CH) * (CH + 1) + i % CH] = ablk[i];
   const size_t qrow0 = (size_t)bh * seq_len + t0;
   const size_t krow0 = (size_t)unit * seq_len + t0;
-  for (int i = threadIdx.x; i < CH * DH; i += blockDim.x) {
+  for (int i = tid; i < CH * DH; i += blockDim.x) {
     const int ii = i / DH, d = i % DH;
     s_q[ii * (DH + 1) + d] = ii < clen ? Elem<T>::load(q, (qrow0 + ii) * DH + d) : 0.f;
     s_k[ii * (DH + 1) + d] = ii < clen ? Elem<T>::load(k, (krow0 + ii) * DH + d) : 0.f;
   }
+  for (int i = tid; i < CH; i += blockDim.x) {
+    s_q[i * (DH + 1) + DH] = i < clen ? 1.f : 0.f;
+    s_k[i * (DH + 1) + DH] = i < clen ? 1.f : 0.f;
+  }
   __syncthreads();
-  if (f >= DCAN) return;
-  int r, t;
-  const int kind = feat_decode(f, r, t);
-  float kf[CH];
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int col = lane & 31, kpar = lane >> 5;
+  float* dout = dcp + ((size_t)bh * n_chunks + c) * DS;
+  for (int ft = wave; ft < DS / 32; ft += 4) {
+    const int f = 32 * ft + col;               // this lane's feature (B column)
+    int r, t;
+    const int kind = feat_decode(f, r, t);
+    const int ia = kind == 0 ? DH : r, ib = kind == 2 ? t : DH;
+    const float fm = kind == 3 ? 0.f : 1.f;
+    float part = 0.f;
 #pragma unroll
-  for (int j = 0; j < CH; ++j) {
-    const float* kr = s_k + j * (DH + 1);
-    kf[j] = kind == 0 ? 1.f : kind == 1 ? kr[r] : kr[r] * kr[t];
-  }
-  // alpha_ij = 0 for j > i: the rows of band B (16 B .. 16 B + 15) stop at key
-  // 16 B + 15 (a compile-time bound, so kf stays in registers)
-  float acc = 0.f;
+    for (int TT = 0; TT < CH / 32; ++TT) {
+      fx16 D[2];
 #pragma unroll
-  for (int B = 0; B < CH / 16; ++B) {
-    const int ie = min(16 * B + 16, clen);
-    for (int i = 16 * B; i < ie; ++i) {
-      const float* qr = s_q + i * (DH + 1);
-      const float qf = kind == 0 ? 1.f : kind == 1 ? qr[r] : qr[r] * qr[t];
-      const float4* ar = reinterpret_cast<const float4*>(s_a + i * CH);
-      float s0 = 0.f, s1 = 0.f;
+      for (int x = 0; x < 2; ++x)
 #pragma unroll
-      for (int j4 = 0; j4 < 4 * B + 4; ++j4) {
-        const float4 av = ar[j4];
-        s0 = fmaf(av.x, kf[4 * j4 + 0], s0);
-        s1 = fmaf(av.y, kf[4 * j4 + 1], s1);
-        s0 = fmaf(av.z, kf[4 * j4 + 2], s0);
-        s1 = fmaf(av.w, kf[4 * j4 + 3], s1);
+        for (int i = 0; i < 16; ++i) D[x][i] = 0.f;
+      const float* arow = s_a + (32 * TT + col) * (CH + 1) + kpar;   // alpha[i][2 kk + kpar]
+#pragma unroll
+      for (int kk0 = 0; kk0 < 16 * (TT + 1); kk0 += 8) {   // keys j < 32 (TT + 1)
+        float av[8], bv[8];
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) {
+          const int j = 2 * (kk0 + jj) + kpar;
+          av[jj] = arow[2 * (kk0 + jj)];
+          const float* kr = s_k + j * (DH + 1);
+          bv[jj] = fm * kr[ia] * kr[ib];
+        }
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) D[jj & 1] = mfma_f32(av[jj], bv[jj], D[jj & 1]);
       }
-      acc = fmaf(qf, s0 + s1, acc);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float* qr = s_q + (32 * TT + mrow(i, kpar)) * (DH + 1);
+        part = fmaf(qr[ia] * qr[ib], D[0][i] + D[1][i], part);
+      }
     }
+    part += __shfl_xor(part, 32, 64);
+    if (kpar == 0 && f < DCAN) dout[f] += part;
   }
-  dcp[((size_t)bh * n_chunks + c) * DS + f] += acc;
 }
 
 // Sum over chunks and batch, then (da, db, dC) of [OAL] Eq. 3: the record's
@@ -1300,13 +1317,13 @@ static oal_status backward_typed(int batch, int n_q_heads, int n_kv_heads, int s
   }
   if (!want_coef) return OAL_OK;
   {
-    const size_t smem = sizeof(float) * ((size_t)chunk * chunk + 2 * chunk * (DH + 1));
+    const size_t smem = sizeof(float) * ((size_t)chunk * (chunk + 1) + 2 * chunk * (DH + 1));
     const void* fn = chunk == 64 ? reinterpret_cast<const void*>(&k_bwd_dc_intra<T, 64>)
                                  : reinterpret_cast<const void*>(&k_bwd_dc_intra<T, 128>);
     if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem) != hipSuccess)
       return set_error(OAL_ERR_HIP, "k_bwd_dc_intra: cannot reserve %zu bytes of LDS", smem);
     ProfScope ps("k_bwd_dc_intra", stream);
-    const dim3 grid((DCAN + 255) / 256, n_chunks, batch * n_q_heads);
+    const dim3 grid(n_chunks, batch * n_q_heads);
     if (chunk == 64)
       hipLaunchKernelGGL((k_bwd_dc_intra<T, 64>), grid, dim3(256), smem, stream, n_q_heads, n_kv_heads,
                          seq_len, n_chunks, qq, kk, w.alpha, w.dcp);
