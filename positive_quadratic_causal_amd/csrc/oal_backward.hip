@@ -77,6 +77,7 @@ __device__ __forceinline__ int feat_decode(int f, int& r, int& t) {
   return 3;
 }
 static_assert(DH == 64, "the pair decode's constants are for d_h = 64");
+static_assert(TB * DH % 256 == 0 && TB * WP % 256 == 0, "staging by 256 threads");
 
 __device__ __forceinline__ float coef_of(const float* rec, int f) {
   if (f == 0) return rec[OAL_COEF_A];
@@ -804,15 +805,32 @@ k_bwd_rbuild(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunks
     for (int i0 = t0; i0 < t1; i0 += TB) {
       const int ni = min(TB, t1 - i0);
       __syncthreads();
-      for (int i = tid; i < TB * DH; i += blockDim.x) {
-        const int ii = i / DH, d = i % DH;
-        s_q[ii][d] = ii < ni ? Elem<T>::load(q, (qrow0 + i0 + ii) * DH + d) : 0.f;
+      // the q and g rows of the tile are contiguous in memory: every load of the
+      // 256 threads is issued before the first is awaited
+      const T* qt = q + (qrow0 + i0) * DH;
+      const float* gt = gbuf + (grow0 + i0) * WP;
+      float lq[TB * DH / 256], lg[TB * WP / 256];
+#pragma unroll
+      for (int e = 0; e < TB * DH / 256; ++e) {
+        const int i = tid + 256 * e;
+        lq[e] = i < ni * DH ? Elem<T>::load(qt, i) : 0.f;
       }
-      for (int i = tid; i < TB; i += blockDim.x) s_q[i][DH] = i < ni ? 1.f : 0.f;
-      for (int i = tid; i < TB * WP; i += blockDim.x) {
-        const int ii = i / WP, w = i % WP;
-        s_g[ii][w] = ii < ni ? gbuf[(grow0 + i0 + ii) * WP + w] : 0.f;
+#pragma unroll
+      for (int e = 0; e < TB * WP / 256; ++e) {
+        const int i = tid + 256 * e;
+        lg[e] = i < ni * WP ? gt[i] : 0.f;
       }
+#pragma unroll
+      for (int e = 0; e < TB * DH / 256; ++e) {
+        const int i = tid + 256 * e;
+        s_q[i / DH][i % DH] = lq[e];
+      }
+#pragma unroll
+      for (int e = 0; e < TB * WP / 256; ++e) {
+        const int i = tid + 256 * e;
+        s_g[i / WP][i % WP] = lg[e];
+      }
+      if (tid < TB) s_q[tid][DH] = tid < ni ? 1.f : 0.f;
       __syncthreads();
 #pragma unroll
       for (int j0 = 0; j0 < TB / 2; j0 += 8) {
