@@ -40,6 +40,7 @@ constexpr int TB = 64;                 // tokens per staged tile
 constexpr int FB = 64;                 // feature rows per build block
 constexpr int NFB = DS / FB;           // 34
 constexpr int WPT = (W + 3) / 4;       // 17 columns per thread in the build
+constexpr int WPH = W + 1;             // LDS row of a staged H block: channels 0..64, a zero
 
 // fp32 matrix-core product v_mfma_f32_32x32x2_f32: A 32 x 2 (lane l holds
 // A[l % 32][l / 32]), B 2 x 32 (lane l holds B[l / 32][l % 32]), D 32 x 32 (lane l,
@@ -78,6 +79,40 @@ __device__ __forceinline__ int feat_decode(int f, int& r, int& t) {
 }
 static_assert(DH == 64, "the pair decode's constants are for d_h = 64");
 static_assert(TB * DH % 256 == 0 && TB * WP % 256 == 0, "staging by 256 threads");
+
+// Row blocks of the features with a gradient, 64 feature slots each.  Block b < 32:
+// the pair rows r = b (pairs (b, t), t = b .. 63) and r = 63 - b (pairs (63 - b, t),
+// t = 63 - b .. 62); block 32: the linear features x_t; block 33: the column
+// (t, 63), t = 32 .. 63.  Every pair and linear feature lies in exactly one block
+// (the constant has no gradient).  A block's slots form up to two rows, each with a
+// multiplier index m and a run of t: slot s < na is (m0, t = ta0 + s), slot
+// na <= s < na + nb is (m1, t = tb0 + s - na).  Multiplier DH is the constant slot
+// q~[64] = 1 of the linear features.
+constexpr int NRB = 34;
+struct RowBlk {
+  int m0, ta0, na, m1, tb0, nb;
+};
+__device__ __forceinline__ RowBlk row_block(int blk) {
+  if (blk < 32) return RowBlk{blk, blk, DH - blk, DH - 1 - blk, DH - 1 - blk, blk};
+  if (blk == 32) return RowBlk{DH, 0, DH, DH, 0, 0};
+  return RowBlk{DH - 1, 32, 32, DH, 0, 0};
+}
+// first pair index of row r of the upper triangle: r (2 DH + 1 - r) / 2
+__device__ __forceinline__ int pair_row_start(int r) { return r * (2 * DH + 1 - r) / 2; }
+// canonical feature of slot s of block blk (-1: an empty slot)
+__device__ __forceinline__ int row_block_feature(int blk, const RowBlk& d, int s) {
+  if (s < d.na) {
+    const int t = d.ta0 + s;
+    if (blk == 32) return 1 + t;
+    if (blk == 33) return 1 + DH + pair_row_start(t) + (DH - 1 - t);   // pair (t, 63)
+    return 1 + DH + pair_row_start(d.m0) + (t - d.m0);
+  }
+  if (s < d.na + d.nb) {
+    const int t = d.tb0 + s - d.na;
+    return 1 + DH + pair_row_start(d.m1) + (t - d.m1);
+  }
+  return -1;
+}
 
 __device__ __forceinline__ float coef_of(const float* rec, int f) {
   if (f == 0) return rec[OAL_COEF_A];
@@ -317,17 +352,18 @@ k_bwd_query(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunks,
   extern __shared__ __attribute__((aligned(16))) float smem[];
   float* s_q = smem;                          // [chunk][DH + 1]
   float* s_dq = s_q + chunk * (DH + 1);       // [SP][chunk][DH + 1] (parts >= 1 also pass u~, g)
-  float* s_H = s_dq + SP * chunk * (DH + 1);  // [32][WP]
-  float* s_cf = s_H + 32 * WP;                // [32]
-  float* s_k = s_cf + 32;                     // [TB][DH + 1]
+  float* s_k = s_dq + SP * chunk * (DH + 1);  // [TB][DH + 1]
   float* s_u = s_k + TB * (DH + 1);           // [TB][WP]
   float* s_b = s_u + TB * WP;                 // [DH]  b'
   float* s_S = s_b + DH;                      // [DH][DH]  C / d_h (symmetric)
+  // step 4 only, in the staged keys' and values' rows: a row block of H_{<c} and its c_f
+  float* s_H = s_k;                           // [64][WPH]
+  float* s_cf = s_k + 64 * WPH;               // [64]
+  static_assert(64 * WPH + 64 <= TB * (DH + 1) + TB * WP, "a row block fits the staged rows");
 
   const float* rec = coef_rec(coeffs, hq);
   const float a = rec[OAL_COEF_A];
   __shared__ __attribute__((aligned(16))) GroupTab gt;
-  __shared__ int s_fdec[32];   // kind | r << 8 | t << 16 of the staged block's features
   const bool grouped = reinterpret_cast<const int32_t*>(rec)[OAL_COEF_NG] >= 1;
   if (grouped) build_group_tab(gt, rec, tid);
   const size_t qrow0 = ((size_t)b * n_q_heads + hq) * seq_len + t0;
@@ -353,7 +389,6 @@ k_bwd_query(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunks,
   }
   for (int i = tid; i < DH; i += nthr) s_b[i] = rec[OAL_COEF_BP + i];
   for (int i = tid; i < DH * DH; i += nthr) s_S[i] = rec[OAL_COEF_CM + i];
-  for (int i = tid; i < 32 * (WP - W); i += nthr) s_H[(i / (WP - W)) * WP + W + i % (WP - W)] = 0.f;
   for (int i = tid; i < TB * (WP - W); i += nthr) s_u[(i / (WP - W)) * WP + W + i % (WP - W)] = 0.f;
   __syncthreads();
   const bool fast = grouped && gt.n_out <= MAX_OUT;   // uniform over the block
@@ -362,31 +397,32 @@ k_bwd_query(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunks,
   const float* Hc = hc + ((size_t)unit * n_chunks + c) * STATE_FLOATS;
   const size_t kbase = (size_t)unit * seq_len + t0;
 
-  // the state blocks of 32 features pass through registers one block ahead of
-  // the LDS copy the threads work on (nthr = 256: 9 values per thread at most)
-  constexpr int PB = (32 * W + 255) / 256;
+  // the row blocks of H_{<c} pass through registers one block ahead of the LDS
+  // copy the threads work on: thread tid moves slot tid % 64 of channels
+  // tid / 64 + 4 e (nthr = 256)
+  constexpr int PB = (64 * W + 255) / 256;
   float pre[PB], pcf = 0.f;
-  auto fetch_block = [&](int f0) {
+  auto fetch_block = [&](int blk) {
+    const RowBlk d = row_block(blk);
+    const int fs = row_block_feature(blk, d, tid & 63);
 #pragma unroll
     for (int e = 0; e < PB; ++e) {
-      const int i = tid + e * 256;
-      if (i < 32 * W) pre[e] = Hc[(size_t)(i / 32) * DS + f0 + i % 32];   // f0 + 31 < DS always
+      const int w = (tid >> 6) + 4 * e;
+      if (w < W) pre[e] = fs >= 0 ? Hc[(size_t)w * DS + fs] : 0.f;
     }
-    if (tid < 32) pcf = coef_of(rec, f0 + tid);
+    if (tid < 64) pcf = fs >= 0 ? coef_of(rec, fs) : 0.f;
   };
-  auto stage_block = [&](int f0) {
+  auto stage_block = [&](int blk) {
 #pragma unroll
     for (int e = 0; e < PB; ++e) {
-      const int i = tid + e * 256;
-      if (i < 32 * W) s_H[(i % 32) * WP + i / 32] = pre[e];
+      const int w = (tid >> 6) + 4 * e;
+      if (w < W) s_H[(tid & 63) * WPH + w] = pre[e];
     }
-    if (tid < 32) {
+    if (tid < 64) {
       s_cf[tid] = pcf;
-      int r, t;
-      const int kind = feat_decode(f0 + tid, r, t);
-      s_fdec[tid] = kind | (r << 8) | (t << 16);
+      s_H[tid * WPH + W] = 0.f;   // channel 65 of the last channel pair
     }
-    if (f0 + 32 < DCAN) fetch_block(f0 + 32);
+    if (blk + 1 < NRB) fetch_block(blk + 1);
   };
   auto stage_keys = [&](int j0, int nj) {
     for (int i = tid; i < TB * DH; i += nthr) {
@@ -616,125 +652,125 @@ k_bwd_query(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunks,
       if (jj >= jmax) arow[j0 + jj] = 0.f;
   }
 
-  // ---- 4. state part of dq: per 32-feature block,
-  //   D[f][tok] = sum_w H_{<c}[f][w] g_tok[w]   on the fp32 matrix cores
-  // (M = features, N = tokens, K = channels; g of the chunk read once into registers
-  // as B operands), c_f D to an LDS tile E[f][tok], then each part adds
-  // c_f D d psi_f / dq into its own dq row for its share of the block's features.
-  // Chunk 64: wave = (token tile wave % 2, channel half wave / 2), the halves' partial
-  // D in two tiles; chunk 128: wave = token tile, all channels.
+  // ---- 4. state part of dq: dq_i += sum_f c_f (H_{<c} g_i)_f d psi_f(q_i) / dq_i,
+  // by the row blocks above.  Per block, D[f][tok] = sum_w H_{<c}[f][w] g_tok[w] on
+  // the fp32 matrix cores (M = the block's 64 slots, N = tokens, K = channels; g of
+  // the chunk read once into registers as B operands) and E = c_f D goes to LDS by
+  // slot, E[slot][tok].  A pair (m, t) of a row adds E q_m to dq[t] (the
+  // t side: each thread keeps its DH / SP entries of dq in registers, so a row is a
+  // masked multiply-add over them) and E q_t to dq[m] (the m side: a dot product over
+  // t, summed over the token's parts; every m < DH receives exactly one, stored to
+  // LDS).  The diagonal (m, m) thus gets 2 E q_m; the linear features' m side (the
+  // constant slot) is dropped.  Chunk 64: wave = (feature tile wave % 2, token tile
+  // wave / 2); chunk 128: wave = token tile, both feature tiles.
   {
     constexpr int GS = W + 1;                    // g row: channels 0..64 and a zero
-    constexpr int NJ = SP == 4 ? 17 : 33;        // channel pairs per wave (the first half: 16)
-    constexpr int NE = SP == 4 ? 2 : 1;          // E tiles (one per channel half)
-    float* s_g = s_k;
-    float* s_E = s_k;                            // [NE][32][chunk], after g is in registers
+    constexpr int NJ = (W + 1) / 2;              // 33 channel pairs
+    constexpr int NFT = SP == 4 ? 1 : 2;         // feature tiles per wave
+    constexpr int NTP = DH / SP;                 // dq entries per thread
+    const int ES = chunk + 1;                    // E row stride (bank spread)
+    float* s_g = s_k;                            // [chunk][GS], until g is in registers (then s_H)
+    float* s_E = s_dq;                           // [64 slots][ES], after the dq rows are read
+    float* s_rd = s_dq + 64 * ES;                // [chunk][DH + 1] the m-side sums
     static_assert((256 / SP) * GS <= TB * (DH + 1) + TB * WP, "the g tile fits the staged rows");
-    static_assert(NE * 32 * (256 / SP) <= TB * (DH + 1) + TB * WP, "the E tiles fit the staged rows");
-    __syncthreads();   // step 3's reads of the staged keys and values are done
+    static_assert(64 * (256 / SP + 1) + (256 / SP) * (DH + 1) <= SP * (256 / SP) * (DH + 1),
+                  "E and the m-side sums fit the dq rows");
+    __syncthreads();   // step 3's reads of the staged keys and values and its dq sums are done
     if (half == 0) {
 #pragma unroll
       for (int w = 0; w < W; ++w) s_g[qx * GS + w] = g[w];
       s_g[qx * GS + W] = 0.f;
     }
+    // this thread's dq entries NTP half + j: the parts' rows summed in order
+    float dqt[NTP], qt[NTP];
+#pragma unroll
+    for (int j = 0; j < NTP; ++j) {
+      float x = 0.f;
+#pragma unroll
+      for (int h = 0; h < SP; ++h) x += s_dq[(h * chunk + qx) * (DH + 1) + NTP * half + j];
+      dqt[j] = x;
+      qt[j] = qi[NTP * half + j];
+    }
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
-    const int TT = SP == 4 ? (wave & 1) : wave;
-    const int KH = SP == 4 ? (wave >> 1) : 0;
-    const int j_begin = SP == 4 ? 16 * KH : 0;
-    const int j_end = SP == 4 ? (KH ? 33 : 16) : 33;
+    const int TT = SP == 4 ? (wave >> 1) : wave;
+    const int FT0 = SP == 4 ? (wave & 1) : 0;
     const int hout = lane >> 5;
     const int tok = 32 * TT + (lane & 31);
     __syncthreads();
-    float gv[NJ];   // B operands: g[tok][2 j + lane / 32] over this wave's channel pairs
+    float gv[NJ];   // B operands: g[tok][2 j + lane / 32]
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      const int jj = j_begin + j;
-      gv[j] = jj < j_end ? s_g[tok * GS + 2 * jj + hout] : 0.f;
-    }
-    const float* hrow = s_H + (lane & 31) * WP + hout;   // A: H[f0 + lane % 32][2 j + lane / 32]
-    float* erow = s_E + KH * 32 * chunk + tok;          // E[kh][row][tok]
+    for (int j = 0; j < NJ; ++j) gv[j] = s_g[tok * GS + 2 * j + hout];
+    const float* hrow = s_H + (lane & 31) * WPH + hout;   // A: H[slot lane % 32][2 j + lane / 32]
     fetch_block(0);
-    for (int f0 = 0; f0 < DCAN; f0 += 32) {
-      __syncthreads();   // also: the last block's E tiles have been read
-      stage_block(f0);
+    for (int blk = 0; blk < NRB; ++blk) {
+      const RowBlk d = row_block(blk);
+      __syncthreads();   // also: the last block's E rows have been read
+      stage_block(blk);
       __syncthreads();
-      fx16 D[2];
 #pragma unroll
-      for (int x = 0; x < 2; ++x)
+      for (int ft = 0; ft < NFT; ++ft) {
+        const int FT = FT0 + ft;
+        if (32 * FT >= d.na + d.nb) continue;   // an empty tile (the column block)
+        fx16 D[2];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) D[x][i] = 0.f;
+        for (int x = 0; x < 2; ++x)
 #pragma unroll
-      for (int j0 = 0; j0 < NJ; j0 += 8) {
-        float av[8];
+          for (int i = 0; i < 16; ++i) D[x][i] = 0.f;
+        const float* ha = hrow + 32 * FT * WPH;
 #pragma unroll
-        for (int jj = 0; jj < 8; ++jj)
-          if (j0 + jj < NJ) av[jj] = j_begin + j0 + jj < j_end ? hrow[2 * (j_begin + j0 + jj)] : 0.f;
+        for (int j0 = 0; j0 < NJ; j0 += 8) {
+          float av[8];
 #pragma unroll
-        for (int jj = 0; jj < 8; ++jj)
-          if (j0 + jj < NJ) D[jj & 1] = mfma_f32(av[jj], gv[j0 + jj], D[jj & 1]);
-      }
+          for (int jj = 0; jj < 8; ++jj)
+            if (j0 + jj < NJ) av[jj] = ha[2 * (j0 + jj)];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int row = mrow(i, hout);
-        erow[row * chunk] = s_cf[row] * (D[0][i] + D[1][i]);
-      }
-      __syncthreads();
-      if (active) {
-        constexpr int NPT = 32 / SP;   // this part's features of the block: ff = half + SP k
-        const int d_first = s_fdec[half], d_last = s_fdec[half + SP * (NPT - 1)];
-        // a block of pairs only, whose features of this part share one r: their t's
-        // are distinct, so the t-side updates go as one batch of reads and one of
-        // writes, and the r-side sums in a register (the pair (r, r) included: its
-        // t-side write lands before the r-side read-modify-write)
-        const bool one_run = f0 >= 1 + DH && f0 + 31 < DCAN &&
-                             ((d_first >> 8) & 255) == ((d_last >> 8) & 255);
-        if (one_run) {
-          const int r = (d_first >> 8) & 255;
-          const float qr = qi[r];
-          int tk[NPT];
-          float cdk[NPT], dv[NPT];
-          float accr = 0.f;
+          for (int jj = 0; jj < 8; ++jj)
+            if (j0 + jj < NJ) D[jj & 1] = mfma_f32(av[jj], gv[j0 + jj], D[jj & 1]);
+        }
 #pragma unroll
-          for (int k = 0; k < NPT; ++k) {
-            const int ff = half + SP * k;
-            tk[k] = s_fdec[ff] >> 16;
-            float cd = s_E[ff * chunk + qx];
-            if (NE == 2) cd += s_E[(32 + ff) * chunk + qx];
-            cdk[k] = cd;
-            accr = fmaf(cd, qi[tk[k]], accr);
-          }
-#pragma unroll
-          for (int k = 0; k < NPT; ++k) dv[k] = dqi[tk[k]];
-#pragma unroll
-          for (int k = 0; k < NPT; ++k) dqi[tk[k]] = fmaf(cdk[k], qr, dv[k]);
-          dqi[r] += accr;
-        } else {
-          const int nf = min(32, DCAN - f0);
-          for (int ff = half; ff < nf; ff += SP) {
-            const int dec = s_fdec[ff];
-            const int kind = dec & 3, r = (dec >> 8) & 255, t = dec >> 16;
-            float cd = s_E[ff * chunk + qx];
-            if (NE == 2) cd += s_E[(32 + ff) * chunk + qx];
-            if (kind == 1) {
-              dqi[r] += cd;
-            } else if (kind == 2) {
-              dqi[r] = fmaf(cd, qi[t], dqi[r]);
-              dqi[t] = fmaf(cd, qi[r], dqi[t]);
-            }
-          }
+        for (int i = 0; i < 16; ++i) {
+          const int sl = 32 * FT + mrow(i, hout);
+          if (sl < d.na + d.nb) s_E[sl * ES + tok] = s_cf[sl] * (D[0][i] + D[1][i]);
         }
       }
+      __syncthreads();
+      // t side into the registers, m side as dot products (masked to the rows' runs)
+      const float q0 = qi[d.m0], q1 = qi[d.m1];
+      float d0 = 0.f, d1 = 0.f;
+#pragma unroll
+      for (int j = 0; j < NTP; ++j) {
+        const int t = NTP * half + j;
+        const int sl = t - d.ta0;   // the slot of (m0, t), read clamped and masked
+        const float e0 = (unsigned)sl < (unsigned)d.na ? s_E[min(max(sl, 0), 63) * ES + qx] : 0.f;
+        dqt[j] = fmaf(e0, q0, dqt[j]);
+        d0 = fmaf(e0, qt[j], d0);
+      }
+      if (d.nb > 0) {
+#pragma unroll
+        for (int j = 0; j < NTP; ++j) {
+          const int t = NTP * half + j;
+          const int sl = t - d.tb0;   // (m1, t) is slot na + sl
+          const float e1 = (unsigned)sl < (unsigned)d.nb ? s_E[min(d.na + max(sl, 0), 63) * ES + qx] : 0.f;
+          dqt[j] = fmaf(e1, q1, dqt[j]);
+          d1 = fmaf(e1, qt[j], d1);
+        }
+      }
+      d0 += __shfl_xor(d0, 1, 64);   // the token's parts are adjacent lanes
+      d1 += __shfl_xor(d1, 1, 64);
+      if (SP == 4) {
+        d0 += __shfl_xor(d0, 2, 64);
+        d1 += __shfl_xor(d1, 2, 64);
+      }
+      if (half == 0) {
+        if (d.m0 < DH) s_rd[qx * (DH + 1) + d.m0] = d0;
+        if (d.nb > 0) s_rd[qx * (DH + 1) + d.m1] = d1;
+      }
     }
-  }
-  __syncthreads();
-  if (active) {   // each part writes DH / SP entries, the parts' rows added in order
-    float* o = dq + (qrow0 + qx) * DH + half * (DH / SP);
+    __syncthreads();
+    if (active) {   // each part writes its NTP entries
+      float* o = dq + (qrow0 + qx) * DH + NTP * half;
 #pragma unroll
-    for (int d = 0; d < DH / SP; ++d) {
-      float x = 0.f;
-#pragma unroll
-      for (int h = 0; h < SP; ++h) x += s_dq[(h * chunk + qx) * (DH + 1) + half * (DH / SP) + d];
-      o[d] = x;
+      for (int j = 0; j < NTP; ++j) o[j] = dqt[j] + s_rd[qx * (DH + 1) + NTP * half + j];
     }
   }
 }
@@ -1274,7 +1310,7 @@ static oal_status backward_typed(int batch, int n_q_heads, int n_kv_heads, int s
     // the kernel's state staging assumes SP * chunk = 256
     const int sp = chunk <= 64 ? 4 : 2;
     if (sp * chunk != 256) return set_error(OAL_ERR_INVALID_ARG, "k_bwd_query: chunk %d", chunk);
-    const size_t smem = sizeof(float) * ((size_t)(1 + sp) * chunk * (DH + 1) + 32 * WP + 32 +
+    const size_t smem = sizeof(float) * ((size_t)(1 + sp) * chunk * (DH + 1) +
                                          TB * (DH + 1) + TB * WP + DH + DH * DH);
     const void* fn = sp == 4 ? reinterpret_cast<const void*>(&k_bwd_query<T, 4>)
                              : reinterpret_cast<const void*>(&k_bwd_query<T, 2>);
