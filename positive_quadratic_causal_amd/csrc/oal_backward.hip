@@ -22,7 +22,9 @@
 //
 // Kernels, in launch order:
 //   prefix build + scan (oal_prefill_vec.hip)  H_{<c}
-//   k_bwd_query     four (chunk 64) or two threads per query: recompute u~_i, g_i; dq_i; alpha rows
+//   k_bwd_query     four (chunk 64) or two threads per query: recompute u~_i, g_i; the pair
+//                   part of dq_i; alpha rows
+//   k_bwd_dqstate   the state part of dq_i: H_{<c} g_i against d psi(q_i) / dq_i, by pair rows
 //   k_bwd_rbuild    per chunk: sum_h c_f psi_f(q_i) g_i^T (suffix deltas) and the
 //                   state part of dc: sum_i psi_f(q_i) (H_{<c} g_i)_f
 //   k_bwd_rscan     exclusive suffix sums over chunks: R_{>c}
@@ -50,6 +52,14 @@ __device__ __forceinline__ fx16 mfma_f32(float a, float b, fx16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
 }
 __device__ __forceinline__ int mrow(int i, int h) { return 8 * (i >> 2) + 4 * h + (i & 3); }
+
+// x of the lane whose index differs in bit 0 (bit 1): DPP quad permutations
+__device__ __forceinline__ float lane_xor1(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float lane_xor2(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false));
+}
 
 // feature f of the canonical order: kind 0 constant, 1 linear x_r, 2 pair x_r x_t,
 // 3 padding
@@ -112,6 +122,12 @@ __device__ __forceinline__ int row_block_feature(int blk, const RowBlk& d, int s
     return 1 + DH + pair_row_start(d.m1) + (t - d.m1);
   }
   return -1;
+}
+
+// record index of c_f for a feature f < DCAN (no branch: for loads that must not
+// wait in a divergent block)
+__device__ __forceinline__ int coef_index(int f) {
+  return f == 0 ? OAL_COEF_A : (f <= DH ? OAL_COEF_BP + f - 1 : OAL_COEF_CP + f - 1 - DH);
 }
 
 __device__ __forceinline__ float coef_of(const float* rec, int f) {
@@ -356,10 +372,6 @@ k_bwd_query(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunks,
   float* s_u = s_k + TB * (DH + 1);           // [TB][WP]
   float* s_b = s_u + TB * WP;                 // [DH]  b'
   float* s_S = s_b + DH;                      // [DH][DH]  C / d_h (symmetric)
-  // step 4 only, in the staged keys' and values' rows: a row block of H_{<c} and its c_f
-  float* s_H = s_k;                           // [64][WPH]
-  float* s_cf = s_k + 64 * WPH;               // [64]
-  static_assert(64 * WPH + 64 <= TB * (DH + 1) + TB * WP, "a row block fits the staged rows");
 
   const float* rec = coef_rec(coeffs, hq);
   const float a = rec[OAL_COEF_A];
@@ -397,33 +409,6 @@ k_bwd_query(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunks,
   const float* Hc = hc + ((size_t)unit * n_chunks + c) * STATE_FLOATS;
   const size_t kbase = (size_t)unit * seq_len + t0;
 
-  // the row blocks of H_{<c} pass through registers one block ahead of the LDS
-  // copy the threads work on: thread tid moves slot tid % 64 of channels
-  // tid / 64 + 4 e (nthr = 256)
-  constexpr int PB = (64 * W + 255) / 256;
-  float pre[PB], pcf = 0.f;
-  auto fetch_block = [&](int blk) {
-    const RowBlk d = row_block(blk);
-    const int fs = row_block_feature(blk, d, tid & 63);
-#pragma unroll
-    for (int e = 0; e < PB; ++e) {
-      const int w = (tid >> 6) + 4 * e;
-      if (w < W) pre[e] = fs >= 0 ? Hc[(size_t)w * DS + fs] : 0.f;
-    }
-    if (tid < 64) pcf = fs >= 0 ? coef_of(rec, fs) : 0.f;
-  };
-  auto stage_block = [&](int blk) {
-#pragma unroll
-    for (int e = 0; e < PB; ++e) {
-      const int w = (tid >> 6) + 4 * e;
-      if (w < W) s_H[(tid & 63) * WPH + w] = pre[e];
-    }
-    if (tid < 64) {
-      s_cf[tid] = pcf;
-      s_H[tid * WPH + W] = 0.f;   // channel 65 of the last channel pair
-    }
-    if (blk + 1 < NRB) fetch_block(blk + 1);
-  };
   auto stage_keys = [&](int j0, int nj) {
     for (int i = tid; i < TB * DH; i += nthr) {
       const int jj = i / DH, d = i % DH;
@@ -652,126 +637,200 @@ k_bwd_query(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunks,
       if (jj >= jmax) arow[j0 + jj] = 0.f;
   }
 
-  // ---- 4. state part of dq: dq_i += sum_f c_f (H_{<c} g_i)_f d psi_f(q_i) / dq_i,
-  // by the row blocks above.  Per block, D[f][tok] = sum_w H_{<c}[f][w] g_tok[w] on
-  // the fp32 matrix cores (M = the block's 64 slots, N = tokens, K = channels; g of
-  // the chunk read once into registers as B operands) and E = c_f D goes to LDS by
-  // slot, E[slot][tok].  A pair (m, t) of a row adds E q_m to dq[t] (the
-  // t side: each thread keeps its DH / SP entries of dq in registers, so a row is a
-  // masked multiply-add over them) and E q_t to dq[m] (the m side: a dot product over
-  // t, summed over the token's parts; every m < DH receives exactly one, stored to
-  // LDS).  The diagonal (m, m) thus gets 2 E q_m; the linear features' m side (the
-  // constant slot) is dropped.  Chunk 64: wave = (feature tile wave % 2, token tile
-  // wave / 2); chunk 128: wave = token tile, both feature tiles.
-  {
-    constexpr int GS = W + 1;                    // g row: channels 0..64 and a zero
-    constexpr int NJ = (W + 1) / 2;              // 33 channel pairs
-    constexpr int NFT = SP == 4 ? 1 : 2;         // feature tiles per wave
-    constexpr int NTP = DH / SP;                 // dq entries per thread
-    const int ES = chunk + 1;                    // E row stride (bank spread)
-    float* s_g = s_k;                            // [chunk][GS], until g is in registers (then s_H)
-    float* s_E = s_dq;                           // [64 slots][ES], after the dq rows are read
-    float* s_rd = s_dq + 64 * ES;                // [chunk][DH + 1] the m-side sums
-    static_assert((256 / SP) * GS <= TB * (DH + 1) + TB * WP, "the g tile fits the staged rows");
-    static_assert(64 * (256 / SP + 1) + (256 / SP) * (DH + 1) <= SP * (256 / SP) * (DH + 1),
-                  "E and the m-side sums fit the dq rows");
-    __syncthreads();   // step 3's reads of the staged keys and values and its dq sums are done
-    if (half == 0) {
+  __syncthreads();
+  if (active) {   // each part writes DH / SP entries, the parts' rows added in order
+    float* o = dq + (qrow0 + qx) * DH + half * (DH / SP);
 #pragma unroll
-      for (int w = 0; w < W; ++w) s_g[qx * GS + w] = g[w];
-      s_g[qx * GS + W] = 0.f;
-    }
-    // this thread's dq entries NTP half + j: the parts' rows summed in order
-    float dqt[NTP], qt[NTP];
-#pragma unroll
-    for (int j = 0; j < NTP; ++j) {
+    for (int d = 0; d < DH / SP; ++d) {
       float x = 0.f;
 #pragma unroll
-      for (int h = 0; h < SP; ++h) x += s_dq[(h * chunk + qx) * (DH + 1) + NTP * half + j];
-      dqt[j] = x;
-      qt[j] = qi[NTP * half + j];
+      for (int h = 0; h < SP; ++h) x += s_dq[(h * chunk + qx) * (DH + 1) + half * (DH / SP) + d];
+      o[d] = x;
     }
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
-    const int TT = SP == 4 ? (wave >> 1) : wave;
-    const int FT0 = SP == 4 ? (wave & 1) : 0;
-    const int hout = lane >> 5;
-    const int tok = 32 * TT + (lane & 31);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// State part of dq:  dq_i += sum_f c_f (H_{<c} g_i)_f d psi_f(q_i) / dq_i, added to
+// the pair part the query kernel wrote.  Block (32 tokens of a chunk, chunk, query
+// head), two waves; the features by the row blocks above.  Per block,
+// D[f][tok] = sum_w H_{<c}[f][w] g_tok[w] on the fp32 matrix cores (wave = tile of
+// 32 slots, N = the 32 tokens, K = channels; g read once into registers as B
+// operands) and E = c_f D goes to LDS by slot.  Four threads per token each own
+// DH / 4 entries of dq in registers: a pair (m, t) of a row adds E q_m to dq[t] (the
+// t side, a masked multiply-add over the thread's entries) and E q_t to dq[m] (the m
+// side, a dot product over t summed over the parts; every m < DH receives exactly
+// one, stored to LDS).  The diagonal (m, m) thus gets 2 E q_m; the linear features'
+// m side (the constant slot q~[64] = 1) is dropped.  The row blocks of H_{<c} and
+// the multipliers q_m pass through registers one block ahead.  The blocks of one
+// (unit, chunk) share an XCD (workgroup id % 8), so its state is read through one L2.
+constexpr int DQ_TG = 32;   // tokens per block
+template <typename T>
+__global__ void __launch_bounds__(128)
+k_bwd_dqstate(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunks, int n_units,
+              const T* __restrict__ q, const void* __restrict__ coeffs,
+              const float* __restrict__ gbuf, const float* __restrict__ hc, float* __restrict__ dq) {
+  constexpr int TG = DQ_TG;
+  constexpr int NTP = DH / 4;            // dq entries per thread
+  constexpr int ES = TG + 1;             // E row stride (bank spread)
+  constexpr int GS = W + 1;              // g row: channels 0..64 and a zero
+  constexpr int NJ = (W + 1) / 2;        // 33 channel pairs
+  constexpr int PB = (64 * W + 127) / 128;
+  const int rep = n_q_heads / n_kv_heads;
+  const int per = rep * (chunk / TG);    // blocks of one (unit, chunk)
+  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  const int uc = (slot / per) * 8 + xcd;
+  if (uc >= n_units * n_chunks) return;
+  const int unit = uc / n_chunks, c = uc % n_chunks;
+  const int b = unit / n_kv_heads;
+  const int hq = (unit % n_kv_heads) * rep + (slot % per) % rep;
+  const int t0 = c * chunk + ((slot % per) / rep) * TG;
+  const int ntok = min(TG, seq_len - t0);
+  if (ntok <= 0) return;                 // a group past the sequence (whole block)
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int FT = __builtin_amdgcn_readfirstlane(tid >> 6);   // the wave's feature tile
+  const int qx = tid >> 2, half = tid & 3;                    // token and part
+  const int hout = lane >> 5, tok = lane & 31;                // matrix-core roles
+
+  // one array, in this order (the masked reads below rely on s_H before s_E and
+  // s_rd after it)
+  __shared__ __attribute__((aligned(16))) float sm[64 * WPH + 64 + 64 * ES + TG * DH];
+  float* s_H = sm;                       // [64][WPH] a row block of H_{<c}
+  float* s_cf = s_H + 64 * WPH;          // [64] its c_f
+  float* s_E = s_cf + 64;                // [64][ES] E[slot][tok]; first the g tile [TG][GS]
+  float* s_rd = s_E + 64 * ES;           // [TG][DH] the m-side sums
+  static_assert(TG * GS <= 64 * ES, "the g tile fits the E rows");
+  static_assert(63 * ES <= 64 * WPH + 64, "reads up to 63 slots before s_E stay in s_H");
+  float* s_g = s_E;
+
+  const float* rec = coef_rec(coeffs, hq);
+  const float* Hc = hc + ((size_t)unit * n_chunks + c) * STATE_FLOATS;
+  const size_t row0 = ((size_t)b * n_q_heads + hq) * seq_len + t0;     // q and dq rows
+  const float* grow = gbuf + (((size_t)b * n_q_heads + hq) * ((size_t)n_chunks * chunk) + t0) * WP;
+  const bool active = qx < ntok;
+  const T* qrow = q + (row0 + (active ? qx : 0)) * DH;
+
+  for (int i = tid; i < TG * GS; i += 128) {
+    const int r = i / GS, w = i % GS;
+    s_g[i] = r < ntok && w < W ? grow[(size_t)r * WP + w] : 0.f;
+  }
+  float qt[NTP];   // this thread's q entries NTP half + j
+#pragma unroll
+  for (int j = 0; j < NTP; ++j) qt[j] = active ? Elem<T>::load(qrow, NTP * half + j) : 0.f;
+  float dqt[NTP];
+#pragma unroll
+  for (int j = 0; j < NTP; ++j) dqt[j] = 0.f;
+  __syncthreads();
+  float gv[NJ];    // B operands: g[tok][2 j + lane / 32]
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) gv[j] = s_g[tok * GS + 2 * j + hout];
+
+  // thread tid moves slot tid % 64 of channels tid / 64 + 2 e.  Every load is
+  // unconditional (clamped index) and its value is kept raw until the next block
+  // uses it, where the selects drop what is not wanted: a load in a divergent block,
+  // or a value used right after its load, is awaited at once, and with it (the
+  // counter drains in order) every load still in flight.
+  float pre[PB], pcf = 0.f;
+  T pq0, pq1;
+  bool pok = false, pm0 = false, pm1 = false;
+  auto fetch_block = [&](int blk) {
+    const RowBlk d = row_block(blk);
+    const int fs = row_block_feature(blk, d, tid & 63);
+    const float* hp = Hc + max(fs, 0);   // an empty slot reads feature 0
+#pragma unroll
+    for (int e = 0; e < PB; ++e) {
+      const int w = (tid >> 6) + 2 * e;
+      pre[e] = hp[(size_t)min(w, W - 1) * DS];
+    }
+    pcf = rec[coef_index(max(fs, 0))];
+    pq0 = qrow[min(d.m0, DH - 1)];
+    pq1 = qrow[min(d.m1, DH - 1)];
+    pok = fs >= 0;
+    pm0 = d.m0 < DH && active;
+    pm1 = d.m1 < DH && active;
+  };
+  fetch_block(0);
+  for (int blk = 0; blk < NRB; ++blk) {
+    const RowBlk d = row_block(blk);
+    __syncthreads();   // the last block's E rows have been read (and, first, the g tile)
+#pragma unroll
+    for (int e = 0; e < PB; ++e) {
+      const int w = (tid >> 6) + 2 * e;
+      if (w < W) s_H[(tid & 63) * WPH + w] = pok ? pre[e] : 0.f;
+    }
+    if (tid < 64) {
+      s_cf[tid] = pok ? pcf : 0.f;
+      s_H[tid * WPH + W] = 0.f;   // channel 65 of the last channel pair
+    }
+    const float q0 = pm0 ? Elem<T>::load(&pq0, 0) : 1.f;
+    const float q1 = pm1 ? Elem<T>::load(&pq1, 0) : 1.f;
+    if (blk + 1 < NRB) fetch_block(blk + 1);
     __syncthreads();
-    float gv[NJ];   // B operands: g[tok][2 j + lane / 32]
+    if (32 * FT < d.na + d.nb) {   // else an empty tile (the column block)
+      fx16 D[2];
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) gv[j] = s_g[tok * GS + 2 * j + hout];
-    const float* hrow = s_H + (lane & 31) * WPH + hout;   // A: H[slot lane % 32][2 j + lane / 32]
-    fetch_block(0);
-    for (int blk = 0; blk < NRB; ++blk) {
-      const RowBlk d = row_block(blk);
-      __syncthreads();   // also: the last block's E rows have been read
-      stage_block(blk);
-      __syncthreads();
+      for (int x = 0; x < 2; ++x)
 #pragma unroll
-      for (int ft = 0; ft < NFT; ++ft) {
-        const int FT = FT0 + ft;
-        if (32 * FT >= d.na + d.nb) continue;   // an empty tile (the column block)
-        fx16 D[2];
+        for (int i = 0; i < 16; ++i) D[x][i] = 0.f;
+      const float* ha = s_H + (32 * FT + tok) * WPH + hout;   // A: H[slot][2 j + lane / 32]
 #pragma unroll
-        for (int x = 0; x < 2; ++x)
+      for (int j0 = 0; j0 < NJ; j0 += 8) {
+        float av[8];
 #pragma unroll
-          for (int i = 0; i < 16; ++i) D[x][i] = 0.f;
-        const float* ha = hrow + 32 * FT * WPH;
+        for (int jj = 0; jj < 8; ++jj)
+          if (j0 + jj < NJ) av[jj] = ha[2 * (j0 + jj)];
 #pragma unroll
-        for (int j0 = 0; j0 < NJ; j0 += 8) {
-          float av[8];
-#pragma unroll
-          for (int jj = 0; jj < 8; ++jj)
-            if (j0 + jj < NJ) av[jj] = ha[2 * (j0 + jj)];
-#pragma unroll
-          for (int jj = 0; jj < 8; ++jj)
-            if (j0 + jj < NJ) D[jj & 1] = mfma_f32(av[jj], gv[j0 + jj], D[jj & 1]);
-        }
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int sl = 32 * FT + mrow(i, hout);
-          if (sl < d.na + d.nb) s_E[sl * ES + tok] = s_cf[sl] * (D[0][i] + D[1][i]);
-        }
+        for (int jj = 0; jj < 8; ++jj)
+          if (j0 + jj < NJ) D[jj & 1] = mfma_f32(av[jj], gv[j0 + jj], D[jj & 1]);
       }
-      __syncthreads();
-      // t side into the registers, m side as dot products (masked to the rows' runs)
-      const float q0 = qi[d.m0], q1 = qi[d.m1];
-      float d0 = 0.f, d1 = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int sl = 32 * FT + mrow(i, hout);
+        s_E[sl * ES + tok] = s_cf[sl] * (D[0][i] + D[1][i]);   // every slot of a tile is used
+      }
+    }
+    __syncthreads();
+    // t side into the registers, m side as dot products, masked to the rows' runs.
+    // Slot t - ta0 of row 0 and na + t - tb0 of row 1 are read for every t of the
+    // thread; outside a run they lie in [-63, 64] slots from s_E, inside s_H before
+    // it or s_rd after it, and are dropped.
+    float d0 = 0.f, d1 = 0.f;
+    {
+      const int lo = d.ta0 - NTP * half;           // j of the run's first t
+      const float* ep = s_E + (NTP * half - d.ta0) * ES + qx;
 #pragma unroll
       for (int j = 0; j < NTP; ++j) {
-        const int t = NTP * half + j;
-        const int sl = t - d.ta0;   // the slot of (m0, t), read clamped and masked
-        const float e0 = (unsigned)sl < (unsigned)d.na ? s_E[min(max(sl, 0), 63) * ES + qx] : 0.f;
+        const float r = ep[j * ES];
+        const float e0 = (unsigned)(j - lo) < (unsigned)d.na ? r : 0.f;
         dqt[j] = fmaf(e0, q0, dqt[j]);
         d0 = fmaf(e0, qt[j], d0);
       }
-      if (d.nb > 0) {
+    }
+    if (d.nb > 0) {
+      const int lo = d.tb0 - NTP * half;
+      const float* ep = s_E + (d.na + NTP * half - d.tb0) * ES + qx;
 #pragma unroll
-        for (int j = 0; j < NTP; ++j) {
-          const int t = NTP * half + j;
-          const int sl = t - d.tb0;   // (m1, t) is slot na + sl
-          const float e1 = (unsigned)sl < (unsigned)d.nb ? s_E[min(d.na + max(sl, 0), 63) * ES + qx] : 0.f;
-          dqt[j] = fmaf(e1, q1, dqt[j]);
-          d1 = fmaf(e1, qt[j], d1);
-        }
-      }
-      d0 += __shfl_xor(d0, 1, 64);   // the token's parts are adjacent lanes
-      d1 += __shfl_xor(d1, 1, 64);
-      if (SP == 4) {
-        d0 += __shfl_xor(d0, 2, 64);
-        d1 += __shfl_xor(d1, 2, 64);
-      }
-      if (half == 0) {
-        if (d.m0 < DH) s_rd[qx * (DH + 1) + d.m0] = d0;
-        if (d.nb > 0) s_rd[qx * (DH + 1) + d.m1] = d1;
+      for (int j = 0; j < NTP; ++j) {
+        const float r = ep[j * ES];
+        const float e1 = (unsigned)(j - lo) < (unsigned)d.nb ? r : 0.f;
+        dqt[j] = fmaf(e1, q1, dqt[j]);
+        d1 = fmaf(e1, qt[j], d1);
       }
     }
-    __syncthreads();
-    if (active) {   // each part writes its NTP entries
-      float* o = dq + (qrow0 + qx) * DH + NTP * half;
-#pragma unroll
-      for (int j = 0; j < NTP; ++j) o[j] = dqt[j] + s_rd[qx * (DH + 1) + NTP * half + j];
+    d0 += lane_xor1(d0);   // the token's parts are the lanes of one quad
+    d1 += lane_xor1(d1);
+    d0 += lane_xor2(d0);
+    d1 += lane_xor2(d1);
+    if (half == 0) {
+      if (d.m0 < DH) s_rd[qx * DH + d.m0] = d0;
+      if (d.nb > 0) s_rd[qx * DH + d.m1] = d1;
     }
+  }
+  __syncthreads();
+  if (active) {
+    float* o = dq + (row0 + qx) * DH + NTP * half;
+#pragma unroll
+    for (int j = 0; j < NTP; ++j) o[j] += dqt[j] + s_rd[qx * DH + NTP * half + j];
   }
 }
 
@@ -1327,6 +1386,14 @@ static oal_status backward_typed(int batch, int n_q_heads, int n_kv_heads, int s
                          stream, n_q_heads, n_kv_heads, seq_len, chunk, n_chunks, units, qq, kk, vv, coeffs, dy,
                          w.hc, w.gbuf, w.alpha, dq);
     if ((st = check_launch("k_bwd_query")) != OAL_OK) return st;
+  }
+  {
+    const int per = (n_q_heads / n_kv_heads) * (chunk / DQ_TG);
+    const dim3 grid((unsigned)(((size_t)units * n_chunks + 7) / 8 * 8 * (size_t)per));
+    ProfScope ps("k_bwd_dqstate", stream);
+    hipLaunchKernelGGL(k_bwd_dqstate<T>, grid, dim3(128), 0, stream, n_q_heads, n_kv_heads, seq_len,
+                       chunk, n_chunks, units, qq, coeffs, w.gbuf, w.hc, dq);
+    if ((st = check_launch("k_bwd_dqstate")) != OAL_OK) return st;
   }
   {
     ProfScope ps("k_bwd_rbuild", stream);
