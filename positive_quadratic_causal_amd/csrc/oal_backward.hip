@@ -654,16 +654,19 @@ k_bwd_query(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunks,
 // State part of dq:  dq_i += sum_f c_f (H_{<c} g_i)_f d psi_f(q_i) / dq_i, added to
 // the pair part the query kernel wrote.  Block (32 tokens of a chunk, chunk, query
 // head), two waves; the features by the row blocks above.  Per block,
-// D[f][tok] = sum_w H_{<c}[f][w] g_tok[w] on the fp32 matrix cores (wave = tile of
-// 32 slots, N = the 32 tokens, K = channels; g read once into registers as B
-// operands) and E = c_f D goes to LDS by slot.  Four threads per token each own
-// DH / 4 entries of dq in registers: a pair (m, t) of a row adds E q_m to dq[t] (the
-// t side, a masked multiply-add over the thread's entries) and E q_t to dq[m] (the m
-// side, a dot product over t summed over the parts; every m < DH receives exactly
-// one, stored to LDS).  The diagonal (m, m) thus gets 2 E q_m; the linear features'
-// m side (the constant slot q~[64] = 1) is dropped.  The row blocks of H_{<c} and
-// the multipliers q_m pass through registers one block ahead.  The blocks of one
-// (unit, chunk) share an XCD (workgroup id % 8), so its state is read through one L2.
+// E[f][tok] = sum_w c_f H_{<c}[f][w] g_tok[w] on the fp32 matrix cores (wave = tile
+// of 32 slots, N = the 32 tokens, K = channels): each lane loads its A operands,
+// c_f H_{<c}[slot][2 j + lane / 32], straight from the state (the slots of a row run
+// are consecutive features, so the loads coalesce), a block ahead of their use; g is
+// read once into registers as the B operands.  E goes to LDS by slot, in two
+// buffers, so one barrier per block separates the products from the update.  Four
+// threads per token each own DH / 4 entries of dq in registers: a pair (m, t) of a
+// row adds E q_m to dq[t] (the t side, a masked multiply-add over the thread's
+// entries) and E q_t to dq[m] (the m side, a dot product over t summed over the
+// parts; every m < DH receives exactly one, stored to LDS).  The diagonal (m, m)
+// thus gets 2 E q_m; the linear features' m side (the constant slot q~[64] = 1) is
+// dropped.  The blocks of one (unit, chunk) share an XCD (workgroup id % 8), so its
+// state is read through one L2.
 constexpr int DQ_TG = 32;   // tokens per block
 template <typename T>
 __global__ void __launch_bounds__(128)
@@ -673,9 +676,9 @@ k_bwd_dqstate(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunk
   constexpr int TG = DQ_TG;
   constexpr int NTP = DH / 4;            // dq entries per thread
   constexpr int ES = TG + 1;             // E row stride (bank spread)
+  constexpr int RS = DH + 1;             // m-side row stride
   constexpr int GS = W + 1;              // g row: channels 0..64 and a zero
   constexpr int NJ = (W + 1) / 2;        // 33 channel pairs
-  constexpr int PB = (64 * W + 127) / 128;
   const int rep = n_q_heads / n_kv_heads;
   const int per = rep * (chunk / TG);    // blocks of one (unit, chunk)
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
@@ -692,16 +695,15 @@ k_bwd_dqstate(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunk
   const int qx = tid >> 2, half = tid & 3;                    // token and part
   const int hout = lane >> 5, tok = lane & 31;                // matrix-core roles
 
-  // one array, in this order (the masked reads below rely on s_H before s_E and
-  // s_rd after it)
-  __shared__ __attribute__((aligned(16))) float sm[64 * WPH + 64 + 64 * ES + TG * DH];
-  float* s_H = sm;                       // [64][WPH] a row block of H_{<c}
-  float* s_cf = s_H + 64 * WPH;          // [64] its c_f
-  float* s_E = s_cf + 64;                // [64][ES] E[slot][tok]; first the g tile [TG][GS]
-  float* s_rd = s_E + 64 * ES;           // [TG][DH] the m-side sums
-  static_assert(TG * GS <= 64 * ES, "the g tile fits the E rows");
-  static_assert(63 * ES <= 64 * WPH + 64, "reads up to 63 slots before s_E stay in s_H");
-  float* s_g = s_E;
+  // one array, in this order: the masked reads of an E buffer reach up to 63 slots
+  // before it (s_rd, or the other buffer) and one slot after it (the other buffer,
+  // or the tail)
+  __shared__ __attribute__((aligned(16))) float sm[TG * RS + 2 * 64 * ES + TG];
+  float* s_rd = sm;                      // [TG][RS] the m-side sums
+  float* s_E0 = s_rd + TG * RS;          // [2][64][ES] E[slot][tok]; first the g tile [TG][GS]
+  static_assert(TG * GS <= 64 * ES, "the g tile fits an E buffer");
+  static_assert(63 * ES <= TG * RS && TG <= 64 * ES, "masked reads stay in the array");
+  float* s_g = s_E0;
 
   const float* rec = coef_rec(coeffs, hq);
   const float* Hc = hc + ((size_t)unit * n_chunks + c) * STATE_FLOATS;
@@ -721,79 +723,63 @@ k_bwd_dqstate(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunk
 #pragma unroll
   for (int j = 0; j < NTP; ++j) dqt[j] = 0.f;
   __syncthreads();
-  float gv[NJ];    // B operands: g[tok][2 j + lane / 32]
+  float gv[NJ];    // B operands: g[tok][2 j + lane / 32] (channel 65: zero)
 #pragma unroll
   for (int j = 0; j < NJ; ++j) gv[j] = s_g[tok * GS + 2 * j + hout];
 
-  // thread tid moves slot tid % 64 of channels tid / 64 + 2 e.  Every load is
+  // A operands of the next block, c_f and the multipliers q_m.  Every load is
   // unconditional (clamped index) and its value is kept raw until the next block
   // uses it, where the selects drop what is not wanted: a load in a divergent block,
   // or a value used right after its load, is awaited at once, and with it (the
   // counter drains in order) every load still in flight.
-  float pre[PB], pcf = 0.f;
+  float na[NJ], ncf = 0.f;
   T pq0, pq1;
-  bool pok = false, pm0 = false, pm1 = false;
+  bool nok = false, pm0 = false, pm1 = false;
   auto fetch_block = [&](int blk) {
     const RowBlk d = row_block(blk);
-    const int fs = row_block_feature(blk, d, tid & 63);
+    const int fs = row_block_feature(blk, d, 32 * FT + tok);
     const float* hp = Hc + max(fs, 0);   // an empty slot reads feature 0
 #pragma unroll
-    for (int e = 0; e < PB; ++e) {
-      const int w = (tid >> 6) + 2 * e;
-      pre[e] = hp[(size_t)min(w, W - 1) * DS];
-    }
-    pcf = rec[coef_index(max(fs, 0))];
+    for (int j = 0; j < NJ; ++j) na[j] = hp[(size_t)min(2 * j + hout, W - 1) * DS];   // channel 65: any finite value
+    ncf = rec[coef_index(max(fs, 0))];
     pq0 = qrow[min(d.m0, DH - 1)];
     pq1 = qrow[min(d.m1, DH - 1)];
-    pok = fs >= 0;
+    nok = fs >= 0;
     pm0 = d.m0 < DH && active;
     pm1 = d.m1 < DH && active;
   };
   fetch_block(0);
+  __syncthreads();   // the g tile has been read: the E buffers are free
   for (int blk = 0; blk < NRB; ++blk) {
     const RowBlk d = row_block(blk);
-    __syncthreads();   // the last block's E rows have been read (and, first, the g tile)
+    float* s_E = s_E0 + (blk & 1) * 64 * ES;
+    // this block's A operands (scaled by c_f, zero for an empty slot) and multipliers
+    const float cf = nok ? ncf : 0.f;
+    float av[NJ];
 #pragma unroll
-    for (int e = 0; e < PB; ++e) {
-      const int w = (tid >> 6) + 2 * e;
-      if (w < W) s_H[(tid & 63) * WPH + w] = pok ? pre[e] : 0.f;
-    }
-    if (tid < 64) {
-      s_cf[tid] = pok ? pcf : 0.f;
-      s_H[tid * WPH + W] = 0.f;   // channel 65 of the last channel pair
-    }
+    for (int j = 0; j < NJ; ++j) av[j] = cf * na[j];
     const float q0 = pm0 ? Elem<T>::load(&pq0, 0) : 1.f;
     const float q1 = pm1 ? Elem<T>::load(&pq1, 0) : 1.f;
     if (blk + 1 < NRB) fetch_block(blk + 1);
-    __syncthreads();
     if (32 * FT < d.na + d.nb) {   // else an empty tile (the column block)
       fx16 D[2];
 #pragma unroll
       for (int x = 0; x < 2; ++x)
 #pragma unroll
         for (int i = 0; i < 16; ++i) D[x][i] = 0.f;
-      const float* ha = s_H + (32 * FT + tok) * WPH + hout;   // A: H[slot][2 j + lane / 32]
 #pragma unroll
-      for (int j0 = 0; j0 < NJ; j0 += 8) {
-        float av[8];
+      for (int j = 0; j < NJ; ++j) D[j & 1] = mfma_f32(av[j], gv[j], D[j & 1]);
 #pragma unroll
-        for (int jj = 0; jj < 8; ++jj)
-          if (j0 + jj < NJ) av[jj] = ha[2 * (j0 + jj)];
-#pragma unroll
-        for (int jj = 0; jj < 8; ++jj)
-          if (j0 + jj < NJ) D[jj & 1] = mfma_f32(av[jj], gv[j0 + jj], D[jj & 1]);
-      }
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int sl = 32 * FT + mrow(i, hout);
-        s_E[sl * ES + tok] = s_cf[sl] * (D[0][i] + D[1][i]);   // every slot of a tile is used
-      }
+      for (int i = 0; i < 16; ++i)   // every slot of a non-empty tile is used
+        s_E[(32 * FT + mrow(i, hout)) * ES + tok] = D[0][i] + D[1][i];
     }
+    // one barrier: this block's E is complete, and the buffer written next (the
+    // block after) was last read two blocks back
     __syncthreads();
     // t side into the registers, m side as dot products, masked to the rows' runs.
     // Slot t - ta0 of row 0 and na + t - tb0 of row 1 are read for every t of the
-    // thread; outside a run they lie in [-63, 64] slots from s_E, inside s_H before
-    // it or s_rd after it, and are dropped.
+    // thread; outside a run they lie in [-63, 64] slots from s_E, inside the array,
+    // and are dropped.
     float d0 = 0.f, d1 = 0.f;
     {
       const int lo = d.ta0 - NTP * half;           // j of the run's first t
@@ -822,15 +808,15 @@ k_bwd_dqstate(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunk
     d0 += lane_xor2(d0);
     d1 += lane_xor2(d1);
     if (half == 0) {
-      if (d.m0 < DH) s_rd[qx * DH + d.m0] = d0;
-      if (d.nb > 0) s_rd[qx * DH + d.m1] = d1;
+      if (d.m0 < DH) s_rd[qx * RS + d.m0] = d0;
+      if (d.nb > 0) s_rd[qx * RS + d.m1] = d1;
     }
   }
   __syncthreads();
   if (active) {
     float* o = dq + (row0 + qx) * DH + NTP * half;
 #pragma unroll
-    for (int j = 0; j < NTP; ++j) o[j] += dqt[j] + s_rd[qx * DH + NTP * half + j];
+    for (int j = 0; j < NTP; ++j) o[j] += dqt[j] + s_rd[qx * RS + NTP * half + j];
   }
 }
 
