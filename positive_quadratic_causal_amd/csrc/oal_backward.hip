@@ -727,52 +727,49 @@ k_bwd_dqstate(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunk
 #pragma unroll
   for (int j = 0; j < NJ; ++j) gv[j] = s_g[tok * GS + 2 * j + hout];
 
-  // A operands of the next block, c_f and the multipliers q_m.  Every load is
-  // unconditional (clamped index) and its value is kept raw until the next block
-  // uses it, where the selects drop what is not wanted: a load in a divergent block,
-  // or a value used right after its load, is awaited at once, and with it (the
-  // counter drains in order) every load still in flight.
-  float na[NJ], ncf = 0.f;
-  T pq0, pq1;
-  bool nok = false, pm0 = false, pm1 = false;
-  auto fetch_block = [&](int blk) {
+  // A operands, c_f and the multipliers q_m of a row block, loaded two blocks ahead
+  // into one of two register sets (the loop is unrolled by two).  Every load is
+  // unconditional (clamped index) and its value is kept raw until its block uses
+  // it, where the selects drop what is not wanted: a load in a divergent block, or a
+  // value used right after its load, is awaited at once, and with it (the counter
+  // drains in order) every load still in flight.
+  struct Ops {
+    float a[NJ], cf;
+    T q0, q1;
+    bool ok, m0, m1;
+  };
+  auto fetch_block = [&](int blk, Ops& o) __attribute__((always_inline)) {
     const RowBlk d = row_block(blk);
     const int fs = row_block_feature(blk, d, 32 * FT + tok);
     const float* hp = Hc + max(fs, 0);   // an empty slot reads feature 0
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) na[j] = hp[(size_t)min(2 * j + hout, W - 1) * DS];   // channel 65: any finite value
-    ncf = rec[coef_index(max(fs, 0))];
-    pq0 = qrow[min(d.m0, DH - 1)];
-    pq1 = qrow[min(d.m1, DH - 1)];
-    nok = fs >= 0;
-    pm0 = d.m0 < DH && active;
-    pm1 = d.m1 < DH && active;
+    for (int j = 0; j < NJ; ++j) o.a[j] = hp[(size_t)min(2 * j + hout, W - 1) * DS];   // channel 65: any finite value
+    o.cf = rec[coef_index(max(fs, 0))];
+    o.q0 = qrow[min(d.m0, DH - 1)];
+    o.q1 = qrow[min(d.m1, DH - 1)];
+    o.ok = fs >= 0;
+    o.m0 = d.m0 < DH && active;
+    o.m1 = d.m1 < DH && active;
   };
-  fetch_block(0);
-  __syncthreads();   // the g tile has been read: the E buffers are free
-  for (int blk = 0; blk < NRB; ++blk) {
+  auto run_block = [&](int blk, Ops& o) __attribute__((always_inline)) {
     const RowBlk d = row_block(blk);
     float* s_E = s_E0 + (blk & 1) * 64 * ES;
-    // this block's A operands (scaled by c_f, zero for an empty slot) and multipliers
-    const float cf = nok ? ncf : 0.f;
-    float av[NJ];
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) av[j] = cf * na[j];
-    const float q0 = pm0 ? Elem<T>::load(&pq0, 0) : 1.f;
-    const float q1 = pm1 ? Elem<T>::load(&pq1, 0) : 1.f;
-    if (blk + 1 < NRB) fetch_block(blk + 1);
+    const float cf = o.ok ? o.cf : 0.f;   // zero for an empty slot
+    const float q0 = o.m0 ? Elem<T>::load(&o.q0, 0) : 1.f;
+    const float q1 = o.m1 ? Elem<T>::load(&o.q1, 0) : 1.f;
     if (32 * FT < d.na + d.nb) {   // else an empty tile (the column block)
-      fx16 D[2];
+      fx16 D;   // one chain: stored as it stands, without an add
 #pragma unroll
-      for (int x = 0; x < 2; ++x)
+      for (int i = 0; i < 16; ++i) D[i] = 0.f;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) D[x][i] = 0.f;
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) D[j & 1] = mfma_f32(av[j], gv[j], D[j & 1]);
+      for (int j = 0; j < NJ; ++j) D = mfma_f32(cf * o.a[j], gv[j], D);
 #pragma unroll
       for (int i = 0; i < 16; ++i)   // every slot of a non-empty tile is used
-        s_E[(32 * FT + mrow(i, hout)) * ES + tok] = D[0][i] + D[1][i];
+        s_E[(32 * FT + mrow(i, hout)) * ES + tok] = D[i];
     }
+    // the set is free again; unconditional (the last two blocks reload a block),
+    // so that the wait before the other set's products counts only its own loads
+    fetch_block(min(blk + 2, NRB - 1), o);
     // one barrier: this block's E is complete, and the buffer written next (the
     // block after) was last read two blocks back
     __syncthreads();
@@ -811,6 +808,15 @@ k_bwd_dqstate(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunk
       if (d.m0 < DH) s_rd[qx * RS + d.m0] = d0;
       if (d.nb > 0) s_rd[qx * RS + d.m1] = d1;
     }
+  };
+  static_assert(NRB % 2 == 0, "the loop takes the row blocks in pairs");
+  Ops oa, ob;
+  fetch_block(0, oa);
+  fetch_block(1, ob);
+  __syncthreads();   // the g tile has been read: the E buffers are free
+  for (int blk = 0; blk < NRB; blk += 2) {
+    run_block(blk, oa);
+    run_block(blk + 1, ob);
   }
   __syncthreads();
   if (active) {
