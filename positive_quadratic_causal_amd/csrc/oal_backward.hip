@@ -137,6 +137,24 @@ __device__ __forceinline__ float coef_of(const float* rec, int f) {
   return 0.f;
 }
 
+// LDS staging of a contiguous span by a 256-thread block: element i < N (the
+// tile's capacity) gets load(i) for i < n and zero beyond (1 <= n <= N).  The loads
+// are unconditional (index clamped to n - 1) and all issued before the first is
+// awaited: a loop striding by blockDim.x is not unrolled, so each element would
+// wait for its own load, and a load in a divergent block is awaited at its end.
+template <int N, typename Load, typename Store>
+__device__ __forceinline__ void stage_span(int tid, int n, Load load, Store store) {
+  constexpr int E = (N + 255) / 256;
+  float x[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) x[e] = load(min(tid + 256 * e, n - 1));
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int i = tid + 256 * e;
+    if (i < N) store(i, i < n ? x[e] : 0.f);
+  }
+}
+
 // acc += s * row (16-byte aligned LDS row of WP floats)
 __device__ __forceinline__ void axpy_row(float (&acc)[WP], float s, const float* row) {
   float4 r4[WP / 4];
@@ -379,9 +397,10 @@ k_bwd_query(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunks,
   const bool grouped = reinterpret_cast<const int32_t*>(rec)[OAL_COEF_NG] >= 1;
   if (grouped) build_group_tab(gt, rec, tid);
   const size_t qrow0 = ((size_t)b * n_q_heads + hq) * seq_len + t0;
-  for (int i = tid; i < chunk * DH; i += nthr) {
-    const int ii = i / DH, d = i % DH;
-    s_q[ii * (DH + 1) + d] = ii < clen ? Elem<T>::load(q, (qrow0 + ii) * DH + d) : 0.f;
+  {
+    const T* qs = q + qrow0 * DH;   // the chunk's q rows, one span (clen >= 1)
+    stage_span<(256 / SP) * DH>(tid, clen * DH, [&](int i) { return Elem<T>::load(qs, i); },
+                                [&](int i, float x) { s_q[(i / DH) * (DH + 1) + i % DH] = x; });
   }
   for (int i = tid; i < chunk; i += nthr) s_q[i * (DH + 1) + DH] = 1.f;   // psi's constant slot
   for (int i = tid; i < SP * chunk * (DH + 1); i += nthr) s_dq[i] = 0.f;
@@ -397,10 +416,12 @@ k_bwd_query(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunks,
     const int kind = feat_decode(f, r, t);
     const int ia = kind == 0 ? DH : r, ib = kind == 2 ? t : DH;
     s_fd[f] = (uint16_t)(ia | (ib << 8));
-    s_fc[f] = f < DCAN ? coef_of(rec, f) : 0.f;
   }
+  stage_span<DS>(tid, DCAN, [&](int f) { return rec[coef_index(f)]; },
+                 [&](int f, float x) { s_fc[f] = x; });
   for (int i = tid; i < DH; i += nthr) s_b[i] = rec[OAL_COEF_BP + i];
-  for (int i = tid; i < DH * DH; i += nthr) s_S[i] = rec[OAL_COEF_CM + i];
+  stage_span<DH * DH>(tid, DH * DH, [&](int i) { return rec[OAL_COEF_CM + i]; },
+                      [&](int i, float x) { s_S[i] = x; });
   for (int i = tid; i < TB * (WP - W); i += nthr) s_u[(i / (WP - W)) * WP + W + i % (WP - W)] = 0.f;
   __syncthreads();
   const bool fast = grouped && gt.n_out <= MAX_OUT;   // uniform over the block
@@ -410,15 +431,18 @@ k_bwd_query(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunks,
   const size_t kbase = (size_t)unit * seq_len + t0;
 
   auto stage_keys = [&](int j0, int nj) {
-    for (int i = tid; i < TB * DH; i += nthr) {
-      const int jj = i / DH, d = i % DH;
-      float kv_ = 0.f, vv_ = 0.f;
-      if (jj < nj) {
-        kv_ = Elem<T>::load(k, (kbase + j0 + jj) * DH + d);
-        vv_ = Elem<T>::load(v, (kbase + j0 + jj) * DV + d);
+    if (nj > 0) {   // uniform; the key and value rows are one span each
+      const T* ks = k + (kbase + j0) * DH;
+      const T* vs = v + (kbase + j0) * DV;
+      stage_span<TB * DH>(tid, nj * DH, [&](int i) { return Elem<T>::load(ks, i); },
+                          [&](int i, float x) { s_k[(i / DH) * (DH + 1) + i % DH] = x; });
+      stage_span<TB * DV>(tid, nj * DV, [&](int i) { return Elem<T>::load(vs, i); },
+                          [&](int i, float x) { s_u[(i / DV) * WP + i % DV] = x; });
+    } else {
+      for (int i = tid; i < TB * DH; i += nthr) {
+        s_k[(i / DH) * (DH + 1) + i % DH] = 0.f;
+        s_u[(i / DV) * WP + i % DV] = 0.f;
       }
-      s_k[jj * (DH + 1) + d] = kv_;
-      s_u[jj * WP + d] = vv_;
     }
     for (int jj = tid; jj < TB; jj += nthr) s_u[jj * WP + DV] = jj < nj ? 1.f : 0.f;
   };
@@ -1016,9 +1040,10 @@ k_bwd_key(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunks,
   float* s_S = s_b + DH;                      // [DH][DH]
 
   const size_t krow0 = (size_t)unit * seq_len + t0;
-  for (int i = tid; i < chunk * DH; i += nthr) {
-    const int jj = i / DH, d = i % DH;
-    s_k[jj * (DH + 1) + d] = jj < clen ? Elem<T>::load(k, (krow0 + jj) * DH + d) : 0.f;
+  {
+    const T* ks = k + krow0 * DH;   // the chunk's key rows, one span (clen >= 1)
+    stage_span<(256 / SP) * DH>(tid, clen * DH, [&](int i) { return Elem<T>::load(ks, i); },
+                                [&](int i, float x) { s_k[(i / DH) * (DH + 1) + i % DH] = x; });
   }
   for (int i = tid; i < SP * chunk * (DH + 1); i += nthr) s_dk[i] = 0.f;
   for (int i = tid; i < 32 * (WP - W); i += nthr) s_R[(i / (WP - W)) * WP + W + i % (WP - W)] = 0.f;
@@ -1098,18 +1123,17 @@ k_bwd_key(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunks,
     __syncthreads();
     if (grouped) build_group_tab(gt, rec, tid);
     for (int i = tid; i < DH; i += nthr) s_b[i] = rec[OAL_COEF_BP + i];
-    for (int i = tid; i < DH * DH; i += nthr) s_S[i] = rec[OAL_COEF_CM + i];
+    stage_span<DH * DH>(tid, DH * DH, [&](int i) { return rec[OAL_COEF_CM + i]; },
+                        [&](int i, float x) { s_S[i] = x; });
     for (int i0 = 0; i0 < clen; i0 += TB) {
       const int ni = min(TB, clen - i0);
       __syncthreads();
-      for (int i = tid; i < TB * DH; i += nthr) {
-        const int ii = i / DH, d = i % DH;
-        s_q[ii * (DH + 1) + d] = ii < ni ? Elem<T>::load(q, (qrow0 + t0 + i0 + ii) * DH + d) : 0.f;
-      }
-      for (int i = tid; i < TB * WP; i += nthr) {
-        const int ii = i / WP, w = i % WP;
-        s_g[ii * WP + w] = ii < ni ? gbuf[(grow0 + t0 + i0 + ii) * WP + w] : 0.f;
-      }
+      const T* qs = q + (qrow0 + t0 + i0) * DH;        // the tile's q rows and g rows,
+      const float* gs = gbuf + (grow0 + t0 + i0) * WP;  // one span each (ni >= 1)
+      stage_span<TB * DH>(tid, ni * DH, [&](int i) { return Elem<T>::load(qs, i); },
+                          [&](int i, float x) { s_q[(i / DH) * (DH + 1) + i % DH] = x; });
+      stage_span<TB * WP>(tid, ni * WP, [&](int i) { return gs[i]; },
+                          [&](int i, float x) { s_g[i] = x; });
       __syncthreads();
       const bool fast = grouped && gt.n_out <= MAX_OUT;   // uniform over the block
       if (active) {
