@@ -281,10 +281,24 @@ k_state_kvmax(int seq_len, int chunk, int n_chunks, int cps, const uint16_t* __r
       mi = max(mi, __float_as_uint(fmaxf(fmaxf(fabsf(x.x), fabsf(x.y)), fmaxf(fabsf(x.z), fabsf(x.w)))));
     }
   }
-  for (int p = tid; p < (t_end - t_begin) * 8; p += 256) {
-    const size_t row = row0 + t_begin + (p >> 3);
-    mk = max(mk, absmax8_bits(reinterpret_cast<const uint4*>(k + row * DH)[p & 7]));
-    mv = max(mv, absmax8_bits(reinterpret_cast<const uint4*>(v + row * DV)[p & 7]));
+  // four rounds of 16-byte loads in flight at a time (a clamped duplicate leaves the
+  // maximum alone); one at a time, each would wait out the memory latency
+  const int np = (t_end - t_begin) * 8;
+  constexpr int KB = 4;
+  for (int p0 = 0; p0 < np; p0 += 256 * KB) {
+    uint4 xk[KB], xv[KB];
+#pragma unroll
+    for (int e = 0; e < KB; ++e) {
+      const int p = min(p0 + tid + 256 * e, np - 1);
+      const size_t row = row0 + t_begin + (p >> 3);
+      xk[e] = reinterpret_cast<const uint4*>(k + row * DH)[p & 7];
+      xv[e] = reinterpret_cast<const uint4*>(v + row * DV)[p & 7];
+    }
+#pragma unroll
+    for (int e = 0; e < KB; ++e) {
+      mk = max(mk, absmax8_bits(xk[e]));
+      mv = max(mv, absmax8_bits(xv[e]));
+    }
   }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) {
