@@ -318,7 +318,7 @@ def bench_prefill_dim(oal, w, chunk, steps, warmup, device):
 
 
 BWD_KERNELS = ["k_build_vec", "k_scan_vec", "k_bwd_query", "k_bwd_dqstate", "k_bwd_rbuild", "k_bwd_rscan",
-               "k_bwd_key", "k_bwd_ksum", "k_bwd_dc_intra", "k_bwd_dcoef"]
+               "k_bwd_key", "k_bwd_kstate", "k_bwd_ksum", "k_bwd_dc_intra", "k_bwd_dcoef"]
 
 
 def backward_flops(w, chunk, grouped=True) -> dict:
@@ -329,7 +329,8 @@ def backward_flops(w, chunk, grouped=True) -> dict:
     dimension-specific record kappa in packed form 64 + 2 (64 + 2080) and its
     gradient 2 * 64 * 64 + 3 * 64 instead.  Per query or key row: two 2145 x 65
     contractions with a state (recompute + H g, or R^T psi(k) + R u); the query
-    side's second one (H g and its contraction with d psi / dq) is k_bwd_dqstate."""
+    side's second one (H g and its contraction with d psi / dq) is k_bwd_dqstate,
+    the key side's two are k_bwd_kstate."""
     n, c = w.seq_len, chunk
     pairs = 0
     for t0 in range(0, n, c):
@@ -345,7 +346,8 @@ def backward_flops(w, chunk, grouped=True) -> dict:
     nk = w.batch * w.n_kv_heads * n
     return {"k_bwd_query": nq * 2 * D * Wc + pairs * (kap + grad + 4 * Wc),
             "k_bwd_dqstate": nq * (2 * D * Wc + 4 * (D - 1 - 64) + 2 * 64),
-            "k_bwd_key": nk * 4 * D * Wc + pairs * (kap + grad + 4 * Wc),
+            "k_bwd_key": pairs * (kap + grad + 4 * Wc),
+            "k_bwd_kstate": nk * (2 * D * Wc + 2 * D * 64 + 4 * (D - 1 - 64) + 2 * 64),
             "k_bwd_rbuild": nq * 2 * D * Wc,
             "k_bwd_dc_intra": pairs * 2 * D}
 

@@ -28,8 +28,10 @@
 //   k_bwd_rbuild    per chunk: sum_h c_f psi_f(q_i) g_i^T (suffix deltas) and the
 //                   state part of dc: sum_i psi_f(q_i) (H_{<c} g_i)_f
 //   k_bwd_rscan     exclusive suffix sums over chunks: R_{>c}
-//   k_bwd_key       four (chunk 64) or two threads per key and slot (a query head's pairs, or R_{>c}):
-//                   parts of dv_j, dk_j;  k_bwd_ksum adds the parts
+//   k_bwd_key       four (chunk 64) or two threads per key and query head: the pair parts of
+//                   dv_j, dk_j
+//   k_bwd_kstate    the parts through R_{>c}: R^T psi(k_j) and R u_j against d psi(k_j) / dk_j,
+//                   by pair rows in four feature splits;  k_bwd_ksum adds the parts
 //   k_bwd_dc_intra  pair part of dc: sum_{i, j<=i in the chunk} alpha_ij psi_f(q_i) psi_f(k_j)
 //   k_bwd_dcoef     sum over chunks and batch; (da, db, dC) of [OAL] Eq. 3
 #include "oal_common.h"
@@ -137,20 +139,20 @@ __device__ __forceinline__ float coef_of(const float* rec, int f) {
   return 0.f;
 }
 
-// LDS staging of a contiguous span by a 256-thread block: element i < N (the
+// LDS staging of a contiguous span by a block of NT threads: element i < N (the
 // tile's capacity) gets load(i) for i < n and zero beyond (1 <= n <= N).  The loads
 // are unconditional (index clamped to n - 1) and all issued before the first is
 // awaited: a loop striding by blockDim.x is not unrolled, so each element would
 // wait for its own load, and a load in a divergent block is awaited at its end.
-template <int N, typename Load, typename Store>
+template <int N, int NT = 256, typename Load, typename Store>
 __device__ __forceinline__ void stage_span(int tid, int n, Load load, Store store) {
-  constexpr int E = (N + 255) / 256;
+  constexpr int E = (N + NT - 1) / NT;
   float x[E];
 #pragma unroll
-  for (int e = 0; e < E; ++e) x[e] = load(min(tid + 256 * e, n - 1));
+  for (int e = 0; e < E; ++e) x[e] = load(min(tid + NT * e, n - 1));
 #pragma unroll
   for (int e = 0; e < E; ++e) {
-    const int i = tid + 256 * e;
+    const int i = tid + NT * e;
     if (i < N) store(i, i < n ? x[e] : 0.f);
   }
 }
@@ -318,7 +320,7 @@ static int key_split(int chunk) { return chunk <= 64 ? 4 : 2; }
 // ranges, one workgroup (and one set of parts) each: it walks all 2145 features
 // while the pair slots meet one chunk of queries, and would otherwise set the
 // kernel's length alone.
-constexpr int KEY_RSPLIT = 4;
+constexpr int KS_NFS = 4;   // feature splits of the key side's state part (k_bwd_kstate)
 
 static BwdWs bwd_ws(void* base, int batch, int n_q_heads, int n_kv_heads, int seq_len, int chunk) {
   const size_t units = (size_t)batch * n_kv_heads;
@@ -335,7 +337,7 @@ static BwdWs bwd_ws(void* base, int batch, int n_q_heads, int n_kv_heads, int se
   const size_t o_g = take(bh * nc * chunk * WP);
   const size_t o_a = take(bh * nc * chunk * chunk);
   const size_t o_d = take(bh * nc * DS);
-  const size_t o_k = take(units * (size_t)key_split(chunk) * (n_q_heads / n_kv_heads + KEY_RSPLIT) * nc * chunk *
+  const size_t o_k = take(units * ((size_t)key_split(chunk) * (n_q_heads / n_kv_heads) + KS_NFS) * nc * chunk *
                           (DH + DV));
   BwdWs w;
   uint8_t* p = reinterpret_cast<uint8_t*>(base);
@@ -1005,22 +1007,21 @@ k_bwd_rscan(int n_chunks, float* __restrict__ rc) {
 }
 
 // ---------------------------------------------------------------------------
-// Key side.  One block per (chunk, unit, slot): slot s < rep sums the chunk's
-// pairs of query head kv * rep + s, slot rep the later chunks through R_{>c}.
-// SP threads per key (thread SP j + h for key t0 + j) split the pairs (by query
-// index mod SP) or the features round robin; each thread writes its part of
-// [dk_j | dv_j] to kpart (part SP slot + h), and k_bwd_ksum adds the SP (rep + 1)
-// parts in order.
+// Key side, the chunk's pairs.  One block per (chunk, unit, slot): slot s sums the
+// chunk's pairs (i >= j) of query head kv * rep + s.  SP threads per key (thread
+// SP j + h for key t0 + j) split the pairs by query index mod SP; each thread writes
+// its part of [dk_j | dv_j] to kpart (part SP slot + h of the unit's SP rep + KS_NFS
+// parts; the last KS_NFS are k_bwd_kstate's), and k_bwd_ksum adds the parts in order.
 template <typename T, int SP>
 __global__ void __launch_bounds__(256)
 k_bwd_key(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunks,
           const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
           const void* __restrict__ coeffs, const float* __restrict__ gbuf,
-          const float* __restrict__ rc, float* __restrict__ kpart) {
+          float* __restrict__ kpart) {
   const int c = blockIdx.x;
   const int rep = n_q_heads / n_kv_heads;
-  const int unit = blockIdx.y / (rep + KEY_RSPLIT);
-  const int slot = blockIdx.y % (rep + KEY_RSPLIT);   // >= rep: suffix states, feature range slot - rep
+  const int unit = blockIdx.y / rep;
+  const int slot = blockIdx.y % rep;
   const int b = unit / n_kv_heads, kv = unit % n_kv_heads;
   const int tid = threadIdx.x;
   const int nthr = blockDim.x;                // SP * chunk
@@ -1033,8 +1034,7 @@ k_bwd_key(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunks,
   extern __shared__ __attribute__((aligned(16))) float smem[];
   float* s_k = smem;                          // [chunk][DH + 1]
   float* s_dk = s_k + chunk * (DH + 1);       // [SP][chunk][DH + 1]
-  float* s_R = s_dk + SP * chunk * (DH + 1);  // [32][WP]
-  float* s_q = s_R + 32 * WP;                 // [TB][DH + 1]
+  float* s_q = s_dk + SP * chunk * (DH + 1);  // [TB][DH + 1]
   float* s_g = s_q + TB * (DH + 1);           // [TB][WP]
   float* s_b = s_g + TB * WP;                 // [DH]
   float* s_S = s_b + DH;                      // [DH][DH]
@@ -1046,7 +1046,6 @@ k_bwd_key(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunks,
                                 [&](int i, float x) { s_k[(i / DH) * (DH + 1) + i % DH] = x; });
   }
   for (int i = tid; i < SP * chunk * (DH + 1); i += nthr) s_dk[i] = 0.f;
-  for (int i = tid; i < 32 * (WP - W); i += nthr) s_R[(i / (WP - W)) * WP + W + i % (WP - W)] = 0.f;
   float uj[WP];
 #pragma unroll
   for (int w = 0; w < WP; ++w) uj[w] = 0.f;
@@ -1062,58 +1061,10 @@ k_bwd_key(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunks,
 #pragma unroll
   for (int w = 0; w < WP; ++w) du[w] = 0.f;
 
-  // ---- later chunks, through R_{>c}: du_j = R^T psi(k_j), d psi(k_j) = R u_j
-  // (the next 32-feature block of R is fetched into registers while the current
-  // one is used; nthr = 256: 9 values per thread at most)
-  const float* Rs = rc + ((size_t)unit * n_chunks + c) * STATE_FLOATS;
-  constexpr int PB = (32 * W + 255) / 256;
-  float pre[PB];
-  auto fetch_block = [&](int f0) {
-#pragma unroll
-    for (int e = 0; e < PB; ++e) {
-      const int i = tid + e * 256;
-      if (i < 32 * W) pre[e] = Rs[(size_t)(i / 32) * DS + f0 + i % 32];   // f0 + 31 < DS always
-    }
-  };
-  // this slot's range of 32-feature blocks
-  constexpr int NBLK = (DCAN + 31) / 32;
-  const int rq = slot - rep;
-  const int fbeg = rq < 0 ? DCAN : 32 * ((NBLK * rq) / KEY_RSPLIT);
-  const int fend = rq < 0 ? DCAN : min(DCAN, 32 * ((NBLK * (rq + 1)) / KEY_RSPLIT));
-  if (fbeg < fend) fetch_block(fbeg);
-  for (int f0 = fbeg; f0 < fend; f0 += 32) {
-    __syncthreads();
-#pragma unroll
-    for (int e = 0; e < PB; ++e) {
-      const int i = tid + e * 256;
-      if (i < 32 * W) s_R[(i % 32) * WP + i / 32] = pre[e];
-    }
-    if (f0 + 32 < fend) fetch_block(f0 + 32);
-    __syncthreads();
-    if (active) {
-      const int nf = min(32, DCAN - f0);
-      for (int ff = half; ff < nf; ff += SP) {
-        int r, t;
-        const int kind = feat_decode(f0 + ff, r, t);
-        const float* row = s_R + ff * WP;
-        const float psi = kind == 0 ? 1.f : kind == 1 ? kj[r] : kj[r] * kj[t];
-        axpy_row(du, psi, row);
-        if (kind == 0) continue;
-        const float e = dot_row(row, uj);
-        if (kind == 1) {
-          dkj[r] += e;
-        } else {
-          dkj[r] = fmaf(e, kj[t], dkj[r]);
-          dkj[t] = fmaf(e, kj[r], dkj[t]);
-        }
-      }
-    }
-  }
-
   // ---- the chunk's pairs (i >= j) of this slot's query head
   const size_t npad = (size_t)n_chunks * chunk;
   __shared__ __attribute__((aligned(16))) GroupTab gt;
-  if (slot < rep) {
+  {
     const int hq = kv * rep + slot;
     const float* rec = coef_rec(coeffs, hq);
     const float a = rec[OAL_COEF_A];
@@ -1165,11 +1116,213 @@ k_bwd_key(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunks,
     }
   }
   if (active) {
-    float* o = kpart + (((size_t)unit * SP * (rep + KEY_RSPLIT) + SP * slot + half) * npad + t0 + jx) * (DH + DV);
+    float* o = kpart + (((size_t)unit * (SP * rep + KS_NFS) + SP * slot + half) * npad + t0 + jx) * (DH + DV);
 #pragma unroll
     for (int d = 0; d < DH; ++d) o[d] = dkj[d];
 #pragma unroll
     for (int w = 0; w < DV; ++w) o[DH + w] = du[w];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Key side, the later chunks through R = R_{>c} (the suffix states, with c_f and the
+// query heads of the group folded in):  dv_j += R^T psi(k_j) and
+// dk_j += sum_f (R u_j)_f d psi_f(k_j) / dk_j, u_j = (v_j, 1).  Block (32 keys,
+// chunk, unit, feature split): two waves over a quarter of the row blocks.  Per row
+// block each lane loads its A operands R[slot][2 j + lane / 32] straight from the
+// state a block ahead (the slots of a run are consecutive features: coalesced) and
+// copies them to LDS; on the fp32 matrix cores
+//   E[slot][tok] = sum_w R[slot][w] u_tok[w]   (wave = tile of 32 slots, K = channels,
+//                                               u read once into registers)
+//   dv[tok][w] += sum_slot psi_slot(k_tok) R[slot][w]
+//                                              (wave = tile of 32 channels, K = slots,
+//                                               A = k~[ia] k~[ib] from the key rows and
+//                                               the block's slot table, B = R from LDS)
+// and E goes through the same t-side / m-side update as the query side (four
+// threads per key, 16 entries of dk each in registers).  The block's [dk | dv] is
+// one part of kpart (part part0 + split); k_bwd_ksum adds the parts.  The blocks of
+// one (unit, chunk) share an XCD (workgroup id % 8).
+constexpr int KS_TG = 32;   // keys per block
+template <typename T>
+__global__ void __launch_bounds__(128)
+k_bwd_kstate(int n_kv_heads, int seq_len, int chunk, int n_chunks, int n_units, int part0,
+             int nparts, const T* __restrict__ k, const T* __restrict__ v,
+             const float* __restrict__ rc, float* __restrict__ kpart) {
+  constexpr int TG = KS_TG;
+  constexpr int NTP = DH / 4;            // dk entries per thread
+  constexpr int ES = TG + 1;             // E row stride (bank spread)
+  constexpr int RS = DH + 1;             // m-side row stride
+  constexpr int KR = DH + 2;             // key row: k, 1 (the constant slot), 0 (empty slots)
+  constexpr int GS = W + 1;              // u row: channels 0..64 and a zero
+  constexpr int NJ = (W + 1) / 2;        // 33 channel pairs
+  const int per = (chunk / TG) * KS_NFS;
+  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  const int uc = (slot / per) * 8 + xcd;
+  if (uc >= n_units * n_chunks) return;
+  const int unit = uc / n_chunks, c = uc % n_chunks;
+  const int split = (slot % per) % KS_NFS;
+  const int t0 = c * chunk + ((slot % per) / KS_NFS) * TG;
+  const int ntok = min(TG, seq_len - t0);
+  if (ntok <= 0) return;                 // a group past the sequence (whole block)
+  const int blk0 = NRB * split / KS_NFS, blk1 = NRB * (split + 1) / KS_NFS;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int FT = __builtin_amdgcn_readfirstlane(tid >> 6);   // the wave's tile
+  const int qx = tid >> 2, half = tid & 3;                    // key and part
+  const int hout = lane >> 5, tok = lane & 31;                // matrix-core roles
+
+  // one array, in this order: the masked reads of an E buffer reach up to 63 slots
+  // before it (s_rd, or the other buffer) and one slot after it (the other buffer,
+  // or the tail)
+  __shared__ __attribute__((aligned(16))) float sm[TG * RS + 2 * 64 * ES + TG + 2 * 64 * WPH + TG * KR];
+  __shared__ int s_fd[2][64];            // the block's slots: k~[ia] k~[ib] = ia | ib << 8
+  float* s_rd = sm;                      // [TG][RS] the m-side sums
+  float* s_E0 = s_rd + TG * RS;          // [2][64][ES] E[slot][tok]; first the u tile [TG][GS]
+  float* s_R0 = s_E0 + 2 * 64 * ES + TG; // [2][64][WPH] the block's R rows
+  float* s_k = s_R0 + 2 * 64 * WPH;      // [TG][KR] the key rows
+  static_assert(TG * GS <= 64 * ES, "the u tile fits an E buffer");
+  static_assert(63 * ES <= TG * RS, "masked reads stay in the array");
+  float* s_u = s_E0;
+
+  const float* Rs = rc + ((size_t)unit * n_chunks + c) * STATE_FLOATS;
+  const size_t row0 = (size_t)unit * seq_len + t0;     // k, v rows
+  const bool active = qx < ntok;
+  stage_span<TG * DH, 128>(tid, ntok * DH, [&](int i) { return Elem<T>::load(k + row0 * DH, i); },
+                           [&](int i, float x) { s_k[(i / DH) * KR + i % DH] = x; });
+  stage_span<TG * DV, 128>(tid, ntok * DV, [&](int i) { return Elem<T>::load(v + row0 * DV, i); },
+                           [&](int i, float x) { s_u[(i / DV) * GS + i % DV] = x; });
+  if (tid < TG) {
+    s_k[tid * KR + DH] = 1.f;
+    s_k[tid * KR + DH + 1] = 0.f;
+    s_u[tid * GS + DV] = tid < ntok ? 1.f : 0.f;
+    s_u[tid * GS + DV + 1] = 0.f;
+  }
+  for (int i = tid; i < TG * RS; i += 128) s_rd[i] = 0.f;   // a split leaves some m-side sums out
+  float dkt[NTP];
+#pragma unroll
+  for (int j = 0; j < NTP; ++j) dkt[j] = 0.f;
+  fx16 DVa;   // dv[tok][32 FT + lane % 32] of this split, rows mrow(i, lane / 32)
+#pragma unroll
+  for (int i = 0; i < 16; ++i) DVa[i] = 0.f;
+  // the constant feature (psi = 1, no dk part, so in no row block) adds R[0][w] to
+  // every key's dv: split 0 carries it
+  const float r0w = split == 0 ? Rs[(size_t)(32 * FT + tok) * DS] : 0.f;
+  __syncthreads();
+  float kt[NTP];   // this thread's k entries NTP half + j
+#pragma unroll
+  for (int j = 0; j < NTP; ++j) kt[j] = s_k[qx * KR + NTP * half + j];
+  float gv[NJ];    // B operands of E: u[tok][2 j + lane / 32] (channel 65: zero)
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) gv[j] = s_u[tok * GS + 2 * j + hout];
+
+  // A operands of the next block and the slot's feature; loads unconditional
+  // (clamped index), their values used a block later (see k_bwd_dqstate)
+  float na[NJ];
+  int nfs = 0;
+  auto fetch_block = [&](int blk) {
+    const RowBlk d = row_block(blk);
+    nfs = row_block_feature(blk, d, 32 * FT + tok);
+    const float* rp = Rs + max(nfs, 0);   // an empty slot reads feature 0
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) na[j] = rp[(size_t)min(2 * j + hout, W - 1) * DS];   // channel 65: any finite value
+  };
+  fetch_block(blk0);
+  __syncthreads();   // the u tile has been read: the E buffers are free
+  for (int blk = blk0; blk < blk1; ++blk) {
+    const RowBlk d = row_block(blk);
+    const int bf = (blk - blk0) & 1;
+    float* s_E = s_E0 + bf * 64 * ES;
+    float* s_R = s_R0 + bf * 64 * WPH;
+    // this block's R rows to LDS (for the dv product) and the slot table
+    {
+      const bool ok = nfs >= 0;
+      const int sl = 32 * FT + tok;
+      float* rrow = s_R + sl * WPH + hout;
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) rrow[2 * j] = ok ? na[j] : 0.f;
+      if (hout == 0) {
+        int r, t;
+        const int kind = feat_decode(max(nfs, 0), r, t);
+        const int ia = !ok ? DH + 1 : (kind == 0 ? DH : r);
+        const int ib = !ok ? DH + 1 : (kind == 2 ? t : DH);
+        s_fd[bf][sl] = ia | (ib << 8);
+      }
+    }
+    if (32 * FT < d.na + d.nb) {   // else an empty tile (the column block)
+      fx16 D;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) D[i] = 0.f;
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) D = mfma_f32(na[j], gv[j], D);
+#pragma unroll
+      for (int i = 0; i < 16; ++i)   // every slot of a non-empty tile is used
+        s_E[(32 * FT + mrow(i, hout)) * ES + tok] = D[i];
+    }
+    fetch_block(min(blk + 1, blk1 - 1));   // unconditional: the last block reloads itself
+    // one barrier: this block's E, R rows and slot table are complete, and the
+    // buffers written next (the block after) were last read two blocks back
+    __syncthreads();
+    // dk: t side into the registers, m side as dot products (masked as on the query side)
+    const float k0 = s_k[qx * KR + d.m0], k1 = s_k[qx * KR + d.m1];
+    float d0 = 0.f, d1 = 0.f;
+    {
+      const int lo = d.ta0 - NTP * half;
+      const float* ep = s_E + (NTP * half - d.ta0) * ES + qx;
+#pragma unroll
+      for (int j = 0; j < NTP; ++j) {
+        const float r = ep[j * ES];
+        const float e0 = (unsigned)(j - lo) < (unsigned)d.na ? r : 0.f;
+        dkt[j] = fmaf(e0, k0, dkt[j]);
+        d0 = fmaf(e0, kt[j], d0);
+      }
+    }
+    if (d.nb > 0) {
+      const int lo = d.tb0 - NTP * half;
+      const float* ep = s_E + (d.na + NTP * half - d.tb0) * ES + qx;
+#pragma unroll
+      for (int j = 0; j < NTP; ++j) {
+        const float r = ep[j * ES];
+        const float e1 = (unsigned)(j - lo) < (unsigned)d.nb ? r : 0.f;
+        dkt[j] = fmaf(e1, k1, dkt[j]);
+        d1 = fmaf(e1, kt[j], d1);
+      }
+    }
+    d0 += lane_xor1(d0);
+    d1 += lane_xor1(d1);
+    d0 += lane_xor2(d0);
+    d1 += lane_xor2(d1);
+    if (half == 0) {
+      if (d.m0 < DH) s_rd[qx * RS + d.m0] = d0;
+      if (d.nb > 0) s_rd[qx * RS + d.m1] = d1;
+    }
+    // dv: K = the block's 64 slots, two per product
+    {
+      const float* krow = s_k + tok * KR;
+      const float* rcol = s_R + hout * WPH + 32 * FT + tok;
+#pragma unroll
+      for (int i0 = 0; i0 < 32; i0 += 8) {
+        float av[8], bv[8];
+#pragma unroll
+        for (int ii = 0; ii < 8; ++ii) {
+          const int dd = s_fd[bf][2 * (i0 + ii) + hout];
+          av[ii] = krow[dd & 255] * krow[dd >> 8];
+          bv[ii] = rcol[2 * (i0 + ii) * WPH];
+        }
+#pragma unroll
+        for (int ii = 0; ii < 8; ++ii) DVa = mfma_f32(av[ii], bv[ii], DVa);
+      }
+    }
+  }
+  __syncthreads();
+  float* kp = kpart + ((size_t)unit * nparts + part0 + split) * ((size_t)n_chunks * chunk) * (DH + DV);
+  if (active) {
+    float* o = kp + (size_t)(t0 + qx) * (DH + DV) + NTP * half;
+#pragma unroll
+    for (int j = 0; j < NTP; ++j) o[j] = dkt[j] + s_rd[qx * RS + NTP * half + j];
+  }
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int r = mrow(i, hout);
+    if (r < ntok) kp[(size_t)(t0 + r) * (DH + DV) + DH + 32 * FT + tok] = DVa[i] + r0w;
   }
 }
 
@@ -1427,7 +1580,7 @@ static oal_status backward_typed(int batch, int n_q_heads, int n_kv_heads, int s
   {
     const int ks = key_split(chunk);
     if (ks * chunk != 256) return set_error(OAL_ERR_INVALID_ARG, "k_bwd_key: chunk %d", chunk);
-    const size_t smem = sizeof(float) * ((size_t)(1 + ks) * chunk * (DH + 1) + 32 * WP + TB * (DH + 1) +
+    const size_t smem = sizeof(float) * ((size_t)(1 + ks) * chunk * (DH + 1) + TB * (DH + 1) +
                                          TB * WP + DH + DH * DH);
     const void* fn = ks == 4 ? reinterpret_cast<const void*>(&k_bwd_key<T, 4>)
                              : reinterpret_cast<const void*>(&k_bwd_key<T, 2>);
@@ -1437,19 +1590,27 @@ static oal_status backward_typed(int batch, int n_q_heads, int n_kv_heads, int s
     {
       ProfScope ps("k_bwd_key", stream);
       if (ks == 4)
-        hipLaunchKernelGGL((k_bwd_key<T, 4>), dim3(n_chunks, units * (rep + KEY_RSPLIT)), dim3(4 * chunk), smem,
+        hipLaunchKernelGGL((k_bwd_key<T, 4>), dim3(n_chunks, units * rep), dim3(4 * chunk), smem,
                            stream, n_q_heads, n_kv_heads, seq_len, chunk, n_chunks, qq, kk, vv, coeffs,
-                           w.gbuf, w.rc, w.kpart);
+                           w.gbuf, w.kpart);
       else
-        hipLaunchKernelGGL((k_bwd_key<T, 2>), dim3(n_chunks, units * (rep + KEY_RSPLIT)), dim3(2 * chunk), smem,
+        hipLaunchKernelGGL((k_bwd_key<T, 2>), dim3(n_chunks, units * rep), dim3(2 * chunk), smem,
                            stream, n_q_heads, n_kv_heads, seq_len, chunk, n_chunks, qq, kk, vv, coeffs,
-                           w.gbuf, w.rc, w.kpart);
+                           w.gbuf, w.kpart);
       if ((st = check_launch("k_bwd_key")) != OAL_OK) return st;
+    }
+    {
+      const int per = (chunk / KS_TG) * KS_NFS;
+      const dim3 grid((unsigned)(((size_t)units * n_chunks + 7) / 8 * 8 * (size_t)per));
+      ProfScope ps("k_bwd_kstate", stream);
+      hipLaunchKernelGGL(k_bwd_kstate<T>, grid, dim3(128), 0, stream, n_kv_heads, seq_len, chunk,
+                         n_chunks, units, ks * rep, ks * rep + KS_NFS, kk, vv, w.rc, w.kpart);
+      if ((st = check_launch("k_bwd_kstate")) != OAL_OK) return st;
     }
     ProfScope ps("k_bwd_ksum", stream);
     const size_t per_unit = (size_t)seq_len * (DH + DV);
     hipLaunchKernelGGL(k_bwd_ksum, dim3((unsigned)((per_unit + 255) / 256), units), dim3(256), 0,
-                       stream, n_kv_heads, ks * (rep + KEY_RSPLIT), seq_len, n_chunks * chunk, w.kpart, dk, dv);
+                       stream, n_kv_heads, ks * rep + KS_NFS, seq_len, n_chunks * chunk, w.kpart, dk, dv);
     if ((st = check_launch("k_bwd_ksum")) != OAL_OK) return st;
   }
   if (!want_coef) return OAL_OK;
