@@ -317,7 +317,8 @@ def bench_prefill_dim(oal, w, chunk, steps, warmup, device):
             "kernels_ms": {k: round(v["avg_ms"], 5) for k, v in kt.items()}}
 
 
-BWD_KERNELS = ["k_build_vec", "k_scan_vec", "k_bwd_query", "k_bwd_dqstate", "k_bwd_rbuild", "k_bwd_rscan",
+BWD_KERNELS = ["k_build_vec", "k_scan_vec", "k_bwd_ustate", "k_bwd_query", "k_bwd_dqstate", "k_bwd_rbuild",
+               "k_bwd_rscan",
                "k_bwd_key", "k_bwd_kstate", "k_bwd_ksum", "k_bwd_dc_intra", "k_bwd_dcoef"]
 
 
@@ -328,9 +329,9 @@ def backward_flops(w, chunk, grouped=True) -> dict:
     multiply-adds and two 65-wide products (alpha and the accumulation); for a
     dimension-specific record kappa in packed form 64 + 2 (64 + 2080) and its
     gradient 2 * 64 * 64 + 3 * 64 instead.  Per query or key row: two 2145 x 65
-    contractions with a state (recompute + H g, or R^T psi(k) + R u); the query
-    side's second one (H g and its contraction with d psi / dq) is k_bwd_dqstate,
-    the key side's two are k_bwd_kstate."""
+    contractions with a state (recompute + H g, or R^T psi(k) + R u): on the query
+    side the recompute is k_bwd_ustate and H g with its contraction with d psi / dq
+    k_bwd_dqstate; on the key side both are k_bwd_kstate."""
     n, c = w.seq_len, chunk
     pairs = 0
     for t0 in range(0, n, c):
@@ -344,7 +345,8 @@ def backward_flops(w, chunk, grouped=True) -> dict:
         kap, grad = 64 + 2 * (64 + 2080), 2 * 64 * 64 + 3 * 64
     nq = w.batch * w.n_q_heads * n
     nk = w.batch * w.n_kv_heads * n
-    return {"k_bwd_query": nq * 2 * D * Wc + pairs * (kap + grad + 4 * Wc),
+    return {"k_bwd_ustate": nq * 2 * D * Wc,
+            "k_bwd_query": pairs * (kap + grad + 4 * Wc),
             "k_bwd_dqstate": nq * (2 * D * Wc + 4 * (D - 1 - 64) + 2 * 64),
             "k_bwd_key": pairs * (kap + grad + 4 * Wc),
             "k_bwd_kstate": nk * (2 * D * Wc + 2 * D * 64 + 4 * (D - 1 - 64) + 2 * 64),
@@ -1034,23 +1036,31 @@ def main() -> int:
         result["chunk_sweep_ms"] = sweep
         w1 = synth.WORKLOADS[1]
         log("linear-time check: N = 2048")
-        ms1, _, _, _ = bench_prefill(oal, w1, args.chunk, args.steps, args.warmup, device)
+        ms1, _, _, ms1_graph = bench_prefill(oal, w1, args.chunk, args.steps, args.warmup, device)
         result["linear_time_check"] = {"ms_n2048": round(ms1, 5), "ms_n32768": round(ms, 5),
                                        "ratio": round(ms / ms1, 3), "ideal_ratio": 16.0}
+        if ms1_graph is not None and ms_graph is not None:
+            # the same two steps replayed from HIP graphs (no host launch cost)
+            result["linear_time_check"].update({
+                "ms_n2048_graph": round(ms1_graph, 5), "ms_n32768_graph": round(ms_graph, 5),
+                "ratio_graph": round(ms_graph / ms1_graph, 3)})
         # the long prefill's first N tokens, N doubling up to the full length:
         # ms per step and the ratio to the half length (2 for linear time)
-        curve = {}
+        curve, curve_g = {}, {}
         for n in (2048, 4096, 8192, 16384):
             log(f"length scaling: first {n} tokens")
             wn = dataclasses.replace(w3, seq_len=n)
-            curve[n] = bench_prefill(oal, wn, args.chunk, args.steps, args.warmup, device)[0]
-        curve[w3.seq_len] = ms
+            r = bench_prefill(oal, wn, args.chunk, args.steps, args.warmup, device)
+            curve[n], curve_g[n] = r[0], r[3]
+        curve[w3.seq_len], curve_g[w3.seq_len] = ms, ms_graph
         ns = sorted(curve)
         result["length_scaling"] = {
             "workload": f"{w3.name}, first N tokens", "chunk": args.chunk,
             "ms_per_step": {str(n): round(curve[n], 5) for n in ns},
             "ratio_to_half_length": {str(n): round(curve[n] / curve[n // 2], 3) for n in ns[1:]},
             "tokens_per_s": {str(n): round(n * w3.batch / (curve[n] * 1e-3), 1) for n in ns}}
+        if all(curve_g[n] is not None for n in ns):
+            result["length_scaling"]["ms_per_step_graph"] = {str(n): round(curve_g[n], 5) for n in ns}
         w2 = synth.WORKLOADS[2]
         log(f"prefill: {w2.name}, chunk {args.chunk}")
         ms2, kt2, _, _ = bench_prefill(oal, w2, args.chunk, args.steps, args.warmup, device)

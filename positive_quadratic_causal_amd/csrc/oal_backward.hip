@@ -22,8 +22,9 @@
 //
 // Kernels, in launch order:
 //   prefix build + scan (oal_prefill_vec.hip)  H_{<c}
-//   k_bwd_query     four (chunk 64) or two threads per query: recompute u~_i, g_i; the pair
-//                   part of dq_i; alpha rows
+//   k_bwd_ustate    the state part of u~_i: Phi(q) H_{<c} (to the g rows)
+//   k_bwd_query     four (chunk 64) or two threads per query: the pair part of u~_i, g_i; the
+//                   pair part of dq_i; alpha rows
 //   k_bwd_dqstate   the state part of dq_i: H_{<c} g_i against d psi(q_i) / dq_i, by pair rows
 //   k_bwd_rbuild    per chunk: sum_h c_f psi_f(q_i) g_i^T (suffix deltas) and the
 //                   state part of dc: sum_i psi_f(q_i) (H_{<c} g_i)_f
@@ -356,6 +357,129 @@ size_t backward_workspace(int batch, int n_q_heads, int n_kv_heads, int seq_len,
 }
 
 // ---------------------------------------------------------------------------
+// State part of u~ for the query kernel:  U[tok][w] = sum_f c_f psi_f(q_tok)
+// H_{<c}[f][w], w <= 64, written to the token's g row of the workspace (the query
+// kernel reads the row there before it writes g over it).  Block (32 tokens of a
+// chunk, chunk, query head), two waves: wave = tile of 32 channels, channel 64 (the
+// denominator's) on the VALU of every lane.  K = the features in 34 blocks of 64,
+// product j of a block pairing feature f0 + j (lanes 0-31) with f0 + 32 + j (lanes
+// 32-63), so that a lane's B operands H[f][w] over the block are 32 consecutive
+// features of its channel: eight 16-byte loads, issued two blocks ahead in two
+// register sets.  A = c_f psi_f(q_tok) formed per lane from the q rows and the
+// feature table (psi_f = q~[ia] q~[ib], q~ = (q, 1)); features past DCAN (state
+// padding, never written) are dropped.  The blocks of one (unit, chunk) share an XCD.
+constexpr int US_TG = 32;   // tokens per block
+template <typename T>
+__global__ void __launch_bounds__(128)
+k_bwd_ustate(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunks, int n_units,
+             const T* __restrict__ q, const void* __restrict__ coeffs,
+             const float* __restrict__ hc, float* __restrict__ gbuf) {
+  constexpr int TG = US_TG;
+  constexpr int QS = DH + 1;             // q~ row: q, 1
+  constexpr int NB = DS / 64;            // feature blocks
+  static_assert(NB % 2 == 0 && DS % 64 == 0, "feature blocks taken in pairs");
+  const int rep = n_q_heads / n_kv_heads;
+  const int per = rep * (chunk / TG);    // blocks of one (unit, chunk)
+  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  const int uc = (slot / per) * 8 + xcd;
+  if (uc >= n_units * n_chunks) return;
+  const int unit = uc / n_chunks, c = uc % n_chunks;
+  const int b = unit / n_kv_heads;
+  const int hq = (unit % n_kv_heads) * rep + (slot % per) % rep;
+  const int t0 = c * chunk + ((slot % per) / rep) * TG;
+  const int ntok = min(TG, seq_len - t0);
+  if (ntok <= 0) return;                 // a group past the sequence (whole block)
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int CT = __builtin_amdgcn_readfirstlane(tid >> 6);   // the wave's channel tile
+  const int tok = lane & 31, h = lane >> 5;
+
+  __shared__ float s_q[TG * QS];
+  __shared__ uint16_t s_fd[DS];          // ia | ib << 8
+  __shared__ float s_fc[DS];             // c_f, zero past DCAN
+  const float* rec = coef_rec(coeffs, hq);
+  const float* Hc = hc + ((size_t)unit * n_chunks + c) * STATE_FLOATS;
+  const size_t row0 = ((size_t)b * n_q_heads + hq) * seq_len + t0;
+  stage_span<TG * DH, 128>(tid, ntok * DH, [&](int i) { return Elem<T>::load(q + row0 * DH, i); },
+                           [&](int i, float x) { s_q[(i / DH) * QS + i % DH] = x; });
+  if (tid < TG) s_q[tid * QS + DH] = 1.f;
+  for (int f = tid; f < DS; f += 128) {
+    int r, t;
+    const int kind = feat_decode(f, r, t);
+    s_fd[f] = (uint16_t)((kind == 0 ? DH : r) | ((kind == 2 ? t : DH) << 8));
+  }
+  stage_span<DS, 128>(tid, DCAN, [&](int f) { return rec[coef_index(f)]; },
+                      [&](int f, float x) { s_fc[f] = x; });
+
+  // B operands H[f0 + 32 h + j][w] of the lane's channel w, and the same features
+  // of the denominator's channel (j = 4 m + e); the block offset f0 is a multiple
+  // of 64 and a state row is 16-byte aligned, so the loads are aligned
+  struct Ops {
+    float4 hb[8], hd[8];
+  };
+  const float* hbp = Hc + (size_t)(32 * CT + tok) * DS + 32 * h;
+  const float* hdp = Hc + (size_t)DV * DS + 32 * h;
+  auto fetch = [&](int blk, Ops& o) __attribute__((always_inline)) {
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      o.hb[m] = *reinterpret_cast<const float4*>(hbp + 64 * blk + 4 * m);
+      o.hd[m] = *reinterpret_cast<const float4*>(hdp + 64 * blk + 4 * m);
+    }
+  };
+  fx16 D[2];
+#pragma unroll
+  for (int x = 0; x < 2; ++x)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) D[x][i] = 0.f;
+  float dacc = 0.f;
+  const float* qrow = s_q + tok * QS;
+  auto run = [&](int blk, Ops& o) __attribute__((always_inline)) {
+    const int fb = 64 * blk + 32 * h;     // the lane's first feature of the block
+    const bool tail = 64 * blk + 64 > DCAN;   // uniform: the block reaching into the padding
+#pragma unroll
+    for (int j0 = 0; j0 < 32; j0 += 8) {
+      float av[8], bv[8], dv[8];
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {
+        const int j = j0 + jj;
+        const int d = s_fd[fb + j];
+        av[jj] = s_fc[fb + j] * qrow[d & 255] * qrow[d >> 8];
+        const float4 x = o.hb[j >> 2], y = o.hd[j >> 2];
+        bv[jj] = (j & 3) == 0 ? x.x : (j & 3) == 1 ? x.y : (j & 3) == 2 ? x.z : x.w;
+        dv[jj] = (j & 3) == 0 ? y.x : (j & 3) == 1 ? y.y : (j & 3) == 2 ? y.z : y.w;
+        if (tail && fb + j >= DCAN) {   // padding rows of the state: any bits
+          bv[jj] = 0.f;
+          dv[jj] = 0.f;
+        }
+      }
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {
+        D[jj & 1] = mfma_f32(av[jj], bv[jj], D[jj & 1]);
+        dacc = fmaf(av[jj], dv[jj], dacc);
+      }
+    }
+    fetch(min(blk + 2, NB - 1), o);   // unconditional: the last blocks reload one
+  };
+  Ops oa, ob;
+  fetch(0, oa);
+  fetch(1, ob);
+  __syncthreads();   // the q rows and the feature table are in LDS
+  for (int blk = 0; blk < NB; blk += 2) {
+    run(blk, oa);
+    run(blk + 1, ob);
+  }
+  // out: D rows are tokens mrow(i, h), columns the channels; the two lane halves'
+  // denominator sums added
+  dacc += __shfl_xor(dacc, 32, 64);
+  float* gr = gbuf + (((size_t)b * n_q_heads + hq) * ((size_t)n_chunks * chunk) + t0) * WP;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int r = mrow(i, h);
+    if (r < ntok) gr[(size_t)r * WP + 32 * CT + tok] = D[0][i] + D[1][i];
+  }
+  if (CT == 0 && h == 0 && tok < ntok) gr[(size_t)tok * WP + DV] = dacc;
+}
+
+// ---------------------------------------------------------------------------
 // Query side.  One block per (chunk, query head, batch); SP threads per query
 // (thread SP i + h, h = 0 .. SP - 1, for query t0 + i; SP = 4 at chunk 64, 2 at
 // chunk 128) split its features and its pairs round robin; the parts of u~_i are
@@ -366,8 +490,7 @@ __global__ void __launch_bounds__(256)
 k_bwd_query(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunks, int n_units,
             const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
             const void* __restrict__ coeffs, const float* __restrict__ dy,
-            const float* __restrict__ hc, float* __restrict__ gbuf, float* __restrict__ alpha,
-            float* __restrict__ dq) {
+            float* __restrict__ gbuf, float* __restrict__ alpha, float* __restrict__ dq) {
   // the query heads of one (unit, chunk) in consecutive slots of one XCD
   // (workgroup id % 8), so that they read that chunk's prefix state through one L2
   const int rep = n_q_heads / n_kv_heads;
@@ -406,21 +529,6 @@ k_bwd_query(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunks,
   }
   for (int i = tid; i < chunk; i += nthr) s_q[i * (DH + 1) + DH] = 1.f;   // psi's constant slot
   for (int i = tid; i < SP * chunk * (DH + 1); i += nthr) s_dq[i] = 0.f;
-  // feature descriptors for the state part of step 1, in the staged keys' rows
-  // (free until the pairs of step 1): psi_f(q) = q~[ia] q~[ib] with q~ = (q, 1),
-  // i.e. (64, 64) for the constant, (r, 64) for x_r, (r, t) for a pair; and c_f
-  // (zero on the padding rows DCAN .. DS - 1)
-  uint16_t* s_fd = reinterpret_cast<uint16_t*>(s_k);
-  float* s_fc = s_k + DS / 2;
-  static_assert(DS / 2 + DS <= TB * (DH + 1), "descriptors fit the staged keys' rows");
-  for (int f = tid; f < DS; f += nthr) {
-    int r, t;
-    const int kind = feat_decode(f, r, t);
-    const int ia = kind == 0 ? DH : r, ib = kind == 2 ? t : DH;
-    s_fd[f] = (uint16_t)(ia | (ib << 8));
-  }
-  stage_span<DS>(tid, DCAN, [&](int f) { return rec[coef_index(f)]; },
-                 [&](int f, float x) { s_fc[f] = x; });
   for (int i = tid; i < DH; i += nthr) s_b[i] = rec[OAL_COEF_BP + i];
   stage_span<DH * DH>(tid, DH * DH, [&](int i) { return rec[OAL_COEF_CM + i]; },
                       [&](int i, float x) { s_S[i] = x; });
@@ -429,7 +537,6 @@ k_bwd_query(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunks,
   const bool fast = grouped && gt.n_out <= MAX_OUT;   // uniform over the block
   const float* qi = s_q + qx * (DH + 1);
   float* dqi = s_dq + (half * chunk + qx) * (DH + 1);
-  const float* Hc = hc + ((size_t)unit * n_chunks + c) * STATE_FLOATS;
   const size_t kbase = (size_t)unit * seq_len + t0;
 
   auto stage_keys = [&](int j0, int nj) {
@@ -449,115 +556,8 @@ k_bwd_query(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunks,
     for (int jj = tid; jj < TB; jj += nthr) s_u[jj * WP + DV] = jj < nj ? 1.f : 0.f;
   };
 
-  // ---- 1. recompute u~_i.  State part on the fp32 matrix cores:
-  //   U[tok][w] = sum_f c_f psi_f(q_tok) H_{<c}[f][w],  w < 64,
-  // over staged 64-feature blocks, two features per product; token tiles of 32
-  // rows (A: lane l forms c_f psi_f(q) of token 32 TT + l % 32 and feature
-  // f0 + 2 j + l / 32 in place) against channel tiles of 32 (B: the staged block).
-  // Chunk 64 (SP 4): wave = (token tile wave % 2, channel tile wave / 2); chunk 128
-  // (SP 2): wave = token tile, both channel tiles.  The all-ones channel w = 64 is a
-  // multiply-add per product (kept from the waves of channel tile 0).  U and that channel go
-  // to part 0's dq rows (unused until step 3) and are added in step 2.
-  constexpr int NCT = SP == 4 ? 1 : 2;            // channel tiles per wave
-  static_assert(SP * 64 == 256 || SP * 128 == 256, "chunk 64 or 128");
-  {
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
-    const int TT = SP == 4 ? (wave & 1) : wave;
-    const int CT0 = SP == 4 ? (wave >> 1) : 0;
-    const int kpar = lane >> 5;
-    fx16 U[2][NCT];   // two chains (even and odd products), added at the end
-#pragma unroll
-    for (int x = 0; x < 2; ++x)
-#pragma unroll
-      for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) U[x][ct][i] = 0.f;
-    float dpart = 0.f;
-    // 64-feature blocks of H_{<c} staged in the value rows s_u (64 x WP, free until
-    // the pairs), each fetched into registers one block ahead
-    constexpr int FB1 = 64;
-    constexpr int PB1 = (FB1 * W + 255) / 256;
-    float pre1[PB1];
-    auto fetch1 = [&](int f0) {
-#pragma unroll
-      for (int e = 0; e < PB1; ++e) {
-        const int i = tid + e * 256;
-        if (i < FB1 * W) pre1[e] = Hc[(size_t)(i / FB1) * DS + f0 + i % FB1];   // f0 + 63 < DS
-      }
-    };
-    // the block's A operand c_f psi_f(q_tok), formed by all threads into part 1's dq
-    // rows (free until step 2) as [feature][token], the token index XOR 32 on odd
-    // features so that the two lane halves of a product read distinct banks
-    float* s_A = s_dq + chunk * (DH + 1);
-    static_assert(FB1 <= DH + 1, "the A tile fits one part's dq rows");
-    constexpr int NA = FB1 * 256 / SP / 256;   // A values per thread: FB1 x chunk / 256
-    fetch1(0);
-    for (int f0 = 0; f0 < DCAN; f0 += FB1) {
-      __syncthreads();
-#pragma unroll
-      for (int e = 0; e < PB1; ++e) {
-        const int i = tid + e * 256;
-        if (i < FB1 * W) s_u[(i % FB1) * WP + i / FB1] = pre1[e];
-      }
-      if (f0 + FB1 < DCAN) fetch1(f0 + FB1);
-#pragma unroll
-      for (int e = 0; e < NA; ++e) {
-        const int v = tid + 256 * e, ff = v / chunk, tok = v % chunk;
-        const int d = s_fd[f0 + ff];
-        const float* qt = s_q + tok * (DH + 1);
-        s_A[ff * chunk + (tok ^ ((ff & 1) << 5))] = s_fc[f0 + ff] * qt[d & 255] * qt[d >> 8];
-      }
-      __syncthreads();
-      const float* arow = s_A + kpar * chunk + ((32 * TT + (lane & 31)) ^ (kpar << 5));
-      const float* hrow = s_u + kpar * WP;   // feature kpar of the block; + 2 j WP for product j
-      // straight-line groups of 8 products, each group's LDS reads issued before its
-      // products; every wave also forms the all-ones channel (kept by channel tile 0)
-      auto products = [&](auto check_t) __attribute__((always_inline)) {
-        constexpr bool CHECK = decltype(check_t)::value;   // the last block: rows past DCAN
-#pragma unroll
-        for (int j0 = 0; j0 < FB1 / 2; j0 += 8) {
-          float av[8], bv[8][NCT], hv[8];
-#pragma unroll
-          for (int jj = 0; jj < 8; ++jj) {
-            const int j = j0 + jj;
-            av[jj] = arow[2 * j * chunk];
-#pragma unroll
-            for (int ct = 0; ct < NCT; ++ct) bv[jj][ct] = hrow[2 * j * WP + 32 * (CT0 + ct) + (lane & 31)];
-            hv[jj] = hrow[2 * j * WP + DV];
-            if (CHECK && f0 + 2 * j + kpar >= DCAN) {
-              av[jj] = 0.f;
-              hv[jj] = 0.f;
-#pragma unroll
-              for (int ct = 0; ct < NCT; ++ct) bv[jj][ct] = 0.f;
-            }
-          }
-#pragma unroll
-          for (int jj = 0; jj < 8; ++jj) {
-#pragma unroll
-            for (int ct = 0; ct < NCT; ++ct) U[jj & 1][ct] = mfma_f32(av[jj], bv[jj][ct], U[jj & 1][ct]);
-            dpart = fmaf(av[jj], hv[jj], dpart);
-          }
-        }
-      };
-      if (f0 + FB1 <= DCAN)
-        products(std::integral_constant<bool, false>{});
-      else
-        products(std::integral_constant<bool, true>{});
-    }
-#pragma unroll
-    for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) U[0][ct][i] += U[1][ct][i];
-    float* urow0 = s_dq + 32 * TT * (DH + 1);   // part 0's rows of token tile TT
-#pragma unroll
-    for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-      for (int i = 0; i < 16; ++i)
-        urow0[mrow(i, kpar) * (DH + 1) + 32 * (CT0 + ct) + (lane & 31)] = U[0][ct][i];
-    dpart += __shfl_xor(dpart, 32, 64);
-    if (CT0 == 0 && kpar == 0) urow0[(lane & 31) * (DH + 1) + DV] = dpart;   // channel tile 0's
-  }
-  // the chunk's pairs, on the vector ALUs: this part's share
+  // ---- 1. u~_i: the state part U was written to this query's g row by
+  // k_bwd_ustate; here the chunk's pairs, on the vector ALUs: this part's share
   float acc[WP];
 #pragma unroll
   for (int w = 0; w < WP; ++w) acc[w] = 0.f;
@@ -596,13 +596,10 @@ k_bwd_query(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunks,
 #pragma unroll
       for (int w = 0; w < W; ++w) acc[w] += pr[w];
     }
-    // + the state part (this part's own row, written in step 1), the row cleared
-    // for the dq sums of step 3
+    // + the state part, read from the g row before g overwrites it
+    const float* ur = gbuf + (((size_t)b * n_q_heads + hq) * ((size_t)n_chunks * chunk) + t0 + qx) * WP;
 #pragma unroll
-    for (int w = 0; w < W; ++w) {
-      acc[w] += xrow[w];
-      xrow[w] = 0.f;
-    }
+    for (int w = 0; w < W; ++w) acc[w] += ur[w];
     if (active) {
       const float inv = 1.0f / acc[DV];
       const float* dyi = dy + (qrow0 + qx) * DV;
@@ -1534,6 +1531,14 @@ static oal_status backward_typed(int batch, int n_q_heads, int n_kv_heads, int s
   oal_status st = launch_prefix_vec(batch, n_kv_heads, seq_len, chunk, in_dtype, k, v, w.hc, stream);
   if (st != OAL_OK) return st;
   {
+    const int per = (n_q_heads / n_kv_heads) * (chunk / US_TG);
+    const dim3 grid((unsigned)(((size_t)units * n_chunks + 7) / 8 * 8 * (size_t)per));
+    ProfScope ps("k_bwd_ustate", stream);
+    hipLaunchKernelGGL(k_bwd_ustate<T>, grid, dim3(128), 0, stream, n_q_heads, n_kv_heads, seq_len,
+                       chunk, n_chunks, units, qq, coeffs, w.hc, w.gbuf);
+    if ((st = check_launch("k_bwd_ustate")) != OAL_OK) return st;
+  }
+  {
     // four threads per query at chunk 64 (256 threads, 143 KB of LDS), two at 128;
     // the kernel's state staging assumes SP * chunk = 256
     const int sp = chunk <= 64 ? 4 : 2;
@@ -1549,11 +1554,11 @@ static oal_status backward_typed(int batch, int n_q_heads, int n_kv_heads, int s
     if (sp == 4)
       hipLaunchKernelGGL((k_bwd_query<T, 4>), grid_q, dim3(4 * chunk), smem,
                          stream, n_q_heads, n_kv_heads, seq_len, chunk, n_chunks, units, qq, kk, vv, coeffs, dy,
-                         w.hc, w.gbuf, w.alpha, dq);
+                         w.gbuf, w.alpha, dq);
     else
       hipLaunchKernelGGL((k_bwd_query<T, 2>), grid_q, dim3(2 * chunk), smem,
                          stream, n_q_heads, n_kv_heads, seq_len, chunk, n_chunks, units, qq, kk, vv, coeffs, dy,
-                         w.hc, w.gbuf, w.alpha, dq);
+                         w.gbuf, w.alpha, dq);
     if ((st = check_launch("k_bwd_query")) != OAL_OK) return st;
   }
   {
