@@ -308,7 +308,7 @@ struct BwdWs {
   float* rc;      // [units][n_chunks][STATE_FLOATS]  suffix deltas, then R_{>c}
   float* gbuf;    // [batch][Hq][n_chunks * chunk][WP] g rows (zero beyond seq_len)
   float* alpha;   // [batch][Hq][n_chunks][chunk][chunk] alpha_ij (zero for j > i)
-  float* dcp;     // [batch][Hq][n_chunks][DS] per-chunk parts of dc
+  float* dcp;     // [DC_PARTS][batch][Hq][n_chunks][DS] per-chunk parts of dc
   float* kpart;   // [units][KS (rep + 1)][n_chunks * chunk][128] parts of [dk | dv]
   size_t bytes;
 };
@@ -321,6 +321,7 @@ static int key_split(int chunk) { return chunk <= 64 ? 4 : 2; }
 // ranges, one workgroup (and one set of parts) each: it walks all 2145 features
 // while the pair slots meet one chunk of queries, and would otherwise set the
 // kernel's length alone.
+constexpr int DC_PARTS = 4;  // parts of the per-chunk dc: the four waves of k_bwd_rbuild (dc_intra adds to part 0)
 constexpr int KS_NFS = 4;   // feature splits of the key side's state part (k_bwd_kstate)
 
 static BwdWs bwd_ws(void* base, int batch, int n_q_heads, int n_kv_heads, int seq_len, int chunk) {
@@ -337,7 +338,7 @@ static BwdWs bwd_ws(void* base, int batch, int n_q_heads, int n_kv_heads, int se
   const size_t o_r = take(units * nc * STATE_FLOATS);
   const size_t o_g = take(bh * nc * chunk * WP);
   const size_t o_a = take(bh * nc * chunk * chunk);
-  const size_t o_d = take(bh * nc * DS);
+  const size_t o_d = take(DC_PARTS * bh * nc * DS);
   const size_t o_k = take(units * ((size_t)key_split(chunk) * (n_q_heads / n_kv_heads) + KS_NFS) * nc * chunk *
                           (DH + DV));
   BwdWs w;
@@ -860,7 +861,7 @@ k_bwd_dqstate(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunk
 // w = 16 (tid >> 6) + j, j < 16, and the all-ones channel on the fourth wave, which
 // adds c_f R_h into the suffix delta and H_{<c} . R_h into the state part of dc.
 template <typename T>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(256, 2)   // two blocks per CU: 256 registers a lane
 k_bwd_rbuild(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunks,
              const T* __restrict__ q, const void* __restrict__ coeffs,
              const float* __restrict__ gbuf, const float* __restrict__ hc,
@@ -876,7 +877,6 @@ k_bwd_rbuild(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunks
   __shared__ float s_q[TB][DH + 1];                          // q~ = (q, 1) rows, zero past the sequence
   __shared__ __attribute__((aligned(16))) float s_g[TB][WP];
   __shared__ __attribute__((aligned(16))) float s_R[FB][WP];  // R_h of the block
-  __shared__ float s_red[4][FB];
   int r, t;
   const int kind = feat_decode(f, r, t);
   const size_t slot = ((size_t)unit * n_chunks + c) * STATE_FLOATS;
@@ -901,6 +901,12 @@ k_bwd_rbuild(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunks
   const int t0 = c * chunk;
   const int t1 = min(seq_len, t0 + chunk);
   const size_t npad = (size_t)n_chunks * chunk;
+  // Two barriers per head (chunk 64): one after the staging, one after R_h is in
+  // LDS.  The staging of a head follows the last one's reads of s_R in program
+  // order, and its products' reads of s_q and s_g precede that head's R_h
+  // barrier.  Each wave stores its own part of the state part of dc (its columns);
+  // k_bwd_dcoef adds the DC_PARTS parts.
+  const size_t dc_stride = (size_t)gridDim.z / n_kv_heads * n_q_heads * n_chunks * DS;   // one part
   for (int hh = 0; hh < rep; ++hh) {
     const int hq = kv * rep + hh;
     const float cf = coef_of(coef_rec(coeffs, hq), f);
@@ -914,32 +920,14 @@ k_bwd_rbuild(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunks
     const size_t grow0 = ((size_t)b * n_q_heads + hq) * npad;
     for (int i0 = t0; i0 < t1; i0 += TB) {
       const int ni = min(TB, t1 - i0);
-      __syncthreads();
-      // the q and g rows of the tile are contiguous in memory: every load of the
-      // 256 threads is issued before the first is awaited
+      if (i0 > t0) __syncthreads();   // the previous token tile's products are done
+      // the q and g rows of the tile are contiguous in memory, one span each
       const T* qt = q + (qrow0 + i0) * DH;
       const float* gt = gbuf + (grow0 + i0) * WP;
-      float lq[TB * DH / 256], lg[TB * WP / 256];
-#pragma unroll
-      for (int e = 0; e < TB * DH / 256; ++e) {
-        const int i = tid + 256 * e;
-        lq[e] = i < ni * DH ? Elem<T>::load(qt, i) : 0.f;
-      }
-#pragma unroll
-      for (int e = 0; e < TB * WP / 256; ++e) {
-        const int i = tid + 256 * e;
-        lg[e] = i < ni * WP ? gt[i] : 0.f;
-      }
-#pragma unroll
-      for (int e = 0; e < TB * DH / 256; ++e) {
-        const int i = tid + 256 * e;
-        s_q[i / DH][i % DH] = lq[e];
-      }
-#pragma unroll
-      for (int e = 0; e < TB * WP / 256; ++e) {
-        const int i = tid + 256 * e;
-        s_g[i / WP][i % WP] = lg[e];
-      }
+      stage_span<TB * DH>(tid, ni * DH, [&](int i) { return Elem<T>::load(qt, i); },
+                          [&](int i, float x) { s_q[i / DH][i % DH] = x; });
+      stage_span<TB * WP>(tid, ni * WP, [&](int i) { return gt[i]; },
+                          [&](int i, float x) { s_g[i / WP][i % WP] = x; });
       if (tid < TB) s_q[tid][DH] = tid < ni ? 1.f : 0.f;
       __syncthreads();
 #pragma unroll
@@ -959,7 +947,7 @@ k_bwd_rbuild(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunks
         }
       }
     }
-    // R_h to LDS (the previous head's readers are done: the token loop's barrier)
+    // R_h to LDS (the previous head's readers are done: the staging barrier)
 #pragma unroll
     for (int i = 0; i < 16; ++i) s_R[32 * FT + mrow(i, kpar)][32 * WT + (lane & 31)] = D[0][i] + D[1][i];
     d64 += __shfl_xor(d64, 32, 64);
@@ -973,13 +961,8 @@ k_bwd_rbuild(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunks
       rd[j] = fmaf(cf, x, rd[j]);
       part = fmaf(hval[j], x, part);
     }
-    if (dcp != nullptr) {
-      s_red[wq][tid & 63] = part;
-      __syncthreads();
-      if (wq == 0)
-        dcp[(((size_t)b * n_q_heads + hq) * n_chunks + c) * DS + f] =
-            kind == 3 ? 0.f : s_red[0][tid] + s_red[1][tid] + s_red[2][tid] + s_red[3][tid];
-    }
+    if (dcp != nullptr)
+      dcp[wq * dc_stride + (((size_t)b * n_q_heads + hq) * n_chunks + c) * DS + f] = kind == 3 ? 0.f : part;
   }
 #pragma unroll
   for (int j = 0; j < WPT; ++j) {
@@ -1431,9 +1414,12 @@ k_bwd_dcoef(int batch, int n_q_heads, int n_chunks, const float* __restrict__ dc
   const int hq = blockIdx.y;
   if (f >= DCAN) return;
   float s = 0.f;
+  const size_t part = (size_t)batch * n_q_heads * n_chunks * DS;
   for (int b = 0; b < batch; ++b) {
     const float* p = dcp + ((size_t)b * n_q_heads + hq) * n_chunks * DS + f;
-    for (int c = 0; c < n_chunks; ++c) s += p[(size_t)c * DS];
+    for (int c = 0; c < n_chunks; ++c)
+#pragma unroll
+      for (int k = 0; k < DC_PARTS; ++k) s += p[k * part + (size_t)c * DS];
   }
   int r, t;
   const int kind = feat_decode(f, r, t);
