@@ -75,22 +75,11 @@ __device__ __forceinline__ int feat_decode(int f, int& r, int& t) {
     return 1;
   }
   if (f < DCAN) {
-    // pair p = pair_index(r, t): row r starts at S(r) = r (2 DH + 1 - r) / 2, so r is
-    // the floor of the smaller root of S(r) = p, corrected by one either way for the
-    // rounding of the square root (exact for all 2080 pairs; no table read)
-    const int p = f - 1 - DH;
-    int rr = (int)((129.f - __builtin_sqrtf(16641.f - 8.f * (float)p)) * 0.5f);
-    if (rr * (129 - rr) / 2 > p)
-      --rr;
-    else if ((rr + 1) * (128 - rr) / 2 <= p)
-      ++rr;
-    r = rr;
-    t = p - rr * (129 - rr) / 2 + rr;
+    pair_decode(f - 1 - DH, r, t);
     return 2;
   }
   return 3;
 }
-static_assert(DH == 64, "the pair decode's constants are for d_h = 64");
 static_assert(TB * DH % 256 == 0 && TB * WP % 256 == 0, "staging by 256 threads");
 
 // Row blocks of the features with a gradient, 64 feature slots each.  Block b < 32:

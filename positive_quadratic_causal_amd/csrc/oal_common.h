@@ -47,6 +47,22 @@ __host__ __device__ constexpr inline int pair_index(int r, int t) {
   return r * DH - r * (r - 1) / 2 + (t - r);
 }
 
+// The pair (r, t), r <= t, of packed index p = pair_index(r, t), by arithmetic: row r
+// starts at S(r) = r (2 DH + 1 - r) / 2, so r is the floor of the smaller root of
+// S(r) = p, corrected by one either way for the rounding of the square root (exact
+// for all NPAIR pairs).  No table read: a lane-indexed table load inside a branch
+// would be awaited on the spot.
+__device__ __forceinline__ void pair_decode(int p, int& r, int& t) {
+  int rr = (int)((129.f - __builtin_sqrtf(16641.f - 8.f * (float)p)) * 0.5f);
+  if (rr * (129 - rr) / 2 > p)
+    --rr;
+  else if ((rr + 1) * (128 - rr) / 2 <= p)
+    ++rr;
+  r = rr;
+  t = p - rr * (129 - rr) / 2 + rr;
+}
+static_assert(DH == 64, "pair_decode's constants are for d_h = 64");
+
 // ---- element access ------------------------------------------------------
 
 __device__ __forceinline__ float bf16_bits_to_float(uint16_t b) {

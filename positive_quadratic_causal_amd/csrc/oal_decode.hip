@@ -17,10 +17,6 @@
 
 namespace oal {
 
-namespace {
-__constant__ PairTable c_dec_pairs = PairTable();
-}
-
 template <typename T, typename O, int HG>
 __global__ void __launch_bounds__(256)
 k_decode(int n_q_heads, int n_kv_heads, int head0, int nh, int update,
@@ -46,23 +42,38 @@ k_decode(int n_q_heads, int n_kv_heads, int head0, int nh, int update,
     s_u[tid] = Elem<T>::load(v, (size_t)unit * DV + tid);
   }
   if (tid == 0) s_u[DV] = 1.0f;
-  for (int i = tid; i < nh * DH; i += blockDim.x) {
-    int hh = i / DH, r = i % DH;
-    int hq = kv * rep + head0 + hh;
-    s_q[hh][r] = Elem<T>::load(q, ((size_t)b * n_q_heads + hq) * DH + r);
+  {
+    // the q rows of the group's nh heads are one span (blockDim.x = 256); loads
+    // unconditional (clamped), all issued before the first is awaited
+    const T* qs = q + ((size_t)b * n_q_heads + kv * rep + head0) * DH;
+    float x[HG * DH / 256 > 0 ? HG * DH / 256 : 1];
+    constexpr int QE = HG * DH / 256 > 0 ? HG * DH / 256 : 1;
+#pragma unroll
+    for (int e = 0; e < QE; ++e) x[e] = Elem<T>::load(qs, min(tid + 256 * e, nh * DH - 1));
+#pragma unroll
+    for (int e = 0; e < QE; ++e) {
+      const int i = tid + 256 * e;
+      if (i < nh * DH) s_q[i / DH][i % DH] = x[e];
+    }
   }
   __syncthreads();
 
+  // feature decode by arithmetic (no table loads), a constant trip count
+  constexpr int FIT = (DS + 255) / 256;   // features per thread
   float* phik = reinterpret_cast<float*>(s_phik4);
-  for (int f = tid; f < DS; f += blockDim.x) {
+#pragma unroll
+  for (int i = 0; i < FIT; ++i) {
+    const int f = tid + 256 * i;
+    if (f >= DS) break;
     float pk;
     if (f == 0) {
       pk = 1.0f;
     } else if (f <= DH) {
       pk = s_k[f - 1];
     } else if (f < DCAN) {
-      uint16_t rt = c_dec_pairs.rt[f - 1 - DH];
-      pk = s_k[rt >> 8] * s_k[rt & 0xff];
+      int r, t;
+      pair_decode(f - 1 - DH, r, t);
+      pk = s_k[r] * s_k[t];
     } else {
       pk = 0.f;
     }
@@ -71,7 +82,6 @@ k_decode(int n_q_heads, int n_kv_heads, int head0, int nh, int update,
   // query features of every head: the coefficient of feature f (a, b'_r or the
   // packed c'_rt) comes from the head's record; all of a thread's coefficient
   // loads are issued before the first is used
-  constexpr int FIT = (DS + 255) / 256;   // features per thread
 #pragma unroll
   for (int hh = 0; hh < HG; ++hh) {
     if (hh >= nh) break;
@@ -95,8 +105,9 @@ k_decode(int n_q_heads, int n_kv_heads, int head0, int nh, int update,
       } else if (f <= DH) {
         pq = cf[i] * s_q[hh][f - 1];
       } else if (f < DCAN) {
-        const uint16_t rt = c_dec_pairs.rt[f - 1 - DH];
-        pq = cf[i] * s_q[hh][rt >> 8] * s_q[hh][rt & 0xff];
+        int r, t;
+        pair_decode(f - 1 - DH, r, t);
+        pq = cf[i] * s_q[hh][r] * s_q[hh][t];
       } else {
         pq = 0.f;
       }
@@ -111,13 +122,10 @@ k_decode(int n_q_heads, int n_kv_heads, int head0, int nh, int update,
   // columns col, col + 4, ..: the next column's loads are issued before the
   // current one is processed (two columns in flight per wave)
   float4 hn[IT];
-  auto load_col = [&](int c) {
-    const float4* src = st4 + (size_t)c * N4;
+  auto load_col = [&](int c) {   // unconditional (clamped): a load inside a branch
+    const float4* src = st4 + (size_t)c * N4;   // would be awaited on the spot
 #pragma unroll
-    for (int it = 0; it < IT; ++it) {
-      const int i4 = lane + 64 * it;
-      if (i4 < N4) hn[it] = src[i4];
-    }
+    for (int it = 0; it < IT; ++it) hn[it] = src[min(lane + 64 * it, N4 - 1)];
   };
   if (wave < W) load_col(wave);
   for (int col = wave; col < W; col += 4) {
