@@ -116,35 +116,11 @@ __device__ __forceinline__ int row_block_feature(int blk, const RowBlk& d, int s
   return -1;
 }
 
-// record index of c_f for a feature f < DCAN (no branch: for loads that must not
-// wait in a divergent block)
-__device__ __forceinline__ int coef_index(int f) {
-  return f == 0 ? OAL_COEF_A : (f <= DH ? OAL_COEF_BP + f - 1 : OAL_COEF_CP + f - 1 - DH);
-}
-
 __device__ __forceinline__ float coef_of(const float* rec, int f) {
   if (f == 0) return rec[OAL_COEF_A];
   if (f <= DH) return rec[OAL_COEF_BP + f - 1];
   if (f < DCAN) return rec[OAL_COEF_CP + f - 1 - DH];
   return 0.f;
-}
-
-// LDS staging of a contiguous span by a block of NT threads: element i < N (the
-// tile's capacity) gets load(i) for i < n and zero beyond (1 <= n <= N).  The loads
-// are unconditional (index clamped to n - 1) and all issued before the first is
-// awaited: a loop striding by blockDim.x is not unrolled, so each element would
-// wait for its own load, and a load in a divergent block is awaited at its end.
-template <int N, int NT = 256, typename Load, typename Store>
-__device__ __forceinline__ void stage_span(int tid, int n, Load load, Store store) {
-  constexpr int E = (N + NT - 1) / NT;
-  float x[E];
-#pragma unroll
-  for (int e = 0; e < E; ++e) x[e] = load(min(tid + NT * e, n - 1));
-#pragma unroll
-  for (int e = 0; e < E; ++e) {
-    const int i = tid + NT * e;
-    if (i < N) store(i, i < n ? x[e] : 0.f);
-  }
 }
 
 // acc += s * row (16-byte aligned LDS row of WP floats)

@@ -32,16 +32,6 @@ constexpr int GMAX = 6;                 // largest supported group count
 constexpr int LDIM = GMAX + 1;          // leading dimension of L and M in coeffs
 constexpr size_t STATE_FLOATS = (size_t)W * DS;  // per (batch, kv head) unit
 
-// Packed pair table: entry p holds (r << 8) | t for the p-th pair r <= t.
-struct PairTable {
-  uint16_t rt[NPAIR];
-  constexpr PairTable() : rt() {
-    int p = 0;
-    for (int r = 0; r < DH; ++r)
-      for (int t = r; t < DH; ++t) rt[p++] = (uint16_t)((r << 8) | t);
-  }
-};
-
 // Index of pair (r, t), r <= t, in the packed order.
 __host__ __device__ constexpr inline int pair_index(int r, int t) {
   return r * DH - r * (r - 1) / 2 + (t - r);
@@ -62,6 +52,47 @@ __device__ __forceinline__ void pair_decode(int p, int& r, int& t) {
   t = p - rr * (129 - rr) / 2 + rr;
 }
 static_assert(DH == 64, "pair_decode's constants are for d_h = 64");
+
+// LDS staging of a contiguous span by a block of NT threads: element i < N (the
+// tile's capacity) gets load(i) for i < n and zero beyond (1 <= n <= N).  The loads
+// are unconditional (index clamped to n - 1) and all issued before the first is
+// awaited: a loop striding by blockDim.x is not unrolled, so each element would
+// wait for its own load, and a load in a divergent block is awaited at its end.
+template <int N, int NT = 256, typename Load, typename Store>
+__device__ __forceinline__ void stage_span(int tid, int n, Load load, Store store) {
+  constexpr int E = (N + NT - 1) / NT;
+  float x[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) x[e] = load(min(tid + NT * e, n - 1));
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int i = tid + NT * e;
+    if (i < N) store(i, i < n ? x[e] : 0.f);
+  }
+}
+
+// record index of c_f for a feature f < DCAN (no branch: for loads that must not
+// wait in a divergent block)
+__device__ __forceinline__ int coef_index(int f) {
+  return f == 0 ? OAL_COEF_A : (f <= DH ? OAL_COEF_BP + f - 1 : OAL_COEF_CP + f - 1 - DH);
+}
+
+// The same for a thread count nt known only at run time (0 <= n <= N): K loads of
+// each thread in flight per round.
+template <int K, typename Load, typename Store>
+__device__ __forceinline__ void stage_span_rt(int tid, int nt, int N, int n, Load load, Store store) {
+  for (int i0 = 0; i0 < N; i0 += K * nt) {
+    float x[K];
+#pragma unroll
+    for (int e = 0; e < K; ++e) x[e] = load(max(min(i0 + tid + e * nt, n - 1), 0));
+#pragma unroll
+    for (int e = 0; e < K; ++e) {
+      const int i = i0 + tid + e * nt;
+      if (i < N) store(i, i < n ? x[e] : 0.f);
+    }
+  }
+}
+
 
 // ---- element access ------------------------------------------------------
 

@@ -19,7 +19,6 @@
 namespace oal {
 
 namespace {
-__constant__ PairTable c_vec_pairs = PairTable();
 constexpr int FB = 64;                 // feature rows per build block
 constexpr int NFB = DS / FB;           // 34 build blocks per unit
 constexpr int TB = 64;                 // tokens staged per step
@@ -63,7 +62,7 @@ k_build_vec(int n_kv_heads, int seq_len, int chunk, int n_chunks, const T* __res
   int r = 0, t = 0, kind;
   if (f == 0) kind = 0;
   else if (f <= DH) { kind = 1; r = f - 1; }
-  else if (f < DCAN) { kind = 2; uint16_t rt = c_vec_pairs.rt[f - 1 - DH]; r = rt >> 8; t = rt & 0xff; }
+  else if (f < DCAN) { kind = 2; pair_decode(f - 1 - DH, r, t); }
   else kind = 3;
 
   float acc[WPT];
@@ -76,17 +75,14 @@ k_build_vec(int n_kv_heads, int seq_len, int chunk, int n_chunks, const T* __res
   for (int j0 = t0; j0 < t1; j0 += TB) {
     const int nj = min(TB, t1 - j0);
     __syncthreads();
-    for (int i = tid; i < TB * DH; i += blockDim.x) {
-      int jj = i / DH, d = i % DH;
-      float kv_ = 0.f, vv_ = 0.f;
-      if (jj < nj) {
-        kv_ = Elem<T>::load(k, (base + j0 + jj) * DH + d);
-        vv_ = Elem<T>::load(v, (base + j0 + jj) * DV + d);
-      }
-      s_k[jj][d] = kv_;
-      s_u[jj][d] = vv_;
-    }
-    for (int jj = tid; jj < TB; jj += blockDim.x) s_u[jj][DV] = jj < nj ? 1.f : 0.f;
+    // the tile's key and value rows are one span each (nj >= 1, 256 threads)
+    const T* ks = k + (base + j0) * DH;
+    const T* vs = v + (base + j0) * DV;
+    stage_span<TB * DH>(tid, nj * DH, [&](int i) { return Elem<T>::load(ks, i); },
+                        [&](int i, float x) { s_k[i / DH][i % DH] = x; });
+    stage_span<TB * DV>(tid, nj * DV, [&](int i) { return Elem<T>::load(vs, i); },
+                        [&](int i, float x) { s_u[i / DV][i % DV] = x; });
+    if (tid < TB) s_u[tid][DV] = tid < nj ? 1.f : 0.f;
     __syncthreads();
     for (int jj = 0; jj < nj; ++jj) {
       float phi = kind == 0 ? 1.f : kind == 1 ? s_k[jj][r] : kind == 2 ? s_k[jj][r] * s_k[jj][t] : 0.f;
@@ -176,10 +172,10 @@ k_readout_vec(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunk
   const float eps = rec[OAL_COEF_EPS];
   const int G = reinterpret_cast<const int32_t*>(rec)[OAL_COEF_NG];
 
-  for (int i = tid; i < chunk * DH; i += nthr) {
-    int ii = i / DH, d = i % DH;
-    s_q[ii * (DH + 1) + d] =
-        ii < clen ? Elem<T>::load(q, (((size_t)b * n_q_heads + hq) * seq_len + t0 + ii) * DH + d) : 0.f;
+  {
+    const T* qs = q + (((size_t)b * n_q_heads + hq) * seq_len + t0) * DH;   // the chunk's q rows
+    stage_span_rt<8>(tid, nthr, chunk * DH, clen * DH, [&](int i) { return Elem<T>::load(qs, i); },
+                     [&](int i, float x) { s_q[(i / DH) * (DH + 1) + i % DH] = x; });
   }
   if constexpr (DIM) {
     for (int i = tid; i < DH; i += nthr) s_ell[i] = rec[OAL_COEF_BP + i];
@@ -212,11 +208,11 @@ k_readout_vec(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunk
   const float* Hc = ws + ((size_t)unit * n_chunks + c) * STATE_FLOATS;
   constexpr int PB = (32 * W + (SPLIT == 2 ? 128 : 256) - 1) / (SPLIT == 2 ? 128 : 256);
   float pre[PB];
-  auto fetch_block = [&](int f0) {
+  auto fetch_block = [&](int f0) {   // unconditional (clamped): no wait on the loads in flight
 #pragma unroll
     for (int e = 0; e < PB; ++e) {
-      const int i = tid + e * nthr;
-      if (i < 32 * W) pre[e] = Hc[(size_t)(i / 32) * DS + f0 + i % 32];   // f0 + 31 < DS always
+      const int i = min(tid + e * nthr, 32 * W - 1);
+      pre[e] = Hc[(size_t)(i / 32) * DS + f0 + i % 32];   // f0 + 31 < DS always
     }
   };
   fetch_block(0);
@@ -229,12 +225,9 @@ k_readout_vec(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunk
     }
     if (f0 + 32 < DCAN) fetch_block(f0 + 32);
     if (tid < 32) {
-      int f = f0 + tid;
-      float cf = 0.f;
-      if (f == 0) cf = a;
-      else if (f <= DH) cf = rec[OAL_COEF_BP + f - 1];
-      else if (f < DCAN) cf = rec[OAL_COEF_CP + f - 1 - DH];
-      s_cf[tid] = cf;
+      const int f = f0 + tid;
+      const float x = rec[coef_index(min(f, DCAN - 1))];   // unconditional, then dropped past DCAN
+      s_cf[tid] = f < DCAN ? x : 0.f;
     }
     __syncthreads();
     if (active) {
@@ -245,8 +238,9 @@ k_readout_vec(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunk
         if (f == 0) phi = s_cf[ff];
         else if (f <= DH) phi = s_cf[ff] * qi[f - 1];
         else {
-          uint16_t rt = c_vec_pairs.rt[f - 1 - DH];
-          phi = s_cf[ff] * qi[rt >> 8] * qi[rt & 0xff];
+          int r, t;
+          pair_decode(f - 1 - DH, r, t);
+          phi = s_cf[ff] * qi[r] * qi[t];
         }
         axpy_row(acc, phi, s_H + ff * WP);
       }
@@ -258,15 +252,13 @@ k_readout_vec(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunk
   for (int j0 = 0; j0 < clen; j0 += TB) {
     const int nj = min(TB, clen - j0);
     __syncthreads();
-    for (int i = tid; i < TB * DH; i += nthr) {
-      int jj = i / DH, d = i % DH;
-      float kv_ = 0.f, vv_ = 0.f;
-      if (jj < nj) {
-        kv_ = Elem<T>::load(k, (kbase + j0 + jj) * DH + d);
-        vv_ = Elem<T>::load(v, (kbase + j0 + jj) * DV + d);
-      }
-      s_k[jj * (DH + 1) + d] = kv_;
-      s_u[jj * WP + d] = vv_;
+    {
+      const T* ks = k + (kbase + j0) * DH;   // the tile's key and value rows, one span each
+      const T* vs = v + (kbase + j0) * DV;
+      stage_span_rt<8>(tid, nthr, TB * DH, nj * DH, [&](int i) { return Elem<T>::load(ks, i); },
+                       [&](int i, float x) { s_k[(i / DH) * (DH + 1) + i % DH] = x; });
+      stage_span_rt<8>(tid, nthr, TB * DV, nj * DV, [&](int i) { return Elem<T>::load(vs, i); },
+                       [&](int i, float x) { s_u[(i / DV) * WP + i % DV] = x; });
     }
     for (int jj = tid; jj < TB; jj += nthr) s_u[jj * WP + DV] = 1.f;
     __syncthreads();
