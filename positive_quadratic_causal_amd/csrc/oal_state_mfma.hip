@@ -712,15 +712,16 @@ k_state_segscan(int n_seg, const float* __restrict__ segsum, uint16_t* __restric
   }
   float4 r = make_float4(run[0], run[1], run[2], run[3]);
   const size_t base = (size_t)unit * n_seg * st::UNIT_SEG_FLOATS + e0;
-  // the loads of SB segments are issued together: one at a time, each thread
-  // would wait out the full memory latency n_seg times
-  constexpr int SB = 8;
+  // the loads of SB segments are issued together (one at a time, each thread
+  // would wait out the full memory latency n_seg times), unconditionally with the
+  // segment index clamped, so that each use waits for its own load only (a load
+  // behind a branch ends its block with a wait for every load in flight)
+  constexpr int SB = 16;
   for (int s0 = 0; s0 < n_seg; s0 += SB) {
     float4 a[SB];
 #pragma unroll
     for (int j = 0; j < SB; ++j)
-      if (s0 + j < n_seg)
-        a[j] = *reinterpret_cast<const float4*>(segsum + base + (size_t)(s0 + j) * st::UNIT_SEG_FLOATS);
+      a[j] = *reinterpret_cast<const float4*>(segsum + base + (size_t)min(s0 + j, n_seg - 1) * st::UNIT_SEG_FLOATS);
 #pragma unroll
     for (int j = 0; j < SB; ++j)
       if (s0 + j < n_seg) {
