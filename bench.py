@@ -937,7 +937,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--warm-seconds", type=float, default=WARM_SECONDS,
                     help="untimed warmup time floor per timed leg (seconds)")
-    ap.add_argument("--chunk", type=int, default=128)
+    ap.add_argument("--chunk", type=int, default=256)
     ap.add_argument("--decode-steps", type=int, default=256)
     ap.add_argument("--decode-reps", type=int, default=3)
     ap.add_argument("--no-decode", action="store_true")
