@@ -400,6 +400,11 @@ def bench_backward(oal, w, chunk, steps, warmup, device):
                          "peak": PEAK_F32_VECTOR_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(fl[dom] / (kms * 1e-3) / 1e12 / PEAK_F32_VECTOR_TFLOPS, 5),
                          "algorithmic_flops": fl[dom]},
+            # the whole backward step: every kernel's algorithmic flops over the step
+            "backward_end_to_end": {
+                "algorithmic_flops": sum(fl.values()),
+                "tflops": round(sum(fl.values()) / (ms * 1e-3) / 1e12, 3),
+                "frac_f32_peak": round(sum(fl.values()) / (ms * 1e-3) / 1e12 / PEAK_F32_VECTOR_TFLOPS, 5)},
             "kernels_ms": {k: round(v["avg_ms"], 5) for k, v in kt.items()}}
 
 
