@@ -274,7 +274,7 @@ struct BwdWs {
   float* gbuf;    // [batch][Hq][n_chunks * chunk][WP] g rows (zero beyond seq_len)
   float* alpha;   // [batch][Hq][n_chunks][chunk][chunk] alpha_ij (zero for j > i)
   float* dcp;     // [DC_PARTS][batch][Hq][n_chunks][DS] per-chunk parts of dc
-  float* kpart;   // [units][KS (rep + 1)][n_chunks * chunk][128] parts of [dk | dv]
+  float* kpart;   // [units][key_split * rep + KS_NFS][n_chunks * chunk][128] parts of [dk | dv]
   size_t bytes;
 };
 
@@ -282,12 +282,14 @@ struct BwdWs {
 // chunk 64 (256 threads, 143 KB of LDS per block), two at chunk 128.
 static int key_split(int chunk) { return chunk <= 64 ? 4 : 2; }
 
-// The suffix-state slot of the key-side kernel is cut into this many feature
-// ranges, one workgroup (and one set of parts) each: it walks all 2145 features
-// while the pair slots meet one chunk of queries, and would otherwise set the
-// kernel's length alone.
-constexpr int DC_PARTS = 4;  // parts of the per-chunk dc: the four waves of k_bwd_rbuild (dc_intra adds to part 0)
-constexpr int KS_NFS = 4;   // feature splits of the key side's state part (k_bwd_kstate)
+// Parts of the per-chunk dc: one per wave of k_bwd_rbuild, each its own columns'
+// sums over the heads (k_bwd_dc_intra adds the pair part into part 0);
+// k_bwd_dcoef adds them.
+constexpr int DC_PARTS = 4;
+// The suffix-state part of dk and dv walks all 2145 features while the pair part
+// meets one chunk of keys; k_bwd_kstate cuts the features into this many ranges,
+// one workgroup and one kpart slot each, so that it does not set the length alone.
+constexpr int KS_NFS = 4;
 
 static BwdWs bwd_ws(void* base, int batch, int n_q_heads, int n_kv_heads, int seq_len, int chunk) {
   const size_t units = (size_t)batch * n_kv_heads;
