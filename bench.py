@@ -943,6 +943,9 @@ def main() -> int:
     ap.add_argument("--warm-seconds", type=float, default=WARM_SECONDS,
                     help="untimed warmup time floor per timed leg (seconds)")
     ap.add_argument("--chunk", type=int, default=256)
+    ap.add_argument("--dim-chunk", type=int, default=128,
+                    help="chunk of the dimension-specific prefill leg (its fastest: its "
+                         "intra-chunk part runs on the vector ALUs and grows with the chunk)")
     ap.add_argument("--decode-steps", type=int, default=256)
     ap.add_argument("--decode-reps", type=int, default=3)
     ap.add_argument("--no-decode", action="store_true")
@@ -993,7 +996,7 @@ def main() -> int:
         print(json.dumps({"metric": METRIC, "calibration": bench_calibration(oal, device)}), flush=True)
         return 0
     if args.only == "prefill_dim":
-        res = bench_prefill_dim(oal, synth.WORKLOADS[1], args.chunk, args.steps, args.warmup, device)
+        res = bench_prefill_dim(oal, synth.WORKLOADS[1], args.dim_chunk, args.steps, args.warmup, device)
         print(json.dumps({"metric": METRIC, "prefill_dim": res}), flush=True)
         return 0
     log(f"prefill: {w3.name}, chunk {args.chunk}, {args.warmup} warmup + {args.steps} steps")
@@ -1088,7 +1091,7 @@ def main() -> int:
         sm["oal_speedup"] = round(sm["ms_per_step"] / ms, 3)
         result["softmax_reference"] = sm
         log("general prefill (dimension-specific kernel): Qwen-shaped N = 2048")
-        result["prefill_dim"] = bench_prefill_dim(oal, synth.WORKLOADS[1], args.chunk,
+        result["prefill_dim"] = bench_prefill_dim(oal, synth.WORKLOADS[1], args.dim_chunk,
                                                   max(3, args.steps // 4), 2, device)
         log("backward (dq, dk, dv, coefficient gradients): Qwen-shaped N = 2048")
         result["backward"] = bench_backward(oal, synth.WORKLOADS[1], 64, max(3, args.steps // 4), 2,
