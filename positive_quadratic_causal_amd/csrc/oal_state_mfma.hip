@@ -408,6 +408,11 @@ k_state_mfma(int seq_len, int chunk, int n_chunks, int n_seg, int cps, int n_blk
   const int tok_begin = c0 * chunk;
   const int tok_end = min(seq_len, c1 * chunk);
   const int n_blocks = (tok_end - tok_begin + st::TB - 1) / st::TB;
+  // Blocks copied and added.  Prefix mode stores each chunk's tile before adding
+  // the chunk; the sum over the segment's last chunk is no tile's prefix (the
+  // scan forms the final state from the segment sums), so that mode adds the
+  // blocks before the last chunk only and stores the last tile after them.
+  const int n_add = MODE == 1 ? (c1 - 1 - c0) * chunk / st::TB : n_blocks;
   const uint8_t* sblk = stg + ((size_t)unit * n_blk + tok_begin / st::TB) * st::STG_BYTES;
   float* segslot = segsum + ((size_t)unit * n_seg + seg) * st::UNIT_SEG_FLOATS;
   const uint16_t* preslot = segpre + ((size_t)unit * n_seg + seg) * st::QUAD_SEG_FLOATS;
@@ -428,8 +433,8 @@ k_state_mfma(int seq_len, int chunk, int n_chunks, int n_seg, int cps, int n_blk
   };
 
   using P4 = std::integral_constant<int, 4>;
-  if (n_blocks > 0) issue(0, s_b0, P4{});
-  if (n_blocks > 1) issue(1, s_b1, P4{});
+  if (n_add > 0) issue(0, s_b0, P4{});
+  if (n_add > 1) issue(1, s_b1, P4{});
 
   if (g < st::NWG - 1) {
     // ===================== quadratic rows (waves 0..23) =====================
@@ -460,45 +465,47 @@ k_state_mfma(int seq_len, int chunk, int n_chunks, int n_seg, int cps, int n_blk
     constexpr int NST = st::QTILES * 2 * 2;   // store instructions per tile store (per lane)
     auto stores_at = [&](int b) { return (MODE == 1 && b >= 0 && (b * st::TB) % chunk == 0) ? NST : 0; };
 
+    // The running prefix is chunk (t0 / chunk)'s exclusive prefix: store it;
+    // rows 8 gq + 4 half .. + 3 of tile m are elements of one K-step.
+    auto store_tile = [&](int t0) {
+      uint16_t* tl = reinterpret_cast<uint16_t*>(ts + ((size_t)unit * n_chunks + t0 / chunk) * tile::BYTES);
+#pragma unroll
+      for (int m = 0; m < st::QTILES; ++m) {
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+          const int w = 32 * nt + col;
+          // K-step ks0 + kk holds rows 8 kk .. 8 kk + 7 of the lane pair (lane,
+          // lane ^ 32): elements 4 half .. + 3 and 8 + 4 half .. + 3 of the 16 of
+          // column w.  One exchange gives each lane 8 contiguous elements, so that
+          // every store writes 16 contiguous bytes (the pass is about 9 % faster
+          // than with two 8-byte stores per lane, measured)
+#pragma unroll
+          for (int kk = 0; kk < 2; ++kk) {
+            const int ks_ = ks0[m] + kk;
+            const uint2 A = pack4_f16(acc[m][nt][8 * kk], acc[m][nt][8 * kk + 1], acc[m][nt][8 * kk + 2],
+                                      acc[m][nt][8 * kk + 3], wscale);
+            const uint2 B = pack4_f16(acc[m][nt][8 * kk + 4], acc[m][nt][8 * kk + 5],
+                                      acc[m][nt][8 * kk + 6], acc[m][nt][8 * kk + 7], wscale);
+            const uint2 X = half ? A : B;   // the half the partner lane stores
+            const uint2 Y = make_uint2(__shfl_xor((int)X.x, 32, 64), __shfl_xor((int)X.y, 32, 64));
+            const uint4 out = half ? make_uint4(Y.x, Y.y, B.x, B.y) : make_uint4(A.x, A.y, Y.x, Y.y);
+            *reinterpret_cast<uint4*>(tl + (size_t)ks_ * 1024 + w * 16 + 8 * half) = out;
+          }
+          asm volatile("" ::: "memory");   // keep the conversions next to their stores
+        }
+      }
+    };
+
     auto body = [&](int bi, const uint8_t* cur, uint8_t* nxt) {
-      if (bi >= n_blocks) return;
+      if (bi >= n_add) return;
       // Block bi has landed, for every wave.  Memory operations complete in issue
       // order, and the ones issued after block bi's copy may stay in flight: the
       // tile stores of the two previous blocks and the copy of block bi + 1.
-      wait_vm_upto(stores_at(bi - 2) + (bi + 1 < n_blocks ? 4 : 0) + stores_at(bi - 1));
+      wait_vm_upto(stores_at(bi - 2) + (bi + 1 < n_add ? 4 : 0) + stores_at(bi - 1));
       barrier_nofence();
-      if (bi + 2 < n_blocks) issue(bi + 2, nxt, P4{});
+      if (bi + 2 < n_add) issue(bi + 2, nxt, P4{});
       const int t0 = tok_begin + bi * st::TB;
-      if (MODE == 1 && (t0 % chunk) == 0) {
-        // the running prefix is chunk (t0 / chunk)'s exclusive prefix: store it;
-        // rows 8 gq + 4 half .. + 3 of tile m are elements of one K-step
-        uint16_t* tl = reinterpret_cast<uint16_t*>(ts + ((size_t)unit * n_chunks + t0 / chunk) * tile::BYTES);
-#pragma unroll
-        for (int m = 0; m < st::QTILES; ++m) {
-#pragma unroll
-          for (int nt = 0; nt < 2; ++nt) {
-            const int w = 32 * nt + col;
-            // K-step ks0 + kk holds rows 8 kk .. 8 kk + 7 of the lane pair (lane,
-            // lane ^ 32): elements 4 half .. + 3 and 8 + 4 half .. + 3 of the 16 of
-            // column w.  One exchange gives each lane 8 contiguous elements, so that
-            // every store writes 16 contiguous bytes (the pass is about 9 % faster
-            // than with two 8-byte stores per lane, measured)
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-              const int ks_ = ks0[m] + kk;
-              const uint2 A = pack4_f16(acc[m][nt][8 * kk], acc[m][nt][8 * kk + 1], acc[m][nt][8 * kk + 2],
-                                        acc[m][nt][8 * kk + 3], wscale);
-              const uint2 B = pack4_f16(acc[m][nt][8 * kk + 4], acc[m][nt][8 * kk + 5],
-                                        acc[m][nt][8 * kk + 6], acc[m][nt][8 * kk + 7], wscale);
-              const uint2 X = half ? A : B;   // the half the partner lane stores
-              const uint2 Y = make_uint2(__shfl_xor((int)X.x, 32, 64), __shfl_xor((int)X.y, 32, 64));
-              const uint4 out = half ? make_uint4(Y.x, Y.y, B.x, B.y) : make_uint4(A.x, A.y, Y.x, Y.y);
-              *reinterpret_cast<uint4*>(tl + (size_t)ks_ * 1024 + w * 16 + 8 * half) = out;
-            }
-            asm volatile("" ::: "memory");   // keep the conversions next to their stores
-          }
-        }
-      }
+      if (MODE == 1 && (t0 % chunk) == 0) store_tile(t0);
       const uint8_t* kt_ = cur;
       const uint8_t* vt_ = cur + DH * 128;
 #pragma unroll
@@ -518,11 +525,12 @@ k_state_mfma(int seq_len, int chunk, int n_chunks, int n_seg, int cps, int n_blk
         }
       }
     };
-    for (int bi = 0; bi < n_blocks; bi += 3) {
+    for (int bi = 0; bi < n_add; bi += 3) {
       body(bi, s_b0, s_b2);
       body(bi + 1, s_b1, s_b0);
       body(bi + 2, s_b2, s_b1);
     }
+    if (MODE == 1) store_tile(tok_begin + n_add * st::TB);   // the last chunk's tile
     if (MODE == 0) {
 #pragma unroll
       for (int m = 0; m < st::QTILES; ++m)
@@ -572,54 +580,55 @@ k_state_mfma(int seq_len, int chunk, int n_chunks, int n_seg, int cps, int n_blk
   // wave 1 16 for Z
   const int side_stores = lin ? 19 : ones ? 16 : 0;
   auto stores_at = [&](int b) { return (MODE == 1 && b >= 0 && (b * st::TB) % chunk == 0) ? side_stores : 0; };
-  auto body = [&](int bi, const uint8_t* cur, uint8_t* nxt) {
-    if (bi >= n_blocks) return;
-    wait_vm_upto(stores_at(bi - 2) + (bi + 1 < n_blocks ? 4 : 0) + stores_at(bi - 1));
-    barrier_nofence();
-    if (bi + 2 < n_blocks) issue(bi + 2, nxt, P4{});
-    const int t0 = tok_begin + bi * st::TB;
-    if (MODE == 1 && (t0 % chunk) == 0) {
-      uint8_t* slotp = ts + ((size_t)unit * n_chunks + t0 / chunk) * tile::BYTES;
-      uint16_t* tl = reinterpret_cast<uint16_t*>(slotp);
-      float* side = reinterpret_cast<float*>(slotp + tile::TILE_BYTES);
-      if (lin) {
+  auto store_tile = [&](int t0) {
+    uint8_t* slotp = ts + ((size_t)unit * n_chunks + t0 / chunk) * tile::BYTES;
+    uint16_t* tl = reinterpret_cast<uint16_t*>(slotp);
+    float* side = reinterpret_cast<float*>(slotp + tile::TILE_BYTES);
+    if (lin) {
 #pragma unroll
-        for (int m = 0; m < 2; ++m)
+      for (int m = 0; m < 2; ++m)
 #pragma unroll
-          for (int nt = 0; nt < 2; ++nt) {
-            const int w = 32 * nt + col;
+        for (int nt = 0; nt < 2; ++nt) {
+          const int w = 32 * nt + col;
 #pragma unroll
-            for (int gq = 0; gq < 4; ++gq) {
-              const int r = 32 * m + 8 * gq + 4 * half;
-              *reinterpret_cast<uint2*>(tl + (size_t)(r >> 4) * 1024 + w * 16 + (r & 15)) =
-                  pack4_f16(acc[m][nt][4 * gq], acc[m][nt][4 * gq + 1], acc[m][nt][4 * gq + 2],
-                            acc[m][nt][4 * gq + 3], h1scale);
-            }
-            asm volatile("" ::: "memory");
+          for (int gq = 0; gq < 4; ++gq) {
+            const int r = 32 * m + 8 * gq + 4 * half;
+            *reinterpret_cast<uint2*>(tl + (size_t)(r >> 4) * 1024 + w * 16 + (r & 15)) =
+                pack4_f16(acc[m][nt][4 * gq], acc[m][nt][4 * gq + 1], acc[m][nt][4 * gq + 2],
+                          acc[m][nt][4 * gq + 3], h1scale);
           }
-        side[tile::SIDE_H0 + lane] = side_h0 * sc_h0;
-        side[tile::SIDE_Z1 + lane] = side_z1 * sc_z1;
-        if (lane == 0) {
-          side[tile::SIDE_Z0] = side_z0;
-          side[tile::SIDE_SEXP] = (float)e_s;
+          asm volatile("" ::: "memory");
         }
-      } else if (ones) {
-#pragma unroll
-        for (int m = 0; m < 2; ++m)
-#pragma unroll
-          for (int nt = 0; nt < 2; ++nt) {
-            // Z is symmetric: block (rows r, columns t) goes to (t, r), so that each
-            // lane's four consecutive rows r form one float4 of row t = 32 nt + col
-            float* zb = side + tile::SIDE_Z + (32 * nt + col) * DH + 32 * m + 4 * half;
-#pragma unroll
-            for (int gq = 0; gq < 4; ++gq)
-              *reinterpret_cast<float4*>(zb + 8 * gq) =
-                  make_float4(acc[m][nt][4 * gq] * sc_acc, acc[m][nt][4 * gq + 1] * sc_acc,
-                              acc[m][nt][4 * gq + 2] * sc_acc, acc[m][nt][4 * gq + 3] * sc_acc);
-            asm volatile("" ::: "memory");
-          }
+      side[tile::SIDE_H0 + lane] = side_h0 * sc_h0;
+      side[tile::SIDE_Z1 + lane] = side_z1 * sc_z1;
+      if (lane == 0) {
+        side[tile::SIDE_Z0] = side_z0;
+        side[tile::SIDE_SEXP] = (float)e_s;
       }
+    } else if (ones) {
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+          // Z is symmetric: block (rows r, columns t) goes to (t, r), so that each
+          // lane's four consecutive rows r form one float4 of row t = 32 nt + col
+          float* zb = side + tile::SIDE_Z + (32 * nt + col) * DH + 32 * m + 4 * half;
+#pragma unroll
+          for (int gq = 0; gq < 4; ++gq)
+            *reinterpret_cast<float4*>(zb + 8 * gq) =
+                make_float4(acc[m][nt][4 * gq] * sc_acc, acc[m][nt][4 * gq + 1] * sc_acc,
+                            acc[m][nt][4 * gq + 2] * sc_acc, acc[m][nt][4 * gq + 3] * sc_acc);
+          asm volatile("" ::: "memory");
+        }
     }
+  };
+  auto body = [&](int bi, const uint8_t* cur, uint8_t* nxt) {
+    if (bi >= n_add) return;
+    wait_vm_upto(stores_at(bi - 2) + (bi + 1 < n_add ? 4 : 0) + stores_at(bi - 1));
+    barrier_nofence();
+    if (bi + 2 < n_add) issue(bi + 2, nxt, P4{});
+    const int t0 = tok_begin + bi * st::TB;
+    if (MODE == 1 && (t0 % chunk) == 0) store_tile(t0);
     const uint8_t* kt_ = cur;
     const uint8_t* vt_ = cur + DH * 128;
     if (lin) {
@@ -657,11 +666,12 @@ k_state_mfma(int seq_len, int chunk, int n_chunks, int n_seg, int cps, int n_blk
       }
     }
   };
-  for (int bi = 0; bi < n_blocks; bi += 3) {
+  for (int bi = 0; bi < n_add; bi += 3) {
     body(bi, s_b0, s_b2);
     body(bi + 1, s_b1, s_b0);
     body(bi + 2, s_b2, s_b1);
   }
+  if (MODE == 1) store_tile(tok_begin + n_add * st::TB);   // the last chunk's tile
   if (MODE == 0 && (lin || ones)) {
 #pragma unroll
     for (int m = 0; m < 2; ++m)
