@@ -317,7 +317,7 @@ def bench_prefill_dim(oal, w, chunk, steps, warmup, device):
             "kernels_ms": {k: round(v["avg_ms"], 5) for k, v in kt.items()}}
 
 
-BWD_KERNELS = ["k_build_vec", "k_scan_vec", "k_bwd_ustate", "k_bwd_query", "k_bwd_dqstate", "k_bwd_rbuild",
+BWD_KERNELS = ["k_build_vec", "k_scan_vec", "k_bwd_ustate", "k_bwd_pair", "k_bwd_query", "k_bwd_dqstate", "k_bwd_rbuild",
                "k_bwd_rscan",
                "k_bwd_key", "k_bwd_kstate", "k_bwd_ksum", "k_bwd_dc_intra", "k_bwd_dcoef"]
 
@@ -345,13 +345,18 @@ def backward_flops(w, chunk, grouped=True) -> dict:
         kap, grad = 64 + 2 * (64 + 2080), 2 * 64 * 64 + 3 * 64
     nq = w.batch * w.n_q_heads * n
     nk = w.batch * w.n_kv_heads * n
-    return {"k_bwd_ustate": nq * 2 * D * Wc,
-            "k_bwd_query": pairs * (kap + grad + 4 * Wc),
-            "k_bwd_dqstate": nq * (2 * D * Wc + 4 * (D - 1 - 64) + 2 * 64),
-            "k_bwd_key": pairs * (kap + grad + 4 * Wc),
-            "k_bwd_kstate": nk * (2 * D * Wc + 2 * D * 64 + 4 * (D - 1 - 64) + 2 * 64),
-            "k_bwd_rbuild": nq * 2 * D * Wc,
-            "k_bwd_dc_intra": pairs * 2 * D}
+    fl = {"k_bwd_ustate": nq * 2 * D * Wc,
+          "k_bwd_query": pairs * (kap + grad + 4 * Wc),
+          "k_bwd_dqstate": nq * (2 * D * Wc + 4 * (D - 1 - 64) + 2 * 64),
+          "k_bwd_key": pairs * (kap + grad + 4 * Wc),
+          "k_bwd_kstate": nk * (2 * D * Wc + 2 * D * 64 + 4 * (D - 1 - 64) + 2 * 64),
+          "k_bwd_rbuild": nq * 2 * D * Wc,
+          "k_bwd_dc_intra": pairs * 2 * D}
+    if grouped and chunk == 64:
+        # both sides of the pairs in one matrix-core kernel (k_bwd_query and
+        # k_bwd_key leave grouped records to it)
+        fl["k_bwd_pair"] = fl.pop("k_bwd_query") + fl.pop("k_bwd_key")
+    return fl
 
 
 def bench_backward(oal, w, chunk, steps, warmup, device):

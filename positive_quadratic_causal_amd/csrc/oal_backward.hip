@@ -23,14 +23,17 @@
 // Kernels, in launch order:
 //   prefix build + scan (oal_prefill_vec.hip)  H_{<c}
 //   k_bwd_ustate    the state part of u~_i: Phi(q) H_{<c} (to the g rows)
-//   k_bwd_query     four (chunk 64) or two threads per query: the pair part of u~_i, g_i; the
-//                   pair part of dq_i; alpha rows
+//   k_bwd_pair      grouped records at chunk 64, on the matrix cores: the chunk's pair
+//                   matrices (group sums, kappa, alpha), g_i, alpha rows and the pair parts
+//                   of dq_i, dk_j, dv_j
+//   k_bwd_query     the other records: four (chunk 64) or two threads per query: the pair
+//                   part of u~_i, g_i; the pair part of dq_i; alpha rows
 //   k_bwd_dqstate   the state part of dq_i: H_{<c} g_i against d psi(q_i) / dq_i, by pair rows
 //   k_bwd_rbuild    per chunk: sum_h c_f psi_f(q_i) g_i^T (suffix deltas) and the
 //                   state part of dc: sum_i psi_f(q_i) (H_{<c} g_i)_f
 //   k_bwd_rscan     exclusive suffix sums over chunks: R_{>c}
-//   k_bwd_key       four (chunk 64) or two threads per key and query head: the pair parts of
-//                   dv_j, dk_j
+//   k_bwd_key       the other records: four (chunk 64) or two threads per key and query
+//                   head: the pair parts of dv_j, dk_j
 //   k_bwd_kstate    the parts through R_{>c}: R^T psi(k_j) and R u_j against d psi(k_j) / dk_j,
 //                   by pair rows in four feature splits;  k_bwd_ksum adds the parts
 //   k_bwd_dc_intra  pair part of dc: sum_{i, j<=i in the chunk} alpha_ij psi_f(q_i) psi_f(k_j)
@@ -280,7 +283,7 @@ struct BwdWs {
 
 // Threads per key of the key-side kernel (and parts per slot in kpart): four at
 // chunk 64 (256 threads, 143 KB of LDS per block), two at chunk 128.
-static int key_split(int chunk) { return chunk <= 64 ? 4 : 2; }
+__host__ __device__ constexpr int key_split(int chunk) { return chunk <= 64 ? 4 : 2; }
 
 // Parts of the per-chunk dc: one per wave of k_bwd_rbuild, each its own columns'
 // sums over the heads (k_bwd_dc_intra adds the pair part into part 0);
@@ -488,6 +491,7 @@ k_bwd_query(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunks,
   const float a = rec[OAL_COEF_A];
   __shared__ __attribute__((aligned(16))) GroupTab gt;
   const bool grouped = reinterpret_cast<const int32_t*>(rec)[OAL_COEF_NG] >= 1;
+  if (SP == 4 && grouped) return;   // chunk 64: k_bwd_pair on the matrix cores
   if (grouped) build_group_tab(gt, rec, tid);
   const size_t qrow0 = ((size_t)b * n_q_heads + hq) * seq_len + t0;
   {
@@ -638,6 +642,335 @@ k_bwd_query(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunks,
       for (int h = 0; h < SP; ++h) x += s_dq[(h * chunk + qx) * (DH + 1) + half * (DH / SP) + d];
       o[d] = x;
     }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Pair part of the backward on the fp32 matrix cores, for grouped records at chunk
+// 64 (one block per (chunk, query head, batch), four waves).  In a grouped record a
+// pair enters only through its group sums s_bar = [1, s_1 .. s_G] ([OAL] Eq. 7), so
+// with the chunk's pair matrices (rows i = queries, columns j = keys, zero for
+// j > i and past the sequence):
+//   S_g = (Q o 1_g) K^T / sqrt(d_h)            group sums, one product chain per group
+//   kappa = eps + s_bar^T M s_bar              per entry, on the vector ALUs
+//   u~ (pair part) = kappa [V 1],  then g from u~ + the state part and dy
+//   alpha = G [V 1]^T,  dv = kappa^T G
+//   dq = sum_v (alpha o s_v) (K o m_v),  dk = sum_v (alpha o s_v)^T (Q o m_v)
+// with s_0 = 1 and m_v[r] = M_{g(r), v} / 4: the gradient of kappa with respect to
+// q_r is k_r w_{g(r)}, w = (2 / sqrt(d_h)) M s_bar, and the sum over v folds the
+// group weights into the B operand so that one accumulator takes all G + 1 terms.
+// Wave w holds the 32 x 32 quadrant (I, J) = (w / 2, w % 2) of the pair matrices
+// and the tiles (I, J) of u~ and dq and (J' = I, J) of dk and dv (32 rows x 32
+// columns); quadrant (0, 1) lies above the diagonal.  The group sums run over the
+// dimensions in group order (a copy of Q and K with permuted columns), each K-step
+// of two dimensions masked to the group whose chain it feeds.  The kernel writes the
+// g rows over the state part of u~ that k_bwd_ustate left there, the alpha rows, the
+// pair part of dq and this head's part of [dk | dv] (part `slot` of kpart, the
+// first of the head's key_split(64) parts); k_bwd_query and k_bwd_key leave grouped
+// records at chunk 64 to it, and k_bwd_ksum reads one part instead of four for such
+// a head.
+constexpr int PR_C = 64;     // chunk of the matrix-core pair kernel
+constexpr int PR_RS = 65;    // LDS row stride of its 64-row matrices (odd: column reads spread)
+
+// acc += A B over the 16 K-steps k0, k0 + 2, ..., k0 + 30: a(k), b(k) give this lane's
+// operands at K index k + (lane / 32); all 32 loads are issued before the products.
+template <typename FA, typename FB>
+__device__ __forceinline__ fx16 mm16(fx16 acc, int k0, FA a, FB b) {
+  float av[16], bv[16];
+#pragma unroll
+  for (int s = 0; s < 16; ++s) {
+    av[s] = a(k0 + 2 * s);
+    bv[s] = b(k0 + 2 * s);
+  }
+#pragma unroll
+  for (int s = 0; s < 16; ++s) acc = mfma_f32(av[s], bv[s], acc);
+  return acc;
+}
+
+template <typename T>
+__global__ void __launch_bounds__(256)
+k_bwd_pair(int n_q_heads, int n_kv_heads, int seq_len, int n_chunks, int n_units, int n_parts,
+           const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+           const void* __restrict__ coeffs, const float* __restrict__ dy, float* __restrict__ gbuf,
+           float* __restrict__ alpha, float* __restrict__ dq, float* __restrict__ kpart) {
+  constexpr int C = PR_C, RS = PR_RS, MS = C * RS;
+  const int rep = n_q_heads / n_kv_heads;
+  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  const int uc = (slot / rep) * 8 + xcd;
+  if (uc >= n_units * n_chunks) return;
+  const int unit = uc / n_chunks, c = uc % n_chunks;
+  const int b = unit / n_kv_heads;
+  const int hh = slot % rep;
+  const int hq = (unit % n_kv_heads) * rep + hh;
+  const float* rec = coef_rec(coeffs, hq);
+  const int32_t* rec_i = reinterpret_cast<const int32_t*>(rec);
+  const int G = min(rec_i[OAL_COEF_NG], GMAX);
+  if (G < 1) return;   // dimension-specific record: k_bwd_query and k_bwd_key
+  const int tid = threadIdx.x;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, col = lane & 31, hf = lane >> 5;
+  const int I = wv >> 1, J = wv & 1;
+  const bool live = !(I == 0 && J == 1);
+  const int t0 = c * C;
+  const int clen = min(C, seq_len - t0);
+  const size_t bh = (size_t)b * n_q_heads + hq;
+  const size_t qrow0 = bh * seq_len + t0;
+  const size_t npad = (size_t)n_chunks * C;
+
+  extern __shared__ __attribute__((aligned(16))) float smem[];
+  float* sQ = smem;         // [C][RS] q rows, zero past the sequence
+  float* sK = sQ + MS;      // [C][RS] k rows
+  float* sU = sK + MS;      // [C][RS] u = (v, 1) rows, zero past the sequence
+  float* sG = sU + MS;      // [C][RS] g rows
+  float* sP = sG + MS;      // [C][RS] kappa (masked)
+  float* sX = sP + MS;      // [2][C][RS] alpha o s_v; first the permuted q and k, then u~
+  __shared__ int s_grp[DH];          // group of each dimension (1 .. G)
+  __shared__ int s_pos[DH];          // its place in group order
+  __shared__ int s_gofs[LDIM + 1];   // group g's places: s_gofs[g] .. s_gofs[g + 1] - 1
+  __shared__ float s_M[LDIM * LDIM];
+
+  if (tid < DH) {
+    const int gr = rec_i[OAL_COEF_GMAP + tid];
+    s_grp[tid] = gr < 1 ? 1 : (gr > G ? G : gr);
+  }
+  if (tid < LDIM * LDIM) s_M[tid] = rec[OAL_COEF_M + tid];
+  __syncthreads();
+  if (tid < DH) {
+    const int gr = s_grp[tid];
+    int pos = 0;
+    for (int r = 0; r < DH; ++r) {
+      const int g2 = s_grp[r];
+      pos += (g2 < gr || (g2 == gr && r < tid)) ? 1 : 0;
+    }
+    s_pos[tid] = pos;
+  } else if (tid < DH + LDIM + 1) {
+    const int g = tid - DH;
+    int n = 0;
+    for (int r = 0; r < DH; ++r) n += s_grp[r] < g ? 1 : 0;
+    s_gofs[g] = n;
+  }
+  __syncthreads();
+  {
+    const T* qs = q + qrow0 * DH;
+    const T* ks = k + ((size_t)unit * seq_len + t0) * DH;
+    const T* vs = v + ((size_t)unit * seq_len + t0) * DV;
+    float* sQp = sX;
+    float* sKp = sX + MS;
+    stage_span<C * DH>(tid, clen * DH, [&](int i) { return Elem<T>::load(qs, i); }, [&](int i, float x) {
+      sQ[(i / DH) * RS + i % DH] = x;
+      sQp[(i / DH) * RS + s_pos[i % DH]] = x;
+    });
+    stage_span<C * DH>(tid, clen * DH, [&](int i) { return Elem<T>::load(ks, i); }, [&](int i, float x) {
+      sK[(i / DH) * RS + i % DH] = x;
+      sKp[(i / DH) * RS + s_pos[i % DH]] = x;
+    });
+    stage_span<C * DV>(tid, clen * DV, [&](int i) { return Elem<T>::load(vs, i); },
+                       [&](int i, float x) { sU[(i / DV) * RS + i % DV] = x; });
+    if (tid < C) sU[tid * RS + DV] = tid < clen ? 1.f : 0.f;
+  }
+  __syncthreads();
+
+  // ---- group sums of this wave's quadrant: sacc[g - 1] = sum_{r in g} q_ir k_jr
+  fx16 sacc[GMAX];
+#pragma unroll
+  for (int g = 0; g < GMAX; ++g)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sacc[g][i] = 0.f;
+  if (live) {
+    const float* qa = sX + (32 * I + col) * RS;        // permuted q row i = 32 I + col
+    const float* kb = sX + MS + (32 * J + col) * RS;   // permuted k row j = 32 J + col
+#pragma unroll
+    for (int g = 1; g <= GMAX; ++g) {
+      if (g > G) break;
+      const int o0 = __builtin_amdgcn_readfirstlane(s_gofs[g]);
+      const int o1 = __builtin_amdgcn_readfirstlane(s_gofs[g + 1]);
+      for (int p = o0 & ~1; p < o1; p += 8) {   // four K-steps per round, masked to [o0, o1)
+        float av[4], bv[4];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const int pos = p + 2 * s + hf;
+          const int pc = min(pos, DH - 1);
+          av[s] = (pos >= o0 && pos < o1) ? qa[pc] : 0.f;
+          bv[s] = kb[pc];
+        }
+#pragma unroll
+        for (int s = 0; s < 4; ++s) sacc[g - 1] = mfma_f32(av[s], bv[s], sacc[g - 1]);
+      }
+    }
+  }
+
+  // ---- kappa of the quadrant's pairs (zero above the diagonal and past the sequence)
+  const float eps = rec[OAL_COEF_EPS];
+  float Mr[LDIM][LDIM];
+#pragma unroll
+  for (int u = 0; u < LDIM; ++u)
+#pragma unroll
+    for (int w = 0; w < LDIM; ++w) Mr[u][w] = rec[OAL_COEF_M + u * LDIM + w];
+  fx16 kap;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int ri = 32 * I + mrow(i, hf), cj = 32 * J + col;
+    float s[LDIM];
+    s[0] = 1.f;
+#pragma unroll
+    for (int g = 0; g < GMAX; ++g) s[g + 1] = sacc[g][i] * 0.125f;
+    float x = eps;
+#pragma unroll
+    for (int u = 0; u < LDIM; ++u) {
+      float tu = 0.f;
+#pragma unroll
+      for (int w = 0; w < LDIM; ++w) tu = fmaf(Mr[u][w], s[w], tu);
+      x = fmaf(s[u], tu, x);
+    }
+    kap[i] = (live && cj <= ri && ri < clen) ? x : 0.f;
+    sP[ri * RS + cj] = kap[i];
+  }
+  __syncthreads();   // sP complete; the permuted copies in sX are no longer read
+
+  // ---- pair part of u~ (tile (I, J) of kappa [V]) to sX, staged for the rows
+  {
+    fx16 acc;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+    const float* pa = sP + (32 * I + col) * RS + hf;   // A[i][j] = kappa_ij
+    const float* ub = sU + hf * RS + 32 * J + col;     // B[j][w] = u_jw
+    auto fa = [&](int kk) { return pa[kk]; };
+    auto fb = [&](int kk) { return ub[kk * RS]; };
+    acc = mm16(acc, 0, fa, fb);
+    if (I == 1) acc = mm16(acc, 32, fa, fb);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sX[(32 * I + mrow(i, hf)) * RS + 32 * J + col] = acc[i];
+  }
+  __syncthreads();
+
+  // ---- g rows: four threads per query, 16 channels each
+  {
+    const int ri = tid >> 2, pp = tid & 3;
+    const bool active = ri < clen;
+    float* gr = gbuf + (bh * npad + t0 + ri) * WP;
+    float u[16], dyv[16];
+    float dsum = 0.f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int w = 16 * pp + e;
+      u[e] = sX[ri * RS + w] + gr[w];   // + the state part (k_bwd_ustate)
+      dsum += sP[ri * RS + w];          // pair part of the denominator: sum_j kappa_ij
+      dyv[e] = dy[(qrow0 + min(ri, clen - 1)) * DV + w];
+    }
+    const float den_state = gr[DV];
+    dsum += lane_xor1(dsum);
+    dsum += lane_xor2(dsum);
+    const float inv = active ? 1.0f / (dsum + den_state) : 0.f;
+    float yd = 0.f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) yd = fmaf(dyv[e], u[e] * inv, yd);
+    yd += lane_xor1(yd);
+    yd += lane_xor2(yd);
+    float g[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      g[e] = dyv[e] * inv;
+      sG[ri * RS + 16 * pp + e] = g[e];
+    }
+    const float g64 = -yd * inv;
+    if (pp == 0) sG[ri * RS + DV] = g64;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      reinterpret_cast<float4*>(gr + 16 * pp)[e] = make_float4(g[4 * e], g[4 * e + 1], g[4 * e + 2], g[4 * e + 3]);
+    if (pp == 0) *reinterpret_cast<float4*>(gr + DV) = make_float4(g64, 0.f, 0.f, 0.f);
+  }
+  __syncthreads();
+
+  // ---- alpha of the quadrant: G [V 1]^T, masked; to the alpha rows
+  fx16 al;
+  {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) al[i] = 0.f;
+    if (live) {
+      const float* ga = sG + (32 * I + col) * RS + hf;   // A[i][w] = g_iw
+      const float* vb = sU + (32 * J + col) * RS + hf;   // B[w][j] = u_jw
+      auto fa = [&](int kk) { return ga[kk]; };
+      auto fb = [&](int kk) { return vb[kk]; };
+      al = mm16(al, 0, fa, fb);
+      al = mm16(al, 32, fa, fb);
+    }
+    float* arow = alpha + ((bh * n_chunks + c) * C) * C;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int ri = 32 * I + mrow(i, hf), cj = 32 * J + col;
+      al[i] = (live && cj <= ri && ri < clen) ? al[i] + sG[ri * RS + DV] : 0.f;
+      arow[(size_t)ri * C + cj] = al[i];
+    }
+  }
+
+  // ---- dv tile (J' = I, J): kappa^T G
+  fx16 dva;
+  {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) dva[i] = 0.f;
+    const float* pa = sP + hf * RS + 32 * I + col;   // A[j][i] = kappa_ij
+    const float* gb = sG + hf * RS + 32 * J + col;   // B[i][w] = g_iw
+    auto fa = [&](int kk) { return pa[kk * RS]; };
+    auto fb = [&](int kk) { return gb[kk * RS]; };
+    if (I == 0) dva = mm16(dva, 0, fa, fb);   // i >= j: rows from 32 I
+    dva = mm16(dva, 32, fa, fb);
+  }
+
+  // ---- dq tile (I, J) and dk tile (J' = I, J): sum over v of (alpha o s_v) times
+  // (K o m_v) and (Q o m_v)
+  fx16 dqa, dka;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    dqa[i] = 0.f;
+    dka[i] = 0.f;
+  }
+  float mv[LDIM];   // m_v of this lane's output column r = 32 J + col
+  {
+    const int gr = s_grp[32 * J + col];
+#pragma unroll
+    for (int vv = 0; vv < LDIM; ++vv) mv[vv] = 0.25f * s_M[gr * LDIM + vv];
+  }
+#pragma unroll
+  for (int vv = 0; vv < LDIM; ++vv) {
+    if (vv > G) break;
+    float* X = sX + (vv & 1) * MS;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float s = vv == 0 ? 1.f : sacc[vv > 0 ? vv - 1 : 0][i] * 0.125f;
+      X[(32 * I + mrow(i, hf)) * RS + 32 * J + col] = al[i] * s;
+    }
+    __syncthreads();   // X_v complete; X_{v-2}'s products (same buffer) came before the last barrier
+    const float m = mv[vv];
+    {
+      const float* xa = X + (32 * I + col) * RS + hf;   // A[i][j] = X_ij
+      const float* kb = sK + hf * RS + 32 * J + col;    // B[j][r] = k_jr m_v[r]
+      auto fa = [&](int kk) { return xa[kk]; };
+      auto fb = [&](int kk) { return kb[kk * RS] * m; };
+      dqa = mm16(dqa, 0, fa, fb);
+      if (I == 1) dqa = mm16(dqa, 32, fa, fb);
+    }
+    {
+      const float* xt = X + hf * RS + 32 * I + col;     // A[j][i] = X_ij
+      const float* qb = sQ + hf * RS + 32 * J + col;    // B[i][r] = q_ir m_v[r]
+      auto fa = [&](int kk) { return xt[kk * RS]; };
+      auto fb = [&](int kk) { return qb[kk * RS] * m; };
+      if (I == 0) dka = mm16(dka, 0, fa, fb);
+      dka = mm16(dka, 32, fa, fb);
+    }
+  }
+
+  // ---- outputs: the pair part of dq (rows in the sequence), this head's [dk | dv] part
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int ri = 32 * I + mrow(i, hf);
+    if (ri < clen) dq[(qrow0 + ri) * DH + 32 * J + col] = dqa[i];
+  }
+  float* kp = kpart + (((size_t)unit * n_parts + hh) * npad + t0) * (DH + DV);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int rj = 32 * I + mrow(i, hf);
+    kp[(size_t)rj * (DH + DV) + 32 * J + col] = dka[i];
+    kp[(size_t)rj * (DH + DV) + DH + 32 * J + col] = dva[i];
   }
 }
 
@@ -957,7 +1290,7 @@ k_bwd_rscan(int n_chunks, float* __restrict__ rc) {
 // Key side, the chunk's pairs.  One block per (chunk, unit, slot): slot s sums the
 // chunk's pairs (i >= j) of query head kv * rep + s.  SP threads per key (thread
 // SP j + h for key t0 + j) split the pairs by query index mod SP; each thread writes
-// its part of [dk_j | dv_j] to kpart (part SP slot + h of the unit's SP rep + KS_NFS
+// its part of [dk_j | dv_j] to kpart (part h rep + slot of the unit's SP rep + KS_NFS
 // parts; the last KS_NFS are k_bwd_kstate's), and k_bwd_ksum adds the parts in order.
 template <typename T, int SP>
 __global__ void __launch_bounds__(256)
@@ -970,6 +1303,8 @@ k_bwd_key(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunks,
   const int unit = blockIdx.y / rep;
   const int slot = blockIdx.y % rep;
   const int b = unit / n_kv_heads, kv = unit % n_kv_heads;
+  if (SP == 4 && reinterpret_cast<const int32_t*>(coef_rec(coeffs, kv * rep + slot))[OAL_COEF_NG] >= 1)
+    return;   // chunk 64, grouped record: k_bwd_pair wrote this head's part
   const int tid = threadIdx.x;
   const int nthr = blockDim.x;                // SP * chunk
   const int jx = tid / SP;                    // key of the chunk
@@ -1063,7 +1398,7 @@ k_bwd_key(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunks,
     }
   }
   if (active) {
-    float* o = kpart + (((size_t)unit * (SP * rep + KS_NFS) + SP * slot + half) * npad + t0 + jx) * (DH + DV);
+    float* o = kpart + (((size_t)unit * (SP * rep + KS_NFS) + half * rep + slot) * npad + t0 + jx) * (DH + DV);
 #pragma unroll
     for (int d = 0; d < DH; ++d) o[d] = dkj[d];
 #pragma unroll
@@ -1273,19 +1608,39 @@ k_bwd_kstate(int n_kv_heads, int seq_len, int chunk, int n_chunks, int n_units, 
   }
 }
 
-// dk, dv = the sum of the nparts parts of every key, in order.
+// dk, dv = the sum of the parts of every key, in order.  Parts 0 .. ks rep - 1 are the
+// pair parts, part h rep + s the h-th of query head s (k_bwd_key); then the nparts -
+// ks rep state parts (k_bwd_kstate).  With pair_mfma set, a head with a grouped
+// record has its pair part in part s alone (k_bwd_pair): when every head of the unit
+// has one, the parts rep .. ks rep - 1 are skipped as a whole.
 __global__ void __launch_bounds__(256)
-k_bwd_ksum(int n_kv_heads, int nparts, int seq_len, int npad, const float* __restrict__ kpart,
-           float* __restrict__ dk, float* __restrict__ dv) {
+k_bwd_ksum(int n_kv_heads, int nparts, int ks, int rep, int pair_mfma, const void* __restrict__ coeffs,
+           int seq_len, int npad, const float* __restrict__ kpart, float* __restrict__ dk,
+           float* __restrict__ dv) {
   const size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   const size_t per_unit = (size_t)seq_len * (DH + DV);
   const int unit = blockIdx.y;
   if (e >= per_unit) return;
   const size_t pos = e / (DH + DV);
   const int comp = (int)(e % (DH + DV));
+  const int kv = unit % n_kv_heads;
+  auto grouped = [&](int s) {
+    return reinterpret_cast<const int32_t*>(coef_rec(coeffs, kv * rep + s))[OAL_COEF_NG] >= 1;
+  };
+  bool all_grouped = pair_mfma != 0;
+  for (int s = 0; s < rep; ++s) all_grouped = all_grouped && grouped(s);
+  const float* kp = kpart + ((size_t)unit * nparts * npad + pos) * (DH + DV) + comp;
+  const size_t stride = (size_t)npad * (DH + DV);
   float s = 0.f;
-  for (int sl = 0; sl < nparts; ++sl)
-    s += kpart[(((size_t)unit * nparts + sl) * npad + pos) * (DH + DV) + comp];
+  if (all_grouped) {
+    for (int sl = 0; sl < rep; ++sl) s += kp[sl * stride];
+    for (int sl = ks * rep; sl < nparts; ++sl) s += kp[sl * stride];
+  } else {
+    for (int sl = 0; sl < nparts; ++sl) {
+      if (pair_mfma && sl >= rep && sl < ks * rep && grouped(sl % rep)) continue;
+      s += kp[sl * stride];
+    }
+  }
   if (comp < DH) dk[((size_t)unit * seq_len + pos) * DH + comp] = s;
   else dv[((size_t)unit * seq_len + pos) * DV + comp - DH] = s;
 }
@@ -1491,6 +1846,20 @@ static oal_status backward_typed(int batch, int n_q_heads, int n_kv_heads, int s
                        chunk, n_chunks, units, qq, coeffs, w.hc, w.gbuf);
     if ((st = check_launch("k_bwd_ustate")) != OAL_OK) return st;
   }
+  const bool pair_mfma = chunk == PR_C;
+  if (pair_mfma) {
+    const size_t smem = sizeof(float) * 7 * (size_t)PR_C * PR_RS;
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&k_bwd_pair<T>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem) != hipSuccess)
+      return set_error(OAL_ERR_HIP, "k_bwd_pair: cannot reserve %zu bytes of LDS", smem);
+    const int rep = n_q_heads / n_kv_heads;
+    const dim3 grid((unsigned)(((size_t)units * n_chunks + 7) / 8 * 8 * (size_t)rep));
+    ProfScope ps("k_bwd_pair", stream);
+    hipLaunchKernelGGL(k_bwd_pair<T>, grid, dim3(256), smem, stream, n_q_heads, n_kv_heads, seq_len,
+                       n_chunks, units, key_split(chunk) * rep + KS_NFS, qq, kk, vv, coeffs, dy, w.gbuf,
+                       w.alpha, dq, w.kpart);
+    if ((st = check_launch("k_bwd_pair")) != OAL_OK) return st;
+  }
   {
     // four threads per query at chunk 64 (256 threads, 143 KB of LDS), two at 128;
     // the kernel's state staging assumes SP * chunk = 256
@@ -1568,7 +1937,8 @@ static oal_status backward_typed(int batch, int n_q_heads, int n_kv_heads, int s
     ProfScope ps("k_bwd_ksum", stream);
     const size_t per_unit = (size_t)seq_len * (DH + DV);
     hipLaunchKernelGGL(k_bwd_ksum, dim3((unsigned)((per_unit + 255) / 256), units), dim3(256), 0,
-                       stream, n_kv_heads, ks * rep + KS_NFS, seq_len, n_chunks * chunk, w.kpart, dk, dv);
+                       stream, n_kv_heads, ks * rep + KS_NFS, ks, rep, pair_mfma ? 1 : 0, coeffs, seq_len,
+                       n_chunks * chunk, w.kpart, dk, dv);
     if ((st = check_launch("k_bwd_ksum")) != OAL_OK) return st;
   }
   if (!want_coef) return OAL_OK;
