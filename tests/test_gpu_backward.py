@@ -113,6 +113,34 @@ def test_backward_dimension_specific_record(oal):
         assert err <= 1e-4, (name, err)
 
 
+@pytest.mark.parametrize("chunk", [64, 128])
+def test_backward_mixed_records(oal, chunk):
+    """Grouped and dimension-specific records in the same GQA groups: at chunk 64
+    the grouped heads take the matrix-core pair kernel and the others the vector
+    kernels, and the key side adds one pair part for the former and four for the
+    latter."""
+    w = synth.small_workload(860, "bwd mixed", 1, 6, 2, 150, "f32", grouping="llama")
+    announce(f"backward with mixed records, 6/2 N=150 f32 chunk={chunk}")
+    case = Case(w)
+    a, b, C = synth.dim_coefficients(w)
+    grouped = case.coeffs()
+    dim = oal.oal_dim_coeffs(*(torch.from_numpy(x).cuda() for x in (a, b, C)))
+    is_dim = [h % 2 == 1 for h in range(6)]   # each KV group holds both kinds
+    coeffs = torch.stack([dim[h] if is_dim[h] else grouped[h] for h in range(6)]).contiguous()
+    dy = _dy(861, (1, 6, 150, 64))
+    got = _run(oal, case, dy, coeffs, chunk)
+
+    def coef(h):
+        if is_dim[h]:
+            return float(a[h]), b[h].astype(np.float64), C[h].astype(np.float64)
+        return _grouped_abc(case, h)
+
+    ref = _oracle_grads(case, dy, coef)
+    for name, g_, r_ in zip(["dq", "dk", "dv", "da", "db", "dC"], got, ref):
+        err = rel_l2(g_, r_)
+        assert err <= 1e-4, (name, err)
+
+
 def test_backward_without_coefficient_gradients(oal):
     w = synth.small_workload(840, "bwd nocoef", 1, 4, 2, 130, "bf16")
     announce("backward without coefficient gradients, 4/2 N=130 bf16")
