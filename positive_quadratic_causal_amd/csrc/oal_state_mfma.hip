@@ -269,16 +269,24 @@ k_state_kvmax(int seq_len, int chunk, int n_chunks, int cps, const uint16_t* __r
   const size_t row0 = (size_t)unit * seq_len;
   uint32_t mk = 0, mv = 0, mi = 0;   // mi: largest |H_init| as bits (non-negative floats order alike)
   if (state != nullptr) {
-    constexpr int PER4 = (int)((STATE_FLOATS / 4 + 255) / 256);   // float4 per thread, at most
-    const size_t per = (STATE_FLOATS / 4 + nip - 1) / nip;
-    const size_t i0 = blockIdx.x * per, i1 = min(STATE_FLOATS / 4, i0 + per);
+    // eight 16-byte loads of each thread in flight per round (with a few workgroups
+    // per unit a thread copies dozens: one at a time, each would wait out the
+    // memory latency); a clamped duplicate leaves the maximum alone
+    constexpr int CB = 8;
+    const int per = (int)((STATE_FLOATS / 4 + nip - 1) / nip);
+    const int i0 = blockIdx.x * per, i1 = min((int)(STATE_FLOATS / 4), i0 + per);
     const float4* src = reinterpret_cast<const float4*>(state + (size_t)unit * STATE_FLOATS);
     float4* dst = reinterpret_cast<float4*>(init + (size_t)unit * STATE_FLOATS);
-    (void)PER4;
-    for (size_t i = i0 + tid; i < i1; i += 256) {
-      const float4 x = src[i];
-      dst[i] = x;
-      mi = max(mi, __float_as_uint(fmaxf(fmaxf(fabsf(x.x), fabsf(x.y)), fmaxf(fabsf(x.z), fabsf(x.w)))));
+    for (int ib = i0 + tid; ib < i1; ib += 256 * CB) {
+      float4 x[CB];
+#pragma unroll
+      for (int e = 0; e < CB; ++e) x[e] = src[min(ib + 256 * e, i1 - 1)];
+#pragma unroll
+      for (int e = 0; e < CB; ++e) {
+        if (ib + 256 * e < i1) dst[ib + 256 * e] = x[e];
+        mi = max(mi, __float_as_uint(fmaxf(fmaxf(fabsf(x[e].x), fabsf(x[e].y)),
+                                           fmaxf(fabsf(x[e].z), fabsf(x[e].w)))));
+      }
     }
   }
   // four rounds of 16-byte loads in flight at a time (a clamped duplicate leaves the
@@ -694,39 +702,85 @@ k_state_mfma(int seq_len, int chunk, int n_chunks, int n_seg, int cps, int n_blk
 // waves 0..23 as fp16 times 2^-e_S, of wave 24 in fp32 (sidepre).  state (when
 // not null): receives init + the total in the canonical layout; init is the
 // initial state's copy (null: zero), so no thread reads what another writes.
+// A workgroup's 1024 elements are one 32 x 32 accumulator tile (16 registers of
+// one wave slot).  The tiles of the quadratic slots and of H1 (the first 148
+// workgroups) hold 32 channels w in their columns and, in their rows, runs of
+// consecutive features of one channel; their initial and final states go through
+// LDS so that the canonical reads and writes run along the features (eight
+// threads per channel, four rows each) instead of striding over channels.
+constexpr int SCAN_TILED_BLOCKS = (st::QUAD_SEG_FLOATS + 64 * 64) / 1024;   // 144 + 4
+template <int SB>   // segments whose loads are in flight together
 __global__ void __launch_bounds__(256)
 k_state_segscan(int n_seg, const float* __restrict__ segsum, uint16_t* __restrict__ segpre,
                 float* __restrict__ sidepre, const float* __restrict__ init, float* __restrict__ state,
                 const float* __restrict__ bound, int n_blk, int nip) {
+  __shared__ float s_t[32][33];
   const int unit = blockIdx.y, units = gridDim.y;
-  const int e0 = 4 * (blockIdx.x * blockDim.x + threadIdx.x);
+  const int tid = threadIdx.x;
+  const int e0 = 4 * (blockIdx.x * blockDim.x + tid);
   const bool in = e0 < st::UNIT_SEG_FLOATS;
   const bool quad = e0 < st::QUAD_SEG_FLOATS;
   const int omega = quad ? e0 / st::QSLOT_FLOATS : 24;
+  const bool tiled = blockIdx.x < SCAN_TILED_BLOCKS;   // uniform over the workgroup
   // every wave evaluates the tile scale (the same value everywhere)
-  const float tscale = segpre ? ldexpf(1.0f, -tile_scale_exp(bound, units, n_blk, nip, unit, threadIdx.x & 63)) : 1.f;
-  if (!in) return;
+  const float tscale = segpre ? ldexpf(1.0f, -tile_scale_exp(bound, units, n_blk, nip, unit, tid & 63)) : 1.f;
+  float* ustate = state ? state + (size_t)unit * STATE_FLOATS : nullptr;
+  const float* uinit = init ? init + (size_t)unit * STATE_FLOATS : nullptr;
+  // tiled workgroups: canonical (f, w) of tile row rho, column c (rho = the
+  // accumulator row, c = the lane's column), for this thread's channel c = tid / 8
+  // and rows 4 (tid % 8) .. + 3
+  const int reg0 = (quad ? (e0 / 64) % st::QSLOT_REGS : (e0 - st::QUAD_SEG_FLOATS) / 64) & ~15;
+  const int cc = tid >> 3, rr0 = 4 * (tid & 7);
+  int cf[4];
+  bool cvalid[4], ckeep[4];
+  if (tiled) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int rho = rr0 + j;
+      const int i = 4 * (rho >> 3) + (rho & 3), h = (rho >> 2) & 1;   // mrow(i, h) = rho
+      int f = 0, w = 0;
+      bool valid = false, primary = false;
+      state_elem(omega, reg0 + i, cc + 32 * h, f, w, valid, primary);
+      cf[j] = w * DS + f;
+      cvalid[j] = valid;
+      ckeep[j] = valid && primary;
+    }
+    float x[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) x[j] = (uinit && cvalid[j]) ? uinit[cf[j]] : 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) s_t[rr0 + j][cc] = x[j];
+    __syncthreads();
+  }
+  if (!in) return;   // (never in a tiled workgroup)
   float run[4];
   int fw[4];
   bool keep[4];
+  const int lane0 = e0 & 63;
+  const int reg = quad ? (e0 / 64) % st::QSLOT_REGS : (e0 - st::QUAD_SEG_FLOATS) / 64;
+  const int trow = acc_row(reg & 15, lane0 >> 5), tcol = lane0 & 31;   // tiled: this thread's tile row
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const int e = e0 + j;
-    const int reg = quad ? (e / 64) % st::QSLOT_REGS : (e - st::QUAD_SEG_FLOATS) / 64, lane = e & 63;
+    if (tiled) {
+      run[j] = s_t[trow][tcol + j];
+      fw[j] = 0;
+      keep[j] = false;
+      continue;
+    }
     int f = 0, w = 0;
     bool valid = false, primary = false;
-    state_elem(omega, reg, lane, f, w, valid, primary);
+    state_elem(omega, reg, lane0 + j, f, w, valid, primary);
     fw[j] = w * DS + f;
     keep[j] = valid && primary;
-    run[j] = (init && valid) ? init[(size_t)unit * STATE_FLOATS + fw[j]] : 0.f;
+    run[j] = (uinit && valid) ? uinit[fw[j]] : 0.f;
   }
   float4 r = make_float4(run[0], run[1], run[2], run[3]);
   const size_t base = (size_t)unit * n_seg * st::UNIT_SEG_FLOATS + e0;
   // the loads of SB segments are issued together (one at a time, each thread
   // would wait out the full memory latency n_seg times), unconditionally with the
   // segment index clamped, so that each use waits for its own load only (a load
-  // behind a branch ends its block with a wait for every load in flight)
-  constexpr int SB = 16;
+  // behind a branch ends its block with a wait for every load in flight); SB
+  // follows n_seg, so that few segments issue few duplicate loads
   for (int s0 = 0; s0 < n_seg; s0 += SB) {
     float4 a[SB];
 #pragma unroll
@@ -752,12 +806,21 @@ k_state_segscan(int n_seg, const float* __restrict__ segsum, uint16_t* __restric
         r.w += a[j].w;
       }
   }
-  if (state) {
-    const float fin[4] = {r.x, r.y, r.z, r.w};
+  if (!ustate) return;   // (uniform)
+  const float fin[4] = {r.x, r.y, r.z, r.w};
+  if (tiled) {
+    __syncthreads();   // every thread has taken its initial values out of s_t
+#pragma unroll
+    for (int j = 0; j < 4; ++j) s_t[trow][tcol + j] = fin[j];
+    __syncthreads();
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      if (keep[j]) state[(size_t)unit * STATE_FLOATS + fw[j]] = fin[j];
+      if (ckeep[j]) ustate[cf[j]] = s_t[rr0 + j][cc];
+    return;
   }
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    if (keep[j]) ustate[fw[j]] = fin[j];
 }
 
 // ---------------------------------------------------------------------------
@@ -826,11 +889,13 @@ size_t state_mfma_workspace(int batch, int n_kv_heads, int seq_len, int chunk, b
 }
 
 // Builds the per-chunk prefix tiles (when ts != null) and the final state (when
-// state != null; its content on entry is the initial state).  ws: the scratch part
-// of state_mfma_workspace (see state_ws).
+// state != null; its content on entry is the initial state, or, with init_zero,
+// ignored: the sequence starts empty and the state is only written).  ws: the
+// scratch part of state_mfma_workspace (see state_ws).
 oal_status launch_state_mfma(int batch, int n_kv_heads, int seq_len, int chunk, const void* k,
-                             const void* v, float* state, uint8_t* ts, void* ws,
+                             const void* v, float* state, bool init_zero, uint8_t* ts, void* ws,
                              hipStream_t stream) {
+  const float* init_src = init_zero ? nullptr : state;   // the initial state, when one is read
   const int units = batch * n_kv_heads;
   const int n_chunks = (seq_len + chunk - 1) / chunk;
   const int n_seg = choose_segments(units, n_chunks);
@@ -845,7 +910,7 @@ oal_status launch_state_mfma(int batch, int n_kv_heads, int seq_len, int chunk, 
   {
     ProfScope ps("k_state_kvmax", stream);
     hipLaunchKernelGGL(k_state_kvmax, dim3(nip, units), dim3(256), 0, stream, seq_len, chunk,
-                       n_chunks, cps, kk, vv, w.kvmax, (const float*)state, w.init,
+                       n_chunks, cps, kk, vv, w.kvmax, init_src, w.init,
                        ts ? w.bound + (size_t)units * n_blk : (float*)nullptr);
     oal_status s = check_launch("k_state_kvmax");
     if (s != OAL_OK) return s;
@@ -868,9 +933,11 @@ oal_status launch_state_mfma(int batch, int n_kv_heads, int seq_len, int chunk, 
   }
   {
     ProfScope ps("k_state_segscan", stream);
-    hipLaunchKernelGGL(k_state_segscan, dim3((st::UNIT_SEG_FLOATS / 4 + 255) / 256, units), dim3(256),
+    auto* fn = n_seg_eff >= 16 ? k_state_segscan<16> : n_seg_eff >= 4 ? k_state_segscan<4>
+                                                                       : k_state_segscan<2>;
+    hipLaunchKernelGGL(fn, dim3((st::UNIT_SEG_FLOATS / 4 + 255) / 256, units), dim3(256),
                        0, stream, n_seg_eff, (const float*)w.segsum, w.segpre, w.sidepre,
-                       state ? (const float*)w.init : (const float*)nullptr, state,
+                       init_src ? (const float*)w.init : (const float*)nullptr, state,
                        (const float*)w.bound, n_blk, nip);
     oal_status s = check_launch("k_state_segscan");
     if (s != OAL_OK) return s;
