@@ -148,11 +148,13 @@ def bench_prefill(oal, w, chunk, steps, warmup, device):
                                                              w.seq_len, chunk, oal.OAL_BF16, True),
                              device)
 
+    # one step: the coefficient expansion and a prefill of the sequence from an
+    # empty state, written into `state` (oal_prefill_fresh: the state is only
+    # written, so no reset pass clears it first)
     def step():
         oal.oal_expand_coeffs(ng, gm, L, w.eps, coeffs)
-        oal.oal_state_reset(state)
-        oal.oal_prefill(x["q"], x["k"], x["v"], coeffs, chunk=chunk, state=state, y=y,
-                        workspace=ws)
+        oal.oal_prefill_fresh(x["q"], x["k"], x["v"], coeffs, state, chunk=chunk, y=y,
+                              workspace=ws)
 
     n_warm = warm_up(step, warmup)
     log(f"prefill warmup: {n_warm} steps ({w.name}, chunk {chunk})")

@@ -157,6 +157,19 @@ oal_status oal_prefill(int batch, int n_q_heads, int n_kv_heads, int seq_len, in
                        oal_dtype out_dtype, void* workspace, size_t workspace_bytes,
                        hipStream_t stream);
 
+/* oal_prefill for a sequence that starts empty ([OAL] Algorithm 1 step 5, then
+ * steps 6-12), into state: the state's contents on entry are ignored (taken as
+ * zero) and replaced by the state after the seq_len tokens; its token count
+ * becomes seq_len.  With bf16 inputs the state is only written, never read or
+ * cleared first (oal_state_reset followed by oal_prefill clears it and reads the
+ * zeros back).  state must not be NULL (OAL_ERR_INVALID_ARG); seq_len == 0 leaves
+ * it zero.  Other arguments and errors as oal_prefill. */
+oal_status oal_prefill_fresh(int batch, int n_q_heads, int n_kv_heads, int seq_len, int d_h, int d_v,
+                             oal_dtype in_dtype, const void* q, const void* k, const void* v,
+                             const void* coeffs, int chunk, oal_state* state, void* y,
+                             oal_dtype out_dtype, void* workspace, size_t workspace_bytes,
+                             hipStream_t stream);
+
 /* ---- allocation-free prefill ----------------------------------------------
  * For callers that cannot allocate device memory (code under HIP graph capture,
  * tight serving loops, harnesses that forbid hipMalloc): oal_prefill with the

@@ -143,8 +143,8 @@ oal_status launch_softmax(int batch, int n_q_heads, int n_kv_heads, int seq_len,
                           hipStream_t stream);
 oal_status launch_prefill_mfma(int batch, int n_q_heads, int n_kv_heads, int seq_len,
                                const void* q, const void* k, const void* v, const void* coeffs,
-                               int chunk, float* state, void* y, oal_dtype out_dtype, void* ws,
-                               hipStream_t stream);
+                               int chunk, float* state, bool init_zero, void* y, oal_dtype out_dtype,
+                               void* ws, hipStream_t stream);
 oal_status launch_prefill_vec(int batch, int n_q_heads, int n_kv_heads, int seq_len,
                               oal_dtype in_dtype, const void* q, const void* k, const void* v,
                               const void* coeffs, int chunk, float* state, void* y,
@@ -371,11 +371,40 @@ oal_status oal_prefill(int batch, int n_q_heads, int n_kv_heads, int seq_len, in
   if (st != OAL_OK || seq_len == 0) return st;
   if (in_dtype == OAL_BF16)
     st = launch_prefill_mfma(batch, n_q_heads, n_kv_heads, seq_len, q, k, v, coeffs, chunk,
-                             state ? state->data : nullptr, y, out_dtype, workspace, stream);
+                             state ? state->data : nullptr, false, y, out_dtype, workspace, stream);
   else
     st = launch_prefill_vec(batch, n_q_heads, n_kv_heads, seq_len, in_dtype, q, k, v, coeffs, chunk,
                             state ? state->data : nullptr, y, out_dtype, workspace, false, stream);
   if (st == OAL_OK && state) state->tokens += seq_len;
+  return st;
+}
+
+oal_status oal_prefill_fresh(int batch, int n_q_heads, int n_kv_heads, int seq_len, int d_h, int d_v,
+                             oal_dtype in_dtype, const void* q, const void* k, const void* v,
+                             const void* coeffs, int chunk, oal_state* state, void* y,
+                             oal_dtype out_dtype, void* workspace, size_t workspace_bytes,
+                             hipStream_t stream) {
+  if (!state) return set_error(OAL_ERR_INVALID_ARG, "oal_prefill_fresh needs a state (else use oal_prefill)");
+  chunk = resolve_chunk(chunk);
+  const size_t need = oal_prefill_workspace_bytes(batch, n_q_heads, n_kv_heads, seq_len, d_h, d_v,
+                                                  chunk, in_dtype, y != nullptr);
+  oal_status st = prefill_checks(batch, n_q_heads, n_kv_heads, seq_len, d_h, d_v, in_dtype, q, k, v,
+                                 coeffs, chunk, state, y, out_dtype, workspace, workspace_bytes, need);
+  if (st != OAL_OK) return st;
+  if (seq_len == 0 || in_dtype != OAL_BF16) {
+    // no tokens, or the fp32 path (which adds to the state it reads): clear, then append
+    st = launch_fill_zero(state->data, state->bytes / sizeof(float), stream);
+    if (st != OAL_OK) return st;
+    state->tokens = 0;
+    if (seq_len == 0) return OAL_OK;
+    return oal_prefill(batch, n_q_heads, n_kv_heads, seq_len, d_h, d_v, in_dtype, q, k, v, coeffs,
+                       chunk, state, y, out_dtype, workspace, workspace_bytes, stream);
+  }
+  // the builder starts from zero without reading the state and writes every entry
+  // of it (the padding beyond the 2145 features is zero from the allocation on)
+  st = launch_prefill_mfma(batch, n_q_heads, n_kv_heads, seq_len, q, k, v, coeffs, chunk, state->data,
+                           true, y, out_dtype, workspace, stream);
+  if (st == OAL_OK) state->tokens = seq_len;
   return st;
 }
 

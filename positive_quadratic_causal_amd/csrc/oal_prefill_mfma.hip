@@ -952,7 +952,7 @@ k_readout_mfma(int n_q_heads, int n_kv_heads, int seq_len, int n_chunks, int n_h
 
 size_t state_mfma_workspace(int batch, int n_kv_heads, int seq_len, int chunk, bool with_tiles);
 oal_status launch_state_mfma(int batch, int n_kv_heads, int seq_len, int chunk, const void* k,
-                             const void* v, float* state, uint8_t* ts, void* ws,
+                             const void* v, float* state, bool init_zero, uint8_t* ts, void* ws,
                              hipStream_t stream);
 
 template <int CH, typename O>
@@ -990,17 +990,18 @@ static oal_status readout_dispatch(int chunk, int batch, int n_q_heads, int n_kv
 
 oal_status launch_prefill_mfma(int batch, int n_q_heads, int n_kv_heads, int seq_len,
                                const void* q, const void* k, const void* v, const void* coeffs,
-                               int chunk, float* state, void* y, oal_dtype out_dtype, void* ws,
-                               hipStream_t stream) {
+                               int chunk, float* state, bool init_zero, void* y, oal_dtype out_dtype,
+                               void* ws, hipStream_t stream) {
   const int units = batch * n_kv_heads;
   const int n_chunks = (seq_len + chunk - 1) / chunk;
   // workspace: the per-chunk prefix tiles (with output), then the builder's scratch
   if (y == nullptr)   // state only: no per-chunk prefixes are needed
-    return launch_state_mfma(batch, n_kv_heads, seq_len, chunk, k, v, state, nullptr, ws, stream);
+    return launch_state_mfma(batch, n_kv_heads, seq_len, chunk, k, v, state, init_zero, nullptr, ws,
+                             stream);
   uint8_t* ts = reinterpret_cast<uint8_t*>(ws);
   uint8_t* scratch = ts + (size_t)units * n_chunks * tile::BYTES;
-  oal_status st = launch_state_mfma(batch, n_kv_heads, seq_len, chunk, k, v, state, ts, scratch,
-                                    stream);
+  oal_status st = launch_state_mfma(batch, n_kv_heads, seq_len, chunk, k, v, state, init_zero, ts,
+                                    scratch, stream);
   if (st != OAL_OK) return st;
   if (out_dtype == OAL_F32)
     return readout_dispatch<float>(chunk, batch, n_q_heads, n_kv_heads, seq_len, n_chunks, q, k, v,

@@ -60,6 +60,9 @@ def _load() -> ctypes.CDLL:
         "oal_prefill": (c_int, [c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_void, c_void,
                                 c_void, c_void, c_int, c_void, c_void, c_int, c_void, c_size,
                                 c_void]),
+        "oal_prefill_fresh": (c_int, [c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_void,
+                                      c_void, c_void, c_void, c_int, c_void, c_void, c_int, c_void,
+                                      c_size, c_void]),
         "oal_prefill_noalloc_scratch_bytes": (c_size, []),
         "oal_prefill_noalloc": (c_int, [c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_void,
                                         c_void, c_void, c_void, c_int, c_void, c_void, c_int,
@@ -106,6 +109,7 @@ _lib = _load()
 EXPORTED = ("oal_coeffs_bytes", "oal_expand_coeffs", "oal_dim_coeffs", "oal_state_alloc",
             "oal_state_reset", "oal_state_free", "oal_state_copy", "oal_state_bytes",
             "oal_state_tokens", "oal_state_export", "oal_prefill_workspace_bytes", "oal_prefill",
+            "oal_prefill_fresh",
             "oal_prefill_noalloc_scratch_bytes", "oal_prefill_noalloc",
             "oal_prefill_dim_workspace_bytes", "oal_prefill_dim",
             "oal_prefill_backward_workspace_bytes", "oal_prefill_backward", "oal_coeffs_backward",
@@ -356,6 +360,22 @@ def oal_prefill(q: torch.Tensor | None, k: torch.Tensor, v: torch.Tensor, coeffs
                 workspace: torch.Tensor | None = None, want_output: bool = True) -> torch.Tensor | None:
     """q [B, Hq, N, 64] (or None with want_output=False), k/v [B, Hkv, N, 64].
     Returns y [B, Hq, N, 64] in q's dtype unless y is given or want_output is False."""
+    return _prefill_call(_lib.oal_prefill, q, k, v, coeffs, chunk, state, y, workspace, want_output)
+
+
+def oal_prefill_fresh(q: torch.Tensor | None, k: torch.Tensor, v: torch.Tensor,
+                      coeffs: torch.Tensor | None, state: OalState, chunk: int = 0,
+                      y: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                      want_output: bool = True) -> torch.Tensor | None:
+    """oal_prefill of a sequence that starts empty, written into state (its contents
+    on entry are ignored and replaced)."""
+    if state is None:
+        raise ValueError("oal_prefill_fresh needs a state")
+    return _prefill_call(_lib.oal_prefill_fresh, q, k, v, coeffs, chunk, state, y, workspace,
+                         want_output)
+
+
+def _prefill_call(fn, q, k, v, coeffs, chunk, state, y, workspace, want_output):
     B, Hkv, N, Hq, y = _prefill_args(q, k, v, coeffs, state, y, want_output)
     dh, dv = D_H, D_V
     in_dt = _dtype_code(k)
@@ -364,10 +384,10 @@ def oal_prefill(q: torch.Tensor | None, k: torch.Tensor, v: torch.Tensor, coeffs
     if workspace is None:
         workspace = alloc_workspace(ws_bytes, k.device)
     _expect_workspace(workspace, ws_bytes, k.device)
-    _check(_lib.oal_prefill(B, Hq, Hkv, N, dh, dv, in_dt, _ptr(q), _ptr(k), _ptr(v), _ptr(coeffs),
-                            chunk, state.handle if state is not None else None, _ptr(y), out_dt,
-                            _ptr(workspace) if workspace is not None else None,
-                            workspace.numel() if workspace is not None else 0, _stream(k)))
+    _check(fn(B, Hq, Hkv, N, dh, dv, in_dt, _ptr(q), _ptr(k), _ptr(v), _ptr(coeffs),
+              chunk, state.handle if state is not None else None, _ptr(y), out_dt,
+              _ptr(workspace) if workspace is not None else None,
+              workspace.numel() if workspace is not None else 0, _stream(k)))
     return y
 
 

@@ -93,6 +93,13 @@ def test_prefill_rejects_invalid_arguments(args, expect, entry):
     assert lib.oal_last_error()
 
 
+def test_prefill_fresh_needs_a_state():
+    lib, oal = _lib()
+    assert lib.oal_prefill_fresh(1, 14, 2, 16, 64, 64, 1, P, P, P, P, 0, None, P, 1, P, 1 << 30,
+                                 None) == 1
+    assert b"state" in lib.oal_last_error()
+
+
 def test_prefill_empty_sequence_is_a_noop():
     lib, oal = _lib()
     assert lib.oal_prefill(1, 14, 2, 0, 64, 64, 1, P, P, P, P, 0, None, P, 1, None, 0, None) == 0

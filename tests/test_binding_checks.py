@@ -15,7 +15,7 @@ LIB = os.path.join(ROOT, "positive_quadratic_causal_amd", "liboal.so")
 
 pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="liboal.so not built")
 
-COMPUTE = ("oal_expand_coeffs", "oal_dim_coeffs", "oal_prefill", "oal_prefill_dim",
+COMPUTE = ("oal_expand_coeffs", "oal_dim_coeffs", "oal_prefill", "oal_prefill_fresh", "oal_prefill_dim",
            "oal_decode_step", "oal_prefill_backward", "oal_coeffs_backward",
            "oal_softmax_attention", "oal_state_export", "oal_calib_grad", "oal_adam_step",
            "oal_output_mse", "oal_embed_global", "oal_contribution_scores",
@@ -93,6 +93,10 @@ def test_prefill_rejects_a_state_of_another_size(oal):
 
     with pytest.raises(ValueError):
         oal.oal_prefill(q, k, v, coeffs(oal), state=fake_state(oal, 2, 2))
+    with pytest.raises(ValueError):
+        oal.oal_prefill_fresh(q, k, v, coeffs(oal), fake_state(oal, 2, 2))
+    with pytest.raises(ValueError):
+        oal.oal_prefill_fresh(q, k, v, coeffs(oal), None)
     with pytest.raises(ValueError):
         oal.oal_decode_step(q[:, :, 0].contiguous(), k[:, :, 0].contiguous(), v[:, :, 0].contiguous(),
                             coeffs(oal), fake_state(oal, 1, 1))
