@@ -49,6 +49,7 @@ KERNEL_BOUND = {
     "k_state_mfma": ("mfma", PEAK_BF16_TFLOPS, "TFLOP/s"),
     "k_readout_vec": ("alu", PEAK_F32_VECTOR_TFLOPS, "TFLOP/s"),
     "k_build_vec": ("alu", PEAK_F32_VECTOR_TFLOPS, "TFLOP/s"),
+    "k_build_mfma": ("mfma", PEAK_F32_VECTOR_TFLOPS, "TFLOP/s"),   # fp32 matrix cores: 157.3 as well
     "k_scan_vec": ("hbm", PEAK_HBM_GBS, "GB/s"),
     "k_decode": ("hbm", PEAK_HBM_GBS, "GB/s"),
 }
@@ -126,7 +127,7 @@ def kernel_times(oal, names):
     return res
 
 
-ALL_KERNELS = ["k_expand", "k_fill_zero", "k_build_vec", "k_scan_vec", "k_readout_vec",
+ALL_KERNELS = ["k_expand", "k_fill_zero", "k_build_mfma", "k_build_vec", "k_scan_vec", "k_readout_vec",
                "k_scan_tile", "k_state_mfma", "k_state_seg", "k_state_segscan", "k_state_kvmax", "k_state_stage",
                "k_readout_mfma",
                "k_decode", "k_export", "k_softmax"]
@@ -319,7 +320,7 @@ def bench_prefill_dim(oal, w, chunk, steps, warmup, device):
             "kernels_ms": {k: round(v["avg_ms"], 5) for k, v in kt.items()}}
 
 
-BWD_KERNELS = ["k_build_vec", "k_scan_vec", "k_bwd_ustate", "k_bwd_pair", "k_bwd_query", "k_bwd_dqstate", "k_bwd_rbuild",
+BWD_KERNELS = ["k_build_mfma", "k_build_vec", "k_scan_vec", "k_bwd_ustate", "k_bwd_pair", "k_bwd_query", "k_bwd_dqstate", "k_bwd_rbuild",
                "k_bwd_rscan",
                "k_bwd_key", "k_bwd_kstate", "k_bwd_ksum", "k_bwd_dc_intra", "k_bwd_dcoef"]
 
@@ -671,7 +672,7 @@ def roofline_prefill(kt, kt_timed, w, chunk):
     avg_s = prefill_kernels[name]["avg_ms"] * 1e-3
     if name.startswith("k_readout"):
         work = tokens * (fl["readout"] + fl["intra"])
-    elif name in ("k_state_mfma", "k_build_vec"):
+    elif name in ("k_state_mfma", "k_build_vec", "k_build_mfma"):
         work = tokens * fl["build"]
     else:   # scan: state slots read + written, fp32
         n_chunks = -(-w.seq_len // chunk)

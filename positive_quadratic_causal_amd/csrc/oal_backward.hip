@@ -1271,18 +1271,27 @@ k_bwd_rbuild(int n_q_heads, int n_kv_heads, int seq_len, int chunk, int n_chunks
   }
 }
 
-// Exclusive suffix sums over the chunks of every unit, in place.
+// Exclusive suffix sums over the chunks of every unit, in place: the loads of RB
+// chunks in flight at a time (clamped index, unconditional), so that each thread
+// waits out the memory latency n_chunks / RB times rather than n_chunks.
 __global__ void __launch_bounds__(256)
 k_bwd_rscan(int n_chunks, float* __restrict__ rc) {
+  constexpr int RB = 8;
   const int unit = blockIdx.y;
   const size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (e >= STATE_FLOATS) return;
   float* p = rc + (size_t)unit * n_chunks * STATE_FLOATS + e;
   float run = 0.f;
-  for (int c = n_chunks - 1; c >= 0; --c) {
-    const float x = p[(size_t)c * STATE_FLOATS];
-    p[(size_t)c * STATE_FLOATS] = run;
-    run += x;
+  for (int c0 = n_chunks - 1; c0 >= 0; c0 -= RB) {
+    float x[RB];
+#pragma unroll
+    for (int j = 0; j < RB; ++j) x[j] = p[(size_t)max(c0 - j, 0) * STATE_FLOATS];
+#pragma unroll
+    for (int j = 0; j < RB; ++j)
+      if (c0 - j >= 0) {
+        p[(size_t)(c0 - j) * STATE_FLOATS] = run;
+        run += x[j];
+      }
   }
 }
 

@@ -41,6 +41,89 @@ __device__ __forceinline__ void axpy_row(float (&acc)[WP], float s, const float*
 }
 }  // namespace
 
+// dH_c = sum_{j in chunk c} phi_k(k_j) u_j^T of one unit for feature rows
+// [fb*64, fb*64+64), stored into the chunk's slot of out: on the fp32 matrix cores
+// (v_mfma_f32_32x32x2_f32: A 32 x 2, lane l holding A[l % 32][l / 32]; B 2 x 32,
+// lane l holding B[l / 32][l % 32]; D 32 x 32, register i of lane l holding
+// D[8 (i / 4) + 4 (l / 32) + i % 4][l % 32]).  M = features, N = channels, K =
+// tokens two per product; wave = (feature half wave % 2, channel half wave / 2);
+// A = psi_f(k) = k~[ia] k~[ib] (k~ = (k, 1)) of the lane's own feature from the
+// staged key rows, B = the staged value rows; the all-ones channel as a
+// multiply-add per product.  The tile goes through LDS so that each thread stores
+// one feature's columns (consecutive threads, consecutive features).
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float fx16;
+template <typename T>
+__global__ void __launch_bounds__(256)
+k_build_mfma(int seq_len, int chunk, int n_chunks, const T* __restrict__ k, const T* __restrict__ v,
+             float* __restrict__ out) {
+  const int fb = blockIdx.x;
+  const int c = blockIdx.y;
+  const int unit = blockIdx.z;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int FT = wave & 1, WT = wave >> 1, kpar = lane >> 5;
+  __shared__ float s_k[TB][DH + 1];                           // k~ rows, zero past the sequence
+  __shared__ __attribute__((aligned(16))) float s_u[TB][WP];  // v rows
+  __shared__ float s_R[FB][W + 1];                            // the block's dH tile
+  const int fa = fb * FB + 32 * FT + (lane & 31);
+  int ia = DH, ib = DH;
+  float amask = 1.f;
+  if (fa >= 1 && fa <= DH) {
+    ia = fa - 1;
+  } else if (fa > DH && fa < DCAN) {
+    pair_decode(fa - 1 - DH, ia, ib);
+  } else if (fa >= DCAN) {
+    amask = 0.f;
+  }
+  fx16 D[2];
+#pragma unroll
+  for (int x = 0; x < 2; ++x)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) D[x][i] = 0.f;
+  float d64 = 0.f;   // all-ones channel of the lane's feature, its tokens of parity kpar
+  const int t0 = c * chunk;
+  const int t1 = min(seq_len, t0 + chunk);
+  const size_t base = (size_t)unit * seq_len;
+  for (int j0 = t0; j0 < t1; j0 += TB) {
+    const int nj = min(TB, t1 - j0);
+    __syncthreads();
+    const T* ks = k + (base + j0) * DH;   // the tile's key and value rows: one span each
+    const T* vs = v + (base + j0) * DV;
+    stage_span<TB * DH>(tid, nj * DH, [&](int i) { return Elem<T>::load(ks, i); },
+                        [&](int i, float x) { s_k[i / DH][i % DH] = x; });
+    stage_span<TB * DV>(tid, nj * DV, [&](int i) { return Elem<T>::load(vs, i); },
+                        [&](int i, float x) { s_u[i / DV][i % DV] = x; });
+    if (tid < TB) s_k[tid][DH] = tid < nj ? 1.f : 0.f;
+    __syncthreads();
+#pragma unroll
+    for (int jp = 0; jp < TB / 2; jp += 8) {
+      float av[8], bv[8];
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {
+        const int tok = 2 * (jp + jj) + kpar;
+        av[jj] = amask * s_k[tok][ia] * s_k[tok][ib];
+        bv[jj] = s_u[tok][32 * WT + (lane & 31)];
+      }
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {
+        D[jj & 1] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[jj], bv[jj], D[jj & 1], 0, 0, 0);
+        d64 += av[jj];   // u[64] = 1 on the sequence; av = 0 past it
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 16; ++i)
+    s_R[32 * FT + 8 * (i >> 2) + 4 * kpar + (i & 3)][32 * WT + (lane & 31)] = D[0][i] + D[1][i];
+  d64 += __shfl_xor(d64, 32, 64);
+  if (WT == 0 && kpar == 0) s_R[32 * FT + (lane & 31)][W - 1] = d64;
+  __syncthreads();
+  const int f = fb * FB + (tid & 63), wq = tid >> 6;
+  float* o = out + ((size_t)unit * n_chunks + c) * STATE_FLOATS + f;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) o[(size_t)(16 * wq + j) * DS] = s_R[tid & 63][16 * wq + j];
+  if (wq == 3) o[(size_t)(W - 1) * DS] = s_R[tid & 63][W - 1];
+}
+
 // dH over tokens [t0, t1) of one unit for feature rows [fb*64, fb*64+64).
 // mode 0: store into out (a per-chunk slot), mode 1: add into out (the state).
 template <typename T>
@@ -384,10 +467,10 @@ static oal_status prefill_vec_typed(int batch, int n_q_heads, int n_kv_heads, in
   const int n_chunks = (seq_len + chunk - 1) / chunk;
   oal_status st;
   {
-    ProfScope ps("k_build_vec", stream);
-    hipLaunchKernelGGL(k_build_vec<T>, dim3(NFB, n_chunks, units), dim3(256), 0, stream,
-                       n_kv_heads, seq_len, chunk, n_chunks, kk, vv, ws, 0);
-    st = check_launch("k_build_vec");
+    ProfScope ps("k_build_mfma", stream);
+    hipLaunchKernelGGL(k_build_mfma<T>, dim3(NFB, n_chunks, units), dim3(256), 0, stream,
+                       seq_len, chunk, n_chunks, kk, vv, ws);
+    st = check_launch("k_build_mfma");
   }
   if (st != OAL_OK) return st;
   {
@@ -425,11 +508,11 @@ oal_status launch_build_vec_chunks(int batch, int n_kv_heads, int seq_len, int c
                                    const void* k, const void* v, float* dh, hipStream_t stream) {
   const int units = batch * n_kv_heads;
   const int n_chunks = (seq_len + chunk - 1) / chunk;
-  ProfScope ps("k_build_vec", stream);
-  hipLaunchKernelGGL(k_build_vec<uint16_t>, dim3(NFB, n_chunks, units), dim3(256), 0, stream,
-                     n_kv_heads, seq_len, chunk, n_chunks, reinterpret_cast<const uint16_t*>(k),
-                     reinterpret_cast<const uint16_t*>(v), dh, 0);
-  return check_launch("k_build_vec");
+  ProfScope ps("k_build_mfma", stream);
+  hipLaunchKernelGGL(k_build_mfma<uint16_t>, dim3(NFB, n_chunks, units), dim3(256), 0, stream,
+                     seq_len, chunk, n_chunks, reinterpret_cast<const uint16_t*>(k),
+                     reinterpret_cast<const uint16_t*>(v), dh);
+  return check_launch("k_build_mfma");
 }
 
 // Exclusive per-chunk prefix states H_{<c} of a sequence that starts empty:
@@ -440,16 +523,16 @@ oal_status launch_prefix_vec(int batch, int n_kv_heads, int seq_len, int chunk, 
   const int units = batch * n_kv_heads;
   const int n_chunks = (seq_len + chunk - 1) / chunk;
   {
-    ProfScope ps("k_build_vec", stream);
+    ProfScope ps("k_build_mfma", stream);
     if (in_dtype == OAL_F32)
-      hipLaunchKernelGGL(k_build_vec<float>, dim3(NFB, n_chunks, units), dim3(256), 0, stream,
-                         n_kv_heads, seq_len, chunk, n_chunks, reinterpret_cast<const float*>(k),
-                         reinterpret_cast<const float*>(v), hc, 0);
+      hipLaunchKernelGGL(k_build_mfma<float>, dim3(NFB, n_chunks, units), dim3(256), 0, stream,
+                         seq_len, chunk, n_chunks, reinterpret_cast<const float*>(k),
+                         reinterpret_cast<const float*>(v), hc);
     else
-      hipLaunchKernelGGL(k_build_vec<uint16_t>, dim3(NFB, n_chunks, units), dim3(256), 0, stream,
-                         n_kv_heads, seq_len, chunk, n_chunks, reinterpret_cast<const uint16_t*>(k),
-                         reinterpret_cast<const uint16_t*>(v), hc, 0);
-    oal_status st = check_launch("k_build_vec");
+      hipLaunchKernelGGL(k_build_mfma<uint16_t>, dim3(NFB, n_chunks, units), dim3(256), 0, stream,
+                         seq_len, chunk, n_chunks, reinterpret_cast<const uint16_t*>(k),
+                         reinterpret_cast<const uint16_t*>(v), hc);
+    oal_status st = check_launch("k_build_mfma");
     if (st != OAL_OK) return st;
   }
   ProfScope ps("k_scan_vec", stream);

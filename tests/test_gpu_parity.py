@@ -329,12 +329,21 @@ def test_prefill_llama_4096_sampled_heads(oal):
     _check_heads(case, y, heads, tol_for(w))
 
 
-@pytest.mark.parametrize("chunk", [64, 128, 256])
-def test_prefill_long_32768_sampled_rows(oal, chunk):
+@pytest.mark.parametrize("chunk,fresh", [(64, False), (128, False), (256, True)])
+def test_prefill_long_32768_sampled_rows(oal, chunk, fresh):
+    """At chunk 256 through oal_prefill_fresh into a state that held other tokens:
+    the call and launch configuration the benchmark times."""
     w = synth.WORKLOADS[3]
-    announce(f"prefill Qwen-shaped 14/2 N=32768 bf16 chunk={chunk}, sampled rows")
+    announce(f"prefill Qwen-shaped 14/2 N=32768 bf16 chunk={chunk} fresh={fresh}, sampled rows")
     case = Case(w)
-    y = _prefill(oal, case, chunk)
+    if fresh:
+        state = oal.oal_state_alloc(w.batch, w.n_kv_heads)
+        oal.oal_prefill(None, case.k[:, :, :5000].contiguous(), case.v[:, :, :5000].contiguous(), None,
+                        chunk=128, state=state, want_output=False)
+        y = oal.oal_prefill_fresh(case.q, case.k, case.v, case.coeffs(), state, chunk=chunk)
+        assert oal.oal_state_tokens(state) == 32768
+    else:
+        y = _prefill(oal, case, chunk)
     torch.cuda.synchronize()
     yc = y.float().cpu().numpy()
     assert np.all(np.isfinite(yc))
