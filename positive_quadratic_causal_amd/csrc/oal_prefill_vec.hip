@@ -53,7 +53,7 @@ __device__ __forceinline__ void axpy_row(float (&acc)[WP], float s, const float*
 // one feature's columns (consecutive threads, consecutive features).
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float fx16;
 template <typename T>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(256, 3)   // three blocks per CU (51 KB of LDS each)
 k_build_mfma(int seq_len, int chunk, int n_chunks, const T* __restrict__ k, const T* __restrict__ v,
              float* __restrict__ out) {
   const int fb = blockIdx.x;
