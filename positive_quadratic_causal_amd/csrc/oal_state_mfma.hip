@@ -383,15 +383,17 @@ k_state_stage(int seq_len, int chunk, int n_seg, int cps, const uint16_t* __rest
     bound[(size_t)unit * n_blk + blk] = (s_bred[0] + s_bred[1]) + (s_bred[2] + s_bred[3]);
 }
 
-template <int MODE>   // 0: segment sums, 1: per-chunk prefix tiles
+// MODE 0: segment sums; 1: per-chunk prefix tiles from the segments' starting
+// prefixes; 2: one segment from zero, the tiles and the sum in one pass.
+template <int MODE>
 __global__ void __launch_bounds__(256, 2)
 k_state_mfma(int seq_len, int chunk, int n_chunks, int n_seg, int cps, int n_blk,
              const uint8_t* __restrict__ stg,     // staged blocks (k_state_stage)
-             float* __restrict__ segsum,          // MODE 0: out sums
+             float* __restrict__ segsum,          // MODE 0, 2: out sums
              const uint16_t* __restrict__ segpre, // MODE 1: starting prefixes of waves 0..23, fp16 times 2^-e_S
              const float* __restrict__ sidepre,   // MODE 1: starting prefixes of wave 24
-             uint8_t* __restrict__ ts,            // MODE 1: per-chunk prefix tiles
-             const float* __restrict__ bound,     // MODE 1: tile-scale bound
+             uint8_t* __restrict__ ts,            // MODE 1, 2: per-chunk prefix tiles
+             const float* __restrict__ bound,     // MODE 1, 2: tile-scale bound
              const float* __restrict__ kvmax,     // per (unit, segment): max |k|, max |v|
              int units, int nip) {
   // three staged blocks in flight: block i is read while i + 1 and i + 2 load
@@ -421,14 +423,16 @@ k_state_mfma(int seq_len, int chunk, int n_chunks, int n_seg, int cps, int n_blk
   // scan forms the final state from the segment sums), so that mode adds the
   // blocks before the last chunk only and stores the last tile after them.
   const int n_add = MODE == 1 ? (c1 - 1 - c0) * chunk / st::TB : n_blocks;
+  constexpr bool TILES = MODE != 0;   // per-chunk prefix tiles stored
+  constexpr bool SUMS = MODE != 1;    // the segment's sum stored
   const uint8_t* sblk = stg + ((size_t)unit * n_blk + tok_begin / st::TB) * st::STG_BYTES;
   float* segslot = segsum + ((size_t)unit * n_seg + seg) * st::UNIT_SEG_FLOATS;
   const uint16_t* preslot = segpre + ((size_t)unit * n_seg + seg) * st::QUAD_SEG_FLOATS;
   // staged values are k 2^-e_k and v 2^-e_v
   const int e_k = st_exp_above(seg_max(kvmax, unit, n_seg, seg, 0)) - 7;
   const int e_v = st_exp_above(seg_max(kvmax, unit, n_seg, seg, 1)) - 7;
-  // MODE 1: the tile scale 2^-e_S of this unit
-  const int e_s = MODE == 1 ? tile_scale_exp(bound, units, n_blk, nip, unit, lane) : 0;
+  // with tiles: the tile scale 2^-e_S of this unit
+  const int e_s = TILES ? tile_scale_exp(bound, units, n_blk, nip, unit, lane) : 0;
   const float tscale = ldexpf(1.0f, -e_s);
 
   // Copies block bi of the segment into buf: PIECES 1 KB pieces per wave.
@@ -471,7 +475,7 @@ k_state_mfma(int seq_len, int chunk, int n_chunks, int n_seg, int cps, int n_blk
     const float wscale = unscale * tscale;   // accumulator -> tile entry
     // tile stores per chunk start: every tile, one 16-byte store per (tile, column half, K-step)
     constexpr int NST = st::QTILES * 2 * 2;   // store instructions per tile store (per lane)
-    auto stores_at = [&](int b) { return (MODE == 1 && b >= 0 && (b * st::TB) % chunk == 0) ? NST : 0; };
+    auto stores_at = [&](int b) { return (TILES && b >= 0 && (b * st::TB) % chunk == 0) ? NST : 0; };
 
     // The running prefix is chunk (t0 / chunk)'s exclusive prefix: store it;
     // rows 8 gq + 4 half .. + 3 of tile m are elements of one K-step.
@@ -513,7 +517,7 @@ k_state_mfma(int seq_len, int chunk, int n_chunks, int n_seg, int cps, int n_blk
       barrier_nofence();
       if (bi + 2 < n_add) issue(bi + 2, nxt, P4{});
       const int t0 = tok_begin + bi * st::TB;
-      if (MODE == 1 && (t0 % chunk) == 0) store_tile(t0);
+      if (TILES && (t0 % chunk) == 0) store_tile(t0);
       const uint8_t* kt_ = cur;
       const uint8_t* vt_ = cur + DH * 128;
 #pragma unroll
@@ -539,7 +543,7 @@ k_state_mfma(int seq_len, int chunk, int n_chunks, int n_seg, int cps, int n_blk
       body(bi + 2, s_b2, s_b1);
     }
     if (MODE == 1) store_tile(tok_begin + n_add * st::TB);   // the last chunk's tile
-    if (MODE == 0) {
+    if (SUMS) {
 #pragma unroll
       for (int m = 0; m < st::QTILES; ++m)
 #pragma unroll
@@ -587,7 +591,7 @@ k_state_mfma(int seq_len, int chunk, int n_chunks, int n_seg, int cps, int n_blk
   // (adjacent words; the lower count, so that the wait below is never short);
   // wave 1 16 for Z
   const int side_stores = lin ? 19 : ones ? 16 : 0;
-  auto stores_at = [&](int b) { return (MODE == 1 && b >= 0 && (b * st::TB) % chunk == 0) ? side_stores : 0; };
+  auto stores_at = [&](int b) { return (TILES && b >= 0 && (b * st::TB) % chunk == 0) ? side_stores : 0; };
   auto store_tile = [&](int t0) {
     uint8_t* slotp = ts + ((size_t)unit * n_chunks + t0 / chunk) * tile::BYTES;
     uint16_t* tl = reinterpret_cast<uint16_t*>(slotp);
@@ -636,7 +640,7 @@ k_state_mfma(int seq_len, int chunk, int n_chunks, int n_seg, int cps, int n_blk
     barrier_nofence();
     if (bi + 2 < n_add) issue(bi + 2, nxt, P4{});
     const int t0 = tok_begin + bi * st::TB;
-    if (MODE == 1 && (t0 % chunk) == 0) store_tile(t0);
+    if (TILES && (t0 % chunk) == 0) store_tile(t0);
     const uint8_t* kt_ = cur;
     const uint8_t* vt_ = cur + DH * 128;
     if (lin) {
@@ -680,7 +684,7 @@ k_state_mfma(int seq_len, int chunk, int n_chunks, int n_seg, int cps, int n_blk
     body(bi + 2, s_b2, s_b1);
   }
   if (MODE == 1) store_tile(tok_begin + n_add * st::TB);   // the last chunk's tile
-  if (MODE == 0 && (lin || ones)) {
+  if (SUMS && (lin || ones)) {
 #pragma unroll
     for (int m = 0; m < 2; ++m)
 #pragma unroll
@@ -898,7 +902,11 @@ oal_status launch_state_mfma(int batch, int n_kv_heads, int seq_len, int chunk, 
   const float* init_src = init_zero ? nullptr : state;   // the initial state, when one is read
   const int units = batch * n_kv_heads;
   const int n_chunks = (seq_len + chunk - 1) / chunk;
-  const int n_seg = choose_segments(units, n_chunks);
+  // With enough units for at most two segments and a sequence that starts empty,
+  // one pass walks whole sequences storing both the tiles and the sums (the final
+  // state's), instead of a sum pass over two segments before the tile pass.
+  const bool one_pass = ts != nullptr && init_src == nullptr && choose_segments(units, n_chunks) <= 2;
+  const int n_seg = one_pass ? 1 : choose_segments(units, n_chunks);
   const int cps = (n_chunks + n_seg - 1) / n_seg;
   const int n_seg_eff = (n_chunks + cps - 1) / cps;
   const int n_blk = (seq_len + st::TB - 1) / st::TB;
@@ -921,6 +929,22 @@ oal_status launch_state_mfma(int batch, int n_kv_heads, int seq_len, int chunk, 
                        cps, kk, vv, (const float*)w.kvmax, w.stg, w.bound);
     oal_status s = check_launch("k_state_stage");
     if (s != OAL_OK) return s;
+  }
+  if (one_pass) {
+    {
+      ProfScope ps("k_state_mfma", stream);
+      hipLaunchKernelGGL(k_state_mfma<2>, grid, dim3(256), 0, stream, seq_len, chunk, n_chunks,
+                         n_seg_eff, cps, n_blk, (const uint8_t*)w.stg, w.segsum, (const uint16_t*)nullptr,
+                         (const float*)nullptr, ts, (const float*)w.bound, (const float*)w.kvmax, units,
+                         nip);
+      oal_status s = check_launch("k_state_mfma");
+      if (s != OAL_OK || state == nullptr) return s;
+    }
+    ProfScope ps("k_state_segscan", stream);   // the one segment's sum to the canonical state
+    hipLaunchKernelGGL(k_state_segscan<2>, dim3((st::UNIT_SEG_FLOATS / 4 + 255) / 256, units), dim3(256),
+                       0, stream, n_seg_eff, (const float*)w.segsum, (uint16_t*)nullptr, (float*)nullptr,
+                       (const float*)nullptr, state, (const float*)w.bound, n_blk, nip);
+    return check_launch("k_state_segscan");
   }
   {
     ProfScope ps("k_state_seg", stream);

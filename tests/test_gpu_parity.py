@@ -239,6 +239,24 @@ def test_state_export_matches_oracle_state(oal, dtype):
     assert rel_l2(exp2, exp) <= 1e-6
 
 
+@pytest.mark.parametrize("n,chunk", [(600, 128), (1000, 256)])
+def test_fresh_prefill_many_units_one_pass(oal, n, chunk):
+    """32 (batch, KV head) units: a fresh prefill's builder walks each sequence in one
+    pass that stores both the prefix tiles and the sums; outputs against the oracle
+    and the final state against the oracle's canonical state."""
+    w = synth.small_workload(303, "one pass", 8, 8, 4, n, "bf16")
+    announce(f"fresh prefill B=8 8/4 N={n} bf16 chunk={chunk} (one-pass builder)")
+    case = Case(w)
+    st = oal.oal_state_alloc(8, 4)
+    y = oal.oal_prefill_fresh(case.q, case.k, case.v, case.coeffs(), st, chunk=chunk)
+    exp = oal.oal_state_export(st).cpu().numpy()
+    torch.cuda.synchronize()
+    _check_heads(case, y, [(0, 0), (3, 5), (7, 7), (5, 2)], tol_for(w))
+    for b, kv in ((0, 0), (4, 3), (7, 1)):
+        _, k, v = case.head_qkv(b, kv * 2, n)
+        assert rel_l2(exp[b, kv], O.canonical_state(k, v)) <= 1e-3
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_decode_after_prefill(oal, dtype):
     n0, steps = 130, 9
