@@ -395,7 +395,8 @@ k_state_mfma(int seq_len, int chunk, int n_chunks, int n_seg, int cps, int n_blk
              uint8_t* __restrict__ ts,            // MODE 1, 2: per-chunk prefix tiles
              const float* __restrict__ bound,     // MODE 1, 2: tile-scale bound
              const float* __restrict__ kvmax,     // per (unit, segment): max |k|, max |v|
-             int units, int nip) {
+             int units, int nip,
+             float* __restrict__ state_out) {     // MODE 2: the final state (canonical), or null
   // three staged blocks in flight: block i is read while i + 1 and i + 2 load
   __shared__ __attribute__((aligned(16))) uint8_t s_b0[st::STG_BYTES];
   __shared__ __attribute__((aligned(16))) uint8_t s_b1[st::STG_BYTES];
@@ -428,6 +429,20 @@ k_state_mfma(int seq_len, int chunk, int n_chunks, int n_seg, int cps, int n_blk
   const uint8_t* sblk = stg + ((size_t)unit * n_blk + tok_begin / st::TB) * st::STG_BYTES;
   float* segslot = segsum + ((size_t)unit * n_seg + seg) * st::UNIT_SEG_FLOATS;
   const uint16_t* preslot = segpre + ((size_t)unit * n_seg + seg) * st::QUAD_SEG_FLOATS;
+  // Where a sum goes: its raw slot (MODE 0), or the canonical final state (MODE 2,
+  // each entry from its stored copy; with no state, nowhere).
+  float* ustate = state_out ? state_out + (size_t)unit * STATE_FLOATS : nullptr;
+  const bool put_sums = MODE == 0 || (MODE == 2 && ustate != nullptr);
+  auto put = [&](float* slot_, int omega_, int reg, float x) __attribute__((always_inline)) {
+    if (MODE == 0) {
+      slot_[(size_t)reg * 64 + lane] = x;
+      return;
+    }
+    int f, w;
+    bool valid, primary;
+    state_elem(omega_, reg, lane, f, w, valid, primary);
+    if (valid && primary) ustate[(size_t)w * DS + f] = x;
+  };
   // staged values are k 2^-e_k and v 2^-e_v
   const int e_k = st_exp_above(seg_max(kvmax, unit, n_seg, seg, 0)) - 7;
   const int e_v = st_exp_above(seg_max(kvmax, unit, n_seg, seg, 1)) - 7;
@@ -543,14 +558,13 @@ k_state_mfma(int seq_len, int chunk, int n_chunks, int n_seg, int cps, int n_blk
       body(bi + 2, s_b2, s_b1);
     }
     if (MODE == 1) store_tile(tok_begin + n_add * st::TB);   // the last chunk's tile
-    if (SUMS) {
+    if (SUMS && put_sums) {
 #pragma unroll
       for (int m = 0; m < st::QTILES; ++m)
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-          for (int i = 0; i < 16; ++i)
-            slot[(size_t)((m * 2 + nt) * 16 + i) * 64 + lane] = acc[m][nt][i] * unscale;
+          for (int i = 0; i < 16; ++i) put(slot, omega, (m * 2 + nt) * 16 + i, acc[m][nt][i] * unscale);
     }
     return;
   }
@@ -684,18 +698,17 @@ k_state_mfma(int seq_len, int chunk, int n_chunks, int n_seg, int cps, int n_blk
     body(bi + 2, s_b2, s_b1);
   }
   if (MODE == 1) store_tile(tok_begin + n_add * st::TB);   // the last chunk's tile
-  if (SUMS && (lin || ones)) {
+  if (SUMS && put_sums && (lin || ones)) {
 #pragma unroll
     for (int m = 0; m < 2; ++m)
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-        for (int i = 0; i < 16; ++i)
-          slot[(size_t)(((mo + m) * 2 + nt) * 16 + i) * 64 + lane] = acc[m][nt][i] * sc_acc;
+        for (int i = 0; i < 16; ++i) put(slot, 24, ((mo + m) * 2 + nt) * 16 + i, acc[m][nt][i] * sc_acc);
     if (lin) {
-      slot[(size_t)st::REG_H0 * 64 + lane] = side_h0 * sc_h0;
-      slot[(size_t)st::REG_Z1 * 64 + lane] = side_z1 * sc_z1;
-      slot[(size_t)st::REG_Z0 * 64 + lane] = lane == 0 ? side_z0 : 0.f;
+      put(slot, 24, st::REG_H0, side_h0 * sc_h0);
+      put(slot, 24, st::REG_Z1, side_z1 * sc_z1);
+      put(slot, 24, st::REG_Z0, lane == 0 ? side_z0 : 0.f);
     }
   }
 }
@@ -930,28 +943,20 @@ oal_status launch_state_mfma(int batch, int n_kv_heads, int seq_len, int chunk, 
     oal_status s = check_launch("k_state_stage");
     if (s != OAL_OK) return s;
   }
-  if (one_pass) {
-    {
-      ProfScope ps("k_state_mfma", stream);
-      hipLaunchKernelGGL(k_state_mfma<2>, grid, dim3(256), 0, stream, seq_len, chunk, n_chunks,
-                         n_seg_eff, cps, n_blk, (const uint8_t*)w.stg, w.segsum, (const uint16_t*)nullptr,
-                         (const float*)nullptr, ts, (const float*)w.bound, (const float*)w.kvmax, units,
-                         nip);
-      oal_status s = check_launch("k_state_mfma");
-      if (s != OAL_OK || state == nullptr) return s;
-    }
-    ProfScope ps("k_state_segscan", stream);   // the one segment's sum to the canonical state
-    hipLaunchKernelGGL(k_state_segscan<2>, dim3((st::UNIT_SEG_FLOATS / 4 + 255) / 256, units), dim3(256),
-                       0, stream, n_seg_eff, (const float*)w.segsum, (uint16_t*)nullptr, (float*)nullptr,
-                       (const float*)nullptr, state, (const float*)w.bound, n_blk, nip);
-    return check_launch("k_state_segscan");
+  if (one_pass) {   // the sums go straight into the canonical state: no scan
+    ProfScope ps("k_state_mfma", stream);
+    hipLaunchKernelGGL(k_state_mfma<2>, grid, dim3(256), 0, stream, seq_len, chunk, n_chunks,
+                       n_seg_eff, cps, n_blk, (const uint8_t*)w.stg, w.segsum, (const uint16_t*)nullptr,
+                       (const float*)nullptr, ts, (const float*)w.bound, (const float*)w.kvmax, units,
+                       nip, state);
+    return check_launch("k_state_mfma");
   }
   {
     ProfScope ps("k_state_seg", stream);
     hipLaunchKernelGGL(k_state_mfma<0>, grid, dim3(256), 0, stream, seq_len, chunk, n_chunks,
                        n_seg_eff, cps, n_blk, (const uint8_t*)w.stg, w.segsum, (const uint16_t*)nullptr,
                        (const float*)nullptr, (uint8_t*)nullptr, (const float*)nullptr,
-                       (const float*)w.kvmax, units, nip);
+                       (const float*)w.kvmax, units, nip, (float*)nullptr);
     oal_status s = check_launch("k_state_seg");
     if (s != OAL_OK) return s;
   }
@@ -971,7 +976,7 @@ oal_status launch_state_mfma(int batch, int n_kv_heads, int seq_len, int chunk, 
   hipLaunchKernelGGL(k_state_mfma<1>, grid, dim3(256), 0, stream, seq_len, chunk, n_chunks,
                      n_seg_eff, cps, n_blk, (const uint8_t*)w.stg, w.segsum, (const uint16_t*)w.segpre,
                      (const float*)w.sidepre, ts, (const float*)w.bound, (const float*)w.kvmax, units,
-                     nip);
+                     nip, (float*)nullptr);
   return check_launch("k_state_mfma");
 }
 
