@@ -32,7 +32,11 @@
 // A batch-1 long sequence has too few units to fill 256 CUs, so the sequence is
 // cut into S segments:  pass 1 (sum mode) adds up every segment,  the scan forms
 // each segment's starting prefix (plus the caller's initial state) and the final
-// state,  pass 2 (prefix mode) replays each segment writing the per-chunk tiles.
+// state,  pass 2 (prefix mode) replays each segment writing the per-chunk tiles
+// (up to the segment's last chunk, whose sum no tile needs).  With enough units
+// for at most two segments and a sequence that starts empty, one pass (mode 2)
+// walks each whole sequence, writing the tiles and, at its end, the final state
+// straight in the canonical layout.
 //
 // fp16 tiles need a scale: every entry of every prefix of a unit is bounded by
 //   B = max |H_init| + sum_j beta_j,   beta_j = max(|k_j|, |k_j|^2) |v_j|
