@@ -98,6 +98,30 @@ def test_backward_grouped_small(oal, dtype, chunk, n):
         assert rel_l2(dL.cpu().numpy(), dLr) <= 1e-5
 
 
+@pytest.mark.parametrize("chunk", [64, 128])
+def test_backward_single_group(oal, chunk):
+    """G = 1 (one group holding every dim): the learned-global kernel through the
+    backward, where the matrix-core pair kernel has one group-sum chain and two
+    weighted terms (v = 0, 1)."""
+    w = synth.small_workload(870, "bwd global", 1, 4, 2, 150, "f32")
+    announce(f"backward G=1 4/2 N=150 f32 chunk={chunk}")
+    case = Case(w)
+    rng = np.random.default_rng(13)
+    for h in range(4):
+        case.st.n_groups[h] = 1
+        case.st.group_map[h] = 1
+        case.st.L[h] = synth.random_L(rng, 1)
+    case.n_groups = torch.from_numpy(case.st.n_groups.astype(np.int32)).to("cuda")
+    case.group_map = torch.from_numpy(case.st.group_map.astype(np.int32)).to("cuda")
+    case.L = torch.from_numpy(case.st.L.astype(np.float32)).to("cuda")
+    dy = _dy(871, (1, 4, 150, 64))
+    got = _run(oal, case, dy, case.coeffs(), chunk)
+    ref = _oracle_grads(case, dy, lambda h: _grouped_abc(case, h))
+    for name, g_, r_ in zip(["dq", "dk", "dv", "da", "db", "dC"], got, ref):
+        err = rel_l2(g_, r_)
+        assert err <= 1e-4, (name, err)
+
+
 def test_backward_dimension_specific_record(oal):
     w = synth.small_workload(830, "bwd dim", 1, 7, 1, 150, "f32")
     announce("backward with a dimension-specific record, 7/1 N=150 f32 chunk=64")
