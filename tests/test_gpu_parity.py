@@ -255,6 +255,19 @@ def test_fresh_prefill_many_units_one_pass(oal, n, chunk):
     for b, kv in ((0, 0), (4, 3), (7, 1)):
         _, k, v = case.head_qkv(b, kv * 2, n)
         assert rel_l2(exp[b, kv], O.canonical_state(k, v)) <= 1e-3
+    # the state the one pass wrote is a valid start: the sequence's first half
+    # fresh, then the second half continued from it (read as the initial state)
+    h = n // 2
+    st2 = oal.oal_state_alloc(8, 4)
+    oal.oal_prefill_fresh(None, case.k[:, :, :h].contiguous(), case.v[:, :, :h].contiguous(), None,
+                          st2, chunk=chunk, want_output=False)
+    y2 = oal.oal_prefill(case.q[:, :, h:].contiguous(), case.k[:, :, h:].contiguous(),
+                         case.v[:, :, h:].contiguous(), case.coeffs(), chunk=chunk, state=st2)
+    exp2 = oal.oal_state_export(st2).cpu().numpy()
+    torch.cuda.synchronize()
+    assert rel_l2(exp2, exp) <= 4e-3
+    yh = y[:, :, h:].float().cpu().numpy()
+    assert rel_l2(y2.float().cpu().numpy(), yh) <= 2e-2
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
