@@ -105,13 +105,19 @@ __device__ __forceinline__ uint8_t* pick4(int i, uint8_t* a, uint8_t* b, uint8_t
   return i == 0 ? a : i == 1 ? b : i == 2 ? c : d;
 }
 
-template <int CH, typename O>
+// HALF: each wave takes one token tile (as N-tile 1) instead of two, so that a
+// workgroup covers half of its head's chunk (chunk 256 only).  A half workgroup
+// takes about 80 % of a whole one's time, so an item that has a round to itself
+// finishes sooner as two of them (short sequences).
+template <int CH, typename O, bool HALF>
 __global__ void __launch_bounds__(256, 2)
 k_readout_mfma(int n_q_heads, int n_kv_heads, int seq_len, int n_chunks, int n_hg, int n_uc,
                const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                const uint16_t* __restrict__ v, const float* __restrict__ coeffs,
                const uint8_t* __restrict__ ws_tile, O* __restrict__ y) {
   using Cfg = ReadoutCfg<CH>;
+  static_assert(!HALF || CH == 256, "half workgroups are laid out for chunk 256");
+  constexpr int NT0 = HALF ? 1 : 0;   // first N-tile of the wave
   __shared__ __attribute__((aligned(16))) uint8_t s_q[Cfg::Q_BYTES];
   __shared__ __attribute__((aligned(16))) uint8_t s_b0[Cfg::HS_BYTES];
   __shared__ __attribute__((aligned(16))) uint8_t s_b1[Cfg::HS_BYTES];
@@ -130,8 +136,12 @@ k_readout_mfma(int n_q_heads, int n_kv_heads, int seq_len, int n_chunks, int n_h
 
   // ---- which (unit, chunk, head group): the head groups of one (unit, chunk)
   //      share an XCD (blockIdx % 8) so they hit the same L2 for the state.
+  //      slot: the item's index among those of its XCD; in half mode two
+  //      consecutive workgroups of an XCD share an item.
   const int L = blockIdx.x;
-  const int xcd = L & 7, slot = L >> 3;
+  const int xcd = L & 7;
+  const int slot = HALF ? (L >> 4) : (L >> 3);
+  const int part = HALF ? (L >> 3) & 1 : 0;
   const int uc = (slot / n_hg) * 8 + xcd;
   const int hg = slot % n_hg;
   if (uc >= n_uc) return;
@@ -148,7 +158,7 @@ k_readout_mfma(int n_q_heads, int n_kv_heads, int seq_len, int n_chunks, int n_h
   // Wave sub >= WPH / 2 meets one key tile fewer inside the chunk than its
   // mirror WPH - 1 - sub (token tiles below): it computes the inter-chunk
   // denominators of both (one Z operand) and hands the mirror's over through LDS.
-  constexpr bool PAIRED = Cfg::WPH > 1;
+  constexpr bool PAIRED = Cfg::WPH > 1 && !HALF;
   const bool den_giver = !PAIRED || sub >= Cfg::WPH / 2;
   const int msub = Cfg::WPH - 1 - sub;
   const int hl = hg * Cfg::HPW + hslot;
@@ -356,7 +366,10 @@ k_readout_mfma(int n_q_heads, int n_kv_heads, int seq_len, int n_chunks, int n_h
 
   // token tiles of this wave (32 tokens each): sub and 2 WPH - 1 - sub, so that
   // the waves of a head meet equal parts of the causal triangle inside the chunk
-  const int T0 = sub, T1 = 2 * Cfg::WPH - 1 - sub;
+  // (half mode: the one tile, as N-tile 1, is 7, 0, 5, 2 in part 0 and 6, 1, 4, 3
+  // in part 1, so that the two workgroups of an item meet 15 and 13 key tiles)
+  const int T1 = HALF ? ((sub & 1) ? sub - 1 + part : 7 - sub - part) : 2 * Cfg::WPH - 1 - sub;
+  const int T0 = HALF ? T1 : sub;
   const uint8_t* qw = s_q + hslot * CH * 128;
   const SwRow qrow0(qw, 32 * T0 + col), qrow1(qw, 32 * T1 + col);   // tokens of N-tiles 0, 1
   // q fragment (B operand, columns = tokens, K = head dims): exact bf16 inputs
@@ -412,6 +425,7 @@ k_readout_mfma(int n_q_heads, int n_kv_heads, int seq_len, int n_chunks, int n_h
     float dd[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) dd[nt] = 0.f;
+    constexpr int D0 = TWO ? 0 : NT0;   // first N-tile computed
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
       const int n = 32 * mt + col;
@@ -422,7 +436,7 @@ k_readout_mfma(int n_q_heads, int n_kv_heads, int seq_len, int n_chunks, int n_h
       for (int g4 = 0; g4 < 4; ++g4) {
         const float4 bz = *reinterpret_cast<const float4*>(ht + htab::BZ + 32 * mt + 8 * g4 + 4 * half);
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
+        for (int nt = D0; nt < NT; ++nt) {
           T[nt][4 * g4 + 0] = bz.x;
           T[nt][4 * g4 + 1] = bz.y;
           T[nt][4 * g4 + 2] = bz.z;
@@ -437,11 +451,11 @@ k_readout_mfma(int n_q_heads, int n_kv_heads, int seq_len, int n_chunks, int n_h
                             z1.x * (float)m8[4], z1.y * (float)m8[5], z1.z * (float)m8[6], z1.w * (float)m8[7]};
         const bf16x8 az = pack8(x);
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
+        for (int nt = D0; nt < NT; ++nt)
           T[nt] = mfma32(az, *reinterpret_cast<const bf16x8*>(rows[nt].chunk(2 * ks + half)), T[nt]);
       }
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
+      for (int nt = D0; nt < NT; ++nt) {
         float d = 0.f;
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {   // rows 32 mt + 8 g4 + 4 half + e, e = 0..3
@@ -457,7 +471,7 @@ k_readout_mfma(int n_q_heads, int n_kv_heads, int seq_len, int n_chunks, int n_h
     const float az0 = half == 0 ? rec[OAL_COEF_A] * ts_side[tile::SIDE_Z0] : 0.f;
     const float sc = ldexpf(F, e_m);
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) den[nt] += dd[nt] * sc + az0 * F;
+    for (int nt = D0; nt < 2; ++nt) den[nt] += dd[nt] * sc + az0 * F;
     if (TWO) {
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {   // whole sums (both lane halves) of the mirror's tokens
@@ -690,7 +704,14 @@ k_readout_mfma(int n_q_heads, int n_kv_heads, int seq_len, int n_chunks, int n_h
     // key tiles 0 .. T1: both token tiles up to T0 (T0 the diagonal one of N-tile
     // 0), then N-tile 1 alone (T1 its diagonal one).  With two passes T0 < 4 <= T1:
     // the first pass holds key tiles 0..3, the second 4..7.
-    if (head_ok) {
+    if constexpr (HALF) {   // N-tile 1 alone: key tiles 0 .. T1 (two passes)
+      if (head_ok) {
+        if (T1 < 4)
+          singles(0, T1 + 1, bool_t<true>{});
+        else
+          singles(0, 4, F_{});
+      }
+    } else if (head_ok) {
       for (int kt = 0; kt < T0; ++kt) unit(kt, M1{}, F_{}, F_{});
       unit(T0, M1{}, bool_t<true>{}, F_{});
       if (Cfg::NPASS == 1)
@@ -703,7 +724,7 @@ k_readout_mfma(int n_q_heads, int n_kv_heads, int seq_len, int n_chunks, int n_h
       __syncthreads();   // every wave is done with the first pass's keys
       stage_kv(1);
       __syncthreads();
-      if (head_ok) singles(0, T1 - 4 + 1, bool_t<true>{});
+      if (head_ok && (!HALF || T1 >= 4)) singles(0, T1 - 4 + 1, bool_t<true>{});
     }
   }
 
@@ -918,7 +939,7 @@ k_readout_mfma(int n_q_heads, int n_kv_heads, int seq_len, int n_chunks, int n_h
   // ================= epilogue: + a F H0, normalise, store ======================
   if (!head_ok) return;
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
+  for (int nt = NT0; nt < 2; ++nt) {
     den[nt] += __shfl_xor(den[nt], 32, 64);
     if (!den_giver) den[nt] += dx[32 * nt + col];   // written before the intra-chunk barrier
   }
@@ -928,7 +949,7 @@ k_readout_mfma(int n_q_heads, int n_kv_heads, int seq_len, int n_chunks, int n_h
   int col_e = (int)(threadIdx.x & 31);
   asm volatile("" : "+v"(col_e));
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
+  for (int nt = NT0; nt < 2; ++nt) {
     const int tok = 32 * (nt ? T1 : T0) + col_e;
     if (tok >= clen) continue;
     // NG = 0 marks a dimension-specific record, which this grouped readout
@@ -955,6 +976,33 @@ oal_status launch_state_mfma(int batch, int n_kv_heads, int seq_len, int chunk, 
                              const void* v, float* state, bool init_zero, uint8_t* ts, void* ws,
                              hipStream_t stream);
 
+// Workgroup slots of one XCD for the readout: two workgroups per CU, the CUs
+// split evenly over the 8 XCDs.
+static int readout_slots_per_xcd() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 8)
+    return 64;
+  return 2 * (cus / 8);
+}
+
+template <int CH, typename O, bool HALF>
+static void readout_grid(int S, int n_q_heads, int n_kv_heads, int seq_len, int n_chunks,
+                         int n_hg, int n_uc, const void* q, const void* k, const void* v,
+                         const void* coeffs, const uint8_t* ts, void* y, hipStream_t stream) {
+  const long long blocks = 8LL * (HALF ? 2 : 1) * S;
+  hipLaunchKernelGGL((k_readout_mfma<CH, O, HALF>), dim3((unsigned)blocks), dim3(256), 0, stream, n_q_heads,
+                     n_kv_heads, seq_len, n_chunks, n_hg, n_uc,
+                     reinterpret_cast<const uint16_t*>(q), reinterpret_cast<const uint16_t*>(k),
+                     reinterpret_cast<const uint16_t*>(v), reinterpret_cast<const float*>(coeffs), ts,
+                     reinterpret_cast<O*>(y));
+}
+
+// The items (unit x chunk, head group) of each XCD run in rounds of its slots.
+// At chunk 256, items that fill at most half of one round run as half
+// workgroups (two per item in the same slots, each about 80 % as long as a whole
+// one): a short sequence then finishes sooner.  A half round after whole rounds
+// stays whole: as a second launch it cost more than it saved (measured).
 template <int CH, typename O>
 static oal_status readout_launch(int batch, int n_q_heads, int n_kv_heads, int seq_len,
                                  int n_chunks, const void* q, const void* k, const void* v,
@@ -965,14 +1013,18 @@ static oal_status readout_launch(int batch, int n_q_heads, int n_kv_heads, int s
   const int rep = n_q_heads / n_kv_heads;
   const int n_hg = (rep + Cfg::HPW - 1) / Cfg::HPW;
   const int n_uc = units * n_chunks;
-  const long long blocks = 8LL * n_hg * ((n_uc + 7) / 8);
-  auto kern = &k_readout_mfma<CH, O>;
+  const int S = n_hg * ((n_uc + 7) / 8);   // items per XCD
   ProfScope ps("k_readout_mfma", stream);
-  hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(256), 0, stream, n_q_heads,
-                     n_kv_heads, seq_len, n_chunks, n_hg, n_uc,
-                     reinterpret_cast<const uint16_t*>(q), reinterpret_cast<const uint16_t*>(k),
-                     reinterpret_cast<const uint16_t*>(v), reinterpret_cast<const float*>(coeffs), ts,
-                     reinterpret_cast<O*>(y));
+  bool half = false;
+  if constexpr (CH == 256) half = 2 * S <= readout_slots_per_xcd();
+  if (half) {
+    if constexpr (CH == 256)
+      readout_grid<CH, O, true>(S, n_q_heads, n_kv_heads, seq_len, n_chunks, n_hg, n_uc, q, k, v, coeffs,
+                                ts, y, stream);
+  } else {
+    readout_grid<CH, O, false>(S, n_q_heads, n_kv_heads, seq_len, n_chunks, n_hg, n_uc, q, k, v, coeffs,
+                               ts, y, stream);
+  }
   return check_launch("k_readout_mfma");
 }
 
