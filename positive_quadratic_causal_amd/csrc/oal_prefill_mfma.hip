@@ -34,12 +34,12 @@ namespace oal {
 // exponent - e_S: the factor cancels in y = u~_{1:64} / u~_65 and all scalings
 // are exact powers of two.
 //
-// LDS.  Every region is a __shared__ object of its own, so that the compiler
-// can tell the state half-slab buffers (filled by direct-to-LDS loads that stay
-// in flight across iterations) from the q tile and the tables it reads
-// meanwhile.  Rows of 64 bf16 are 128 bytes with the 16-byte chunks XOR-swizzled
-// by row_key(row) instead of padded.  Before the inter-chunk loop the buffers
-// hold the chunk's k rows and v^T rows.
+// LDS.  Every region is a __shared__ object of its own (the q tile, four 8 KB
+// buffers that hold the chunk's k rows and v^T rows for the intra-chunk part,
+// the per-head tables).  Rows of 64 bf16 are 128 bytes with the 16-byte chunks
+// XOR-swizzled by row_key(row) instead of padded.  The state tile is not staged:
+// each wave reads its fragments from the tile in global memory (an L2 shared by
+// the head groups of the chunk) one half-slab ahead.
 // ---------------------------------------------------------------------------
 template <int CH>
 struct ReadoutCfg {
@@ -71,14 +71,6 @@ constexpr int FLOATS = BZ + DH;
 }  // namespace htab
 
 
-// Swizzled LDS offset of the 16-byte half-row (w, h) of a K-step inside a
-// half-slab: the half is flipped by bit 2 ^ bit 3 ^ bit 4 of w, so that lanes
-// reading rows w = 0..31 hit distinct banks for 8, 16 or 32 lanes per cycle.
-__device__ __forceinline__ int slab_flip(int w) { return ((w >> 2) ^ (w >> 3) ^ (w >> 4)) & 1; }
-__device__ __forceinline__ int slab_off(int kk, int w, int h) {
-  return kk * tile::KS_BYTES + w * 32 + 16 * (h ^ slab_flip(w));
-}
-
 __device__ __forceinline__ float wave_max(float x) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
@@ -100,10 +92,6 @@ __device__ __forceinline__ int exp_above(float x) {
 
 template <bool B>
 using bool_t = std::integral_constant<bool, B>;
-
-__device__ __forceinline__ uint8_t* pick4(int i, uint8_t* a, uint8_t* b, uint8_t* c, uint8_t* d) {
-  return i == 0 ? a : i == 1 ? b : i == 2 ? c : d;
-}
 
 // HALF: each wave takes one token tile (as N-tile 1) instead of two, so that a
 // workgroup covers half of its head's chunk (chunk 256 only).  A half workgroup
@@ -218,7 +206,7 @@ k_readout_mfma(int n_q_heads, int n_kv_heads, int seq_len, int n_chunks, int n_h
   // reductions, barrier and tables, and the denominator is computed before the
   // intra-chunk part; with one (C = 64, four
   // heads staged, where holding it would spill) it is loaded in place, after the
-  // intra-chunk barrier, while the first half-slabs load.
+  // intra-chunk part, while the first half-slab's fragments load.
   constexpr bool ZPRE = Cfg::WPH > 1;
   float4 zv[2][4][2];
   auto load_z = [&]() {
@@ -383,34 +371,6 @@ k_readout_mfma(int n_q_heads, int n_kv_heads, int seq_len, int n_chunks, int n_h
   for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = splat16(0.f);
-
-  // Half-slab hs of the tile goes to buffer hs % 4 by direct-to-LDS buffer loads,
-  // issued while half-slab hs - 4 is multiplied from registers (the buffers hold
-  // k and v^T until the intra-chunk part is done).  Each wave moves two 1 KB pieces of a
-  // half-slab, lane l writing bytes 16 l .. 16 l + 15 of a piece,
-  // fetched from the tile position that the swizzle of slab_off puts there.
-  // The loads are issued from inline assembly: the compiler then neither waits
-  // for them before LDS reads it cannot prove disjoint from the buffers, nor
-  // before rewriting their operand registers.  Their completion is awaited by
-  // hand (wait_vmcnt) before the barrier that hands a buffer to the waves;
-  // other memory operations of the wave complete in issue order with them, so
-  // the compiler's own counts stay safe (only stricter).
-  uint32_t dma_off[2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int piece = wave * 2 + i;                 // 1 KB piece of the half-slab
-    const int kk = piece >> 1, pos = (piece & 1) * 64 + lane;
-    const int w = pos >> 1, hh = (pos & 1) ^ slab_flip(w);
-    dma_off[i] = kk * tile::KS_BYTES + w * 32 + hh * 16;
-  }
-  const i32x4 tile_rsrc = buffer_rsrc(tsrc, (uint32_t)tile::TILE_BYTES);
-  auto buf = [&](int hs) -> uint8_t* { return pick4(hs & 3, s_b0, s_b1, s_b2, s_b3); };
-  auto issue = [&](int hs, uint8_t* buf) {
-    const int soff = min(hs, Cfg::NHS - 1) * Cfg::HS_BYTES;
-    const uint32_t dst = lds_addr(buf) + wave * 2048;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) load_lds16(tile_rsrc, dst + i * 1024, dma_off[i], soff);
-  };
 
   // ---- inter-chunk denominator: a z0 + sum_r q_r (b'_r z1_r + ((C / d_h o Z) q)_r),
   //      T = b' o z1 + (C/d_h o Z) q^T on the matrix cores (the first term as the
@@ -729,54 +689,58 @@ k_readout_mfma(int n_q_heads, int n_kv_heads, int seq_len, int n_chunks, int n_h
   }
 
   // ================= inter-chunk part ======================================
-  __syncthreads();   // the half-slab buffers held k / v^T
-  issue(0, buf(0));
-  issue(1, buf(1));
-  issue(2, buf(2));
-  issue(3, buf(3));
+  // The main loop uses no LDS buffer; the waves still meet here so that they
+  // start it together and their fragment reads of the same tile meet in the
+  // caches (without it, 3 % slower at N=32768, measured).  It also orders the
+  // mirror waves' denominators (dx) before their reads in the epilogue.
+  __syncthreads();
   if (!ZPRE && head_ok) denominator(bool_t<false>{});
 
   // ---- main K loop over the 37 half-slabs: 1 linear, then 4 c + 3 per t-block c
-  //      (the last of them the merged rows of the diagonal block); half-slab hs
-  //      sits in buffer hs % 4
+  //      (the last of them the merged rows of the diagonal block).  Each wave
+  //      reads its state fragments straight from the tile (L2: the head groups of
+  //      a (unit, chunk) share an XCD) one half-slab ahead into registers, so the
+  //      loop has no barrier and the waves of a workgroup run independently.
   const uint8_t* mgh0 = reinterpret_cast<const uint8_t*>(s_mg + hslot * LDIM * DH);
   const uint8_t* mgh = mgh0 + 16 * half;
-  f16x8 qt[2], qh[2];
+  f16x8 qt[2], qh[2];   // qh: q_t M of the current group (chunk 64)
   int cur = -1;
   // The state fragments of a half-slab in registers: K-step i, rows 32 mt + col.
   using AFrag = f16x8[4][2];
-  auto load_af = [&](AFrag& af, const uint8_t* sb) {
+  auto load_af = [&](AFrag& af, int hs) {
+    const uint8_t* g = tsrc + (size_t)min(hs, Cfg::NHS - 1) * Cfg::HS_BYTES + col * 32 + 16 * half;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
-        af[i][mt] = *reinterpret_cast<const f16x8*>(sb + slab_off(i, 32 * mt + col, half));
+        af[i][mt] = *reinterpret_cast<const f16x8*>(g + i * tile::KS_BYTES + mt * 32 * 32);
   };
-  // Every product step first issues its own LDS reads (q rows, M rows), then the
-  // reads of the next half-slab's fragments (nx from nsb, when pf), then its
-  // products: LDS reads return in order, so the products wait only for their own
-  // operands and the next fragments arrive behind them.
-  // one half-slab of rows r0 .. r0 + 3 of t-block c: K-steps (r0 + i, c)
-  auto quad = [&](int c, int h, const AFrag& af, AFrag& nx, const uint8_t* nsb, bool pf) {
+  // One half-slab of rows r0 .. r0 + 3 of t-block c (K-steps (r0 + i, c)) from the
+  // fragments af, while the fragments of half-slab nsb load into nx (when pf).
+  // From chunk 128 on the feature build has no branch (every row's M row is read
+  // and q_t M formed again), so that the compiler can interleave the next step's
+  // multiplies with the current step's products; at chunk 64 (four heads staged,
+  // where the extra registers would spill) M rows are read and q_t M formed only
+  // where the group changes from the row before.
+  constexpr bool BRANCH_FREE = CH >= 128;
+  auto quad = [&](int c, int h, const AFrag& af, AFrag& nx, int nsb, bool pf) {
     const int r0 = 4 * h;
     uint2 u[2];
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) u[nt] = *reinterpret_cast<const uint2*>((nt ? qrow1 : qrow0).elem(r0));
     const uint8_t* mgc = mgh + 32 * c;
     int gi[4];
-    f16x8 m8[4];   // M_{g(r), g(t)} / d_h (scaled), read only for a row whose group differs from the row before
+    f16x8 m8[4];   // M_{g(r), g(t)} / d_h (scaled) of the four rows
     int pg = cur;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       gi[i] = __builtin_amdgcn_readlane(gl, r0 + i);
-      if (gi[i] != pg) m8[i] = *reinterpret_cast<const f16x8*>(mgc + gi[i] * (DH * 2));
+      if (BRANCH_FREE || gi[i] != pg) m8[i] = *reinterpret_cast<const f16x8*>(mgc + gi[i] * (DH * 2));
       pg = gi[i];
     }
     __builtin_amdgcn_sched_barrier(0);
     if (pf) load_af(nx, nsb);
     __builtin_amdgcn_sched_barrier(0);
-    // m q_r of r0 .. r0 + 3, scaled, as fp16: m = 2 off the diagonal 16-block and
-    // for its upper t-half (whose mirrored pairs are not stored), 1 otherwise
     const float qs = (r0 < 16 * c || half == 1) ? 2.0f * qr_scale : qr_scale;
     _Float16 qr[2][4];
 #pragma unroll
@@ -790,20 +754,22 @@ k_readout_mfma(int n_q_heads, int n_kv_heads, int seq_len, int n_chunks, int n_h
       qr[nt][2] = hi[0];
       qr[nt][3] = hi[1];
     }
-    // the 16 products of the half-slab at raised wave priority, so that a wave
-    // with its products ready issues them ahead of the co-resident waves' loads
-    // and feature arithmetic (about 1 % on this kernel, measured)
     __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      // qhat = q_t M_{g(r), g(t)} / d_h (scaled), recomputed when g(r) changes
-      if (gi[i] != cur) {
-        cur = gi[i];
-        qh[0] = qt[0] * m8[i];
-        qh[1] = qt[1] * m8[i];
+      f16x8 f0, f1;
+      if constexpr (BRANCH_FREE) {
+        f0 = (qt[0] * m8[i]) * qr[0][i];
+        f1 = (qt[1] * m8[i]) * qr[1][i];
+      } else {
+        if (gi[i] != cur) {   // qhat = q_t M_{g(r), g(t)} / d_h (scaled), recomputed when g(r) changes
+          cur = gi[i];
+          qh[0] = qt[0] * m8[i];
+          qh[1] = qt[1] * m8[i];
+        }
+        f0 = qh[0] * qr[0][i];
+        f1 = qh[1] * qr[1][i];
       }
-      const f16x8 f0 = qh[0] * qr[0][i];
-      const f16x8 f1 = qh[1] * qr[1][i];
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt) {
         acc[mt][0] = mfma32h(af[i][mt], f0, acc[mt][0]);
@@ -814,7 +780,7 @@ k_readout_mfma(int n_q_heads, int n_kv_heads, int seq_len, int n_chunks, int n_h
   };
   // the merged half-slab of t-block c: K-step i holds rows 16 c + 8 + 2 i + half
   // against t = 16 c + 8 .. 16 c + 15 in both lane halves (multiplicity 1)
-  auto quad_merged = [&](int c, const AFrag& af, AFrag& nx, const uint8_t* nsb, bool pf) {
+  auto quad_merged = [&](int c, const AFrag& af, AFrag& nx, int nsb, bool pf) {
     bf16x8 qv[2];
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) qv[nt] = *reinterpret_cast<const bf16x8*>((nt ? qrow1 : qrow0).chunk(2 * c + 1));
@@ -853,25 +819,11 @@ k_readout_mfma(int n_q_heads, int n_kv_heads, int seq_len, int n_chunks, int n_h
       }
     }
   };
-  // Step hs of the half-slab ring: every wave holds the fragments of half-slab hs
-  // in registers (read during step hs - 1) and half-slab hs + 1 has landed; the
-  // buffer of hs is then refilled with hs + 4 while the products of hs run.  The
-  // wait also covers this wave's LDS reads, so no buffer is refilled while a read
-  // of it is in flight.
-  auto ring_step = [&](int hs) {
-    wait_vmcnt<4, true>();   // hs + 1 landed; hs + 2, hs + 3 may be in flight
-    barrier_nofence();
-    issue(hs + 4, buf(hs));
-  };
-  auto main_loop = [&](auto compute_t) {
-    constexpr bool COMPUTE = decltype(compute_t)::value;
+  auto main_loop = [&]() {
     AFrag afa, afb;
-    wait_vmcnt<6, true>();   // half-slab 0 landed
-    barrier_nofence();
-    if (COMPUTE) load_af(afa, buf(0));
+    load_af(afa, 0);
     // linear half-slab 0: phi = b'_r F_f q_r, r = 16 ks + 8 half + j
-    ring_step(0);
-    if (COMPUTE) {
+    {
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         const float4 b0 = *reinterpret_cast<const float4*>(ht + htab::BPF + 16 * ks + 8 * half);
@@ -895,12 +847,12 @@ k_readout_mfma(int n_q_heads, int n_kv_heads, int seq_len, int n_chunks, int n_h
         }
       }
       __builtin_amdgcn_sched_barrier(0);
-      load_af(afb, buf(1));
+      load_af(afb, 1);
     }
     // t-block c: 4 c + 2 half-slabs of 4 c rows, then the merged one; its first
     // half-slab hs0 has its fragments in X
     auto cblock = [&](int c, int hs0, AFrag& X, AFrag& Y) {
-      if (COMPUTE) {
+      {
         // q_t of this lane's 8 t's of block c, times qt_scale, as fp16
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) {
@@ -916,32 +868,25 @@ k_readout_mfma(int n_q_heads, int n_kv_heads, int seq_len, int n_chunks, int n_h
       }
       for (int pr = 0; pr < 2 * c + 1; ++pr) {
         const int hs = hs0 + 2 * pr;
-        ring_step(hs);
-        if (COMPUTE) quad(c, 2 * pr, X, Y, buf(hs + 1), true);
-        ring_step(hs + 1);
-        if (COMPUTE) quad(c, 2 * pr + 1, Y, X, buf(hs + 2), true);
+        quad(c, 2 * pr, X, Y, hs + 1, true);
+        quad(c, 2 * pr + 1, Y, X, hs + 2, true);
       }
       const int hs = hs0 + 4 * c + 2;
-      ring_step(hs);
-      if (COMPUTE) quad_merged(c, X, Y, buf(hs + 1), hs + 1 < Cfg::NHS);
+      quad_merged(c, X, Y, hs + 1, hs + 1 < Cfg::NHS);
     };
     cblock(0, 1, afb, afa);
     cblock(1, 4, afa, afb);
     cblock(2, 11, afb, afa);
     cblock(3, 22, afa, afb);
-    wait_vmcnt<0>();   // the last (repeated) prefetches
   };
-  if (head_ok)
-    main_loop(bool_t<true>{});
-  else
-    main_loop(bool_t<false>{});
+  if (head_ok) main_loop();
 
   // ================= epilogue: + a F H0, normalise, store ======================
   if (!head_ok) return;
 #pragma unroll
   for (int nt = NT0; nt < 2; ++nt) {
     den[nt] += __shfl_xor(den[nt], 32, 64);
-    if (!den_giver) den[nt] += dx[32 * nt + col];   // written before the intra-chunk barrier
+    if (!den_giver) den[nt] += dx[32 * nt + col];   // written before the barrier ahead of the main loop
   }
   const float aF = rec[OAL_COEF_A] * F;
   // the lane's column taken afresh: the compiler would otherwise compute the
