@@ -48,10 +48,13 @@ struct ReadoutCfg {
   static constexpr int HS_BYTES = 4 * tile::KS_BYTES;   // one half-slab = 4 K-steps = 8 KB
   static constexpr int NHS = tile::NKS / 4;         // 37 half-slabs per tile
   static constexpr int Q_BYTES = HPW * CH * 128;    // = 32 KB
-  // The chunk's keys are staged for the intra-chunk part in the half-slab buffers,
-  // 128 at a time (k rows in buffers 0, 1, v^T rows in 2, 3): one pass up to
-  // C = 128, two at C = 256 (which keeps the workgroup's LDS below 80 KB, so that
-  // two workgroups fit a CU).
+  // The chunk's keys are staged for the intra-chunk part in the four 8 KB
+  // buffers, 128 at a time (k rows in buffers 0, 1, v^T rows in 2, 3): one pass
+  // up to C = 128, two at C = 256 (which keeps the workgroup's LDS below 80 KB, so
+  // that two workgroups fit a CU).  With two passes, pass p holds the 32-key tiles
+  // p, p + 2, p + 4, p + 6: every wave's token tiles (t, 7 - t) then meet five key
+  // tiles in the first pass and four in the second (contiguous halves gave 5 to 8
+  // and 4 to 1, and the barrier between the passes waits for the slowest).
   static constexpr int KPASS = CH < 128 ? CH : 128;  // keys per staging pass
   static constexpr int NPASS = CH / KPASS;
   static constexpr int KIT = KPASS / 64;             // token pairs per thread and pass
@@ -170,8 +173,13 @@ k_readout_mfma(int n_q_heads, int n_kv_heads, int seq_len, int n_chunks, int n_h
     const size_t row = ((size_t)b * n_q_heads + kv * rep + hh) * seq_len + t0 + min(tok, clen - 1);
     qv[it] = reinterpret_cast<const uint4*>(q + row * DH)[part];
   }
-  // k and v of a staging pass: thread t holds dims 8 (t & 7) .. + 7 of the tokens
-  // KPASS pass + 64 it + 2 (t >> 3) + e
+  // Chunk key of key s (0 .. KPASS - 1) of staging pass `pass`: staged 32-key tile
+  // j is the chunk's key tile 2 j + pass with two passes, j with one.
+  auto pass_key = [](int s, int pass) {
+    return Cfg::NPASS == 1 ? s : 32 * (2 * (s >> 5) + pass) + (s & 31);
+  };
+  // k and v of a staging pass: thread t holds dims 8 (t & 7) .. + 7 of the keys
+  // 64 it + 2 (t >> 3) + e of the pass
   const size_t kvrow0 = (size_t)unit * seq_len + t0;
   const int kpart = tid & 7, kpair = tid >> 3;
   uint4 kq[KIT][2], vq[KIT][2];
@@ -180,7 +188,7 @@ k_readout_mfma(int n_q_heads, int n_kv_heads, int seq_len, int n_chunks, int n_h
     for (int it = 0; it < KIT; ++it)
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
-        const size_t row = kvrow0 + min(Cfg::KPASS * pass + 64 * it + 2 * kpair + e, clen - 1);
+        const size_t row = kvrow0 + min(pass_key(64 * it + 2 * kpair + e, pass), clen - 1);
         kq[it][e] = reinterpret_cast<const uint4*>(k + row * DH)[kpart];
         vq[it][e] = reinterpret_cast<const uint4*>(v + row * DV)[kpart];
       }
@@ -236,7 +244,7 @@ k_readout_mfma(int n_q_heads, int n_kv_heads, int seq_len, int n_chunks, int n_h
   // ---- k rows, and v^T rows with the keys of each 16-block permuted: position
   //      8h + 4a + e holds key 8a + 4h + e (the key order of the kappa accumulator
   //      rows); the two tokens of a thread are adjacent there (one 32-bit write).
-  //      tok: the key inside the pass, KPASS pass + tok inside the chunk.
+  //      tok: the key inside the pass, pass_key(tok, pass) inside the chunk.
   auto stage_kv = [&](int pass) {
   // the thread's indices taken afresh: the compiler would otherwise keep the first
   // pass's LDS addresses live (spilled) across the intra-chunk part for the second
@@ -245,7 +253,7 @@ k_readout_mfma(int n_q_heads, int n_kv_heads, int seq_len, int n_chunks, int n_h
 #pragma unroll
   for (int it = 0; it < KIT; ++it) {
     const int tok = 64 * it + 2 * kpair_;      // even; tok + 1 is the pair's second token
-    const int ctok = Cfg::KPASS * pass + tok;
+    const int ctok = pass_key(tok, pass);     // tok even: ctok + 1 is the pair's second key
     const bool ok0 = ctok < clen, ok1 = ctok + 1 < clen;
     const uint4 k0 = ok0 ? kq[it][0] : make_uint4(0, 0, 0, 0);
     const uint4 k1 = ok1 ? kq[it][1] : make_uint4(0, 0, 0, 0);
@@ -661,30 +669,36 @@ k_readout_mfma(int n_q_heads, int n_kv_heads, int seq_len, int n_chunks, int n_h
         unit(hi - 1, M0{}, F_{}, ML{});
       }
     };
-    // key tiles 0 .. T1: both token tiles up to T0 (T0 the diagonal one of N-tile
-    // 0), then N-tile 1 alone (T1 its diagonal one).  With two passes T0 < 4 <= T1:
-    // the first pass holds key tiles 0..3, the second 4..7.
-    if constexpr (HALF) {   // N-tile 1 alone: key tiles 0 .. T1 (two passes)
-      if (head_ok) {
-        if (T1 < 4)
-          singles(0, T1 + 1, bool_t<true>{});
-        else
-          singles(0, 4, F_{});
+    // The key tiles of a pass against this wave's token tiles: both token tiles for
+    // key tiles up to T0 (T0 the diagonal one of N-tile 0), then N-tile 1 alone up
+    // to T1 (its diagonal one); in half mode N-tile 1 alone.  Units take staged
+    // key tiles j (chunk key tile kt_of(j)).
+    auto pass_units = [&](int pass) __attribute__((always_inline)) {
+      auto kt_of = [&](int j) { return Cfg::NPASS == 1 ? j : 2 * j + pass; };
+      // staged tiles with a chunk key tile <= kt, and the first one >= kt
+      auto j_upto = [&](int kt) { return Cfg::NPASS == 1 ? kt + 1 : (kt >= pass ? ((kt - pass) >> 1) + 1 : 0); };
+      auto j_from = [&](int kt) { return Cfg::NPASS == 1 ? kt : (kt <= pass ? 0 : (kt - pass + 1) >> 1); };
+      int lo = 0;
+      if constexpr (!HALF) {
+        const int m = j_upto(T0);
+        const bool d0 = m > 0 && kt_of(m - 1) == T0;
+        for (int j = 0; j + (d0 ? 1 : 0) < m; ++j) unit(j, M1{}, F_{}, F_{});
+        if (d0) unit(m - 1, M1{}, bool_t<true>{}, F_{});
+        lo = j_from(T0 + 1);
       }
-    } else if (head_ok) {
-      for (int kt = 0; kt < T0; ++kt) unit(kt, M1{}, F_{}, F_{});
-      unit(T0, M1{}, bool_t<true>{}, F_{});
-      if (Cfg::NPASS == 1)
-        singles(T0 + 1, T1 + 1, bool_t<true>{});
+      const int hi = j_upto(T1);
+      if (hi > 0 && kt_of(hi - 1) == T1)
+        singles(lo, hi, bool_t<true>{});
       else
-        singles(T0 + 1, 4, F_{});
-    }
+        singles(lo, hi, F_{});
+    };
+    if (head_ok) pass_units(0);
     if (Cfg::NPASS > 1) {
       load_kv(1);        // (issued here: in flight during the first pass they would spill)
       __syncthreads();   // every wave is done with the first pass's keys
       stage_kv(1);
       __syncthreads();
-      if (head_ok && (!HALF || T1 >= 4)) singles(0, T1 - 4 + 1, bool_t<true>{});
+      if (head_ok) pass_units(1);
     }
   }
 
