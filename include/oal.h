@@ -100,7 +100,10 @@ oal_status oal_expand_coeffs(int n_q_heads, int d_h, int g_max, const int32_t* n
  *   coeffs  device output, oal_coeffs_bytes(n_q_heads, d_h, 1) bytes; the record
  *       has NG = 0, EPS = 0, A = a, BP, CM and CP filled and the group fields zero.
  * Such a record is read by oal_prefill_dim and oal_decode_step.  oal_prefill's
- * readouts evaluate grouped records only and return NaN outputs for it.
+ * readouts evaluate grouped records only and return NaN outputs for it: the
+ * record lives in device memory, and telling its kind on the host would take a
+ * device-to-host copy and a synchronisation inside every prefill call (the
+ * Python binding refuses, on the host, a buffer that oal_dim_coeffs filled).
  * kappa_dim must stay positive on the inputs for the outputs to be meaningful
  * (e.g. [[a, b^T/2], [b/2, C]] positive definite); nothing checks this. */
 oal_status oal_dim_coeffs(int n_q_heads, int d_h, const float* a, const float* b, const float* C,

@@ -10,6 +10,7 @@ from __future__ import annotations
 
 import ctypes
 import os
+import weakref
 
 import torch
 
@@ -216,6 +217,28 @@ def _expect_workspace(ws: torch.Tensor | None, nbytes: int, device) -> None:
 # ---------------------------------------------------------------------------
 
 
+# Buffers that oal_dim_coeffs filled last (keyed by address, holding the tensor
+# weakly): the grouped prefill calls refuse them on the host, since the library
+# reads a record's kind only on the device (where it can only make the outputs NaN).
+_DIM_RECORDS: dict = {}
+
+
+def _mark_record(coeffs: torch.Tensor, dimension_specific: bool) -> None:
+    if dimension_specific:
+        _DIM_RECORDS[coeffs.data_ptr()] = weakref.ref(coeffs)
+    else:
+        _DIM_RECORDS.pop(coeffs.data_ptr(), None)
+
+
+def _refuse_dim_record(coeffs: torch.Tensor | None) -> None:
+    if coeffs is None:
+        return
+    ref = _DIM_RECORDS.get(coeffs.data_ptr())
+    if ref is not None and ref() is coeffs:
+        raise ValueError("coeffs holds a dimension-specific record (oal_dim_coeffs): "
+                         "the grouped prefill cannot evaluate it; use oal_prefill_dim")
+
+
 def oal_coeffs_bytes(n_q_heads: int, d_h: int = D_H, g_max: int = 6) -> int:
     return int(_lib.oal_coeffs_bytes(n_q_heads, d_h, g_max))
 
@@ -235,6 +258,7 @@ def oal_expand_coeffs(n_groups: torch.Tensor, group_map: torch.Tensor, L: torch.
     _expect_coeffs(coeffs, Hq, dev)
     _check(_lib.oal_expand_coeffs(Hq, group_map.shape[-1], g_max, _ptr(n_groups), _ptr(group_map),
                                   _ptr(L), float(eps), _ptr(coeffs), _stream(L)))
+    _mark_record(coeffs, False)
     return coeffs
 
 
@@ -251,6 +275,7 @@ def oal_dim_coeffs(a: torch.Tensor, b: torch.Tensor, C: torch.Tensor,
         coeffs = torch.empty((Hq, COEF_WORDS), dtype=torch.float32, device=dev)
     _expect_coeffs(coeffs, Hq, dev)
     _check(_lib.oal_dim_coeffs(Hq, D_H, _ptr(a), _ptr(b), _ptr(C), _ptr(coeffs), _stream(a)))
+    _mark_record(coeffs, True)
     return coeffs
 
 
@@ -376,6 +401,7 @@ def oal_prefill_fresh(q: torch.Tensor | None, k: torch.Tensor, v: torch.Tensor,
 
 
 def _prefill_call(fn, q, k, v, coeffs, chunk, state, y, workspace, want_output):
+    _refuse_dim_record(coeffs)
     B, Hkv, N, Hq, y = _prefill_args(q, k, v, coeffs, state, y, want_output)
     dh, dv = D_H, D_V
     in_dt = _dtype_code(k)
@@ -403,6 +429,7 @@ def oal_prefill_noalloc(q: torch.Tensor | None, k: torch.Tensor, v: torch.Tensor
     are wanted (the caller owns every buffer)."""
     if want_output and y is None:
         raise ValueError("oal_prefill_noalloc allocates nothing: pass y")
+    _refuse_dim_record(coeffs)
     B, Hkv, N, Hq, y = _prefill_args(q, k, v, coeffs, state, y, want_output)
     out_dt = _dtype_code(y) if y is not None else OAL_F32
     _check(_lib.oal_prefill_noalloc(B, Hq, Hkv, N, D_H, D_V, _dtype_code(k), _ptr(q), _ptr(k), _ptr(v),

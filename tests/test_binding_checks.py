@@ -144,3 +144,22 @@ def test_other_calls_reject_mismatches(oal):
     with pytest.raises(ValueError):      # y_ref shape
         oal.oal_output_mse(torch.zeros(1, 4, 16, 64, dtype=f32), torch.zeros(1, 4, 8, 64, dtype=f32))
     assert not oal._reached
+
+
+def test_grouped_prefill_refuses_a_dimension_specific_record(oal):
+    """A buffer that oal_dim_coeffs filled last is refused by the grouped prefill
+    calls on the host (the library could only make the outputs NaN); once
+    oal_expand_coeffs refills it, it is accepted again."""
+    q, k, v = qkv()
+    c = coeffs(oal)
+    a, b, C = torch.zeros(4, dtype=f32), torch.zeros(4, 64, dtype=f32), torch.zeros(4, 64, 64, dtype=f32)
+    oal.oal_dim_coeffs(a, b, C, c)
+    for call in (lambda: oal.oal_prefill(q, k, v, c),
+                 lambda: oal.oal_prefill_fresh(q, k, v, c, fake_state(oal, 1, 2)),
+                 lambda: oal.oal_prefill_noalloc(q, k, v, c, y=torch.zeros(1, 4, 16, 64, dtype=bf))):
+        with pytest.raises(ValueError, match="dimension-specific"):
+            call()
+    assert "oal_prefill" not in oal._reached and "oal_prefill_fresh" not in oal._reached
+    ng, gm, L = torch.ones(4, dtype=i32), torch.zeros(4, 64, dtype=i32), torch.zeros(4, 7, 7, dtype=f32)
+    oal.oal_expand_coeffs(ng, gm, L, 1e-6, c)
+    oal._refuse_dim_record(c)   # accepted again

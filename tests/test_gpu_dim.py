@@ -111,14 +111,18 @@ def test_grouped_record_through_prefill_dim(oal, dtype):
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_grouped_prefill_poisons_a_dim_record(oal, dtype):
-    """oal_prefill's readouts evaluate grouped records only: a dimension-specific
-    record yields NaN outputs rather than a silently wrong value."""
+    """oal_prefill's readouts evaluate grouped records only: the binding refuses the
+    buffer that oal_dim_coeffs filled, and the library itself (reached here through
+    another tensor over the same memory) yields NaN outputs rather than a silently
+    wrong value."""
     w = synth.small_workload(740, "dim misuse", 1, 2, 1, 150, dtype)
     announce(f"oal_prefill with a dimension-specific record, {dtype}")
     case = Case(w)
     _, (a, b, C) = _dim(case)
     coeffs = oal.oal_dim_coeffs(a, b, C)
-    y = oal.oal_prefill(case.q, case.k, case.v, coeffs, chunk=64)
+    with pytest.raises(ValueError, match="dimension-specific"):
+        oal.oal_prefill(case.q, case.k, case.v, coeffs, chunk=64)
+    y = oal.oal_prefill(case.q, case.k, case.v, coeffs[:], chunk=64)
     torch.cuda.synchronize()
     assert torch.isnan(y.float()).all()
 
