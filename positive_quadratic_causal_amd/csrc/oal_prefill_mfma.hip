@@ -768,7 +768,6 @@ k_readout_mfma(int n_q_heads, int n_kv_heads, int seq_len, int n_chunks, int n_h
       qr[nt][2] = hi[0];
       qr[nt][3] = hi[1];
     }
-    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       f16x8 f0, f1;
@@ -790,7 +789,6 @@ k_readout_mfma(int n_q_heads, int n_kv_heads, int seq_len, int n_chunks, int n_h
         acc[mt][1] = mfma32h(af[i][mt], f1, acc[mt][1]);
       }
     }
-    __builtin_amdgcn_s_setprio(0);
   };
   // the merged half-slab of t-block c: K-step i holds rows 16 c + 8 + 2 i + half
   // against t = 16 c + 8 .. 16 c + 15 in both lane halves (multiplicity 1)
